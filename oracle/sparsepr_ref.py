@@ -1,0 +1,513 @@
+"""Plain fp64 NumPy oracle of SparsePR's per-call sparse attention operator.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; nothing in the HIP library uses
+it and the two share no code.
+
+Source: "Partition the Support, Reconstruct the Residual: Training-Free Sparse
+Attention for Video Generation and World Models" (Taghavi, Langari, Pandey),
+paper text as rendered on paperpeel.com.  Each function names the section or
+equation it follows.  Every step is a separate function so that tests can run
+it on intermediates produced by the GPU ("lockstep").
+
+Everything is fp64.  Inputs (bf16 or fp32 values) convert to fp64 exactly.
+
+Readings taken where the pages are silent or garbled (all "parity unpinned"
+against the pages; the tests pin them against mathematics instead):
+
+* F = U_r diag(sqrt(lambda_r)) from the eigendecomposition of the metric,
+  eigenvalues below ``eig_clamp * lambda_1`` set to zero.
+* mu_K is the unweighted mean of the nonempty key-group centroids; C_k in M_Q
+  counts nonempty groups.
+* k-means: initial centres are feature rows drawn uniformly with replacement
+  by SplitMix64; ties go to the lowest centre index; an empty centre keeps its
+  previous position; a run stops after an assignment pass whose labels did not
+  change or whose assignment cost fell by at most ``tol`` relative to the
+  previous pass, or after ``max_iters`` passes.  Nonempty clusters are then
+  renumbered in ascending order.
+* Routing score overflow is avoided by a per-query-group shift (the order of
+  the scores within a query group does not depend on it).  Score ties go to the
+  lower K/V group.  The prefix is the shortest one whose key count reaches the
+  budget, at least one group, all groups if the budget cannot be reached.
+* Probe allocation (the text of App. A.2 that defines m_a is missing):
+  largest-remainder apportionment of M over query groups by size; remainder
+  ties go to the larger group, then the lower group id; inside a group the
+  rows with the smallest d_i (ties: lower row index).
+* Text tokens (trailing ``n_text`` rows): not partitioned; their keys form one
+  extra group that every query group selects; their query rows attend densely;
+  they take no part in probes or the fit.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Params", "splitmix64", "init_indices", "sample_rows", "key_metric", "metric_factor",
+    "project", "kmeans_assign", "kmeans_update", "kmeans", "compact_labels", "group_perm",
+    "key_group_stats", "query_metric", "query_coords", "query_group_stats", "key_budget",
+    "route_scores", "route_select", "route", "sparse_attention_rows", "dense_attention_rows",
+    "executed_density", "allocate_probes", "select_probes", "ridge_fit", "correct", "relative_error",
+    "sparsepr_head",
+]
+
+U64 = (1 << 64) - 1
+GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+
+
+@dataclasses.dataclass
+class Params:
+    """Operator hyperparameters (Table C.1 of the paper's App. C.2 gives the defaults)."""
+    Ck: int = 1000
+    Cq: int = 300
+    rK: int = 48
+    rQ: int = 64
+    Ms: int = 2048
+    max_iters: int = 25
+    tol: float = 1e-4
+    rms_eps: float = 1e-6
+    eig_clamp: float = 1e-6
+    seed: int = 0
+    M: int = 64
+    rho: float = 0.22
+    lam: float = 1.0
+    std_eps: float = 1e-6
+    n_text: int = 0
+
+
+# --------------------------------------------------------------------------- RNG
+def splitmix64(seed: int, counter: int) -> int:
+    """Counter-based SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): the output
+    that the generator seeded with ``seed`` returns on call ``counter`` (0-based)."""
+    z = (seed + (counter + 1) * GOLDEN_GAMMA) & U64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & U64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & U64
+    return z ^ (z >> 31)
+
+
+def init_indices(seed: int, head: int, stage: int, C: int, N: int) -> np.ndarray:
+    """Initial k-means centres: C feature rows drawn uniformly with replacement
+    (App. C.1).  Counter = ((head*2 + stage) << 20) + m; stage 0 = K/V, 1 = query."""
+    base = (head * 2 + stage) << 20
+    return np.array([splitmix64(seed, base + m) % N for m in range(C)], dtype=np.int64)
+
+
+# ------------------------------------------------------------- metric and factors
+def sample_rows(Nv: int, Ms: int) -> np.ndarray:
+    """Evenly spaced query rows for the key metric (App. C.2: up to Ms rows, all
+    rows when fewer are available): s_i = floor(i * Nv / Ms)."""
+    m = min(Ms, Nv)
+    return (np.arange(m, dtype=np.int64) * Nv) // m
+
+
+def key_metric(Q: np.ndarray, Ms: int) -> np.ndarray:
+    """Key-response metric M_K = Q_s^T Q_s / M_s (Sec. 4.1, App. B.1)."""
+    Qs = np.asarray(Q, dtype=np.float64)[sample_rows(Q.shape[0], Ms)]
+    return Qs.T @ Qs / Qs.shape[0]
+
+
+def metric_factor(Mmat: np.ndarray, r: int, clamp: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Rank-r factor F with F F^T = the rank-r truncation of the metric (Sec. 4.1:
+    distances in phi = x F reproduce the truncated response metric).
+    Returns (F [d, r], eigenvalues descending after clamping)."""
+    w, U = np.linalg.eigh(np.asarray(Mmat, dtype=np.float64))
+    w, U = w[::-1].copy(), U[:, ::-1]
+    top = w[0] if w.size and w[0] > 0 else 0.0
+    w[w < clamp * top] = 0.0
+    w[w < 0] = 0.0
+    return U[:, :r] * np.sqrt(w[:r])[None, :], w
+
+
+def project(X: np.ndarray, F: np.ndarray) -> np.ndarray:
+    """Response coordinates phi(x) = x F (Sec. 4.1)."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(F, dtype=np.float64)
+
+
+# ------------------------------------------------------------------------ k-means
+def kmeans_assign(X: np.ndarray, cent: np.ndarray):
+    """Nearest centre by squared Euclidean distance, ties to the lowest index.
+    Returns (labels, distance to the chosen centre, relative margin
+    (d_second - d_best) / d_second per point)."""
+    X = np.asarray(X, dtype=np.float64)
+    cent = np.asarray(cent, dtype=np.float64)
+    D = (X * X).sum(1)[:, None] + (cent * cent).sum(1)[None, :] - 2.0 * (X @ cent.T)
+    labels = np.argmin(D, axis=1)
+    diff = X - cent[labels]
+    dbest = (diff * diff).sum(1)
+    # Margins are taken over distinct centre positions: bitwise-equal centres
+    # (duplicates of the sampling with replacement) tie exactly and the
+    # lowest-index rule settles them the same way in any implementation.
+    uniq, first = np.unique(cent, axis=0, return_index=True)
+    if uniq.shape[0] > 1:
+        part = np.partition(D[:, np.sort(first)], 1, axis=1)
+        d2 = np.maximum(part[:, 1], 0.0)
+        d1 = np.maximum(part[:, 0], 0.0)
+        margin = np.where(d2 > 0, (d2 - d1) / np.where(d2 > 0, d2, 1.0), 0.0)
+    else:
+        margin = np.full(X.shape[0], np.inf)
+    return labels.astype(np.int64), dbest, margin
+
+
+def kmeans_update(X: np.ndarray, labels: np.ndarray, cent: np.ndarray) -> np.ndarray:
+    """Lloyd update: each centre moves to the mean of its members; a centre with no
+    members keeps its position."""
+    X = np.asarray(X, dtype=np.float64)
+    C = cent.shape[0]
+    sums = np.zeros((C, X.shape[1]))
+    np.add.at(sums, labels, X)
+    cnt = np.bincount(labels, minlength=C)
+    new = np.array(cent, dtype=np.float64, copy=True)
+    nz = cnt > 0
+    new[nz] = sums[nz] / cnt[nz, None]
+    return new
+
+
+def kmeans(X: np.ndarray, C: int, seed: int, head: int, stage: int, max_iters: int, tol: float):
+    """k-means with C requested clusters (Sec. 4.1; App. C.1 initialisation, Table C.1
+    limits).  Returns dict(labels (uncompacted), centres used by the final
+    assignment, passes, min_margin, stop_margin)."""
+    X = np.asarray(X, dtype=np.float64)
+    N = X.shape[0]
+    cent = X[init_indices(seed, head, stage, C, N)].copy()
+    prev = None
+    J_prev = None
+    min_margin = np.inf
+    stop_margin = np.inf
+    t = 0
+    for t in range(1, max_iters + 1):
+        labels, dbest, margin = kmeans_assign(X, cent)
+        min_margin = min(min_margin, float(margin.min()) if margin.size else np.inf)
+        J = float(dbest.sum())
+        if t > 1:
+            if np.array_equal(labels, prev):
+                break
+            # distance of the tolerance decision from its threshold, relative
+            gap = (J_prev - J) - tol * J_prev
+            stop_margin = min(stop_margin, abs(gap) / max(tol * J_prev, 1e-300))
+            if J_prev - J <= tol * J_prev:
+                break
+        if t == max_iters:
+            break
+        cent = kmeans_update(X, labels, cent)
+        prev, J_prev = labels, J
+    return dict(labels=labels, centres=cent, passes=t, min_margin=min_margin,
+                stop_margin=stop_margin)
+
+
+def compact_labels(labels: np.ndarray, C: int) -> Tuple[np.ndarray, int]:
+    """Drop empty clusters and renumber the rest in ascending order (Sec. 4.1:
+    C_k counts nonempty K/V groups)."""
+    nonempty = np.bincount(labels, minlength=C) > 0
+    newid = np.cumsum(nonempty) - 1
+    return newid[labels].astype(np.int64), int(nonempty.sum())
+
+
+def group_perm(labels_c: np.ndarray, n_groups: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Contiguous group-major order (Sec. 4.3), rows of a group in ascending original
+    index.  Returns (perm: position -> original row, offsets [n_groups + 1])."""
+    perm = np.argsort(labels_c, kind="stable")
+    off = np.zeros(n_groups + 1, dtype=np.int64)
+    off[1:] = np.cumsum(np.bincount(labels_c, minlength=n_groups))
+    return perm.astype(np.int64), off
+
+
+# ------------------------------------------------------------ query coordinates
+def key_group_stats(K: np.ndarray, V: np.ndarray, labels_c: np.ndarray, n_groups: int):
+    """Group sizes and key / value centroids (original space) of the K/V groups."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    size = np.bincount(labels_c, minlength=n_groups)
+    kbar = np.zeros((n_groups, K.shape[1]))
+    vbar = np.zeros((n_groups, V.shape[1]))
+    np.add.at(kbar, labels_c, K)
+    np.add.at(vbar, labels_c, V)
+    return size, kbar / size[:, None], vbar / size[:, None]
+
+
+def query_metric(kbar: np.ndarray) -> np.ndarray:
+    """Query-response metric M_Q = K~^T K~ / (C_k d), K~ rows = kbar_b - mu_K
+    (Sec. 4.1; the centring of App. B.2)."""
+    Ck, d = kbar.shape
+    Kt = kbar - kbar.mean(0)[None, :]
+    return Kt.T @ Kt / (Ck * d)
+
+
+def query_coords(Q: np.ndarray, FQ: np.ndarray, eps: float) -> np.ndarray:
+    """phi_Q(q) = RMSNorm(q F_Q) = q F_Q / max(sqrt(|q F_Q|^2 / r_Q), eps) (App. B.2)."""
+    Y = np.asarray(Q, dtype=np.float64) @ FQ
+    rms = np.sqrt((Y * Y).sum(1) / FQ.shape[1])
+    return Y / np.maximum(rms, eps)[:, None]
+
+
+def query_group_stats(Q: np.ndarray, phi: np.ndarray, labels_c: np.ndarray, n_groups: int):
+    """Query-group sizes, mean queries qbar_a (original space), mean coordinates c_a
+    and the distances d_i = |phi_Q(q_i) - c_a| of App. A.2."""
+    Q = np.asarray(Q, dtype=np.float64)
+    size = np.bincount(labels_c, minlength=n_groups)
+    qbar = np.zeros((n_groups, Q.shape[1]))
+    cbar = np.zeros((n_groups, phi.shape[1]))
+    np.add.at(qbar, labels_c, Q)
+    np.add.at(cbar, labels_c, phi)
+    qbar /= size[:, None]
+    cbar /= size[:, None]
+    dist = np.sqrt(((phi - cbar[labels_c]) ** 2).sum(1))
+    return size, qbar, cbar, dist
+
+
+# ---------------------------------------------------------------------- routing
+def key_budget(rho: float, N: int, Nv: int, M: int, n_text: int) -> int:
+    """Common per-query key budget after reserving probe cost (Sec. 4.3).  The
+    executed-pair target rho * N^2 minus the fixed costs (probe rows against all
+    keys, text query rows, text keys of every video row) is spread over the Nv
+    video query rows; a prefix count is an integer, so reaching the real budget T
+    means reaching ceil(T)."""
+    total = rho * N * N
+    fixed = float(n_text) * N + float(M) * N + float(Nv) * n_text
+    T = (total - fixed) / Nv
+    return int(math.ceil(T))
+
+
+def executed_density(route_pairs: int, N: int, M: int, n_text: int) -> float:
+    """rho_exec = rho_route + M / N_q (Sec. 4.3): routed pairs plus every exact pair of
+    the M probe rows (counted although they are recomputed) and, with text tokens,
+    the dense text query rows, over the N x N grid."""
+    return (route_pairs + n_text * N + M * N) / float(N) ** 2
+
+
+def route_scores(qbar: np.ndarray, K: np.ndarray, V: np.ndarray, kv_labels_c: np.ndarray,
+                 kbar: np.ndarray, vbar: np.ndarray, groups: Optional[Sequence[int]] = None):
+    """Value-error routing score of App. B.3:
+    s_ab = 1/|G_b| sum_{j in G_b} | e^{qbar_a kbar_b / sqrt d} vbar_b - e^{qbar_a k_j / sqrt d} v_j |^2,
+    evaluated with every exponent shifted by m_a = max over all logits of row a
+    (one positive factor per query group, so the order within a row is unchanged).
+    Returns scores [len(groups), C_k] and the shifts."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    d = K.shape[1]
+    Ck = kbar.shape[0]
+    size = np.bincount(kv_labels_c, minlength=Ck)
+    rows = range(qbar.shape[0]) if groups is None else groups
+    out = np.zeros((len(rows), Ck))
+    shifts = np.zeros(len(rows))
+    order = np.argsort(kv_labels_c, kind="stable")
+    starts = np.concatenate([[0], np.cumsum(size)[:-1]])
+    for ia, a in enumerate(rows):
+        lbar = kbar @ qbar[a] / math.sqrt(d)
+        lkey = K @ qbar[a] / math.sqrt(d)
+        m = max(lbar.max(), lkey.max())
+        A = np.exp(lbar - m)
+        Bj = np.exp(lkey - m)
+        diff = A[kv_labels_c][:, None] * vbar[kv_labels_c] - Bj[:, None] * V
+        err = (diff * diff).sum(1)
+        out[ia] = np.add.reduceat(err[order], starts) / size
+        shifts[ia] = m
+    return out, shifts
+
+
+def route_select(scores_a: np.ndarray, kv_size: np.ndarray, T: int) -> Tuple[np.ndarray, Dict]:
+    """Budgeted prefix (Sec. 4.3): rank K/V groups by descending score (ties to the
+    lower group), keep the shortest prefix whose cumulative key count reaches T
+    (at least one group; all groups if T is out of reach).  Returns the ranked
+    selected groups and the relative score gaps next to the prefix boundary."""
+    Ck = scores_a.shape[0]
+    order = np.lexsort((np.arange(Ck), -scores_a))
+    cum = np.cumsum(kv_size[order])
+    hit = np.nonzero(cum >= T)[0]
+    L = int(hit[0]) + 1 if hit.size else Ck
+    L = max(L, 1)
+    s = scores_a[order]
+    gaps = []
+    for t in range(max(L - 2, 0), min(L + 1, Ck - 1)):
+        hi, lo = s[t], s[t + 1]
+        gaps.append((hi - lo) / max(abs(hi), 1e-300))
+    return order[:L].astype(np.int64), dict(L=L, min_gap=min(gaps) if gaps else np.inf)
+
+
+def route(qbar, K, V, kv_labels_c, kbar, vbar, kv_size, T):
+    """Scores and prefix for every query group.  Returns (list of ranked selections,
+    scores, info list)."""
+    scores, _ = route_scores(qbar, K, V, kv_labels_c, kbar, vbar)
+    sel, info = [], []
+    for a in range(qbar.shape[0]):
+        s, inf = route_select(scores[a], kv_size, T)
+        sel.append(s)
+        info.append(inf)
+    return sel, scores, info
+
+
+# -------------------------------------------------------------------- attention
+def _softmax_rows(Z: np.ndarray) -> np.ndarray:
+    Z = Z - Z.max(1, keepdims=True)
+    E = np.exp(Z)
+    return E / E.sum(1, keepdims=True)
+
+
+def dense_attention_rows(Q, K, V, rows) -> np.ndarray:
+    """Dense attention O = softmax(Q K^T / sqrt d) V (Sec. 3) for the given rows."""
+    Q = np.asarray(Q, dtype=np.float64)[np.asarray(rows)]
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    return _softmax_rows(Q @ K.T / math.sqrt(K.shape[1])) @ V
+
+
+def sparse_attention_rows(Q, K, V, rows, q_labels_c, kv_labels_c, selections, n_text: int = 0):
+    """Renormalised block-sparse output (Eq. (2) of Sec. 3): row i of video query
+    group a attends to the keys of the selected K/V groups of a, plus the text keys;
+    text query rows attend to every key."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    N, d = K.shape
+    Nv = N - n_text
+    kv_labels_c = np.asarray(kv_labels_c)
+    out = np.zeros((len(rows), V.shape[1]))
+    text = np.arange(Nv, N)
+    for r, i in enumerate(rows):
+        if i >= Nv:
+            keys = np.arange(N)
+        else:
+            sel = selections[int(q_labels_c[i])]
+            keys = np.nonzero(np.isin(kv_labels_c, sel))[0]
+            keys = np.concatenate([keys, text])
+        z = K[keys] @ Q[i] / math.sqrt(d)
+        p = np.exp(z - z.max())
+        out[r] = (p / p.sum()) @ V[keys]
+    return out
+
+
+# ------------------------------------------------------------------------ probes
+def allocate_probes(q_size: np.ndarray, M: int) -> np.ndarray:
+    """m_a: largest-remainder apportionment of M probes by group size, capped at the
+    group size; remainder ties to the larger group, then the lower group id."""
+    q_size = np.asarray(q_size, dtype=np.int64)
+    Nv = int(q_size.sum())
+    prod = M * q_size
+    m = np.minimum(prod // Nv, q_size)
+    rem = prod % Nv
+    left = M - int(m.sum())
+    order = sorted(range(q_size.size), key=lambda a: (-int(rem[a]), -int(q_size[a]), a))
+    while left > 0:
+        progressed = False
+        for a in order:
+            if left == 0:
+                break
+            if m[a] < q_size[a]:
+                m[a] += 1
+                left -= 1
+                progressed = True
+        if not progressed:
+            break
+    return m
+
+
+def select_probes(q_labels_c: np.ndarray, dist: np.ndarray, q_size: np.ndarray, M: int):
+    """Query-group-stratified probes (App. A.2): in each group the m_a rows closest to
+    the group's mean coordinate (smallest d_i, ties to the lower row); weights
+    w_p = |G_a| / m_a.  Returns (rows in group-major order, w, m_a)."""
+    m = allocate_probes(q_size, M)
+    rows, w = [], []
+    for a in range(q_size.size):
+        if m[a] == 0:
+            continue
+        members = np.nonzero(q_labels_c == a)[0]
+        order = np.lexsort((members, dist[members]))
+        take = members[order[: m[a]]]
+        rows.extend(take.tolist())
+        w.extend([q_size[a] / m[a]] * int(m[a]))
+    return np.array(rows, dtype=np.int64), np.array(w, dtype=np.float64), m
+
+
+# -------------------------------------------------------------------------- fit
+def ridge_fit(X: np.ndarray, R: np.ndarray, w: np.ndarray, lam: float, std_eps: float):
+    """Weighted affine fit of Sec. 4.2 / App. A.3:
+    alpha = w / sum w, W = diag(M w / sum w); features standardised with the
+    alpha-weighted mean and sqrt(weighted variance + std_eps) (App. D.3); residuals
+    centred by their alpha-weighted mean mu_R; B minimises
+    |W^{1/2}(Rbar - Xbar B)|_F^2 + lam |B|_F^2, solved through the normal equations
+    by Cholesky.  Returns dict(muX, sd, muR, B)."""
+    X = np.asarray(X, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    M, d = X.shape
+    alpha = w / w.sum()
+    wt = M * w / w.sum()
+    muX = alpha @ X
+    var = alpha @ ((X - muX) ** 2)
+    sd = np.sqrt(var + std_eps)
+    Xb = (X - muX) / sd
+    muR = alpha @ R
+    Rb = R - muR
+    G = Xb.T @ (wt[:, None] * Xb) + lam * np.eye(d)
+    H = Xb.T @ (wt[:, None] * Rb)
+    L = np.linalg.cholesky(G)
+    B = np.linalg.solve(L.T, np.linalg.solve(L, H))
+    return dict(muX=muX, sd=sd, muR=muR, B=B)
+
+
+def correct(O_sp: np.ndarray, fit: Dict) -> np.ndarray:
+    """Residual prediction and corrected output for unprobed rows (Sec. 4.2):
+    O_i + mu_R + ((O_i - mu_X) / sd) B."""
+    O_sp = np.asarray(O_sp, dtype=np.float64)
+    return O_sp + fit["muR"] + ((O_sp - fit["muX"]) / fit["sd"]) @ fit["B"]
+
+
+def relative_error(O: np.ndarray, O_dense: np.ndarray) -> np.ndarray:
+    """Per-row |O_i - O_i^dense|_2 / (|O_i^dense|_2 + 1e-8) (caption of Table D.1)."""
+    O = np.asarray(O, dtype=np.float64)
+    O_dense = np.asarray(O_dense, dtype=np.float64)
+    return np.linalg.norm(O - O_dense, axis=1) / (np.linalg.norm(O_dense, axis=1) + 1e-8)
+
+
+# ------------------------------------------------------------------ whole head
+def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int]] = None,
+                  full: bool = True) -> Dict:
+    """One head of the operator, every stage in the order of Sec. 4 and App. C.3.
+    ``rows`` limits the attention outputs to a subset (default: all rows)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, d = q.shape
+    Nv = N - p.n_text
+    qv, kv, vv = q[:Nv], k[:Nv], v[:Nv]
+    out: Dict = {}
+    MK = key_metric(qv, p.Ms)
+    FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
+    phiK = project(kv, FK)
+    km = kmeans(phiK, p.Ck, p.seed, head, 0, p.max_iters, p.tol)
+    kv_lab, nkv = compact_labels(km["labels"], p.Ck)
+    kv_size, kbar, vbar = key_group_stats(kv, vv, kv_lab, nkv)
+    MQ = query_metric(kbar)
+    FQ, wQ = metric_factor(MQ, p.rQ, p.eig_clamp)
+    phiQ = query_coords(qv, FQ, p.rms_eps)
+    qm = kmeans(phiQ, p.Cq, p.seed, head, 1, p.max_iters, p.tol)
+    q_lab, nq = compact_labels(qm["labels"], p.Cq)
+    q_size, qbar, cbar, dist = query_group_stats(qv, phiQ, q_lab, nq)
+    T = key_budget(p.rho, N, Nv, p.M, p.n_text)
+    sel, scores, rinfo = route(qbar, kv, vv, kv_lab, kbar, vbar, kv_size, T)
+    pairs = int(sum(int(q_size[a]) * (int(kv_size[sel[a]].sum()) + p.n_text) for a in range(nq)))
+    rho_exec = executed_density(pairs, N, p.M, p.n_text)
+    probes, w, m_a = select_probes(q_lab, dist, q_size, p.M)
+    out.update(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
+               kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, phiQ=phiQ, kmQ=qm, q_label=q_lab, n_q=nq,
+               q_size=q_size, qbar=qbar, cbar=cbar, qdist=dist, T=T, sel=sel, scores=scores,
+               route_info=rinfo, pairs=pairs, rho_exec=rho_exec, probes=probes, probe_w=w, m_a=m_a)
+    if not full:
+        return out
+    q_lab_full = np.concatenate([q_lab, np.full(p.n_text, -1)])
+    X = sparse_attention_rows(q, k, v, probes, q_lab_full, kv_lab, sel, p.n_text)
+    Od = dense_attention_rows(q, k, v, probes)
+    fit = ridge_fit(X, Od - X, w, p.lam, p.std_eps)
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    Osp = sparse_attention_rows(q, k, v, rows, q_lab_full, kv_lab, sel, p.n_text)
+    Ohat = Osp.copy()
+    video = rows < Nv
+    Ohat[video] = correct(Osp[video], fit)
+    pos = {int(r): i for i, r in enumerate(probes)}
+    for ir, r in enumerate(rows):
+        if int(r) in pos:
+            Ohat[ir] = Od[pos[int(r)]]
+    out.update(rows=rows, O_sp=Osp, O_hat=Ohat, probe_dense=Od, probe_sparse=X, fit=fit)
+    return out
