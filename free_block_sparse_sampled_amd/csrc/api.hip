@@ -1,0 +1,263 @@
+// extern "C" entry points of libsparsepr: argument validation, workspace layout and the
+// stream-ordered stage launches.  Validation runs on the host before any HIP call, so a
+// rejected call has no effect on the device.
+#include <cmath>
+
+#include "common.hpp"
+#include "stages.hpp"
+
+namespace spr {
+
+static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
+  Workspace L = {};
+  const size_t BH = size_t(desc.B) * desc.H, d = desc.d, Nv = size_t(desc.N - desc.n_text);
+  L.Cmax = p.Ck > p.Cq ? p.Ck : p.Cq;
+  L.rmax = p.rK > p.rQ ? p.rK : p.rQ;
+  L.nblk = int((Nv + kAssignThreads - 1) / kAssignThreads);
+  L.splits = kProbeSplits;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.metric = take(BH * d * d * 8);
+  L.ktilde = take(BH * p.Ck * d * 8);
+  L.phiK = take(BH * Nv * p.rK * 8);
+  L.phiQ = take(BH * Nv * p.rQ * 8);
+  L.km_cent = take(BH * L.Cmax * L.rmax * 8);
+  L.km_cent32 = take(BH * L.Cmax * L.rmax * 4);
+  L.km_sums = take(BH * L.Cmax * L.rmax * 8);
+  L.km_cnt = take(BH * L.Cmax * 4);
+  L.km_lab = take(BH * Nv * 4);
+  L.km_jpart = take(BH * L.nblk * 8);
+  L.km_cpart = take(BH * L.nblk * 4);
+  L.km_ctrl = take(BH * 4 * 8);
+  L.cbar = take(BH * p.Cq * p.rQ * 8);
+  L.vstat = take(BH * Nv * 2 * 8);
+  L.gstat = take(BH * 8 * 4);
+  L.pstat = take(BH * p.Cq * 2 * 4);
+  L.shift = take(BH * p.Cq * 8);
+  L.scores = take(BH * p.Cq * p.Ck * 8);
+  const size_t Mm = M > 0 ? size_t(M) : 1;
+  L.pr_part = take(BH * Mm * L.splits * (d + 2) * 4);
+  L.fitX = take(BH * Mm * d * 8);
+  L.fitR = take(BH * Mm * d * 8);
+  L.fitG = take(BH * d * d * 8);
+  L.fitH = take(BH * d * d * 8);
+  L.fitS = take(BH * 4 * d * 8);
+  L.fitW = take(BH * Mm * 8);
+  L.applyB = take(BH * d * d * 4);
+  L.applyC = take(BH * d * 4);
+  L.total = o;
+  return L;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static spr_status check_desc(const spr_desc* d) {
+  if (!d) return SPR_EINVAL;
+  if (d->B < 1 || d->H < 1 || d->N < 2) return SPR_EINVAL;
+  if (d->dtype != SPR_BF16 && d->dtype != SPR_F32) return SPR_EUNSUPPORTED;
+  if (d->d != 64 && d->d != 128) return SPR_EUNSUPPORTED;
+  if (d->n_text < 0 || d->N - d->n_text < 2) return SPR_EINVAL;
+  const int64_t es = d->dtype == SPR_BF16 ? 2 : 4;
+  if (d->sn < d->d || d->sh < 1 || d->sb < 1) return SPR_EINVAL;
+  if ((d->sn * es) % 16 || (d->sh * es) % 16 || (d->sb * es) % 16) return SPR_EINVAL;
+  return SPR_OK;
+}
+
+static spr_status check_params(const spr_desc* d, const spr_part_params* p) {
+  if (!p) return SPR_EINVAL;
+  const int Nv = d->N - d->n_text;
+  if (p->Ck < 1 || p->Cq < 1 || p->Ck > 1024 || p->Cq > 1024 || p->Ck > Nv || p->Cq > Nv) return SPR_EINVAL;
+  if (p->rK < 1 || p->rQ < 1 || p->rK > d->d || p->rQ > d->d) return SPR_EINVAL;
+  if (!kmeans_rank_supported(p->rK) || !kmeans_rank_supported(p->rQ)) return SPR_EUNSUPPORTED;
+  if (p->Ms < 1 || p->max_iters < 1) return SPR_EINVAL;
+  if (!(p->tol >= 0.0) || !(p->rms_eps > 0.0) || !(p->eig_clamp >= 0.0)) return SPR_EINVAL;
+  return SPR_OK;
+}
+
+// ceil of the per-query key budget of Sec. 4.3 (same expression order as the documented one)
+static int64_t key_budget(double rho, int N, int Nv, int M, int n_text) {
+  const double total = rho * double(N) * double(N);
+  const double fixed = double(n_text) * double(N) + double(M) * double(N) + double(Nv) * double(n_text);
+  const double T = (total - fixed) / double(Nv);
+  return int64_t(std::ceil(T));
+}
+
+static spr_status check_ws(const spr_desc* d, const spr_part_params* p, int M, void* ws, size_t ws_bytes,
+                           Workspace* L) {
+  *L = layout(*d, *p, M);
+  if (!ws || !aligned16(ws)) return SPR_EINVAL;
+  if (ws_bytes < L->total) return SPR_EWORKSPACE;
+  return SPR_OK;
+}
+
+}  // namespace spr
+
+using namespace spr;
+
+extern "C" {
+
+const char* sparsepr_status_string(spr_status s) {
+  switch (s) {
+    case SPR_OK: return "ok";
+    case SPR_EINVAL: return "invalid argument";
+    case SPR_EUNSUPPORTED: return "unsupported head dimension, rank or dtype";
+    case SPR_EWORKSPACE: return "workspace too small";
+    case SPR_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t sparsepr_workspace_size(const spr_desc* desc, const spr_part_params* params, int32_t M) {
+  if (check_desc(desc) != SPR_OK || check_params(desc, params) != SPR_OK) return 0;
+  return layout(*desc, *params, M).total;
+}
+
+spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k, const void* v,
+                              const spr_part_params* params, spr_partition* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if ((s = check_params(desc, params)) != SPR_OK) return s;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
+  const void* req[] = {out->kv_label, out->q_label, out->kv_perm, out->q_perm, out->q_pos, out->kv_off,
+                       out->q_off, out->n_kv, out->n_q, out->kbar, out->vbar, out->qbar, out->qdist,
+                       out->FK, out->FQ, out->Qp, out->Kp, out->Vp};
+  for (const void* p : req)
+    if (!p) return SPR_EINVAL;
+  if (!aligned16(out->Qp) || !aligned16(out->Kp) || !aligned16(out->Vp)) return SPR_EINVAL;
+  Workspace L;
+  if ((s = check_ws(desc, params, 1, ws, ws_bytes, &L)) != SPR_OK) return s;
+  return run_partition(*desc, q, k, v, *params, *out, ws, L, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
+                          double rho_exec_target, int32_t M, spr_route* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if ((s = check_params(desc, params)) != SPR_OK) return s;
+  if (!part || !out) return SPR_EINVAL;
+  const int Nv = desc->N - desc->n_text;
+  if (M < 1 || M >= Nv) return SPR_EINVAL;
+  if (!(rho_exec_target > 0.0) || rho_exec_target > 1.0) return SPR_EINVAL;
+  const int64_t Tk = key_budget(rho_exec_target, desc->N, Nv, M, desc->n_text);
+  if (Tk < 1) return SPR_EINVAL;
+  if (!out->sel_cnt || !out->sel_kv || !out->tile_off || !out->probe_idx || !out->probe_w || !out->pairs ||
+      !out->rho_exec)
+    return SPR_EINVAL;
+  Workspace L;
+  if ((s = check_ws(desc, params, M, ws, ws_bytes, &L)) != SPR_OK) return s;
+  return run_route(*desc, *params, *part, rho_exec_target, M, Tk, *out, ws, L, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_attn_sparse(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
+                                const spr_route* route, float* o_sp, void* ws, size_t ws_bytes, void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if ((s = check_params(desc, params)) != SPR_OK) return s;
+  if (!part || !route || !o_sp || !aligned16(o_sp)) return SPR_EINVAL;
+  Workspace L;
+  if ((s = check_ws(desc, params, 1, ws, ws_bytes, &L)) != SPR_OK) return s;
+  return run_attn_sparse(*desc, *params, *part, *route, o_sp, ws, L, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* probe_idx, int32_t M, float* o_probe, void* ws, size_t ws_bytes,
+                                void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if (!q || !k || !v || !probe_idx || !o_probe || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
+  const int Nv = desc->N - desc->n_text;
+  if (M < 1 || M >= Nv) return SPR_EINVAL;
+  // the probe stage only needs the split-K partial buffer, sized by (BH, M, d)
+  const size_t need = size_t(desc->B) * desc->H * M * kProbeSplits * (desc->d + 2) * 4;
+  if (!ws || !aligned16(ws)) return SPR_EINVAL;
+  if (ws_bytes < need) return SPR_EWORKSPACE;
+  Workspace L = {};
+  L.pr_part = 0;
+  L.splits = kProbeSplits;
+  return run_probe_exact(*desc, q, k, v, probe_idx, M, o_probe, ws, L, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
+                                const spr_route* route, const float* o_sp, const float* o_probe, int32_t M,
+                                double lam, double std_eps, void* out, int32_t out_dtype, double* fit_state,
+                                int32_t* head_status, void* ws, size_t ws_bytes, void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if ((s = check_params(desc, params)) != SPR_OK) return s;
+  const int Nv = desc->N - desc->n_text;
+  if (M < 1 || M >= Nv) return SPR_EINVAL;
+  if (!(lam >= 0.0) || !(std_eps > 0.0)) return SPR_EINVAL;
+  if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
+  if (!part || !route || !o_sp || !o_probe || !out || !head_status) return SPR_EINVAL;
+  Workspace L;
+  if ((s = check_ws(desc, params, M, ws, ws_bytes, &L)) != SPR_OK) return s;
+  return run_fit_correct(*desc, *params, *part, *route, o_sp, o_probe, M, lam, std_eps, out, out_dtype, fit_state,
+                         head_status, ws, L, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v, void* out,
+                               int32_t out_dtype, void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
+  if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
+  return run_attn_dense(*desc, q, k, v, out, out_dtype, static_cast<hipStream_t>(stream));
+}
+
+size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C) {
+  if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || r < 1 || r > 64) return 0;
+  const int nblk = (n + kAssignThreads - 1) / kAssignThreads;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { o = align_up(o + bytes); };
+  take(size_t(BH) * C * r * 4);  // cent32
+  take(size_t(BH) * C * r * 8);  // sums
+  take(size_t(BH) * C * 4);      // counts
+  take(size_t(BH) * nblk * 8);   // jpart
+  take(size_t(BH) * nblk * 4);   // cpart
+  take(size_t(BH) * 4 * 8);      // ctrl
+  return o;
+}
+
+spr_status sparsepr_kmeans(int32_t BH, int32_t n, int32_t r, int32_t C, const double* feat, uint64_t seed,
+                           int32_t stage, int32_t max_iters, double tol, int32_t* labels, double* centres,
+                           int32_t* passes, void* ws, size_t ws_bytes, void* stream) {
+  if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || max_iters < 1 || !(tol >= 0.0)) return SPR_EINVAL;
+  if (stage != 0 && stage != 1) return SPR_EINVAL;
+  if (!kmeans_rank_supported(r)) return SPR_EUNSUPPORTED;
+  if (!feat || !labels || !centres || !passes || !ws || !aligned16(ws)) return SPR_EINVAL;
+  const size_t need = sparsepr_kmeans_workspace_size(BH, n, r, C);
+  if (ws_bytes < need) return SPR_EWORKSPACE;
+  const int nblk = (n + kAssignThreads - 1) / kAssignThreads;
+  char* w = static_cast<char*>(ws);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return w + at;
+  };
+  KmArgs a;
+  a.BH = BH; a.n = n; a.r = r; a.C = C; a.stage = stage; a.max_iters = max_iters; a.nblk = nblk; a.tol = tol;
+  a.seed = seed; a.feat = feat; a.cent = centres; a.labels = labels;
+  a.cent32 = reinterpret_cast<float*>(take(size_t(BH) * C * r * 4));
+  a.sums = reinterpret_cast<double*>(take(size_t(BH) * C * r * 8));
+  a.cnt = reinterpret_cast<int*>(take(size_t(BH) * C * 4));
+  a.jpart = reinterpret_cast<double*>(take(size_t(BH) * nblk * 8));
+  a.cpart = reinterpret_cast<int*>(take(size_t(BH) * nblk * 4));
+  a.ctrl = reinterpret_cast<double*>(take(size_t(BH) * 4 * 8));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  spr_status s = run_kmeans(a, st);
+  if (s != SPR_OK) return s;
+  launch_copy_passes1(a.ctrl, BH, passes, st);
+  SPR_CHECK_LAUNCH();
+  return SPR_OK;
+}
+
+}  // extern "C"

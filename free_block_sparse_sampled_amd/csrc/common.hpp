@@ -1,0 +1,184 @@
+// Internal helpers shared by the HIP translation units of libsparsepr.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparsepr.h"
+
+namespace spr {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- element access
+// bf16 values are handled as raw 16-bit patterns; widening to fp32 is exact.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+  if constexpr (DT == SPR_BF16) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  } else {
+    return static_cast<const float*>(base)[idx];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_out(void* base, int64_t idx, float x) {
+  if constexpr (DT == SPR_BF16) {
+    // round to nearest even
+    uint32_t u = __float_as_uint(x);
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    if ((u & 0x7F800000u) == 0x7F800000u) r = u;  // inf / nan pass through
+    static_cast<uint16_t*>(base)[idx] = uint16_t(r >> 16);
+  } else {
+    static_cast<float*>(base)[idx] = x;
+  }
+}
+
+template <int DT>
+struct ElemSize {
+  static constexpr int value = DT == SPR_BF16 ? 2 : 4;
+};
+
+// ----------------------------------------------------------------- head geometry
+struct HeadGeom {
+  int32_t B, H, N, Nv, d, n_text;
+  int64_t sb, sh, sn;
+  __host__ __device__ int64_t base(int hd) const { return int64_t(hd / H) * sb + int64_t(hd % H) * sh; }
+};
+
+inline HeadGeom make_geom(const spr_desc& d) {
+  HeadGeom g;
+  g.B = d.B; g.H = d.H; g.N = d.N; g.Nv = d.N - d.n_text; g.d = d.d; g.n_text = d.n_text;
+  g.sb = d.sb; g.sh = d.sh; g.sn = d.sn;
+  return g;
+}
+
+// ----------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum_d(double x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Deterministic block sum (fixed tree) of one double per thread; blockDim.x <= 1024.
+__device__ inline double block_sum_d(double x, double* red /* [32] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  x = wave_sum_d(x);
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < nw; ++i) t += red[i];
+    red[0] = t;
+  }
+  __syncthreads();
+  t = red[0];
+  __syncthreads();
+  return t;
+}
+
+__device__ inline int64_t block_sum_i64(int64_t x, int64_t* red /* [32] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  int64_t t = 0;
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < nw; ++i) t += red[i];
+    red[0] = t;
+  }
+  __syncthreads();
+  t = red[0];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive scan of one int per thread over the block (blockDim.x <= 1024); returns the
+// exclusive prefix and writes the total to *total.
+__device__ inline int block_exscan_i(int x, int* buf /* [1024] */, int* total) {
+  const int t = threadIdx.x;
+  buf[t] = x;
+  __syncthreads();
+  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
+    int y = (t >= o) ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += y;
+    __syncthreads();
+  }
+  int incl = buf[t];
+  int tot = buf[blockDim.x - 1];
+  __syncthreads();
+  *total = tot;
+  return incl - x;
+}
+
+// ----------------------------------------------------------------- SplitMix64
+// Counter-based SplitMix64 (Steele, Lea & Flood 2014): output number `counter` of the
+// generator seeded with `seed`.
+__host__ __device__ inline uint64_t splitmix64(uint64_t seed, uint64_t counter) {
+  uint64_t z = seed + (counter + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ----------------------------------------------------------------- workspace layout
+// Every internal buffer of one operator invocation, as byte offsets into the caller's
+// workspace.  Offsets are 256-byte aligned.
+struct Workspace {
+  size_t metric;     // double [BH][d][d]        M_K, later M_Q
+  size_t ktilde;     // double [BH][Ck][d]       centred key centroids
+  size_t phiK;       // double [BH][Nv][rK]      (unless the caller keeps them)
+  size_t phiQ;       // double [BH][Nv][rQ]
+  size_t km_cent;    // double [BH][Cmax][rmax]  k-means centres
+  size_t km_cent32;  // float  [BH][Cmax][rmax]  fp32 copy for the screening pass
+  size_t km_sums;    // double [BH][Cmax][rmax]
+  size_t km_cnt;     // int    [BH][Cmax]
+  size_t km_lab;     // int    [BH][Nv]          uncompacted labels
+  size_t km_jpart;   // double [BH][nblk]
+  size_t km_cpart;   // int    [BH][nblk]
+  size_t km_ctrl;    // double [BH][4]           done, passes, J_prev
+  size_t cbar;       // double [BH][Cq][rQ]      mean query coordinates c_a
+  size_t vstat;      // double [BH][Nv][2]       v_j . vbar_b(j), |v_j|^2 in Kp order
+  size_t gstat;      // int    [BH][8]           flags / counters per head
+  size_t pstat;      // int    [BH][Cq][2]       probes per query group, prefix
+  size_t shift;      // double [BH][Cq]          per-query-group exponent shift of the scores
+  size_t scores;     // double [BH][Cq][Ck]      (unless the caller keeps them)
+  size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows
+  size_t fitX;       // double [BH][M][d]        standardised probe features
+  size_t fitR;       // double [BH][M][d]        centred probe residuals
+  size_t fitG;       // double [BH][d][d]        normal matrix
+  size_t fitH;       // double [BH][d][d]        right-hand sides, then B
+  size_t fitS;       // double [BH][4][d]        mu_X, sd, mu_R, weights scratch
+  size_t fitW;       // double [BH][M]           unit-mean weights
+  size_t applyB;     // float  [BH][d][d]        I + diag(1/sd) B
+  size_t applyC;     // float  [BH][d]           mu_R - (mu_X / sd) B
+  size_t total;
+  int nblk;          // k-means assign blocks per head
+  int Cmax, rmax, splits;
+};
+
+constexpr int kAssignThreads = 256;
+constexpr int kProbeSplits = 16;
+
+Workspace layout(const spr_desc& desc, const spr_part_params& p, int M);
+
+}  // namespace spr
+
+#define SPR_CHECK_LAUNCH()                          \
+  do {                                              \
+    if (hipGetLastError() != hipSuccess) return SPR_EHIP; \
+  } while (0)

@@ -1,0 +1,57 @@
+// Stage drivers of libsparsepr (host side), implemented in the per-stage .hip files.
+#pragma once
+#include "common.hpp"
+
+namespace spr {
+
+struct KmArgs {
+  int BH, n, r, C, stage, max_iters, nblk;
+  double tol;
+  uint64_t seed;
+  const double* feat;
+  double* cent;
+  float* cent32;
+  double* sums;
+  int* cnt;
+  int* labels;
+  double* jpart;
+  int* cpart;
+  double* ctrl;
+};
+
+spr_status run_kmeans(const KmArgs& a, hipStream_t st);
+void launch_copy_passes1(const double* ctrl, int BH, int* passes, hipStream_t st);
+bool kmeans_rank_supported(int r);
+size_t compact_smem(int C);
+size_t jacobi_smem(int d);
+spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, int* perm, int* pos_of, int* off,
+                          int* ngroups, int* gstat, int empty_bit, hipStream_t st);
+
+spr_status run_partition(const spr_desc& desc, const void* q, const void* k, const void* v, const spr_part_params& p,
+                         spr_partition& out, void* ws, const Workspace& L, hipStream_t st);
+spr_status run_route(const spr_desc& desc, const spr_part_params& p, const spr_partition& part, double rho, int M,
+                     int64_t Tk, spr_route& out, void* ws, const Workspace& L, hipStream_t st);
+spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
+                           const spr_route& route, float* o_sp, void* ws, const Workspace& L, hipStream_t st);
+spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, const void* v, const int* probe_idx,
+                           int M, float* o_probe, void* ws, const Workspace& L, hipStream_t st);
+spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
+                           const spr_route& route, const float* o_sp, const float* o_probe, int M, double lam,
+                           double std_eps, void* out, int out_dtype, double* fit_state, int* head_status, void* ws,
+                           const Workspace& L, hipStream_t st);
+spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
+                          int out_dtype, hipStream_t st);
+
+// Raise the dynamic-LDS limit of a kernel above the 64 KB default once per process.
+template <typename K>
+inline void allow_lds(K kernel, size_t bytes) {
+  if (bytes > 65536) hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+template <typename T>
+inline T* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace spr

@@ -1,0 +1,323 @@
+"""ctypes binding of libsparsepr (include/sparsepr.h).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP
+stream; every step of the operator runs in the library's HIP kernels.  The library must
+have been built (``python -m free_block_sparse_sampled_amd.build``); nothing here falls
+back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparsepr.so")
+
+SPR_BF16, SPR_F32 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP launch failed"}
+HS_BITS = {1: "cholesky_fallback", 2: "budget_unreached", 4: "kv_groups_empty", 8: "q_groups_empty", 16: "rms_floor"}
+
+P = ctypes.c_void_p
+
+
+class spr_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("n_text", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64)]
+
+
+class spr_part_params(ctypes.Structure):
+    _fields_ = [("Ck", ctypes.c_int32), ("Cq", ctypes.c_int32), ("rK", ctypes.c_int32), ("rQ", ctypes.c_int32),
+                ("Ms", ctypes.c_int32), ("max_iters", ctypes.c_int32), ("tol", ctypes.c_double),
+                ("rms_eps", ctypes.c_double), ("eig_clamp", ctypes.c_double), ("seed", ctypes.c_uint64)]
+
+
+_PART_FIELDS = ["kv_label", "q_label", "kv_perm", "q_perm", "q_pos", "kv_off", "q_off", "n_kv", "n_q", "kbar",
+                "vbar", "qbar", "qdist", "FK", "FQ", "Qp", "Kp", "Vp", "phiK", "phiQ", "cK_last", "cQ_last", "passes"]
+_ROUTE_FIELDS = ["sel_cnt", "sel_kv", "tile_off", "probe_idx", "probe_w", "pairs", "rho_exec", "scores"]
+
+
+class spr_partition(ctypes.Structure):
+    _fields_ = [(n, P) for n in _PART_FIELDS]
+
+
+class spr_route(ctypes.Structure):
+    _fields_ = [(n, P) for n in _ROUTE_FIELDS]
+
+
+class SparsePRError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def library():
+    """Load libsparsepr.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SparsePRError(f"{LIB_PATH} is missing: build it with `python -m free_block_sparse_sampled_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        st = ctypes.c_int
+        lib.sparsepr_workspace_size.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params), ctypes.c_int32]
+        lib.sparsepr_workspace_size.restype = ctypes.c_size_t
+        lib.sparsepr_partition.argtypes = [ctypes.POINTER(spr_desc), P, P, P, ctypes.POINTER(spr_part_params),
+                                           ctypes.POINTER(spr_partition), P, ctypes.c_size_t, P]
+        lib.sparsepr_partition.restype = st
+        lib.sparsepr_route.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
+                                       ctypes.POINTER(spr_partition), ctypes.c_double, ctypes.c_int32,
+                                       ctypes.POINTER(spr_route), P, ctypes.c_size_t, P]
+        lib.sparsepr_route.restype = st
+        lib.sparsepr_attn_sparse.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
+                                             ctypes.POINTER(spr_partition), ctypes.POINTER(spr_route), P, P,
+                                             ctypes.c_size_t, P]
+        lib.sparsepr_attn_sparse.restype = st
+        lib.sparsepr_probe_exact.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P, P,
+                                             ctypes.c_size_t, P]
+        lib.sparsepr_probe_exact.restype = st
+        lib.sparsepr_fit_correct.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
+                                             ctypes.POINTER(spr_partition), ctypes.POINTER(spr_route), P, P,
+                                             ctypes.c_int32, ctypes.c_double, ctypes.c_double, P, ctypes.c_int32, P, P,
+                                             P, ctypes.c_size_t, P]
+        lib.sparsepr_fit_correct.restype = st
+        lib.sparsepr_attn_dense.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P]
+        lib.sparsepr_attn_dense.restype = st
+        lib.sparsepr_kmeans.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
+                                        ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P, P, P,
+                                        ctypes.c_size_t, P]
+        lib.sparsepr_kmeans.restype = st
+        lib.sparsepr_kmeans_workspace_size.argtypes = [ctypes.c_int32] * 4
+        lib.sparsepr_kmeans_workspace_size.restype = ctypes.c_size_t
+        lib.sparsepr_status_string.argtypes = [ctypes.c_int]
+        lib.sparsepr_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+EXPORTED = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attn_sparse",
+            "sparsepr_probe_exact", "sparsepr_fit_correct", "sparsepr_attn_dense", "sparsepr_kmeans",
+            "sparsepr_kmeans_workspace_size", "sparsepr_status_string"]
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise SparsePRError(f"{what}: {STATUS.get(status, status)}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclasses.dataclass
+class OperatorConfig:
+    """Hyperparameters of one operator call (defaults: Table C.1 of the paper's App. C.2)."""
+    Ck: int = 1000
+    Cq: int = 300
+    rK: int = 48
+    rQ: int = 64
+    Ms: int = 2048
+    max_iters: int = 25
+    tol: float = 1e-4
+    rms_eps: float = 1e-6
+    eig_clamp: float = 1e-6
+    seed: int = 0
+    M: int = 64
+    rho: float = 0.22
+    lam: float = 1.0
+    std_eps: float = 1e-6
+
+    def part_params(self) -> spr_part_params:
+        return spr_part_params(self.Ck, self.Cq, self.rK, self.rQ, self.Ms, self.max_iters, self.tol, self.rms_eps,
+                               self.eig_clamp, self.seed)
+
+
+def make_desc(q: torch.Tensor, n_text: int = 0) -> spr_desc:
+    """Descriptor of a [B, H, N, d] tensor (any strides with a contiguous last dim)."""
+    if q.dim() != 4 or q.stride(3) != 1:
+        raise SparsePRError("q, k, v must be [B, H, N, d] with a contiguous last dimension")
+    dt = {torch.bfloat16: SPR_BF16, torch.float32: SPR_F32}.get(q.dtype)
+    if dt is None:
+        raise SparsePRError(f"unsupported dtype {q.dtype}")
+    B, H, N, d = q.shape
+    return spr_desc(B, H, N, d, n_text, dt, q.stride(0), q.stride(1), q.stride(2))
+
+
+class Partition:
+    """Device buffers of sparsepr_partition's outputs."""
+
+    def __init__(self, desc: spr_desc, cfg: OperatorConfig, device, diagnostics: bool = False):
+        BH, N, d = desc.B * desc.H, desc.N, desc.d
+        Nv = N - desc.n_text
+        i32, f64 = torch.int32, torch.float64
+        dt = torch.bfloat16 if desc.dtype == SPR_BF16 else torch.float32
+        z = lambda shape, t: torch.empty(shape, dtype=t, device=device)  # noqa: E731
+        self.kv_label = z((BH, Nv), i32)
+        self.q_label = z((BH, Nv), i32)
+        self.kv_perm = z((BH, Nv), i32)
+        self.q_perm = z((BH, Nv), i32)
+        self.q_pos = z((BH, Nv), i32)
+        self.kv_off = z((BH, cfg.Ck + 1), i32)
+        self.q_off = z((BH, cfg.Cq + 1), i32)
+        self.n_kv = z((BH,), i32)
+        self.n_q = z((BH,), i32)
+        self.kbar = z((BH, cfg.Ck, d), f64)
+        self.vbar = z((BH, cfg.Ck, d), f64)
+        self.qbar = z((BH, cfg.Cq, d), f64)
+        self.qdist = z((BH, Nv), f64)
+        self.FK = z((BH, d, cfg.rK), f64)
+        self.FQ = z((BH, d, cfg.rQ), f64)
+        self.Qp = z((BH, N, d), dt)
+        self.Kp = z((BH, N, d), dt)
+        self.Vp = z((BH, N, d), dt)
+        self.phiK = self.phiQ = self.cK_last = self.cQ_last = self.passes = None
+        if diagnostics:
+            self.phiK = z((BH, Nv, cfg.rK), f64)
+            self.phiQ = z((BH, Nv, cfg.rQ), f64)
+            self.cK_last = z((BH, cfg.Ck, cfg.rK), f64)
+            self.cQ_last = z((BH, cfg.Cq, cfg.rQ), f64)
+            self.passes = z((BH, 2), i32)
+        self.struct = spr_partition(*[_ptr(getattr(self, n)) for n in _PART_FIELDS])
+
+
+class Route:
+    """Device buffers of sparsepr_route's outputs."""
+
+    def __init__(self, desc: spr_desc, cfg: OperatorConfig, device, keep_scores: bool = False):
+        BH = desc.B * desc.H
+        i32 = torch.int32
+        z = lambda shape, t: torch.empty(shape, dtype=t, device=device)  # noqa: E731
+        self.sel_cnt = z((BH, cfg.Cq + 1), i32)
+        self.sel_kv = z((BH, cfg.Cq + 1, cfg.Ck + 1), i32)
+        self.tile_off = z((BH, cfg.Cq + 2), i32)
+        self.probe_idx = z((BH, cfg.M), i32)
+        self.probe_w = z((BH, cfg.M), torch.float64)
+        self.pairs = z((BH,), torch.int64)
+        self.rho_exec = z((BH,), torch.float64)
+        self.scores = z((BH, cfg.Cq, cfg.Ck), torch.float64) if keep_scores else None
+        self.struct = spr_route(*[_ptr(getattr(self, n)) for n in _ROUTE_FIELDS])
+
+
+# ----------------------------------------------------------------- C-ABI calls
+def sparsepr_workspace_size(desc: spr_desc, cfg: OperatorConfig) -> int:
+    n = library().sparsepr_workspace_size(ctypes.byref(desc), ctypes.byref(cfg.part_params()), cfg.M)
+    if n == 0:
+        raise SparsePRError("sparsepr_workspace_size: invalid descriptor or parameters")
+    return int(n)
+
+
+def sparsepr_partition(desc, q, k, v, cfg: OperatorConfig, part: Partition, ws: torch.Tensor, stream=None):
+    pp = cfg.part_params()
+    _check(library().sparsepr_partition(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(pp),
+                                        ctypes.byref(part.struct), _ptr(ws), ws.numel(), _stream(stream)),
+           "sparsepr_partition")
+
+
+def sparsepr_route(desc, cfg: OperatorConfig, part: Partition, route: Route, ws: torch.Tensor, stream=None):
+    pp = cfg.part_params()
+    _check(library().sparsepr_route(ctypes.byref(desc), ctypes.byref(pp), ctypes.byref(part.struct), cfg.rho, cfg.M,
+                                    ctypes.byref(route.struct), _ptr(ws), ws.numel(), _stream(stream)),
+           "sparsepr_route")
+
+
+def sparsepr_attn_sparse(desc, cfg: OperatorConfig, part: Partition, route: Route, o_sp: torch.Tensor,
+                         ws: torch.Tensor, stream=None):
+    pp = cfg.part_params()
+    _check(library().sparsepr_attn_sparse(ctypes.byref(desc), ctypes.byref(pp), ctypes.byref(part.struct),
+                                          ctypes.byref(route.struct), _ptr(o_sp), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "sparsepr_attn_sparse")
+
+
+def sparsepr_probe_exact(desc, q, k, v, probe_idx: torch.Tensor, M: int, o_probe: torch.Tensor, ws: torch.Tensor,
+                         stream=None):
+    _check(library().sparsepr_probe_exact(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(probe_idx), M,
+                                          _ptr(o_probe), _ptr(ws), ws.numel(), _stream(stream)),
+           "sparsepr_probe_exact")
+
+
+def sparsepr_fit_correct(desc, cfg: OperatorConfig, part: Partition, route: Route, o_sp, o_probe, out,
+                         head_status, ws, fit_state=None, stream=None):
+    pp = cfg.part_params()
+    out_dt = SPR_BF16 if out.dtype == torch.bfloat16 else SPR_F32
+    _check(library().sparsepr_fit_correct(ctypes.byref(desc), ctypes.byref(pp), ctypes.byref(part.struct),
+                                          ctypes.byref(route.struct), _ptr(o_sp), _ptr(o_probe), cfg.M, cfg.lam,
+                                          cfg.std_eps, _ptr(out), out_dt, _ptr(fit_state), _ptr(head_status), _ptr(ws),
+                                          ws.numel(), _stream(stream)), "sparsepr_fit_correct")
+
+
+def sparsepr_attn_dense(desc, q, k, v, out, stream=None):
+    out_dt = SPR_BF16 if out.dtype == torch.bfloat16 else SPR_F32
+    _check(library().sparsepr_attn_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dt,
+                                         _stream(stream)), "sparsepr_attn_dense")
+
+
+def sparsepr_kmeans(feat: torch.Tensor, C: int, seed: int, stage: int, max_iters: int, tol: float, stream=None):
+    """k-means helper on feat [BH, n, r] fp64; returns (labels, centres of the final pass, passes)."""
+    BH, n, r = feat.shape
+    lib = library()
+    nbytes = lib.sparsepr_kmeans_workspace_size(BH, n, r, C)
+    if nbytes == 0:
+        raise SparsePRError("sparsepr_kmeans_workspace_size: invalid arguments")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=feat.device)
+    labels = torch.empty((BH, n), dtype=torch.int32, device=feat.device)
+    cent = torch.empty((BH, C, r), dtype=torch.float64, device=feat.device)
+    passes = torch.empty((BH,), dtype=torch.int32, device=feat.device)
+    _check(lib.sparsepr_kmeans(BH, n, r, C, _ptr(feat), seed, stage, max_iters, tol, _ptr(labels), _ptr(cent),
+                               _ptr(passes), _ptr(ws), nbytes, _stream(stream)), "sparsepr_kmeans")
+    return labels, cent, passes
+
+
+# ----------------------------------------------------------------- whole operator
+class SparsePR:
+    """The five calls of one operator invocation with buffers allocated once.
+
+    ``run(q, k, v)`` returns the corrected output [B, H, N, d] (fp32 by default)."""
+
+    def __init__(self, q: torch.Tensor, cfg: OperatorConfig, n_text: int = 0, out_dtype=torch.float32,
+                 diagnostics: bool = False, keep_scores: bool = False):
+        self.cfg = cfg
+        self.desc = make_desc(q, n_text)
+        dev = q.device
+        B, H, N, d = q.shape
+        self.ws = torch.empty(sparsepr_workspace_size(self.desc, cfg), dtype=torch.uint8, device=dev)
+        self.part = Partition(self.desc, cfg, dev, diagnostics)
+        self.route = Route(self.desc, cfg, dev, keep_scores)
+        self.o_sp = torch.empty((B * H, N, d), dtype=torch.float32, device=dev)
+        self.o_probe = torch.empty((B * H, cfg.M, d), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+        self.head_status = torch.empty((B * H,), dtype=torch.int32, device=dev)
+        self.fit_state = torch.empty((B * H, 3 * d + d * d), dtype=torch.float64, device=dev) if diagnostics else None
+
+    def partition(self, q, k, v):
+        sparsepr_partition(self.desc, q, k, v, self.cfg, self.part, self.ws)
+
+    def route_(self):
+        sparsepr_route(self.desc, self.cfg, self.part, self.route, self.ws)
+
+    def attn_sparse(self):
+        sparsepr_attn_sparse(self.desc, self.cfg, self.part, self.route, self.o_sp, self.ws)
+
+    def probe_exact(self, q, k, v):
+        sparsepr_probe_exact(self.desc, q, k, v, self.route.probe_idx, self.cfg.M, self.o_probe, self.ws)
+
+    def fit_correct(self):
+        sparsepr_fit_correct(self.desc, self.cfg, self.part, self.route, self.o_sp, self.o_probe, self.out,
+                             self.head_status, self.ws, self.fit_state)
+
+    def run(self, q, k, v) -> torch.Tensor:
+        self.partition(q, k, v)
+        self.route_()
+        self.attn_sparse()
+        self.probe_exact(q, k, v)
+        self.fit_correct()
+        return self.out

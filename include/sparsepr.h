@@ -1,0 +1,214 @@
+/*
+ * sparsepr.h - C ABI of an MI355X (gfx950) implementation of SparsePR's
+ * per-call sparse attention operator.
+ *
+ * Source of the method: "Partition the Support, Reconstruct the Residual:
+ * Training-Free Sparse Attention for Video Generation and World Models"
+ * (Taghavi, Langari, Pandey).  Section references below are to that paper.
+ *
+ * One operator call, for every (batch, head), maps Q, K, V [N, d] to the
+ * corrected output O^hat [N, d] in five stream-ordered calls:
+ *
+ *   sparsepr_partition    response-coupled partitioning (Sec. 4.1, App. B.1-B.2)
+ *   sparsepr_route        routing scores, budgeted prefixes, probe choice
+ *                         (Sec. 4.3, App. B.3, App. A.2)
+ *   sparsepr_attn_sparse  renormalised block-sparse attention (Eq. (2), Sec. 3)
+ *   sparsepr_probe_exact  exact dense attention of the probe rows (Sec. 4.2)
+ *   sparsepr_fit_correct  weighted ridge fit + correction + order restore
+ *                         (Sec. 4.2, App. A.3)
+ *
+ * Conventions shared by every call
+ * ---------------------------------
+ *  - All data pointers are DEVICE pointers unless a parameter says "host".
+ *    The caller allocates every buffer (the library never allocates device
+ *    memory) and keeps it alive until the stream has passed the call.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Nothing synchronises with the host; counts that depend on the data stay
+ *    on the device.
+ *  - Heads are flattened: head index hd = b * H + h, BH = B * H.  Per-head
+ *    arrays below are laid out [BH][...] with the stated inner size even where
+ *    the used part is smaller (for example only n_kv[hd] of Ck groups).
+ *  - The last n_text of the N tokens of a head are text tokens: they are not
+ *    partitioned, their keys form one extra K/V group (index n_kv[hd]) that
+ *    every query group selects, and their query rows attend to all keys.
+ *    Nv = N - n_text video tokens are partitioned.
+ *  - Every call first validates its arguments on the host and returns a
+ *    status without launching anything when they are invalid:
+ *      SPR_EINVAL        null pointer, bad size or parameter (see each call)
+ *      SPR_EUNSUPPORTED  head dimension or dtype not built
+ *      SPR_EWORKSPACE    workspace smaller than sparsepr_workspace_size()
+ *      SPR_EHIP          a HIP launch failed (the stream state is undefined)
+ *    Anomalies that depend on the data are reported per head in the device
+ *    array `head_status` of sparsepr_fit_correct (SPR_HS_* bits).
+ *  - The workspace `ws` is scratch owned by the caller; the same workspace
+ *    must be passed to all five calls of one operator invocation (later calls
+ *    read state that earlier ones left there) and must not be shared by two
+ *    invocations in flight.
+ */
+#ifndef SPARSEPR_H
+#define SPARSEPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPR_OK = 0,
+  SPR_EINVAL = 1,
+  SPR_EUNSUPPORTED = 2,
+  SPR_EWORKSPACE = 3,
+  SPR_EHIP = 4
+} spr_status;
+
+typedef enum { SPR_BF16 = 0, SPR_F32 = 1 } spr_dtype;
+
+/* per-head status bits written by sparsepr_fit_correct */
+enum {
+  SPR_HS_CHOLESKY_FALLBACK = 1, /* normal matrix not positive definite: mean-only correction */
+  SPR_HS_BUDGET_UNREACHED = 2,  /* some query group selected every K/V group below budget */
+  SPR_HS_KV_GROUPS_EMPTY = 4,   /* fewer nonempty K/V groups than requested */
+  SPR_HS_Q_GROUPS_EMPTY = 8,    /* fewer nonempty query groups than requested */
+  SPR_HS_RMS_FLOOR = 16         /* some query coordinate norm fell below rms_eps */
+};
+
+/* Shape of q, k, v: element (b, h, n, c) lives at b*sb + h*sh + n*sn + c. */
+typedef struct {
+  int32_t B, H, N, d; /* d in {64, 128}; N includes the n_text trailing text tokens */
+  int32_t n_text;     /* 0 <= n_text < N */
+  int32_t dtype;      /* spr_dtype of q, k, v */
+  int64_t sb, sh, sn; /* element strides; the innermost stride is 1 */
+} spr_desc;
+
+/* Partition hyperparameters (defaults of Table C.1, App. C.2, in brackets). */
+typedef struct {
+  int32_t Ck, Cq;    /* requested K/V and query groups [1000, 300]; 1 <= C <= min(Nv, 1024) */
+  int32_t rK, rQ;    /* response ranks [48, 64]; 1 <= r <= min(d, 64) */
+  int32_t Ms;        /* metric query-sampling budget [2048]; min(Ms, Nv) evenly spaced rows */
+  int32_t max_iters; /* k-means assignment passes [25]; >= 1 */
+  double tol;        /* k-means relative cost-decrease tolerance [1e-4]; >= 0 */
+  double rms_eps;    /* RMSNorm floor of the query coordinates [1e-6]; > 0 */
+  double eig_clamp;  /* eigenvalues below eig_clamp * lambda_max count as zero [1e-6] */
+  uint64_t seed;     /* k-means initialisation seed (SplitMix64) */
+} spr_part_params;
+
+/* Outputs of sparsepr_partition (caller-owned device buffers). */
+typedef struct {
+  int32_t* kv_label; /* [BH][Nv]  K/V group of each video key, original order, groups renumbered
+                                  0..n_kv-1 in ascending cluster id (empty clusters dropped) */
+  int32_t* q_label;  /* [BH][Nv]  query group of each video query row, likewise */
+  int32_t* kv_perm;  /* [BH][Nv]  group-major position -> original key row (stable) */
+  int32_t* q_perm;   /* [BH][Nv]  group-major position -> original query row (stable) */
+  int32_t* q_pos;    /* [BH][Nv]  original query row -> group-major position */
+  int32_t* kv_off;   /* [BH][Ck+1] start of each K/V group in kv_perm order; kv_off[n_kv] = Nv */
+  int32_t* q_off;    /* [BH][Cq+1] start of each query group; q_off[n_q] = Nv */
+  int32_t* n_kv;     /* [BH] nonempty K/V groups */
+  int32_t* n_q;      /* [BH] nonempty query groups */
+  double* kbar;      /* [BH][Ck][d] key centroids of the K/V groups (original space) */
+  double* vbar;      /* [BH][Ck][d] value centroids */
+  double* qbar;      /* [BH][Cq][d] mean query of each query group */
+  double* qdist;     /* [BH][Nv]  |phi_Q(q_i) - c_a| (App. A.2), original order */
+  double* FK;        /* [BH][d][rK] key response factor, F F^T = rank-rK truncation of M_K */
+  double* FQ;        /* [BH][d][rQ] query response factor */
+  void* Qp;          /* [BH][N][d] q rows in group-major order, then the text rows; input dtype */
+  void* Kp;          /* [BH][N][d] k rows likewise (kv_perm order) */
+  void* Vp;          /* [BH][N][d] v rows likewise (kv_perm order) */
+  /* optional diagnostics, each may be NULL */
+  double* phiK;      /* [BH][Nv][rK] key coordinates k F_K */
+  double* phiQ;      /* [BH][Nv][rQ] query coordinates RMSNorm(q F_Q) */
+  double* cK_last;   /* [BH][Ck][rK] k-means centres used by the final K/V assignment pass */
+  double* cQ_last;   /* [BH][Cq][rQ] k-means centres used by the final query assignment pass */
+  int32_t* passes;   /* [BH][2] assignment passes run by the K/V and the query k-means */
+} spr_partition;
+
+/* Outputs of sparsepr_route (caller-owned device buffers). */
+typedef struct {
+  int32_t* sel_cnt;   /* [BH][Cq+1] number of selected K/V groups of each query group; entry n_q
+                                    is the text query group (when n_text > 0) */
+  int32_t* sel_kv;    /* [BH][Cq+1][Ck+1] selected video K/V groups in descending score order,
+                                    followed by the text group n_kv when n_text > 0 */
+  int32_t* tile_off;  /* [BH][Cq+2] prefix count of 64-row query tiles per query group */
+  int32_t* probe_idx; /* [BH][M] original row of each probe, group-major, nearest first */
+  double* probe_w;    /* [BH][M] coverage weight w_p = |G_a| / m_a */
+  int64_t* pairs;     /* [BH] routed query-key pairs, text keys of video rows included */
+  double* rho_exec;   /* [BH] executed-pair density incl. probes and text rows */
+  double* scores;     /* optional [BH][Cq][Ck] routing scores times a positive per-row factor */
+} spr_route;
+
+/* Bytes of workspace the five calls need for this shape (host function, no device work).
+   Returns 0 when the arguments are invalid. */
+size_t sparsepr_workspace_size(const spr_desc* desc, const spr_part_params* params, int32_t M);
+
+/* Response-coupled partitioning (Sec. 4.1, App. B.1-B.2, App. C.1):
+   M_K from min(Ms, Nv) evenly spaced video query rows; F_K from its eigendecomposition;
+   k-means of phi_K = k F_K into Ck K/V groups (values follow their keys); key/value
+   centroids; M_Q = K~^T K~ / (n_kv d) with K~ the centred key centroids; F_Q;
+   phi_Q = RMSNorm(q F_Q); k-means into Cq query groups; group-major copies of Q, K, V.
+   EINVAL: null required pointer, B, H < 1, N < 2, n_text out of range, strides,
+   C, r, Ms, max_iters, tol, rms_eps, eig_clamp out of range. */
+spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k, const void* v,
+                              const spr_part_params* params, spr_partition* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Routing and probe selection (Sec. 4.3, App. B.3, App. A.2):
+   value-error scores s_ab for every (query group, K/V group); per query group the
+   shortest descending-score prefix whose key count reaches the common budget
+   ceil((rho*N^2 - n_text*N - M*N - Nv*n_text) / Nv); M probe rows stratified by query
+   group.  `rho_exec_target` is the total executed-pair target including probes.
+   EINVAL: 1 <= M < Nv violated, or the budget is below one key. */
+spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
+                          double rho_exec_target, int32_t M, spr_route* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Renormalised block-sparse attention (Eq. (2)): each row of query group a attends to the
+   keys of its selected K/V groups (and the text keys); text rows attend to all keys.
+   o_sp: [BH][N][d] fp32, rows in Qp order. */
+spr_status sparsepr_attn_sparse(const spr_desc* desc, const spr_part_params* params,
+                                const spr_partition* part, const spr_route* route, float* o_sp,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* Exact dense attention (Eq. (1)) of the probe rows probe_idx [BH][M] against all N keys of the
+   original q, k, v.  o_probe: [BH][M][d] fp32. */
+spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* probe_idx, int32_t M, float* o_probe, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Weighted ridge fit of the probe residuals against the sparse outputs and correction of the
+   unprobed rows (Sec. 4.2, App. A.3, App. D.3): alpha = w / sum w; W = diag(M w / sum w);
+   features standardised by the alpha-weighted mean and sqrt(weighted variance + std_eps);
+   residuals centred by their weighted mean mu_R; B = (Xb^T W Xb + lam I)^-1 Xb^T W Rb (fp64
+   Cholesky); O^hat_i = O^sp_i + mu_R + Xb_i B for unprobed video rows, the exact row for probes,
+   O^sp for text rows.  `out` is [B][H][N][d] contiguous in original row order, fp32 or bf16
+   (out_dtype).  `fit_state` (nullable) receives [BH][3d + d*d] fp64: mu_X, sd, mu_R, B.
+   `head_status` [BH] receives SPR_HS_* bits.  EINVAL: lam < 0, std_eps <= 0, M out of range. */
+spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* params,
+                                const spr_partition* part, const spr_route* route, const float* o_sp,
+                                const float* o_probe, int32_t M, double lam, double std_eps, void* out,
+                                int32_t out_dtype, double* fit_state, int32_t* head_status, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Baseline: dense flash attention softmax(q k^T / sqrt d) v for every row, same kernel family as
+   sparsepr_attn_sparse.  out: [B][H][N][d] contiguous, fp32 or bf16 (out_dtype). */
+spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v,
+                               void* out, int32_t out_dtype, void* stream);
+
+/* Test helper: k-means of `feat` [BH][n][r] fp64 (r <= 64, C <= min(n, 1024)) with the operator's
+   initialisation (stage 0 or 1), assignment, update and stopping rules.  labels [BH][n] receive
+   the uncompacted cluster ids; centres [BH][C][r] the centres used by the final assignment pass;
+   passes [BH] the number of assignment passes. */
+spr_status sparsepr_kmeans(int32_t BH, int32_t n, int32_t r, int32_t C, const double* feat, uint64_t seed,
+                           int32_t stage, int32_t max_iters, double tol, int32_t* labels, double* centres,
+                           int32_t* passes, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sparsepr_kmeans. */
+size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C);
+
+/* Static description of a status code (host). */
+const char* sparsepr_status_string(spr_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEPR_H */
