@@ -130,19 +130,23 @@ def project(X: np.ndarray, F: np.ndarray) -> np.ndarray:
 def kmeans_assign(X: np.ndarray, cent: np.ndarray):
     """Nearest centre by squared Euclidean distance, ties to the lowest index.
     Returns (labels, distance to the chosen centre, relative margin
-    (d_second - d_best) / d_second per point)."""
+    (d_second - d_best) / d_second per point).
+
+    Distances are evaluated once per distinct centre position, each standing for the
+    lowest index that holds it: bitwise-equal centres (duplicates of the sampling with
+    replacement) then tie exactly, which a library matmul does not guarantee for two
+    equal columns.  Margins are taken over distinct positions."""
     X = np.asarray(X, dtype=np.float64)
     cent = np.asarray(cent, dtype=np.float64)
-    D = (X * X).sum(1)[:, None] + (cent * cent).sum(1)[None, :] - 2.0 * (X @ cent.T)
-    labels = np.argmin(D, axis=1)
+    uniq, first = np.unique(cent, axis=0, return_index=True)
+    order = np.argsort(first)
+    uniq, first = uniq[order], first[order]
+    D = (X * X).sum(1)[:, None] + (uniq * uniq).sum(1)[None, :] - 2.0 * (X @ uniq.T)
+    labels = first[np.argmin(D, axis=1)]
     diff = X - cent[labels]
     dbest = (diff * diff).sum(1)
-    # Margins are taken over distinct centre positions: bitwise-equal centres
-    # (duplicates of the sampling with replacement) tie exactly and the
-    # lowest-index rule settles them the same way in any implementation.
-    uniq, first = np.unique(cent, axis=0, return_index=True)
     if uniq.shape[0] > 1:
-        part = np.partition(D[:, np.sort(first)], 1, axis=1)
+        part = np.partition(D, 1, axis=1)
         d2 = np.maximum(part[:, 1], 0.0)
         d1 = np.maximum(part[:, 0], 0.0)
         margin = np.where(d2 > 0, (d2 - d1) / np.where(d2 > 0, d2, 1.0), 0.0)

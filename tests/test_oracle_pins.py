@@ -93,6 +93,17 @@ def test_assign_matches_brute_force_direct_difference_and_lowest_index_ties():
     assert lab3[0] == 1
 
 
+def test_assign_duplicate_centres_go_to_the_lowest_index():
+    rng = _rng(6)
+    C = rng.standard_normal((40, 7))
+    C[31] = C[3]                                           # an exact duplicate at a higher index
+    C[38] = C[3]
+    X = np.vstack([C[3], C[3] + 1e-3 * rng.standard_normal(7), rng.standard_normal((50, 7))])
+    lab, _, _ = O.kmeans_assign(X, C)
+    assert lab[0] == 3 and lab[1] == 3
+    assert not np.isin(lab, [31, 38]).any()
+
+
 def _partition_key(labels):
     groups = {}
     for i, l in enumerate(labels):
