@@ -1,0 +1,214 @@
+"""Benchmark of one SparsePR operator call on one MI355X.
+
+A step is one whole call (partition -> route -> block-sparse attention -> exact probes ->
+fit + correct + restore) over one batch of seeded synthetic Q/K/V already resident in
+HBM.  Prints one JSON line.  Default workload: the mid-size video DiT call (B=1, H=40,
+N=32760 tokens on a 21x39x40 grid, d=128, bf16, 512 K/V and 512 query groups, 256
+probes, 22% executed-pair density).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="mid")
+    ap.add_argument("--rho", type=float, default=None)
+    ap.add_argument("--M", type=int, default=None)
+    ap.add_argument("--max-iters", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, opc):
+    """The oracle, untuned, on head 0 of the workload: partition, routing and probes in full,
+    the sparse attention of 64 evenly spaced rows, the exact probe rows and the fit; scaled to
+    a whole call (every head, every attention row)."""
+    import oracle as O
+    from workloads import head_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    q, k, v = head_inputs(cfg, 0, 0)
+    p = O.Params(Ck=opc.Ck, Cq=opc.Cq, rK=opc.rK, rQ=opc.rQ, Ms=opc.Ms, max_iters=opc.max_iters, tol=opc.tol,
+                 seed=opc.seed, M=opc.M, rho=opc.rho, lam=opc.lam, n_text=cfg.n_text)
+    t0 = time.perf_counter()
+    st = O.sparsepr_head(q, k, v, p, head=0, full=False)
+    t_part = time.perf_counter() - t0
+    rows = np.linspace(0, cfg.Nv - 1, 64).astype(np.int64)
+    qlab = np.concatenate([st["q_label"], np.full(cfg.n_text, -1)])
+    t0 = time.perf_counter()
+    O.sparse_attention_rows(q, k, v, rows, qlab, st["kv_label"], st["sel"], cfg.n_text)
+    t_rows = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    X = O.sparse_attention_rows(q, k, v, st["probes"], qlab, st["kv_label"], st["sel"], cfg.n_text)
+    Od = O.dense_attention_rows(q, k, v, st["probes"])
+    fit = O.ridge_fit(X, Od - X, st["probe_w"], p.lam, p.std_eps)
+    O.correct(X, fit)
+    t_fit = time.perf_counter() - t0
+    sample = t_part + t_rows + t_fit
+    per_head = t_part + t_rows * (cfg.N / len(rows)) + t_fit
+    return {"value": per_head * cfg.heads * 1e3, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
+            "sample": (f"head 0 of {cfg.heads}: partition, routing and probes in full, sparse attention of "
+                       f"{len(rows)} of {cfg.N} rows, probe rows and fit ({sample:.1f} s of CPU); scaled by "
+                       f"rows and heads to one call (extrapolated)"),
+            "sample_seconds": round(sample, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the operator shards by head with no communication); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import free_block_sparse_sampled_amd as spr
+    from workloads import batch_inputs, config
+
+    cfg = config(args.config)
+    if args.rho is not None:
+        cfg = cfg.with_(rho=args.rho)
+    if args.M is not None:
+        cfg = cfg.with_(M=args.M)
+    if args.max_iters is not None:
+        cfg = cfg.with_(max_iters=args.max_iters)
+    opc = spr.OperatorConfig(Ck=cfg.Ck, Cq=cfg.Cq, rK=cfg.rK, rQ=min(cfg.rQ, cfg.d), Ms=cfg.Ms,
+                             max_iters=cfg.max_iters, tol=cfg.tol, M=cfg.M, rho=cfg.rho, lam=cfg.lam, seed=0)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    q, k, v = batch_inputs(cfg)
+    tq, tk, tv = (torch.from_numpy(x).to(dt).cuda() for x in (q, k, v))
+    del q, k, v
+    op = spr.SparsePR(tq, opc, n_text=cfg.n_text)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        stages = (lambda: op.partition(tq, tk, tv), op.route_, op.attn_sparse, lambda: op.probe_exact(tq, tk, tv),
+                  op.fit_correct)
+        for i, f in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            f()
+        if ev is not None:
+            ev[len(stages)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    names = ["partition", "route", "attn_sparse", "probe_exact", "fit_correct"]
+    per = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(5)] for s in range(args.steps)])
+    total = np.array([evs[s][0].elapsed_time(evs[s][5]) for s in range(args.steps)])
+    ms_call = float(np.median(total))
+
+    pairs = op.route.pairs.double().sum().item()
+    rho_exec = op.route.rho_exec.mean().item()
+    passes = None
+    BH, N, d = cfg.heads, cfg.N, cfg.d
+    dense_flops = 4.0 * BH * N * N * d
+    exec_flops = 4.0 * d * (pairs + BH * cfg.M * N + BH * cfg.n_text * N)
+    t_attn = float(np.median(per[:, 2]))
+    t_probe = float(np.median(per[:, 3]))
+    sparse_tflops = 4.0 * d * pairs / (t_attn * 1e-3) / 1e12
+
+    result = {
+        "metric": "ms/call & dense-equiv TFLOP/s at 22% density; rel-L2 err vs dense",
+        "value": round(dense_flops / (ms_call * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s (dense-equivalent attention, whole call)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_call, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded positional-Fourier Q/K + noise + sinks, Gaussian V)",
+        "config": {"workload": (f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} grid={'x'.join(map(str, cfg.grid))} "
+                                f"d={cfg.d} {cfg.dtype} n_text={cfg.n_text}"),
+                   "Ck": cfg.Ck, "Cq": cfg.Cq, "M": cfg.M, "rho_target": cfg.rho, "max_iters": cfg.max_iters,
+                   "parallelism": "single GPU, heads batched"},
+        "ms_per_call": round(ms_call, 4),
+        "stages_ms": {n: round(float(np.median(per[:, i])), 4) for i, n in enumerate(names)},
+        "rho_exec": round(rho_exec, 5),
+        "executed_pair_mfma_frac": round(exec_flops / ((t_attn + t_probe) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
+        "roofline": {"kernel": "attn_mfma_kernel<128, sparse> (sparsepr_attn_sparse)", "bound": "mfma",
+                     "achieved": round(sparse_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "work": "4*d flops per routed query-key pair, pairs summed over heads"},
+    }
+    status = op.head_status.cpu().numpy()
+    result["head_status_bits"] = int(np.bitwise_or.reduce(status))
+
+    if not args.no_dense:
+        dense_out = torch.empty((cfg.B, cfg.H, N, d), dtype=torch.float32, device="cuda")
+        desc = spr.make_desc(tq)
+        for _ in range(2):
+            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(2, args.steps // 2)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_dense = e0.elapsed_time(e1) / reps
+        result["dense_fa_ms"] = round(t_dense, 4)
+        result["dense_fa_tflops"] = round(dense_flops / (t_dense * 1e-3) / 1e12, 2)
+        result["speedup_vs_dense_fa"] = round(t_dense / ms_call, 3)
+        # method error of the corrected output against dense attention, unprobed video rows
+        op.run(tq, tk, tv)
+        torch.cuda.synchronize()
+        o = op.out.float().reshape(BH, N, d)
+        dref = dense_out.reshape(BH, N, d)
+        err = (o - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8)
+        mask = torch.ones_like(err, dtype=torch.bool)
+        mask.scatter_(1, op.route.probe_idx.long(), False)
+        mask[:, cfg.Nv:] = False
+        e = err[mask]
+        osp = torch.empty_like(o)
+        osp.scatter_(1, op.part.q_perm.long()[..., None].expand(-1, -1, d), op.o_sp[:, : cfg.Nv])
+        esp = ((osp - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8))[mask]
+        ph = (err * mask).sum(1) / mask.sum(1)
+        phs = (((osp - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8)) * mask).sum(1) / mask.sum(1)
+        result["err_vs_dense_per_head"] = {
+            "corrected_mean_min_med_max": [round(x, 4) for x in torch.quantile(ph, torch.tensor(
+                [0.0, 0.5, 1.0], device=ph.device, dtype=ph.dtype)).tolist()],
+            "sparse_only_mean_min_med_max": [round(x, 4) for x in torch.quantile(phs, torch.tensor(
+                [0.0, 0.5, 1.0], device=phs.device, dtype=phs.dtype)).tolist()],
+            "heads_worsened_by_correction": int((ph > phs).sum().item())}
+        result["err_vs_dense"] = {"corrected_mean": round(e.mean().item(), 5),
+                                  "corrected_p99": round(torch.quantile(e.float()[:1 << 24], 0.99).item(), 5),
+                                  "sparse_only_mean": round(esp.mean().item(), 5),
+                                  "sparse_only_p99": round(torch.quantile(esp.float()[:1 << 24], 0.99).item(), 5),
+                                  "rows": "all unprobed video rows, dense reference = sparsepr_attn_dense"}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, opc)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

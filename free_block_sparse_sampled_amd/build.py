@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsparsepr.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "partition.hip", "route.hip", "attention.hip", "fit.hip"]
+SOURCES = ["api.hip", "partition.hip", "kmeans.hip", "route.hip", "attention.hip", "fit.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

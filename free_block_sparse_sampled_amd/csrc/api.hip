@@ -28,13 +28,8 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.phiK = take(BH * Nv * p.rK * 8);
   L.phiQ = take(BH * Nv * p.rQ * 8);
   L.km_cent = take(BH * L.Cmax * L.rmax * 8);
-  L.km_cent32 = take(BH * L.Cmax * L.rmax * 4);
-  L.km_sums = take(BH * L.Cmax * L.rmax * 8);
-  L.km_cnt = take(BH * L.Cmax * 4);
   L.km_lab = take(BH * Nv * 4);
-  L.km_jpart = take(BH * L.nblk * 8);
-  L.km_cpart = take(BH * L.nblk * 4);
-  L.km_ctrl = take(BH * 4 * 8);
+  L.km_region = take(kmeans_ws_bytes(int(BH), int(Nv), L.Cmax, L.rmax));
   L.cbar = take(BH * p.Cq * p.rQ * 8);
   L.vstat = take(BH * Nv * 2 * 8);
   L.gstat = take(BH * 8 * 4);
@@ -214,16 +209,7 @@ spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* 
 
 size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C) {
   if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || r < 1 || r > 64) return 0;
-  const int nblk = (n + kAssignThreads - 1) / kAssignThreads;
-  size_t o = 0;
-  auto take = [&](size_t bytes) { o = align_up(o + bytes); };
-  take(size_t(BH) * C * r * 4);  // cent32
-  take(size_t(BH) * C * r * 8);  // sums
-  take(size_t(BH) * C * 4);      // counts
-  take(size_t(BH) * nblk * 8);   // jpart
-  take(size_t(BH) * nblk * 4);   // cpart
-  take(size_t(BH) * 4 * 8);      // ctrl
-  return o;
+  return kmeans_ws_bytes(BH, n, C, r);
 }
 
 spr_status sparsepr_kmeans(int32_t BH, int32_t n, int32_t r, int32_t C, const double* feat, uint64_t seed,
@@ -232,30 +218,15 @@ spr_status sparsepr_kmeans(int32_t BH, int32_t n, int32_t r, int32_t C, const do
   if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || max_iters < 1 || !(tol >= 0.0)) return SPR_EINVAL;
   if (stage != 0 && stage != 1) return SPR_EINVAL;
   if (!kmeans_rank_supported(r)) return SPR_EUNSUPPORTED;
-  if (!feat || !labels || !centres || !passes || !ws || !aligned16(ws)) return SPR_EINVAL;
-  const size_t need = sparsepr_kmeans_workspace_size(BH, n, r, C);
-  if (ws_bytes < need) return SPR_EWORKSPACE;
-  const int nblk = (n + kAssignThreads - 1) / kAssignThreads;
-  char* w = static_cast<char*>(ws);
-  size_t o = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = o;
-    o = align_up(o + bytes);
-    return w + at;
-  };
-  KmArgs a;
-  a.BH = BH; a.n = n; a.r = r; a.C = C; a.stage = stage; a.max_iters = max_iters; a.nblk = nblk; a.tol = tol;
+  if (!feat || !labels || !centres || !passes || !ws || !aligned16(ws) || !aligned16(feat)) return SPR_EINVAL;
+  if (ws_bytes < kmeans_ws_bytes(BH, n, C, r)) return SPR_EWORKSPACE;
+  KmArgs a = kmeans_carve(ws, BH, n, C, r);
+  a.BH = BH; a.n = n; a.r = r; a.C = C; a.stage = stage; a.max_iters = max_iters; a.tol = tol;
   a.seed = seed; a.feat = feat; a.cent = centres; a.labels = labels;
-  a.cent32 = reinterpret_cast<float*>(take(size_t(BH) * C * r * 4));
-  a.sums = reinterpret_cast<double*>(take(size_t(BH) * C * r * 8));
-  a.cnt = reinterpret_cast<int*>(take(size_t(BH) * C * 4));
-  a.jpart = reinterpret_cast<double*>(take(size_t(BH) * nblk * 8));
-  a.cpart = reinterpret_cast<int*>(take(size_t(BH) * nblk * 4));
-  a.ctrl = reinterpret_cast<double*>(take(size_t(BH) * 4 * 8));
   hipStream_t st = static_cast<hipStream_t>(stream);
   spr_status s = run_kmeans(a, st);
   if (s != SPR_OK) return s;
-  launch_copy_passes1(a.ctrl, BH, passes, st);
+  launch_copy_passes(a.ctrl, BH, passes, 1, 0, st);
   SPR_CHECK_LAUNCH();
   return SPR_OK;
 }

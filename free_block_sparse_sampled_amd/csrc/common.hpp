@@ -144,13 +144,8 @@ struct Workspace {
   size_t phiK;       // double [BH][Nv][rK]      (unless the caller keeps them)
   size_t phiQ;       // double [BH][Nv][rQ]
   size_t km_cent;    // double [BH][Cmax][rmax]  k-means centres
-  size_t km_cent32;  // float  [BH][Cmax][rmax]  fp32 copy for the screening pass
-  size_t km_sums;    // double [BH][Cmax][rmax]
-  size_t km_cnt;     // int    [BH][Cmax]
   size_t km_lab;     // int    [BH][Nv]          uncompacted labels
-  size_t km_jpart;   // double [BH][nblk]
-  size_t km_cpart;   // int    [BH][nblk]
-  size_t km_ctrl;    // double [BH][4]           done, passes, J_prev
+  size_t km_region;  // k-means scratch (see kmeans_carve)
   size_t cbar;       // double [BH][Cq][rQ]      mean query coordinates c_a
   size_t vstat;      // double [BH][Nv][2]       v_j . vbar_b(j), |v_j|^2 in Kp order
   size_t gstat;      // int    [BH][8]           flags / counters per head

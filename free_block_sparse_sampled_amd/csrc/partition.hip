@@ -235,215 +235,6 @@ __global__ __launch_bounds__(256) void project_kernel(const void* __restrict__ x
   }
 }
 
-// ------------------------------------------------------------------ k-means
-// State per head in ctrl[4]: done flag, passes run, cost of the previous pass, and the
-// largest centre norm (for the screening error bound).
-__global__ __launch_bounds__(256) void km_init_kernel(const double* __restrict__ feat, int n, int r, int C,
-                                                      uint64_t seed, int stage, double* __restrict__ cent,
-                                                      float* __restrict__ cent32, double* __restrict__ sums,
-                                                      int* __restrict__ cnt, double* __restrict__ ctrl) {
-  __shared__ double red[32];
-  const int hd = blockIdx.x;
-  double cmax = 0.0;
-  for (int m = threadIdx.x; m < C; m += blockDim.x) {
-    // counter layout: ((head * 2 + stage) << 20) + m   (App. C.1: uniform with replacement)
-    const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
-    const int j = int(splitmix64(seed, ctr) % uint64_t(n));
-    const double* f = feat + (size_t(hd) * n + j) * r;
-    double* c = cent + (size_t(hd) * C + m) * r;
-    float* c32 = cent32 + (size_t(hd) * C + m) * r;
-    double s = 0.0;
-    for (int e = 0; e < r; ++e) {
-      c[e] = f[e];
-      c32[e] = float(f[e]);
-      s = fma(f[e], f[e], s);
-      sums[(size_t(hd) * C + m) * r + e] = 0.0;
-    }
-    cnt[size_t(hd) * C + m] = 0;
-    cmax = fmax(cmax, sqrt(s));
-  }
-  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int w = 0; w < int(blockDim.x >> 6); ++w) t = fmax(t, red[w]);
-    ctrl[hd * 4 + 0] = 0.0;
-    ctrl[hd * 4 + 1] = 0.0;
-    ctrl[hd * 4 + 2] = 0.0;
-    ctrl[hd * 4 + 3] = t;
-  }
-}
-
-// One assignment pass.  Each lane owns one point: an fp32 screening pass over all centres
-// keeps the best and second-best distance; when their gap is inside a bound on the fp32
-// error (rounding of the coordinates to fp32 plus the arithmetic), the point is re-scored
-// over all centres in fp64 so that the decision is the exact fp64 nearest centre (ties to
-// the lowest index).  The pass also accumulates the Lloyd sums of the update: each wave
-// walks its 64 points in order with one lane per coordinate and flushes a running sum
-// with fp64 atomics whenever the label changes.
-template <int R>
-__global__ __launch_bounds__(kAssignThreads) void km_assign_kernel(
-    const double* __restrict__ feat, int n, int C, const double* __restrict__ cent,
-    const float* __restrict__ cent32, int* __restrict__ labels, double* __restrict__ jpart,
-    int* __restrict__ cpart, const double* __restrict__ ctrl, double* __restrict__ sums,
-    int* __restrict__ cnt, int nblk) {
-  __shared__ double red[32];
-  __shared__ int64_t redi[32];
-  const int hd = blockIdx.y;
-  if (ctrl[hd * 4 + 0] != 0.0) return;
-  const int j = blockIdx.x * kAssignThreads + threadIdx.x;
-  const bool valid = j < n;
-  const double* f = feat + (size_t(hd) * n + (valid ? j : 0)) * R;
-  float x[R];
-  double xn2 = 0.0;
-#pragma unroll
-  for (int e = 0; e < R; ++e) {
-    x[e] = float(f[e]);
-    xn2 = fma(f[e], f[e], xn2);
-  }
-  const float* c32 = cent32 + size_t(hd) * C * R;
-  float best = 3.0e38f, second = 3.0e38f;
-  int bi = 0;
-  for (int m = 0; m < C; ++m) {
-    const float* cm = c32 + size_t(m) * R;
-    float dd = 0.f;
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const float t = x[e] - cm[e];
-      dd = fmaf(t, t, dd);
-    }
-    if (dd < best) {
-      second = best;
-      best = dd;
-      bi = m;
-    } else if (dd < second) {
-      second = dd;
-    }
-  }
-  const double* c64 = cent + size_t(hd) * C * R;
-  // error bound of the screened distances (not squared): coordinate rounding contributes
-  // eps32 * (|x| + max |c|), the subtraction/accumulation (R/2 + 2) eps32 * D; factor 4 margin
-  const double eps32 = 5.960464477539063e-8;
-  const double cmax = ctrl[hd * 4 + 3];
-  const double d1 = sqrt(double(best)), d2 = sqrt(double(second));
-  const double bound = 4.0 * (2.0 * eps32 * (sqrt(xn2) + cmax) + (0.5 * R + 2.0) * eps32 * (d1 + d2));
-  int lab = bi;
-  if (valid && C > 1 && !(d2 - d1 > bound)) {
-    double bd = 1.0e308;
-    for (int m = 0; m < C; ++m) {
-      const double* cm = c64 + size_t(m) * R;
-      double dd = 0.0;
-      for (int e = 0; e < R; ++e) {
-        const double t = f[e] - cm[e];
-        dd = fma(t, t, dd);
-      }
-      if (dd < bd) {
-        bd = dd;
-        lab = m;
-      }
-    }
-  }
-  double dist = 0.0;
-  int changed = 0;
-  if (valid) {
-    const double* cm = c64 + size_t(lab) * R;
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const double t = f[e] - cm[e];
-      dist = fma(t, t, dist);
-    }
-    int* lp = labels + size_t(hd) * n + j;
-    changed = (*lp != lab);
-    *lp = lab;
-  }
-  // Lloyd sums for the update step
-  const int lane = threadIdx.x & 63;
-  const int wbase = blockIdx.x * kAssignThreads + (threadIdx.x & ~63);
-  const int L = valid ? lab : -1;
-  int cur = __shfl(L, 0);
-  double acc = 0.0;
-  int run = 0;
-  for (int p = 0; p < 64; ++p) {
-    const int Lp = __shfl(L, p);
-    if (Lp < 0) break;
-    if (Lp != cur) {
-      if (lane < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + lane, acc);
-      if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
-      acc = 0.0;
-      run = 0;
-      cur = Lp;
-    }
-    if (lane < R) acc += feat[(size_t(hd) * n + wbase + p) * R + lane];
-    ++run;
-  }
-  if (run > 0) {
-    if (lane < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + lane, acc);
-    if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
-  }
-  const double jsum = block_sum_d(dist, red);
-  const int64_t csum = block_sum_i64(changed, redi);
-  if (threadIdx.x == 0) {
-    jpart[size_t(hd) * nblk + blockIdx.x] = jsum;
-    cpart[size_t(hd) * nblk + blockIdx.x] = int(csum);
-  }
-}
-
-// Stopping rule and centre update after a pass: stop when the labels did not change, when
-// the cost fell by at most tol relative to the previous pass, or at max_iters; otherwise
-// move every nonempty centre to its members' mean (empty centres stay).
-__global__ __launch_bounds__(256) void km_finalize_kernel(int C, int r, int max_iters, double tol, int nblk,
-                                                          const double* __restrict__ jpart,
-                                                          const int* __restrict__ cpart, double* __restrict__ cent,
-                                                          float* __restrict__ cent32, double* __restrict__ sums,
-                                                          int* __restrict__ cnt, double* __restrict__ ctrl) {
-  __shared__ double red[32];
-  __shared__ int64_t redi[32];
-  const int hd = blockIdx.x;
-  if (ctrl[hd * 4 + 0] != 0.0) return;
-  double js = 0.0;
-  int64_t cs = 0;
-  for (int i = threadIdx.x; i < nblk; i += blockDim.x) {
-    js += jpart[size_t(hd) * nblk + i];
-    cs += cpart[size_t(hd) * nblk + i];
-  }
-  const double J = block_sum_d(js, red);
-  const int64_t chg = block_sum_i64(cs, redi);
-  const int passes = int(ctrl[hd * 4 + 1]) + 1;
-  const double Jprev = ctrl[hd * 4 + 2];
-  const bool stop = (passes > 1 && (chg == 0 || Jprev - J <= tol * Jprev)) || passes >= max_iters;
-  double cmax = 0.0;
-  for (int m = threadIdx.x; m < C; m += blockDim.x) {
-    const int k = cnt[size_t(hd) * C + m];
-    double* c = cent + (size_t(hd) * C + m) * r;
-    float* c32 = cent32 + (size_t(hd) * C + m) * r;
-    double* s = sums + (size_t(hd) * C + m) * r;
-    double n2 = 0.0;
-    for (int e = 0; e < r; ++e) {
-      if (!stop && k > 0) {
-        c[e] = s[e] / double(k);
-        c32[e] = float(c[e]);
-      }
-      n2 = fma(c[e], c[e], n2);
-      s[e] = 0.0;
-    }
-    cnt[size_t(hd) * C + m] = 0;
-    cmax = fmax(cmax, sqrt(n2));
-  }
-  for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = cmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int w = 0; w < int(blockDim.x >> 6); ++w) t = fmax(t, red[w]);
-    ctrl[hd * 4 + 0] = stop ? 1.0 : 0.0;
-    ctrl[hd * 4 + 1] = double(passes);
-    ctrl[hd * 4 + 2] = J;
-    ctrl[hd * 4 + 3] = t;
-  }
-}
-
 // ------------------------------------------------------------------ compaction
 // One block of 1024 threads per head: drop empty clusters (renumber the rest in ascending
 // id), group offsets, and a stable counting-sort scatter that lists each group's members in
@@ -599,36 +390,6 @@ __global__ __launch_bounds__(256) void qdist_kernel(const double* __restrict__ f
 }
 
 // ------------------------------------------------------------------ host drivers
-template <int R>
-static void launch_assign(const KmArgs& a, hipStream_t st) {
-  dim3 grid(a.nblk, a.BH);
-  hipLaunchKernelGGL(km_assign_kernel<R>, grid, dim3(kAssignThreads), 0, st, a.feat, a.n, a.C, a.cent, a.cent32,
-                     a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
-}
-
-spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(km_init_kernel, dim3(a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.cent,
-                     a.cent32, a.sums, a.cnt, a.ctrl);
-  SPR_CHECK_LAUNCH();
-  for (int it = 0; it < a.max_iters; ++it) {
-    switch (a.r) {
-      case 48: launch_assign<48>(a, st); break;
-      case 64: launch_assign<64>(a, st); break;
-      case 32: launch_assign<32>(a, st); break;
-      case 16: launch_assign<16>(a, st); break;
-      case 8: launch_assign<8>(a, st); break;
-      default: return SPR_EUNSUPPORTED;
-    }
-    SPR_CHECK_LAUNCH();
-    hipLaunchKernelGGL(km_finalize_kernel, dim3(a.BH), dim3(256), 0, st, a.C, a.r, a.max_iters, a.tol, a.nblk,
-                       a.jpart, a.cpart, a.cent, a.cent32, a.sums, a.cnt, a.ctrl);
-    SPR_CHECK_LAUNCH();
-  }
-  return SPR_OK;
-}
-
-bool kmeans_rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 48 || r == 64; }
-
 size_t compact_smem(int C) { return size_t(3 * C + 1024 + 16 * C) * sizeof(int); }
 
 spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, int* perm, int* pos_of, int* off,
@@ -638,26 +399,6 @@ spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, 
                      pos_of, off, ngroups, gstat, empty_bit);
   SPR_CHECK_LAUNCH();
   return SPR_OK;
-}
-
-static void copy_passes(const double* ctrl, int BH, int* passes, int slot, hipStream_t st);
-
-__global__ void copy_passes_kernel(const double* ctrl, int BH, int* passes, int slot) {
-  const int hd = blockIdx.x * blockDim.x + threadIdx.x;
-  if (hd < BH) passes[hd * 2 + slot] = int(ctrl[hd * 4 + 1]);
-}
-
-static void copy_passes(const double* ctrl, int BH, int* passes, int slot, hipStream_t st) {
-  hipLaunchKernelGGL(copy_passes_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, ctrl, BH, passes, slot);
-}
-
-__global__ void copy_passes1_kernel(const double* ctrl, int BH, int* passes) {
-  const int hd = blockIdx.x * blockDim.x + threadIdx.x;
-  if (hd < BH) passes[hd] = int(ctrl[hd * 4 + 1]);
-}
-
-void launch_copy_passes1(const double* ctrl, int BH, int* passes, hipStream_t st) {
-  hipLaunchKernelGGL(copy_passes1_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, ctrl, BH, passes);
 }
 
 __global__ void copy_doubles_kernel(const double* src, double* dst, size_t n) {
@@ -702,15 +443,13 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
                      out.FK, p.rK, p.rms_eps, phiK, gstat);
   SPR_CHECK_LAUNCH();
   // K/V k-means
-  KmArgs ka;
+  KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
   ka.BH = BH; ka.n = Nv; ka.r = p.rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
-  ka.max_iters = p.max_iters; ka.tol = p.tol; ka.nblk = L.nblk;
-  ka.cent = wsp<double>(ws, L.km_cent); ka.cent32 = wsp<float>(ws, L.km_cent32); ka.sums = wsp<double>(ws, L.km_sums);
-  ka.cnt = wsp<int>(ws, L.km_cnt); ka.labels = wsp<int>(ws, L.km_lab); ka.jpart = wsp<double>(ws, L.km_jpart);
-  ka.cpart = wsp<int>(ws, L.km_cpart); ka.ctrl = wsp<double>(ws, L.km_ctrl);
+  ka.max_iters = p.max_iters; ka.tol = p.tol;
+  ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
   spr_status s = run_kmeans(ka, st);
   if (s != SPR_OK) return s;
-  if (out.passes) copy_passes(ka.ctrl, BH, out.passes, 0, st);
+  if (out.passes) launch_copy_passes(ka.ctrl, BH, out.passes, 2, 0, st);
   if (out.cK_last) {
     // centres are stored with stride rK, exactly the caller's layout
     const size_t nel = size_t(BH) * p.Ck * p.rK;
@@ -747,7 +486,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1;
   s = run_kmeans(qa, st);
   if (s != SPR_OK) return s;
-  if (out.passes) copy_passes(qa.ctrl, BH, out.passes, 1, st);
+  if (out.passes) launch_copy_passes(qa.ctrl, BH, out.passes, 2, 1, st);
   if (out.cQ_last) {
     const size_t nel = size_t(BH) * p.Cq * p.rQ;
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, qa.cent,

@@ -8,19 +8,32 @@ struct KmArgs {
   int BH, n, r, C, stage, max_iters, nblk;
   double tol;
   uint64_t seed;
-  const double* feat;
-  double* cent;
-  float* cent32;
+  const double* feat;  // [BH][n][r] coordinates
+  double* cent;        // [BH][C][r] centres
+  int* labels;         // [BH][n] labels after the last pass
+  // scratch carved by kmeans_carve()
   double* sums;
   int* cnt;
-  int* labels;
+  int* lab_new;
   double* jpart;
   int* cpart;
   double* ctrl;
+  double* mu;
+  void* xh;
+  void* xl;
+  float* xnrm;
+  void* ch;
+  void* cl;
+  float* cn2;
+  int* rq_count;
+  int* rq_list;
 };
 
+size_t kmeans_ws_bytes(int BH, int n, int C, int rmax);
+KmArgs kmeans_carve(void* ws, int BH, int n, int C, int rmax);
+void launch_copy_passes(const double* ctrl, int BH, int* passes, int stride, int slot, hipStream_t st);
+
 spr_status run_kmeans(const KmArgs& a, hipStream_t st);
-void launch_copy_passes1(const double* ctrl, int BH, int* passes, hipStream_t st);
 bool kmeans_rank_supported(int r);
 size_t compact_smem(int C);
 size_t jacobi_smem(int d);
