@@ -31,18 +31,27 @@ constexpr int KC = 256;       // centres per LDS chunk
 constexpr int CROW = RP + 8;  // LDS row stride in fp16 elements (keeps 16-row reads conflict free)
 constexpr int CTRL = 8;       // doubles of control word per head
 
-enum { C_DONE = 0, C_PASSES = 1, C_JPREV = 2, C_CMAX = 3, C_SCALE = 4 };
+enum { C_DONE = 0, C_PASSES = 1, C_JPREV = 2, C_CMAX = 3, C_SCALE = 4, C_AMAX = 5 };
 
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 
-// Mean point mu and the power-of-two scale s with 2 max|x| s <= 2^14 (one block per head).
+// Mean point mu and the power-of-two scale s with 2 max|x| s <= 2^14.  Row slices of the
+// points are reduced by 64 blocks per head into fp64 sums (atomics) and a max (atomicMax on the
+// bit pattern, monotone for non-negative doubles); km_stats_final_kernel divides and scales.
+__global__ void km_stats_zero_kernel(double* __restrict__ mu, double* __restrict__ ctrl, int BH) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < BH * RP) mu[i] = 0.0;
+  if (i < BH) ctrl[i * CTRL + C_AMAX] = 0.0;
+}
+
 __global__ __launch_bounds__(256) void km_point_stats_kernel(const double* __restrict__ feat, int n, int r,
                                                              double* __restrict__ mu, double* __restrict__ ctrl) {
   __shared__ double ssum[256], smax[256];
-  const int hd = blockIdx.x, t = threadIdx.x, e = t & 63, r0 = t >> 6;
+  const int hd = blockIdx.y, t = threadIdx.x, e = t & 63, r0 = t >> 6;
+  const int j0 = int(int64_t(n) * blockIdx.x / gridDim.x), j1 = int(int64_t(n) * (blockIdx.x + 1) / gridDim.x);
   double s = 0.0, m = 0.0;
   if (e < r)
-    for (int j = r0; j < n; j += 4) {
+    for (int j = j0 + r0; j < j1; j += 4) {
       const double x = feat[(size_t(hd) * n + j) * r + e];
       s += x;
       m = fmax(m, fabs(x));
@@ -52,13 +61,20 @@ __global__ __launch_bounds__(256) void km_point_stats_kernel(const double* __res
   __syncthreads();
   if (t < 64) {
     const double tot = ssum[t] + ssum[t + 64] + ssum[t + 128] + ssum[t + 192];
-    mu[size_t(hd) * RP + t] = t < r ? tot / double(n) : 0.0;
-    smax[t] = fmax(fmax(smax[t], smax[t + 64]), fmax(smax[t + 128], smax[t + 192]));
+    double mx = fmax(fmax(smax[t], smax[t + 64]), fmax(smax[t + 128], smax[t + 192]));
+    if (t < r) atomicAdd(mu + size_t(hd) * RP + t, tot);
+    for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    if (t == 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(ctrl + hd * CTRL + C_AMAX),
+                (unsigned long long)__double_as_longlong(mx));
   }
-  __syncthreads();
-  if (t == 0) {
-    double amax = 0.0;
-    for (int i = 0; i < 64; ++i) amax = fmax(amax, smax[i]);
+}
+
+__global__ void km_stats_final_kernel(double* __restrict__ mu, double* __restrict__ ctrl, int n) {
+  const int hd = blockIdx.x, e = threadIdx.x;
+  mu[size_t(hd) * RP + e] /= double(n);
+  if (e == 0) {
+    const double amax = ctrl[hd * CTRL + C_AMAX];
     double sc = 1.0;
     if (amax > 0.0) sc = ldexp(1.0, int(floor(log2(8192.0 / amax))));  // 2 amax sc <= 2^14
     ctrl[hd * CTRL + C_SCALE] = sc;
@@ -100,25 +116,25 @@ __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __rest
 }
 
 // fp16 split of the centres (same centring and scale as the points), their squared norms and
-// the largest norm.  Called by a whole block of one head.
+// the largest norm.  Element-parallel over the whole block of one head; n2s is LDS [C].
 __device__ void prep_centres(int hd, int C, int r, const double* __restrict__ cent, const double* __restrict__ mu,
                              double sc, _Float16* __restrict__ ch, _Float16* __restrict__ cl,
-                             float* __restrict__ cn2, double* __restrict__ ctrl, double* red) {
+                             float* __restrict__ cn2, double* __restrict__ ctrl, double* n2s, double* red) {
+  for (int m = threadIdx.x; m < C; m += blockDim.x) n2s[m] = 0.0;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < C * RP; idx += blockDim.x) {
+    const int m = idx / RP, e = idx % RP;
+    const double x = e < r ? (cent[(size_t(hd) * C + m) * r + e] - mu[size_t(hd) * RP + e]) * sc : 0.0;
+    const _Float16 h = _Float16(float(x));
+    ch[(size_t(hd) * C + m) * RP + e] = h;
+    cl[(size_t(hd) * C + m) * RP + e] = _Float16(float(x - double(h)));
+    if (x != 0.0) atomicAdd(&n2s[m], x * x);
+  }
+  __syncthreads();
   double cmax = 0.0;
   for (int m = threadIdx.x; m < C; m += blockDim.x) {
-    const double* c = cent + (size_t(hd) * C + m) * r;
-    _Float16* hp = ch + (size_t(hd) * C + m) * RP;
-    _Float16* lp = cl + (size_t(hd) * C + m) * RP;
-    double n2 = 0.0;
-    for (int e = 0; e < RP; ++e) {
-      const double x = e < r ? (c[e] - mu[size_t(hd) * RP + e]) * sc : 0.0;
-      const _Float16 h = _Float16(float(x));
-      hp[e] = h;
-      lp[e] = _Float16(float(x - double(h)));
-      n2 = fma(x, x, n2);
-    }
-    cn2[size_t(hd) * C + m] = float(n2);
-    cmax = fmax(cmax, sqrt(n2));
+    cn2[size_t(hd) * C + m] = float(n2s[m]);
+    cmax = fmax(cmax, sqrt(n2s[m]));
   }
   for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o));
   __syncthreads();
@@ -133,27 +149,25 @@ __device__ void prep_centres(int hd, int C, int r, const double* __restrict__ ce
 
 // Initial centres: C feature rows drawn uniformly with replacement by SplitMix64,
 // counter ((head * 2 + stage) << 20) + m (App. C.1).
-__global__ __launch_bounds__(256) void km_init_kernel(const double* __restrict__ feat, int n, int r, int C,
+__global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict__ feat, int n, int r, int C,
                                                       uint64_t seed, int stage, const double* __restrict__ mu,
                                                       double* __restrict__ cent, double* __restrict__ sums,
                                                       int* __restrict__ cnt, double* __restrict__ ctrl,
                                                       _Float16* __restrict__ ch, _Float16* __restrict__ cl,
                                                       float* __restrict__ cn2, int* __restrict__ rq_count) {
   __shared__ double red[32];
+  __shared__ double n2s[1024];
   const int hd = blockIdx.x;
-  for (int m = threadIdx.x; m < C; m += blockDim.x) {
+  for (int idx = threadIdx.x; idx < C * r; idx += blockDim.x) {
+    const int m = idx / r, e = idx % r;
     const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
     const int j = int(splitmix64(seed, ctr) % uint64_t(n));
-    const double* f = feat + (size_t(hd) * n + j) * r;
-    double* c = cent + (size_t(hd) * C + m) * r;
-    for (int e = 0; e < r; ++e) {
-      c[e] = f[e];
-      sums[(size_t(hd) * C + m) * r + e] = 0.0;
-    }
-    cnt[size_t(hd) * C + m] = 0;
+    cent[(size_t(hd) * C + m) * r + e] = feat[(size_t(hd) * n + j) * r + e];
+    sums[(size_t(hd) * C + m) * r + e] = 0.0;
   }
+  for (int m = threadIdx.x; m < C; m += blockDim.x) cnt[size_t(hd) * C + m] = 0;
   __syncthreads();
-  prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, red);
+  prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, n2s, red);
   if (threadIdx.x == 0) {
     ctrl[hd * CTRL + C_DONE] = 0.0;
     ctrl[hd * CTRL + C_PASSES] = 0.0;
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
 }
 
 // Stopping rule, centre update and the fp16 split of the updated centres.
-__global__ __launch_bounds__(256) void km_finalize_kernel(int C, int r, int max_iters, double tol, int nblk,
+__global__ __launch_bounds__(1024) void km_finalize_kernel(int C, int r, int max_iters, double tol, int nblk,
                                                           const double* __restrict__ jpart,
                                                           const int* __restrict__ cpart, double* __restrict__ cent,
                                                           double* __restrict__ sums, int* __restrict__ cnt,
@@ -421,18 +435,16 @@ __global__ __launch_bounds__(256) void km_finalize_kernel(int C, int r, int max_
   const int passes = int(ctrl[hd * CTRL + C_PASSES]) + 1;
   const double Jprev = ctrl[hd * CTRL + C_JPREV];
   const bool stop = (passes > 1 && (chg == 0 || Jprev - J <= tol * Jprev)) || passes >= max_iters;
-  for (int m = threadIdx.x; m < C; m += blockDim.x) {
+  __shared__ double n2s[1024];
+  for (int idx = threadIdx.x; idx < C * r; idx += blockDim.x) {
+    const int m = idx / r;
     const int k = cnt[size_t(hd) * C + m];
-    double* c = cent + (size_t(hd) * C + m) * r;
-    double* s = sums + (size_t(hd) * C + m) * r;
-    for (int e = 0; e < r; ++e) {
-      if (!stop && k > 0) c[e] = s[e] / double(k);
-      s[e] = 0.0;
-    }
-    cnt[size_t(hd) * C + m] = 0;
+    if (!stop && k > 0) cent[size_t(hd) * C * r + idx] = sums[size_t(hd) * C * r + idx] / double(k);
+    sums[size_t(hd) * C * r + idx] = 0.0;
   }
   __syncthreads();
-  if (!stop) prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, red);
+  for (int m = threadIdx.x; m < C; m += blockDim.x) cnt[size_t(hd) * C + m] = 0;
+  if (!stop) prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, n2s, red);
   if (threadIdx.x == 0) {
     ctrl[hd * CTRL + C_DONE] = stop ? 1.0 : 0.0;
     ctrl[hd * CTRL + C_PASSES] = double(passes);
@@ -518,15 +530,17 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
                      a.rq_count, a.rq_list, a.lab_new);
   hipLaunchKernelGGL(km_accum_kernel<R>, dim3(a.nblk, a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent, a.lab_new,
                      a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
-  hipLaunchKernelGGL(km_finalize_kernel, dim3(a.BH), dim3(256), 0, st, a.C, a.r, a.max_iters, a.tol, a.nblk, a.jpart,
+  hipLaunchKernelGGL(km_finalize_kernel, dim3(a.BH), dim3(1024), 0, st, a.C, a.r, a.max_iters, a.tol, a.nblk, a.jpart,
                      a.cpart, a.cent, a.sums, a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
 }
 
 spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(km_point_stats_kernel, dim3(a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.mu, a.ctrl);
+  hipLaunchKernelGGL(km_stats_zero_kernel, dim3(ceil_div(a.BH * RP, 256)), dim3(256), 0, st, a.mu, a.ctrl, a.BH);
+  hipLaunchKernelGGL(km_point_stats_kernel, dim3(64, a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.mu, a.ctrl);
+  hipLaunchKernelGGL(km_stats_final_kernel, dim3(a.BH), dim3(RP), 0, st, a.mu, a.ctrl, a.n);
   hipLaunchKernelGGL(km_point_prep_kernel, dim3(ceil_div(a.n * 8, 256), a.BH), dim3(256), 0, st, a.feat, a.n, a.r,
                      a.mu, a.ctrl, reinterpret_cast<_Float16*>(a.xh), reinterpret_cast<_Float16*>(a.xl), a.xnrm);
-  hipLaunchKernelGGL(km_init_kernel, dim3(a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
+  hipLaunchKernelGGL(km_init_kernel, dim3(a.BH), dim3(1024), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
                      a.cent, a.sums, a.cnt, a.ctrl, reinterpret_cast<_Float16*>(a.ch),
                      reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count);
   SPR_CHECK_LAUNCH();

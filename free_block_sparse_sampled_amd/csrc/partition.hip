@@ -93,19 +93,20 @@ __global__ __launch_bounds__(256) void query_metric_kernel(const double* __restr
 // consecutive lanes share one pair.  X lives in LDS in fp64 (128 KB at d = 128).
 __global__ __launch_bounds__(256) void jacobi_factor_kernel(const double* __restrict__ Mall, int d, int r,
                                                             double clamp, double* __restrict__ Fall) {
-  extern __shared__ double X[];  // column-major d x d
+  extern __shared__ double X[];  // column-major d x d, column stride ld (padded against bank conflicts)
   __shared__ int rotated;
+  const int ld = d + 1;
   __shared__ double lam[128];
   __shared__ double red[32];
   const int hd = blockIdx.x;
   const double* Mm = Mall + size_t(hd) * d * d;
-  for (int e = threadIdx.x; e < d * d; e += blockDim.x) X[e] = Mm[e];  // symmetric
+  for (int e = threadIdx.x; e < d * d; e += blockDim.x) X[(e / d) * ld + e % d] = Mm[e];  // symmetric
   __syncthreads();
   // largest squared column norm sets the scale below which columns count as null
   double nmax2 = 0.0;
   if (threadIdx.x < d) {
     double s = 0.0;
-    for (int i = 0; i < d; ++i) s += X[threadIdx.x * d + i] * X[threadIdx.x * d + i];
+    for (int i = 0; i < d; ++i) s += X[threadIdx.x * ld + i] * X[threadIdx.x * ld + i];
     nmax2 = s;
   }
   for (int o = 32; o > 0; o >>= 1) nmax2 = fmax(nmax2, __shfl_xor(nmax2, o));
@@ -126,8 +127,8 @@ __global__ __launch_bounds__(256) void jacobi_factor_kernel(const double* __rest
       const int i = (p == 0) ? 0 : 1 + ((p - 1 + rd) % (d - 1));
       const int kk = d - 1 - p;
       const int j = 1 + ((kk - 1 + rd) % (d - 1));
-      double* xi = X + size_t(i) * d;
-      double* xj = X + size_t(j) * d;
+      double* xi = X + size_t(i) * ld;
+      double* xj = X + size_t(j) * ld;
       double a = 0.0, b = 0.0, c = 0.0;
       for (int rr = sub; rr < d; rr += G) {
         const double u = xi[rr], v = xj[rr];
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void jacobi_factor_kernel(const double* __rest
   // eigenvalues = column norms; rank by descending value (ties: lower column first)
   if (threadIdx.x < d) {
     double s = 0.0;
-    for (int i = 0; i < d; ++i) s = fma(X[threadIdx.x * d + i], X[threadIdx.x * d + i], s);
+    for (int i = 0; i < d; ++i) s = fma(X[threadIdx.x * ld + i], X[threadIdx.x * ld + i], s);
     lam[threadIdx.x] = sqrt(s);
   }
   __syncthreads();
@@ -176,63 +177,83 @@ __global__ __launch_bounds__(256) void jacobi_factor_kernel(const double* __rest
     for (int j = 0; j < d; ++j) rank += (lam[j] > li) || (lam[j] == li && j < i);
     if (rank < r && li > 0.0 && li >= clamp * lmax) {
       const double s = 1.0 / sqrt(li);
-      for (int row = 0; row < d; ++row) F[size_t(row) * r + rank] = X[size_t(i) * d + row] * s;
+      for (int row = 0; row < d; ++row) F[size_t(row) * r + rank] = X[size_t(i) * ld + row] * s;
     }
   }
 }
 
 // ------------------------------------------------------------------ projection
-// phi = X F (Sec. 4.1) for 64 rows per block; with RMS the rows are RMS-normalised as in
-// App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  Four consecutive lanes share a row.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// phi = X F (Sec. 4.1) on v_mfma_f64_16x16x4f64, 128 rows per block (8 waves x 16 rows); with
+// RMS the rows are RMS-normalised as in App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  The
+// fp64 MFMA takes A[i][k] from lane i + 16k and B[k][j] from lane j + 16k, and returns
+// D[(lane / 16) + 4 v][lane % 16] in slot v.
 template <int DT, bool RMS>
-__global__ __launch_bounds__(256) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
+__global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
                                                       const double* __restrict__ Fall, int r, double eps,
                                                       double* __restrict__ out, int* __restrict__ gstat) {
   extern __shared__ double smem[];
   const int d = g.d;
-  double* Fs = smem;                                  // [d][r]
-  float* Xs = reinterpret_cast<float*>(smem + d * r);  // [64][d + 1]
-  const int hd = blockIdx.y, row0 = blockIdx.x * 64;
+  const int NT = (r + 15) >> 4;
+  const int FS = NT * 16 + 8;  // F row stride (doubles)
+  const int XS = d + 4;        // X tile row stride (floats)
+  double* Fs = smem;                                      // [d][FS]
+  float* Xs = reinterpret_cast<float*>(smem + d * FS);  // [128][XS]
+  const int hd = blockIdx.y, row0 = blockIdx.x * 128;
   const double* F = Fall + size_t(hd) * d * r;
-  for (int e = threadIdx.x; e < d * r; e += 256) Fs[e] = F[e];
+  for (int e = threadIdx.x; e < d * FS; e += 512) {
+    const int kk = e / FS, c = e % FS;
+    Fs[e] = c < r ? F[size_t(kk) * r + c] : 0.0;
+  }
   const int64_t base = g.base(hd);
-  for (int e = threadIdx.x; e < 64 * d; e += 256) {
+  for (int e = threadIdx.x; e < 128 * d; e += 512) {
     const int rr = e / d, cc = e % d, row = row0 + rr;
-    Xs[rr * (d + 1) + cc] = row < rows ? load_elem<DT>(x, base + int64_t(row) * g.sn + cc) : 0.f;
+    Xs[rr * XS + cc] = row < rows ? load_elem<DT>(x, base + int64_t(row) * g.sn + cc) : 0.f;
   }
   __syncthreads();
-  const int rr = threadIdx.x >> 2, l4 = threadIdx.x & 3;
-  double acc[16];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
+  f64x4_t acc[4];
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0;
-  for (int k = 0; k < d; ++k) {
-    const double xv = Xs[rr * (d + 1) + k];
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  for (int ks = 0; ks < d / 4; ++ks) {
+    const double av = Xs[(w * 16 + r16) * XS + ks * 4 + gq];
+    const double* fr = Fs + (ks * 4 + gq) * FS + r16;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int c = l4 + 4 * jj;
-      if (c < r) acc[jj] = fma(xv, Fs[k * r + c], acc[jj]);
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt < NT) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, fr[nt * 16], acc[nt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    double scale = 1.0;
+    const int row = row0 + w * 16 + gq + 4 * v;
+    if constexpr (RMS) {
+      double s2 = 0.0;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (nt < NT) s2 = fma(acc[nt][v], acc[nt][v], s2);
+      s2 += __shfl_xor(s2, 1);
+      s2 += __shfl_xor(s2, 2);
+      s2 += __shfl_xor(s2, 4);
+      s2 += __shfl_xor(s2, 8);
+      const double rms = sqrt(s2 / double(r));
+      scale = 1.0 / fmax(rms, eps);
+      if (rms < eps && row < rows && r16 == 0) atomicOr(gstat + hd * 8 + 0, SPR_HS_RMS_FLOOR);
+    }
+    if (row < rows) {
+      double* o = out + (size_t(hd) * rows + row) * r;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int c = nt * 16 + r16;
+        if (nt < NT && c < r) o[c] = acc[nt][v] * scale;
+      }
     }
   }
-  double scale = 1.0;
-  if constexpr (RMS) {
-    double s = 0.0;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) s = fma(acc[jj], acc[jj], s);
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    const double rms = sqrt(s / double(r));
-    scale = 1.0 / fmax(rms, eps);
-    if (rms < eps && row0 + rr < rows && l4 == 0) atomicOr(gstat + hd * 8 + 0, SPR_HS_RMS_FLOOR);
-  }
-  const int row = row0 + rr;
-  if (row < rows) {
-    double* o = out + (size_t(hd) * rows + row) * r;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int c = l4 + 4 * jj;
-      if (c < r) o[c] = acc[jj] * scale;
-    }
-  }
+}
+
+size_t project_smem(int d, int r) {
+  const int NT = (r + 15) >> 4;
+  return size_t(d) * (NT * 16 + 8) * sizeof(double) + size_t(128) * (d + 4) * sizeof(float);
 }
 
 // ------------------------------------------------------------------ compaction
@@ -431,15 +452,15 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   // M_K and F_K
   hipLaunchKernelGGL(key_metric_kernel<DT>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, q, g, p.Ms, metric);
   SPR_CHECK_LAUNCH();
-  const size_t jac_smem = size_t(d) * d * sizeof(double);
+  const size_t jac_smem = jacobi_smem(d);
   allow_lds(jacobi_factor_kernel, jac_smem);
   hipLaunchKernelGGL(jacobi_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK);
   SPR_CHECK_LAUNCH();
   // phi_K = K F_K
-  const size_t prj_smem = size_t(d) * 64 * sizeof(double) + size_t(64) * (d + 1) * sizeof(float);
+  const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
   allow_lds(project_kernel<DT, false>, prj_smem);
   allow_lds(project_kernel<DT, true>, prj_smem);
-  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(Nv, 64), BH), dim3(256), prj_smem, st, k, g, Nv,
+  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, k, g, Nv,
                      out.FK, p.rK, p.rms_eps, phiK, gstat);
   SPR_CHECK_LAUNCH();
   // K/V k-means
@@ -478,7 +499,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(jacobi_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ);
   SPR_CHECK_LAUNCH();
   // phi_Q = RMSNorm(Q F_Q)
-  hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(Nv, 64), BH), dim3(256), prj_smem, st, q, g, Nv,
+  hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, q, g, Nv,
                      out.FQ, p.rQ, p.rms_eps, phiQ, gstat);
   SPR_CHECK_LAUNCH();
   // query k-means
@@ -513,6 +534,6 @@ spr_status run_partition(const spr_desc& desc, const void* q, const void* k, con
   return partition_impl<SPR_F32>(desc, q, k, v, p, out, ws, L, st);
 }
 
-size_t jacobi_smem(int d) { return size_t(d) * d * sizeof(double); }
+size_t jacobi_smem(int d) { return size_t(d) * (d + 1) * sizeof(double); }
 
 }  // namespace spr

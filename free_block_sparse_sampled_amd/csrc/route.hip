@@ -56,12 +56,15 @@ __global__ __launch_bounds__(256) void route_shift_kernel(const double* __restri
   if (lane == 0) shift[size_t(hd) * Cq + a] = m;
 }
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 // Scores for a tile of 64 query groups x 16 K/V groups.  The keys of the 16 groups are
-// contiguous in group-major order and are streamed in 64-key chunks; each thread computes
-// a 4 (query group) x 4 (key) block of fp64 logits and adds E u and E^2 w to per-(a, b)
-// accumulators in LDS.
-template <int DT>
-__global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict__ Kp, int N, int Nv, int d,
+// contiguous in group-major order and stream through LDS in 64-key chunks.  Logits come from
+// v_mfma_f64_16x16x4f64 (each wave: 16 query groups, A fragments of qbar kept in registers;
+// lane l, slot v holds the logit of group (l / 16) + 4 v and key l % 16 of a 16-key tile);
+// E u and E^2 w are added to per-(a, b) accumulators in LDS.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict__ Kp, int N, int Nv,
                                                           const double* __restrict__ qbar,
                                                           const double* __restrict__ kbar,
                                                           const double* __restrict__ vbar,
@@ -71,44 +74,44 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
                                                           const double* __restrict__ shift,
                                                           const double* __restrict__ vstat,
                                                           double* __restrict__ scores) {
+  constexpr int KSD = D + 4;  // key tile row stride (floats)
   extern __shared__ double sm[];
   const int hd = blockIdx.z;
   const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 16;
   const int nq = n_q[hd], nkv = n_kv[hd];
   if (a0 >= nq || b0 >= nkv) return;
   const int b1 = min(b0 + 16, nkv);
-  double* qsT = sm;                  // [d][64]
-  double* acc = qsT + d * 64;        // [64][16][2]
-  double* kst = acc + 64 * 16 * 2;   // as float [d][65]
-  float* ksT = reinterpret_cast<float*>(kst);
+  double* acc = sm;                                       // [64][16][2]
+  float* Ks = reinterpret_cast<float*>(acc + 64 * 16 * 2);  // [64][KSD]
   __shared__ double us[64], wsv[64], shs[64];
   __shared__ int grp[64];
   const int* off = kv_off + size_t(hd) * (Ck + 1);
-  for (int e = threadIdx.x; e < 64 * d; e += 256) {
-    const int al = e / d, c = e % d, a = a0 + al;
-    qsT[c * 64 + al] = a < nq ? qbar[(size_t(hd) * Cq + a) * d + c] : 0.0;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
+  double qa[D / 4];
+  {
+    const int a = a0 + w * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < D / 4; ++ks) qa[ks] = a < nq ? qbar[(size_t(hd) * Cq + a) * D + ks * 4 + gq] : 0.0;
   }
   for (int e = threadIdx.x; e < 64 * 32; e += 256) acc[e] = 0.0;
   if (threadIdx.x < 64) {
     const int a = a0 + threadIdx.x;
     shs[threadIdx.x] = a < nq ? shift[size_t(hd) * Cq + a] : 0.0;
   }
-  const double inv = 1.0 / sqrt(double(d));
+  const double inv = 1.0 / sqrt(double(D));
   const int k0 = off[b0], k1 = off[b1];
-  const int ia = (threadIdx.x >> 4), ij = threadIdx.x & 15;  // a = ia + 16u, key = ij + 16v
   for (int kc = k0; kc < k1; kc += 64) {
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * d; e += 256) {
-      const int jl = e / d, c = e % d, pos = kc + jl;
-      ksT[c * 65 + jl] = pos < k1 ? load_elem<DT>(Kp, (size_t(hd) * N + pos) * d + c) : 0.f;
+    for (int e = threadIdx.x; e < 64 * D; e += 256) {
+      const int jl = e / D, c = e % D, pos = kc + jl;
+      Ks[jl * KSD + c] = pos < k1 ? load_elem<DT>(Kp, (size_t(hd) * N + pos) * D + c) : 0.f;
     }
     if (threadIdx.x < 64) {
       const int pos = kc + threadIdx.x;
       if (pos < k1) {
         us[threadIdx.x] = vstat[(size_t(hd) * Nv + pos) * 2 + 0];
         wsv[threadIdx.x] = vstat[(size_t(hd) * Nv + pos) * 2 + 1];
-        // group of this key: last b with off[b] <= pos
-        int lo = b0, hi = b1 - 1;
+        int lo = b0, hi = b1 - 1;  // group of this key: last b with off[b] <= pos
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
           if (off[mid] <= pos) lo = mid; else hi = mid - 1;
@@ -119,34 +122,24 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
       }
     }
     __syncthreads();
-    double lg[4][4];
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+      const int jl = kt * 16 + r16;
+      if (kc + kt * 16 >= k1) break;  // uniform
+      f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+      const float* kr = Ks + jl * KSD + gq;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) lg[u][v] = 0.0;
-    for (int c = 0; c < d; ++c) {
-      double qa[4], kk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) qa[u] = qsT[c * 64 + ia + 16 * u];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) kk[v] = ksT[c * 65 + ij + 16 * v];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) lg[u][v] = fma(qa[u], kk[v], lg[u][v]);
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int jl = ij + 16 * v;
+      for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], double(kr[ks * 4]), lg, 0, 0, 0);
       const int gb = grp[jl];
-      if (gb < 0) continue;
-      const double uu = us[jl], ww = wsv[jl];
+      if (gb >= 0) {
+        const double uu = us[jl], ww = wsv[jl];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int al = ia + 16 * u;
-        const double E = exp(lg[u][v] * inv - shs[al]);
-        atomicAdd(&acc[(al * 16 + gb) * 2 + 0], E * uu);
-        atomicAdd(&acc[(al * 16 + gb) * 2 + 1], E * E * ww);
+        for (int v = 0; v < 4; ++v) {
+          const int al = w * 16 + gq + 4 * v;
+          const double E = exp(lg[v] * inv - shs[al]);
+          atomicAdd(&acc[(al * 16 + gb) * 2 + 0], E * uu);
+          atomicAdd(&acc[(al * 16 + gb) * 2 + 1], E * E * ww);
+        }
       }
     }
   }
@@ -155,17 +148,18 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
   for (int e = threadIdx.x; e < 64 * 16; e += 256) {
     const int al = e >> 4, gb = e & 15, a = a0 + al, b = b0 + gb;
     if (a >= nq || b >= b1) continue;
-    const double* kb = kbar + (size_t(hd) * Ck + b) * d;
-    const double* vb = vbar + (size_t(hd) * Ck + b) * d;
+    const double* qb = qbar + (size_t(hd) * Cq + a) * D;
+    const double* kb = kbar + (size_t(hd) * Ck + b) * D;
+    const double* vb = vbar + (size_t(hd) * Ck + b) * D;
     double l = 0.0, vn = 0.0;
-    for (int c = 0; c < d; ++c) {
-      l = fma(qsT[c * 64 + al], kb[c], l);
+    for (int c = 0; c < D; ++c) {
+      l = fma(qb[c], kb[c], l);
       vn = fma(vb[c], vb[c], vn);
     }
     const double A = exp(l * inv - shs[al]);
     const double g = double(off[b + 1] - off[b]);
-    const double s = A * A * vn - 2.0 * A * acc[(al * 16 + gb) * 2 + 0] / g + acc[(al * 16 + gb) * 2 + 1] / g;
-    scores[(size_t(hd) * Cq + a) * Ck + b] = s;
+    const double sc = A * A * vn - 2.0 * A * acc[(al * 16 + gb) * 2 + 0] / g + acc[(al * 16 + gb) * 2 + 1] / g;
+    scores[(size_t(hd) * Cq + a) * Ck + b] = sc;
   }
 }
 
@@ -368,11 +362,14 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   hipLaunchKernelGGL(route_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.qbar, part.kbar,
                      part.n_q, part.n_kv, p.Cq, p.Ck, d, shift);
   SPR_CHECK_LAUNCH();
-  const size_t smem = size_t(d) * 64 * sizeof(double) + 64 * 16 * 2 * sizeof(double) + size_t(d) * 65 * sizeof(float);
-  allow_lds(route_score_kernel<DT>, smem);
-  hipLaunchKernelGGL(route_score_kernel<DT>, dim3(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH), dim3(256), smem, st,
-                     part.Kp, N, Nv, d, part.qbar, part.kbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck,
-                     shift, vstat, scores);
+  const size_t smem = 64 * 16 * 2 * sizeof(double) + size_t(64) * (d + 4) * sizeof(float);
+  const dim3 sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
+  if (d == 128)
+    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), smem, st, part.Kp, N, Nv, part.qbar, part.kbar,
+                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
+  else
+    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), smem, st, part.Kp, N, Nv, part.qbar, part.kbar,
+                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(zero_i64_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, out.pairs, BH);
   hipLaunchKernelGGL(route_select_kernel, dim3(p.Cq + 1, BH), dim3(256), 0, st, scores, part.kv_off, part.q_off,
