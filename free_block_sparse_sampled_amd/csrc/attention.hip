@@ -52,6 +52,7 @@ struct AttnParams {
   float* o_sp;           // SPARSE: [BH][N][d]
   void* out;             // DENSE: [BH][N][d] contiguous
   int out_dtype;
+  int v_f16;             // v holds fp16 values (group-major fp16 copy of the values)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -66,7 +67,7 @@ struct TileInfo {
   bool valid;
 };
 
-template <int MODE>
+template <int MODE, int ROWS>
 __device__ inline TileInfo decode_tile(const AttnParams& P) {
   TileInfo t;
   t.hd = blockIdx.y;
@@ -100,14 +101,14 @@ __device__ inline TileInfo decode_tile(const AttnParams& P) {
       g0 = P.g.Nv;
       g1 = P.g.N;
     }
-    t.row0 = g0 + ti * kTileRows;
-    t.nrows = min(kTileRows, g1 - t.row0);
+    t.row0 = g0 + ti * ROWS;
+    t.nrows = min(ROWS, g1 - t.row0);
   } else if constexpr (MODE == MODE_DENSE) {
-    t.row0 = blockIdx.x * kTileRows;
-    t.nrows = min(kTileRows, P.g.N - t.row0);
+    t.row0 = blockIdx.x * ROWS;
+    t.nrows = min(ROWS, P.g.N - t.row0);
   } else {
-    t.row0 = blockIdx.x * kTileRows;  // probe slots
-    t.nrows = min(kTileRows, P.M - t.row0);
+    t.row0 = blockIdx.x * ROWS;  // probe slots
+    t.nrows = min(ROWS, P.M - t.row0);
     t.split = blockIdx.z;
     const int64_t N = P.g.N;
     t.key0 = int(N * t.split / P.splits);
@@ -164,30 +165,42 @@ __device__ __forceinline__ int seg_row(const int* seg_start, const int* seg_cum,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams P) {
-  constexpr int KS = D + 8;   // Ks row stride (bf16 elements)
+// WAVES waves of 16 query rows share each 64-key chunk staged in LDS (K as bf16 rows, V
+// transposed to fp16).  The global loads of chunk c+1 are issued into registers before the
+// MFMAs of chunk c, and the row indices of chunk c+1 are resolved meanwhile, so memory latency
+// overlaps compute.  Only the final chunk is masked.  The running maximum used for the
+// exponentials is raised lazily: O and l are rescaled only when a row's maximum grows by more
+// than 2^8, which keeps p <= 256 (exact range in fp16) and skips most rescales.
+template <int D, int MODE, int WAVES, int RS, bool VF16>
+__global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int ROWS = WAVES * 16 * RS;
+  constexpr int KS = D + 8;       // Ks row stride (bf16 elements)
   constexpr int VS = kChunk + 4;  // Vt row stride (fp16 elements)
   constexpr int NT = D / 16;
   constexpr int KSTEPS = D / 32;
+  constexpr int KPIECES = kChunk * (D / 8);              // 16-byte pieces of a K chunk
+  constexpr int VITEMS = (kChunk / 4) * (D / 8);         // 4 keys x 8 columns items of a V chunk
+  constexpr int KPT = (KPIECES + NTH - 1) / NTH;         // per thread
+  constexpr int VPT = (VITEMS + NTH - 1) / NTH;
+  constexpr float kRescale = 8.0f;                       // lazy rescale threshold (log2 units)
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_raw);
   _Float16* Vt = reinterpret_cast<_Float16*>(smem_raw + kChunk * KS * 2);
-  int* rowidx = reinterpret_cast<int*>(smem_raw + kChunk * KS * 2 + D * VS * 2);
-  int* seg_start = rowidx + kChunk;
+  int* rowidx = reinterpret_cast<int*>(smem_raw + kChunk * KS * 2 + D * VS * 2);  // [2][kChunk]
+  int* seg_start = rowidx + 2 * kChunk;
   int* seg_cum = seg_start + (MODE == MODE_SPARSE ? 1040 : 0);
   int* scan = seg_cum + (MODE == MODE_SPARSE ? 1040 : 0);
 
-  const TileInfo t = decode_tile<MODE>(P);
+  const TileInfo t = decode_tile<MODE, ROWS>(P);
   if (!t.valid || t.nrows <= 0) return;
   const int hd = t.hd;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
 
-  // key source
   const uint16_t* Kb;
   const uint16_t* Vb;
-  int64_t krs;  // key row stride (elements)
+  int64_t krs;
   if constexpr (MODE == MODE_SPARSE) {
     Kb = static_cast<const uint16_t*>(P.k) + size_t(hd) * P.g.N * D;
     Vb = static_cast<const uint16_t*>(P.v) + size_t(hd) * P.g.N * D;
@@ -204,12 +217,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams P) {
   } else {
     total = t.key1 - t.key0;
   }
+  const int nchunks = (total + kChunk - 1) / kChunk;
 
-  // query fragments: lane holds row r16 of this wave's 16 rows, dims ks*32 + 8g .. +7
-  const int qslot = w * 16 + r16;
-  const bool qvalid = qslot < t.nrows;
-  bf16x8_t qf[KSTEPS];
-  {
+  // query fragments: for row-set rs the lane holds row r16 of 16 rows, dims ks*32 + 8g .. +7
+  bf16x8_t qf[RS][KSTEPS];
+#pragma unroll
+  for (int rs = 0; rs < RS; ++rs) {
+    const int qslot = (w * RS + rs) * 16 + r16;
+    const bool qvalid = qslot < t.nrows;
     const uint16_t* qrow = nullptr;
     if (qvalid) {
       if constexpr (MODE == MODE_SPARSE) {
@@ -225,102 +240,160 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams P) {
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (qvalid) u = *reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g);
-      qf[ks] = as_bf16x8(u);
+      qf[rs][ks] = as_bf16x8(u);
     }
   }
-  const bool wave_active = (w * 16) < t.nrows;
+  const bool wave_active = (w * RS * 16) < t.nrows;
+  const bool set1_active = RS > 1 && (w * RS * 16 + 16) < t.nrows;
+
+  auto key_row = [&](int pos) -> int {
+    if constexpr (MODE == MODE_SPARSE) return seg_row(seg_start, seg_cum, nseg, pos);
+    else return t.key0 + pos;
+  };
+  // row indices of chunk 0
+  if (threadIdx.x < kChunk) rowidx[threadIdx.x] = int(threadIdx.x) < min(kChunk, total) ? key_row(threadIdx.x) : -1;
+  __syncthreads();
+
+  uint4 kreg[KPT];
+  uint4 vreg[VPT][4];
+  auto load_chunk = [&](const int* ridx) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      if (e < KPIECES) {
+        const int row = ridx[e / (D / 8)];
+        if (row >= 0) kreg[i] = *reinterpret_cast<const uint4*>(Kb + int64_t(row) * krs + (e % (D / 8)) * 8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * NTH;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vreg[i][j] = make_uint4(0, 0, 0, 0);
+      if (e < VITEMS) {
+        const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = ridx[kq * 4 + j];
+          if (row >= 0) vreg[i][j] = *reinterpret_cast<const uint4*>(Vb + int64_t(row) * krs + dq * 8);
+        }
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      if (e < KPIECES) *reinterpret_cast<uint4*>(Ks + (e / (D / 8)) * KS + (e % (D / 8)) * 8) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      if (e < VITEMS) {
+        const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
+        _Float16 vv[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (VF16) {
+            const f16x8_t h8 = __builtin_bit_cast(f16x8_t, vreg[i][j]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) vv[j][c] = h8[c];
+          } else {
+            const uint32_t wv[4] = {vreg[i][j].x, vreg[i][j].y, vreg[i][j].z, vreg[i][j].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              vv[j][2 * c] = _Float16(__uint_as_float(wv[c] << 16));
+              vv[j][2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          f16x4_t pk = {vv[0][c], vv[1][c], vv[2][c], vv[3][c]};
+          *reinterpret_cast<f16x4_t*>(Vt + (dq * 8 + c) * VS + kq * 4) = pk;
+        }
+      }
+    }
+  };
 
   const float scale = kLog2e / sqrtf(float(D));
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t oacc[NT];
+  float m_run[RS], l_run[RS];
+  f32x4_t oacc[RS][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) oacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rs = 0; rs < RS; ++rs) {
+    m_run[rs] = -INFINITY;
+    l_run[rs] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  const int nchunks = (total + kChunk - 1) / kChunk;
+  if (nchunks > 0) load_chunk(rowidx);
   for (int ch = 0; ch < nchunks; ++ch) {
     const int cbase = ch * kChunk;
     const int nvalid = min(kChunk, total - cbase);
-    if (threadIdx.x < kChunk) {
-      int row = -1;
-      if (int(threadIdx.x) < nvalid) {
-        if constexpr (MODE == MODE_SPARSE) row = seg_row(seg_start, seg_cum, nseg, cbase + threadIdx.x);
-        else row = t.key0 + cbase + threadIdx.x;
-      }
-      rowidx[threadIdx.x] = row;
+    store_chunk();
+    int* ridx_next = rowidx + ((ch + 1) & 1) * kChunk;
+    if (threadIdx.x < kChunk && ch + 1 < nchunks) {
+      const int pos = cbase + kChunk + threadIdx.x;
+      ridx_next[threadIdx.x] = pos < total ? key_row(pos) : -1;
     }
     __syncthreads();
-    // K chunk: 64 rows x D bf16, 16-byte pieces
-    for (int e = threadIdx.x; e < kChunk * (D / 8); e += 256) {
-      const int rr = e / (D / 8), cp = e % (D / 8);
-      const int row = rowidx[rr];
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row >= 0) u = *reinterpret_cast<const uint4*>(Kb + int64_t(row) * krs + cp * 8);
-      *reinterpret_cast<uint4*>(Ks + rr * KS + cp * 8) = u;
-    }
-    // V chunk, transposed and converted to fp16: 4 keys x 8 columns per item
-    for (int e = threadIdx.x; e < (kChunk / 4) * (D / 8); e += 256) {
-      const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
-      _Float16 vv[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rowidx[kq * 4 + i];
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row >= 0) u = *reinterpret_cast<const uint4*>(Vb + int64_t(row) * krs + dq * 8);
-        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          vv[i][2 * c] = _Float16(__uint_as_float(wv[c] << 16));
-          vv[i][2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        f16x4_t pk = {vv[0][c], vv[1][c], vv[2][c], vv[3][c]};
-        *reinterpret_cast<f16x4_t*>(Vt + (dq * 8 + c) * VS + kq * 4) = pk;
-      }
-    }
-    __syncthreads();
+    if (ch + 1 < nchunks) load_chunk(ridx_next);
     if (wave_active) {
-      // S^T tiles: 4 x (16 keys x 16 rows)
-      f32x4_t s[4];
+      // S^T tiles: 4 x (16 keys x 16 rows) per row-set; each K fragment read serves all sets
+      f32x4_t s[RS][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) s[rs][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          const uint4 u = *reinterpret_cast<const uint4*>(Ks + (mt * 16 + r16) * KS + ks * 32 + 8 * g);
-          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u), qf[ks], s[mt], 0, 0, 0);
+          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
+          s[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][mt], 0, 0, 0);
+          if (RS > 1 && set1_active)
+            s[RS - 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[RS - 1][ks], s[RS - 1][mt], 0, 0, 0);
         }
       }
-      // online softmax for row r16; this lane holds keys mt*16 + 4g + v
-      float mx = -INFINITY;
+      f16x8_t pf[RS][2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int rs = 0; rs < RS; ++rs) {
+        // this lane holds keys mt*16 + 4g + v of row r16 of the set
+        if (nvalid < kChunk) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = mt * 16 + 4 * g + v;
-          const float x = key < nvalid ? s[mt][v] * scale : -INFINITY;
-          s[mt][v] = x;
-          mx = fmaxf(mx, x);
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (mt * 16 + 4 * g + v >= nvalid) s[rs][mt][v] = -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float ls = 0.f;
-      f16x8_t pf[2];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float pv = exp2f(s[mt][v] - m_new);
-          ls += pv;
-          pf[mt >> 1][(mt & 1) * 4 + v] = _Float16(pv);
+          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[rs][mt][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= scale;
+        const bool grow = mx > m_run[rs] + kRescale;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run[rs];
+          const float alpha = exp2f(m_run[rs] - m_new);
+          m_run[rs] = m_new;
+          l_run[rs] *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] *= alpha;
         }
-      l_run = l_run * alpha + ls;
+        float ls = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) oacc[nt] *= alpha;
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float pv = exp2f(fmaf(s[rs][mt][v], scale, -m_run[rs]));
+            ls += pv;
+            pf[rs][mt >> 1][(mt & 1) * 4 + v] = _Float16(pv);
+          }
+        l_run[rs] += ls;
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -329,42 +402,49 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams P) {
           const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow);
           const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + 16);
           const f16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[h], oacc[nt], 0, 0, 0);
+          oacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[0][h], oacc[0][nt], 0, 0, 0);
+          if (RS > 1 && set1_active)
+            oacc[RS - 1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[RS - 1][h], oacc[RS - 1][nt], 0, 0, 0);
         }
       }
     }
     __syncthreads();
   }
-  if (!qvalid) return;
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-  if constexpr (MODE == MODE_PROBE) {
-    float* dst = P.part + ((size_t(hd) * P.M + t.row0 + qslot) * P.splits + t.split) * (D + 2);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) = make_float4(oacc[nt][0], oacc[nt][1], oacc[nt][2], oacc[nt][3]);
-    if (g == 0) {
-      dst[D] = m_run;
-      dst[D + 1] = lt;
-    }
-  } else {
-    const float inv = 1.f / lt;
-    if constexpr (MODE == MODE_SPARSE) {
-      float* dst = P.o_sp + (size_t(hd) * P.g.N + t.row0 + qslot) * D;
+  for (int rs = 0; rs < RS; ++rs) {
+    const int qslot = (w * RS + rs) * 16 + r16;
+    if (qslot >= t.nrows) continue;
+    float lt = l_run[rs] + __shfl_xor(l_run[rs], 16);
+    lt += __shfl_xor(lt, 32);
+    if constexpr (MODE == MODE_PROBE) {
+      float* dst = P.part + ((size_t(hd) * P.M + t.row0 + qslot) * P.splits + t.split) * (D + 2);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) =
-            make_float4(oacc[nt][0] * inv, oacc[nt][1] * inv, oacc[nt][2] * inv, oacc[nt][3] * inv);
+            make_float4(oacc[rs][nt][0], oacc[rs][nt][1], oacc[rs][nt][2], oacc[rs][nt][3]);
+      if (g == 0) {
+        dst[D] = m_run[rs];
+        dst[D + 1] = lt;
+      }
     } else {
-      const size_t rowbase = (size_t(hd) * P.g.N + t.row0 + qslot) * D;
+      const float inv = 1.f / lt;
+      if constexpr (MODE == MODE_SPARSE) {
+        float* dst = P.o_sp + (size_t(hd) * P.g.N + t.row0 + qslot) * D;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
+          *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) = make_float4(
+              oacc[rs][nt][0] * inv, oacc[rs][nt][1] * inv, oacc[rs][nt][2] * inv, oacc[rs][nt][3] * inv);
+      } else {
+        const size_t rowbase = (size_t(hd) * P.g.N + t.row0 + qslot) * D;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const size_t idx = rowbase + nt * 16 + 4 * g + v;
-          if (P.out_dtype == SPR_BF16) store_out<SPR_BF16>(P.out, idx, oacc[nt][v] * inv);
-          else store_out<SPR_F32>(P.out, idx, oacc[nt][v] * inv);
-        }
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const size_t idx = rowbase + nt * 16 + 4 * g + v;
+            if (P.out_dtype == SPR_BF16) store_out<SPR_BF16>(P.out, idx, oacc[rs][nt][v] * inv);
+            else store_out<SPR_F32>(P.out, idx, oacc[rs][nt][v] * inv);
+          }
+      }
     }
   }
 }
@@ -374,7 +454,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams P) {
 template <int D, int MODE>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
   __shared__ int seg_start[1040], seg_cum[1040], scan[1024];
-  const TileInfo t = decode_tile<MODE>(P);
+  const TileInfo t = decode_tile<MODE, kTileRows>(P);
   if (!t.valid || t.nrows <= 0) return;
   const int hd = t.hd, lane = threadIdx.x;
   const float* Kb;
@@ -476,17 +556,44 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
 // ------------------------------------------------------------------ host drivers
 template <int D, int MODE>
 static size_t mfma_smem() {
-  size_t s = size_t(kChunk) * (D + 8) * 2 + size_t(D) * (kChunk + 4) * 2 + kChunk * sizeof(int);
+  size_t s = size_t(kChunk) * (D + 8) * 2 + size_t(D) * (kChunk + 4) * 2 + 2 * kChunk * sizeof(int);
   if (MODE == MODE_SPARSE) s += (1040 * 2 + 1024) * sizeof(int);
   return s;
 }
 
+// Block shapes of the MFMA kernel: waves per block and 16-row sets per wave (a wave with two
+// sets reads each K and V fragment from LDS once for 32 rows).
+#ifndef SPR_SPARSE_WAVES
+#define SPR_SPARSE_WAVES 4
+#endif
+#ifndef SPR_SPARSE_RS
+#define SPR_SPARSE_RS 1
+#endif
+#ifndef SPR_DENSE_WAVES
+#define SPR_DENSE_WAVES 8
+#endif
+#ifndef SPR_DENSE_RS
+#define SPR_DENSE_RS 1
+#endif
+template <int MODE>
+constexpr int mfma_waves() { return MODE == MODE_SPARSE ? SPR_SPARSE_WAVES : MODE == MODE_DENSE ? SPR_DENSE_WAVES : 4; }
+template <int MODE>
+constexpr int mfma_rowsets() { return MODE == MODE_SPARSE ? SPR_SPARSE_RS : MODE == MODE_DENSE ? SPR_DENSE_RS : 1; }
+template <int MODE>
+constexpr int mfma_rows() { return 16 * mfma_waves<MODE>() * mfma_rowsets<MODE>(); }
+
 template <int D, int MODE>
 static void launch_attn(const AttnParams& P, dim3 grid, int dtype, hipStream_t st) {
   if (dtype == SPR_BF16) {
+    constexpr int W = mfma_waves<MODE>(), RS = mfma_rowsets<MODE>();
     const size_t sm = mfma_smem<D, MODE>();
-    allow_lds(attn_mfma_kernel<D, MODE>, sm);
-    hipLaunchKernelGGL((attn_mfma_kernel<D, MODE>), grid, dim3(256), sm, st, P);
+    if (MODE == MODE_SPARSE && P.v_f16) {
+      allow_lds(attn_mfma_kernel<D, MODE, W, RS, true>, sm);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, RS, true>), grid, dim3(W * 64), sm, st, P);
+    } else {
+      allow_lds(attn_mfma_kernel<D, MODE, W, RS, false>, sm);
+      hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, RS, false>), grid, dim3(W * 64), sm, st, P);
+    }
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, MODE>), grid, dim3(64), 0, st, P);
   }
@@ -503,16 +610,20 @@ static spr_status dispatch_d(const AttnParams& P, dim3 grid, int d, int dtype, h
 
 spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
                            const spr_route& route, float* o_sp, void* ws, const Workspace& L, hipStream_t st) {
-  (void)ws; (void)L;
   AttnParams P = {};
   P.q = part.Qp; P.k = part.Kp; P.v = part.Vp;
+  if (desc.dtype == SPR_BF16) {
+    P.v = ws_ptr<void>(ws, L.vh);
+    P.v_f16 = 1;
+  }
   P.g = make_geom(desc);
   P.tile_off = route.tile_off; P.q_off = part.q_off; P.n_q = part.n_q; P.n_kv = part.n_kv;
   P.kv_off = part.kv_off; P.sel_cnt = route.sel_cnt; P.sel_kv = route.sel_kv;
   P.Cq = p.Cq; P.Ck = p.Ck;
   P.o_sp = o_sp;
   const int Nv = desc.N - desc.n_text;
-  const int max_tiles = p.Cq + ceil_div(Nv, kTileRows) + ceil_div(desc.n_text, kTileRows) + 1;
+  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_SPARSE>() : kTileRows;
+  const int max_tiles = p.Cq + ceil_div(Nv, rows) + ceil_div(desc.n_text, rows) + 1;
   return dispatch_d<MODE_SPARSE>(P, dim3(max_tiles, desc.B * desc.H), desc.d, desc.dtype, st);
 }
 
@@ -537,7 +648,12 @@ spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, co
   P.q = q; P.k = k; P.v = v;
   P.g = make_geom(desc);
   P.out = out; P.out_dtype = out_dtype;
-  return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, kTileRows), desc.B * desc.H), desc.d, desc.dtype, st);
+  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_DENSE>() : kTileRows;
+  return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, rows), desc.B * desc.H), desc.d, desc.dtype, st);
 }
 
+}  // namespace spr
+
+namespace spr {
+int sparse_rows_per_block(int dtype) { return dtype == SPR_BF16 ? mfma_rows<MODE_SPARSE>() : kTileRows; }
 }  // namespace spr

@@ -352,6 +352,23 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict
   *reinterpret_cast<uint4*>(dd) = *reinterpret_cast<const uint4*>(s);
 }
 
+// fp16 copy of the group-major bf16 values (the operand type of the P V products).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src, _Float16* __restrict__ dst,
+                                                          size_t n) {
+  const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const uint4 u = *reinterpret_cast<const uint4*>(src + i);
+  const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  h8 o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o[2 * c] = _Float16(__uint_as_float(wv[c] << 16));
+    o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+  }
+  *reinterpret_cast<h8*>(dst + i) = o;
+}
+
 // Means of rows [off[b], off[b+1]) of a group-major [BH][N][d] tensor, one wave per group.
 template <int DT>
 __global__ __launch_bounds__(256) void group_mean_kernel(const void* __restrict__ src, int N, int d,
@@ -486,6 +503,12 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(gather_rows_kernel<DT>, ggrid, dim3(256), 0, st, k, g, out.kv_perm, out.Kp);
   hipLaunchKernelGGL(gather_rows_kernel<DT>, ggrid, dim3(256), 0, st, v, g, out.kv_perm, out.Vp);
   SPR_CHECK_LAUNCH();
+  if constexpr (DT == SPR_BF16) {
+    const size_t nel = size_t(BH) * desc.N * d;
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(unsigned(ceil_div64(int64_t(nel / 8), 256))), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(out.Vp), wsp<_Float16>(ws, L.vh), nel);
+    SPR_CHECK_LAUNCH();
+  }
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BH), dim3(256), 0, st, out.Kp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.kbar);
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BH), dim3(256), 0, st, out.Vp, desc.N, d,

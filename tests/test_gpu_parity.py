@@ -128,7 +128,8 @@ def _oracle_is_tie_free(ref):
             and min(i["min_gap"] for i in ref["route_info"]) > TIE)
 
 
-@pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 7)])])
+@pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 7)]),
+                                        ("small_text", [(0, 0), (0, 1)])])
 def test_operator_end_to_end(name, heads):
     cfg = config(name)
     opc = op_config(cfg)
@@ -142,10 +143,12 @@ def test_operator_end_to_end(name, heads):
             [np.arange(0, cfg.N, 7), np.arange(cfg.N - 100, cfg.N)]))
         ref = O.sparsepr_head(q[b, h], k[b, h], v[b, h], p, head=hd, rows=rows)
         ref["lam"] = p.lam
-        tie_free = _oracle_is_tie_free(ref)
-        if not tie_free:
-            pytest.skip(f"oracle run of head {hd} has a decision within the 1e-6 tie margin")
-        _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text)
+        if _oracle_is_tie_free(ref):
+            _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text)
+        else:
+            # a decision of the oracle's run lies within the 1e-6 tie margin: the two runs may
+            # legitimately part there, so check every stage in lockstep instead
+            _lockstep_head(g, q, k, v, cfg, opc, b, h, np.random.default_rng(1))
     assert np.all(g["head_status"] & 1 == 0)
 
 
@@ -198,76 +201,85 @@ def test_lockstep_stages_small():
         np.testing.assert_allclose(g["probe_w"][hd], w, rtol=1e-15)
 
 
-def _full_size_lockstep(name, heads, nrows=96, ngroups=6):
-    """Full-size workload in the benchmark's launch configuration: every stage checked on
-    sampled outputs with the oracle's stage functions applied to the GPU's own inputs."""
+def _lockstep_head(g, q, k, v, cfg, opc, b, h, rng, nrows=96, ngroups=6):
+    """Every stage of head (b, h) checked on sampled outputs with the oracle's stage functions
+    applied to the GPU's own inputs of that stage."""
+    N, Nv, d = cfg.N, cfg.Nv, cfg.d
+    T = O.key_budget(opc.rho, N, Nv, opc.M, cfg.n_text)
+    hd = b * cfg.H + h
+    qh, kh, vh = (x[b, h].astype(np.float64) for x in (q, k, v))
+    nkv, nq = int(g["n_kv"][hd]), int(g["n_q"][hd])
+    # K/V and query partitions: final assignment pass and compaction
+    for feat, cent, lab_g, C in ((g["phiK"][hd], g["cK_last"][hd], g["kv_label"][hd], opc.Ck),
+                                 (g["phiQ"][hd], g["cQ_last"][hd], g["q_label"][hd], opc.Cq)):
+        lab, _, margin = O.kmeans_assign(feat, cent)
+        lab_c, n = O.compact_labels(lab, C)
+        ok = margin > TIE
+        assert ok.mean() > 0.99
+        assert np.array_equal(lab_g[ok], lab_c[ok])
+    perm, off = O.group_perm(g["kv_label"][hd], nkv)
+    assert np.array_equal(g["kv_perm"][hd], perm) and np.array_equal(g["kv_off"][hd][: nkv + 1], off)
+    perm, off = O.group_perm(g["q_label"][hd], nq)
+    assert np.array_equal(g["q_perm"][hd], perm) and np.array_equal(g["q_off"][hd][: nq + 1], off)
+    size, kbar, vbar = O.key_group_stats(kh[:Nv], vh[:Nv], g["kv_label"][hd], nkv)
+    np.testing.assert_allclose(g["kbar"][hd][:nkv], kbar, rtol=0, atol=1e-12)
+    # routing of sampled query groups from the GPU's centroids
+    groups = rng.choice(nq, size=min(ngroups, nq), replace=False)
+    sc, _ = O.route_scores(g["qbar"][hd][:nq], kh[:Nv], vh[:Nv], g["kv_label"][hd], g["kbar"][hd][:nkv],
+                           g["vbar"][hd][:nkv], groups=groups)
+    for ia, a in enumerate(groups):
+        sel, info = O.route_select(sc[ia], size, T)
+        cnt = int(g["sel_cnt"][hd][a])
+        got = list(g["sel_kv"][hd][a][:cnt])
+        if cfg.n_text:
+            assert got[-1] == nkv
+            got = got[:-1]
+        if info["min_gap"] > TIE:
+            assert got == list(sel), (hd, a)
+    # probes
+    qs = np.diff(g["q_off"][hd][: nq + 1])
+    rows_p, w, _ = O.select_probes(g["q_label"][hd], g["qdist"][hd], qs, opc.M)
+    assert np.array_equal(g["probe_idx"][hd], rows_p)
+    # sparse and dense rows on the GPU's routes
+    sel_all = [g["sel_kv"][hd][a][: int(g["sel_cnt"][hd][a]) - (1 if cfg.n_text else 0)] for a in range(nq)]
+    qlab = np.concatenate([g["q_label"][hd], np.full(cfg.n_text, -1)])
+    rows = np.unique(np.concatenate([rng.choice(N, nrows, replace=False), [0, Nv - 1, N - 1]]))
+    qpos = g["q_pos"][hd]
+    osp = O.sparse_attention_rows(qh, kh, vh, rows, qlab, g["kv_label"][hd], sel_all, cfg.n_text)
+    pos = np.where(rows < Nv, qpos[np.minimum(rows, Nv - 1)], rows)
+    err = row_rel_err(g["o_sp"][hd][pos], osp)
+    assert err.max() < ROW_TOL, ("o_sp", err.max())
+    od = O.dense_attention_rows(qh, kh, vh, g["probe_idx"][hd])
+    err = row_rel_err(g["o_probe"][hd], od)
+    assert err.max() < ROW_TOL, ("o_probe", err.max())
+    # fit from the GPU's probe features and residuals, then the final rows
+    X = g["o_sp"][hd][qpos[g["probe_idx"][hd]]].astype(np.float64)
+    fit = O.ridge_fit(X, g["o_probe"][hd] - X, g["probe_w"][hd], opc.lam, opc.std_eps)
+    Bg = g["fit_state"][hd][3 * d:].reshape(d, d)
+    assert np.linalg.norm(Bg - fit["B"]) <= 1e-6 * max(np.linalg.norm(fit["B"]), 1e-12)
+    want = O.correct(g["o_sp"][hd][pos].astype(np.float64), fit)
+    want[rows >= Nv] = g["o_sp"][hd][pos][rows >= Nv]
+    isprobe = np.isin(rows, g["probe_idx"][hd])
+    err = row_rel_err(g["out"][hd][rows][~isprobe], want[~isprobe])
+    assert err.max() < ROW_TOL, ("out", err.max())
+
+
+def _full_size_lockstep(name, heads):
+    """Full-size workload in the benchmark's launch configuration, checked in lockstep."""
     cfg = config(name)
     opc = op_config(cfg)
     (q, k, v), (tq, tk, tv) = device_inputs(cfg)
     op = run_operator(cfg, opc, tq, tk, tv)
     g = pull(op)
     del tq, tk, tv
-    N, Nv, d = cfg.N, cfg.Nv, cfg.d
-    T = O.key_budget(opc.rho, N, Nv, opc.M, cfg.n_text)
     rng = np.random.default_rng(0)
     for (b, h) in heads:
-        hd = b * cfg.H + h
-        qh, kh, vh = (x[b, h].astype(np.float64) for x in (q, k, v))
-        nkv, nq = int(g["n_kv"][hd]), int(g["n_q"][hd])
-        # K/V and query partitions: final assignment pass and compaction
-        for feat, cent, lab_g, C in ((g["phiK"][hd], g["cK_last"][hd], g["kv_label"][hd], opc.Ck),
-                                     (g["phiQ"][hd], g["cQ_last"][hd], g["q_label"][hd], opc.Cq)):
-            lab, _, margin = O.kmeans_assign(feat, cent)
-            lab_c, n = O.compact_labels(lab, C)
-            ok = margin > TIE
-            assert ok.mean() > 0.99
-            assert np.array_equal(lab_g[ok], lab_c[ok])
-        perm, off = O.group_perm(g["kv_label"][hd], nkv)
-        assert np.array_equal(g["kv_perm"][hd], perm) and np.array_equal(g["kv_off"][hd][: nkv + 1], off)
-        perm, off = O.group_perm(g["q_label"][hd], nq)
-        assert np.array_equal(g["q_perm"][hd], perm) and np.array_equal(g["q_off"][hd][: nq + 1], off)
-        size, kbar, vbar = O.key_group_stats(kh[:Nv], vh[:Nv], g["kv_label"][hd], nkv)
-        np.testing.assert_allclose(g["kbar"][hd][:nkv], kbar, rtol=0, atol=1e-12)
-        # routing of sampled query groups from the GPU's centroids
-        groups = rng.choice(nq, size=min(ngroups, nq), replace=False)
-        sc, _ = O.route_scores(g["qbar"][hd][:nq], kh[:Nv], vh[:Nv], g["kv_label"][hd], g["kbar"][hd][:nkv],
-                               g["vbar"][hd][:nkv], groups=groups)
-        for ia, a in enumerate(groups):
-            sel, info = O.route_select(sc[ia], size, T)
-            cnt = int(g["sel_cnt"][hd][a])
-            got = list(g["sel_kv"][hd][a][:cnt])
-            if cfg.n_text:
-                assert got[-1] == nkv
-                got = got[:-1]
-            if info["min_gap"] > TIE:
-                assert got == list(sel), (hd, a)
-        # probes
-        qs = np.diff(g["q_off"][hd][: nq + 1])
-        rows_p, w, _ = O.select_probes(g["q_label"][hd], g["qdist"][hd], qs, opc.M)
-        assert np.array_equal(g["probe_idx"][hd], rows_p)
-        # sparse and dense rows on the GPU's routes
-        sel_all = [g["sel_kv"][hd][a][: int(g["sel_cnt"][hd][a]) - (1 if cfg.n_text else 0)] for a in range(nq)]
-        qlab = np.concatenate([g["q_label"][hd], np.full(cfg.n_text, -1)])
-        rows = np.unique(np.concatenate([rng.choice(N, nrows, replace=False), [0, Nv - 1, N - 1]]))
-        qpos = g["q_pos"][hd]
-        osp = O.sparse_attention_rows(qh, kh, vh, rows, qlab, g["kv_label"][hd], sel_all, cfg.n_text)
-        pos = np.where(rows < Nv, qpos[np.minimum(rows, Nv - 1)], rows)
-        err = row_rel_err(g["o_sp"][hd][pos], osp)
-        assert err.max() < ROW_TOL, ("o_sp", err.max())
-        od = O.dense_attention_rows(qh, kh, vh, g["probe_idx"][hd])
-        err = row_rel_err(g["o_probe"][hd], od)
-        assert err.max() < ROW_TOL, ("o_probe", err.max())
-        # fit from the GPU's probe features and residuals, then the final rows
-        X = g["o_sp"][hd][qpos[g["probe_idx"][hd]]].astype(np.float64)
-        fit = O.ridge_fit(X, g["o_probe"][hd] - X, g["probe_w"][hd], opc.lam, opc.std_eps)
-        Bg = g["fit_state"][hd][3 * d:].reshape(d, d)
-        assert np.linalg.norm(Bg - fit["B"]) <= 1e-6 * max(np.linalg.norm(fit["B"]), 1e-12)
-        want = O.correct(g["o_sp"][hd][pos].astype(np.float64), fit)
-        want[rows >= Nv] = g["o_sp"][hd][pos][rows >= Nv]
-        isprobe = np.isin(rows, g["probe_idx"][hd])
-        err = row_rel_err(g["out"][hd][rows][~isprobe], want[~isprobe])
-        assert err.max() < ROW_TOL, ("out", err.max())
+        _lockstep_head(g, q, k, v, cfg, opc, b, h, rng)
 
 
 def test_full_size_mid_sampled():
     _full_size_lockstep("mid", [(0, 0), (0, 39)])
+
+
+def test_full_size_joint_text_sampled():
+    _full_size_lockstep("joint", [(0, 0), (1, 23)])

@@ -83,6 +83,8 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "joint": WorkloadConfig("joint", 5, 2, 24, (21, 39, 40), 128, "bf16", 256, 512, 512, 256, 2048,
                             0.22, 1.0),
 }
+# parity-test shape with text tokens: the small video latent plus 128 text tokens, two heads
+CONFIGS["small_text"] = CONFIGS["small"].with_(name="small_text", H=2, n_text=128)
 
 
 def config(name: str) -> WorkloadConfig:
