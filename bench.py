@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--max-iters", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (scale for traffic counters)")
     return ap.parse_args()
 
 
@@ -100,6 +102,12 @@ def main():
     del q, k, v
     op = spr.SparsePR(tq, opc, n_text=cfg.n_text)
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mb:
+        src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         stages = (lambda: op.partition(tq, tk, tv), op.route_, op.attn_sparse, lambda: op.probe_exact(tq, tk, tv),

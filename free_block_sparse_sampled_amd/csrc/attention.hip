@@ -13,6 +13,8 @@
 // bf16 to fp16 while it is staged, transposed, into LDS).  Computing the transposes puts a
 // query row's scores and its output columns in the same lane, so the softmax rescaling needs
 // no cross-lane traffic.  fp32 inputs use a plain VALU kernel.
+#include <type_traits>
+
 #include "common.hpp"
 #include "stages.hpp"
 
@@ -172,11 +174,11 @@ __device__ __forceinline__ int seg_row(const int* seg_start, const int* seg_cum,
 // exponentials is raised lazily: O and l are rescaled only when a row's maximum grows by more
 // than 2^8, which keeps p <= 256 (exact range in fp16) and skips most rescales.
 template <int D, int MODE, int WAVES, int RS, bool VF16>
-__global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnParams P) {
   constexpr int NTH = WAVES * 64;
   constexpr int ROWS = WAVES * 16 * RS;
   constexpr int KS = D + 8;       // Ks row stride (bf16 elements)
-  constexpr int VS = kChunk + 4;  // Vt row stride (fp16 elements)
+  constexpr int VS = kChunk + 8;  // Vt row stride (fp16 elements; 16-byte aligned rows)
   constexpr int NT = D / 16;
   constexpr int KSTEPS = D / 32;
   constexpr int KPIECES = kChunk * (D / 8);              // 16-byte pieces of a K chunk
@@ -281,6 +283,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
       }
     }
   };
+  // V chunk stored transposed ([column][key], fp16).  Inside each 32-key half the key k sits at
+  // position 8*((k % 16) / 4) + 4*(k / 16) + k % 4, so the eight keys that lane group g feeds to
+  // one P V product ({4g..4g+3} and {16+4g..16+4g+3}) are one contiguous 16-byte read.
   auto store_chunk = [&]() {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -292,41 +297,117 @@ __global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
       const int e = threadIdx.x + i * NTH;
       if (e < VITEMS) {
         const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
-        _Float16 vv[4][8];
+        uint32_t wv[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (VF16) {
-            const f16x8_t h8 = __builtin_bit_cast(f16x8_t, vreg[i][j]);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) vv[j][c] = h8[c];
+            wv[j][0] = vreg[i][j].x; wv[j][1] = vreg[i][j].y; wv[j][2] = vreg[i][j].z; wv[j][3] = vreg[i][j].w;
           } else {
-            const uint32_t wv[4] = {vreg[i][j].x, vreg[i][j].y, vreg[i][j].z, vreg[i][j].w};
+            const uint32_t src[4] = {vreg[i][j].x, vreg[i][j].y, vreg[i][j].z, vreg[i][j].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              vv[j][2 * c] = _Float16(__uint_as_float(wv[c] << 16));
-              vv[j][2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+              const _Float16 lo = _Float16(__uint_as_float(src[c] << 16));
+              const _Float16 hi = _Float16(__uint_as_float(src[c] & 0xFFFF0000u));
+              wv[j][c] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
             }
           }
         }
+        const int pos = (kq / 8) * 32 + 8 * (kq % 4) + 4 * ((kq % 8) / 4);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          f16x4_t pk = {vv[0][c], vv[1][c], vv[2][c], vv[3][c]};
-          *reinterpret_cast<f16x4_t*>(Vt + (dq * 8 + c) * VS + kq * 4) = pk;
+        for (int c = 0; c < 4; ++c) {
+          // columns 2c (low halves) and 2c + 1 (high halves) of the four keys
+          const uint2 lo = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x05040100u),
+                                      __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x05040100u));
+          const uint2 hi = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x07060302u),
+                                      __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x07060302u));
+          *reinterpret_cast<uint2*>(Vt + (dq * 8 + 2 * c) * VS + pos) = lo;
+          *reinterpret_cast<uint2*>(Vt + (dq * 8 + 2 * c + 1) * VS + pos) = hi;
         }
       }
     }
   };
 
   const float scale = kLog2e / sqrtf(float(D));
-  float m_run[RS], l_run[RS];
-  f32x4_t oacc[RS][NT];
+  float m_run[RS];
+  f32x4_t oacc[RS][NT], lacc[RS];
 #pragma unroll
   for (int rs = 0; rs < RS; ++rs) {
     m_run[rs] = -INFINITY;
-    l_run[rs] = 0.f;
+    lacc[rs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+
+  // one chunk: S^T = K Q^T, online softmax, O^T += V^T P^T; row sums come from the same fp16
+  // P through an MFMA against a tile of ones.  TAIL masks keys past the end.
+  auto compute_chunk = [&](auto tail_tag, int nvalid) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    f32x4_t sacc[RS][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int rs = 0; rs < RS; ++rs) sacc[rs][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
+        sacc[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], sacc[0][mt], 0, 0, 0);
+        if (RS > 1 && set1_active)
+          sacc[RS - 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[RS - 1][ks], sacc[RS - 1][mt], 0, 0, 0);
+      }
+    }
+    f16x8_t pf[RS][2];
+#pragma unroll
+    for (int rs = 0; rs < RS; ++rs) {
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (mt * 16 + 4 * g + v >= nvalid) sacc[rs][mt][v] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(sacc[rs][0][0], sacc[rs][0][1]), fmaxf(sacc[rs][0][2], sacc[rs][0][3]));
+#pragma unroll
+      for (int mt = 1; mt < 4; ++mt)
+        mx = fmaxf(fmaxf(mx, fmaxf(sacc[rs][mt][0], sacc[rs][mt][1])), fmaxf(sacc[rs][mt][2], sacc[rs][mt][3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= scale;
+      const bool grow = mx > m_run[rs] + kRescale;
+      if (__builtin_expect(__any(grow), 0)) {
+        __asm__ volatile("; rare rescale of the running output" ::);
+        const float m_new = grow ? mx : m_run[rs];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);
+        m_run[rs] = m_new;
+        lacc[rs] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] *= alpha;
+      }
+      const float mneg = -m_run[rs];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          pf[rs][mt >> 1][(mt & 1) * 4 + v] = _Float16(__builtin_amdgcn_exp2f(fmaf(sacc[rs][mt][v], scale, mneg)));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[0][h], lacc[0], 0, 0, 0);
+      if (RS > 1 && set1_active)
+        lacc[RS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[RS - 1][h], lacc[RS - 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f16x8_t av = __builtin_bit_cast(
+            f16x8_t, *reinterpret_cast<const uint4*>(Vt + (nt * 16 + r16) * VS + h * 32 + 8 * g));
+        oacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[0][h], oacc[0][nt], 0, 0, 0);
+        if (RS > 1 && set1_active)
+          oacc[RS - 1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[RS - 1][h], oacc[RS - 1][nt], 0, 0, 0);
+      }
+    }
+  };
 
   if (nchunks > 0) load_chunk(rowidx);
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -341,72 +422,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
     __syncthreads();
     if (ch + 1 < nchunks) load_chunk(ridx_next);
     if (wave_active) {
-      // S^T tiles: 4 x (16 keys x 16 rows) per row-set; each K fragment read serves all sets
-      f32x4_t s[RS][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs) s[rs][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
-          s[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][mt], 0, 0, 0);
-          if (RS > 1 && set1_active)
-            s[RS - 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[RS - 1][ks], s[RS - 1][mt], 0, 0, 0);
-        }
-      }
-      f16x8_t pf[RS][2];
-#pragma unroll
-      for (int rs = 0; rs < RS; ++rs) {
-        // this lane holds keys mt*16 + 4g + v of row r16 of the set
-        if (nvalid < kChunk) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (mt * 16 + 4 * g + v >= nvalid) s[rs][mt][v] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[rs][mt][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mx *= scale;
-        const bool grow = mx > m_run[rs] + kRescale;
-        if (__any(grow)) {
-          const float m_new = grow ? mx : m_run[rs];
-          const float alpha = exp2f(m_run[rs] - m_new);
-          m_run[rs] = m_new;
-          l_run[rs] *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] *= alpha;
-        }
-        float ls = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float pv = exp2f(fmaf(s[rs][mt][v], scale, -m_run[rs]));
-            ls += pv;
-            pf[rs][mt >> 1][(mt & 1) * 4 + v] = _Float16(pv);
-          }
-        l_run[rs] += ls;
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const _Float16* vrow = Vt + (nt * 16 + r16) * VS + h * 32 + 4 * g;
-          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow);
-          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + 16);
-          const f16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[0][h], oacc[0][nt], 0, 0, 0);
-          if (RS > 1 && set1_active)
-            oacc[RS - 1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[RS - 1][h], oacc[RS - 1][nt], 0, 0, 0);
-        }
-      }
+      if (__builtin_expect(nvalid == kChunk, 1)) compute_chunk(std::false_type{}, nvalid);
+      else compute_chunk(std::true_type{}, nvalid);
     }
     __syncthreads();
   }
@@ -414,8 +431,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_mfma_kernel(AttnParams P) {
   for (int rs = 0; rs < RS; ++rs) {
     const int qslot = (w * RS + rs) * 16 + r16;
     if (qslot >= t.nrows) continue;
-    float lt = l_run[rs] + __shfl_xor(l_run[rs], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lacc[rs][0];
     if constexpr (MODE == MODE_PROBE) {
       float* dst = P.part + ((size_t(hd) * P.M + t.row0 + qslot) * P.splits + t.split) * (D + 2);
 #pragma unroll
@@ -556,7 +572,7 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
 // ------------------------------------------------------------------ host drivers
 template <int D, int MODE>
 static size_t mfma_smem() {
-  size_t s = size_t(kChunk) * (D + 8) * 2 + size_t(D) * (kChunk + 4) * 2 + 2 * kChunk * sizeof(int);
+  size_t s = size_t(kChunk) * (D + 8) * 2 + size_t(D) * (kChunk + 8) * 2 + 2 * kChunk * sizeof(int);
   if (MODE == MODE_SPARSE) s += (1040 * 2 + 1024) * sizeof(int);
   return s;
 }

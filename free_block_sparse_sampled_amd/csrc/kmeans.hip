@@ -31,7 +31,7 @@ constexpr int KC = 256;       // centres per LDS chunk
 constexpr int CROW = RP + 8;  // LDS row stride in fp16 elements (keeps 16-row reads conflict free)
 constexpr int CTRL = 8;       // doubles of control word per head
 
-enum { C_DONE = 0, C_PASSES = 1, C_JPREV = 2, C_CMAX = 3, C_SCALE = 4, C_AMAX = 5 };
+enum { C_DONE = 0, C_PASSES = 1, C_JPREV = 2, C_CMAX = 3, C_SCALE = 4, C_AMAX = 5, C_STOPNOW = 6 };
 
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 
@@ -258,15 +258,12 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
+          // branch-free running best / index / second best
           const float val = fmaf(-2.f, acc[v], cv[v]);
           const int m = c0 + cb * 16 + 4 * g + v;
-          if (val < b1[pt]) {
-            b2[pt] = b1[pt];
-            b1[pt] = val;
-            i1[pt] = m;
-          } else if (val < b2[pt]) {
-            b2[pt] = val;
-          }
+          b2[pt] = fminf(b2[pt], fmaxf(b1[pt], val));
+          i1[pt] = val < b1[pt] ? m : i1[pt];
+          b1[pt] = fminf(b1[pt], val);
         }
       }
     }
@@ -351,7 +348,9 @@ __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const doub
   }
 }
 
-// Cost, label changes and Lloyd sums of the pass (see the file comment).
+// Cost, label changes and Lloyd sums of the pass.  Each wave walks its 64 points in order with
+// one lane per coordinate: it adds x to a running sum that is flushed (fp64 atomics) when the
+// label changes, and (x - c_label)^2 to the lane's share of the cost.
 template <int R>
 __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict__ feat, int n, int C,
                                                        const double* __restrict__ cent,
@@ -365,18 +364,9 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int j = blockIdx.x * 256 + threadIdx.x;
   const bool valid = j < n;
-  int lab = 0;
-  double dist = 0.0;
-  int changed = 0;
+  int lab = 0, changed = 0;
   if (valid) {
     lab = lab_new[size_t(hd) * n + j];
-    const double* f = feat + (size_t(hd) * n + j) * R;
-    const double* c = cent + (size_t(hd) * C + lab) * R;
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const double tdiff = f[e] - c[e];
-      dist = fma(tdiff, tdiff, dist);
-    }
     int* lp = labels + size_t(hd) * n + j;
     changed = (*lp != lab);
     *lp = lab;
@@ -385,7 +375,8 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
   const int wbase = blockIdx.x * 256 + (threadIdx.x & ~63);
   const int L = valid ? lab : -1;
   int cur = __shfl(L, 0);
-  double acc = 0.0;
+  double acc = 0.0, jsq = 0.0;
+  double cc = (lane < R && cur >= 0) ? cent[(size_t(hd) * C + cur) * R + lane] : 0.0;
   int run = 0;
   for (int p = 0; p < 64; ++p) {
     const int Lp = __shfl(L, p);
@@ -396,15 +387,21 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
       acc = 0.0;
       run = 0;
       cur = Lp;
+      if (lane < R) cc = cent[(size_t(hd) * C + cur) * R + lane];
     }
-    if (lane < R) acc += feat[(size_t(hd) * n + wbase + p) * R + lane];
+    if (lane < R) {
+      const double x = feat[(size_t(hd) * n + wbase + p) * R + lane];
+      acc += x;
+      const double t = x - cc;
+      jsq = fma(t, t, jsq);
+    }
     ++run;
   }
   if (run > 0) {
     if (lane < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + lane, acc);
     if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
   }
-  const double jsum = block_sum_d(dist, red);
+  const double jsum = block_sum_d(jsq, red);
   const int64_t csum = block_sum_i64(changed, redi);
   if (threadIdx.x == 0) {
     jpart[size_t(hd) * nblk + blockIdx.x] = jsum;
@@ -412,14 +409,12 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
   }
 }
 
-// Stopping rule, centre update and the fp16 split of the updated centres.
-__global__ __launch_bounds__(1024) void km_finalize_kernel(int C, int r, int max_iters, double tol, int nblk,
-                                                          const double* __restrict__ jpart,
-                                                          const int* __restrict__ cpart, double* __restrict__ cent,
-                                                          double* __restrict__ sums, int* __restrict__ cnt,
-                                                          double* __restrict__ ctrl, const double* __restrict__ mu,
-                                                          _Float16* __restrict__ ch, _Float16* __restrict__ cl,
-                                                          float* __restrict__ cn2, int* __restrict__ rq_count) {
+// Stopping rule after a pass (one block per head): stop when the labels did not change, when
+// the cost fell by at most tol relative to the previous pass, or at max_iters.  The decision is
+// written to ctrl[C_STOPNOW]; km_update_kernel then moves the centres of heads that go on.
+__global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double tol, int nblk,
+                                                        const double* __restrict__ jpart,
+                                                        const int* __restrict__ cpart, double* __restrict__ ctrl) {
   __shared__ double red[32];
   __shared__ int64_t redi[32];
   const int hd = blockIdx.x;
@@ -432,24 +427,60 @@ __global__ __launch_bounds__(1024) void km_finalize_kernel(int C, int r, int max
   }
   const double J = block_sum_d(js, red);
   const int64_t chg = block_sum_i64(cs, redi);
-  const int passes = int(ctrl[hd * CTRL + C_PASSES]) + 1;
-  const double Jprev = ctrl[hd * CTRL + C_JPREV];
-  const bool stop = (passes > 1 && (chg == 0 || Jprev - J <= tol * Jprev)) || passes >= max_iters;
-  __shared__ double n2s[1024];
-  for (int idx = threadIdx.x; idx < C * r; idx += blockDim.x) {
-    const int m = idx / r;
-    const int k = cnt[size_t(hd) * C + m];
-    if (!stop && k > 0) cent[size_t(hd) * C * r + idx] = sums[size_t(hd) * C * r + idx] / double(k);
-    sums[size_t(hd) * C * r + idx] = 0.0;
-  }
-  __syncthreads();
-  for (int m = threadIdx.x; m < C; m += blockDim.x) cnt[size_t(hd) * C + m] = 0;
-  if (!stop) prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, n2s, red);
   if (threadIdx.x == 0) {
-    ctrl[hd * CTRL + C_DONE] = stop ? 1.0 : 0.0;
+    const int passes = int(ctrl[hd * CTRL + C_PASSES]) + 1;
+    const double Jprev = ctrl[hd * CTRL + C_JPREV];
+    const bool stop = (passes > 1 && (chg == 0 || Jprev - J <= tol * Jprev)) || passes >= max_iters;
+    ctrl[hd * CTRL + C_STOPNOW] = stop ? 1.0 : 0.0;
     ctrl[hd * CTRL + C_PASSES] = double(passes);
     ctrl[hd * CTRL + C_JPREV] = J;
+    ctrl[hd * CTRL + C_CMAX] = 0.0;
+  }
+}
+
+// Centre update (members' mean; empty centres stay), reset of the sums, and the fp16 split of
+// the new centres for the next screening pass.  64 centres per block, one wave per centre row
+// at a time; the largest centre norm is combined with atomicMax on its (non-negative) bits.
+__global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __restrict__ cent,
+                                                        double* __restrict__ sums, int* __restrict__ cnt,
+                                                        double* __restrict__ ctrl, const double* __restrict__ mu,
+                                                        _Float16* __restrict__ ch, _Float16* __restrict__ cl,
+                                                        float* __restrict__ cn2, int* __restrict__ rq_count) {
+  const int hd = blockIdx.y;
+  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  const bool stop = ctrl[hd * CTRL + C_STOPNOW] != 0.0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double sc = ctrl[hd * CTRL + C_SCALE];
+  double cmax = 0.0;
+  for (int m = blockIdx.x * 64 + w; m < min(C, blockIdx.x * 64 + 64); m += 4) {
+    const size_t base = (size_t(hd) * C + m);
+    const int k = cnt[base];
+    double x = 0.0;
+    if (lane < r) {
+      double c = cent[base * r + lane];
+      if (!stop && k > 0) {
+        c = sums[base * r + lane] / double(k);
+        cent[base * r + lane] = c;
+      }
+      sums[base * r + lane] = 0.0;
+      x = (c - mu[size_t(hd) * RP + lane]) * sc;
+    }
+    if (!stop) {
+      const _Float16 h = _Float16(float(x));
+      ch[base * RP + lane] = h;
+      cl[base * RP + lane] = _Float16(float(x - double(h)));
+      const double n2 = wave_sum_d(x * x);
+      if (lane == 0) cn2[base] = float(n2);
+      cmax = fmax(cmax, sqrt(n2));
+    }
+    if (lane == 0) cnt[base] = 0;
+  }
+  if (!stop && lane == 0 && cmax > 0.0)
+    atomicMax(reinterpret_cast<unsigned long long*>(ctrl + hd * CTRL + C_CMAX),
+              (unsigned long long)__double_as_longlong(cmax));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     rq_count[hd] = 0;
+    if (stop) ctrl[hd * CTRL + C_DONE] = 1.0;
   }
 }
 
@@ -526,12 +557,14 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
   allow_lds(km_screen_kernel<KS>, sm);
   hipLaunchKernelGGL(km_screen_kernel<KS>, dim3(ceil_div(a.n, 256), a.BH), dim3(256), sm, st, a.n, a.C, xh, xl, a.xnrm,
                      ch, cl, a.cn2, a.ctrl, a.lab_new, a.rq_count, a.rq_list);
-  hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(64, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
+  hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(16, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
                      a.rq_count, a.rq_list, a.lab_new);
   hipLaunchKernelGGL(km_accum_kernel<R>, dim3(a.nblk, a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent, a.lab_new,
                      a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
-  hipLaunchKernelGGL(km_finalize_kernel, dim3(a.BH), dim3(1024), 0, st, a.C, a.r, a.max_iters, a.tol, a.nblk, a.jpart,
-                     a.cpart, a.cent, a.sums, a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
+  hipLaunchKernelGGL(km_decide_kernel, dim3(a.BH), dim3(256), 0, st, a.max_iters, a.tol, a.nblk, a.jpart, a.cpart,
+                     a.ctrl);
+  hipLaunchKernelGGL(km_update_kernel, dim3(ceil_div(a.C, 64), a.BH), dim3(256), 0, st, a.C, a.r, a.cent, a.sums,
+                     a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
 }
 
 spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
