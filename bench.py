@@ -11,6 +11,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -21,6 +22,24 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_mid_counters.txt")
+ATTN_SOURCE = os.path.join(ROOT, "free_block_sparse_sampled_amd", "csrc", "attention.hip")
+
+
+def measured_traffic(cfg_name):
+    """HBM-side bytes per sparse-attention launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when that summary is for another workload or another version of the kernel source."""
+    import hashlib
+    if cfg_name != "mid" or not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    sha = re.search(r"attention\.hip sha1 ([0-9a-f]{40})", text)
+    val = re.search(r"sparse attention traffic per launch: ([0-9.e+]+) bytes", text)
+    if not sha or not val:
+        return None
+    if hashlib.sha1(open(ATTN_SOURCE, "rb").read()).hexdigest() != sha.group(1):
+        return None
+    return float(val.group(1))
 
 
 def parse():
@@ -164,7 +183,7 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
         "roofline": {"kernel": "attn_mfma_kernel<128, sparse> (sparsepr_attn_sparse)", "bound": "mfma",
                      "achieved": round(sparse_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
                      "work": "4*d flops per routed query-key pair, pairs summed over heads"},
     }
     status = op.head_status.cpu().numpy()

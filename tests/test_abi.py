@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: libsparsepr loads, exports every function include/sparsepr.h declares,
+and its host-side validation answers before any device work (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import free_block_sparse_sampled_amd as spr
+from free_block_sparse_sampled_amd import sparsepr as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsepr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsepr_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libsparsepr.so is not built")
+    return spr.library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small")]:
+        assert lib.sparsepr_status_string(code) == text
+    assert lib.sparsepr_status_string(99) == b"unknown status"
+
+
+def _desc(N=4096, d=128, dtype=B.SPR_BF16, n_text=0, H=2):
+    return B.spr_desc(B=1, H=H, N=N, d=d, n_text=n_text, dtype=dtype, sb=H * N * d, sh=N * d, sn=d)
+
+
+def _params(Ck=64, Cq=64, rK=48, rQ=64):
+    return B.spr_part_params(Ck=Ck, Cq=Cq, rK=rK, rQ=rQ, Ms=256, max_iters=25, tol=1e-4, rms_eps=1e-6,
+                             eig_clamp=1e-6, seed=0)
+
+
+def test_workspace_size_validates_and_grows(lib):
+    d, p = _desc(), _params()
+    small = lib.sparsepr_workspace_size(ctypes.byref(d), ctypes.byref(p), 64)
+    big = lib.sparsepr_workspace_size(ctypes.byref(_desc(N=8192)), ctypes.byref(p), 64)
+    assert 0 < small < big
+    assert small % 256 == 0
+    bad = [(_desc(d=96), p), (_desc(dtype=7), p), (_desc(n_text=4095), p), (d, _params(Ck=2000)),
+           (d, _params(rK=0)), (d, _params(rQ=129))]
+    for dd, pp in bad:
+        assert lib.sparsepr_workspace_size(ctypes.byref(dd), ctypes.byref(pp), 64) == 0
+    assert lib.sparsepr_workspace_size(None, ctypes.byref(p), 64) == 0
+
+
+def test_kmeans_workspace_size_limits(lib):
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 48, 64) > 0
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 48, 1025) == 0  # C above the supported 1024
+    assert lib.sparsepr_kmeans_workspace_size(2, 10, 48, 11) == 0      # more centres than points
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 65, 64) == 0    # rank above 64
+
+
+def test_entry_points_reject_invalid_arguments_on_the_host(lib):
+    d, p = _desc(), _params()
+    part, route = B.spr_partition(), B.spr_route()
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails before any device work
+    assert lib.sparsepr_partition(None, dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(part), dummy, 0, None) == 1
+    # required partition outputs missing
+    assert lib.sparsepr_partition(ctypes.byref(d), dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(part), dummy,
+                                  1 << 40, None) == 1
+    # unsupported head dimension
+    assert lib.sparsepr_attn_dense(ctypes.byref(_desc(d=80)), dummy, dummy, dummy, dummy, 0, None) == 2
+    assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 5, None) == 2
+    # probes: M must lie in [1, Nv)
+    assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, dummy, dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 4096, dummy, dummy, 1 << 40,
+                                    None) == 1
+    # probe workspace too small
+    assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 64, dummy, dummy, 16, None) == 3
+    # route: density target out of range, and a budget below one key (rho*N^2 <= M*N)
+    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 1.5, 64, ctypes.byref(route),
+                              dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 64 / 4096, 64,
+                              ctypes.byref(route), dummy, 1 << 40, None) == 1
+    # fit: negative lambda, then zero std_eps
+    args = (ctypes.byref(part), ctypes.byref(route), dummy, dummy, 64)
+    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, -1.0, 1e-6, dummy, 1, None, dummy,
+                                    dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, 1.0, 0.0, dummy, 1, None, dummy,
+                                    dummy, 1 << 40, None) == 1
+    # k-means helper: stage outside {0, 1}, rank not built
+    assert lib.sparsepr_kmeans(1, 100, 48, 8, dummy, 0, 2, 25, 1e-4, dummy, dummy, dummy, dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_kmeans(1, 100, 20, 8, dummy, 0, 0, 25, 1e-4, dummy, dummy, dummy, dummy, 1 << 40, None) == 2
+    # workspace smaller than required
+    ws_need = lib.sparsepr_workspace_size(ctypes.byref(d), ctypes.byref(p), 1)
+    assert lib.sparsepr_attn_sparse(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), ctypes.byref(route), dummy,
+                                    dummy, ws_need - 1, None) == 3
