@@ -47,6 +47,9 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.fitW = take(BH * Mm * 8);
   L.applyB = take(BH * d * d * 4);
   L.applyC = take(BH * d * 4);
+  L.tmax = sparse_tile_capacity(p.Cq, int(Nv), desc.n_text);
+  L.tiles = take(BH * size_t(L.tmax) * 8 * 4);
+  L.ntiles = take(BH * 4);
   L.total = o;
   return L;
 }
@@ -63,6 +66,12 @@ static spr_status check_desc(const spr_desc* d) {
   if (d->sn < d->d || d->sh < 1 || d->sb < 1) return SPR_EINVAL;
   if ((d->sn * es) % 16 || (d->sh * es) % 16 || (d->sb * es) % 16) return SPR_EINVAL;
   return SPR_OK;
+}
+
+// The attention kernels address one head's rows with 32-bit byte offsets.
+static bool head_fits_32bit(const spr_desc* d) {
+  const int64_t es = d->dtype == SPR_BF16 ? 2 : 4;
+  return (int64_t(d->N) - 1) * d->sn * es + int64_t(d->d) * es < (int64_t(1) << 31);
 }
 
 static spr_status check_params(const spr_desc* d, const spr_part_params* p) {
@@ -127,6 +136,7 @@ spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k
   for (const void* p : req)
     if (!p) return SPR_EINVAL;
   if (!aligned16(out->Qp) || !aligned16(out->Kp) || !aligned16(out->Vp)) return SPR_EINVAL;
+  if (int64_t(desc->N) * desc->d * 4 >= (int64_t(1) << 31)) return SPR_EUNSUPPORTED;
   Workspace L;
   if ((s = check_ws(desc, params, 1, ws, ws_bytes, &L)) != SPR_OK) return s;
   return run_partition(*desc, q, k, v, *params, *out, ws, L, static_cast<hipStream_t>(stream));
@@ -144,7 +154,7 @@ spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, c
   if (!(rho_exec_target > 0.0) || rho_exec_target > 1.0) return SPR_EINVAL;
   const int64_t Tk = key_budget(rho_exec_target, desc->N, Nv, M, desc->n_text);
   if (Tk < 1) return SPR_EINVAL;
-  if (!out->sel_cnt || !out->sel_kv || !out->tile_off || !out->probe_idx || !out->probe_w || !out->pairs ||
+  if (!out->sel_cnt || !out->sel_kv || !out->probe_idx || !out->probe_w || !out->pairs ||
       !out->rho_exec)
     return SPR_EINVAL;
   Workspace L;
@@ -169,6 +179,7 @@ spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void*
   spr_status s = check_desc(desc);
   if (s != SPR_OK) return s;
   if (!q || !k || !v || !probe_idx || !o_probe || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
+  if (!head_fits_32bit(desc)) return SPR_EUNSUPPORTED;
   const int Nv = desc->N - desc->n_text;
   if (M < 1 || M >= Nv) return SPR_EINVAL;
   // the probe stage only needs the split-K partial buffer, sized by (BH, M, d)
@@ -205,6 +216,7 @@ spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* 
   if (s != SPR_OK) return s;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
   if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
+  if (!head_fits_32bit(desc)) return SPR_EUNSUPPORTED;
   return run_attn_dense(*desc, q, k, v, out, out_dtype, static_cast<hipStream_t>(stream));
 }
 

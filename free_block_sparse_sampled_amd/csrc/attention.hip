@@ -1,18 +1,22 @@
 // Flash-style attention kernels for the SparsePR operator on gfx950.
 //
 //  - block-sparse (Eq. (2) of "Partition the Support, Reconstruct the Residual", Sec. 3;
-//    execution as in Sec. 4.3): one block per 64-row tile of a query group, keys streamed
-//    from the concatenation of the group's selected K/V groups (ragged lengths, only the
-//    last 64-key chunk is partial), row-wise renormalised online softmax;
+//    execution as in Sec. 4.3).  A block holds two halves of up to 64 query rows.  A query
+//    group with more than 64 rows fills both halves of its blocks; smaller groups are paired,
+//    and the block streams the union of the two groups' selected K/V groups (groups selected
+//    by both halves first, then those of one half only), each half skipping or masking keys it
+//    did not select.  Either way every K/V chunk staged in LDS serves up to 128 query rows,
+//    which is what bounds the kernel: with 64 rows per fetch it is limited by the traffic of
+//    re-fetching K/V, not by the MFMA pipe.
 //  - dense (Eq. (1)): the same kernel over one segment holding every key;
 //  - probe rows (Sec. 4.2): gathered query rows against a contiguous key range (split-K),
 //    partial (max, sum, unnormalised output) merged by a second kernel.
 //
 // bf16 inputs use MFMA: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (exact products, fp32
-// sums), P rounded to fp16 and O^T += V^T P^T with v_mfma_f32_16x16x32_f16 (V converted from
-// bf16 to fp16 while it is staged, transposed, into LDS).  Computing the transposes puts a
-// query row's scores and its output columns in the same lane, so the softmax rescaling needs
-// no cross-lane traffic.  fp32 inputs use a plain VALU kernel.
+// sums), P rounded to fp16 and O^T += V^T P^T with v_mfma_f32_16x16x32_f16 (V staged,
+// transposed, into LDS as fp16).  Computing the transposes puts a query row's scores and its
+// output columns in the same lane, so the softmax rescaling needs no cross-lane traffic.
+// fp32 inputs use a plain VALU kernel.
 #include <type_traits>
 
 #include "common.hpp"
@@ -28,7 +32,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 enum { MODE_SPARSE = 0, MODE_DENSE = 1, MODE_PROBE = 2 };
 
 constexpr int kChunk = 64;     // keys per LDS chunk
-constexpr int kTileRows = 64;  // query rows per block (4 waves x 16)
+constexpr int kTileRows = 64;  // query rows per block of the fp32 kernel and the probe kernel
+constexpr int kSegCap = 1040;  // segment table capacity (>= Ck + 1 groups)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnParams {
@@ -38,9 +43,9 @@ struct AttnParams {
   const void* v;
   HeadGeom g;
   // sparse routing
-  const int* tile_off;   // [BH][Cq+2]
-  const int* q_off;      // [BH][Cq+1]
-  const int* n_q;
+  const int* tiles;      // [BH][tmax][8]: a0, row0, n0, a1, row1, n1 (row0 / row1 index Qp rows)
+  const int* ntiles;     // [BH]
+  int tmax;
   const int* n_kv;
   const int* kv_off;     // [BH][Ck+1]
   const int* sel_cnt;    // [BH][Cq+1]
@@ -54,7 +59,6 @@ struct AttnParams {
   float* o_sp;           // SPARSE: [BH][N][d]
   void* out;             // DENSE: [BH][N][d] contiguous
   int out_dtype;
-  int v_f16;             // v holds fp16 values (group-major fp16 copy of the values)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -62,10 +66,11 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_ca
 // ------------------------------------------------------------------ tile geometry
 struct TileInfo {
   int hd;
-  int row0, nrows;  // rows [row0, row0 + nrows) of the query source (SPARSE / DENSE)
-  int a;            // query group (SPARSE); probe tile base (PROBE)
-  int key0, key1;   // DENSE / PROBE key range
+  int a0, row0, n0;  // half 0 (the only half of DENSE / PROBE tiles): query group, first row, rows
+  int a1, row1, n1;  // half 1 (SPARSE)
+  int key0, key1;    // DENSE / PROBE key range
   int split;
+  bool pair;         // SPARSE: the halves hold two different query groups
   bool valid;
 };
 
@@ -77,40 +82,24 @@ __device__ inline TileInfo decode_tile(const AttnParams& P) {
   t.split = 0;
   t.key0 = 0;
   t.key1 = P.g.N;
-  t.a = 0;
+  t.a0 = t.a1 = 0;
+  t.row1 = t.n1 = 0;
+  t.pair = false;
   if constexpr (MODE == MODE_SPARSE) {
-    const int hd = t.hd;
-    const int nq = P.n_q[hd];
-    const int ngt = nq + (P.g.n_text > 0 ? 1 : 0);
-    const int* to = P.tile_off + size_t(hd) * (P.Cq + 2);
-    const int tid = blockIdx.x;
-    if (tid >= to[ngt]) {
+    if (int(blockIdx.x) >= P.ntiles[t.hd]) {
       t.valid = false;
       return t;
     }
-    int lo = 0, hi = ngt - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (to[mid] <= tid) lo = mid; else hi = mid - 1;
-    }
-    t.a = lo;
-    const int ti = tid - to[lo];
-    int g0, g1;
-    if (lo < nq) {
-      g0 = P.q_off[size_t(hd) * (P.Cq + 1) + lo];
-      g1 = P.q_off[size_t(hd) * (P.Cq + 1) + lo + 1];
-    } else {
-      g0 = P.g.Nv;
-      g1 = P.g.N;
-    }
-    t.row0 = g0 + ti * ROWS;
-    t.nrows = min(ROWS, g1 - t.row0);
+    const int* td = P.tiles + (size_t(t.hd) * P.tmax + blockIdx.x) * 8;
+    t.a0 = td[0]; t.row0 = td[1]; t.n0 = td[2];
+    t.a1 = td[3]; t.row1 = td[4]; t.n1 = td[5];
+    t.pair = t.n1 > 0 && t.a1 != t.a0;
   } else if constexpr (MODE == MODE_DENSE) {
     t.row0 = blockIdx.x * ROWS;
-    t.nrows = min(ROWS, P.g.N - t.row0);
+    t.n0 = min(ROWS, P.g.N - t.row0);
   } else {
     t.row0 = blockIdx.x * ROWS;  // probe slots
-    t.nrows = min(ROWS, P.M - t.row0);
+    t.n0 = min(ROWS, P.M - t.row0);
     t.split = blockIdx.z;
     const int64_t N = P.g.N;
     t.key0 = int(N * t.split / P.splits);
@@ -119,122 +108,199 @@ __device__ inline TileInfo decode_tile(const AttnParams& P) {
   return t;
 }
 
-// Build the segment table (start row and cumulative length) of a sparse tile's keys.
-// Returns the total number of keys.
-__device__ inline int build_segments(const AttnParams& P, const TileInfo& t, int* seg_start, int* seg_cum,
-                                     int* scan) {
-  const int hd = t.hd;
-  const int cnt = P.sel_cnt[size_t(hd) * (P.Cq + 1) + t.a];
-  const int* sel = P.sel_kv + (size_t(hd) * (P.Cq + 1) + t.a) * (P.Ck + 1);
-  const int* off = P.kv_off + size_t(hd) * (P.Ck + 1);
-  const int nkv = P.n_kv[hd];
-  const int per = (cnt + blockDim.x - 1) / blockDim.x;
+// Length of K/V group b of head hd (the text group when b == n_kv) and its first row in Kp.
+__device__ __forceinline__ void kv_group(const AttnParams& P, const int* off, int nkv, int b, int* s, int* l) {
+  if (b < nkv) {
+    *s = off[b];
+    *l = off[b + 1] - off[b];
+  } else {
+    *s = P.g.Nv;
+    *l = P.g.n_text;
+  }
+}
+
+// Lengths in seg_cum[0..nseg) -> exclusive prefix, total in seg_cum[nseg]; returns the total.
+__device__ inline int prefix_lengths(int* seg_cum, int nseg, int* scan) {
+  const int per = (nseg + blockDim.x - 1) / blockDim.x;
   const int i0 = threadIdx.x * per;
   int local = 0;
-  for (int i = i0; i < min(i0 + per, cnt); ++i) {
-    const int b = sel[i];
-    int s, l;
-    if (b < nkv) {
-      s = off[b];
-      l = off[b + 1] - s;
-    } else {
-      s = P.g.Nv;
-      l = P.g.n_text;
-    }
-    seg_start[i] = s;
-    seg_cum[i] = l;  // temporarily the length
-    local += l;
-  }
+  for (int i = i0; i < min(i0 + per, nseg); ++i) local += seg_cum[i];
   int total;
   int run = block_exscan_i(local, scan, &total);
-  for (int i = i0; i < min(i0 + per, cnt); ++i) {
+  for (int i = i0; i < min(i0 + per, nseg); ++i) {
     const int l = seg_cum[i];
     seg_cum[i] = run;
     run += l;
   }
-  if (threadIdx.x == 0) seg_cum[cnt] = total;
+  if (threadIdx.x == 0) seg_cum[nseg] = total;
   __syncthreads();
   return total;
 }
 
-__device__ __forceinline__ int seg_row(const int* seg_start, const int* seg_cum, int cnt, int pos) {
+// Segment table of one query group's selected K/V groups, in selection order (fp32 kernel).
+__device__ inline int build_segments(const AttnParams& P, int hd, int a, int* seg_start, int* seg_cum, int* scan,
+                                     int* nseg) {
+  const int cnt = P.sel_cnt[size_t(hd) * (P.Cq + 1) + a];
+  const int* sel = P.sel_kv + (size_t(hd) * (P.Cq + 1) + a) * (P.Ck + 1);
+  const int* off = P.kv_off + size_t(hd) * (P.Ck + 1);
+  const int nkv = P.n_kv[hd];
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) kv_group(P, off, nkv, sel[i], seg_start + i, seg_cum + i);
+  __syncthreads();
+  *nseg = cnt;
+  return prefix_lengths(seg_cum, cnt, scan);
+}
+
+// Segment table of a sparse tile: every K/V group selected by either half, as runs of Kp rows
+// with cumulative key counts and a 2-bit mask of the halves that selected them (bit h: half h).
+// Groups selected by both halves come first, then half 0 alone, then half 1 alone, each run in
+// ascending group id.  Returns the total number of keys.
+__device__ inline int build_union_segments(const AttnParams& P, const TileInfo& t, int* seg_start, int* seg_cum,
+                                           int* seg_cat, unsigned* bm /* [2][33] */, int* scan, int* nseg_out) {
+  const int hd = t.hd;
+  const int nkv = P.n_kv[hd];
+  const int ng = nkv + (P.g.n_text > 0 ? 1 : 0);
+  for (int i = threadIdx.x; i < 66; i += blockDim.x) bm[i] = 0u;
+  __syncthreads();
+  const int nh = t.pair ? 2 : 1;
+  for (int h = 0; h < nh; ++h) {
+    const size_t row = size_t(hd) * (P.Cq + 1) + (h ? t.a1 : t.a0);
+    const int cnt = P.sel_cnt[row];
+    const int* sel = P.sel_kv + row * (P.Ck + 1);
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+      const int b = sel[i];
+      atomicOr(bm + h * 33 + (b >> 5), 1u << (b & 31));
+    }
+  }
+  __syncthreads();
+  auto cat_of = [&](int b) -> int {
+    const unsigned bit = 1u << (b & 31);
+    const int in0 = (bm[b >> 5] & bit) ? 1 : 0;
+    const int in1 = t.pair ? ((bm[33 + (b >> 5)] & bit) ? 1 : 0) : in0;
+    return in0 | (in1 << 1);
+  };
+  const int per = (ng + blockDim.x - 1) / blockDim.x;
+  const int i0 = threadIdx.x * per;
+  int c3 = 0, c1 = 0, c2 = 0;
+  for (int b = i0; b < min(i0 + per, ng); ++b) {
+    const int c = cat_of(b);
+    c3 += c == 3;
+    c1 += c == 1;
+    c2 += c == 2;
+  }
+  // three counts (each <= 1025) packed in 11-bit fields share one scan
+  int tot;
+  const int ex = block_exscan_i(c3 | (c1 << 11) | (c2 << 22), scan, &tot);
+  const int n3 = tot & 0x7ff, n1 = (tot >> 11) & 0x7ff, n2 = (tot >> 22) & 0x7ff;
+  int o3 = ex & 0x7ff, o1 = n3 + ((ex >> 11) & 0x7ff), o2 = n3 + n1 + ((ex >> 22) & 0x7ff);
+  const int* off = P.kv_off + size_t(hd) * (P.Ck + 1);
+  for (int b = i0; b < min(i0 + per, ng); ++b) {
+    const int c = cat_of(b);
+    if (c == 0) continue;
+    const int pos = c == 3 ? o3++ : c == 1 ? o1++ : o2++;
+    kv_group(P, off, nkv, b, seg_start + pos, seg_cum + pos);
+    seg_cat[pos] = c;
+  }
+  __syncthreads();
+  *nseg_out = n3 + n1 + n2;
+  return prefix_lengths(seg_cum, n3 + n1 + n2, scan);
+}
+
+__device__ __forceinline__ int seg_find(const int* seg_cum, int cnt, int pos) {
   int lo = 0, hi = cnt - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (seg_cum[mid] <= pos) lo = mid; else hi = mid - 1;
   }
-  return seg_start[lo] + (pos - seg_cum[lo]);
+  return lo;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 // WAVES waves of 16 query rows share each 64-key chunk staged in LDS (K as bf16 rows, V
 // transposed to fp16).  The global loads of chunk c+1 are issued into registers before the
-// MFMAs of chunk c, and the row indices of chunk c+1 are resolved meanwhile, so memory latency
-// overlaps compute.  Only the final chunk is masked.  The running maximum used for the
+// MFMAs of chunk c, and the rows of chunk c+1 (with, for sparse tiles, a 64-bit mask per half
+// of the keys that half selected) are resolved meanwhile, so memory latency overlaps compute.
+// Full chunks run unmasked, empty ones are skipped.  The running maximum used for the
 // exponentials is raised lazily: O and l are rescaled only when a row's maximum grows by more
 // than 2^8, which keeps p <= 256 (exact range in fp16) and skips most rescales.
-template <int D, int MODE, int WAVES, int RS, bool VF16>
+template <int D, int MODE, int WAVES, bool VF16>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnParams P) {
+  constexpr bool SPARSE = MODE == MODE_SPARSE;
   constexpr int NTH = WAVES * 64;
-  constexpr int ROWS = WAVES * 16 * RS;
+  constexpr int HW = SPARSE ? WAVES / 2 : WAVES;  // waves per row half
+  constexpr int ROWS = WAVES * 16;
   constexpr int KS = D + 8;       // Ks row stride (bf16 elements)
   constexpr int VS = kChunk + 8;  // Vt row stride (fp16 elements; 16-byte aligned rows)
   constexpr int NT = D / 16;
   constexpr int KSTEPS = D / 32;
   constexpr int KPIECES = kChunk * (D / 8);              // 16-byte pieces of a K chunk
   constexpr int VITEMS = (kChunk / 4) * (D / 8);         // 4 keys x 8 columns items of a V chunk
-  constexpr int KPT = (KPIECES + NTH - 1) / NTH;         // per thread
-  constexpr int VPT = (VITEMS + NTH - 1) / NTH;
+  // threads [0, VTH) stage V (VPT items each), threads [VTH, NTH) stage K (up to KPT pieces each)
+  constexpr int VPT = (VITEMS + NTH / 2 - 1) / (NTH / 2);
+  constexpr int VTH = VITEMS / VPT;
+  constexpr int KPT = (KPIECES + (NTH - VTH) - 1) / (NTH - VTH);
+  constexpr int KTH = KPIECES / KPT;  // threads [VTH, VTH + KTH) stage K
+  constexpr int NPRE = 4 * VPT > KPT ? 4 * VPT : KPT;  // 16-byte registers per stage
+  static_assert(VTH * VPT == VITEMS && VTH % 64 == 0, "staging split (V)");
+  static_assert(KTH * KPT == KPIECES && KTH % 64 == 0 && VTH + KTH <= NTH, "staging split (K)");
   constexpr float kRescale = 8.0f;                       // lazy rescale threshold (log2 units)
+  static_assert(!SPARSE || HW * 16 == kHalfRows, "a sparse tile half is kHalfRows rows");
+  constexpr int KBUF = kChunk * KS;  // bf16 elements of one K buffer
+  constexpr int VBUF = D * VS;       // fp16 elements of one V buffer
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_raw);
-  _Float16* Vt = reinterpret_cast<_Float16*>(smem_raw + kChunk * KS * 2);
-  int* rowidx = reinterpret_cast<int*>(smem_raw + kChunk * KS * 2 + D * VS * 2);  // [2][kChunk]
-  int* seg_start = rowidx + 2 * kChunk;
-  int* seg_cum = seg_start + (MODE == MODE_SPARSE ? 1040 : 0);
-  int* scan = seg_cum + (MODE == MODE_SPARSE ? 1040 : 0);
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_raw);                    // [2][KBUF]
+  _Float16* Vt = reinterpret_cast<_Float16*>(smem_raw + 2 * KBUF * 2);     // [3][VBUF]
+  int* rowidx = reinterpret_cast<int*>(smem_raw + 2 * KBUF * 2 + 3 * VBUF * 2);  // [8][kChunk]
+  unsigned long long* cmask = reinterpret_cast<unsigned long long*>(rowidx + 8 * kChunk);  // [8][2]
+  int* seg_start = reinterpret_cast<int*>(cmask + 16);
+  int* seg_cum = seg_start + (SPARSE ? kSegCap : 0);
+  int* seg_cat = seg_cum + (SPARSE ? kSegCap : 0);
+  unsigned* bm = reinterpret_cast<unsigned*>(seg_cat + (SPARSE ? kSegCap : 0));
+  int* scan = reinterpret_cast<int*>(bm + (SPARSE ? 66 : 0));
 
   const TileInfo t = decode_tile<MODE, ROWS>(P);
-  if (!t.valid || t.nrows <= 0) return;
+  if (!t.valid || t.n0 <= 0) return;
   const int hd = t.hd;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
+  const int half = SPARSE ? w / HW : 0;
+  const int my_row0 = half ? t.row1 : t.row0;
+  const int my_n = half ? t.n1 : t.n0;
+  const int qslot = (w % HW) * 16 + r16;
 
+  // K and V rows of the head are read through buffer resources with 32-bit byte offsets (the
+  // host guarantees that a head's rows span less than 2 GiB)
   const uint16_t* Kb;
   const uint16_t* Vb;
-  int64_t krs;
-  if constexpr (MODE == MODE_SPARSE) {
+  int row_bytes;
+  if constexpr (SPARSE) {
     Kb = static_cast<const uint16_t*>(P.k) + size_t(hd) * P.g.N * D;
     Vb = static_cast<const uint16_t*>(P.v) + size_t(hd) * P.g.N * D;
-    krs = D;
+    row_bytes = D * 2;
   } else {
     Kb = static_cast<const uint16_t*>(P.k) + P.g.base(hd);
     Vb = static_cast<const uint16_t*>(P.v) + P.g.base(hd);
-    krs = P.g.sn;
+    row_bytes = int(P.g.sn) * 2;
   }
+  const int head_bytes = (P.g.N - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, head_bytes, 0x00020000);
   int nseg = 0, total;
-  if constexpr (MODE == MODE_SPARSE) {
-    nseg = P.sel_cnt[size_t(hd) * (P.Cq + 1) + t.a];
-    total = build_segments(P, t, seg_start, seg_cum, scan);
-  } else {
-    total = t.key1 - t.key0;
-  }
+  if constexpr (SPARSE) total = build_union_segments(P, t, seg_start, seg_cum, seg_cat, bm, scan, &nseg);
+  else total = t.key1 - t.key0;
   const int nchunks = (total + kChunk - 1) / kChunk;
 
-  // query fragments: for row-set rs the lane holds row r16 of 16 rows, dims ks*32 + 8g .. +7
-  bf16x8_t qf[RS][KSTEPS];
-#pragma unroll
-  for (int rs = 0; rs < RS; ++rs) {
-    const int qslot = (w * RS + rs) * 16 + r16;
-    const bool qvalid = qslot < t.nrows;
+  // query fragments: the lane holds row r16 of the wave's 16 rows, dims ks*32 + 8g .. +7
+  bf16x8_t qf[KSTEPS];
+  const bool qvalid = qslot < my_n;
+  {
     const uint16_t* qrow = nullptr;
     if (qvalid) {
-      if constexpr (MODE == MODE_SPARSE) {
-        qrow = static_cast<const uint16_t*>(P.q) + (size_t(hd) * P.g.N + t.row0 + qslot) * D;
+      if constexpr (SPARSE) {
+        qrow = static_cast<const uint16_t*>(P.q) + (size_t(hd) * P.g.N + my_row0 + qslot) * D;
       } else if constexpr (MODE == MODE_DENSE) {
-        qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(t.row0 + qslot) * P.g.sn;
+        qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(my_row0 + qslot) * P.g.sn;
       } else {
-        const int pr = P.probe_idx[size_t(hd) * P.M + t.row0 + qslot];
+        const int pr = P.probe_idx[size_t(hd) * P.M + my_row0 + qslot];
         qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(pr) * P.g.sn;
       }
     }
@@ -242,68 +308,94 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (qvalid) u = *reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g);
-      qf[rs][ks] = as_bf16x8(u);
+      qf[ks] = as_bf16x8(u);
     }
   }
-  const bool wave_active = (w * RS * 16) < t.nrows;
-  const bool set1_active = RS > 1 && (w * RS * 16 + 16) < t.nrows;
+  const bool wave_active = (w % HW) * 16 < my_n;
 
-  auto key_row = [&](int pos) -> int {
-    if constexpr (MODE == MODE_SPARSE) return seg_row(seg_start, seg_cum, nseg, pos);
-    else return t.key0 + pos;
-  };
-  // row indices of chunk 0
-  if (threadIdx.x < kChunk) rowidx[threadIdx.x] = int(threadIdx.x) < min(kChunk, total) ? key_row(threadIdx.x) : -1;
-  __syncthreads();
-
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][4];
-  auto load_chunk = [&](const int* ridx) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = threadIdx.x + i * NTH;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (e < KPIECES) {
-        const int row = ridx[e / (D / 8)];
-        if (row >= 0) kreg[i] = *reinterpret_cast<const uint4*>(Kb + int64_t(row) * krs + (e % (D / 8)) * 8);
+  // Wave 0: Kp rows of chunk ch and, per half, the mask of keys that half attends to (ring of 8
+  // slots).  Chunks are resolved in increasing order, so the segment holding the chunk's first
+  // key is carried over from the previous chunk and only the segment starts inside the chunk are
+  // visited.  Keys past the end get row 0 and no mask bit.
+  int seg_cursor = 0;
+  auto resolve = [&](int ch) __attribute__((always_inline)) {
+    const int stage = ch & 7;
+    const int p0 = ch * kChunk, pos = p0 + lane;
+    int row = 0, cat = 0;
+    if constexpr (SPARSE) {
+      int sg = seg_cursor;
+      for (int k = seg_cursor + 1; k < nseg; ++k) {
+        const int start = __builtin_amdgcn_readfirstlane(seg_cum[k]);
+        if (start > p0 + kChunk) break;
+        if (pos >= start) sg = k;
+        seg_cursor = k;
+      }
+      if (pos < total) {
+        row = seg_start[sg] + (pos - seg_cum[sg]);
+        cat = seg_cat[sg];
+      }
+    } else {
+      if (pos < total) {
+        row = t.key0 + pos;
+        cat = 3;
       }
     }
+    rowidx[stage * kChunk + lane] = row;
+    const unsigned long long m0 = __ballot(cat & 1), m1 = __ballot(cat & 2);
+    if (lane == 0) {
+      cmask[stage * 2] = m0;
+      cmask[stage * 2 + 1] = m1;
+    }
+  };
+  // Staging of one chunk in registers: threads [0, VTH) hold VPT V items (4 keys x 8 columns
+  // each), threads [VTH, VTH + KTH) hold KPT 16-byte pieces of K.  Two register sets and two LDS buffers
+  // pipeline the chunks: while chunk c is computed, chunk c+1 sits in LDS and chunks c+2, c+3
+  // are in flight.
+  const bool stages_v = threadIdx.x < VTH;
+  const int sidx = stages_v ? threadIdx.x : threadIdx.x - VTH;
+  const bool stages_k = !stages_v && sidx < KTH;
+  uint4 pre0[NPRE], pre1[NPRE];
+  // Every thread issues exactly NPRE loads per chunk on every path (roles with fewer pieces, and
+  // idle threads, load row 0 again) so that the wait before a register set is consumed counts
+  // only the loads of the other set issued after it.
+  auto load_into = [&](uint4 (&pre)[NPRE], int ch) __attribute__((always_inline)) {
+    const int* ridx = rowidx + (ch & 7) * kChunk;
+    if (stages_v) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * NTH;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vreg[i][j] = make_uint4(0, 0, 0, 0);
-      if (e < VITEMS) {
+      for (int i = 0; i < NPRE; ++i) {
+        const int it = i / 4 < VPT ? i / 4 : 0;
+        const int e = sidx + it * VTH;
         const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
+        const int off = ridx[kq * 4 + (i & 3)] * row_bytes + dq * 16;
+        pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = ridx[kq * 4 + j];
-          if (row >= 0) vreg[i][j] = *reinterpret_cast<const uint4*>(Vb + int64_t(row) * krs + dq * 8);
-        }
+      for (int i = 0; i < NPRE; ++i) {
+        const int e = stages_k ? sidx + (i < KPT ? i : 0) * KTH : 0;
+        const int off = ridx[e / (D / 8)] * row_bytes + (e % (D / 8)) * 16;
+        pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
       }
     }
   };
   // V chunk stored transposed ([column][key], fp16).  Inside each 32-key half the key k sits at
   // position 8*((k % 16) / 4) + 4*(k / 16) + k % 4, so the eight keys that lane group g feeds to
   // one P V product ({4g..4g+3} and {16+4g..16+4g+3}) are one contiguous 16-byte read.
-  auto store_chunk = [&]() {
+  auto store_out_of = [&](const uint4 (&pre)[NPRE], int kbuf, int vbuf) __attribute__((always_inline)) {
+    if (stages_v) {
+      _Float16* V = Vt + vbuf * VBUF;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = threadIdx.x + i * NTH;
-      if (e < KPIECES) *reinterpret_cast<uint4*>(Ks + (e / (D / 8)) * KS + (e % (D / 8)) * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int e = threadIdx.x + i * NTH;
-      if (e < VITEMS) {
+      for (int i = 0; i < VPT; ++i) {
+        const int e = sidx + i * VTH;
         const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
         uint32_t wv[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          const uint4 u = pre[4 * i + j];
           if constexpr (VF16) {
-            wv[j][0] = vreg[i][j].x; wv[j][1] = vreg[i][j].y; wv[j][2] = vreg[i][j].z; wv[j][3] = vreg[i][j].w;
+            wv[j][0] = u.x; wv[j][1] = u.y; wv[j][2] = u.z; wv[j][3] = u.w;
           } else {
-            const uint32_t src[4] = {vreg[i][j].x, vreg[i][j].y, vreg[i][j].z, vreg[i][j].w};
+            const uint32_t src[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const _Float16 lo = _Float16(__uint_as_float(src[c] << 16));
@@ -320,158 +412,203 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
                                       __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x05040100u));
           const uint2 hi = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x07060302u),
                                       __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x07060302u));
-          *reinterpret_cast<uint2*>(Vt + (dq * 8 + 2 * c) * VS + pos) = lo;
-          *reinterpret_cast<uint2*>(Vt + (dq * 8 + 2 * c + 1) * VS + pos) = hi;
+          *reinterpret_cast<uint2*>(V + (dq * 8 + 2 * c) * VS + pos) = lo;
+          *reinterpret_cast<uint2*>(V + (dq * 8 + 2 * c + 1) * VS + pos) = hi;
         }
+      }
+    } else if (stages_k) {
+      uint16_t* K = Ks + kbuf * KBUF;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int e = sidx + i * KTH;
+        *reinterpret_cast<uint4*>(K + (e / (D / 8)) * KS + (e % (D / 8)) * 8) = pre[i];
       }
     }
   };
 
+  auto load_to = [&](auto set, int ch) __attribute__((always_inline)) {
+    if constexpr (decltype(set)::value) load_into(pre1, ch);
+    else load_into(pre0, ch);
+  };
+  auto store_from = [&](auto set, int kbuf, int vbuf) __attribute__((always_inline)) {
+    if constexpr (decltype(set)::value) store_out_of(pre1, kbuf, vbuf);
+    else store_out_of(pre0, kbuf, vbuf);
+  };
+
   const float scale = kLog2e / sqrtf(float(D));
-  float m_run[RS];
-  f32x4_t oacc[RS][NT], lacc[RS];
+  float m_run = -INFINITY;
+  f32x4_t oacc[NT], lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rs = 0; rs < RS; ++rs) {
-    m_run[rs] = -INFINITY;
-    lacc[rs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nt = 0; nt < NT; ++nt) oacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
-  // one chunk: S^T = K Q^T, online softmax, O^T += V^T P^T; row sums come from the same fp16
-  // P through an MFMA against a tile of ones.  TAIL masks keys past the end.
-  auto compute_chunk = [&](auto tail_tag, int nvalid) {
-    constexpr bool TAIL = decltype(tail_tag)::value;
-    f32x4_t sacc[RS][4];
+  // S^T = K Q^T of one chunk
+  auto qk = [&](f32x4_t (&sacc)[4], int kbuf) __attribute__((always_inline)) {
+    const uint16_t* K = Ks + kbuf * KBUF;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int rs = 0; rs < RS; ++rs) sacc[rs][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
-        sacc[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], sacc[0][mt], 0, 0, 0);
-        if (RS > 1 && set1_active)
-          sacc[RS - 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[RS - 1][ks], sacc[RS - 1][mt], 0, 0, 0);
+        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(K + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
+        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
       }
     }
-    f16x8_t pf[RS][2];
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs) {
-      if constexpr (TAIL) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (mt * 16 + 4 * g + v >= nvalid) sacc[rs][mt][v] = -INFINITY;
-      }
-      float mx = fmaxf(fmaxf(sacc[rs][0][0], sacc[rs][0][1]), fmaxf(sacc[rs][0][2], sacc[rs][0][3]));
-#pragma unroll
-      for (int mt = 1; mt < 4; ++mt)
-        mx = fmaxf(fmaxf(mx, fmaxf(sacc[rs][mt][0], sacc[rs][mt][1])), fmaxf(sacc[rs][mt][2], sacc[rs][mt][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx *= scale;
-      const bool grow = mx > m_run[rs] + kRescale;
-      if (__builtin_expect(__any(grow), 0)) {
-        __asm__ volatile("; rare rescale of the running output" ::);
-        const float m_new = grow ? mx : m_run[rs];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rs] - m_new);
-        m_run[rs] = m_new;
-        lacc[rs] *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[rs][nt] *= alpha;
-      }
-      const float mneg = -m_run[rs];
+  };
+  // Online softmax of one chunk's scores and O^T += V^T P^T; the row sums come from the same
+  // fp16 P through an MFMA against a tile of ones.  MASKED drops the keys whose bit in m is
+  // clear.  P is formed with the running shift first; the lane's own 16 keys then decide whether
+  // anything may need rescaling, and only in that rare case is the row maximum over the four
+  // lanes of the row formed and P recomputed.
+  auto softmax_pv = [&](auto masked_tag, f32x4_t (&sacc)[4], unsigned long long m, int vbuf)
+                        __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const _Float16* V = Vt + vbuf * VBUF;
+    if constexpr (MASKED) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          pf[rs][mt >> 1][(mt & 1) * 4 + v] = _Float16(__builtin_amdgcn_exp2f(fmaf(sacc[rs][mt][v], scale, mneg)));
+          if (!((m >> (mt * 16 + 4 * g + v)) & 1ull)) sacc[mt][v] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
+#pragma unroll
+    for (int mt = 1; mt < 4; ++mt)
+      mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][0], sacc[mt][1])), fmaxf(sacc[mt][2], sacc[mt][3]));
+    mx *= scale;
+    f16x8_t pf[2];
+    auto make_p = [&]() __attribute__((always_inline)) {
+      const float mneg = -m_run;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          pf[mt >> 1][(mt & 1) * 4 + v] = _Float16(__builtin_amdgcn_exp2f(fmaf(sacc[mt][v], scale, mneg)));
+    };
+    make_p();
+    if (__builtin_expect(__any(mx > m_run + kRescale), 0)) {
+      __asm__ volatile("; rare rescale of the running output" ::);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx > m_run + kRescale;
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      lacc *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[nt] *= alpha;
+      make_p();
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[0][h], lacc[0], 0, 0, 0);
-      if (RS > 1 && set1_active)
-        lacc[RS - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[RS - 1][h], lacc[RS - 1], 0, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h) lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[h], lacc, 0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f16x8_t av = __builtin_bit_cast(
-            f16x8_t, *reinterpret_cast<const uint4*>(Vt + (nt * 16 + r16) * VS + h * 32 + 8 * g));
-        oacc[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[0][h], oacc[0][nt], 0, 0, 0);
-        if (RS > 1 && set1_active)
-          oacc[RS - 1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[RS - 1][h], oacc[RS - 1][nt], 0, 0, 0);
+            f16x8_t, *reinterpret_cast<const uint4*>(V + (nt * 16 + r16) * VS + h * 32 + 8 * g));
+        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[h], oacc[nt], 0, 0, 0);
       }
     }
   };
+  auto half_mask = [&](int c) __attribute__((always_inline)) -> unsigned long long {
+    const unsigned long long mk = cmask[(c & 7) * 2 + half];
+    const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(mk));
+    const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(mk >> 32));
+    return (static_cast<unsigned long long>(hi) << 32) | lo;
+  };
 
-  if (nchunks > 0) load_chunk(rowidx);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int cbase = ch * kChunk;
-    const int nvalid = min(kChunk, total - cbase);
-    store_chunk();
-    int* ridx_next = rowidx + ((ch + 1) & 1) * kChunk;
-    if (threadIdx.x < kChunk && ch + 1 < nchunks) {
-      const int pos = cbase + kChunk + threadIdx.x;
-      ridx_next[threadIdx.x] = pos < total ? key_row(pos) : -1;
-    }
-    __syncthreads();
-    if (ch + 1 < nchunks) load_chunk(ridx_next);
+  // Pipeline over 64-key chunks.  Chunk x is staged in register set x & 1, then in K buffer
+  // x & 1 and V buffer x % 3.  Step c computes the scores of chunk c+1 and the softmax and PV
+  // product of chunk c (whose scores step c-1 computed), stores chunk c+2 into LDS, issues the
+  // loads of chunk c+4 and resolves the rows of chunk c+5.  Loads, stores and row resolution
+  // run for chunks past the end too (rows clamp to 0, masks are empty), so no branch skips a
+  // load and every step keeps the same number of loads in flight.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (w == 0)
+    for (int c = 0; c < 5; ++c) resolve(c);
+  __syncthreads();
+  load_to(S0{}, 0);
+  load_to(S1{}, 1);
+  store_from(S0{}, 0, 0);
+  load_to(S0{}, 2);
+  store_from(S1{}, 1, 1);
+  load_to(S1{}, 3);
+  __syncthreads();
+  f32x4_t sa[4], sb[4];
+  if (wave_active && half_mask(0) != 0ull) qk(sa, 0);
+  __syncthreads();  // step 0 overwrites K buffer 0
+  auto step = [&](auto set, int c, f32x4_t (&s_cur)[4], f32x4_t (&s_nxt)[4]) __attribute__((always_inline)) {
+    store_from(set, c & 1, (c + 2) % 3);
+    load_to(set, c + 4);
+    if (w == 0) resolve(c + 5);
     if (wave_active) {
-      if (__builtin_expect(nvalid == kChunk, 1)) compute_chunk(std::false_type{}, nvalid);
-      else compute_chunk(std::true_type{}, nvalid);
+      if (half_mask(c + 1) != 0ull) qk(s_nxt, (c + 1) & 1);
+      const unsigned long long m = half_mask(c);
+      if (__builtin_expect(m == ~0ull, 1)) softmax_pv(std::false_type{}, s_cur, m, c % 3);
+      else if (m != 0ull) softmax_pv(std::true_type{}, s_cur, m, c % 3);
     }
     __syncthreads();
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    step(S0{}, c, sa, sb);
+    step(S1{}, c + 1, sb, sa);
   }
+  if (!qvalid) return;
+  const float lt = lacc[0];
+  if constexpr (MODE == MODE_PROBE) {
+    float* dst = P.part + ((size_t(hd) * P.M + my_row0 + qslot) * P.splits + t.split) * (D + 2);
 #pragma unroll
-  for (int rs = 0; rs < RS; ++rs) {
-    const int qslot = (w * RS + rs) * 16 + r16;
-    if (qslot >= t.nrows) continue;
-    const float lt = lacc[rs][0];
-    if constexpr (MODE == MODE_PROBE) {
-      float* dst = P.part + ((size_t(hd) * P.M + t.row0 + qslot) * P.splits + t.split) * (D + 2);
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) = make_float4(oacc[nt][0], oacc[nt][1], oacc[nt][2], oacc[nt][3]);
+    if (g == 0) {
+      dst[D] = m_run;
+      dst[D + 1] = lt;
+    }
+  } else {
+    const float inv = 1.f / lt;
+    if constexpr (SPARSE) {
+      float* dst = P.o_sp + (size_t(hd) * P.g.N + my_row0 + qslot) * D;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) =
-            make_float4(oacc[rs][nt][0], oacc[rs][nt][1], oacc[rs][nt][2], oacc[rs][nt][3]);
-      if (g == 0) {
-        dst[D] = m_run[rs];
-        dst[D + 1] = lt;
-      }
+            make_float4(oacc[nt][0] * inv, oacc[nt][1] * inv, oacc[nt][2] * inv, oacc[nt][3] * inv);
     } else {
-      const float inv = 1.f / lt;
-      if constexpr (MODE == MODE_SPARSE) {
-        float* dst = P.o_sp + (size_t(hd) * P.g.N + t.row0 + qslot) * D;
+      const size_t rowbase = (size_t(hd) * P.g.N + my_row0 + qslot) * D;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) = make_float4(
-              oacc[rs][nt][0] * inv, oacc[rs][nt][1] * inv, oacc[rs][nt][2] * inv, oacc[rs][nt][3] * inv);
-      } else {
-        const size_t rowbase = (size_t(hd) * P.g.N + t.row0 + qslot) * D;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const size_t idx = rowbase + nt * 16 + 4 * g + v;
-            if (P.out_dtype == SPR_BF16) store_out<SPR_BF16>(P.out, idx, oacc[rs][nt][v] * inv);
-            else store_out<SPR_F32>(P.out, idx, oacc[rs][nt][v] * inv);
-          }
-      }
+        for (int v = 0; v < 4; ++v) {
+          const size_t idx = rowbase + nt * 16 + 4 * g + v;
+          if (P.out_dtype == SPR_BF16) store_out<SPR_BF16>(P.out, idx, oacc[nt][v] * inv);
+          else store_out<SPR_F32>(P.out, idx, oacc[nt][v] * inv);
+        }
     }
   }
 }
 
 // ------------------------------------------------------------------ fp32 VALU kernel
-// One wave per 64-row tile, one lane per query row; keys are read by all lanes at once.
+// One wave per 64-row tile (for sparse tiles: one half of a tile), one lane per query row;
+// keys are read by all lanes at once.
 template <int D, int MODE>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
-  __shared__ int seg_start[1040], seg_cum[1040], scan[1024];
-  const TileInfo t = decode_tile<MODE, kTileRows>(P);
-  if (!t.valid || t.nrows <= 0) return;
+  __shared__ int seg_start[kSegCap], seg_cum[kSegCap], scan[64];
+  TileInfo t;
+  int a = 0;
+  if constexpr (MODE == MODE_SPARSE) {
+    t.hd = blockIdx.y;
+    t.key0 = 0;
+    const int tile = blockIdx.x >> 1, half = blockIdx.x & 1;
+    if (tile >= P.ntiles[t.hd]) return;
+    const int* td = P.tiles + (size_t(t.hd) * P.tmax + tile) * 8 + 3 * half;
+    a = td[0];
+    t.row0 = td[1];
+    t.n0 = td[2];
+  } else {
+    t = decode_tile<MODE, kTileRows>(P);
+  }
+  if (t.n0 <= 0) return;
   const int hd = t.hd, lane = threadIdx.x;
   const float* Kb;
   const float* Vb;
@@ -487,12 +624,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
   }
   int nseg = 0, total;
   if constexpr (MODE == MODE_SPARSE) {
-    nseg = P.sel_cnt[size_t(hd) * (P.Cq + 1) + t.a];
-    total = build_segments(P, t, seg_start, seg_cum, scan);
+    total = build_segments(P, hd, a, seg_start, seg_cum, scan, &nseg);
   } else {
     total = t.key1 - t.key0;
   }
-  const bool valid = lane < t.nrows;
+  const bool valid = lane < t.n0;
   float qv[D];
   {
     const float* qrow = nullptr;
@@ -516,8 +652,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
   for (int c = 0; c < D; ++c) o[c] = 0.f;
   for (int pos = 0; pos < total; ++pos) {
     int row;
-    if constexpr (MODE == MODE_SPARSE) row = seg_row(seg_start, seg_cum, nseg, pos);
-    else row = t.key0 + pos;
+    if constexpr (MODE == MODE_SPARSE) {
+      const int sg = seg_find(seg_cum, nseg, pos);
+      row = seg_start[sg] + (pos - seg_cum[sg]);
+    } else {
+      row = t.key0 + pos;
+    }
     const float* kr = Kb + int64_t(row) * krs;
     const float* vr = Vb + int64_t(row) * krs;
     float s = 0.f;
@@ -569,47 +709,79 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
   }
 }
 
-// ------------------------------------------------------------------ host drivers
-template <int D, int MODE>
-static size_t mfma_smem() {
-  size_t s = size_t(kChunk) * (D + 8) * 2 + size_t(D) * (kChunk + 8) * 2 + 2 * kChunk * sizeof(int);
-  if (MODE == MODE_SPARSE) s += (1040 * 2 + 1024) * sizeof(int);
-  return s;
+// ------------------------------------------------------------------ sparse tiles
+// Per head, the tile list of the block-sparse kernel: text rows first (they attend to every key,
+// so their tiles are the longest), then each query group of more than kHalfRows rows in tiles of
+// 2 kHalfRows rows, then the remaining groups paired in ascending id order.  A tile is
+// {a0, row0, n0, a1, row1, n1}: the query group, first Qp row and row count of each half.
+__global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restrict__ q_off, const int* __restrict__ n_q,
+                                                            int Cq, int Nv, int n_text, int tmax,
+                                                            int* __restrict__ tiles, int* __restrict__ ntiles) {
+  __shared__ int buf[1024];
+  const int hd = blockIdx.x, t = threadIdx.x;
+  const int nq = n_q[hd];
+  const int* qo = q_off + size_t(hd) * (Cq + 1);
+  int* out = tiles + size_t(hd) * tmax * 8;
+  constexpr int H2 = 2 * kHalfRows;
+  const int n_text_tiles = (n_text + H2 - 1) / H2;
+  int s = 0;
+  if (t < nq) s = qo[t + 1] - qo[t];
+  const bool big = t < nq && s > kHalfRows, small = t < nq && !big;
+  const int my_big_tiles = big ? (s + H2 - 1) / H2 : 0;
+  int n_big_tiles, n_small;
+  const int big_off = block_exscan_i(my_big_tiles, buf, &n_big_tiles);
+  const int small_rank = block_exscan_i(small ? 1 : 0, buf, &n_small);
+  auto put = [&](int tile, int h, int a, int row, int n) {
+    if (tile >= tmax) return;  // cannot happen: tmax bounds the count
+    int* d = out + size_t(tile) * 8 + 3 * h;
+    d[0] = a;
+    d[1] = row;
+    d[2] = n;
+  };
+  for (int k = t; k < n_text_tiles; k += blockDim.x) {
+    const int r = Nv + k * H2, n = min(H2, n_text - k * H2);
+    put(k, 0, nq, r, min(kHalfRows, n));
+    put(k, 1, nq, r + kHalfRows, max(0, n - kHalfRows));
+  }
+  if (big) {
+    for (int k = 0; k < my_big_tiles; ++k) {
+      const int r = qo[t] + k * H2, n = min(H2, s - k * H2);
+      put(n_text_tiles + big_off + k, 0, t, r, min(kHalfRows, n));
+      put(n_text_tiles + big_off + k, 1, t, r + kHalfRows, max(0, n - kHalfRows));
+    }
+  }
+  if (small) {
+    const int tile = n_text_tiles + n_big_tiles + small_rank / 2;
+    put(tile, small_rank & 1, t, qo[t], s);
+    if ((small_rank & 1) == 0 && small_rank == n_small - 1) put(tile, 1, t, qo[t], 0);  // no partner
+  }
+  if (t == 0) ntiles[hd] = min(tmax, n_text_tiles + n_big_tiles + (n_small + 1) / 2);
 }
 
-// Block shapes of the MFMA kernel: waves per block and 16-row sets per wave (a wave with two
-// sets reads each K and V fragment from LDS once for 32 rows).
-#ifndef SPR_SPARSE_WAVES
-#define SPR_SPARSE_WAVES 4
-#endif
-#ifndef SPR_SPARSE_RS
-#define SPR_SPARSE_RS 1
-#endif
-#ifndef SPR_DENSE_WAVES
-#define SPR_DENSE_WAVES 8
-#endif
-#ifndef SPR_DENSE_RS
-#define SPR_DENSE_RS 1
-#endif
+// ------------------------------------------------------------------ host drivers
+// Waves per block of the MFMA kernel: sparse tiles are two 64-row halves, dense and probe
+// tiles 128 rows.
 template <int MODE>
-constexpr int mfma_waves() { return MODE == MODE_SPARSE ? SPR_SPARSE_WAVES : MODE == MODE_DENSE ? SPR_DENSE_WAVES : 4; }
+constexpr int mfma_waves() { return 8; }
 template <int MODE>
-constexpr int mfma_rowsets() { return MODE == MODE_SPARSE ? SPR_SPARSE_RS : MODE == MODE_DENSE ? SPR_DENSE_RS : 1; }
-template <int MODE>
-constexpr int mfma_rows() { return 16 * mfma_waves<MODE>() * mfma_rowsets<MODE>(); }
+constexpr int mfma_rows() { return 16 * mfma_waves<MODE>(); }
+
+template <int D, int MODE>
+static size_t mfma_smem() {
+  size_t s = 2 * size_t(kChunk) * (D + 8) * 2 + 3 * size_t(D) * (kChunk + 8) * 2 + 8 * kChunk * sizeof(int) +
+             16 * sizeof(unsigned long long);
+  if (MODE == MODE_SPARSE) s += (3 * kSegCap + 66 + mfma_waves<MODE>() * 64) * sizeof(int);
+  return s;
+}
 
 template <int D, int MODE>
 static void launch_attn(const AttnParams& P, dim3 grid, int dtype, hipStream_t st) {
   if (dtype == SPR_BF16) {
-    constexpr int W = mfma_waves<MODE>(), RS = mfma_rowsets<MODE>();
+    constexpr int W = mfma_waves<MODE>();
+    constexpr bool VF16 = MODE == MODE_SPARSE;  // the sparse kernel reads the fp16 copy of V
     const size_t sm = mfma_smem<D, MODE>();
-    if (MODE == MODE_SPARSE && P.v_f16) {
-      allow_lds(attn_mfma_kernel<D, MODE, W, RS, true>, sm);
-      hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, RS, true>), grid, dim3(W * 64), sm, st, P);
-    } else {
-      allow_lds(attn_mfma_kernel<D, MODE, W, RS, false>, sm);
-      hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, RS, false>), grid, dim3(W * 64), sm, st, P);
-    }
+    allow_lds(attn_mfma_kernel<D, MODE, W, VF16>, sm);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, VF16>), grid, dim3(W * 64), sm, st, P);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, MODE>), grid, dim3(64), 0, st, P);
   }
@@ -626,21 +798,23 @@ static spr_status dispatch_d(const AttnParams& P, dim3 grid, int d, int dtype, h
 
 spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
                            const spr_route& route, float* o_sp, void* ws, const Workspace& L, hipStream_t st) {
+  const int BH = desc.B * desc.H, Nv = desc.N - desc.n_text;
+  int* tiles = ws_ptr<int>(ws, L.tiles);
+  int* ntiles = ws_ptr<int>(ws, L.ntiles);
+  hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, Nv, desc.n_text,
+                     L.tmax, tiles, ntiles);
+  SPR_CHECK_LAUNCH();
   AttnParams P = {};
   P.q = part.Qp; P.k = part.Kp; P.v = part.Vp;
-  if (desc.dtype == SPR_BF16) {
-    P.v = ws_ptr<void>(ws, L.vh);
-    P.v_f16 = 1;
-  }
+  if (desc.dtype == SPR_BF16) P.v = ws_ptr<void>(ws, L.vh);
   P.g = make_geom(desc);
-  P.tile_off = route.tile_off; P.q_off = part.q_off; P.n_q = part.n_q; P.n_kv = part.n_kv;
-  P.kv_off = part.kv_off; P.sel_cnt = route.sel_cnt; P.sel_kv = route.sel_kv;
+  P.tiles = tiles; P.ntiles = ntiles; P.tmax = L.tmax;
+  P.n_kv = part.n_kv; P.kv_off = part.kv_off; P.sel_cnt = route.sel_cnt; P.sel_kv = route.sel_kv;
   P.Cq = p.Cq; P.Ck = p.Ck;
   P.o_sp = o_sp;
-  const int Nv = desc.N - desc.n_text;
-  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_SPARSE>() : kTileRows;
-  const int max_tiles = p.Cq + ceil_div(Nv, rows) + ceil_div(desc.n_text, rows) + 1;
-  return dispatch_d<MODE_SPARSE>(P, dim3(max_tiles, desc.B * desc.H), desc.d, desc.dtype, st);
+  // bf16: one block per tile; fp32: one block per tile half
+  const int gx = desc.dtype == SPR_BF16 ? L.tmax : 2 * L.tmax;
+  return dispatch_d<MODE_SPARSE>(P, dim3(gx, BH), desc.d, desc.dtype, st);
 }
 
 spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, const void* v, const int* probe_idx,
@@ -651,7 +825,8 @@ spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, c
   P.probe_idx = probe_idx; P.M = M; P.splits = L.splits;
   P.part = ws_ptr<float>(ws, L.pr_part);
   const int BH = desc.B * desc.H;
-  spr_status s = dispatch_d<MODE_PROBE>(P, dim3(ceil_div(M, kTileRows), BH, L.splits), desc.d, desc.dtype, st);
+  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_PROBE>() : kTileRows;
+  spr_status s = dispatch_d<MODE_PROBE>(P, dim3(ceil_div(M, rows), BH, L.splits), desc.d, desc.dtype, st);
   if (s != SPR_OK) return s;
   hipLaunchKernelGGL(probe_merge_kernel, dim3(BH * M), dim3(128), 0, st, P.part, M, L.splits, desc.d, BH, o_probe);
   SPR_CHECK_LAUNCH();
@@ -668,8 +843,4 @@ spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, co
   return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, rows), desc.B * desc.H), desc.d, desc.dtype, st);
 }
 
-}  // namespace spr
-
-namespace spr {
-int sparse_rows_per_block(int dtype) { return dtype == SPR_BF16 ? mfma_rows<MODE_SPARSE>() : kTileRows; }
 }  // namespace spr

@@ -162,12 +162,23 @@ struct Workspace {
   size_t fitW;       // double [BH][M]           unit-mean weights
   size_t applyB;     // float  [BH][d][d]        I + diag(1/sd) B
   size_t applyC;     // float  [BH][d]           mu_R - (mu_X / sd) B
+  size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
+  size_t ntiles;     // int    [BH]              tiles used per head
   size_t total;
+  int tmax;          // tile capacity per head
   int nblk;          // k-means assign blocks per head
   int Cmax, rmax, splits;
 };
 
 constexpr int kAssignThreads = 256;
+constexpr int kHalfRows = 64;  // query rows per half of a block-sparse attention tile
+
+// Capacity of the per-head tile list: a query group of s > kHalfRows rows takes ceil(s / 2h)
+// tiles (< s / 2h + 1), smaller groups go two to a tile, text rows take ceil(n_text / 2h).
+inline int sparse_tile_capacity(int Cq, int Nv, int n_text) {
+  const int h2 = 2 * kHalfRows;
+  return Cq + (Nv + h2 - 1) / h2 + (n_text + h2 - 1) / h2 + 1;
+}
 constexpr int kProbeSplits = 16;
 
 Workspace layout(const spr_desc& desc, const spr_part_params& p, int M);

@@ -265,28 +265,18 @@ __global__ void zero_i64_kernel(int64_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// Per head: 64-row tile prefix over the query groups (and the text group), rho_exec, and
-// the probe allocation m_a (largest remainder of M |G_a| / Nv; remainder ties to the larger
-// group, then the lower id).
+// Per head: rho_exec and the probe allocation m_a (largest remainder of M |G_a| / Nv;
+// remainder ties to the larger group, then the lower id).
 __global__ __launch_bounds__(1024) void route_finalize_kernel(const int* __restrict__ q_off,
                                                               const int* __restrict__ n_q, int Cq, int N, int Nv,
-                                                              int n_text, int M, int tile_rows,
-                                                              const int64_t* __restrict__ pairs,
-                                                              int* __restrict__ tile_off, double* __restrict__ rho,
-                                                              int* __restrict__ pstat) {
+                                                              int n_text, int M, const int64_t* __restrict__ pairs,
+                                                              double* __restrict__ rho, int* __restrict__ pstat) {
   __shared__ int buf[1024];
   __shared__ long long rem[1024];
   __shared__ int sz[1024];
   const int hd = blockIdx.x, t = threadIdx.x;
   const int nq = n_q[hd];
   const int* qo = q_off + size_t(hd) * (Cq + 1);
-  const int ngt = nq + (n_text > 0 ? 1 : 0);
-  int tiles = 0;
-  if (t < nq) tiles = (qo[t + 1] - qo[t] + tile_rows - 1) / tile_rows;
-  else if (t == nq && n_text > 0) tiles = (n_text + tile_rows - 1) / tile_rows;
-  int total;
-  const int pre = block_exscan_i(tiles, buf, &total);
-  if (t <= ngt) tile_off[size_t(hd) * (Cq + 2) + t] = t < ngt ? pre : total;
   // probes
   long long base = 0;
   if (t < nq) {
@@ -377,7 +367,7 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
                      part.n_q, part.n_kv, p.Cq, p.Ck, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_finalize_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, N, Nv,
-                     desc.n_text, M, sparse_tile_rows(desc.dtype), out.pairs, out.tile_off, out.rho_exec, pstat);
+                     desc.n_text, M, out.pairs, out.rho_exec, pstat);
   hipLaunchKernelGGL(probe_select_kernel, dim3(p.Cq, BH), dim3(256), 0, st, part.q_off, part.q_perm, part.n_q,
                      part.qdist, pstat, p.Cq, Nv, M, out.probe_idx, out.probe_w);
   SPR_CHECK_LAUNCH();

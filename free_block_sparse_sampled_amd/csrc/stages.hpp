@@ -55,10 +55,6 @@ spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const
 spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
                           int out_dtype, hipStream_t st);
 
-// Query rows per block of the block-sparse attention kernel (tile prefix sums use the same).
-int sparse_rows_per_block(int dtype);
-inline int sparse_tile_rows(int dtype) { return sparse_rows_per_block(dtype); }
-
 // Raise the dynamic-LDS limit of a kernel above the 64 KB default once per process.
 template <typename K>
 inline void allow_lds(K kernel, size_t bytes) {

@@ -38,7 +38,7 @@ class spr_part_params(ctypes.Structure):
 
 _PART_FIELDS = ["kv_label", "q_label", "kv_perm", "q_perm", "q_pos", "kv_off", "q_off", "n_kv", "n_q", "kbar",
                 "vbar", "qbar", "qdist", "FK", "FQ", "Qp", "Kp", "Vp", "phiK", "phiQ", "cK_last", "cQ_last", "passes"]
-_ROUTE_FIELDS = ["sel_cnt", "sel_kv", "tile_off", "probe_idx", "probe_w", "pairs", "rho_exec", "scores"]
+_ROUTE_FIELDS = ["sel_cnt", "sel_kv", "probe_idx", "probe_w", "pairs", "rho_exec", "scores"]
 
 
 class spr_partition(ctypes.Structure):
@@ -199,7 +199,6 @@ class Route:
         z = lambda shape, t: torch.empty(shape, dtype=t, device=device)  # noqa: E731
         self.sel_cnt = z((BH, cfg.Cq + 1), i32)
         self.sel_kv = z((BH, cfg.Cq + 1, cfg.Ck + 1), i32)
-        self.tile_off = z((BH, cfg.Cq + 2), i32)
         self.probe_idx = z((BH, cfg.M), i32)
         self.probe_w = z((BH, cfg.M), torch.float64)
         self.pairs = z((BH,), torch.int64)

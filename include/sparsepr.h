@@ -35,7 +35,9 @@
  *  - Every call first validates its arguments on the host and returns a
  *    status without launching anything when they are invalid:
  *      SPR_EINVAL        null pointer, bad size or parameter (see each call)
- *      SPR_EUNSUPPORTED  head dimension or dtype not built
+ *      SPR_EUNSUPPORTED  head dimension or dtype not built, or one head's rows
+ *                        span 2 GiB or more (the kernels use 32-bit offsets
+ *                        within a head)
  *      SPR_EWORKSPACE    workspace smaller than sparsepr_workspace_size()
  *      SPR_EHIP          a HIP launch failed (the stream state is undefined)
  *    Anomalies that depend on the data are reported per head in the device
@@ -129,7 +131,6 @@ typedef struct {
                                     is the text query group (when n_text > 0) */
   int32_t* sel_kv;    /* [BH][Cq+1][Ck+1] selected video K/V groups in descending score order,
                                     followed by the text group n_kv when n_text > 0 */
-  int32_t* tile_off;  /* [BH][Cq+2] prefix count of 64-row query tiles per query group */
   int32_t* probe_idx; /* [BH][M] original row of each probe, group-major, nearest first */
   double* probe_w;    /* [BH][M] coverage weight w_p = |G_a| / m_a */
   int64_t* pairs;     /* [BH] routed query-key pairs, text keys of video rows included */
