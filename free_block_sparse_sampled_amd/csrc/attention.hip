@@ -228,8 +228,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   constexpr int NTH = WAVES * 64;
   constexpr int HW = SPARSE ? WAVES / 2 : WAVES;  // waves per row half
   constexpr int ROWS = WAVES * 16;
-  constexpr int KS = D + 8;       // Ks row stride (bf16 elements)
-  constexpr int VS = kChunk + 8;  // Vt row stride (fp16 elements; 16-byte aligned rows)
+  // LDS tiles are unpadded; 16-byte pieces are XOR-swizzled so that the fragment reads of a
+  // 16-lane group (and the staging writes) touch every bank once:
+  //   K  [key][D]:   piece p of row r at p ^ (r % (D / 8))
+  //   V^T[col][64]:  piece p of row r at p ^ ((r / 2) % 8)   (two 128-byte rows per bank line)
+  constexpr int KS = D;           // Ks row stride (bf16 elements)
+  constexpr int VS = kChunk;      // Vt row stride (fp16 elements)
+  constexpr int KPR = D / 8;      // 16-byte pieces per K row
   constexpr int NT = D / 16;
   constexpr int KSTEPS = D / 32;
   constexpr int KPIECES = kChunk * (D / 8);              // 16-byte pieces of a K chunk
@@ -260,7 +265,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const TileInfo t = decode_tile<MODE, ROWS>(P);
   if (!t.valid || t.n0 <= 0) return;
   const int hd = t.hd;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index comes from a scalar register so that every per-wave decision is a scalar branch
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int half = SPARSE ? w / HW : 0;
   const int my_row0 = half ? t.row1 : t.row0;
@@ -351,32 +357,33 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   // each), threads [VTH, VTH + KTH) hold KPT 16-byte pieces of K.  Two register sets and two LDS buffers
   // pipeline the chunks: while chunk c is computed, chunk c+1 sits in LDS and chunks c+2, c+3
   // are in flight.
-  const bool stages_v = threadIdx.x < VTH;
+  const bool stages_v = w * 64 < VTH;
   const int sidx = stages_v ? threadIdx.x : threadIdx.x - VTH;
-  const bool stages_k = !stages_v && sidx < KTH;
+  const bool stages_k = !stages_v && w * 64 - VTH < KTH;
   uint4 pre0[NPRE], pre1[NPRE];
-  // Every thread issues exactly NPRE loads per chunk on every path (roles with fewer pieces, and
-  // idle threads, load row 0 again) so that the wait before a register set is consumed counts
-  // only the loads of the other set issued after it.
+  // Every thread issues exactly NPRE loads per chunk from straight-line code (no branch between
+  // the loads of the two roles, which would make the loads of a set wait for each other): load
+  // i reads row slot lslot[i] of the chunk at byte column lcol[i] through the wave's descriptor.
+  // Roles with fewer pieces, and idle threads, load row slot 0 again.
+  int lslot[NPRE], lcol[NPRE];
+#pragma unroll
+  for (int i = 0; i < NPRE; ++i) {
+    if (stages_v) {
+      const int e = sidx + (i / 4 < VPT ? i / 4 : 0) * VTH;
+      lslot[i] = (e % (kChunk / 4)) * 4 + (i & 3);
+      lcol[i] = (e / (kChunk / 4)) * 16;
+    } else {
+      const int e = stages_k ? sidx + (i < KPT ? i : 0) * KTH : 0;
+      lslot[i] = e / KPR;
+      lcol[i] = (e % KPR) * 16;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t lrsrc = stages_v ? vrsrc : krsrc;
   auto load_into = [&](uint4 (&pre)[NPRE], int ch) __attribute__((always_inline)) {
     const int* ridx = rowidx + (ch & 7) * kChunk;
-    if (stages_v) {
 #pragma unroll
-      for (int i = 0; i < NPRE; ++i) {
-        const int it = i / 4 < VPT ? i / 4 : 0;
-        const int e = sidx + it * VTH;
-        const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
-        const int off = ridx[kq * 4 + (i & 3)] * row_bytes + dq * 16;
-        pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, off, 0, 0));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NPRE; ++i) {
-        const int e = stages_k ? sidx + (i < KPT ? i : 0) * KTH : 0;
-        const int off = ridx[e / (D / 8)] * row_bytes + (e % (D / 8)) * 16;
-        pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, off, 0, 0));
-      }
-    }
+    for (int i = 0; i < NPRE; ++i)
+      pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lrsrc, ridx[lslot[i]] * row_bytes + lcol[i], 0, 0));
   };
   // V chunk stored transposed ([column][key], fp16).  Inside each 32-key half the key k sits at
   // position 8*((k % 16) / 4) + 4*(k / 16) + k % 4, so the eight keys that lane group g feeds to
@@ -412,8 +419,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
                                       __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x05040100u));
           const uint2 hi = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x07060302u),
                                       __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x07060302u));
-          *reinterpret_cast<uint2*>(V + (dq * 8 + 2 * c) * VS + pos) = lo;
-          *reinterpret_cast<uint2*>(V + (dq * 8 + 2 * c + 1) * VS + pos) = hi;
+          // rows 2c and 2c + 1 (relative to dq * 8) share one swizzle
+          const int row = dq * 8 + 2 * c;
+          const int at = ((pos >> 3) ^ ((row >> 1) & 7)) * 8 + (pos & 7);
+          *reinterpret_cast<uint2*>(V + row * VS + at) = lo;
+          *reinterpret_cast<uint2*>(V + (row + 1) * VS + at) = hi;
         }
       }
     } else if (stages_k) {
@@ -421,7 +431,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int e = sidx + i * KTH;
-        *reinterpret_cast<uint4*>(K + (e / (D / 8)) * KS + (e % (D / 8)) * 8) = pre[i];
+        const int row = e / KPR;
+        *reinterpret_cast<uint4*>(K + row * KS + ((e % KPR) ^ (row % KPR)) * 8) = pre[i];
       }
     }
   };
@@ -450,44 +461,47 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(K + (mt * 16 + r16) * KS + ks * 32 + 8 * g));
+        const int row = mt * 16 + r16;
+        const bf16x8_t kf = as_bf16x8(
+            *reinterpret_cast<const uint4*>(K + row * KS + (((ks * 4 + g) ^ (row % KPR)) * 8)));
         sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
       }
     }
   };
+  // Keys whose bit in m is clear get the score -inf (partial chunks only: tails and the seams
+  // between the runs of a paired tile).
+  auto apply_mask = [&](f32x4_t (&sacc)[4], unsigned long long m) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (!((m >> (mt * 16 + 4 * g + v)) & 1ull)) sacc[mt][v] = -INFINITY;
+  };
   // Online softmax of one chunk's scores and O^T += V^T P^T; the row sums come from the same
-  // fp16 P through an MFMA against a tile of ones.  MASKED drops the keys whose bit in m is
-  // clear.  P is formed with the running shift first; the lane's own 16 keys then decide whether
-  // anything may need rescaling, and only in that rare case is the row maximum over the four
-  // lanes of the row formed and P recomputed.
-  auto softmax_pv = [&](auto masked_tag, f32x4_t (&sacc)[4], unsigned long long m, int vbuf)
-                        __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // fp16 P through an MFMA against a tile of ones.  P is formed with the running shift first; if
+  // any p of the wave exceeds 2^8 (tested on the bit patterns, which order non-negative floats
+  // and put inf and NaN above every finite value) the rare path forms the row maxima over the
+  // four lanes of each row, raises the shift where it grew by more than 2^8, rescales O and l,
+  // and forms P again.
+  auto exps = [&](const f32x4_t (&sacc)[4], float (&pv)[16]) __attribute__((always_inline)) {
+    const float mneg = -m_run;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pv[mt * 4 + v] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][v], scale, mneg));
+  };
+  auto finish_pv = [&](const f32x4_t (&sacc)[4], float (&pv)[16], int vbuf) __attribute__((always_inline)) {
     const _Float16* V = Vt + vbuf * VBUF;
-    if constexpr (MASKED) {
+    unsigned big = 0;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (!((m >> (mt * 16 + 4 * g + v)) & 1ull)) sacc[mt][v] = -INFINITY;
-    }
-    float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
-#pragma unroll
-    for (int mt = 1; mt < 4; ++mt)
-      mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][0], sacc[mt][1])), fmaxf(sacc[mt][2], sacc[mt][3]));
-    mx *= scale;
-    f16x8_t pf[2];
-    auto make_p = [&]() __attribute__((always_inline)) {
-      const float mneg = -m_run;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          pf[mt >> 1][(mt & 1) * 4 + v] = _Float16(__builtin_amdgcn_exp2f(fmaf(sacc[mt][v], scale, mneg)));
-    };
-    make_p();
-    if (__builtin_expect(__any(mx > m_run + kRescale), 0)) {
+    for (int i = 0; i < 16; ++i) big = max(big, __float_as_uint(pv[i]));
+    if (__builtin_expect(__any(big > 0x43800000u), 0)) {
       __asm__ volatile("; rare rescale of the running output" ::);
+      float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
+#pragma unroll
+      for (int mt = 1; mt < 4; ++mt)
+        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][0], sacc[mt][1])), fmaxf(sacc[mt][2], sacc[mt][3]));
+      mx *= scale;
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool grow = mx > m_run + kRescale;
@@ -497,8 +511,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       lacc *= alpha;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) oacc[nt] *= alpha;
-      make_p();
+      exps(sacc, pv);
     }
+    f16x8_t pf[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = _Float16(pv[i]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[h], lacc, 0, 0, 0);
 #pragma unroll
@@ -506,9 +523,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f16x8_t av = __builtin_bit_cast(
-            f16x8_t, *reinterpret_cast<const uint4*>(V + (nt * 16 + r16) * VS + h * 32 + 8 * g));
+            f16x8_t, *reinterpret_cast<const uint4*>(V + (nt * 16 + r16) * VS +
+                                                      (((4 * h + g) ^ (((nt * 16 + r16) >> 1) & 7)) * 8)));
         oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[h], oacc[nt], 0, 0, 0);
       }
+    }
+  };
+  auto softmax_pv = [&](f32x4_t (&sacc)[4], int vbuf) __attribute__((always_inline)) {
+    float pv[16];
+    exps(sacc, pv);
+    finish_pv(sacc, pv, vbuf);
+  };
+  // The scores of the next chunk on the matrix cores interleaved with the exponentials of this
+  // chunk on the vector ALU (one K fragment read, one MFMA and two VALU operations per slot).
+  auto qk_exps = [&](f32x4_t (&s_nxt)[4], int kbuf, const f32x4_t (&s_cur)[4], float (&pv)[16])
+                     __attribute__((always_inline)) {
+    qk(s_nxt, kbuf);
+    exps(s_cur, pv);
+    constexpr int AHEAD = 4;  // K fragment reads issued ahead of their MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      if (i + AHEAD < 4 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
   };
   auto half_mask = [&](int c) __attribute__((always_inline)) -> unsigned long long {
@@ -544,10 +582,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     load_to(set, c + 4);
     if (w == 0) resolve(c + 5);
     if (wave_active) {
-      if (half_mask(c + 1) != 0ull) qk(s_nxt, (c + 1) & 1);
-      const unsigned long long m = half_mask(c);
-      if (__builtin_expect(m == ~0ull, 1)) softmax_pv(std::false_type{}, s_cur, m, c % 3);
-      else if (m != 0ull) softmax_pv(std::true_type{}, s_cur, m, c % 3);
+      const unsigned long long mn = half_mask(c + 1), m = half_mask(c);
+      if (__builtin_expect(m != ~0ull, 0) && m != 0ull) apply_mask(s_cur, m);
+      if (__builtin_expect(mn != 0ull && m != 0ull, 1)) {
+        float pv[16];
+        qk_exps(s_nxt, (c + 1) & 1, s_cur, pv);
+        finish_pv(s_cur, pv, c % 3);
+      } else if (mn != 0ull) {
+        qk(s_nxt, (c + 1) & 1);
+      } else if (m != 0ull) {
+        softmax_pv(s_cur, c % 3);
+      }
     }
     __syncthreads();
   };
@@ -768,7 +813,7 @@ constexpr int mfma_rows() { return 16 * mfma_waves<MODE>(); }
 
 template <int D, int MODE>
 static size_t mfma_smem() {
-  size_t s = 2 * size_t(kChunk) * (D + 8) * 2 + 3 * size_t(D) * (kChunk + 8) * 2 + 8 * kChunk * sizeof(int) +
+  size_t s = 2 * size_t(kChunk) * D * 2 + 3 * size_t(D) * kChunk * 2 + 8 * kChunk * sizeof(int) +
              16 * sizeof(unsigned long long);
   if (MODE == MODE_SPARSE) s += (3 * kSegCap + 66 + mfma_waves<MODE>() * 64) * sizeof(int);
   return s;
