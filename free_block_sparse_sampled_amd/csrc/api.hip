@@ -35,6 +35,7 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.gstat = take(BH * 8 * 4);
   L.pstat = take(BH * p.Cq * 2 * 4);
   L.shift = take(BH * p.Cq * 8);
+  L.lbar = take(BH * p.Cq * p.Ck * 8);
   L.scores = take(BH * p.Cq * p.Ck * 8);
   L.vh = take(desc.dtype == SPR_BF16 ? BH * size_t(desc.N) * d * 2 : 0);
   const size_t Mm = M > 0 ? size_t(M) : 1;

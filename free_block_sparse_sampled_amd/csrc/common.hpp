@@ -151,6 +151,7 @@ struct Workspace {
   size_t gstat;      // int    [BH][8]           flags / counters per head
   size_t pstat;      // int    [BH][Cq][2]       probes per query group, prefix
   size_t shift;      // double [BH][Cq]          per-query-group exponent shift of the scores
+  size_t lbar;       // double [BH][Cq][Ck]      centroid logits qbar_a . kbar_b / sqrt d
   size_t scores;     // double [BH][Cq][Ck]      (unless the caller keeps them)
   size_t vh;         // fp16   [BH][N][d]        group-major values converted to fp16 (bf16 inputs)
   size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows

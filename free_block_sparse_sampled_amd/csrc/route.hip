@@ -35,38 +35,68 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
   vstat[(size_t(hd) * Nv + pos) * 2 + 1] = w;
 }
 
-// m_a = max_b qbar_a . kbar_b / sqrt d, one wave per query group.
-__global__ __launch_bounds__(256) void route_shift_kernel(const double* __restrict__ qbar,
-                                                          const double* __restrict__ kbar,
-                                                          const int* __restrict__ n_q, const int* __restrict__ n_kv,
-                                                          int Cq, int Ck, int d, double* __restrict__ shift) {
-  const int hd = blockIdx.y;
-  const int a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (a >= n_q[hd]) return;
-  const double* qa = qbar + (size_t(hd) * Cq + a) * d;
-  const double inv = 1.0 / sqrt(double(d));
-  double m = -1.0e308;
-  for (int b = lane; b < n_kv[hd]; b += 64) {
-    const double* kb = kbar + (size_t(hd) * Ck + b) * d;
-    double s = 0.0;
-    for (int c = 0; c < d; ++c) s = fma(qa[c], kb[c], s);
-    m = fmax(m, s * inv);
-  }
-  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
-  if (lane == 0) shift[size_t(hd) * Cq + a] = m;
-}
-
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// Scores for a tile of 64 query groups x 16 K/V groups.  The keys of the 16 groups are
-// contiguous in group-major order and stream through LDS in 64-key chunks.  Logits come from
-// v_mfma_f64_16x16x4f64 (each wave: 16 query groups, A fragments of qbar kept in registers;
-// lane l, slot v holds the logit of group (l / 16) + 4 v and key l % 16 of a 16-key tile);
-// E u and E^2 w are added to per-(a, b) accumulators in LDS.
+// Centroid logits lbar_ab = qbar_a . kbar_b / sqrt d on the fp64 matrix cores, and the shift
+// m_a = max_b lbar_ab.  One block per 64 query groups of a head: wave w owns query groups
+// a0 + 16 w .. + 15 (A fragments of qbar in registers: lane l holds qbar[a0 + 16 w + l % 16]
+// at columns 4 ks + l / 16) and walks the K/V groups in tiles of 16 (B fragments read from
+// kbar); lane l, slot v of the result holds the logit of query group 16 w + l / 16 + 4 v and
+// K/V group l % 16 of the tile.
+template <int D>
+__global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __restrict__ qbar,
+                                                              const double* __restrict__ kbar,
+                                                              const int* __restrict__ n_q,
+                                                              const int* __restrict__ n_kv, int Cq, int Ck,
+                                                              double* __restrict__ lbar, double* __restrict__ shift) {
+  const int hd = blockIdx.y, a0 = blockIdx.x * 64;
+  const int nq = n_q[hd], nkv = n_kv[hd];
+  if (a0 >= nq) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
+  double qa[D / 4];
+  {
+    const int a = a0 + w * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < D / 4; ++ks) qa[ks] = a < nq ? qbar[(size_t(hd) * Cq + a) * D + ks * 4 + gq] : 0.0;
+  }
+  const double inv = 1.0 / sqrt(double(D));
+  double mx[4] = {-1.0e308, -1.0e308, -1.0e308, -1.0e308};
+  for (int b0 = 0; b0 < nkv; b0 += 16) {
+    const int b = b0 + r16;
+    const double* kb = kbar + (size_t(hd) * Ck + min(b, nkv - 1)) * D + gq;
+    f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks * 4], lg, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int a = a0 + w * 16 + gq + 4 * v;
+      const double x = lg[v] * inv;
+      if (b < nkv && a < nq) {
+        lbar[(size_t(hd) * Cq + a) * Ck + b] = x;
+        mx[v] = fmax(mx[v], x);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    for (int o = 1; o < 16; o <<= 1) mx[v] = fmax(mx[v], __shfl_xor(mx[v], o));
+  if (r16 == 0)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int a = a0 + w * 16 + gq + 4 * v;
+      if (a < nq) shift[size_t(hd) * Cq + a] = mx[v];
+    }
+}
+
+// Scores of 64 query groups x 16 K/V groups.  The K/V groups are taken one at a time; their
+// keys (contiguous in group-major order) are staged in LDS in pieces of 64 and processed in
+// 16-key tiles: logits on the fp64 matrix cores (same fragment layout as the centroid logits),
+// then E = e^{logit - m_a} and the per-lane sums of E u and E^2 w in registers.  At the end of a
+// group the sums are reduced over the 16 lanes of each query group and the score is written.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict__ Kp, int N, int Nv,
                                                           const double* __restrict__ qbar,
-                                                          const double* __restrict__ kbar,
+                                                          const double* __restrict__ lbar,
                                                           const double* __restrict__ vbar,
                                                           const int* __restrict__ kv_off,
                                                           const int* __restrict__ n_q,
@@ -74,17 +104,15 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
                                                           const double* __restrict__ shift,
                                                           const double* __restrict__ vstat,
                                                           double* __restrict__ scores) {
-  constexpr int KSD = D + 4;  // key tile row stride (floats)
-  extern __shared__ double sm[];
+  constexpr int PIECE = 64;   // keys staged per piece
+  constexpr int KSD = D + 4;  // key row stride in LDS (floats)
+  __shared__ float Ks[PIECE * KSD];
+  __shared__ double us[PIECE], wsv[PIECE], vns[16];
   const int hd = blockIdx.z;
   const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 16;
   const int nq = n_q[hd], nkv = n_kv[hd];
   if (a0 >= nq || b0 >= nkv) return;
   const int b1 = min(b0 + 16, nkv);
-  double* acc = sm;                                       // [64][16][2]
-  float* Ks = reinterpret_cast<float*>(acc + 64 * 16 * 2);  // [64][KSD]
-  __shared__ double us[64], wsv[64], shs[64];
-  __shared__ int grp[64];
   const int* off = kv_off + size_t(hd) * (Ck + 1);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   double qa[D / 4];
@@ -93,73 +121,96 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
 #pragma unroll
     for (int ks = 0; ks < D / 4; ++ks) qa[ks] = a < nq ? qbar[(size_t(hd) * Cq + a) * D + ks * 4 + gq] : 0.0;
   }
-  for (int e = threadIdx.x; e < 64 * 32; e += 256) acc[e] = 0.0;
-  if (threadIdx.x < 64) {
-    const int a = a0 + threadIdx.x;
-    shs[threadIdx.x] = a < nq ? shift[size_t(hd) * Cq + a] : 0.0;
+  double m_a[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int a = a0 + w * 16 + gq + 4 * v;
+    m_a[v] = a < nq ? shift[size_t(hd) * Cq + a] : 0.0;
+  }
+  // |vbar_b|^2 of the block's groups: wave w takes groups b0 + 4 w .. + 3
+  for (int k = 0; k < 4; ++k) {
+    const int b = b0 + w * 4 + k;
+    double x = 0.0;
+    if (b < b1)
+      for (int c = lane; c < D; c += 64) {
+        const double y = vbar[(size_t(hd) * Ck + b) * D + c];
+        x = fma(y, y, x);
+      }
+    x = wave_sum_d(x);
+    if (lane == 0) vns[w * 4 + k] = x;
   }
   const double inv = 1.0 / sqrt(double(D));
-  const int k0 = off[b0], k1 = off[b1];
-  for (int kc = k0; kc < k1; kc += 64) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * D; e += 256) {
-      const int jl = e / D, c = e % D, pos = kc + jl;
-      Ks[jl * KSD + c] = pos < k1 ? load_elem<DT>(Kp, (size_t(hd) * N + pos) * D + c) : 0.f;
-    }
-    if (threadIdx.x < 64) {
-      const int pos = kc + threadIdx.x;
-      if (pos < k1) {
-        us[threadIdx.x] = vstat[(size_t(hd) * Nv + pos) * 2 + 0];
-        wsv[threadIdx.x] = vstat[(size_t(hd) * Nv + pos) * 2 + 1];
-        int lo = b0, hi = b1 - 1;  // group of this key: last b with off[b] <= pos
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (off[mid] <= pos) lo = mid; else hi = mid - 1;
-        }
-        grp[threadIdx.x] = lo - b0;
-      } else {
-        grp[threadIdx.x] = -1;
-      }
-    }
-    __syncthreads();
-#pragma unroll 1
-    for (int kt = 0; kt < 4; ++kt) {
-      const int jl = kt * 16 + r16;
-      if (kc + kt * 16 >= k1) break;  // uniform
-      f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
-      const float* kr = Ks + jl * KSD + gq;
+  for (int b = b0; b < b1; ++b) {
+    const int k0 = off[b], k1 = off[b + 1];
+    double s1[4] = {0.0, 0.0, 0.0, 0.0}, s2[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int p0 = k0; p0 < k1; p0 += PIECE) {
+      const int n = min(PIECE, k1 - p0);
+      __syncthreads();
+      for (int e = threadIdx.x; e < PIECE * (D / 8); e += 256) {
+        const int jl = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        float x[8];
+        if (jl < n) {
+          const size_t base = (size_t(hd) * N + p0 + jl) * D + c8;
+          if constexpr (DT == SPR_BF16) {
+            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Kp) + base);
+            const uint32_t q[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], double(kr[ks * 4]), lg, 0, 0, 0);
-      const int gb = grp[jl];
-      if (gb >= 0) {
+            for (int t = 0; t < 4; ++t) {
+              x[2 * t] = __uint_as_float(q[t] << 16);
+              x[2 * t + 1] = __uint_as_float(q[t] & 0xFFFF0000u);
+            }
+          } else {
+            const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(Kp) + base);
+            const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(Kp) + base + 4);
+            x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
+            x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = 0.f;
+        }
+        float* dst = Ks + jl * KSD + c8;
+        *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      }
+      if (threadIdx.x < PIECE) {
+        const int jl = threadIdx.x;
+        us[jl] = jl < n ? vstat[(size_t(hd) * Nv + p0 + jl) * 2 + 0] : 0.0;
+        wsv[jl] = jl < n ? vstat[(size_t(hd) * Nv + p0 + jl) * 2 + 1] : 0.0;
+      }
+      __syncthreads();
+      for (int t = 0; t * 16 < n; ++t) {
+        const int jl = t * 16 + r16;
+        f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+        const float* kr = Ks + jl * KSD + gq;
+#pragma unroll
+        for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], double(kr[ks * 4]), lg, 0, 0, 0);
+        const bool valid = jl < n;
         const double uu = us[jl], ww = wsv[jl];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int al = w * 16 + gq + 4 * v;
-          const double E = exp(lg[v] * inv - shs[al]);
-          atomicAdd(&acc[(al * 16 + gb) * 2 + 0], E * uu);
-          atomicAdd(&acc[(al * 16 + gb) * 2 + 1], E * E * ww);
+          const double E = valid ? exp(lg[v] * inv - m_a[v]) : 0.0;
+          s1[v] = fma(E, uu, s1[v]);
+          s2[v] = fma(E * E, ww, s2[v]);
         }
       }
     }
-  }
-  __syncthreads();
-  // combine: s_ab = A^2 |vbar|^2 - 2 A S1 / |G| + S2 / |G|
-  for (int e = threadIdx.x; e < 64 * 16; e += 256) {
-    const int al = e >> 4, gb = e & 15, a = a0 + al, b = b0 + gb;
-    if (a >= nq || b >= b1) continue;
-    const double* qb = qbar + (size_t(hd) * Cq + a) * D;
-    const double* kb = kbar + (size_t(hd) * Ck + b) * D;
-    const double* vb = vbar + (size_t(hd) * Ck + b) * D;
-    double l = 0.0, vn = 0.0;
-    for (int c = 0; c < D; ++c) {
-      l = fma(qb[c], kb[c], l);
-      vn = fma(vb[c], vb[c], vn);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      for (int o = 1; o < 16; o <<= 1) {
+        s1[v] += __shfl_xor(s1[v], o);
+        s2[v] += __shfl_xor(s2[v], o);
+      }
+    if (r16 == 0) {
+      const double g = double(k1 - k0), vn = vns[b - b0];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int a = a0 + w * 16 + gq + 4 * v;
+        if (a >= nq) continue;
+        const double A = exp(lbar[(size_t(hd) * Cq + a) * Ck + b] - m_a[v]);
+        scores[(size_t(hd) * Cq + a) * Ck + b] = A * A * vn - 2.0 * A * s1[v] / g + s2[v] / g;
+      }
     }
-    const double A = exp(l * inv - shs[al]);
-    const double g = double(off[b + 1] - off[b]);
-    const double sc = A * A * vn - 2.0 * A * acc[(al * 16 + gb) * 2 + 0] / g + acc[(al * 16 + gb) * 2 + 1] / g;
-    scores[(size_t(hd) * Cq + a) * Ck + b] = sc;
   }
 }
 
@@ -350,17 +401,19 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   int* pstat = ws_ptr<int>(ws, L.pstat);
   hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256), BH), dim3(256), 0, st, part.Vp, N, Nv, d,
                      part.kv_perm, part.kv_label, part.vbar, p.Ck, vstat);
-  hipLaunchKernelGGL(route_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.qbar, part.kbar,
-                     part.n_q, part.n_kv, p.Cq, p.Ck, d, shift);
-  SPR_CHECK_LAUNCH();
-  const size_t smem = 64 * 16 * 2 * sizeof(double) + size_t(64) * (d + 4) * sizeof(float);
-  const dim3 sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
-  if (d == 128)
-    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), smem, st, part.Kp, N, Nv, part.qbar, part.kbar,
+  double* lbar = ws_ptr<double>(ws, L.lbar);
+  const dim3 lgrid(ceil_div(p.Cq, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
+  if (d == 128) {
+    hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
+                       part.n_kv, p.Cq, p.Ck, lbar, shift);
+    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), 0, st, part.Kp, N, Nv, part.qbar, lbar,
                        part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
-  else
-    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), smem, st, part.Kp, N, Nv, part.qbar, part.kbar,
+  } else {
+    hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
+                       part.n_kv, p.Cq, p.Ck, lbar, shift);
+    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), 0, st, part.Kp, N, Nv, part.qbar, lbar,
                        part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
+  }
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(zero_i64_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, out.pairs, BH);
   hipLaunchKernelGGL(route_select_kernel, dim3(p.Cq + 1, BH), dim3(256), 0, st, scores, part.kv_off, part.q_off,
