@@ -86,98 +86,240 @@ __global__ __launch_bounds__(256) void query_metric_kernel(const double* __restr
 
 // ------------------------------------------------------------------ factor
 // Rank-r factor F with F F^T = the eigenvalue-clamped rank-r truncation of a symmetric PSD
-// d x d matrix.  One-sided (Hestenes) Jacobi applied to X = M itself: rotating column pairs
-// until all columns are orthogonal leaves X = M V = V diag(lambda), so column i is
-// lambda_i v_i and F's columns are x_i / sqrt(|x_i|) in descending |x_i| order.  Parallel
-// round-robin ordering: d/2 disjoint pairs per round, d-1 rounds per sweep; blockDim/(d/2)
-// consecutive lanes share one pair.  X lives in LDS in fp64 (128 KB at d = 128).
-__global__ __launch_bounds__(256) void jacobi_factor_kernel(const double* __restrict__ Mall, int d, int r,
-                                                            double clamp, double* __restrict__ Fall) {
-  extern __shared__ double X[];  // column-major d x d, column stride ld (padded against bank conflicts)
-  __shared__ int rotated;
-  const int ld = d + 1;
-  __shared__ double lam[128];
-  __shared__ double red[32];
-  const int hd = blockIdx.x;
-  const double* Mm = Mall + size_t(hd) * d * d;
-  for (int e = threadIdx.x; e < d * d; e += blockDim.x) X[(e / d) * ld + e % d] = Mm[e];  // symmetric
-  __syncthreads();
-  // largest squared column norm sets the scale below which columns count as null
-  double nmax2 = 0.0;
-  if (threadIdx.x < d) {
-    double s = 0.0;
-    for (int i = 0; i < d; ++i) s += X[threadIdx.x * ld + i] * X[threadIdx.x * ld + i];
-    nmax2 = s;
-  }
-  for (int o = 32; o > 0; o >>= 1) nmax2 = fmax(nmax2, __shfl_xor(nmax2, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nmax2;
-  __syncthreads();
-  nmax2 = 0.0;
-  for (int w = 0; w < int(blockDim.x >> 6); ++w) nmax2 = fmax(nmax2, red[w]);
-  const double tiny = fmax(nmax2 * 1e-30, 1e-300);
-  const double tol = 1e-14;
+// d x d matrix (d <= 128), one workgroup per head, everything in fp64 in LDS:
+//  1. Householder reduction to tridiagonal form.  Step i (i = d-1 .. 1) takes the reflector u
+//     of row i restricted to columns 0..i-1 (u^T u = 2h), forms p = A u / h, q = p - (u^T p /
+//     2h) u and updates the leading block A -= u q^T + q u^T (kept fully symmetric).  Row i
+//     keeps u and column i keeps u / h.
+//  2. Explicit accumulation of Q = H_{d-1} ... H_1 in place of A.
+//  3. Implicit QL iterations with Wilkinson-type shifts on the tridiagonal matrix.  In each
+//     sweep one lane runs the Givens recurrence and records the rotations; then every lane
+//     applies the sweep's rotations, in order, to its own row of Q, so eigenvectors need two
+//     barriers per sweep rather than per rotation.
+// Columns of F are sqrt(lambda_i) times the eigenvectors, in descending lambda order (ties: lower
+// index first); eigenvalues below clamp * lambda_max (or not positive) give zero columns.
+constexpr int kEigMax = 128;
 
-  const int npairs = d / 2;
-  const int G = blockDim.x / npairs;  // lanes per pair: 4 at d = 128, 8 at d = 64
-  const int p = threadIdx.x / G, sub = threadIdx.x % G;
-  for (int sweep = 0; sweep < 60; ++sweep) {
-    if (threadIdx.x == 0) rotated = 0;
+__global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restrict__ Mall, int d, int r,
+                                                           double clamp, double* __restrict__ Fall,
+                                                           int* __restrict__ gstat) {
+  extern __shared__ double A[];  // d x ld, row-major
+  __shared__ double dg[kEigMax], ev[kEigMax], pv[kEigMax], rc[kEigMax], rs[kEigMax];
+  __shared__ double red[8];
+  __shared__ double sh_h, sh_scale;
+  __shared__ int sh_nrot, sh_m, sh_fail;
+  const int ld = d + 1;
+  const int hd = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
+  const int lane = tid & 63, wv = tid >> 6, nw = nth >> 6;
+  const double* Mm = Mall + size_t(hd) * d * d;
+  for (int e = tid; e < d * d; e += nth) A[(e / d) * ld + e % d] = Mm[e];
+  if (tid == 0) sh_fail = 0;
+  __syncthreads();
+
+  auto block_sum = [&](double x) -> double {
+    x = wave_sum_d(x);
     __syncthreads();
-    for (int rd = 0; rd < d - 1; ++rd) {
-      const int i = (p == 0) ? 0 : 1 + ((p - 1 + rd) % (d - 1));
-      const int kk = d - 1 - p;
-      const int j = 1 + ((kk - 1 + rd) % (d - 1));
-      double* xi = X + size_t(i) * ld;
-      double* xj = X + size_t(j) * ld;
-      double a = 0.0, b = 0.0, c = 0.0;
-      for (int rr = sub; rr < d; rr += G) {
-        const double u = xi[rr], v = xj[rr];
-        a = fma(u, u, a);
-        b = fma(v, v, b);
-        c = fma(u, v, c);
+    if (lane == 0) red[wv] = x;
+    __syncthreads();
+    double t = 0.0;
+    for (int k = 0; k < nw; ++k) t += red[k];
+    return t;
+  };
+
+  // 1. tridiagonal reduction
+  for (int i = d - 1; i >= 1; --i) {
+    const int l = i - 1;
+    double* Ai = A + size_t(i) * ld;
+    double part = 0.0;
+    for (int k = tid; k <= l; k += nth) part += fabs(Ai[k]);
+    const double scale = block_sum(part);
+    if (l == 0 || scale == 0.0) {
+      if (tid == 0) {
+        ev[i] = Ai[l];
+        dg[i] = 0.0;
       }
-      for (int o = G >> 1; o > 0; o >>= 1) {
-        a += __shfl_xor(a, o);
-        b += __shfl_xor(b, o);
-        c += __shfl_xor(c, o);
+      __syncthreads();
+      continue;
+    }
+    part = 0.0;
+    for (int k = tid; k <= l; k += nth) {
+      const double u = Ai[k] / scale;
+      Ai[k] = u;
+      part += u * u;
+    }
+    double h = block_sum(part);
+    const double f = Ai[l];
+    const double g = f >= 0.0 ? -sqrt(h) : sqrt(h);
+    h -= f * g;
+    __syncthreads();
+    if (tid == 0) {
+      ev[i] = scale * g;
+      Ai[l] = f - g;
+      dg[i] = h;
+    }
+    __syncthreads();
+    // u/h into column i; p = A u / h
+    for (int j = tid; j <= l; j += nth) A[size_t(j) * ld + i] = Ai[j] / h;
+    part = 0.0;
+    for (int j = tid; j <= l; j += nth) {
+      const double* Aj = A + size_t(j) * ld;
+      double s = 0.0;
+      for (int k = 0; k <= l; ++k) s = fma(Aj[k], Ai[k], s);
+      pv[j] = s / h;
+      part += pv[j] * Ai[j];
+    }
+    const double K = block_sum(part) / (h + h);
+    for (int j = tid; j <= l; j += nth) pv[j] -= K * Ai[j];
+    __syncthreads();
+    for (int e = tid; e < (l + 1) * (l + 1); e += nth) {
+      const int j = e / (l + 1), k = e % (l + 1);
+      A[size_t(j) * ld + k] -= Ai[j] * pv[k] + pv[j] * Ai[k];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dg[0] = 0.0;
+    ev[0] = 0.0;
+  }
+  __syncthreads();
+  // 2. accumulate Q in place
+  for (int i = 0; i < d; ++i) {
+    const int l = i - 1;
+    if (dg[i] != 0.0) {  // a reflector was applied at step i
+      for (int j = tid; j <= l; j += nth) {
+        double s = 0.0;
+        for (int k = 0; k <= l; ++k) s = fma(A[size_t(i) * ld + k], A[size_t(k) * ld + j], s);
+        pv[j] = s;
       }
-      if (a > tiny && b > tiny && fabs(c) > tol * sqrt(a * b)) {
-        const double z = (b - a) / (2.0 * c);
-        const double t = (z >= 0.0 ? 1.0 : -1.0) / (fabs(z) + sqrt(1.0 + z * z));
-        const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
-        for (int rr = sub; rr < d; rr += G) {
-          const double u = xi[rr], v = xj[rr];
-          xi[rr] = cs * u - sn * v;
-          xj[rr] = sn * u + cs * v;
-        }
-        if (sub == 0) rotated = 1;
+      __syncthreads();
+      for (int e = tid; e < (l + 1) * (l + 1); e += nth) {
+        const int k = e / (l + 1), j = e % (l + 1);
+        A[size_t(k) * ld + j] -= pv[j] * A[size_t(k) * ld + i];
       }
       __syncthreads();
     }
-    const int again = rotated;
+    if (tid == 0) dg[i] = A[size_t(i) * ld + i];
     __syncthreads();
-    if (!again) break;
+    if (tid == 0) A[size_t(i) * ld + i] = 1.0;
+    for (int j = tid; j <= l; j += nth) {
+      A[size_t(j) * ld + i] = 0.0;
+      A[size_t(i) * ld + j] = 0.0;
+    }
+    __syncthreads();
   }
-  // eigenvalues = column norms; rank by descending value (ties: lower column first)
-  if (threadIdx.x < d) {
-    double s = 0.0;
-    for (int i = 0; i < d; ++i) s = fma(X[threadIdx.x * ld + i], X[threadIdx.x * ld + i], s);
-    lam[threadIdx.x] = sqrt(s);
+  // 3. implicit QL on (dg, ev); e[i] couples i and i + 1 after the shift below
+  if (tid == 0) {
+    for (int i = 1; i < d; ++i) ev[i - 1] = ev[i];
+    ev[d - 1] = 0.0;
   }
+  __syncthreads();
+  for (int l = 0; l < d; ++l) {
+    for (int iter = 0;; ++iter) {
+      if (wv == 0) {
+        // first m >= l whose off-diagonal is negligible (m = d - 1 if none), by ballots
+        int m = d - 1;
+        for (int m0 = l; m0 < d - 1; m0 += 64) {
+          const int mm = m0 + lane;
+          bool small = false;
+          if (mm < d - 1) {
+            const double dd = fabs(dg[mm]) + fabs(dg[mm + 1]);
+            small = fabs(ev[mm]) <= 1e-17 * dd || fabs(ev[mm]) + dd == dd;
+          }
+          const unsigned long long bal = __ballot(small);
+          if (bal) {
+            m = m0 + __builtin_ctzll(bal);
+            break;
+          }
+        }
+        if (lane == 0) {
+          sh_m = m;
+          int nrot = 0;
+          if (m != l) {
+            if (iter >= 60) sh_fail = 1;  // no convergence: keep the current values, flag the head
+            double g = (dg[l + 1] - dg[l]) / (2.0 * ev[l]);
+            double rr = sqrt(g * g + 1.0);
+            g = dg[m] - dg[l] + ev[l] / (g + (g >= 0.0 ? rr : -rr));
+            double s = 1.0, c = 1.0, p = 0.0;
+            int i = m - 1;
+            bool early = false;
+            // dg[i + 1] and (dg[i], ev[i]) of the next rotation are carried in registers
+            double d_hi = dg[m], d_i = dg[i], e_i = ev[i];
+            for (; i >= l; --i) {
+              const double d_lo = i > l ? dg[i - 1] : 0.0, e_lo = i > l ? ev[i - 1] : 0.0;
+              const double f = s * e_i;
+              const double b = c * e_i;
+              const double x = fma(f, f, g * g);
+              if (x == 0.0) {
+                ev[i + 1] = 0.0;
+                dg[i + 1] = d_hi - p;
+                ev[m] = 0.0;
+                early = true;
+                break;
+              }
+              // 1 / sqrt(x): hardware estimate and two Newton steps
+              double y = __builtin_amdgcn_rsq(x);
+              y = y * fma(-0.5 * x * y, y, 1.5);
+              y = y * fma(-0.5 * x * y, y, 1.5);
+              ev[i + 1] = x * y;
+              s = f * y;
+              c = g * y;
+              g = d_hi - p;
+              rr = (d_i - g) * s + 2.0 * c * b;
+              p = s * rr;
+              dg[i + 1] = g + p;
+              g = c * rr - b;
+              rc[nrot] = c;
+              rs[nrot] = s;
+              ++nrot;
+              d_hi = d_i;
+              d_i = d_lo;
+              e_i = e_lo;
+            }
+            if (!early) {
+              dg[l] -= p;
+              ev[l] = g;
+              ev[m] = 0.0;
+            }
+          }
+          sh_nrot = nrot;
+        }
+      }
+      __syncthreads();
+      const int m = sh_m, nrot = sh_nrot;
+      if (m == l || sh_fail) break;
+      // rotation t acts on columns (m - 1 - t, m - t)
+      if (tid < d) {
+        double* Zk = A + size_t(tid) * ld;
+        double zhi = Zk[m];
+        for (int t = 0; t < nrot; ++t) {
+          const int i = m - 1 - t;
+          const double zi = Zk[i];
+          const double c = rc[t], s = rs[t];
+          Zk[i + 1] = s * zi + c * zhi;
+          zhi = c * zi - s * zhi;
+        }
+        Zk[m - nrot] = zhi;
+      }
+      __syncthreads();
+    }
+    if (sh_fail) break;
+  }
+  if (tid == 0 && sh_fail) atomicOr(gstat + hd * 8 + 0, SPR_HS_EIGEN_NOCONV);
+  // ranks and output
   __syncthreads();
   double lmax = 0.0;
-  for (int i = 0; i < d; ++i) lmax = fmax(lmax, lam[i]);
+  for (int i = 0; i < d; ++i) lmax = fmax(lmax, dg[i]);
   double* F = Fall + size_t(hd) * d * r;
-  for (int e = threadIdx.x; e < d * r; e += blockDim.x) F[e] = 0.0;
+  for (int e = tid; e < d * r; e += nth) F[e] = 0.0;
   __syncthreads();
-  if (threadIdx.x < d) {
-    const int i = threadIdx.x;
-    const double li = lam[i];
+  if (tid < d) {
+    const int i = tid;
+    const double li = dg[i];
     int rank = 0;
-    for (int j = 0; j < d; ++j) rank += (lam[j] > li) || (lam[j] == li && j < i);
+    for (int j = 0; j < d; ++j) rank += (dg[j] > li) || (dg[j] == li && j < i);
     if (rank < r && li > 0.0 && li >= clamp * lmax) {
-      const double s = 1.0 / sqrt(li);
-      for (int row = 0; row < d; ++row) F[size_t(row) * r + rank] = X[size_t(i) * ld + row] * s;
+      const double s = sqrt(li);
+      for (int row = 0; row < d; ++row) F[size_t(row) * r + rank] = A[size_t(row) * ld + i] * s;
     }
   }
 }
@@ -470,8 +612,9 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(key_metric_kernel<DT>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, q, g, p.Ms, metric);
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
-  allow_lds(jacobi_factor_kernel, jac_smem);
-  hipLaunchKernelGGL(jacobi_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK);
+  allow_lds(eigen_factor_kernel, jac_smem);
+  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
+                     gstat);
   SPR_CHECK_LAUNCH();
   // phi_K = K F_K
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
@@ -519,7 +662,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(ktilde_kernel, dim3(BH), dim3(d), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
   hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
                      metric);
-  hipLaunchKernelGGL(jacobi_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ);
+  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
+                     gstat);
   SPR_CHECK_LAUNCH();
   // phi_Q = RMSNorm(Q F_Q)
   hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, q, g, Nv,

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 
 SPR_BF16, SPR_F32 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP launch failed"}
-HS_BITS = {1: "cholesky_fallback", 2: "budget_unreached", 4: "kv_groups_empty", 8: "q_groups_empty", 16: "rms_floor"}
+HS_BITS = {1: "cholesky_fallback", 2: "budget_unreached", 4: "kv_groups_empty", 8: "q_groups_empty", 16: "rms_floor",
+           32: "eigen_noconv"}
 
 P = ctypes.c_void_p
 

@@ -73,7 +73,8 @@ enum {
   SPR_HS_BUDGET_UNREACHED = 2,  /* some query group selected every K/V group below budget */
   SPR_HS_KV_GROUPS_EMPTY = 4,   /* fewer nonempty K/V groups than requested */
   SPR_HS_Q_GROUPS_EMPTY = 8,    /* fewer nonempty query groups than requested */
-  SPR_HS_RMS_FLOOR = 16         /* some query coordinate norm fell below rms_eps */
+  SPR_HS_RMS_FLOOR = 16,        /* some query coordinate norm fell below rms_eps */
+  SPR_HS_EIGEN_NOCONV = 32      /* a metric eigendecomposition did not converge in 60 QL iterations */
 };
 
 /* Shape of q, k, v: element (b, h, n, c) lives at b*sb + h*sh + n*sn + c. */
