@@ -36,6 +36,12 @@ against the pages; the tests pin them against mathematics instead):
 * Text tokens (trailing ``n_text`` rows): not partitioned; their keys form one
   extra group that every query group selects; their query rows attend densely;
   they take no part in probes or the fit.
+* Later calls (App. C.1): the previous centroids in the original space go through
+  the current feature map, RMSNorm included for queries; centre slots beyond the
+  previous number of nonempty groups take the cold draws of their index.  The two
+  subspace iterations orthonormalise by Cholesky QR and the factor is F = U L with
+  L L^T = U^T M U; a Cholesky pivot at or below eig_clamp times the largest
+  diagonal entry sends the head back to the cold eigendecomposition.
 """
 from __future__ import annotations
 
@@ -51,7 +57,7 @@ __all__ = [
     "key_group_stats", "query_metric", "query_coords", "query_group_stats", "key_budget",
     "route_scores", "route_select", "route", "sparse_attention_rows", "dense_attention_rows",
     "executed_density", "allocate_probes", "select_probes", "ridge_fit", "correct", "relative_error",
-    "sparsepr_head",
+    "sparsepr_head", "cholesky_upper", "metric_factor_warm", "warm_centres",
 ]
 
 U64 = (1 << 64) - 1
@@ -169,13 +175,19 @@ def kmeans_update(X: np.ndarray, labels: np.ndarray, cent: np.ndarray) -> np.nda
     return new
 
 
-def kmeans(X: np.ndarray, C: int, seed: int, head: int, stage: int, max_iters: int, tol: float):
+def kmeans(X: np.ndarray, C: int, seed: int, head: int, stage: int, max_iters: int, tol: float,
+           init: Optional[np.ndarray] = None):
     """k-means with C requested clusters (Sec. 4.1; App. C.1 initialisation, Table C.1
-    limits).  Returns dict(labels (uncompacted), centres used by the final
-    assignment, passes, min_margin, stop_margin)."""
+    limits).  ``init`` (C x r) replaces the sampled initial centres (warm start).
+    Returns dict(labels (uncompacted), centres used by the final assignment, passes,
+    min_margin, stop_margin)."""
     X = np.asarray(X, dtype=np.float64)
     N = X.shape[0]
-    cent = X[init_indices(seed, head, stage, C, N)].copy()
+    if init is None:
+        cent = X[init_indices(seed, head, stage, C, N)].copy()
+    else:
+        cent = np.array(init, dtype=np.float64, copy=True)
+        assert cent.shape == (C, X.shape[1])
     prev = None
     J_prev = None
     min_margin = np.inf
@@ -259,6 +271,61 @@ def query_group_stats(Q: np.ndarray, phi: np.ndarray, labels_c: np.ndarray, n_gr
     cbar /= size[:, None]
     dist = np.sqrt(((phi - cbar[labels_c]) ** 2).sum(1))
     return size, qbar, cbar, dist
+
+
+# -------------------------------------------------------------------- warm start
+def cholesky_upper(G: np.ndarray, clamp: float) -> Optional[np.ndarray]:
+    """Textbook Cholesky G = R^T R with R upper triangular, column by column.  Returns
+    None when a pivot is not above clamp times the largest diagonal entry of G (G not
+    numerically positive definite at the metric's eigenvalue clamp)."""
+    G = np.asarray(G, dtype=np.float64)
+    n = G.shape[0]
+    R = np.zeros_like(G)
+    floor = clamp * float(np.max(np.diag(G))) if n else 0.0
+    for j in range(n):
+        piv = G[j, j] - R[:j, j] @ R[:j, j]
+        if not piv > floor:
+            return None
+        R[j, j] = math.sqrt(piv)
+        R[j, j + 1:] = (G[j, j + 1:] - R[:j, j] @ R[:j, j + 1:]) / R[j, j]
+    return R
+
+
+def metric_factor_warm(Mmat: np.ndarray, F_prev: np.ndarray, r: int, clamp: float,
+                       iters: int = 2) -> Tuple[np.ndarray, bool]:
+    """Factor update of later calls (App. C.1): subspace iterations started from the
+    previous factor, U <- orth(M U), each orthonormalised by Cholesky QR (Z = M U,
+    Z^T Z = R^T R, U = Z R^{-1}); then F = U L with L L^T = U^T M U (Cholesky), so that
+    F F^T = U U^T M U U^T, the metric compressed to the iterated subspace.  When a
+    Cholesky pivot fails the test of cholesky_upper the cold factor is returned
+    instead.  Returns (F [d, r], warm_ok)."""
+    M = np.asarray(Mmat, dtype=np.float64)
+    U = np.asarray(F_prev, dtype=np.float64)
+    for _ in range(iters):
+        Z = M @ U
+        R = cholesky_upper(Z.T @ Z, clamp)
+        if R is None:
+            return metric_factor(M, r, clamp)[0], False
+        U = np.linalg.solve(R.T, Z.T).T
+    H = U.T @ (M @ U)
+    H = 0.5 * (H + H.T)
+    R = cholesky_upper(H, clamp)
+    if R is None:
+        return metric_factor(M, r, clamp)[0], False
+    return U @ R.T, True
+
+
+def warm_centres(prev_orig: np.ndarray, feature_map, X: np.ndarray, C: int, seed: int, head: int,
+                 stage: int) -> np.ndarray:
+    """Initial centres of a later call (App. C.1): the previous call's centroids in the
+    original space, mapped by the current feature map (k F_K for keys, RMSNorm(q F_Q)
+    for queries) into the current coordinates.  Slots beyond the previous number of
+    groups take the cold draws of their index."""
+    init = np.asarray(X, dtype=np.float64)[init_indices(seed, head, stage, C, X.shape[0])].copy()
+    n = min(C, prev_orig.shape[0])
+    if n:
+        init[:n] = feature_map(prev_orig[:n])
+    return init
 
 
 # ---------------------------------------------------------------------- routing
@@ -467,9 +534,12 @@ def relative_error(O: np.ndarray, O_dense: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ whole head
 def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int]] = None,
-                  full: bool = True) -> Dict:
+                  full: bool = True, warm: Optional[Dict] = None) -> Dict:
     """One head of the operator, every stage in the order of Sec. 4 and App. C.3.
-    ``rows`` limits the attention outputs to a subset (default: all rows)."""
+    ``rows`` limits the attention outputs to a subset (default: all rows).  ``warm``
+    (the ``state`` of the previous call of this head: FK, FQ, kbar, qbar) selects the
+    later-call path of App. C.1: factors by subspace iteration from the previous ones
+    and k-means started from the previous centroids."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -478,15 +548,30 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
     qv, kv, vv = q[:Nv], k[:Nv], v[:Nv]
     out: Dict = {}
     MK = key_metric(qv, p.Ms)
-    FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
+    warm_ok = []
+    if warm is None:
+        FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
+    else:
+        FK, ok = metric_factor_warm(MK, warm["FK"], p.rK, p.eig_clamp)
+        wK = None
+        warm_ok.append(ok)
     phiK = project(kv, FK)
-    km = kmeans(phiK, p.Ck, p.seed, head, 0, p.max_iters, p.tol)
+    initK = None if warm is None else warm_centres(warm["kbar"], lambda x: project(x, FK), phiK, p.Ck,
+                                                   p.seed, head, 0)
+    km = kmeans(phiK, p.Ck, p.seed, head, 0, p.max_iters, p.tol, init=initK)
     kv_lab, nkv = compact_labels(km["labels"], p.Ck)
     kv_size, kbar, vbar = key_group_stats(kv, vv, kv_lab, nkv)
     MQ = query_metric(kbar)
-    FQ, wQ = metric_factor(MQ, p.rQ, p.eig_clamp)
+    if warm is None:
+        FQ, wQ = metric_factor(MQ, p.rQ, p.eig_clamp)
+    else:
+        FQ, ok = metric_factor_warm(MQ, warm["FQ"], p.rQ, p.eig_clamp)
+        wQ = None
+        warm_ok.append(ok)
     phiQ = query_coords(qv, FQ, p.rms_eps)
-    qm = kmeans(phiQ, p.Cq, p.seed, head, 1, p.max_iters, p.tol)
+    initQ = None if warm is None else warm_centres(warm["qbar"], lambda x: query_coords(x, FQ, p.rms_eps),
+                                                   phiQ, p.Cq, p.seed, head, 1)
+    qm = kmeans(phiQ, p.Cq, p.seed, head, 1, p.max_iters, p.tol, init=initQ)
     q_lab, nq = compact_labels(qm["labels"], p.Cq)
     q_size, qbar, cbar, dist = query_group_stats(qv, phiQ, q_lab, nq)
     T = key_budget(p.rho, N, Nv, p.M, p.n_text)
@@ -497,7 +582,8 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
     out.update(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
                kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, phiQ=phiQ, kmQ=qm, q_label=q_lab, n_q=nq,
                q_size=q_size, qbar=qbar, cbar=cbar, qdist=dist, T=T, sel=sel, scores=scores,
-               route_info=rinfo, pairs=pairs, rho_exec=rho_exec, probes=probes, probe_w=w, m_a=m_a)
+               route_info=rinfo, pairs=pairs, rho_exec=rho_exec, probes=probes, probe_w=w, m_a=m_a,
+               warm_ok=warm_ok, state=dict(FK=FK, FQ=FQ, kbar=kbar, qbar=qbar))
     if not full:
         return out
     q_lab_full = np.concatenate([q_lab, np.full(p.n_text, -1)])

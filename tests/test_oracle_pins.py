@@ -446,3 +446,128 @@ def test_pipeline_density_and_bounds():
     rho_route = out["pairs"] / N ** 2
     assert abs(out["rho_exec"] - rho_route - 16 / N) < 1e-15
     assert len(out["probes"]) == 16 and len(set(out["probes"].tolist())) == 16
+
+
+# ------------------------------------------------------------------ warm start (App. C.1)
+def _psd_with_gap(rng, d, r, top=(5.0, 10.0), rest=0.1):
+    U, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    lam = np.concatenate([np.linspace(top[1], top[0], r), np.linspace(rest, 0.0, d - r)])
+    return (U * lam) @ U.T, U, lam
+
+
+def test_cholesky_upper_matches_library_and_rejects_indefinite():
+    rng = _rng(70)
+    A = rng.standard_normal((12, 12))
+    G = A.T @ A + 0.1 * np.eye(12)
+    R = O.cholesky_upper(G, 1e-12)
+    np.testing.assert_allclose(R, np.linalg.cholesky(G).T, rtol=1e-12, atol=1e-12)
+    assert np.allclose(R, np.triu(R))
+    G2 = G.copy()
+    G2[5, 5] = -1.0
+    assert O.cholesky_upper(G2, 1e-12) is None
+    # a pivot at the clamp level counts as singular
+    B = rng.standard_normal((12, 6))
+    assert O.cholesky_upper(B @ B.T, 1e-9) is None
+
+
+def test_warm_factor_is_the_projection_after_two_subspace_iterations():
+    rng = _rng(71)
+    d, r = 24, 6
+    M, _, _ = _psd_with_gap(rng, d, r)
+    F0 = rng.standard_normal((d, r))
+    F, ok = O.metric_factor_warm(M, F0, r, 1e-9)
+    assert ok
+    # independent statement: U spans range(M^2 F0) (library QR), F F^T = U U^T M U U^T
+    Q, _ = np.linalg.qr(M @ (M @ F0))
+    P = Q @ Q.T
+    np.testing.assert_allclose(F @ F.T, P @ M @ P, rtol=0, atol=1e-10 * np.abs(M).max())
+
+
+def test_warm_factor_keeps_the_exact_factor():
+    rng = _rng(72)
+    d, r = 32, 8
+    M, _, _ = _psd_with_gap(rng, d, r)
+    Fc, _ = O.metric_factor(M, r, 1e-9)
+    F, ok = O.metric_factor_warm(M, Fc, r, 1e-9)
+    assert ok
+    np.testing.assert_allclose(F @ F.T, Fc @ Fc.T, rtol=0, atol=1e-11 * np.abs(M).max())
+
+
+def test_warm_factor_converges_to_the_truncation_at_the_subspace_rate():
+    rng = _rng(73)
+    d, r = 32, 8
+    M, U, lam = _psd_with_gap(rng, d, r, top=(5.0, 10.0), rest=0.05)
+    trunc = (U[:, :r] * lam[:r]) @ U[:, :r].T
+    F0 = rng.standard_normal((d, r))
+    F1, _ = O.metric_factor_warm(M, F0, r, 1e-9, iters=1)
+    F2, _ = O.metric_factor_warm(M, F0, r, 1e-9, iters=2)
+    e1 = np.abs(F1 @ F1.T - trunc).max()
+    e2 = np.abs(F2 @ F2.T - trunc).max()
+    # each iteration shrinks the component outside the top subspace by lam_{r+1} / lam_r = 0.01
+    assert e2 < 1e-3 * 5.0 and e2 < 0.05 * e1
+
+
+def test_warm_factor_falls_back_to_cold_when_rank_deficient():
+    rng = _rng(74)
+    d, r = 20, 8
+    B = rng.standard_normal((d, 5))
+    M = B @ B.T                      # rank 5 < r
+    Fc, _ = O.metric_factor(M, r, 1e-6)
+    F, ok = O.metric_factor_warm(M, rng.standard_normal((d, r)), r, 1e-6)
+    assert not ok
+    np.testing.assert_array_equal(F, Fc)
+
+
+def test_warm_centres_are_group_means_in_current_coordinates():
+    rng = _rng(75)
+    N, d, r, C = 300, 10, 4, 9
+    K = rng.standard_normal((N, d))
+    F = rng.standard_normal((d, r))
+    phi = K @ F
+    lab = rng.integers(0, 7, size=N)                 # 7 nonempty groups of a previous call
+    _, kbar, _ = O.key_group_stats(K, K, lab, 7)
+    init = O.warm_centres(kbar, lambda x: O.project(x, F), phi, C, 3, 2, 0)
+    # a linear map: the mapped original-space centroid is the mean of the mapped members
+    for b in range(7):
+        np.testing.assert_allclose(init[b], phi[lab == b].mean(0), rtol=1e-12, atol=1e-12)
+    # the two slots without a previous group take the cold draws of their index
+    cold = phi[O.init_indices(3, 2, 0, C, N)]
+    np.testing.assert_array_equal(init[7:], cold[7:])
+
+
+def test_warm_kmeans_from_a_fixed_point_stops_after_one_unchanged_pass():
+    rng = _rng(76)
+    centres = rng.standard_normal((5, 3)) * 10
+    X = np.concatenate([c + 0.1 * rng.standard_normal((40, 3)) for c in centres])
+    cold = O.kmeans(X, 5, 1, 0, 0, 50, 0.0)
+    warm = O.kmeans(X, 5, 1, 0, 0, 2, 0.0, init=cold["centres"])
+    assert warm["passes"] == 2
+    assert np.array_equal(warm["labels"], cold["labels"])
+    # with the cold draws as an explicit start the result is the cold run
+    init = X[O.init_indices(1, 0, 0, 5, X.shape[0])]
+    again = O.kmeans(X, 5, 1, 0, 0, 50, 0.0, init=init)
+    assert np.array_equal(again["labels"], cold["labels"]) and again["passes"] == cold["passes"]
+
+
+def test_warm_pipeline_on_the_same_inputs_reproduces_the_partition():
+    rng = _rng(77)
+    N, d = 384, 16
+    q, k, v = rng.standard_normal((3, N, d))
+    # 24 K/V groups give M_Q rank up to d = 16 > r_Q: both factors stay on the warm path
+    p = O.Params(Ck=24, Cq=8, rK=8, rQ=8, Ms=384, M=8, rho=0.4, lam=1.0, seed=4, max_iters=50, tol=0.0)
+    first = O.sparsepr_head(q, k, v, p, full=False)
+    p2 = O.Params(**{**p.__dict__, "max_iters": 2})
+    second = O.sparsepr_head(q, k, v, p2, full=False, warm=first["state"])
+    assert second["warm_ok"] == [True, True]
+    np.testing.assert_allclose(second["FK"] @ second["FK"].T, first["FK"] @ first["FK"].T,
+                               atol=1e-9 * np.abs(first["MK"]).max())
+    # K/V: the mapped centroids are the members' mean coordinates, a Lloyd fixed point
+    assert np.array_equal(second["kv_label"], first["kv_label"])
+    assert second["kmK"]["passes"] == 2
+    # queries: RMSNorm does not commute with the mean, so the warm start is the mapped
+    # centroid RMSNorm(qbar F_Q) (unit RMS), not the members' mean coordinate
+    init = O.warm_centres(first["qbar"], lambda x: O.query_coords(x, second["FQ"], p.rms_eps),
+                          second["phiQ"], p.Cq, p.seed, 0, 1)
+    n = first["n_q"]
+    np.testing.assert_allclose(np.sqrt((init[:n] ** 2).mean(1)), 1.0, rtol=1e-12)
+    assert second["kmQ"]["passes"] <= 2
