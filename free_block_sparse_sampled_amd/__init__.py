@@ -6,5 +6,5 @@ this package holds the build script and a thin ctypes binding with the same call
 from .sparsepr import (  # noqa: F401
     OperatorConfig, Partition, Route, SparsePR, SparsePRError, library, make_desc, sparsepr_attn_dense,
     sparsepr_attn_sparse, sparsepr_fit_correct, sparsepr_kmeans, sparsepr_partition, sparsepr_probe_exact,
-    sparsepr_route, sparsepr_workspace_size,
+    sparsepr_route, sparsepr_workspace_size, warm_state,
 )

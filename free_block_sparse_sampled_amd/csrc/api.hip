@@ -125,8 +125,8 @@ size_t sparsepr_workspace_size(const spr_desc* desc, const spr_part_params* para
 }
 
 spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k, const void* v,
-                              const spr_part_params* params, spr_partition* out, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              const spr_part_params* params, const spr_warm* warm, spr_partition* out, void* ws,
+                              size_t ws_bytes, void* stream) {
   spr_status s = check_desc(desc);
   if (s != SPR_OK) return s;
   if ((s = check_params(desc, params)) != SPR_OK) return s;
@@ -138,9 +138,11 @@ spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k
     if (!p) return SPR_EINVAL;
   if (!aligned16(out->Qp) || !aligned16(out->Kp) || !aligned16(out->Vp)) return SPR_EINVAL;
   if (int64_t(desc->N) * desc->d * 4 >= (int64_t(1) << 31)) return SPR_EUNSUPPORTED;
+  if (warm && (!warm->FK || !warm->FQ || !warm->kbar || !warm->qbar || !warm->n_kv || !warm->n_q))
+    return SPR_EINVAL;
   Workspace L;
   if ((s = check_ws(desc, params, 1, ws, ws_bytes, &L)) != SPR_OK) return s;
-  return run_partition(*desc, q, k, v, *params, *out, ws, L, static_cast<hipStream_t>(stream));
+  return run_partition(*desc, q, k, v, *params, warm, *out, ws, L, static_cast<hipStream_t>(stream));
 }
 
 spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,

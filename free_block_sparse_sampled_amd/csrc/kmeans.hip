@@ -154,15 +154,18 @@ __global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict_
                                                       double* __restrict__ cent, double* __restrict__ sums,
                                                       int* __restrict__ cnt, double* __restrict__ ctrl,
                                                       _Float16* __restrict__ ch, _Float16* __restrict__ cl,
-                                                      float* __restrict__ cn2, int* __restrict__ rq_count) {
+                                                      float* __restrict__ cn2, int* __restrict__ rq_count,
+                                                      int cent_given) {
   __shared__ double red[32];
   __shared__ double n2s[1024];
   const int hd = blockIdx.x;
   for (int idx = threadIdx.x; idx < C * r; idx += blockDim.x) {
     const int m = idx / r, e = idx % r;
-    const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
-    const int j = int(splitmix64(seed, ctr) % uint64_t(n));
-    cent[(size_t(hd) * C + m) * r + e] = feat[(size_t(hd) * n + j) * r + e];
+    if (!cent_given) {
+      const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
+      const int j = int(splitmix64(seed, ctr) % uint64_t(n));
+      cent[(size_t(hd) * C + m) * r + e] = feat[(size_t(hd) * n + j) * r + e];
+    }
     sums[(size_t(hd) * C + m) * r + e] = 0.0;
   }
   for (int m = threadIdx.x; m < C; m += blockDim.x) cnt[size_t(hd) * C + m] = 0;
@@ -575,7 +578,7 @@ spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
                      a.mu, a.ctrl, reinterpret_cast<_Float16*>(a.xh), reinterpret_cast<_Float16*>(a.xl), a.xnrm);
   hipLaunchKernelGGL(km_init_kernel, dim3(a.BH), dim3(1024), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
                      a.cent, a.sums, a.cnt, a.ctrl, reinterpret_cast<_Float16*>(a.ch),
-                     reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count);
+                     reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count, a.cent_given ? 1 : 0);
   SPR_CHECK_LAUNCH();
   for (int it = 0; it < a.max_iters; ++it) {
     switch (a.r) {

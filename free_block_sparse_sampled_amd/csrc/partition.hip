@@ -102,8 +102,10 @@ constexpr int kEigMax = 128;
 
 __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restrict__ Mall, int d, int r,
                                                            double clamp, double* __restrict__ Fall,
-                                                           int* __restrict__ gstat) {
+                                                           int* __restrict__ gstat, int skip_slot) {
   extern __shared__ double A[];  // d x ld, row-major
+  // heads whose factor the later-call update produced are left alone
+  if (skip_slot >= 0 && gstat[blockIdx.x * 8 + skip_slot]) return;
   __shared__ double dg[kEigMax], ev[kEigMax], pv[kEigMax], rc[kEigMax], rs[kEigMax];
   __shared__ double red[8];
   __shared__ double sh_h, sh_scale;
@@ -321,6 +323,201 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
       const double s = sqrt(li);
       for (int row = 0; row < d; ++row) F[size_t(row) * r + rank] = A[size_t(row) * ld + i] * s;
     }
+  }
+}
+
+// ------------------------------------------------------------------ later-call factor
+// Factor update of later calls (App. C.1): two subspace iterations from the span of the previous
+// factor (columns scaled to unit length), U <- orth(M U) by Cholesky QR (Z = M U, Z^T Z = R^T R,
+// U = Z R^{-1}), then F = U L with L L^T = U^T M U, so F F^T = U U^T M U U^T.  One workgroup per
+// head; M is read from global memory, U and Z live in LDS.  A pivot of Z^T Z at or below clamp^2,
+// or of U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero
+// previous column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes
+// over; otherwise ok = 1 and F is written.
+__device__ inline void mul_MU(const double* __restrict__ M, const double* U, double* Z, int d, int r) {
+  for (int e = threadIdx.x; e < d * r; e += blockDim.x) {
+    const int i = e / r, j = e % r;
+    const double* Mi = M + size_t(i) * d;
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) s = fma(Mi[k], U[k * r + j], s);
+    Z[e] = s;
+  }
+}
+
+// In-place upper Cholesky of the symmetric n x n matrix G (row stride n): the upper triangle
+// becomes R with G = R^T R.  Returns false (for every thread) when a pivot is not above floor.
+__device__ inline bool chol_upper(double* G, int n, double floor, int* fail) {
+  for (int j = 0; j < n; ++j) {
+    __syncthreads();
+    const double piv = G[j * n + j];
+    if (!(piv > floor)) return false;
+    const double rjj = sqrt(piv);
+    __syncthreads();
+    for (int k = j + threadIdx.x; k < n; k += blockDim.x) G[j * n + k] = k == j ? rjj : G[j * n + k] / rjj;
+    __syncthreads();
+    const int m = n - j - 1;
+    for (int e = threadIdx.x; e < m * m; e += blockDim.x) {
+      const int a = j + 1 + e / m, b = j + 1 + e % m;
+      if (b >= a) G[a * n + b] -= G[j * n + a] * G[j * n + b];
+    }
+  }
+  __syncthreads();
+  (void)fail;
+  return true;
+}
+
+__global__ __launch_bounds__(256) void subspace_factor_kernel(const double* __restrict__ Mall,
+                                                              const double* __restrict__ Fprev, int d, int r,
+                                                              double clamp, double* __restrict__ Fall,
+                                                              int* __restrict__ gstat, int ok_slot) {
+  extern __shared__ double sub_sm[];
+  __shared__ double red[8];
+  __shared__ int dummy;
+  const int hd = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
+  const int lane = tid & 63, wv = tid >> 6, nw = nth >> 6;
+  const double* M = Mall + size_t(hd) * d * d;
+  double* U = sub_sm;          // [d][r]
+  double* Z = sub_sm + d * r;  // [d][r]
+  for (int e = tid; e < d * r; e += nth) U[e] = Fprev[size_t(hd) * d * r + e];
+  __syncthreads();
+  // the previous factor's span, columns scaled to unit length; a zero column means a rank
+  // below r, which the update cannot recover
+  __shared__ int zero_col;
+  if (tid == 0) zero_col = 0;
+  __syncthreads();
+  for (int j = tid; j < r; j += nth) {
+    double s = 0.0;
+    for (int i = 0; i < d; ++i) s = fma(U[i * r + j], U[i * r + j], s);
+    if (s > 0.0) {
+      const double inv = 1.0 / sqrt(s);
+      for (int i = 0; i < d; ++i) U[i * r + j] *= inv;
+    } else {
+      zero_col = 1;
+    }
+  }
+  __syncthreads();
+  auto block_max = [&](double x) -> double {
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+    __syncthreads();
+    if (lane == 0) red[wv] = x;
+    __syncthreads();
+    double t = red[0];
+    for (int k = 1; k < nw; ++k) t = fmax(t, red[k]);
+    return t;
+  };
+  bool ok = zero_col == 0;
+  for (int it = 0; it < 2 && ok; ++it) {
+    mul_MU(M, U, Z, d, r);
+    __syncthreads();
+    // G = Z^T Z into U's buffer
+    double* G = U;
+    for (int e = tid; e < r * r; e += nth) {
+      const int a = e / r, b = e % r;
+      if (b < a) continue;
+      double g = 0.0;
+      for (int i = 0; i < d; ++i) g = fma(Z[i * r + a], Z[i * r + b], g);
+      G[a * r + b] = g;
+      G[b * r + a] = g;
+    }
+    __syncthreads();
+    double dm = 0.0;
+    for (int a = tid; a < r; a += nth) dm = fmax(dm, G[a * r + a]);
+    // Z^T Z scales with the squared singular values of Z: tested against clamp^2
+    ok = chol_upper(G, r, clamp * clamp * block_max(dm), &dummy);
+    if (!ok) break;
+    // U = Z R^{-1}, row by row in place (Z becomes U)
+    for (int i = tid; i < d; i += nth) {
+      double* zi = Z + i * r;
+      for (int j = 0; j < r; ++j) {
+        double x = zi[j];
+        for (int k = 0; k < j; ++k) x = fma(-zi[k], G[k * r + j], x);
+        zi[j] = x / G[j * r + j];
+      }
+    }
+    __syncthreads();
+    double* t = U;
+    U = Z;
+    Z = t;
+  }
+  if (ok) {
+    // W = M U into the other buffer, H = (U^T W + W^T U) / 2 (r x r) over it
+    double* W = Z;
+    mul_MU(M, U, W, d, r);
+    __syncthreads();
+    double h[16];
+    int cnt = 0;
+    for (int e = tid; e < r * r; e += nth, ++cnt) {
+      const int a = e / r, b = e % r;
+      double x = 0.0, y = 0.0;
+      for (int i = 0; i < d; ++i) {
+        x = fma(U[i * r + a], W[i * r + b], x);
+        y = fma(U[i * r + b], W[i * r + a], y);
+      }
+      h[cnt] = 0.5 * (x + y);
+    }
+    __syncthreads();
+    cnt = 0;
+    for (int e = tid; e < r * r; e += nth, ++cnt) W[e] = h[cnt];
+    __syncthreads();
+    double dm = 0.0;
+    for (int a = tid; a < r; a += nth) dm = fmax(dm, W[a * r + a]);
+    ok = chol_upper(W, r, clamp * block_max(dm), &dummy);
+    if (ok) {
+      // F = U R^T: F[i][j] = sum_{k >= j} U[i][k] R[j][k]
+      double* F = Fall + size_t(hd) * d * r;
+      for (int e = tid; e < d * r; e += nth) {
+        const int i = e / r, j = e % r;
+        double x = 0.0;
+        for (int k = j; k < r; ++k) x = fma(U[i * r + k], W[j * r + k], x);
+        F[e] = x;
+      }
+    }
+  }
+  if (tid == 0) gstat[hd * 8 + ok_slot] = ok ? 1 : 0;
+}
+
+// Initial centres of a later call (App. C.1): previous centroid m (original space) mapped to the
+// current coordinates, x F (RMS-normalised as in App. B.2 for queries); slots m >= n_prev take
+// the cold draw of index m.  One block per 64 centres of a head.
+template <bool RMS>
+__global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restrict__ prev,
+                                                           const int* __restrict__ n_prev, int C, int d,
+                                                           const double* __restrict__ Fall, int r, double eps,
+                                                           const double* __restrict__ feat, int n, uint64_t seed,
+                                                           int stage, double* __restrict__ cent) {
+  __shared__ double ys[64][65];
+  const int hd = blockIdx.y, m0 = blockIdx.x * 64;
+  const int np = min(n_prev[hd], C);
+  const double* F = Fall + size_t(hd) * d * r;
+  for (int e = threadIdx.x; e < 64 * r; e += blockDim.x) {
+    const int ml = e / r, j = e % r, m = m0 + ml;
+    if (m >= C) continue;
+    double y;
+    if (m < np) {
+      const double* x = prev + (size_t(hd) * C + m) * d;
+      y = 0.0;
+      for (int c = 0; c < d; ++c) y = fma(x[c], F[size_t(c) * r + j], y);
+    } else {
+      const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
+      const int row = int(splitmix64(seed, ctr) % uint64_t(n));
+      y = feat[(size_t(hd) * n + row) * r + j];
+    }
+    ys[ml][j] = y;
+  }
+  __syncthreads();
+  if (RMS && threadIdx.x < 64) {
+    const int ml = threadIdx.x, m = m0 + ml;
+    if (m < np) {
+      double s = 0.0;
+      for (int j = 0; j < r; ++j) s = fma(ys[ml][j], ys[ml][j], s);
+      const double den = fmax(sqrt(s / double(r)), eps);
+      for (int j = 0; j < r; ++j) ys[ml][j] /= den;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * r; e += blockDim.x) {
+    const int ml = e / r, j = e % r, m = m0 + ml;
+    if (m < C) cent[(size_t(hd) * C + m) * r + j] = ys[ml][j];
   }
 }
 
@@ -598,8 +795,8 @@ static T* wsp(void* ws, size_t off) {
 
 template <int DT>
 static spr_status partition_impl(const spr_desc& desc, const void* q, const void* k, const void* v,
-                                 const spr_part_params& p, spr_partition& out, void* ws, const Workspace& L,
-                                 hipStream_t st) {
+                                 const spr_part_params& p, const spr_warm* warm, spr_partition& out, void* ws,
+                                 const Workspace& L, hipStream_t st) {
   const HeadGeom g = make_geom(desc);
   const int BH = desc.B * desc.H, d = desc.d, Nv = g.Nv;
   double* metric = wsp<double>(ws, L.metric);
@@ -613,8 +810,13 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
   allow_lds(eigen_factor_kernel, jac_smem);
+  const size_t sub_smem = 2 * size_t(d) * (p.rK > p.rQ ? p.rK : p.rQ) * sizeof(double);
+  allow_lds(subspace_factor_kernel, sub_smem);
+  if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
+    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BH), dim3(256), sub_smem, st, metric, warm->FK, d, p.rK,
+                       p.eig_clamp, out.FK, gstat, 2);
   hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
-                     gstat);
+                     gstat, warm ? 2 : -1);
   SPR_CHECK_LAUNCH();
   // phi_K = K F_K
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
@@ -628,6 +830,12 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   ka.BH = BH; ka.n = Nv; ka.r = p.rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
   ka.max_iters = p.max_iters; ka.tol = p.tol;
   ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
+  if (warm) {
+    hipLaunchKernelGGL(warm_centres_kernel<false>, dim3(ceil_div(p.Ck, 64), BH), dim3(256), 0, st, warm->kbar,
+                       warm->n_kv, p.Ck, d, out.FK, p.rK, p.rms_eps, phiK, Nv, p.seed, 0, ka.cent);
+    SPR_CHECK_LAUNCH();
+    ka.cent_given = true;
+  }
   spr_status s = run_kmeans(ka, st);
   if (s != SPR_OK) return s;
   if (out.passes) launch_copy_passes(ka.ctrl, BH, out.passes, 2, 0, st);
@@ -662,8 +870,11 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(ktilde_kernel, dim3(BH), dim3(d), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
   hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
                      metric);
+  if (warm)
+    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BH), dim3(256), sub_smem, st, metric, warm->FQ, d, p.rQ,
+                       p.eig_clamp, out.FQ, gstat, 3);
   hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
-                     gstat);
+                     gstat, warm ? 3 : -1);
   SPR_CHECK_LAUNCH();
   // phi_Q = RMSNorm(Q F_Q)
   hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, q, g, Nv,
@@ -672,6 +883,11 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   // query k-means
   KmArgs qa = ka;
   qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1;
+  if (warm) {
+    hipLaunchKernelGGL(warm_centres_kernel<true>, dim3(ceil_div(p.Cq, 64), BH), dim3(256), 0, st, warm->qbar,
+                       warm->n_q, p.Cq, d, out.FQ, p.rQ, p.rms_eps, phiQ, Nv, p.seed, 1, qa.cent);
+    SPR_CHECK_LAUNCH();
+  }
   s = run_kmeans(qa, st);
   if (s != SPR_OK) return s;
   if (out.passes) launch_copy_passes(qa.ctrl, BH, out.passes, 2, 1, st);
@@ -696,9 +912,9 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
 }
 
 spr_status run_partition(const spr_desc& desc, const void* q, const void* k, const void* v, const spr_part_params& p,
-                         spr_partition& out, void* ws, const Workspace& L, hipStream_t st) {
-  if (desc.dtype == SPR_BF16) return partition_impl<SPR_BF16>(desc, q, k, v, p, out, ws, L, st);
-  return partition_impl<SPR_F32>(desc, q, k, v, p, out, ws, L, st);
+                         const spr_warm* warm, spr_partition& out, void* ws, const Workspace& L, hipStream_t st) {
+  if (desc.dtype == SPR_BF16) return partition_impl<SPR_BF16>(desc, q, k, v, p, warm, out, ws, L, st);
+  return partition_impl<SPR_F32>(desc, q, k, v, p, warm, out, ws, L, st);
 }
 
 size_t jacobi_smem(int d) { return size_t(d) * (d + 1) * sizeof(double); }

@@ -10,6 +10,7 @@ struct KmArgs {
   uint64_t seed;
   const double* feat;  // [BH][n][r] coordinates
   double* cent;        // [BH][C][r] centres
+  bool cent_given;     // cent already holds the initial centres (later calls)
   int* labels;         // [BH][n] labels after the last pass
   // scratch carved by kmeans_carve()
   double* sums;
@@ -41,7 +42,7 @@ spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, 
                           int* ngroups, int* gstat, int empty_bit, hipStream_t st);
 
 spr_status run_partition(const spr_desc& desc, const void* q, const void* k, const void* v, const spr_part_params& p,
-                         spr_partition& out, void* ws, const Workspace& L, hipStream_t st);
+                         const spr_warm* warm, spr_partition& out, void* ws, const Workspace& L, hipStream_t st);
 spr_status run_route(const spr_desc& desc, const spr_part_params& p, const spr_partition& part, double rho, int M,
                      int64_t Tk, spr_route& out, void* ws, const Workspace& L, hipStream_t st);
 spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,

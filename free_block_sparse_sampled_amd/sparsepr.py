@@ -50,6 +50,13 @@ class spr_route(ctypes.Structure):
     _fields_ = [(n, P) for n in _ROUTE_FIELDS]
 
 
+_WARM_FIELDS = ["FK", "FQ", "kbar", "qbar", "n_kv", "n_q"]
+
+
+class spr_warm(ctypes.Structure):
+    _fields_ = [(n, P) for n in _WARM_FIELDS]
+
+
 class SparsePRError(RuntimeError):
     pass
 
@@ -68,7 +75,8 @@ def library():
         lib.sparsepr_workspace_size.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params), ctypes.c_int32]
         lib.sparsepr_workspace_size.restype = ctypes.c_size_t
         lib.sparsepr_partition.argtypes = [ctypes.POINTER(spr_desc), P, P, P, ctypes.POINTER(spr_part_params),
-                                           ctypes.POINTER(spr_partition), P, ctypes.c_size_t, P]
+                                           ctypes.POINTER(spr_warm), ctypes.POINTER(spr_partition), P,
+                                           ctypes.c_size_t, P]
         lib.sparsepr_partition.restype = st
         lib.sparsepr_route.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
                                        ctypes.POINTER(spr_partition), ctypes.c_double, ctypes.c_int32,
@@ -216,9 +224,16 @@ def sparsepr_workspace_size(desc: spr_desc, cfg: OperatorConfig) -> int:
     return int(n)
 
 
-def sparsepr_partition(desc, q, k, v, cfg: OperatorConfig, part: Partition, ws: torch.Tensor, stream=None):
+def warm_state(prev: "Partition") -> spr_warm:
+    """Later-call state (App. C.1) taken from a previous call's partition buffers."""
+    return spr_warm(*[_ptr(getattr(prev, n)) for n in _WARM_FIELDS])
+
+
+def sparsepr_partition(desc, q, k, v, cfg: OperatorConfig, part: Partition, ws: torch.Tensor, stream=None,
+                       warm: Optional[spr_warm] = None):
     pp = cfg.part_params()
     _check(library().sparsepr_partition(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(pp),
+                                        ctypes.byref(warm) if warm is not None else None,
                                         ctypes.byref(part.struct), _ptr(ws), ws.numel(), _stream(stream)),
            "sparsepr_partition")
 
@@ -297,9 +312,16 @@ class SparsePR:
         self.out = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
         self.head_status = torch.empty((B * H,), dtype=torch.int32, device=dev)
         self.fit_state = torch.empty((B * H, 3 * d + d * d), dtype=torch.float64, device=dev) if diagnostics else None
+        self.warm_iters = 2  # k-means iteration limit of later calls (Table C.1)
 
-    def partition(self, q, k, v):
-        sparsepr_partition(self.desc, q, k, v, self.cfg, self.part, self.ws)
+    def partition(self, q, k, v, warm: bool = False):
+        """warm: later call of App. C.1 from this object's previous partition (in place), with
+        the warm iteration limit ``warm_iters``."""
+        if warm:
+            cfg = dataclasses.replace(self.cfg, max_iters=self.warm_iters)
+            sparsepr_partition(self.desc, q, k, v, cfg, self.part, self.ws, warm=warm_state(self.part))
+        else:
+            sparsepr_partition(self.desc, q, k, v, self.cfg, self.part, self.ws)
 
     def route_(self):
         sparsepr_route(self.desc, self.cfg, self.part, self.route, self.ws)
@@ -314,8 +336,8 @@ class SparsePR:
         sparsepr_fit_correct(self.desc, self.cfg, self.part, self.route, self.o_sp, self.o_probe, self.out,
                              self.head_status, self.ws, self.fit_state)
 
-    def run(self, q, k, v) -> torch.Tensor:
-        self.partition(q, k, v)
+    def run(self, q, k, v, warm: bool = False) -> torch.Tensor:
+        self.partition(q, k, v, warm)
         self.route_()
         self.attn_sparse()
         self.probe_exact(q, k, v)

@@ -126,6 +126,18 @@ typedef struct {
   int32_t* passes;   /* [BH][2] assignment passes run by the K/V and the query k-means */
 } spr_partition;
 
+/* State of the previous call of the same heads, for the later-call path of App. C.1
+   (device buffers laid out as the corresponding spr_partition outputs; they may be the
+   very buffers this call writes: every one is read before it is overwritten). */
+typedef struct {
+  const double* FK;    /* [BH][d][rK] previous key response factor */
+  const double* FQ;    /* [BH][d][rQ] previous query response factor */
+  const double* kbar;  /* [BH][Ck][d] previous key centroids (original space) */
+  const double* qbar;  /* [BH][Cq][d] previous mean queries (original space) */
+  const int32_t* n_kv; /* [BH] previous nonempty K/V groups */
+  const int32_t* n_q;  /* [BH] previous nonempty query groups */
+} spr_warm;
+
 /* Outputs of sparsepr_route (caller-owned device buffers). */
 typedef struct {
   int32_t* sel_cnt;   /* [BH][Cq+1] number of selected K/V groups of each query group; entry n_q
@@ -148,11 +160,18 @@ size_t sparsepr_workspace_size(const spr_desc* desc, const spr_part_params* para
    k-means of phi_K = k F_K into Ck K/V groups (values follow their keys); key/value
    centroids; M_Q = K~^T K~ / (n_kv d) with K~ the centred key centroids; F_Q;
    phi_Q = RMSNorm(q F_Q); k-means into Cq query groups; group-major copies of Q, K, V.
+   `warm` (nullable) selects the later-call path of App. C.1: each factor comes from two
+   subspace iterations started at the previous factor (Cholesky QR, then F = U L with
+   L L^T = U^T M U), a head whose Cholesky meets a pivot at or below eig_clamp times the
+   largest diagonal entry takes the eigendecomposition instead; each k-means starts from
+   the previous centroids mapped into the current coordinates (k F_K, RMSNorm(q F_Q)), slots
+   beyond the previous group count from the cold draws.  The caller sets max_iters (2 in
+   Table C.1) for such calls.
    EINVAL: null required pointer, B, H < 1, N < 2, n_text out of range, strides,
-   C, r, Ms, max_iters, tol, rms_eps, eig_clamp out of range. */
+   C, r, Ms, max_iters, tol, rms_eps, eig_clamp out of range, a null member of *warm. */
 spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k, const void* v,
-                              const spr_part_params* params, spr_partition* out, void* ws,
-                              size_t ws_bytes, void* stream);
+                              const spr_part_params* params, const spr_warm* warm, spr_partition* out,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Routing and probe selection (Sec. 4.3, App. B.3, App. A.2):
    value-error scores s_ab for every (query group, K/V group); per query group the

@@ -39,9 +39,11 @@ against the pages; the tests pin them against mathematics instead):
 * Later calls (App. C.1): the previous centroids in the original space go through
   the current feature map, RMSNorm included for queries; centre slots beyond the
   previous number of nonempty groups take the cold draws of their index.  The two
-  subspace iterations orthonormalise by Cholesky QR and the factor is F = U L with
-  L L^T = U^T M U; a Cholesky pivot at or below eig_clamp times the largest
-  diagonal entry sends the head back to the cold eigendecomposition.
+  subspace iterations start from the previous factor's columns scaled to unit length,
+  orthonormalise by Cholesky QR and give F = U L with L L^T = U^T M U; a pivot of
+  Z^T Z at or below eig_clamp^2, or of U^T M U at or below eig_clamp, times the
+  largest diagonal entry (or a zero previous column) sends the head back to the cold
+  eigendecomposition.
 """
 from __future__ import annotations
 
@@ -293,17 +295,23 @@ def cholesky_upper(G: np.ndarray, clamp: float) -> Optional[np.ndarray]:
 
 def metric_factor_warm(Mmat: np.ndarray, F_prev: np.ndarray, r: int, clamp: float,
                        iters: int = 2) -> Tuple[np.ndarray, bool]:
-    """Factor update of later calls (App. C.1): subspace iterations started from the
-    previous factor, U <- orth(M U), each orthonormalised by Cholesky QR (Z = M U,
-    Z^T Z = R^T R, U = Z R^{-1}); then F = U L with L L^T = U^T M U (Cholesky), so that
-    F F^T = U U^T M U U^T, the metric compressed to the iterated subspace.  When a
-    Cholesky pivot fails the test of cholesky_upper the cold factor is returned
-    instead.  Returns (F [d, r], warm_ok)."""
+    """Factor update of later calls (App. C.1): subspace iterations started from the span
+    of the previous factor (its columns scaled to unit length), U <- orth(M U), each
+    orthonormalised by Cholesky QR (Z = M U, Z^T Z = R^T R, U = Z R^{-1}); then F = U L
+    with L L^T = U^T M U (Cholesky), so that F F^T = U U^T M U U^T, the metric compressed
+    to the iterated subspace.  Z^T Z has the squared singular values of Z as its scale, so
+    its pivots are tested against clamp^2 (Z numerically rank deficient at the metric's
+    eigenvalue clamp), those of U^T M U against clamp.  A zero column of the previous
+    factor or a failed pivot returns the cold factor instead.  Returns (F [d, r], warm_ok)."""
     M = np.asarray(Mmat, dtype=np.float64)
-    U = np.asarray(F_prev, dtype=np.float64)
+    U = np.array(F_prev, dtype=np.float64, copy=True)
+    norms = np.sqrt((U * U).sum(0))
+    if not np.all(norms > 0):
+        return metric_factor(M, r, clamp)[0], False
+    U /= norms[None, :]
     for _ in range(iters):
         Z = M @ U
-        R = cholesky_upper(Z.T @ Z, clamp)
+        R = cholesky_upper(Z.T @ Z, clamp * clamp)
         if R is None:
             return metric_factor(M, r, clamp)[0], False
         U = np.linalg.solve(R.T, Z.T).T

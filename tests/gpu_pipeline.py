@@ -17,8 +17,8 @@ def op_config(cfg: WorkloadConfig, **kw) -> spr.OperatorConfig:
     return spr.OperatorConfig(**base)
 
 
-def device_inputs(cfg: WorkloadConfig, heads=None):
-    q, k, v = batch_inputs(cfg, heads)
+def device_inputs(cfg: WorkloadConfig, heads=None, step: int = 0):
+    q, k, v = batch_inputs(cfg, heads, step)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     to = lambda x: torch.from_numpy(x).to(dt).cuda()  # noqa: E731
     return (q, k, v), (to(q), to(k), to(v))

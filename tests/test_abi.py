@@ -73,10 +73,16 @@ def test_entry_points_reject_invalid_arguments_on_the_host(lib):
     d, p = _desc(), _params()
     part, route = B.spr_partition(), B.spr_route()
     dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails before any device work
-    assert lib.sparsepr_partition(None, dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(part), dummy, 0, None) == 1
+    assert lib.sparsepr_partition(None, dummy, dummy, dummy, ctypes.byref(p), None, ctypes.byref(part), dummy, 0,
+                                  None) == 1
     # required partition outputs missing
-    assert lib.sparsepr_partition(ctypes.byref(d), dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(part), dummy,
-                                  1 << 40, None) == 1
+    assert lib.sparsepr_partition(ctypes.byref(d), dummy, dummy, dummy, ctypes.byref(p), None, ctypes.byref(part),
+                                  dummy, 1 << 40, None) == 1
+    # a warm state with a null member
+    full = B.spr_partition(*([dummy] * len(B._PART_FIELDS)))
+    warm = B.spr_warm(dummy, dummy, dummy, None, dummy, dummy)
+    assert lib.sparsepr_partition(ctypes.byref(d), dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(warm),
+                                  ctypes.byref(full), dummy, 1 << 40, None) == 1
     # unsupported head dimension
     assert lib.sparsepr_attn_dense(ctypes.byref(_desc(d=80)), dummy, dummy, dummy, dummy, 0, None) == 2
     assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 5, None) == 2

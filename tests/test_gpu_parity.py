@@ -152,6 +152,40 @@ def test_operator_end_to_end(name, heads):
     assert np.all(g["head_status"] & 1 == 0)
 
 
+@pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 7)]),
+                                        ("small_text", [(0, 1)])])
+def test_warm_start_end_to_end(name, heads):
+    """A later call (App. C.1): call 1 cold on the step-0 inputs, call 2 on fresh-noise step-1
+    inputs started from call 1's factors and centroids, with the warm iteration limit.  The
+    oracle runs the same two calls from its own state (the factors agree up to a rotation,
+    which neither the subspace iteration nor the distances see)."""
+    cfg = config(name)
+    opc = op_config(cfg)
+    (q0, k0, v0), (tq0, tk0, tv0) = device_inputs(cfg, step=0)
+    (q1, k1, v1), (tq1, tk1, tv1) = device_inputs(cfg, step=1)
+    op = spr.SparsePR(tq0, opc, n_text=cfg.n_text, diagnostics=True, keep_scores=True)
+    op.run(tq0, tk0, tv0)
+    op.run(tq1, tk1, tv1, warm=True)
+    torch.cuda.synchronize()
+    g = pull(op)
+    assert np.all(g["passes"] <= op.warm_iters)
+    p = _oracle_params(opc, cfg.n_text)
+    p2 = O.Params(**{**p.__dict__, "max_iters": op.warm_iters})
+    for (b, h) in heads:
+        hd = b * cfg.H + h
+        first = O.sparsepr_head(q0[b, h], k0[b, h], v0[b, h], p, head=hd, full=False)
+        rows = None if cfg.N <= 2048 else np.unique(np.concatenate(
+            [np.arange(0, cfg.N, 7), np.arange(cfg.N - 100, cfg.N)]))
+        ref = O.sparsepr_head(q1[b, h], k1[b, h], v1[b, h], p2, head=hd, rows=rows, warm=first["state"])
+        ref["lam"] = p.lam
+        assert _oracle_is_tie_free(first) and _oracle_is_tie_free(ref), "tie in the oracle run"
+        if name == "tiny":
+            assert ref["warm_ok"] == [True, False]  # M_Q has rank 15 < r_Q: cold factor
+        else:
+            assert ref["warm_ok"] == [True, True]
+        _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text)
+
+
 def test_lockstep_stages_small():
     """Each stage's oracle function applied to the GPU's own inputs of that stage."""
     cfg = config("small")

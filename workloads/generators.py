@@ -23,6 +23,11 @@ Token order is row-major over (t, h, w): n = (t*Hg + h)*Wg + w.
 Seeds: per-head draws use ``numpy.random.default_rng([cfg_seed, b, h])``,
 sink positions ``[cfg_seed, b, h, 7]``, text tokens ``[cfg_seed, b, h, 11]``
 and draws shared by a whole config ``[cfg_seed, 999]``.
+
+``step`` > 0 gives the inputs of a later call of the same heads (consecutive
+denoising steps): same frequencies, positions, sinks and mixture centres, fresh
+token noise and values from ``[cfg_seed, b, h, 1000 + step]`` (text tokens from
+``[cfg_seed, b, h, 11, step]``).
 """
 from __future__ import annotations
 
@@ -116,12 +121,13 @@ def _round_bf16(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
 
 
-def head_inputs(cfg: WorkloadConfig, b: int, h: int):
+def head_inputs(cfg: WorkloadConfig, b: int, h: int, step: int = 0):
     """Q, K, V of one head as float32 arrays [N, d] (bf16-exact values for bf16 configs)."""
     N, Nv, d = cfg.N, cfg.Nv, cfg.d
+    key = [cfg.seed, b, h] if step == 0 else [cfg.seed, b, h, 1000 + step]
     if cfg.generator == "mixture":
         centres = np.random.default_rng([cfg.seed, 999]).standard_normal((8, d))
-        rng = np.random.default_rng([cfg.seed, b, h])
+        rng = np.random.default_rng(key)
         q_id = rng.integers(0, 8, size=Nv)
         q_noise = rng.standard_normal((Nv, d))
         k_id = rng.integers(0, 8, size=Nv)
@@ -133,14 +139,14 @@ def head_inputs(cfg: WorkloadConfig, b: int, h: int):
         q, k, v = (x.astype(np.float32) for x in (q, k, v))
     else:
         feat = _fourier_features(cfg)
-        rng = np.random.default_rng([cfg.seed, b, h])
+        rng = np.random.default_rng(key)
         q = feat + np.float32(0.5) * rng.standard_normal((Nv, d), dtype=np.float32)
         k = feat + np.float32(0.5) * rng.standard_normal((Nv, d), dtype=np.float32)
         v = rng.standard_normal((Nv, d), dtype=np.float32)
         sinks = np.random.default_rng([cfg.seed, b, h, 7]).choice(Nv, size=4, replace=False)
         k[sinks] *= np.float32(5.0)
     if cfg.n_text:
-        rng_t = np.random.default_rng([cfg.seed, b, h, 11])
+        rng_t = np.random.default_rng([cfg.seed, b, h, 11] if step == 0 else [cfg.seed, b, h, 11, step])
         s = np.float32(np.sqrt(0.75))
         qt = s * rng_t.standard_normal((cfg.n_text, d), dtype=np.float32)
         kt = s * rng_t.standard_normal((cfg.n_text, d), dtype=np.float32)
@@ -154,7 +160,7 @@ def head_inputs(cfg: WorkloadConfig, b: int, h: int):
     return q, k, v
 
 
-def batch_inputs(cfg: WorkloadConfig, heads=None):
+def batch_inputs(cfg: WorkloadConfig, heads=None, step: int = 0):
     """Q, K, V as float32 arrays [B, H, N, d]; ``heads`` optionally restricts to a list of (b, h)."""
     B, H = cfg.B, cfg.H
     out = np.empty((3, B, H, cfg.N, cfg.d), dtype=np.float32)
@@ -163,5 +169,5 @@ def batch_inputs(cfg: WorkloadConfig, heads=None):
             if heads is not None and (b, h) not in heads:
                 out[:, b, h] = 0.0
                 continue
-            out[0, b, h], out[1, b, h], out[2, b, h] = head_inputs(cfg, b, h)
+            out[0, b, h], out[1, b, h], out[2, b, h] = head_inputs(cfg, b, h, step)
     return out[0], out[1], out[2]
