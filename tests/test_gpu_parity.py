@@ -152,8 +152,8 @@ def test_operator_end_to_end(name, heads):
     assert np.all(g["head_status"] & 1 == 0)
 
 
-@pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 7)]),
-                                        ("small_text", [(0, 1)])])
+@pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 4)]),
+                                        ("small_text", [(0, 0)])])
 def test_warm_start_end_to_end(name, heads):
     """A later call (App. C.1): call 1 cold on the step-0 inputs, call 2 on fresh-noise step-1
     inputs started from call 1's factors and centroids, with the warm iteration limit.  The
