@@ -35,6 +35,26 @@ __device__ __forceinline__ void store_out(void* base, int64_t idx, float x) {
   }
 }
 
+// Eight consecutive elements starting at idx (a multiple of 8, 16-byte aligned rows) widened to
+// fp32: one 16-byte load for bf16, two for fp32.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&x)[8]) {
+  if constexpr (DT == SPR_BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x[2 * c] = __uint_as_float(w[c] << 16);
+      x[2 * c + 1] = __uint_as_float(w[c] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
 template <int DT>
 struct ElemSize {
   static constexpr int value = DT == SPR_BF16 ? 2 : 4;

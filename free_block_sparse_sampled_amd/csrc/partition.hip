@@ -44,18 +44,28 @@ __global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict_
   out[size_t(hd) * g.d * g.d + size_t(i0 + ti) * g.d + j0 + tj] = acc / double(m);
 }
 
-// Centred key centroids K~ = kbar_b - mu_K over the n_kv nonempty groups (App. B.2).
-__global__ void ktilde_kernel(const double* __restrict__ kbar, const int* __restrict__ n_kv, int Ck, int d,
-                              double* __restrict__ kt) {
-  const int hd = blockIdx.x, c = threadIdx.x;
-  if (c >= d) return;
+// Centred key centroids K~ = kbar_b - mu_K over the n_kv nonempty groups (App. B.2).  One block
+// of 1024 threads per head: 1024 / d row stripes accumulate column sums, combined in LDS.
+__global__ __launch_bounds__(1024) void ktilde_kernel(const double* __restrict__ kbar, const int* __restrict__ n_kv,
+                                                      int Ck, int d, double* __restrict__ kt) {
+  __shared__ double part[1024];
+  const int hd = blockIdx.x, c = threadIdx.x % d, stripe = threadIdx.x / d, ns = blockDim.x / d;
   const int n = n_kv[hd];
   const double* kb = kbar + size_t(hd) * Ck * d;
+  double s0 = 0.0, s1 = 0.0;
+  int b = stripe;
+  for (; b + ns < n; b += 2 * ns) {
+    s0 += kb[size_t(b) * d + c];
+    s1 += kb[size_t(b + ns) * d + c];
+  }
+  if (b < n) s0 += kb[size_t(b) * d + c];
+  part[threadIdx.x] = s0 + s1;
+  __syncthreads();
   double mu = 0.0;
-  for (int b = 0; b < n; ++b) mu += kb[size_t(b) * d + c];
+  for (int t = 0; t < ns; ++t) mu += part[t * d + c];
   mu /= double(n);
   double* o = kt + size_t(hd) * Ck * d;
-  for (int b = 0; b < n; ++b) o[size_t(b) * d + c] = kb[size_t(b) * d + c] - mu;
+  for (b = stripe; b < n; b += ns) o[size_t(b) * d + c] = kb[size_t(b) * d + c] - mu;
 }
 
 // M_Q = K~^T K~ / (n_kv d) (Sec. 4.1).
@@ -327,26 +337,48 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
 }
 
 // ------------------------------------------------------------------ later-call factor
-// Factor update of later calls (App. C.1): two subspace iterations from the span of the previous
-// factor (columns scaled to unit length), U <- orth(M U) by Cholesky QR (Z = M U, Z^T Z = R^T R,
-// U = Z R^{-1}), then F = U L with L L^T = U^T M U, so F F^T = U U^T M U U^T.  One workgroup per
-// head; M is read from global memory, U and Z live in LDS.  A pivot of Z^T Z at or below clamp^2,
-// or of U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero
-// previous column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes
-// over; otherwise ok = 1 and F is written.
-__device__ inline void mul_MU(const double* __restrict__ M, const double* U, double* Z, int d, int r) {
-  for (int e = threadIdx.x; e < d * r; e += blockDim.x) {
-    const int i = e / r, j = e % r;
-    const double* Mi = M + size_t(i) * d;
-    double s = 0.0;
-    for (int k = 0; k < d; ++k) s = fma(Mi[k], U[k * r + j], s);
-    Z[e] = s;
+// C (m x n, row stride ldc) = op(A) op(B) with 4 x 4 register tiles per thread (16 independent
+// accumulators hide the load latency).  op(A)(i, k) = A[i * lda + k], or A[k * lda + i] when AT;
+// op(B)(k, j) = B[k * ldb + j], or B[j * ldb + k] when BT; K terms; m, n multiples of 4 (d is 64
+// or 128, ranks are 8 to 64 in steps of 8 or 16).
+template <bool AT, bool BT>
+__device__ inline void gemm_4x4(const double* A, int lda, const double* B, int ldb, double* C, int ldc, int m, int n,
+                                int K) {
+  const int tr = m / 4, tc = n / 4;
+  for (int t = threadIdx.x; t < tr * tc; t += blockDim.x) {
+    const int i0 = (t / tc) * 4, j0 = (t % tc) * 4;
+    double acc[4][4] = {};
+    for (int k = 0; k < K; ++k) {
+      double a[4], b[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[x] = AT ? A[size_t(k) * lda + i0 + x] : A[size_t(i0 + x) * lda + k];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) b[y] = BT ? B[size_t(j0 + y) * ldb + k] : B[size_t(k) * ldb + j0 + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) C[size_t(i0 + x) * ldc + j0 + y] = acc[x][y];
   }
 }
 
+// Largest diagonal entry of the n x n matrix G (n <= 64), computed by every wave on its own so
+// that no shared scratch is needed; all threads return the same value.
+__device__ inline double diag_max(const double* G, int n) {
+  const int lane = threadIdx.x & 63;
+  double x = lane < n ? G[lane * n + lane] : 0.0;
+  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  return x;
+}
+
 // In-place upper Cholesky of the symmetric n x n matrix G (row stride n): the upper triangle
-// becomes R with G = R^T R.  Returns false (for every thread) when a pivot is not above floor.
-__device__ inline bool chol_upper(double* G, int n, double floor, int* fail) {
+// becomes R with G = R^T R and the strict lower triangle is cleared.  Returns false (for every
+// thread) when a pivot is not above floor.
+__device__ inline bool chol_upper(double* G, int n, double floor) {
   for (int j = 0; j < n; ++j) {
     __syncthreads();
     const double piv = G[j * n + j];
@@ -362,116 +394,92 @@ __device__ inline bool chol_upper(double* G, int n, double floor, int* fail) {
     }
   }
   __syncthreads();
-  (void)fail;
+  for (int e = threadIdx.x; e < n * n; e += blockDim.x)
+    if (e % n < e / n) G[e] = 0.0;
+  __syncthreads();
   return true;
 }
 
+// In-place inverse of the upper triangular R (strict lower triangle zero), column by column:
+// column j of R^{-1} is -(1 / R_jj) times the leading inverse block applied to column j of R.
+// The new column is formed in registers and written after a barrier, since its rows are read
+// as the old column while it is formed.
+__device__ inline void tri_inv_upper_inplace(double* R, int n) {
+  for (int j = 0; j < n; ++j) {
+    const double rjj = R[j * n + j];
+    double x = 0.0;
+    const int i = threadIdx.x;
+    if (i < j)
+      for (int k = i; k < j; ++k) x = fma(R[i * n + k], R[k * n + j], x);
+    __syncthreads();
+    if (i < j) R[i * n + j] = -x / rjj;
+    if (i == j) R[j * n + j] = 1.0 / rjj;
+    __syncthreads();
+  }
+}
+
+// Factor update of later calls (App. C.1): two subspace iterations from the span of the previous
+// factor (columns scaled to unit length), U <- orth(M U) by Cholesky QR (Z = M U, Z^T Z = R^T R,
+// U = Z R^{-1}), then F = U L with L L^T = U^T M U, so F F^T = U U^T M U U^T.  One workgroup per
+// head; M is read from global memory, U and Z (d x r each) and one r x r matrix live in LDS.  A pivot of Z^T Z at or below clamp^2,
+// or of U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero
+// previous column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes
+// over; otherwise ok = 1 and F is written.
 __global__ __launch_bounds__(256) void subspace_factor_kernel(const double* __restrict__ Mall,
                                                               const double* __restrict__ Fprev, int d, int r,
                                                               double clamp, double* __restrict__ Fall,
                                                               int* __restrict__ gstat, int ok_slot) {
   extern __shared__ double sub_sm[];
-  __shared__ double red[8];
-  __shared__ int dummy;
   const int hd = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
-  const int lane = tid & 63, wv = tid >> 6, nw = nth >> 6;
   const double* M = Mall + size_t(hd) * d * d;
-  double* U = sub_sm;          // [d][r]
-  double* Z = sub_sm + d * r;  // [d][r]
+  double* U = sub_sm;              // [d][r]
+  double* Z = sub_sm + d * r;      // [d][r]
+  double* G = sub_sm + 2 * d * r;  // [r][r]
   for (int e = tid; e < d * r; e += nth) U[e] = Fprev[size_t(hd) * d * r + e];
   __syncthreads();
   // the previous factor's span, columns scaled to unit length; a zero column means a rank
-  // below r, which the update cannot recover
-  __shared__ int zero_col;
-  if (tid == 0) zero_col = 0;
+  // below r, which the update cannot recover.  Every wave forms all r column norms (lane j holds
+  // column j), so the scale and the zero test need no shared scratch.
+  const int lane = tid & 63;
+  double cs = 0.0;
+  if (lane < r)
+    for (int i = 0; i < d; ++i) cs = fma(U[i * r + lane], U[i * r + lane], cs);
+  bool ok = !__any(lane < r && !(cs > 0.0));
+  const double cinv = cs > 0.0 ? 1.0 / sqrt(cs) : 0.0;
   __syncthreads();
-  for (int j = tid; j < r; j += nth) {
-    double s = 0.0;
-    for (int i = 0; i < d; ++i) s = fma(U[i * r + j], U[i * r + j], s);
-    if (s > 0.0) {
-      const double inv = 1.0 / sqrt(s);
-      for (int i = 0; i < d; ++i) U[i * r + j] *= inv;
-    } else {
-      zero_col = 1;
-    }
+  if (ok) {
+    for (int e = tid; e < d * r; e += nth) U[e] *= __shfl(cinv, e % r);
+    __syncthreads();
   }
-  __syncthreads();
-  auto block_max = [&](double x) -> double {
-    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
-    __syncthreads();
-    if (lane == 0) red[wv] = x;
-    __syncthreads();
-    double t = red[0];
-    for (int k = 1; k < nw; ++k) t = fmax(t, red[k]);
-    return t;
-  };
-  bool ok = zero_col == 0;
   for (int it = 0; it < 2 && ok; ++it) {
-    mul_MU(M, U, Z, d, r);
+    gemm_4x4<false, false>(M, d, U, r, Z, r, d, r, d);  // Z = M U
     __syncthreads();
-    // G = Z^T Z into U's buffer
-    double* G = U;
-    for (int e = tid; e < r * r; e += nth) {
-      const int a = e / r, b = e % r;
-      if (b < a) continue;
-      double g = 0.0;
-      for (int i = 0; i < d; ++i) g = fma(Z[i * r + a], Z[i * r + b], g);
-      G[a * r + b] = g;
-      G[b * r + a] = g;
-    }
+    gemm_4x4<true, false>(Z, r, Z, r, G, r, r, r, d);   // G = Z^T Z
     __syncthreads();
-    double dm = 0.0;
-    for (int a = tid; a < r; a += nth) dm = fmax(dm, G[a * r + a]);
     // Z^T Z scales with the squared singular values of Z: tested against clamp^2
-    ok = chol_upper(G, r, clamp * clamp * block_max(dm), &dummy);
+    ok = chol_upper(G, r, clamp * clamp * diag_max(G, r));
     if (!ok) break;
-    // U = Z R^{-1}, row by row in place (Z becomes U)
-    for (int i = tid; i < d; i += nth) {
-      double* zi = Z + i * r;
-      for (int j = 0; j < r; ++j) {
-        double x = zi[j];
-        for (int k = 0; k < j; ++k) x = fma(-zi[k], G[k * r + j], x);
-        zi[j] = x / G[j * r + j];
-      }
-    }
+    tri_inv_upper_inplace(G, r);
+    gemm_4x4<false, false>(Z, r, G, r, U, r, d, r, r);  // U = Z R^{-1}
     __syncthreads();
-    double* t = U;
-    U = Z;
-    Z = t;
   }
   if (ok) {
-    // W = M U into the other buffer, H = (U^T W + W^T U) / 2 (r x r) over it
-    double* W = Z;
-    mul_MU(M, U, W, d, r);
+    gemm_4x4<false, false>(M, d, U, r, Z, r, d, r, d);  // W = M U
     __syncthreads();
-    double h[16];
-    int cnt = 0;
-    for (int e = tid; e < r * r; e += nth, ++cnt) {
+    gemm_4x4<true, false>(U, r, Z, r, G, r, r, r, d);   // U^T W
+    __syncthreads();
+    for (int e = tid; e < r * r; e += nth) {
       const int a = e / r, b = e % r;
-      double x = 0.0, y = 0.0;
-      for (int i = 0; i < d; ++i) {
-        x = fma(U[i * r + a], W[i * r + b], x);
-        y = fma(U[i * r + b], W[i * r + a], y);
-      }
-      h[cnt] = 0.5 * (x + y);
-    }
-    __syncthreads();
-    cnt = 0;
-    for (int e = tid; e < r * r; e += nth, ++cnt) W[e] = h[cnt];
-    __syncthreads();
-    double dm = 0.0;
-    for (int a = tid; a < r; a += nth) dm = fmax(dm, W[a * r + a]);
-    ok = chol_upper(W, r, clamp * block_max(dm), &dummy);
-    if (ok) {
-      // F = U R^T: F[i][j] = sum_{k >= j} U[i][k] R[j][k]
-      double* F = Fall + size_t(hd) * d * r;
-      for (int e = tid; e < d * r; e += nth) {
-        const int i = e / r, j = e % r;
-        double x = 0.0;
-        for (int k = j; k < r; ++k) x = fma(U[i * r + k], W[j * r + k], x);
-        F[e] = x;
+      if (b > a) {
+        const double h = 0.5 * (G[a * r + b] + G[b * r + a]);
+        G[a * r + b] = h;
+        G[b * r + a] = h;
       }
     }
+    __syncthreads();
+    ok = chol_upper(G, r, clamp * diag_max(G, r));
+    // F = U R^T
+    if (ok) gemm_4x4<false, true>(U, r, G, r, Fall + size_t(hd) * d * r, r, d, r, r);
   }
   if (tid == 0) gstat[hd * 8 + ok_slot] = ok ? 1 : 0;
 }
@@ -708,7 +716,9 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __rest
   *reinterpret_cast<h8*>(dst + i) = o;
 }
 
-// Means of rows [off[b], off[b+1]) of a group-major [BH][N][d] tensor, one wave per group.
+// Means of rows [off[b], off[b+1]) of a group-major [BH][N][d] tensor, one wave per group: d / 8
+// lanes cover a row with 16-byte loads, so one load instruction reads 64 / (d / 8) rows; the row
+// slots are summed across lanes at the end.
 template <int DT>
 __global__ __launch_bounds__(256) void group_mean_kernel(const void* __restrict__ src, int N, int d,
                                                          const int* __restrict__ off, const int* __restrict__ ngroups,
@@ -721,19 +731,35 @@ __global__ __launch_bounds__(256) void group_mean_kernel(const void* __restrict_
     for (int c = lane; c < d; c += 64) o[c] = 0.0;
     return;
   }
+  const int L = d >> 3, step = 64 / L, slot = lane / L, sub = lane % L;
   const int r0 = off[size_t(hd) * (C + 1) + b], r1 = off[size_t(hd) * (C + 1) + b + 1];
-  double a0 = 0.0, a1 = 0.0;
-  for (int rr = r0; rr < r1; ++rr) {
-    const size_t base = (size_t(hd) * N + rr) * d;
-    a0 += load_elem<DT>(src, base + lane);
-    if (lane + 64 < d) a1 += load_elem<DT>(src, base + lane + 64);
+  double acc[8] = {};
+  int rr = r0 + slot;
+  for (; rr + step < r1; rr += 2 * step) {
+    float x[8], y[8];
+    load8<DT>(src, (int64_t(hd) * N + rr) * d + sub * 8, x);
+    load8<DT>(src, (int64_t(hd) * N + rr + step) * d + sub * 8, y);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += double(x[c]) + double(y[c]);
   }
-  const double inv = 1.0 / double(r1 - r0);
-  o[lane] = a0 * inv;
-  if (lane + 64 < d) o[lane + 64] = a1 * inv;
+  if (rr < r1) {
+    float x[8];
+    load8<DT>(src, (int64_t(hd) * N + rr) * d + sub * 8, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += double(x[c]);
+  }
+  for (int o2 = L; o2 < 64; o2 <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], o2);
+  if (slot == 0) {
+    const double inv = 1.0 / double(r1 - r0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[sub * 8 + c] = acc[c] * inv;
+  }
 }
 
-// c_a = mean of phi_Q over group a (App. A.2), members listed by perm.
+// c_a = mean of phi_Q over group a (App. A.2), members listed by perm.  One wave per group: each
+// half-wave reads a member row as 16-byte pairs, two rows per step, four steps in flight.
 __global__ __launch_bounds__(256) void group_mean_perm_kernel(const double* __restrict__ feat, int n, int r,
                                                               const int* __restrict__ perm,
                                                               const int* __restrict__ off,
@@ -741,29 +767,57 @@ __global__ __launch_bounds__(256) void group_mean_perm_kernel(const double* __re
                                                               double* __restrict__ out) {
   const int hd = blockIdx.y;
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (b >= C || b >= ngroups[hd] || lane >= r) return;
+  if (b >= C || b >= ngroups[hd]) return;
+  const int half = lane >> 5, col = (lane & 31) * 2;
+  const bool act = col < r;
   const int r0 = off[size_t(hd) * (C + 1) + b], r1 = off[size_t(hd) * (C + 1) + b + 1];
-  double a = 0.0;
-  for (int p = r0; p < r1; ++p) a += feat[(size_t(hd) * n + perm[size_t(hd) * n + p]) * r + lane];
-  out[(size_t(hd) * C + b) * r + lane] = a / double(r1 - r0);
+  const int* pm = perm + size_t(hd) * n;
+  const double* fh = feat + size_t(hd) * n * r + (act ? col : 0);
+  double a0 = 0.0, a1 = 0.0;
+  int p = r0 + half;
+  for (; p + 6 < r1; p += 8) {
+    double2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const double2*>(fh + size_t(pm[p + 2 * u]) * r);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a0 += v[u].x;
+      a1 += v[u].y;
+    }
+  }
+  for (; p < r1; p += 2) {
+    const double2 v = *reinterpret_cast<const double2*>(fh + size_t(pm[p]) * r);
+    a0 += v.x;
+    a1 += v.y;
+  }
+  a0 += __shfl_xor(a0, 32);
+  a1 += __shfl_xor(a1, 32);
+  if (half == 0 && act) {
+    const double inv = 1.0 / double(r1 - r0);
+    out[(size_t(hd) * C + b) * r + col] = a0 * inv;
+    out[(size_t(hd) * C + b) * r + col + 1] = a1 * inv;
+  }
 }
 
-// d_i = |phi_Q(q_i) - c_a| for every video query row (App. A.2), original order.
+// d_i = |phi_Q(q_i) - c_a| for every video query row (App. A.2), original order.  16 lanes per row,
+// strided over the r coordinates, reduced across those lanes.
 __global__ __launch_bounds__(256) void qdist_kernel(const double* __restrict__ feat, int n, int r,
                                                     const int* __restrict__ lab, const double* __restrict__ cbar,
                                                     int C, double* __restrict__ out) {
   const int hd = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int a = lab[size_t(hd) * n + i];
-  const double* f = feat + (size_t(hd) * n + i) * r;
-  const double* c = cbar + (size_t(hd) * C + a) * r;
+  const int i = blockIdx.x * 16 + (threadIdx.x >> 4), sub = threadIdx.x & 15;
   double s = 0.0;
-  for (int e = 0; e < r; ++e) {
-    const double t = f[e] - c[e];
-    s = fma(t, t, s);
+  if (i < n) {
+    const int a = lab[size_t(hd) * n + i];
+    const double* f = feat + (size_t(hd) * n + i) * r;
+    const double* c = cbar + (size_t(hd) * C + a) * r;
+    for (int e = sub; e < r; e += 16) {
+      const double t = f[e] - c[e];
+      s = fma(t, t, s);
+    }
   }
-  out[size_t(hd) * n + i] = sqrt(s);
+  for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (i < n && sub == 0) out[size_t(hd) * n + i] = sqrt(s);
 }
 
 // ------------------------------------------------------------------ host drivers
@@ -810,7 +864,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
   allow_lds(eigen_factor_kernel, jac_smem);
-  const size_t sub_smem = 2 * size_t(d) * (p.rK > p.rQ ? p.rK : p.rQ) * sizeof(double);
+  const int rmx = p.rK > p.rQ ? p.rK : p.rQ;
+  const size_t sub_smem = (2 * size_t(d) * rmx + size_t(rmx) * rmx) * sizeof(double);
   allow_lds(subspace_factor_kernel, sub_smem);
   if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
     hipLaunchKernelGGL(subspace_factor_kernel, dim3(BH), dim3(256), sub_smem, st, metric, warm->FK, d, p.rK,
@@ -867,7 +922,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   SPR_CHECK_LAUNCH();
   // M_Q and F_Q
   double* kt = wsp<double>(ws, L.ktilde);
-  hipLaunchKernelGGL(ktilde_kernel, dim3(BH), dim3(d), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
+  hipLaunchKernelGGL(ktilde_kernel, dim3(BH), dim3(1024), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
   hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
                      metric);
   if (warm)
@@ -905,7 +960,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   double* cbar = wsp<double>(ws, L.cbar);
   hipLaunchKernelGGL(group_mean_perm_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, phiQ, Nv, p.rQ,
                      out.q_perm, out.q_off, out.n_q, p.Cq, cbar);
-  hipLaunchKernelGGL(qdist_kernel, dim3(ceil_div(Nv, 256), BH), dim3(256), 0, st, phiQ, Nv, p.rQ, out.q_label, cbar,
+  hipLaunchKernelGGL(qdist_kernel, dim3(ceil_div(Nv, 16), BH), dim3(256), 0, st, phiQ, Nv, p.rQ, out.q_label, cbar,
                      p.Cq, out.qdist);
   SPR_CHECK_LAUNCH();
   return SPR_OK;

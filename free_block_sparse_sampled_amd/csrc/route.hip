@@ -12,7 +12,8 @@
 
 namespace spr {
 
-// Per key (group-major order): u_j = v_j . vbar_b(j) and w_j = |v_j|^2, fp64.
+// Per key (group-major order): u_j = v_j . vbar_b(j) and w_j = |v_j|^2, fp64.  d / 8 lanes per
+// key, eight consecutive elements each (one 16-byte load for bf16), reduced across those lanes.
 template <int DT>
 __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp, int N, int Nv, int d,
                                                     const int* __restrict__ kv_perm,
@@ -20,19 +21,28 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
                                                     const double* __restrict__ vbar, int Ck,
                                                     double* __restrict__ vstat) {
   const int hd = blockIdx.y;
-  const int pos = blockIdx.x * 256 + threadIdx.x;
-  if (pos >= Nv) return;
-  const int b = kv_label[size_t(hd) * Nv + kv_perm[size_t(hd) * Nv + pos]];
-  const double* vb = vbar + (size_t(hd) * Ck + b) * d;
-  const size_t base = (size_t(hd) * N + pos) * d;
+  const int L = d >> 3;
+  const int pos = blockIdx.x * (256 / L) + threadIdx.x / L, sub = threadIdx.x % L;
   double u = 0.0, w = 0.0;
-  for (int c = 0; c < d; ++c) {
-    const double x = load_elem<DT>(Vp, base + c);
-    u = fma(x, vb[c], u);
-    w = fma(x, x, w);
+  if (pos < Nv) {
+    const int b = kv_label[size_t(hd) * Nv + kv_perm[size_t(hd) * Nv + pos]];
+    const double* vb = vbar + (size_t(hd) * Ck + b) * d + sub * 8;
+    float x[8];
+    load8<DT>(Vp, (int64_t(hd) * N + pos) * d + sub * 8, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u = fma(double(x[c]), vb[c], u);
+      w = fma(double(x[c]), double(x[c]), w);
+    }
   }
-  vstat[(size_t(hd) * Nv + pos) * 2 + 0] = u;
-  vstat[(size_t(hd) * Nv + pos) * 2 + 1] = w;
+  for (int o = L >> 1; o > 0; o >>= 1) {
+    u += __shfl_xor(u, o);
+    w += __shfl_xor(w, o);
+  }
+  if (pos < Nv && sub == 0) {
+    vstat[(size_t(hd) * Nv + pos) * 2 + 0] = u;
+    vstat[(size_t(hd) * Nv + pos) * 2 + 1] = w;
+  }
 }
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
@@ -399,7 +409,7 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   double* scores = out.scores ? out.scores : ws_ptr<double>(ws, L.scores);
   int* gstat = ws_ptr<int>(ws, L.gstat);
   int* pstat = ws_ptr<int>(ws, L.pstat);
-  hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256), BH), dim3(256), 0, st, part.Vp, N, Nv, d,
+  hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256 / (d / 8)), BH), dim3(256), 0, st, part.Vp, N, Nv, d,
                      part.kv_perm, part.kv_label, part.vbar, p.Ck, vstat);
   double* lbar = ws_ptr<double>(ws, L.lbar);
   const dim3 lgrid(ceil_div(p.Cq, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
