@@ -181,7 +181,7 @@ struct Workspace {
   size_t fitH;       // double [BH][d][d]        right-hand sides, then B
   size_t fitS;       // double [BH][4][d]        mu_X, sd, mu_R, weights scratch
   size_t fitW;       // double [BH][M]           unit-mean weights
-  size_t applyB;     // float  [BH][d][d]        I + diag(1/sd) B
+  size_t applyB;     // bf16   [BH][2][d][d]     E^T = (diag(1/sd) B)^T, high then low part
   size_t applyC;     // float  [BH][d]           mu_R - (mu_X / sd) B
   size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
   size_t ntiles;     // int    [BH]              tiles used per head

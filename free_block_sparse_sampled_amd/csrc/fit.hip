@@ -13,42 +13,63 @@
 
 namespace spr {
 
+// Probe features and residuals of one head and 32 columns per block: thread (column c,
+// stripe s) takes probes p = s, s + 8, ...; the weighted means and variance are combined over
+// the 8 stripes in LDS.
 __global__ __launch_bounds__(256) void fit_prep_kernel(const float* __restrict__ o_sp, const float* __restrict__ o_probe,
                                                        const int* __restrict__ probe_idx, const double* __restrict__ probe_w,
                                                        const int* __restrict__ q_pos, int N, int Nv, int d, int M,
                                                        double std_eps, double* __restrict__ Xb, double* __restrict__ Rb,
                                                        double* __restrict__ S, double* __restrict__ Wt) {
   __shared__ double red[32];
-  const int hd = blockIdx.x;
+  __shared__ double part[2][8][32];
+  const int hd = blockIdx.y, c = blockIdx.x * 32 + (threadIdx.x & 31), st = threadIdx.x >> 5;
   const int* pidx = probe_idx + size_t(hd) * M;
   const double* pw = probe_w + size_t(hd) * M;
   double ws = 0.0;
   for (int p = threadIdx.x; p < M; p += blockDim.x) ws += pw[p];
   const double wsum = block_sum_d(ws, red);
-  for (int p = threadIdx.x; p < M; p += blockDim.x) Wt[size_t(hd) * M + p] = double(M) * pw[p] / wsum;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    double mx = 0.0, mr = 0.0;
-    for (int p = 0; p < M; ++p) {
-      const int pos = q_pos[size_t(hd) * Nv + pidx[p]];
-      const double x = o_sp[(size_t(hd) * N + pos) * d + c];
-      const double r = double(o_probe[(size_t(hd) * M + p) * d + c]) - x;
-      const double al = pw[p] / wsum;
-      mx = fma(al, x, mx);
-      mr = fma(al, r, mr);
-      Xb[(size_t(hd) * M + p) * d + c] = x;
-      Rb[(size_t(hd) * M + p) * d + c] = r;
-    }
-    double var = 0.0;
-    for (int p = 0; p < M; ++p) {
-      const double t = Xb[(size_t(hd) * M + p) * d + c] - mx;
-      var = fma(pw[p] / wsum, t * t, var);
-    }
-    const double sd = sqrt(var + std_eps);
-    for (int p = 0; p < M; ++p) {
-      double* xp = Xb + (size_t(hd) * M + p) * d + c;
-      *xp = (*xp - mx) / sd;
-      Rb[(size_t(hd) * M + p) * d + c] -= mr;
-    }
+  if (blockIdx.x == 0)
+    for (int p = threadIdx.x; p < M; p += blockDim.x) Wt[size_t(hd) * M + p] = double(M) * pw[p] / wsum;
+  double* xb = Xb + size_t(hd) * M * d + c;
+  double* rb = Rb + size_t(hd) * M * d + c;
+  double mx = 0.0, mr = 0.0;
+#pragma unroll 4
+  for (int p = st; p < M; p += 8) {
+    const int pos = q_pos[size_t(hd) * Nv + pidx[p]];
+    const double x = o_sp[(size_t(hd) * N + pos) * d + c];
+    const double r = double(o_probe[(size_t(hd) * M + p) * d + c]) - x;
+    const double al = pw[p] / wsum;
+    mx = fma(al, x, mx);
+    mr = fma(al, r, mr);
+    xb[size_t(p) * d] = x;
+    rb[size_t(p) * d] = r;
+  }
+  part[0][st][threadIdx.x & 31] = mx;
+  part[1][st][threadIdx.x & 31] = mr;
+  __syncthreads();
+  mx = 0.0;
+  mr = 0.0;
+  for (int t = 0; t < 8; ++t) {
+    mx += part[0][t][threadIdx.x & 31];
+    mr += part[1][t][threadIdx.x & 31];
+  }
+  double var = 0.0;
+  for (int p = st; p < M; p += 8) {
+    const double t = xb[size_t(p) * d] - mx;
+    var = fma(pw[p] / wsum, t * t, var);
+  }
+  __syncthreads();
+  part[0][st][threadIdx.x & 31] = var;
+  __syncthreads();
+  var = 0.0;
+  for (int t = 0; t < 8; ++t) var += part[0][t][threadIdx.x & 31];
+  const double sd = sqrt(var + std_eps);
+  for (int p = st; p < M; p += 8) {
+    xb[size_t(p) * d] = (xb[size_t(p) * d] - mx) / sd;
+    rb[size_t(p) * d] -= mr;
+  }
+  if (st == 0) {
     S[(size_t(hd) * 4 + 0) * d + c] = mx;
     S[(size_t(hd) * 4 + 1) * d + c] = sd;
     S[(size_t(hd) * 4 + 2) * d + c] = mr;
@@ -87,137 +108,280 @@ __global__ __launch_bounds__(256) void normal_eq_kernel(const double* __restrict
   Hm[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = h;
 }
 
-// In-LDS fp64 Cholesky G = L L^T (right-looking), then B = L^-T L^-1 H with one thread per
-// column of H.  A pivot <= 0 (possible only with lam = 0) gives B = 0: the mean-only
-// correction, flagged in head_status.  Finally the affine map of the apply step.
-__global__ __launch_bounds__(256) void cholesky_solve_kernel(const double* __restrict__ Gall, double* __restrict__ Hall,
-                                                             const double* __restrict__ S, int d,
-                                                             float* __restrict__ applyB, float* __restrict__ applyC,
-                                                             double* __restrict__ fit_state, const int* __restrict__ gstat,
-                                                             int* __restrict__ head_status) {
-  extern __shared__ double Lm[];  // d x d row-major
-  __shared__ int fail;
-  const int hd = blockIdx.x;
-  const double* Gm = Gall + size_t(hd) * d * d;
-  double* Hm = Hall + size_t(hd) * d * d;
-  for (int e = threadIdx.x; e < d * d; e += blockDim.x) Lm[e] = Gm[e];
-  if (threadIdx.x == 0) fail = 0;
-  __syncthreads();
-  for (int k = 0; k < d; ++k) {
-    const double pivot = Lm[k * d + k];
-    if (!(pivot > 0.0)) {
-      if (threadIdx.x == 0) fail = 1;
-      break;  // uniform: every thread read the same pivot
+// C (m x n, row stride ldc) = op(A) B with 4 x 4 register tiles per thread; op(A)(i, k) is
+// A[i * lda + k], or A[k * lda + i] when AT; B(k, j) = B[k * ldb + j]; m, n multiples of 4.
+template <bool AT>
+__device__ inline void fit_gemm(const double* A, int lda, const double* B, int ldb, double* C, int ldc, int m, int n,
+                                int K) {
+  const int tr = m / 4, tc = n / 4;
+  for (int t = threadIdx.x; t < tr * tc; t += blockDim.x) {
+    const int i0 = (t / tc) * 4, j0 = (t % tc) * 4;
+    double acc[4][4] = {};
+#pragma unroll 2
+    for (int k = 0; k < K; ++k) {
+      double a[4], b[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) a[x] = AT ? A[size_t(k) * lda + i0 + x] : A[size_t(i0 + x) * lda + k];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) b[y] = B[size_t(k) * ldb + j0 + y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
     }
-    const double lkk = sqrt(pivot);
-    __syncthreads();
-    for (int i = k + 1 + threadIdx.x; i < d; i += blockDim.x) Lm[i * d + k] /= lkk;
-    __syncthreads();
-    if (threadIdx.x == 0) Lm[k * d + k] = lkk;
-    const int m = d - k - 1;
-    for (int e = threadIdx.x; e < m * m; e += blockDim.x) {
-      const int i = k + 1 + e / m, j = k + 1 + e % m;
-      if (j <= i) Lm[i * d + j] -= Lm[i * d + k] * Lm[j * d + k];
-    }
-    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) C[size_t(i0 + x) * ldc + j0 + y] = acc[x][y];
   }
-  __syncthreads();
-  const bool failed = fail != 0;
-  if (threadIdx.x < d) {
-    const int j = threadIdx.x;
-    if (failed) {
-      for (int i = 0; i < d; ++i) Hm[size_t(i) * d + j] = 0.0;
-    } else {
-      for (int i = 0; i < d; ++i) {  // forward: L y = h
-        double s = Hm[size_t(i) * d + j];
-        for (int kk = 0; kk < i; ++kk) s -= Lm[i * d + kk] * Hm[size_t(kk) * d + j];
-        Hm[size_t(i) * d + j] = s / Lm[i * d + i];
-      }
-      for (int i = d - 1; i >= 0; --i) {  // backward: L^T b = y
-        double s = Hm[size_t(i) * d + j];
-        for (int kk = i + 1; kk < d; ++kk) s -= Lm[kk * d + i] * Hm[size_t(kk) * d + j];
-        Hm[size_t(i) * d + j] = s / Lm[i * d + i];
-      }
-    }
-  }
-  __syncthreads();
-  const double* mx = S + (size_t(hd) * 4 + 0) * d;
-  const double* sd = S + (size_t(hd) * 4 + 1) * d;
-  const double* mr = S + (size_t(hd) * 4 + 2) * d;
-  for (int e = threadIdx.x; e < d * d; e += blockDim.x) {
-    const int i = e / d, j = e % d;
-    applyB[size_t(hd) * d * d + e] = float((i == j ? 1.0 : 0.0) + Hm[e] / sd[i]);
-  }
-  if (threadIdx.x < d) {
-    const int j = threadIdx.x;
-    double c = mr[j];
-    for (int i = 0; i < d; ++i) c -= mx[i] / sd[i] * Hm[size_t(i) * d + j];
-    applyC[size_t(hd) * d + j] = float(c);
-  }
-  if (fit_state) {
-    double* fs = fit_state + size_t(hd) * (3 * d + d * d);
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-      fs[c] = mx[c];
-      fs[d + c] = sd[c];
-      fs[2 * d + c] = mr[c];
-    }
-    for (int e = threadIdx.x; e < d * d; e += blockDim.x) fs[3 * d + e] = Hm[e];
-  }
-  if (threadIdx.x == 0) head_status[hd] = gstat[hd * 8 + 0] | (failed ? SPR_HS_CHOLESKY_FALLBACK : 0);
 }
 
-// O^hat rows for 64 group-major positions: corrected video rows scattered to their original
-// row, text rows copied.  Thread = 4 rows x 8 columns; X tile stored transposed in LDS.
-template <int D, int OUT_DT>
-__global__ __launch_bounds__(256) void apply_kernel(const float* __restrict__ o_sp, const int* __restrict__ q_perm,
-                                                    const float* __restrict__ applyB, const float* __restrict__ applyC,
-                                                    int N, int Nv, void* __restrict__ out) {
-  extern __shared__ float fsm[];
-  float* Bs = fsm;               // [D][D]
-  float* XT = fsm + D * D;       // [D][65]
-  const int hd = blockIdx.y, row0 = blockIdx.x * 64;
-  const float* Bm = applyB + size_t(hd) * D * D;
-  for (int e = threadIdx.x * 4; e < D * D; e += 1024) *reinterpret_cast<float4*>(Bs + e) = *reinterpret_cast<const float4*>(Bm + e);
-  for (int e = threadIdx.x; e < 64 * D; e += 256) {
-    const int rr = e / D, c = e % D, pos = row0 + rr;
-    XT[c * 65 + rr] = pos < N ? o_sp[(size_t(hd) * N + pos) * D + c] : 0.f;
+// Round to the nearest bf16 (ties to even) as a bit pattern.
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Per head, one workgroup of 8 D threads: thread t owns column b = t / 8 of the d x d matrix,
+// rows a = (t % 8) + 8 i (i < D / 8) in registers, so the 8 owners of a column sit in adjacent
+// lanes.
+//  - Upper Cholesky G = R^T R, right-looking: step k publishes row k of the reduced matrix in
+//    LDS (double-buffered, one barrier per step), every thread scales it by 1 / sqrt(pivot)
+//    and updates its own entries a_ab -= r_ka r_kb (k < a <= b).
+//  - R^{-1} row by row from the bottom (R T = I): T_ij = -(sum_{i<k<=j} R_ik T_kj) / R_ii,
+//    T_ii = 1 / R_ii; row i of R is published in LDS, each thread sums over its own rows k
+//    and the 8 owners of column j combine their sums by lane shuffles.
+//  - B = R^{-1} (R^{-T} H) by two register-tiled products (R^{-1} in LDS; R^{-T} H goes to the
+//    G buffer, B to the H buffer).
+// A pivot <= 0 (possible only with lam = 0) gives B = 0: the mean-only correction, flagged in
+// head_status.  Finally the affine map of the apply step: E = diag(1 / sd) B, stored transposed
+// (E^T[n][k]) as bf16 high and low parts so that hi + lo carries E to about 2^-16, and
+// c = mu_R - (mu_X / sd) B in fp32.
+template <int D>
+__global__ __launch_bounds__(8 * D) void cholesky_solve_kernel(double* __restrict__ Gall, double* __restrict__ Hall,
+                                                               const double* __restrict__ S,
+                                                               uint16_t* __restrict__ applyE,
+                                                               float* __restrict__ applyC,
+                                                               double* __restrict__ fit_state,
+                                                               const int* __restrict__ gstat,
+                                                               int* __restrict__ head_status) {
+  constexpr int NI = D / 8;
+  extern __shared__ double Rm[];  // D x D row-major (R^{-1}), then scratch
+  __shared__ double rowbuf[2][D];
+  const int hd = blockIdx.x, tid = threadIdx.x, nth = 8 * D;
+  const int b = tid >> 3, s = tid & 7;
+  double* Gm = Gall + size_t(hd) * D * D;
+  double* Hm = Hall + size_t(hd) * D * D;
+  double A[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) A[i] = Gm[size_t(s + 8 * i) * D + b];
+  // Row k = 8 ib + s0 lives in register slot ib of the threads with s == s0.  The slot loop is
+  // unrolled so that every register index is a constant (a runtime index would send the array
+  // to scratch memory).
+  bool failed = false;
+#pragma unroll
+  for (int ib = 0; ib < NI; ++ib) {
+#pragma unroll 1
+    for (int s0 = 0; s0 < 8; ++s0) {
+      const int k = 8 * ib + s0;
+      double* rb = rowbuf[k & 1];
+      if (s == s0) rb[b] = A[ib];
+      __syncthreads();
+      const double piv = rb[k];
+      if (!(piv > 0.0)) {  // uniform: every thread read the same pivot
+        failed = true;
+        break;
+      }
+      const double inv = 1.0 / sqrt(piv);
+      const double rkb = b > k ? rb[b] * inv : (b == k ? sqrt(piv) : 0.0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (i < ib) continue;  // rows above the pivot row are final
+        const int a = s + 8 * i;
+        const double upd = fma(-rb[a] * inv, rkb, A[i]);
+        A[i] = a == k ? rkb : (a > k && a <= b ? upd : A[i]);
+      }
+    }
+    if (failed) break;
+  }
+  __syncthreads();  // the last step's row buffer is the first one the inverse writes
+  if (!failed) {
+    // the strict lower triangle holds leftovers of G: clear it
+#pragma unroll
+    for (int i = 0; i < NI; ++i) A[i] = s + 8 * i > b ? 0.0 : A[i];
+#pragma unroll
+    for (int ib = NI - 1; ib >= 0; --ib) {
+#pragma unroll 1
+      for (int s0 = 7; s0 >= 0; --s0) {
+        const int i0 = 8 * ib + s0;
+        double* rb = rowbuf[i0 & 1];
+        if (s == s0) rb[b] = A[ib];
+        __syncthreads();
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          if (i < ib) continue;  // rows k <= i0 do not enter row i0 of the inverse
+          const int kk = s + 8 * i;
+          part = kk > i0 && kk <= b ? fma(rb[kk], A[i], part) : part;
+        }
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 4);
+        const double rii = rb[i0];
+        const double t = b > i0 ? -part / rii : (b == i0 ? 1.0 / rii : 0.0);
+        A[ib] = s == s0 ? t : A[ib];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) Rm[(s + 8 * i) * D + b] = A[i];
+    __syncthreads();
+    fit_gemm<true>(Rm, D, Hm, D, Gm, D, D, D, D);  // Y = R^{-T} H
+    __syncthreads();
+    fit_gemm<false>(Rm, D, Gm, D, Hm, D, D, D, D);  // B = R^{-1} Y
+  } else {
+    for (int e = tid; e < D * D; e += nth) Hm[e] = 0.0;
   }
   __syncthreads();
-  constexpr int CQ = D / 8;          // column blocks of 8
-  constexpr int RQ = 256 / CQ;       // row groups
-  constexpr int RPT = 64 / RQ;       // rows per thread
-  const int cq = threadIdx.x % CQ, rq = threadIdx.x / CQ;
-  float acc[RPT][8];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = applyC[size_t(hd) * D + cq * 8 + j];
-  for (int k = 0; k < D; ++k) {
-    float xr[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) xr[i] = XT[k * 65 + rq * RPT + i];
-    const float4 b0 = *reinterpret_cast<const float4*>(Bs + k * D + cq * 8);
-    const float4 b1 = *reinterpret_cast<const float4*>(Bs + k * D + cq * 8 + 4);
-    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xr[i], bb[j], acc[i][j]);
+  const double* mx = S + (size_t(hd) * 4 + 0) * D;
+  const double* sd = S + (size_t(hd) * 4 + 1) * D;
+  const double* mr = S + (size_t(hd) * 4 + 2) * D;
+  double* isd = Rm;      // 1 / sd
+  double* wmx = Rm + D;  // mu_X / sd
+  for (int c = tid; c < D; c += nth) {
+    isd[c] = 1.0 / sd[c];
+    wmx[c] = mx[c] / sd[c];
   }
+  __syncthreads();
+  uint16_t* Eh = applyE + size_t(hd) * 2 * D * D;
+  uint16_t* El = Eh + size_t(D) * D;
+  for (int e = tid; e < D * D; e += nth) {
+    const int k = e / D, n = e % D;
+    const float x = float(Hm[e] * isd[k]);
+    const uint16_t h = bf16_rne(x);
+    Eh[size_t(n) * D + k] = h;
+    El[size_t(n) * D + k] = bf16_rne(x - __uint_as_float(uint32_t(h) << 16));
+  }
+  {
+    // c_j = mu_R_j - sum_i (mu_X_i / sd_i) B_ij: column j = b, rows i = s + 8 t, lanes combined
+    double part = 0.0;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int pos = row0 + rq * RPT + i;
-    if (pos >= N) continue;
-    size_t dst;
-    if (pos < Nv) {
-      dst = (size_t(hd) * N + q_perm[size_t(hd) * Nv + pos]) * D + cq * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_out<OUT_DT>(out, dst + j, acc[i][j]);
-    } else {
-      dst = (size_t(hd) * N + pos) * D + cq * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_out<OUT_DT>(out, dst + j, XT[(cq * 8 + j) * 65 + rq * RPT + i]);
+    for (int i = 0; i < NI; ++i) part = fma(wmx[s + 8 * i], Hm[size_t(s + 8 * i) * D + b], part);
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    if (s == 0) applyC[size_t(hd) * D + b] = float(mr[b] - part);
+  }
+  if (fit_state) {
+    double* fs = fit_state + size_t(hd) * (3 * D + D * D);
+    for (int c = tid; c < D; c += nth) {
+      fs[c] = mx[c];
+      fs[D + c] = sd[c];
+      fs[2 * D + c] = mr[c];
     }
+    for (int e = tid; e < D * D; e += nth) fs[3 * D + e] = Hm[e];
+  }
+  if (tid == 0) head_status[hd] = gstat[hd * 8 + 0] | (failed ? SPR_HS_CHOLESKY_FALLBACK : 0);
+}
+
+typedef __bf16 fit_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float fit_f32x4_t __attribute__((ext_vector_type(4)));
+
+// O^hat = X + X E + c for 16-row tiles of group-major positions (X = O^sp rows, fp32), each
+// video row scattered to its original row, text rows copied.  X E runs on the bf16 matrix cores
+// as X_hi E_hi + X_hi E_lo + X_lo E_hi with fp32 accumulation (X = X_hi + X_lo, likewise E), the
+// identity term X stays exact fp32.  E^T (hi and lo) sits in LDS; each wave takes 16-row tiles,
+// loads them straight into A fragments (lane l: row l % 16, columns 32 ks + 8 (l / 16) .. + 7),
+// and turns the C fragments back into that row layout through a per-wave LDS tile.
+template <int D, int OUT_DT>
+__global__ __launch_bounds__(512) void apply_kernel(const float* __restrict__ o_sp, const int* __restrict__ q_perm,
+                                                    const uint16_t* __restrict__ applyE,
+                                                    const float* __restrict__ applyC, int N, int Nv,
+                                                    int tiles_per_block, void* __restrict__ out) {
+  constexpr int KS = D / 32, CT = D / 16, LDE = D + 8, LDO = D + 4;
+  extern __shared__ uint16_t esm[];  // [2][D][LDE] E^T hi, lo; then 8 x [16][LDO] fp32 tiles
+  float* otile = reinterpret_cast<float*>(esm + 2 * D * LDE) + (threadIdx.x >> 6) * 16 * LDO;
+  const int hd = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
+  const uint16_t* Eg = applyE + size_t(hd) * 2 * D * D;
+  for (int e = threadIdx.x * 8; e < 2 * D * D; e += 512 * 8) {
+    const int part = e / (D * D), n = (e % (D * D)) / D, k = e % D;
+    *reinterpret_cast<uint4*>(esm + (part * D + n) * LDE + k) = *reinterpret_cast<const uint4*>(Eg + e);
+  }
+  float cb[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) cb[ct] = applyC[size_t(hd) * D + ct * 16 + r16];
+  __syncthreads();
+  const int ntiles = (N + 15) / 16;
+  const int t0 = blockIdx.x * tiles_per_block, t1 = min(t0 + tiles_per_block, ntiles);
+  for (int t = t0 + w; t < t1; t += 8) {
+    const int pos = t * 16 + r16;
+    const float* xr = o_sp + (size_t(hd) * N + (pos < N ? pos : 0)) * D + 8 * kg;
+    float x[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 u = *reinterpret_cast<const float4*>(xr + 32 * ks);
+      const float4 v = *reinterpret_cast<const float4*>(xr + 32 * ks + 4);
+      x[ks][0] = u.x; x[ks][1] = u.y; x[ks][2] = u.z; x[ks][3] = u.w;
+      x[ks][4] = v.x; x[ks][5] = v.y; x[ks][6] = v.z; x[ks][7] = v.w;
+    }
+    fit_f32x4_t acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = fit_f32x4_t{cb[ct], cb[ct], cb[ct], cb[ct]};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fit_bf16x8_t ah, al;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint16_t h = bf16_rne(x[ks][c]);
+        const float hf = __uint_as_float(uint32_t(h) << 16);
+        ah[c] = __builtin_bit_cast(__bf16, h);
+        al[c] = __builtin_bit_cast(__bf16, bf16_rne(x[ks][c] - hf));
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int off = (ct * 16 + r16) * LDE + 32 * ks + 8 * kg;
+        const fit_bf16x8_t bh = *reinterpret_cast<const fit_bf16x8_t*>(esm + off);
+        const fit_bf16x8_t bl = *reinterpret_cast<const fit_bf16x8_t*>(esm + D * LDE + off);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[ct], 0, 0, 0);
+      }
+    }
+    // C fragment: lane l holds rows 4 (l / 16) + v, column 16 ct + l % 16
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) otile[(4 * kg + v) * LDO + ct * 16 + r16] = acc[ct][v];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (pos < N) {
+      const bool video = pos < Nv;
+      const size_t row = video ? size_t(q_perm[size_t(hd) * Nv + pos]) : size_t(pos);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int col = 32 * ks + 8 * kg;
+        const float4 u = *reinterpret_cast<const float4*>(otile + r16 * LDO + col);
+        const float4 v = *reinterpret_cast<const float4*>(otile + r16 * LDO + col + 4);
+        const float cx[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+        float y[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] = video ? x[ks][c] + cx[c] : x[ks][c];
+        const size_t dst = (size_t(hd) * N + row) * D + col;
+        if constexpr (OUT_DT == SPR_BF16) {
+          uint4 o;
+          o.x = uint32_t(bf16_rne(y[0])) | (uint32_t(bf16_rne(y[1])) << 16);
+          o.y = uint32_t(bf16_rne(y[2])) | (uint32_t(bf16_rne(y[3])) << 16);
+          o.z = uint32_t(bf16_rne(y[4])) | (uint32_t(bf16_rne(y[5])) << 16);
+          o.w = uint32_t(bf16_rne(y[6])) | (uint32_t(bf16_rne(y[7])) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + dst) = o;
+        } else {
+          float* o = static_cast<float*>(out) + dst;
+          *reinterpret_cast<float4*>(o) = make_float4(y[0], y[1], y[2], y[3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -231,12 +395,13 @@ __global__ void probe_write_kernel(const float* __restrict__ o_probe, const int*
 }
 
 template <int D, int OUT_DT>
-static void launch_apply(const spr_desc& desc, const float* o_sp, const int* q_perm, const float* B, const float* C,
+static void launch_apply(const spr_desc& desc, const float* o_sp, const int* q_perm, const uint16_t* E, const float* C,
                          void* out, hipStream_t st) {
-  const size_t sm = size_t(D) * D * sizeof(float) + size_t(D) * 65 * sizeof(float);
+  const size_t sm = size_t(2) * D * (D + 8) * sizeof(uint16_t) + size_t(8) * 16 * (D + 4) * sizeof(float);
+  constexpr int kTilesPerBlock = 64;
   allow_lds(apply_kernel<D, OUT_DT>, sm);
-  hipLaunchKernelGGL((apply_kernel<D, OUT_DT>), dim3(ceil_div(desc.N, 64), desc.B * desc.H), dim3(256), sm, st, o_sp,
-                     q_perm, B, C, desc.N, desc.N - desc.n_text, out);
+  hipLaunchKernelGGL((apply_kernel<D, OUT_DT>), dim3(ceil_div(ceil_div(desc.N, 16), kTilesPerBlock), desc.B * desc.H),
+                     dim3(512), sm, st, o_sp, q_perm, E, C, desc.N, desc.N - desc.n_text, kTilesPerBlock, out);
 }
 
 spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
@@ -251,16 +416,22 @@ spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const
   double* Hm = ws_ptr<double>(ws, L.fitH);
   double* S = ws_ptr<double>(ws, L.fitS);
   double* Wt = ws_ptr<double>(ws, L.fitW);
-  float* AB = ws_ptr<float>(ws, L.applyB);
+  uint16_t* AB = ws_ptr<uint16_t>(ws, L.applyB);
   float* AC = ws_ptr<float>(ws, L.applyC);
-  hipLaunchKernelGGL(fit_prep_kernel, dim3(BH), dim3(256), 0, st, o_sp, o_probe, route.probe_idx, route.probe_w,
+  hipLaunchKernelGGL(fit_prep_kernel, dim3(d / 32, BH), dim3(256), 0, st, o_sp, o_probe, route.probe_idx, route.probe_w,
                      part.q_pos, N, Nv, d, M, std_eps, Xb, Rb, S, Wt);
   hipLaunchKernelGGL(normal_eq_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M, lam, G, Hm);
   SPR_CHECK_LAUNCH();
   const size_t sm = size_t(d) * d * sizeof(double);
-  allow_lds(cholesky_solve_kernel, sm);
-  hipLaunchKernelGGL(cholesky_solve_kernel, dim3(BH), dim3(256), sm, st, G, Hm, S, d, AB, AC, fit_state,
-                     ws_ptr<int>(ws, L.gstat), head_status);
+  if (d == 128) {
+    allow_lds(cholesky_solve_kernel<128>, sm);
+    hipLaunchKernelGGL(cholesky_solve_kernel<128>, dim3(BH), dim3(1024), sm, st, G, Hm, S, AB, AC, fit_state,
+                       ws_ptr<int>(ws, L.gstat), head_status);
+  } else {
+    allow_lds(cholesky_solve_kernel<64>, sm);
+    hipLaunchKernelGGL(cholesky_solve_kernel<64>, dim3(BH), dim3(512), sm, st, G, Hm, S, AB, AC, fit_state,
+                       ws_ptr<int>(ws, L.gstat), head_status);
+  }
   SPR_CHECK_LAUNCH();
   if (d == 128) {
     if (out_dtype == SPR_BF16) launch_apply<128, SPR_BF16>(desc, o_sp, part.q_perm, AB, AC, out, st);

@@ -532,14 +532,16 @@ __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restr
 // ------------------------------------------------------------------ projection
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// phi = X F (Sec. 4.1) on v_mfma_f64_16x16x4f64, 128 rows per block (8 waves x 16 rows); with
-// RMS the rows are RMS-normalised as in App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  The
-// fp64 MFMA takes A[i][k] from lane i + 16k and B[k][j] from lane j + 16k, and returns
-// D[(lane / 16) + 4 v][lane % 16] in slot v.
+// phi = X F (Sec. 4.1) on v_mfma_f64_16x16x4f64; with RMS the rows are RMS-normalised as in
+// App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  The fp64 MFMA takes A[i][k] from lane i + 16k
+// and B[k][j] from lane j + 16k, and returns D[(lane / 16) + 4 v][lane % 16] in slot v.  F is
+// staged in LDS once per block; the block then walks `chunks` chunks of 128 rows (8 waves x 16
+// rows), the next chunk's rows loaded into registers (16-byte loads) while the current one is
+// multiplied, then widened to fp32 in LDS.
 template <int DT, bool RMS>
 __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
                                                       const double* __restrict__ Fall, int r, double eps,
-                                                      double* __restrict__ out, int* __restrict__ gstat) {
+                                                      double* __restrict__ out, int* __restrict__ gstat, int chunks) {
   extern __shared__ double smem[];
   const int d = g.d;
   const int NT = (r + 15) >> 4;
@@ -547,52 +549,82 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
   const int XS = d + 4;        // X tile row stride (floats)
   double* Fs = smem;                                      // [d][FS]
   float* Xs = reinterpret_cast<float*>(smem + d * FS);  // [128][XS]
-  const int hd = blockIdx.y, row0 = blockIdx.x * 128;
+  const int hd = blockIdx.y;
   const double* F = Fall + size_t(hd) * d * r;
   for (int e = threadIdx.x; e < d * FS; e += 512) {
     const int kk = e / FS, c = e % FS;
     Fs[e] = c < r ? F[size_t(kk) * r + c] : 0.0;
   }
   const int64_t base = g.base(hd);
-  for (int e = threadIdx.x; e < 128 * d; e += 512) {
-    const int rr = e / d, cc = e % d, row = row0 + rr;
-    Xs[rr * XS + cc] = row < rows ? load_elem<DT>(x, base + int64_t(row) * g.sn + cc) : 0.f;
-  }
-  __syncthreads();
+  // this thread's share of a chunk: groups of 8 elements e8 = threadIdx.x + 512 u, u < d / 32
+  const int per = d >> 5;  // 4 for d = 128, 2 for d = 64
+  float xv[4][8];
+  auto fetch = [&](int row0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < per) {
+        const int e = (threadIdx.x + 512 * u) * 8, rr = e / d, cc = e % d;
+        const int row = row0 + rr < rows ? row0 + rr : rows - 1;
+        load8<DT>(x, base + int64_t(row) * g.sn + cc, xv[u]);
+      }
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < per) {
+        const int e = (threadIdx.x + 512 * u) * 8, rr = e / d, cc = e % d;
+        float* dst = Xs + rr * XS + cc;
+        *reinterpret_cast<float4*>(dst) = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[u][4], xv[u][5], xv[u][6], xv[u][7]);
+      }
+    }
+  };
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
-  f64x4_t acc[4];
+  const int first = blockIdx.x * chunks * 128;
+  fetch(first);
+  for (int ch = 0; ch < chunks; ++ch) {
+    const int row0 = first + ch * 128;
+    if (row0 >= rows) break;
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (ch + 1 < chunks && row0 + 128 < rows) fetch(row0 + 128);
+    f64x4_t acc[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-  for (int ks = 0; ks < d / 4; ++ks) {
-    const double av = Xs[(w * 16 + r16) * XS + ks * 4 + gq];
-    const double* fr = Fs + (ks * 4 + gq) * FS + r16;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      if (nt < NT) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, fr[nt * 16], acc[nt], 0, 0, 0);
-  }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    double scale = 1.0;
-    const int row = row0 + w * 16 + gq + 4 * v;
-    if constexpr (RMS) {
-      double s2 = 0.0;
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int ks = 0; ks < d / 4; ++ks) {
+      const double av = Xs[(w * 16 + r16) * XS + ks * 4 + gq];
+      const double* fr = Fs + (ks * 4 + gq) * FS + r16;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        if (nt < NT) s2 = fma(acc[nt][v], acc[nt][v], s2);
-      s2 += __shfl_xor(s2, 1);
-      s2 += __shfl_xor(s2, 2);
-      s2 += __shfl_xor(s2, 4);
-      s2 += __shfl_xor(s2, 8);
-      const double rms = sqrt(s2 / double(r));
-      scale = 1.0 / fmax(rms, eps);
-      if (rms < eps && row < rows && r16 == 0) atomicOr(gstat + hd * 8 + 0, SPR_HS_RMS_FLOOR);
+        if (nt < NT) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, fr[nt * 16], acc[nt], 0, 0, 0);
     }
-    if (row < rows) {
-      double* o = out + (size_t(hd) * rows + row) * r;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int c = nt * 16 + r16;
-        if (nt < NT && c < r) o[c] = acc[nt][v] * scale;
+    for (int v = 0; v < 4; ++v) {
+      double scale = 1.0;
+      const int row = row0 + w * 16 + gq + 4 * v;
+      if constexpr (RMS) {
+        double s2 = 0.0;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) s2 = fma(acc[nt][v], acc[nt][v], s2);
+        s2 += __shfl_xor(s2, 1);
+        s2 += __shfl_xor(s2, 2);
+        s2 += __shfl_xor(s2, 4);
+        s2 += __shfl_xor(s2, 8);
+        const double rms = sqrt(s2 / double(r));
+        scale = 1.0 / fmax(rms, eps);
+        if (rms < eps && row < rows && r16 == 0) atomicOr(gstat + hd * 8 + 0, SPR_HS_RMS_FLOOR);
+      }
+      if (row < rows) {
+        double* o = out + (size_t(hd) * rows + row) * r;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int c = nt * 16 + r16;
+          if (nt < NT && c < r) o[c] = acc[nt][v] * scale;
+        }
       }
     }
   }
@@ -601,6 +633,22 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
 size_t project_smem(int d, int r) {
   const int NT = (r + 15) >> 4;
   return size_t(d) * (NT * 16 + 8) * sizeof(double) + size_t(128) * (d + 4) * sizeof(float);
+}
+
+// Chunks of 128 rows per projection block (one block per CU fits in LDS): the count in [4, 16]
+// with the shortest schedule, rounds of 256 blocks times chunks per block, the larger on ties.
+static int project_chunks(int rows, int BH) {
+  const int total = ceil_div(rows, 128);
+  int best = 4, best_cost = 1 << 30;
+  for (int c = 4; c <= 16; ++c) {
+    const int64_t blocks = int64_t(BH) * ceil_div(total, c);
+    const int64_t cost = (blocks + 255) / 256 * c;
+    if (cost <= best_cost) {
+      best = c;
+      best_cost = int(cost);
+    }
+  }
+  return best;
 }
 
 // ------------------------------------------------------------------ compaction
@@ -875,10 +923,11 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   SPR_CHECK_LAUNCH();
   // phi_K = K F_K
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
+  const int pchunks = project_chunks(Nv, BH);
   allow_lds(project_kernel<DT, false>, prj_smem);
   allow_lds(project_kernel<DT, true>, prj_smem);
-  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, k, g, Nv,
-                     out.FK, p.rK, p.rms_eps, phiK, gstat);
+  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
+                     prj_smem, st, k, g, Nv, out.FK, p.rK, p.rms_eps, phiK, gstat, pchunks);
   SPR_CHECK_LAUNCH();
   // K/V k-means
   KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
@@ -932,8 +981,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
                      gstat, warm ? 3 : -1);
   SPR_CHECK_LAUNCH();
   // phi_Q = RMSNorm(Q F_Q)
-  hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(Nv, 128), BH), dim3(512), prj_smem, st, q, g, Nv,
-                     out.FQ, p.rQ, p.rms_eps, phiQ, gstat);
+  hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
+                     prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks);
   SPR_CHECK_LAUNCH();
   // query k-means
   KmArgs qa = ka;
