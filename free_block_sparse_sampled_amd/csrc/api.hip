@@ -51,6 +51,7 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.tmax = sparse_tile_capacity(p.Cq, int(Nv), desc.n_text);
   L.tiles = take(BH * size_t(L.tmax) * 8 * 4);
   L.ntiles = take(BH * 4);
+  L.tile_prefix = take((BH + 1) * 4);
   L.total = o;
   return L;
 }

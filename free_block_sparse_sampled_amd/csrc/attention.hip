@@ -43,9 +43,10 @@ struct AttnParams {
   const void* v;
   HeadGeom g;
   // sparse routing
-  const int* tiles;      // [BH][tmax][8]: a0, row0, n0, a1, row1, n1 (row0 / row1 index Qp rows)
-  const int* ntiles;     // [BH]
-  int tmax;
+  const int* tiles;        // [BH][tmax][8]: a0, row0, n0, a1, row1, n1 (row0 / row1 index Qp rows)
+  const int* ntiles;       // [BH]
+  const int* tile_prefix;  // [BH + 1]: tiles of the heads before each head; [BH] = all tiles
+  int tmax, BH;
   const int* n_kv;
   const int* kv_off;     // [BH][Ck+1]
   const int* sel_cnt;    // [BH][Cq+1]
@@ -86,11 +87,26 @@ __device__ inline TileInfo decode_tile(const AttnParams& P) {
   t.row1 = t.n1 = 0;
   t.pair = false;
   if constexpr (MODE == MODE_SPARSE) {
-    if (int(blockIdx.x) >= P.ntiles[t.hd]) {
+    // Workgroups reach the 8 XCDs round-robin (block L on XCD L % 8), each XCD with its own L2.
+    // Block L takes tile j = L / 8 of the contiguous share of XCD L % 8 in the head-major list
+    // of all tiles, so one XCD works through a few heads at a time and its concurrent tiles
+    // share those heads' K/V groups in its L2.
+    const int total = P.tile_prefix[P.BH];
+    const int per = (total + 7) >> 3;
+    const int j = int(blockIdx.x) >> 3;
+    const int n = (int(blockIdx.x) & 7) * per + j;
+    if (j >= per || n >= total) {
       t.valid = false;
       return t;
     }
-    const int* td = P.tiles + (size_t(t.hd) * P.tmax + blockIdx.x) * 8;
+    int lo = 0, hi = P.BH;  // last head with tile_prefix[head] <= n
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P.tile_prefix[mid] <= n) lo = mid;
+      else hi = mid;
+    }
+    t.hd = lo;
+    const int* td = P.tiles + (size_t(t.hd) * P.tmax + (n - P.tile_prefix[lo])) * 8;
     t.a0 = td[0]; t.row0 = td[1]; t.n0 = td[2];
     t.a1 = td[3]; t.row1 = td[4]; t.n1 = td[5];
     t.pair = t.n1 > 0 && t.a1 != t.a0;
@@ -806,6 +822,21 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
 // ------------------------------------------------------------------ host drivers
 // Waves per block of the MFMA kernel: sparse tiles are two 64-row halves, dense and probe
 // tiles 128 rows.
+// Exclusive prefix of the per-head tile counts; prefix[BH] is the number of tiles of the call.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict__ ntiles, int BH,
+                                                           int* __restrict__ prefix) {
+  __shared__ int buf[1024];
+  int carry = 0;
+  for (int base = 0; base < BH; base += 1024) {
+    const int i = base + int(threadIdx.x);
+    int tot;
+    const int ex = block_exscan_i(i < BH ? ntiles[i] : 0, buf, &tot);
+    if (i < BH) prefix[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) prefix[BH] = carry;
+}
+
 template <int MODE>
 constexpr int mfma_waves() { return 8; }
 template <int MODE>
@@ -848,18 +879,22 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
   int* ntiles = ws_ptr<int>(ws, L.ntiles);
   hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, Nv, desc.n_text,
                      L.tmax, tiles, ntiles);
+  int* tprefix = ws_ptr<int>(ws, L.tile_prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, ntiles, BH, tprefix);
   SPR_CHECK_LAUNCH();
   AttnParams P = {};
   P.q = part.Qp; P.k = part.Kp; P.v = part.Vp;
   if (desc.dtype == SPR_BF16) P.v = ws_ptr<void>(ws, L.vh);
   P.g = make_geom(desc);
-  P.tiles = tiles; P.ntiles = ntiles; P.tmax = L.tmax;
+  P.tiles = tiles; P.ntiles = ntiles; P.tile_prefix = tprefix; P.tmax = L.tmax; P.BH = BH;
   P.n_kv = part.n_kv; P.kv_off = part.kv_off; P.sel_cnt = route.sel_cnt; P.sel_kv = route.sel_kv;
   P.Cq = p.Cq; P.Ck = p.Ck;
   P.o_sp = o_sp;
-  // bf16: one block per tile; fp32: one block per tile half
-  const int gx = desc.dtype == SPR_BF16 ? L.tmax : 2 * L.tmax;
-  return dispatch_d<MODE_SPARSE>(P, dim3(gx, BH), desc.d, desc.dtype, st);
+  // bf16: one block per tile, 1-D grid mapped onto the tile list (a multiple of 8 blocks, one
+  // share per XCD); fp32: one block per tile half, grid (2 tmax, BH)
+  const dim3 grid = desc.dtype == SPR_BF16 ? dim3(unsigned(8 * ceil_div64(int64_t(BH) * L.tmax, 8)))
+                                           : dim3(2 * L.tmax, BH);
+  return dispatch_d<MODE_SPARSE>(P, grid, desc.d, desc.dtype, st);
 }
 
 spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, const void* v, const int* probe_idx,

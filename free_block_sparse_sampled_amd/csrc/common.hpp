@@ -185,6 +185,7 @@ struct Workspace {
   size_t applyC;     // float  [BH][d]           mu_R - (mu_X / sd) B
   size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
   size_t ntiles;     // int    [BH]              tiles used per head
+  size_t tile_prefix;  // int  [BH + 1]          exclusive prefix of ntiles
   size_t total;
   int tmax;          // tile capacity per head
   int nblk;          // k-means assign blocks per head
