@@ -506,7 +506,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
       for (int v = 0; v < 4; ++v) pv[mt * 4 + v] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][v], scale, mneg));
   };
-  auto finish_pv = [&](const f32x4_t (&sacc)[4], float (&pv)[16], int vbuf) __attribute__((always_inline)) {
+  auto finish_pv = [&](const f32x4_t (&sacc)[4], float (&pv)[16], int vbuf, auto&& mid) __attribute__((always_inline)) {
     const _Float16* V = Vt + vbuf * VBUF;
     unsigned big = 0;
 #pragma unroll
@@ -534,6 +534,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = _Float16(pv[i]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[h], lacc, 0, 0, 0);
+    mid();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -545,10 +546,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
       }
     }
   };
-  auto softmax_pv = [&](f32x4_t (&sacc)[4], int vbuf) __attribute__((always_inline)) {
+  auto softmax_pv = [&](f32x4_t (&sacc)[4], int vbuf, auto&& mid) __attribute__((always_inline)) {
     float pv[16];
     exps(sacc, pv);
-    finish_pv(sacc, pv, vbuf);
+    finish_pv(sacc, pv, vbuf, mid);
   };
   // The scores of the next chunk on the matrix cores interleaved with the exponentials of this
   // chunk on the vector ALU (one K fragment read, one MFMA and two VALU operations per slot).
@@ -593,22 +594,40 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   f32x4_t sa[4], sb[4];
   if (wave_active && half_mask(0) != 0ull) qk(sa, 0);
   __syncthreads();  // step 0 overwrites K buffer 0
+  // The LDS staging of chunk c+2 runs inside the P V products of chunk c (its VALU and LDS
+  // writes issue while the matrix cores work); the loads of chunk c+4 reuse its registers after.
   auto step = [&](auto set, int c, f32x4_t (&s_cur)[4], f32x4_t (&s_nxt)[4]) __attribute__((always_inline)) {
-    store_from(set, c & 1, (c + 2) % 3);
-    load_to(set, c + 4);
+    auto stage = [&]() __attribute__((always_inline)) { store_from(set, c & 1, (c + 2) % 3); };
+    // the dense and probe kernels convert V while staging, which needs the registers the
+    // overlap would take: they stage first
+    constexpr bool kLate = SPARSE;
+    if constexpr (!kLate) {
+      stage();
+      load_to(set, c + 4);
+    }
+    auto mid = [&]() __attribute__((always_inline)) {
+      if constexpr (kLate) stage();
+    };
     if (w == 0) resolve(c + 5);
+    bool staged = !kLate;
     if (wave_active) {
       const unsigned long long mn = half_mask(c + 1), m = half_mask(c);
       if (__builtin_expect(m != ~0ull, 0) && m != 0ull) apply_mask(s_cur, m);
       if (__builtin_expect(mn != 0ull && m != 0ull, 1)) {
         float pv[16];
         qk_exps(s_nxt, (c + 1) & 1, s_cur, pv);
-        finish_pv(s_cur, pv, c % 3);
+        finish_pv(s_cur, pv, c % 3, mid);
+        staged = true;
       } else if (mn != 0ull) {
         qk(s_nxt, (c + 1) & 1);
       } else if (m != 0ull) {
-        softmax_pv(s_cur, c % 3);
+        softmax_pv(s_cur, c % 3, mid);
+        staged = true;
       }
+    }
+    if constexpr (kLate) {
+      if (!staged) stage();
+      load_to(set, c + 4);
     }
     __syncthreads();
   };
