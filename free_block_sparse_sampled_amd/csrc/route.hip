@@ -98,11 +98,42 @@ __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __re
     }
 }
 
+// e^x in fp64 by Tang's table method: x = (64 n + j) ln2 / 64 + r with |r| <= ln2 / 128,
+// e^x = 2^n 2^(j/64) e^r, e^r - 1 by its Taylor polynomial to degree 6 (truncation below 1e-19
+// relative); ln2 / 64 in two parts (the split of ln2 whose high part has 32 trailing zero bits)
+// so that n ln2_hi is exact.  T[j] = 2^(j/64).  About one ulp; arguments below -745 give 0.
+__device__ __forceinline__ double exp_table(double x, const double* T) {
+  constexpr double kInvL = 92.332482616893656877;        // 64 / ln2
+  constexpr double kLhi = 6.93147180369123816490e-01 / 64;  // high part of ln2, / 64 (exact)
+  constexpr double kLlo = 1.90821492927058770002e-10 / 64;  // ln2 - high part, / 64
+  x = fmax(x, -746.0);
+  const double n = __builtin_rint(x * kInvL);
+  const int ni = int(n);
+  double r = fma(-n, kLhi, x);
+  r = fma(-n, kLlo, r);
+  double p = fma(r, 1.0 / 720, 1.0 / 120);
+  p = fma(p, r, 1.0 / 24);
+  p = fma(p, r, 1.0 / 6);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p *= r;  // e^r - 1
+  const double t = T[ni & 63];
+  return ldexp(fma(t, p, t), ni >> 6);
+}
+
 // Scores of 64 query groups x 16 K/V groups.  The K/V groups are taken one at a time; their
-// keys (contiguous in group-major order) are staged in LDS in pieces of 64 and processed in
-// 16-key tiles: logits on the fp64 matrix cores (same fragment layout as the centroid logits),
-// then E = e^{logit - m_a} and the per-lane sums of E u and E^2 w in registers.  At the end of a
-// group the sums are reduced over the 16 lanes of each query group and the score is written.
+// keys (contiguous in group-major order) are staged in LDS as fp64 in pieces of 64 and
+// processed in 16-key tiles: logits on the fp64 matrix cores (same fragment layout as the
+// centroid logits), then E = e^{logit - m_a} and the per-lane sums of E u and E^2 w in
+// registers.  A key row is stored with column c at (c % 4) D / 4 + c / 4, so the D / 4 values a
+// lane feeds to the products (columns 4 ks + l / 16) are contiguous and load before them.  Keys
+// past a group's end are zero with u = w = 0 and add nothing.  At the end of a group the sums
+// are reduced over the 16 lanes of each query group and the score is written.
+constexpr int kScorePiece = 64;
+template <int D>
+constexpr size_t route_score_smem() {
+  return (size_t(kScorePiece) * (D + 2) + 2 * kScorePiece + 64 + 16) * sizeof(double);
+}
 template <int DT, int D>
 __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict__ Kp, int N, int Nv,
                                                           const double* __restrict__ qbar,
@@ -114,10 +145,14 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
                                                           const double* __restrict__ shift,
                                                           const double* __restrict__ vstat,
                                                           double* __restrict__ scores) {
-  constexpr int PIECE = 64;   // keys staged per piece
-  constexpr int KSD = D + 4;  // key row stride in LDS (floats)
-  __shared__ float Ks[PIECE * KSD];
-  __shared__ double us[PIECE], wsv[PIECE], vns[16];
+  constexpr int PIECE = kScorePiece;
+  constexpr int KSD = D + 2;  // key row stride in LDS (doubles)
+  extern __shared__ double rs_sm[];
+  double* Ks = rs_sm;                 // [PIECE][KSD]
+  double* us = Ks + PIECE * KSD;      // [PIECE]
+  double* wsv = us + PIECE;           // [PIECE]
+  double* T = wsv + PIECE;            // [64] 2^(j/64)
+  double* vns = T + 64;               // [16]
   const int hd = blockIdx.z;
   const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 16;
   const int nq = n_q[hd], nkv = n_kv[hd];
@@ -125,6 +160,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
   const int b1 = min(b0 + 16, nkv);
   const int* off = kv_off + size_t(hd) * (Ck + 1);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
+  if (threadIdx.x < 64) T[threadIdx.x] = exp2(double(threadIdx.x) / 64.0);
   double qa[D / 4];
   {
     const int a = a0 + w * 16 + r16;
@@ -160,28 +196,16 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
         const int jl = e / (D / 8), c8 = (e % (D / 8)) * 8;
         float x[8];
         if (jl < n) {
-          const size_t base = (size_t(hd) * N + p0 + jl) * D + c8;
-          if constexpr (DT == SPR_BF16) {
-            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Kp) + base);
-            const uint32_t q[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              x[2 * t] = __uint_as_float(q[t] << 16);
-              x[2 * t + 1] = __uint_as_float(q[t] & 0xFFFF0000u);
-            }
-          } else {
-            const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(Kp) + base);
-            const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(Kp) + base + 4);
-            x[0] = f0.x; x[1] = f0.y; x[2] = f0.z; x[3] = f0.w;
-            x[4] = f1.x; x[5] = f1.y; x[6] = f1.z; x[7] = f1.w;
-          }
+          load8<DT>(Kp, (int64_t(hd) * N + p0 + jl) * D + c8, x);
         } else {
 #pragma unroll
           for (int t = 0; t < 8; ++t) x[t] = 0.f;
         }
-        float* dst = Ks + jl * KSD + c8;
-        *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        // columns c8 .. c8 + 7 go to (c % 4) D / 4 + c / 4: two runs of 2 per residue class
+        double* dst = Ks + jl * KSD + c8 / 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          *reinterpret_cast<double2*>(dst + m * (D / 4)) = make_double2(x[m], x[m + 4]);
       }
       if (threadIdx.x < PIECE) {
         const int jl = threadIdx.x;
@@ -191,15 +215,21 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
       __syncthreads();
       for (int t = 0; t * 16 < n; ++t) {
         const int jl = t * 16 + r16;
-        f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
-        const float* kr = Ks + jl * KSD + gq;
+        const double* kr = Ks + jl * KSD + gq * (D / 4);
+        double kb[D / 4];
 #pragma unroll
-        for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], double(kr[ks * 4]), lg, 0, 0, 0);
-        const bool valid = jl < n;
+        for (int i = 0; i < D / 8; ++i) {
+          const double2 u = *reinterpret_cast<const double2*>(kr + 2 * i);
+          kb[2 * i] = u.x;
+          kb[2 * i + 1] = u.y;
+        }
+        f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks], lg, 0, 0, 0);
         const double uu = us[jl], ww = wsv[jl];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const double E = valid ? exp(lg[v] * inv - m_a[v]) : 0.0;
+          const double E = exp_table(fma(lg[v], inv, -m_a[v]), T);
           s1[v] = fma(E, uu, s1[v]);
           s2[v] = fma(E * E, ww, s2[v]);
         }
@@ -416,12 +446,16 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   if (d == 128) {
     hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
                        part.n_kv, p.Cq, p.Ck, lbar, shift);
-    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), 0, st, part.Kp, N, Nv, part.qbar, lbar,
+    allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
+    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), route_score_smem<128>(), st, part.Kp, N, Nv,
+                       part.qbar, lbar,
                        part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
   } else {
     hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
                        part.n_kv, p.Cq, p.Ck, lbar, shift);
-    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), 0, st, part.Kp, N, Nv, part.qbar, lbar,
+    allow_lds(route_score_kernel<DT, 64>, route_score_smem<64>());
+    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), route_score_smem<64>(), st, part.Kp, N, Nv,
+                       part.qbar, lbar,
                        part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
   }
   SPR_CHECK_LAUNCH();
