@@ -44,6 +44,12 @@ against the pages; the tests pin them against mathematics instead):
   Z^T Z at or below eig_clamp^2, or of U^T M U at or below eig_clamp, times the
   largest diagonal entry (or a zero previous column) sends the head back to the cold
   eigendecomposition.
+* Probe and estimator variants (Table 4; App. D.3, D.4): random probes are the M rows
+  with the smallest SplitMix64 draws of a separate probe stream (a sample without
+  replacement, nested in M); uniform spatiotemporal probes are M evenly spaced rows of
+  the row-major (t, h, w) sequence; both carry weights Nv / M.  The output truncation
+  takes the leading eigenvectors of Rbar^T W Rbar, eigenvalues at or below eig_clamp
+  times the largest counted as absent.
 """
 from __future__ import annotations
 
@@ -58,6 +64,7 @@ __all__ = [
     "project", "kmeans_assign", "kmeans_update", "kmeans", "compact_labels", "group_perm",
     "key_group_stats", "query_metric", "query_coords", "query_group_stats", "key_budget",
     "route_scores", "route_select", "route", "sparse_attention_rows", "dense_attention_rows",
+    "select_probes_random", "select_probes_uniform", "output_projector",
     "executed_density", "allocate_probes", "select_probes", "ridge_fit", "correct", "relative_error",
     "sparsepr_head", "cholesky_upper", "metric_factor_warm", "warm_centres",
 ]
@@ -84,6 +91,9 @@ class Params:
     lam: float = 1.0
     std_eps: float = 1e-6
     n_text: int = 0
+    probe_mode: str = "stratified"   # "stratified" | "random" | "uniform" (Table 4)
+    fit_family: str = "full"         # "full" | "mean" | "scalar" | "diag" (App. D.4)
+    out_rank: int = 0                # rank of the output truncation (App. D.3); 0: none
 
 
 # --------------------------------------------------------------------------- RNG
@@ -499,14 +509,54 @@ def select_probes(q_labels_c: np.ndarray, dist: np.ndarray, q_size: np.ndarray, 
     return np.array(rows, dtype=np.int64), np.array(w, dtype=np.float64), m
 
 
+PROBE_STREAM = 0x70726F6265  # "probe": the seed offset of the probe draws
+
+
+def select_probes_random(Nv: int, M: int, seed: int, head: int):
+    """Random probes (Table 4): the M video rows whose SplitMix64 draws
+    splitmix64(seed xor "probe", head Nv + i) are smallest (ties to the lower row), i.e. a
+    uniform sample without replacement whose draws for M probes contain those for fewer
+    (nested probes, App. D.3).  Listed in ascending row; weights Nv / M."""
+    keys = np.array([splitmix64(seed ^ PROBE_STREAM, head * Nv + i) for i in range(Nv)], dtype=np.uint64)
+    order = np.lexsort((np.arange(Nv), keys))
+    rows = np.sort(order[:M]).astype(np.int64)
+    return rows, np.full(M, Nv / M)
+
+
+def select_probes_uniform(Nv: int, M: int):
+    """Uniform spatiotemporal probes (Table 4): with tokens in row-major (t, h, w) order, rows
+    evenly spaced over the sequence, row_i = floor((2 i + 1) Nv / (2 M)) (the centre of each
+    of M equal stretches); weights Nv / M."""
+    i = np.arange(M, dtype=np.int64)
+    return (2 * i + 1) * Nv // (2 * M), np.full(M, Nv / M)
+
+
 # -------------------------------------------------------------------------- fit
-def ridge_fit(X: np.ndarray, R: np.ndarray, w: np.ndarray, lam: float, std_eps: float):
+def output_projector(Rb: np.ndarray, wt: np.ndarray, r: int, clamp: float) -> np.ndarray:
+    """V_r V_r^T for the leading r right singular vectors of W^{1/2} Rbar (App. D.3), from
+    the eigendecomposition of Rbar^T W Rbar; directions whose eigenvalue is at or below
+    clamp times the largest count as absent (as in the metric factors)."""
+    C = Rb.T @ (wt[:, None] * Rb)
+    lam, U = np.linalg.eigh(C)
+    idx = np.argsort(-lam, kind="stable")[:r]
+    keep = [i for i in idx if lam[i] > 0 and lam[i] >= clamp * lam.max()]
+    V = U[:, keep]
+    return V @ V.T
+
+
+def ridge_fit(X: np.ndarray, R: np.ndarray, w: np.ndarray, lam: float, std_eps: float, family: str = "full",
+              out_rank: int = 0, clamp: float = 1e-6):
     """Weighted affine fit of Sec. 4.2 / App. A.3:
     alpha = w / sum w, W = diag(M w / sum w); features standardised with the
     alpha-weighted mean and sqrt(weighted variance + std_eps) (App. D.3); residuals
     centred by their alpha-weighted mean mu_R; B minimises
     |W^{1/2}(Rbar - Xbar B)|_F^2 + lam |B|_F^2, solved through the normal equations
-    by Cholesky.  Returns dict(muX, sd, muR, B)."""
+    by Cholesky.  ``family`` restricts B as in App. D.4 (same weighted error and penalty):
+    "mean" B = 0; "scalar" B = a I (penalty lam d a^2, a = tr H / tr G); "diag"
+    B = diag(b) (b_c = H_cc / G_cc); "full" unrestricted.  ``out_rank`` r in [1, d)
+    projects the centred prediction onto the leading r right singular vectors of
+    W^{1/2} Rbar (App. D.3): B <- B V_r V_r^T; mu_R is not truncated.
+    Returns dict(muX, sd, muR, B)."""
     X = np.asarray(X, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
     w = np.asarray(w, dtype=np.float64)
@@ -521,8 +571,19 @@ def ridge_fit(X: np.ndarray, R: np.ndarray, w: np.ndarray, lam: float, std_eps: 
     Rb = R - muR
     G = Xb.T @ (wt[:, None] * Xb) + lam * np.eye(d)
     H = Xb.T @ (wt[:, None] * Rb)
-    L = np.linalg.cholesky(G)
-    B = np.linalg.solve(L.T, np.linalg.solve(L, H))
+    if family == "full":
+        L = np.linalg.cholesky(G)
+        B = np.linalg.solve(L.T, np.linalg.solve(L, H))
+    elif family == "mean":
+        B = np.zeros((d, d))
+    elif family == "scalar":
+        B = (np.trace(H) / np.trace(G)) * np.eye(d)
+    elif family == "diag":
+        B = np.diag(np.diag(H) / np.diag(G))
+    else:
+        raise ValueError(family)
+    if 0 < out_rank < d:
+        B = B @ output_projector(Rb, wt, out_rank, clamp)
     return dict(muX=muX, sd=sd, muR=muR, B=B)
 
 
@@ -586,7 +647,14 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
     sel, scores, rinfo = route(qbar, kv, vv, kv_lab, kbar, vbar, kv_size, T)
     pairs = int(sum(int(q_size[a]) * (int(kv_size[sel[a]].sum()) + p.n_text) for a in range(nq)))
     rho_exec = executed_density(pairs, N, p.M, p.n_text)
-    probes, w, m_a = select_probes(q_lab, dist, q_size, p.M)
+    if p.probe_mode == "stratified":
+        probes, w, m_a = select_probes(q_lab, dist, q_size, p.M)
+    elif p.probe_mode == "random":
+        (probes, w), m_a = select_probes_random(Nv, p.M, p.seed, head), None
+    elif p.probe_mode == "uniform":
+        (probes, w), m_a = select_probes_uniform(Nv, p.M), None
+    else:
+        raise ValueError(p.probe_mode)
     out.update(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
                kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, phiQ=phiQ, kmQ=qm, q_label=q_lab, n_q=nq,
                q_size=q_size, qbar=qbar, cbar=cbar, qdist=dist, T=T, sel=sel, scores=scores,
@@ -597,7 +665,7 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
     q_lab_full = np.concatenate([q_lab, np.full(p.n_text, -1)])
     X = sparse_attention_rows(q, k, v, probes, q_lab_full, kv_lab, sel, p.n_text)
     Od = dense_attention_rows(q, k, v, probes)
-    fit = ridge_fit(X, Od - X, w, p.lam, p.std_eps)
+    fit = ridge_fit(X, Od - X, w, p.lam, p.std_eps, p.fit_family, p.out_rank, p.eig_clamp)
     rows = np.arange(N) if rows is None else np.asarray(rows)
     Osp = sparse_attention_rows(q, k, v, rows, q_lab_full, kv_lab, sel, p.n_text)
     Ohat = Osp.copy()

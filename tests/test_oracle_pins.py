@@ -571,3 +571,129 @@ def test_warm_pipeline_on_the_same_inputs_reproduces_the_partition():
     n = first["n_q"]
     np.testing.assert_allclose(np.sqrt((init[:n] ** 2).mean(1)), 1.0, rtol=1e-12)
     assert second["kmQ"]["passes"] <= 2
+
+
+# ---------------------------------------------------------------- probe and estimator variants
+def test_random_probes_are_a_nested_sample_without_replacement():
+    Nv = 500
+    rows, w = O.select_probes_random(Nv, 40, seed=3, head=2)
+    assert rows.size == 40 and np.unique(rows).size == 40 and np.all(np.diff(rows) > 0)
+    assert rows.min() >= 0 and rows.max() < Nv
+    np.testing.assert_allclose(w, Nv / 40)
+    assert abs(w.sum() - Nv) < 1e-9
+    # nested in M (App. D.3): fewer probes are a subset of more
+    small, _ = O.select_probes_random(Nv, 16, seed=3, head=2)
+    assert set(small.tolist()) <= set(rows.tolist())
+    # other heads and seeds draw other samples
+    assert not np.array_equal(O.select_probes_random(Nv, 40, seed=3, head=3)[0], rows)
+    assert not np.array_equal(O.select_probes_random(Nv, 40, seed=4, head=2)[0], rows)
+    # uniform inclusion: over many seeds every row is taken about M / Nv of the time
+    Nv, M, S = 64, 16, 400
+    cnt = np.zeros(Nv)
+    for sd in range(S):
+        cnt[O.select_probes_random(Nv, M, seed=sd, head=0)[0]] += 1
+    expect = S * M / Nv
+    assert np.all(np.abs(cnt - expect) < 6 * math.sqrt(expect))
+
+
+def test_uniform_probes_are_the_centres_of_equal_stretches():
+    rows, w = O.select_probes_uniform(1000, 10)
+    assert rows.tolist() == [50 + 100 * i for i in range(10)]
+    np.testing.assert_allclose(w, 100.0)
+    rows, _ = O.select_probes_uniform(37, 37)
+    assert rows.tolist() == list(range(37))
+    rows, _ = O.select_probes_uniform(1001, 7)
+    assert np.unique(rows).size == 7 and rows.max() < 1001
+
+
+def _family_problem(seed, M=40, d=6):
+    rng = _rng(seed)
+    X = rng.standard_normal((M, d)) * rng.uniform(0.5, 2.0, d) + rng.standard_normal(d)
+    R = X @ rng.standard_normal((d, d)) * 0.3 + rng.standard_normal((M, d)) + 0.5
+    w = rng.uniform(0.5, 3.0, M)
+    return X, R, w
+
+
+def _standardised(X, R, w, eps):
+    alpha = w / w.sum()
+    wt = len(w) * alpha
+    muX = alpha @ X
+    Xb = (X - muX) / np.sqrt(alpha @ ((X - muX) ** 2) + eps)
+    Rb = R - alpha @ R
+    return Xb, Rb, wt
+
+
+def test_correction_families_solve_their_penalised_problems():
+    X, R, w = _family_problem(5)
+    lam, eps = 0.7, 1e-6
+    M, d = X.shape
+    Xb, Rb, wt = _standardised(X, R, w, eps)
+    sw = np.sqrt(wt)[:, None]
+    fits = {f: O.ridge_fit(X, R, w, lam, eps, family=f)["B"] for f in ["full", "diag", "scalar", "mean"]}
+    assert np.all(fits["mean"] == 0)
+    # scalar: one least-squares unknown over all entries, penalty lam * d * a^2
+    A = np.concatenate([(sw * Xb).ravel(), [math.sqrt(lam * d)]])
+    b = np.concatenate([(sw * Rb).ravel(), [0.0]])
+    a = np.linalg.lstsq(A[:, None], b, rcond=None)[0][0]
+    np.testing.assert_allclose(fits["scalar"], a * np.eye(d), rtol=1e-12, atol=1e-14)
+    # diagonal: one ridge per column, penalty lam * b_c^2
+    for c in range(d):
+        A = np.concatenate([sw[:, 0] * Xb[:, c], [math.sqrt(lam)]])
+        b = np.concatenate([sw[:, 0] * Rb[:, c], [0.0]])
+        bc = np.linalg.lstsq(A[:, None], b, rcond=None)[0][0]
+        assert abs(fits["diag"][c, c] - bc) <= 1e-12 * max(1.0, abs(bc))
+    assert np.all(fits["diag"][~np.eye(d, dtype=bool)] == 0)
+    # the feasible sets are nested (0 in aI in diag(b) in all B) under one objective, so the
+    # penalised objective can only fall from mean-only to full ridge
+    J = {f: (wt[:, None] * (Rb - Xb @ B) ** 2).sum() + lam * (B ** 2).sum() for f, B in fits.items()}
+    assert J["full"] <= J["diag"] + 1e-9 and J["diag"] <= J["scalar"] + 1e-9 and J["scalar"] <= J["mean"] + 1e-9
+    assert J["full"] < J["mean"]
+
+
+def test_output_truncation_projects_onto_leading_residual_directions():
+    X, R, w = _family_problem(9, M=50, d=7)
+    lam, eps = 1.0, 1e-6
+    Xb, Rb, wt = _standardised(X, R, w, eps)
+    full = O.ridge_fit(X, R, w, lam, eps)["B"]
+    for r in [1, 3, 6]:
+        Br = O.ridge_fit(X, R, w, lam, eps, out_rank=r)["B"]
+        # the projector from the SVD of W^{1/2} Rbar (another library routine than eigh)
+        _, sv, Vt = np.linalg.svd(np.sqrt(wt)[:, None] * Rb, full_matrices=False)
+        assert np.all(np.diff(sv) < 0)
+        P = Vt[:r].T @ Vt[:r]
+        np.testing.assert_allclose(Br, full @ P, rtol=1e-10, atol=1e-12)
+        # predictions lie in the span of the r directions, and truncating again changes nothing
+        pred = Xb @ Br
+        np.testing.assert_allclose(pred - pred @ P, 0.0, atol=1e-10)
+        np.testing.assert_allclose(Br @ P, Br, atol=1e-12)
+    # rank 0 and rank >= d mean no truncation
+    for r in [0, 7, 9]:
+        np.testing.assert_allclose(O.ridge_fit(X, R, w, lam, eps, out_rank=r)["B"], full, rtol=0, atol=0)
+    # truncation applies to the restricted families too, and mu_R is left whole
+    fd = O.ridge_fit(X, R, w, lam, eps, family="diag", out_rank=2)
+    _, _, Vt = np.linalg.svd(np.sqrt(wt)[:, None] * Rb, full_matrices=False)
+    np.testing.assert_allclose(fd["B"], O.ridge_fit(X, R, w, lam, eps, family="diag")["B"] @ Vt[:2].T @ Vt[:2],
+                               rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(fd["muR"], (w / w.sum()) @ R, rtol=1e-13)
+
+
+def test_variant_pipeline_runs_and_reduces_to_reference_choices():
+    rng = _rng(31)
+    N, d = 256, 16
+    q, k, v = rng.standard_normal((3, N, d))
+    base = dict(Ck=8, Cq=8, rK=8, rQ=8, Ms=256, M=12, rho=0.5, lam=1.0, seed=2, max_iters=20, tol=0.0)
+    ref = O.sparsepr_head(q, k, v, O.Params(**base), rows=np.arange(0, N, 7))
+    for mode in ["random", "uniform"]:
+        out = O.sparsepr_head(q, k, v, O.Params(**base, probe_mode=mode), rows=np.arange(0, N, 7))
+        assert out["probes"].size == 12 and np.unique(out["probes"]).size == 12
+        # the partition and route do not depend on the probe choice
+        assert np.array_equal(out["q_label"], ref["q_label"]) and all(
+            np.array_equal(a, b) for a, b in zip(out["sel"], ref["sel"]))
+        # probe rows of the output are exact
+        pos = {int(r): i for i, r in enumerate(out["rows"])}
+        for i, r in enumerate(out["probes"]):
+            if int(r) in pos:
+                np.testing.assert_allclose(out["O_hat"][pos[int(r)]], out["probe_dense"][i], rtol=1e-12)
+    mean = O.sparsepr_head(q, k, v, O.Params(**base, fit_family="mean"), rows=np.arange(0, N, 7))
+    un = ~np.isin(mean["rows"], mean["probes"])
+    np.testing.assert_allclose(mean["O_hat"][un], mean["O_sp"][un] + mean["fit"]["muR"], rtol=1e-12)
