@@ -48,6 +48,7 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.fitW = take(BH * Mm * 8);
   L.applyB = take(BH * d * d * 4);
   L.applyC = take(BH * d * 4);
+  L.fitF = take(BH * d * d * 8);
   L.tmax = sparse_tile_capacity(p.Cq, int(Nv), desc.n_text);
   L.tiles = take(BH * size_t(L.tmax) * 8 * 4);
   L.ntiles = take(BH * 4);
@@ -147,8 +148,8 @@ spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k
 }
 
 spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
-                          double rho_exec_target, int32_t M, spr_route* out, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          double rho_exec_target, int32_t M, const spr_probe_options* probes, spr_route* out,
+                          void* ws, size_t ws_bytes, void* stream) {
   spr_status s = check_desc(desc);
   if (s != SPR_OK) return s;
   if ((s = check_params(desc, params)) != SPR_OK) return s;
@@ -161,9 +162,13 @@ spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, c
   if (!out->sel_cnt || !out->sel_kv || !out->probe_idx || !out->probe_w || !out->pairs ||
       !out->rho_exec)
     return SPR_EINVAL;
+  spr_probe_options po = {SPR_PROBES_STRATIFIED, 0};
+  if (probes) po = *probes;
+  if (po.mode != SPR_PROBES_STRATIFIED && po.mode != SPR_PROBES_RANDOM && po.mode != SPR_PROBES_UNIFORM)
+    return SPR_EINVAL;
   Workspace L;
   if ((s = check_ws(desc, params, M, ws, ws_bytes, &L)) != SPR_OK) return s;
-  return run_route(*desc, *params, *part, rho_exec_target, M, Tk, *out, ws, L, static_cast<hipStream_t>(stream));
+  return run_route(*desc, *params, *part, rho_exec_target, M, Tk, po, *out, ws, L, static_cast<hipStream_t>(stream));
 }
 
 spr_status sparsepr_attn_sparse(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
@@ -198,8 +203,9 @@ spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void*
 
 spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
                                 const spr_route* route, const float* o_sp, const float* o_probe, int32_t M,
-                                double lam, double std_eps, void* out, int32_t out_dtype, double* fit_state,
-                                int32_t* head_status, void* ws, size_t ws_bytes, void* stream) {
+                                double lam, double std_eps, const spr_fit_options* opts, void* out,
+                                int32_t out_dtype, double* fit_state, int32_t* head_status, void* ws,
+                                size_t ws_bytes, void* stream) {
   spr_status s = check_desc(desc);
   if (s != SPR_OK) return s;
   if ((s = check_params(desc, params)) != SPR_OK) return s;
@@ -208,10 +214,13 @@ spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* par
   if (!(lam >= 0.0) || !(std_eps > 0.0)) return SPR_EINVAL;
   if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
   if (!part || !route || !o_sp || !o_probe || !out || !head_status) return SPR_EINVAL;
+  spr_fit_options fo = {SPR_FIT_FULL, 0};
+  if (opts) fo = *opts;
+  if (fo.family < SPR_FIT_FULL || fo.family > SPR_FIT_DIAG || fo.out_rank < 0) return SPR_EINVAL;
   Workspace L;
   if ((s = check_ws(desc, params, M, ws, ws_bytes, &L)) != SPR_OK) return s;
-  return run_fit_correct(*desc, *params, *part, *route, o_sp, o_probe, M, lam, std_eps, out, out_dtype, fit_state,
-                         head_status, ws, L, static_cast<hipStream_t>(stream));
+  return run_fit_correct(*desc, *params, *part, *route, o_sp, o_probe, M, lam, std_eps, fo.family, fo.out_rank, out,
+                         out_dtype, fit_state, head_status, ws, L, static_cast<hipStream_t>(stream));
 }
 
 spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v, void* out,

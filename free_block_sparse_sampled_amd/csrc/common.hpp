@@ -183,6 +183,7 @@ struct Workspace {
   size_t fitW;       // double [BH][M]           unit-mean weights
   size_t applyB;     // bf16   [BH][2][d][d]     E^T = (diag(1/sd) B)^T, high then low part
   size_t applyC;     // float  [BH][d]           mu_R - (mu_X / sd) B
+  size_t fitF;       // double [BH][d][d]        factor of Rb^T W Rb for the output truncation
   size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
   size_t ntiles;     // int    [BH]              tiles used per head
   size_t tile_prefix;  // int  [BH + 1]          exclusive prefix of ntiles

@@ -76,16 +76,19 @@ __global__ __launch_bounds__(256) void fit_prep_kernel(const float* __restrict__
   }
 }
 
-// G = Xb^T W Xb + lam I and H = Xb^T W Rb, 16 x 16 tiles, probes staged in LDS.
+// G = Xb^T W Xb + lam I and H = Xb^T W Rb, 16 x 16 tiles, probes staged in LDS; with Cr
+// WITH_C also Cr = Rb^T W Rb (the residual second moment of the output truncation, App. D.3).
+template <bool WITH_C>
 __global__ __launch_bounds__(256) void normal_eq_kernel(const double* __restrict__ Xb, const double* __restrict__ Rb,
                                                         const double* __restrict__ Wt, int d, int M, double lam,
-                                                        double* __restrict__ G, double* __restrict__ Hm) {
-  __shared__ double Xi[32][17], Xj[32][17], Rj[32][17], Ws[32];
+                                                        double* __restrict__ G, double* __restrict__ Hm,
+                                                        double* __restrict__ Cr) {
+  __shared__ double Xi[32][17], Xj[32][17], Rj[32][17], Ri[WITH_C ? 32 : 1][17], Ws[32];
   const int hd = blockIdx.y;
   const int tiles = d / 16;
   const int i0 = (blockIdx.x / tiles) * 16, j0 = (blockIdx.x % tiles) * 16;
   const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-  double g = 0.0, h = 0.0;
+  double g = 0.0, h = 0.0, cr = 0.0;
   for (int p0 = 0; p0 < M; p0 += 32) {
     for (int e = threadIdx.x; e < 32 * 16; e += 256) {
       const int pp = e >> 4, cc = e & 15, p = p0 + pp;
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(256) void normal_eq_kernel(const double* __restrict
       Xi[pp][cc] = ok ? Xb[(size_t(hd) * M + p) * d + i0 + cc] : 0.0;
       Xj[pp][cc] = ok ? Xb[(size_t(hd) * M + p) * d + j0 + cc] : 0.0;
       Rj[pp][cc] = ok ? Rb[(size_t(hd) * M + p) * d + j0 + cc] : 0.0;
+      if constexpr (WITH_C) Ri[pp][cc] = ok ? Rb[(size_t(hd) * M + p) * d + i0 + cc] : 0.0;
     }
     if (threadIdx.x < 32) Ws[threadIdx.x] = p0 + threadIdx.x < M ? Wt[size_t(hd) * M + p0 + threadIdx.x] : 0.0;
     __syncthreads();
@@ -101,16 +105,20 @@ __global__ __launch_bounds__(256) void normal_eq_kernel(const double* __restrict
       g = fma(wx, Xj[pp][tj], g);
       h = fma(wx, Rj[pp][tj], h);
     }
+    if constexpr (WITH_C)
+      for (int pp = 0; pp < 32; ++pp) cr = fma(Ws[pp] * Ri[pp][ti], Rj[pp][tj], cr);
     __syncthreads();
   }
   if (i0 + ti == j0 + tj) g += lam;
   G[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = g;
   Hm[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = h;
+  if constexpr (WITH_C) Cr[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = cr;
 }
 
-// C (m x n, row stride ldc) = op(A) B with 4 x 4 register tiles per thread; op(A)(i, k) is
-// A[i * lda + k], or A[k * lda + i] when AT; B(k, j) = B[k * ldb + j]; m, n multiples of 4.
-template <bool AT>
+// C (m x n, row stride ldc) = op(A) op(B) with 4 x 4 register tiles per thread; op(A)(i, k) is
+// A[i * lda + k], or A[k * lda + i] when AT; op(B)(k, j) is B[k * ldb + j], or B[j * ldb + k]
+// when BT; m, n multiples of 4.
+template <bool AT, bool BT = false>
 __device__ inline void fit_gemm(const double* A, int lda, const double* B, int ldb, double* C, int ldc, int m, int n,
                                 int K) {
   const int tr = m / 4, tc = n / 4;
@@ -123,7 +131,7 @@ __device__ inline void fit_gemm(const double* A, int lda, const double* B, int l
 #pragma unroll
       for (int x = 0; x < 4; ++x) a[x] = AT ? A[size_t(k) * lda + i0 + x] : A[size_t(i0 + x) * lda + k];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) b[y] = B[size_t(k) * ldb + j0 + y];
+      for (int y = 0; y < 4; ++y) b[y] = BT ? B[size_t(j0 + y) * ldb + k] : B[size_t(k) * ldb + j0 + y];
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -142,6 +150,73 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// The affine map of the apply step from B (in the H buffer): E = diag(1 / sd) B, stored
+// transposed (E^T[n][k]) as bf16 high and low parts so that hi + lo carries E to about 2^-16,
+// and c = mu_R - (mu_X / sd) B in fp32; the fit state and the head status.  8 D threads:
+// column b = t / 8 of B, rows s + 8 i.
+template <int D>
+__device__ inline void fit_epilogue(const double* __restrict__ Hall, const double* __restrict__ S,
+                                    uint16_t* __restrict__ applyE, float* __restrict__ applyC,
+                                    double* __restrict__ fit_state, const int* __restrict__ gstat,
+                                    int* __restrict__ head_status, double* isd, double* wmx) {
+  constexpr int NI = D / 8;
+  const int hd = blockIdx.x, tid = threadIdx.x, nth = 8 * D;
+  const int b = tid >> 3, s = tid & 7;
+  const double* Hm = Hall + size_t(hd) * D * D;
+  const double* mx = S + (size_t(hd) * 4 + 0) * D;
+  const double* sd = S + (size_t(hd) * 4 + 1) * D;
+  const double* mr = S + (size_t(hd) * 4 + 2) * D;
+  for (int c = tid; c < D; c += nth) {
+    isd[c] = 1.0 / sd[c];
+    wmx[c] = mx[c] / sd[c];
+  }
+  __syncthreads();
+  uint16_t* Eh = applyE + size_t(hd) * 2 * D * D;
+  uint16_t* El = Eh + size_t(D) * D;
+  for (int e = tid; e < D * D; e += nth) {
+    const int k = e / D, n = e % D;
+    const float x = float(Hm[e] * isd[k]);
+    const uint16_t h = bf16_rne(x);
+    Eh[size_t(n) * D + k] = h;
+    El[size_t(n) * D + k] = bf16_rne(x - __uint_as_float(uint32_t(h) << 16));
+  }
+  {
+    // c_j = mu_R_j - sum_i (mu_X_i / sd_i) B_ij: column j = b, rows i = s + 8 t, lanes combined
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) part = fma(wmx[s + 8 * i], Hm[size_t(s + 8 * i) * D + b], part);
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    if (s == 0) applyC[size_t(hd) * D + b] = float(mr[b] - part);
+  }
+  if (fit_state) {
+    double* fs = fit_state + size_t(hd) * (3 * D + D * D);
+    for (int c = tid; c < D; c += nth) {
+      fs[c] = mx[c];
+      fs[D + c] = sd[c];
+      fs[2 * D + c] = mr[c];
+    }
+    for (int e = tid; e < D * D; e += nth) fs[3 * D + e] = Hm[e];
+  }
+  if (tid == 0) head_status[hd] = gstat[hd * 8 + 0];
+}
+
+template <int D>
+__global__ __launch_bounds__(8 * D) void fit_epilogue_kernel(const double* __restrict__ Hall,
+                                                             const double* __restrict__ S,
+                                                             uint16_t* __restrict__ applyE,
+                                                             float* __restrict__ applyC,
+                                                             double* __restrict__ fit_state,
+                                                             const int* __restrict__ gstat,
+                                                             int* __restrict__ head_status) {
+  __shared__ double isd[D], wmx[D];
+  fit_epilogue<D>(Hall, S, applyE, applyC, fit_state, gstat, head_status, isd, wmx);
+}
+
+template <int D>
+__device__ inline void solve_full(double* Gm, double* Hm, double* Rm, double (*rowbuf)[D], int* gstat);
+
 // Per head, one workgroup of 8 D threads: thread t owns column b = t / 8 of the d x d matrix,
 // rows a = (t % 8) + 8 i (i < D / 8) in registers, so the 8 owners of a column sit in adjacent
 // lanes.
@@ -154,24 +229,63 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 //  - B = R^{-1} (R^{-T} H) by two register-tiled products (R^{-1} in LDS; R^{-T} H goes to the
 //    G buffer, B to the H buffer).
 // A pivot <= 0 (possible only with lam = 0) gives B = 0: the mean-only correction, flagged in
-// head_status.  Finally the affine map of the apply step: E = diag(1 / sd) B, stored transposed
-// (E^T[n][k]) as bf16 high and low parts so that hi + lo carries E to about 2^-16, and
-// c = mu_R - (mu_X / sd) B in fp32.
+// head_status.  The restricted families of App. D.4 minimise the same penalised error over
+// smaller sets and need no factorisation: B = 0 (mean-only), B = a I with a = tr H / tr G
+// (scalar, penalty lam d a^2), B = diag(H_cc / G_cc) (diagonal).  B goes to the H buffer.
 template <int D>
 __global__ __launch_bounds__(8 * D) void cholesky_solve_kernel(double* __restrict__ Gall, double* __restrict__ Hall,
+                                                               int family, int* __restrict__ gstat, bool epilogue,
                                                                const double* __restrict__ S,
                                                                uint16_t* __restrict__ applyE,
                                                                float* __restrict__ applyC,
                                                                double* __restrict__ fit_state,
-                                                               const int* __restrict__ gstat,
                                                                int* __restrict__ head_status) {
-  constexpr int NI = D / 8;
-  extern __shared__ double Rm[];  // D x D row-major (R^{-1}), then scratch
+  extern __shared__ double Rm[];  // D x D row-major (R^{-1})
   __shared__ double rowbuf[2][D];
   const int hd = blockIdx.x, tid = threadIdx.x, nth = 8 * D;
-  const int b = tid >> 3, s = tid & 7;
   double* Gm = Gall + size_t(hd) * D * D;
   double* Hm = Hall + size_t(hd) * D * D;
+  if (family != SPR_FIT_FULL) {
+    double* gd = rowbuf[0];
+    double* hdg = rowbuf[1];
+    for (int c = tid; c < D; c += nth) {
+      gd[c] = Gm[size_t(c) * D + c];
+      hdg[c] = Hm[size_t(c) * D + c];
+    }
+    __syncthreads();
+    double a = 0.0;
+    if (family == SPR_FIT_SCALAR) {
+      double tg = 0.0, th = 0.0;
+      for (int c = 0; c < D; ++c) {
+        tg += gd[c];
+        th += hdg[c];
+      }
+      a = tg > 0.0 ? th / tg : 0.0;
+    }
+    for (int e = tid; e < D * D; e += nth) {
+      const int i = e / D, j = e % D;
+      double v = 0.0;
+      if (i == j) {
+        if (family == SPR_FIT_SCALAR) v = a;
+        else if (family == SPR_FIT_DIAG) v = gd[i] > 0.0 ? hdg[i] / gd[i] : 0.0;
+      }
+      Hm[e] = v;
+    }
+  } else {
+    solve_full<D>(Gm, Hm, Rm, rowbuf, gstat);
+  }
+  if (epilogue) {
+    __syncthreads();
+    fit_epilogue<D>(Hall, S, applyE, applyC, fit_state, gstat, head_status, rowbuf[0], rowbuf[1]);
+  }
+}
+
+// Full ridge: Cholesky, triangular inverse and the two products (see above).
+template <int D>
+__device__ inline void solve_full(double* Gm, double* Hm, double* Rm, double (*rowbuf)[D], int* gstat) {
+  constexpr int NI = D / 8;
+  const int hd = blockIdx.x, tid = threadIdx.x, nth = 8 * D;
+  const int b = tid >> 3, s = tid & 7;
   double A[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) A[i] = Gm[size_t(s + 8 * i) * D + b];
@@ -240,47 +354,39 @@ __global__ __launch_bounds__(8 * D) void cholesky_solve_kernel(double* __restric
     fit_gemm<false>(Rm, D, Gm, D, Hm, D, D, D, D);  // B = R^{-1} Y
   } else {
     for (int e = tid; e < D * D; e += nth) Hm[e] = 0.0;
+    if (tid == 0) gstat[hd * 8 + 0] |= SPR_HS_CHOLESKY_FALLBACK;
+  }
+}
+
+// Output truncation (App. D.3): B <- B V_r V_r^T with V_r the leading eigenvectors of
+// Rb^T W Rb, given as the columns f_k of its factor F = U_r Lambda_r^{1/2} ([D][r], zero columns
+// for clamped eigenvalues): V_r V_r^T = sum_k f_k f_k^T / |f_k|^2.  F is staged in LDS with the
+// rank padded to a multiple of 4 by zero columns; T = B F goes to the G buffer.
+template <int D>
+__global__ __launch_bounds__(256) void truncate_kernel(double* __restrict__ Hall, double* __restrict__ Gall,
+                                                       const double* __restrict__ Fall, int r) {
+  extern __shared__ double Fs[];  // [D][r4], then norms [r4]
+  const int hd = blockIdx.x, tid = threadIdx.x;
+  const int r4 = (r + 3) & ~3;
+  double* nrm = Fs + D * r4;
+  const double* F = Fall + size_t(hd) * D * r;
+  double* Hm = Hall + size_t(hd) * D * D;
+  double* Tm = Gall + size_t(hd) * D * D;
+  for (int e = tid; e < D * r4; e += 256) {
+    const int i = e / r4, k = e % r4;
+    Fs[e] = k < r ? F[size_t(i) * r + k] : 0.0;
   }
   __syncthreads();
-  const double* mx = S + (size_t(hd) * 4 + 0) * D;
-  const double* sd = S + (size_t(hd) * 4 + 1) * D;
-  const double* mr = S + (size_t(hd) * 4 + 2) * D;
-  double* isd = Rm;      // 1 / sd
-  double* wmx = Rm + D;  // mu_X / sd
-  for (int c = tid; c < D; c += nth) {
-    isd[c] = 1.0 / sd[c];
-    wmx[c] = mx[c] / sd[c];
+  for (int k = tid; k < r4; k += 256) {
+    double x = 0.0;
+    for (int i = 0; i < D; ++i) x = fma(Fs[i * r4 + k], Fs[i * r4 + k], x);
+    nrm[k] = x > 0.0 ? 1.0 / x : 0.0;
   }
+  fit_gemm<false>(Hm, D, Fs, r4, Tm, r4, D, r4, D);  // T = B F
   __syncthreads();
-  uint16_t* Eh = applyE + size_t(hd) * 2 * D * D;
-  uint16_t* El = Eh + size_t(D) * D;
-  for (int e = tid; e < D * D; e += nth) {
-    const int k = e / D, n = e % D;
-    const float x = float(Hm[e] * isd[k]);
-    const uint16_t h = bf16_rne(x);
-    Eh[size_t(n) * D + k] = h;
-    El[size_t(n) * D + k] = bf16_rne(x - __uint_as_float(uint32_t(h) << 16));
-  }
-  {
-    // c_j = mu_R_j - sum_i (mu_X_i / sd_i) B_ij: column j = b, rows i = s + 8 t, lanes combined
-    double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) part = fma(wmx[s + 8 * i], Hm[size_t(s + 8 * i) * D + b], part);
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
-    if (s == 0) applyC[size_t(hd) * D + b] = float(mr[b] - part);
-  }
-  if (fit_state) {
-    double* fs = fit_state + size_t(hd) * (3 * D + D * D);
-    for (int c = tid; c < D; c += nth) {
-      fs[c] = mx[c];
-      fs[D + c] = sd[c];
-      fs[2 * D + c] = mr[c];
-    }
-    for (int e = tid; e < D * D; e += nth) fs[3 * D + e] = Hm[e];
-  }
-  if (tid == 0) head_status[hd] = gstat[hd * 8 + 0] | (failed ? SPR_HS_CHOLESKY_FALLBACK : 0);
+  for (int e = tid; e < D * r4; e += 256) Fs[e] *= nrm[e % r4];
+  __syncthreads();
+  fit_gemm<false, true>(Tm, r4, Fs, r4, Hm, D, D, D, r4);  // B = T (F diag(1/|f|^2))^T
 }
 
 typedef __bf16 fit_bf16x8_t __attribute__((ext_vector_type(8)));
@@ -406,9 +512,8 @@ static void launch_apply(const spr_desc& desc, const float* o_sp, const int* q_p
 
 spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
                            const spr_route& route, const float* o_sp, const float* o_probe, int M, double lam,
-                           double std_eps, void* out, int out_dtype, double* fit_state, int* head_status, void* ws,
-                           const Workspace& L, hipStream_t st) {
-  (void)p;
+                           double std_eps, int family, int out_rank, void* out, int out_dtype, double* fit_state,
+                           int* head_status, void* ws, const Workspace& L, hipStream_t st) {
   const int BH = desc.B * desc.H, d = desc.d, N = desc.N, Nv = N - desc.n_text;
   double* Xb = ws_ptr<double>(ws, L.fitX);
   double* Rb = ws_ptr<double>(ws, L.fitR);
@@ -418,19 +523,45 @@ spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const
   double* Wt = ws_ptr<double>(ws, L.fitW);
   uint16_t* AB = ws_ptr<uint16_t>(ws, L.applyB);
   float* AC = ws_ptr<float>(ws, L.applyC);
+  int* gstat = ws_ptr<int>(ws, L.gstat);
+  const bool trunc = out_rank > 0 && out_rank < d;
+  double* Cr = trunc ? ws_ptr<double>(ws, L.metric) : nullptr;  // the metric buffer is free after partitioning
+  double* Fr = ws_ptr<double>(ws, L.fitF);
   hipLaunchKernelGGL(fit_prep_kernel, dim3(d / 32, BH), dim3(256), 0, st, o_sp, o_probe, route.probe_idx, route.probe_w,
                      part.q_pos, N, Nv, d, M, std_eps, Xb, Rb, S, Wt);
-  hipLaunchKernelGGL(normal_eq_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M, lam, G, Hm);
+  if (trunc)
+    hipLaunchKernelGGL(normal_eq_kernel<true>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M, lam,
+                       G, Hm, Cr);
+  else
+    hipLaunchKernelGGL(normal_eq_kernel<false>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M,
+                       lam, G, Hm, Cr);
   SPR_CHECK_LAUNCH();
+  if (trunc) {
+    const spr_status s = launch_eigen_factor(Cr, BH, d, out_rank, p.eig_clamp, Fr, gstat, st);
+    if (s != SPR_OK) return s;
+  }
   const size_t sm = size_t(d) * d * sizeof(double);
+  const size_t tsm = (size_t(d) + 1) * ((out_rank + 3) & ~3) * sizeof(double);
   if (d == 128) {
     allow_lds(cholesky_solve_kernel<128>, sm);
-    hipLaunchKernelGGL(cholesky_solve_kernel<128>, dim3(BH), dim3(1024), sm, st, G, Hm, S, AB, AC, fit_state,
-                       ws_ptr<int>(ws, L.gstat), head_status);
+    hipLaunchKernelGGL(cholesky_solve_kernel<128>, dim3(BH), dim3(1024), sm, st, G, Hm, family, gstat, !trunc, S, AB,
+                       AC, fit_state, head_status);
+    if (trunc) {
+      allow_lds(truncate_kernel<128>, tsm);
+      hipLaunchKernelGGL(truncate_kernel<128>, dim3(BH), dim3(256), tsm, st, Hm, G, Fr, out_rank);
+      hipLaunchKernelGGL(fit_epilogue_kernel<128>, dim3(BH), dim3(1024), 0, st, Hm, S, AB, AC, fit_state, gstat,
+                         head_status);
+    }
   } else {
     allow_lds(cholesky_solve_kernel<64>, sm);
-    hipLaunchKernelGGL(cholesky_solve_kernel<64>, dim3(BH), dim3(512), sm, st, G, Hm, S, AB, AC, fit_state,
-                       ws_ptr<int>(ws, L.gstat), head_status);
+    hipLaunchKernelGGL(cholesky_solve_kernel<64>, dim3(BH), dim3(512), sm, st, G, Hm, family, gstat, !trunc, S, AB,
+                       AC, fit_state, head_status);
+    if (trunc) {
+      allow_lds(truncate_kernel<64>, tsm);
+      hipLaunchKernelGGL(truncate_kernel<64>, dim3(BH), dim3(256), tsm, st, Hm, G, Fr, out_rank);
+      hipLaunchKernelGGL(fit_epilogue_kernel<64>, dim3(BH), dim3(512), 0, st, Hm, S, AB, AC, fit_state, gstat,
+                         head_status);
+    }
   }
   SPR_CHECK_LAUNCH();
   if (d == 128) {

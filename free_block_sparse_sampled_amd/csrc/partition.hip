@@ -895,6 +895,15 @@ static T* wsp(void* ws, size_t off) {
   return ws_ptr<T>(ws, off);
 }
 
+spr_status launch_eigen_factor(const double* Mall, int BH, int d, int r, double clamp, double* Fall, int* gstat,
+                               hipStream_t st) {
+  const size_t sm = jacobi_smem(d);
+  allow_lds(eigen_factor_kernel, sm);
+  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), sm, st, Mall, d, r, clamp, Fall, gstat, -1);
+  SPR_CHECK_LAUNCH();
+  return SPR_OK;
+}
+
 template <int DT>
 static spr_status partition_impl(const spr_desc& desc, const void* q, const void* k, const void* v,
                                  const spr_part_params& p, const spr_warm* warm, spr_partition& out, void* ws,

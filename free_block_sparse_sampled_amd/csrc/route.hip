@@ -430,9 +430,85 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int* __restrict
   }
 }
 
+// Random and uniform probes (Table 4), one block of 1024 threads per head; weights Nv / M.
+// Random: the M rows with the smallest draws splitmix64(seed ^ "probe", hd Nv + i), found by an
+// 8-pass radix selection of the M-th smallest draw (8 bits per pass, most significant first);
+// rows below it, and the first rows equal to it, are listed in ascending row.  Uniform: rows
+// floor((2 i + 1) Nv / (2 M)).
+constexpr uint64_t kProbeStream = 0x70726F6265ull;
+__global__ __launch_bounds__(1024) void probe_plain_kernel(int mode, uint64_t seed, int Nv, int M,
+                                                           int* __restrict__ probe_idx,
+                                                           double* __restrict__ probe_w) {
+  __shared__ int hist[256];
+  __shared__ int buf[1024];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_need;
+  const int hd = blockIdx.x, tid = threadIdx.x;
+  int* out = probe_idx + size_t(hd) * M;
+  double* ow = probe_w + size_t(hd) * M;
+  const double wgt = double(Nv) / double(M);
+  if (mode == SPR_PROBES_UNIFORM) {
+    for (int i = tid; i < M; i += 1024) {
+      out[i] = int((2 * int64_t(i) + 1) * Nv / (2 * int64_t(M)));
+      ow[i] = wgt;
+    }
+    return;
+  }
+  const uint64_t sd = seed ^ kProbeStream, c0 = uint64_t(hd) * uint64_t(Nv);
+  uint64_t prefix = 0;
+  int need = M;  // rank (1-based) of the wanted draw among those matching the prefix
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    const uint64_t hi = pass == 0 ? 0ull : ~0ull << (shift + 8);
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < Nv; i += 1024) {
+      const uint64_t k = splitmix64(sd, c0 + i);
+      if ((k & hi) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, bin = 255;
+      for (int b = 0; b < 256; ++b) {
+        if (cum + hist[b] >= need) {
+          bin = b;
+          break;
+        }
+        cum += hist[b];
+      }
+      s_prefix = prefix | (uint64_t(bin) << shift);
+      s_need = need - cum;
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    __syncthreads();
+  }
+  // prefix is the M-th smallest draw; take every smaller draw and the first `need` equal ones
+  int base = 0, eq_seen = 0;
+  for (int c = 0; c < Nv; c += 1024) {
+    const int i = c + tid;
+    uint64_t k = ~0ull;
+    if (i < Nv) k = splitmix64(sd, c0 + i);
+    const bool lt = i < Nv && k < prefix, eq = i < Nv && k == prefix;
+    int n_eq;
+    const int r_eq = block_exscan_i(eq ? 1 : 0, buf, &n_eq);
+    const bool take = lt || (eq && eq_seen + r_eq < need);
+    int n_take;
+    const int pos = block_exscan_i(take ? 1 : 0, buf, &n_take);
+    if (take) {
+      out[base + pos] = i;
+      ow[base + pos] = wgt;
+    }
+    base += n_take;
+    eq_seen += n_eq;
+  }
+}
+
 template <int DT>
 static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, const spr_partition& part, int M,
-                             int64_t Tk, spr_route& out, void* ws, const Workspace& L, hipStream_t st) {
+                             int64_t Tk, const spr_probe_options& probes, spr_route& out, void* ws,
+                             const Workspace& L, hipStream_t st) {
   const int BH = desc.B * desc.H, d = desc.d, N = desc.N, Nv = N - desc.n_text;
   double* vstat = ws_ptr<double>(ws, L.vstat);
   double* shift = ws_ptr<double>(ws, L.shift);
@@ -465,17 +541,22 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_finalize_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, N, Nv,
                      desc.n_text, M, out.pairs, out.rho_exec, pstat);
-  hipLaunchKernelGGL(probe_select_kernel, dim3(p.Cq, BH), dim3(256), 0, st, part.q_off, part.q_perm, part.n_q,
-                     part.qdist, pstat, p.Cq, Nv, M, out.probe_idx, out.probe_w);
+  if (probes.mode == SPR_PROBES_STRATIFIED)
+    hipLaunchKernelGGL(probe_select_kernel, dim3(p.Cq, BH), dim3(256), 0, st, part.q_off, part.q_perm, part.n_q,
+                       part.qdist, pstat, p.Cq, Nv, M, out.probe_idx, out.probe_w);
+  else
+    hipLaunchKernelGGL(probe_plain_kernel, dim3(BH), dim3(1024), 0, st, probes.mode, probes.seed, Nv, M,
+                       out.probe_idx, out.probe_w);
   SPR_CHECK_LAUNCH();
   return SPR_OK;
 }
 
 spr_status run_route(const spr_desc& desc, const spr_part_params& p, const spr_partition& part, double rho, int M,
-                     int64_t Tk, spr_route& out, void* ws, const Workspace& L, hipStream_t st) {
+                     int64_t Tk, const spr_probe_options& probes, spr_route& out, void* ws, const Workspace& L,
+                     hipStream_t st) {
   (void)rho;
-  if (desc.dtype == SPR_BF16) return route_impl<SPR_BF16>(desc, p, part, M, Tk, out, ws, L, st);
-  return route_impl<SPR_F32>(desc, p, part, M, Tk, out, ws, L, st);
+  if (desc.dtype == SPR_BF16) return route_impl<SPR_BF16>(desc, p, part, M, Tk, probes, out, ws, L, st);
+  return route_impl<SPR_F32>(desc, p, part, M, Tk, probes, out, ws, L, st);
 }
 
 }  // namespace spr

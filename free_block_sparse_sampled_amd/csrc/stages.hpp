@@ -44,15 +44,20 @@ spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, 
 spr_status run_partition(const spr_desc& desc, const void* q, const void* k, const void* v, const spr_part_params& p,
                          const spr_warm* warm, spr_partition& out, void* ws, const Workspace& L, hipStream_t st);
 spr_status run_route(const spr_desc& desc, const spr_part_params& p, const spr_partition& part, double rho, int M,
-                     int64_t Tk, spr_route& out, void* ws, const Workspace& L, hipStream_t st);
+                     int64_t Tk, const spr_probe_options& probes, spr_route& out, void* ws, const Workspace& L,
+                     hipStream_t st);
 spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
                            const spr_route& route, float* o_sp, void* ws, const Workspace& L, hipStream_t st);
 spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, const void* v, const int* probe_idx,
                            int M, float* o_probe, void* ws, const Workspace& L, hipStream_t st);
 spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const spr_partition& part,
                            const spr_route& route, const float* o_sp, const float* o_probe, int M, double lam,
-                           double std_eps, void* out, int out_dtype, double* fit_state, int* head_status, void* ws,
-                           const Workspace& L, hipStream_t st);
+                           double std_eps, int family, int out_rank, void* out, int out_dtype, double* fit_state,
+                           int* head_status, void* ws, const Workspace& L, hipStream_t st);
+// Factor F = U_r Lambda_r^{1/2} [BH][d][r] of the symmetric d x d matrices Mall (eigendecomposition
+// of the partitioning stage; eigenvalues at or below clamp times the largest give zero columns).
+spr_status launch_eigen_factor(const double* Mall, int BH, int d, int r, double clamp, double* Fall, int* gstat,
+                               hipStream_t st);
 spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
                           int out_dtype, hipStream_t st);
 

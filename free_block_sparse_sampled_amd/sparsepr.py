@@ -57,6 +57,19 @@ class spr_warm(ctypes.Structure):
     _fields_ = [(n, P) for n in _WARM_FIELDS]
 
 
+class spr_probe_options(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class spr_fit_options(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("out_rank", ctypes.c_int32)]
+
+
+# spr_probe_mode and spr_fit_family of include/sparsepr.h
+PROBE_MODES = {"stratified": 0, "random": 1, "uniform": 2}
+FIT_FAMILIES = {"full": 0, "mean": 1, "scalar": 2, "diag": 3}
+
+
 class SparsePRError(RuntimeError):
     pass
 
@@ -80,7 +93,8 @@ def library():
         lib.sparsepr_partition.restype = st
         lib.sparsepr_route.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
                                        ctypes.POINTER(spr_partition), ctypes.c_double, ctypes.c_int32,
-                                       ctypes.POINTER(spr_route), P, ctypes.c_size_t, P]
+                                       ctypes.POINTER(spr_probe_options), ctypes.POINTER(spr_route), P,
+                                       ctypes.c_size_t, P]
         lib.sparsepr_route.restype = st
         lib.sparsepr_attn_sparse.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
                                              ctypes.POINTER(spr_partition), ctypes.POINTER(spr_route), P, P,
@@ -91,8 +105,9 @@ def library():
         lib.sparsepr_probe_exact.restype = st
         lib.sparsepr_fit_correct.argtypes = [ctypes.POINTER(spr_desc), ctypes.POINTER(spr_part_params),
                                              ctypes.POINTER(spr_partition), ctypes.POINTER(spr_route), P, P,
-                                             ctypes.c_int32, ctypes.c_double, ctypes.c_double, P, ctypes.c_int32, P, P,
-                                             P, ctypes.c_size_t, P]
+                                             ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                             ctypes.POINTER(spr_fit_options), P, ctypes.c_int32, P, P, P,
+                                             ctypes.c_size_t, P]
         lib.sparsepr_fit_correct.restype = st
         lib.sparsepr_attn_dense.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P]
         lib.sparsepr_attn_dense.restype = st
@@ -145,6 +160,15 @@ class OperatorConfig:
     rho: float = 0.22
     lam: float = 1.0
     std_eps: float = 1e-6
+    probe_mode: str = "stratified"  # Table 4: "stratified" | "random" | "uniform"
+    fit_family: str = "full"        # App. D.4: "full" | "mean" | "scalar" | "diag"
+    out_rank: int = 0               # App. D.3 output truncation rank; 0: none
+
+    def probe_options(self) -> spr_probe_options:
+        return spr_probe_options(PROBE_MODES[self.probe_mode], self.seed)
+
+    def fit_options(self) -> spr_fit_options:
+        return spr_fit_options(FIT_FAMILIES[self.fit_family], self.out_rank)
 
     def part_params(self) -> spr_part_params:
         return spr_part_params(self.Ck, self.Cq, self.rK, self.rQ, self.Ms, self.max_iters, self.tol, self.rms_eps,
@@ -240,8 +264,10 @@ def sparsepr_partition(desc, q, k, v, cfg: OperatorConfig, part: Partition, ws: 
 
 def sparsepr_route(desc, cfg: OperatorConfig, part: Partition, route: Route, ws: torch.Tensor, stream=None):
     pp = cfg.part_params()
+    po = cfg.probe_options()
     _check(library().sparsepr_route(ctypes.byref(desc), ctypes.byref(pp), ctypes.byref(part.struct), cfg.rho, cfg.M,
-                                    ctypes.byref(route.struct), _ptr(ws), ws.numel(), _stream(stream)),
+                                    ctypes.byref(po), ctypes.byref(route.struct), _ptr(ws), ws.numel(),
+                                    _stream(stream)),
            "sparsepr_route")
 
 
@@ -264,10 +290,12 @@ def sparsepr_fit_correct(desc, cfg: OperatorConfig, part: Partition, route: Rout
                          head_status, ws, fit_state=None, stream=None):
     pp = cfg.part_params()
     out_dt = SPR_BF16 if out.dtype == torch.bfloat16 else SPR_F32
+    fo = cfg.fit_options()
     _check(library().sparsepr_fit_correct(ctypes.byref(desc), ctypes.byref(pp), ctypes.byref(part.struct),
                                           ctypes.byref(route.struct), _ptr(o_sp), _ptr(o_probe), cfg.M, cfg.lam,
-                                          cfg.std_eps, _ptr(out), out_dt, _ptr(fit_state), _ptr(head_status), _ptr(ws),
-                                          ws.numel(), _stream(stream)), "sparsepr_fit_correct")
+                                          cfg.std_eps, ctypes.byref(fo), _ptr(out), out_dt, _ptr(fit_state),
+                                          _ptr(head_status), _ptr(ws), ws.numel(), _stream(stream)),
+           "sparsepr_fit_correct")
 
 
 def sparsepr_attn_dense(desc, q, k, v, out, stream=None):

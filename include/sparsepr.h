@@ -144,12 +144,45 @@ typedef struct {
                                     is the text query group (when n_text > 0) */
   int32_t* sel_kv;    /* [BH][Cq+1][Ck+1] selected video K/V groups in descending score order,
                                     followed by the text group n_kv when n_text > 0 */
-  int32_t* probe_idx; /* [BH][M] original row of each probe, group-major, nearest first */
-  double* probe_w;    /* [BH][M] coverage weight w_p = |G_a| / m_a */
+  int32_t* probe_idx; /* [BH][M] original row of each probe: stratified probes group-major, nearest
+                                 first; the other modes in ascending row */
+  double* probe_w;    /* [BH][M] coverage weight w_p (|G_a| / m_a, or Nv / M) */
   int64_t* pairs;     /* [BH] routed query-key pairs, text keys of video rows included */
   double* rho_exec;   /* [BH] executed-pair density incl. probes and text rows */
   double* scores;     /* optional [BH][Cq][Ck] routing scores times a positive per-row factor */
 } spr_route;
+
+/* Probe choice of sparsepr_route (Table 4; App. D.3).  Weights w_p: |G_a| / m_a for stratified
+   probes, Nv / M for the others. */
+typedef enum {
+  SPR_PROBES_STRATIFIED = 0, /* query-group stratified (App. A.2), the operator's choice */
+  SPR_PROBES_RANDOM = 1,     /* the M video rows i with the smallest SplitMix64 draws
+                                splitmix64(seed ^ 0x70726F6265, hd * Nv + i) (ties to the lower row):
+                                a uniform sample without replacement, nested in M */
+  SPR_PROBES_UNIFORM = 2     /* evenly spaced rows floor((2 i + 1) Nv / (2 M)), i < M (row-major
+                                (t, h, w) tokens: uniform over the spatiotemporal grid) */
+} spr_probe_mode;
+
+typedef struct {
+  int32_t mode;  /* spr_probe_mode */
+  uint64_t seed; /* SPR_PROBES_RANDOM only */
+} spr_probe_options;
+
+/* Estimator of sparsepr_fit_correct (App. D.3, D.4).  Every family minimises the same weighted
+   squared error with penalty lam |B|_F^2. */
+typedef enum {
+  SPR_FIT_FULL = 0,   /* unrestricted B (the operator's choice) */
+  SPR_FIT_MEAN = 1,   /* B = 0: the weighted mean residual only */
+  SPR_FIT_SCALAR = 2, /* B = a I, a = tr H / tr G (penalty lam d a^2) */
+  SPR_FIT_DIAG = 3    /* B = diag(b), b_c = H_cc / G_cc */
+} spr_fit_family;
+
+typedef struct {
+  int32_t family;   /* spr_fit_family */
+  int32_t out_rank; /* r in [1, d): the centred prediction is projected onto the r leading right
+                       singular vectors of W^{1/2} Rb (B <- B V_r V_r^T; eigenvalues of Rb^T W Rb
+                       at or below eig_clamp times the largest count as absent); 0 or >= d: none */
+} spr_fit_options;
 
 /* Bytes of workspace the five calls need for this shape (host function, no device work).
    Returns 0 when the arguments are invalid. */
@@ -177,11 +210,12 @@ spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k
    value-error scores s_ab for every (query group, K/V group); per query group the
    shortest descending-score prefix whose key count reaches the common budget
    ceil((rho*N^2 - n_text*N - M*N - Nv*n_text) / Nv); M probe rows stratified by query
-   group.  `rho_exec_target` is the total executed-pair target including probes.
-   EINVAL: 1 <= M < Nv violated, or the budget is below one key. */
+   group (or the choice in `probes`, host, nullable: NULL is SPR_PROBES_STRATIFIED).
+   `rho_exec_target` is the total executed-pair target including probes.
+   EINVAL: 1 <= M < Nv violated, the budget is below one key, an unknown probe mode. */
 spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
-                          double rho_exec_target, int32_t M, spr_route* out, void* ws,
-                          size_t ws_bytes, void* stream);
+                          double rho_exec_target, int32_t M, const spr_probe_options* probes, spr_route* out,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Renormalised block-sparse attention (Eq. (2)): each row of query group a attends to the
    keys of its selected K/V groups (and the text keys); text rows attend to all keys.
@@ -202,13 +236,15 @@ spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void*
    residuals centred by their weighted mean mu_R; B = (Xb^T W Xb + lam I)^-1 Xb^T W Rb (fp64
    Cholesky); O^hat_i = O^sp_i + mu_R + Xb_i B for unprobed video rows, the exact row for probes,
    O^sp for text rows.  `out` is [B][H][N][d] contiguous in original row order, fp32 or bf16
-   (out_dtype).  `fit_state` (nullable) receives [BH][3d + d*d] fp64: mu_X, sd, mu_R, B.
-   `head_status` [BH] receives SPR_HS_* bits.  EINVAL: lam < 0, std_eps <= 0, M out of range. */
+   (out_dtype).  `opts` (host, nullable: NULL is the full ridge without truncation) selects the
+   estimator family and output truncation of App. D.3-D.4.  `fit_state` (nullable) receives
+   [BH][3d + d*d] fp64: mu_X, sd, mu_R, B.  `head_status` [BH] receives SPR_HS_* bits.
+   EINVAL: lam < 0, std_eps <= 0, M out of range, an unknown family, out_rank < 0. */
 spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* params,
                                 const spr_partition* part, const spr_route* route, const float* o_sp,
-                                const float* o_probe, int32_t M, double lam, double std_eps, void* out,
-                                int32_t out_dtype, double* fit_state, int32_t* head_status, void* ws,
-                                size_t ws_bytes, void* stream);
+                                const float* o_probe, int32_t M, double lam, double std_eps,
+                                const spr_fit_options* opts, void* out, int32_t out_dtype, double* fit_state,
+                                int32_t* head_status, void* ws, size_t ws_bytes, void* stream);
 
 /* Baseline: dense flash attention softmax(q k^T / sqrt d) v for every row, same kernel family as
    sparsepr_attn_sparse.  out: [B][H][N][d] contiguous, fp32 or bf16 (out_dtype). */

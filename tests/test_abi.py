@@ -93,16 +93,25 @@ def test_entry_points_reject_invalid_arguments_on_the_host(lib):
     # probe workspace too small
     assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 64, dummy, dummy, 16, None) == 3
     # route: density target out of range, and a budget below one key (rho*N^2 <= M*N)
-    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 1.5, 64, ctypes.byref(route),
-                              dummy, 1 << 40, None) == 1
-    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 64 / 4096, 64,
+    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 1.5, 64, None,
                               ctypes.byref(route), dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), 64 / 4096, 64, None,
+                              ctypes.byref(route), dummy, 1 << 40, None) == 1
+    # an unknown probe mode
+    full_route = B.spr_route(*([dummy] * len(B.spr_route._fields_)))
+    assert lib.sparsepr_route(ctypes.byref(d), ctypes.byref(p), ctypes.byref(full), 0.3, 64,
+                              ctypes.byref(B.spr_probe_options(7, 0)), ctypes.byref(full_route), dummy, 1 << 40,
+                              None) == 1
     # fit: negative lambda, then zero std_eps
     args = (ctypes.byref(part), ctypes.byref(route), dummy, dummy, 64)
-    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, -1.0, 1e-6, dummy, 1, None, dummy,
+    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, -1.0, 1e-6, None, dummy, 1, None,
+                                    dummy, dummy, 1 << 40, None) == 1
+    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, 1.0, 0.0, None, dummy, 1, None, dummy,
                                     dummy, 1 << 40, None) == 1
-    assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, 1.0, 0.0, dummy, 1, None, dummy,
-                                    dummy, 1 << 40, None) == 1
+    # an unknown estimator family, a negative truncation rank
+    for fo in [B.spr_fit_options(4, 0), B.spr_fit_options(0, -1)]:
+        assert lib.sparsepr_fit_correct(ctypes.byref(d), ctypes.byref(p), *args, 1.0, 1e-6, ctypes.byref(fo), dummy,
+                                        1, None, dummy, dummy, 1 << 40, None) == 1
     # k-means helper: stage outside {0, 1}, rank not built
     assert lib.sparsepr_kmeans(1, 100, 48, 8, dummy, 0, 2, 25, 1e-4, dummy, dummy, dummy, dummy, 1 << 40, None) == 1
     assert lib.sparsepr_kmeans(1, 100, 20, 8, dummy, 0, 0, 25, 1e-4, dummy, dummy, dummy, dummy, 1 << 40, None) == 2

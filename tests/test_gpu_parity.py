@@ -317,3 +317,59 @@ def test_full_size_mid_sampled():
 
 def test_full_size_joint_text_sampled():
     _full_size_lockstep("joint", [(0, 0), (1, 23)])
+
+
+# ------------------------------------------------------------------ probe and estimator variants
+@pytest.mark.parametrize("name,heads,probe_mode,family,out_rank", [
+    ("tiny", [0], "random", "full", 0),
+    ("tiny", [0], "uniform", "full", 0),
+    ("tiny", [0], "stratified", "mean", 0),
+    ("tiny", [0], "stratified", "scalar", 0),
+    ("tiny", [0], "stratified", "diag", 0),
+    ("tiny", [0], "stratified", "full", 8),
+    ("small", [0, 5], "random", "diag", 16),
+    ("small", [3], "uniform", "full", 32),
+])
+def test_probe_and_estimator_variants(name, heads, probe_mode, family, out_rank):
+    """Table 4's probe choices and App. D.3-D.4's estimators through the C ABI: probe rows and
+    weights bit-exact against the oracle's rule, then the fit in lockstep (the oracle's estimator
+    on the GPU's own probe features and residuals) and the corrected rows."""
+    cfg = config(name)
+    opc = op_config(cfg, probe_mode=probe_mode, fit_family=family, out_rank=out_rank)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    N, Nv, d = cfg.N, cfg.Nv, cfg.d
+    for hd in heads:
+        if probe_mode == "random":
+            rows, w = O.select_probes_random(Nv, opc.M, opc.seed, hd)
+        elif probe_mode == "uniform":
+            rows, w = O.select_probes_uniform(Nv, opc.M)
+        else:
+            rows, w = None, None
+        if rows is not None:
+            assert np.array_equal(g["probe_idx"][hd], rows)
+            np.testing.assert_array_equal(g["probe_w"][hd], w)
+        qpos = g["q_pos"][hd]
+        P = g["probe_idx"][hd]
+        X = g["o_sp"][hd][qpos[P]].astype(np.float64)
+        fit = O.ridge_fit(X, g["o_probe"][hd] - X, g["probe_w"][hd], opc.lam, opc.std_eps, family, out_rank,
+                          opc.eig_clamp)
+        Bg = g["fit_state"][hd][3 * d:].reshape(d, d)
+        assert np.linalg.norm(Bg - fit["B"]) <= 1e-6 * max(np.linalg.norm(fit["B"]), 1e-12), family
+        if out_rank:
+            pass  # the truncation mixes columns: B V_r V_r^T has no family structure left
+        elif family == "mean":
+            assert np.all(Bg == 0)
+        elif family == "scalar":
+            assert np.all(Bg[~np.eye(d, dtype=bool)] == 0) and np.ptp(np.diag(Bg)) == 0
+        elif family == "diag":
+            assert np.all(Bg[~np.eye(d, dtype=bool)] == 0)
+        # corrected rows: every 5th video row that is not a probe
+        rr = np.setdiff1d(np.arange(0, Nv, 5), P)
+        want = O.correct(g["o_sp"][hd][qpos[rr]].astype(np.float64), fit)
+        err = row_rel_err(g["out"][hd][rr], want)
+        assert err.max() < ROW_TOL, ("out", err.max())
+        # probe rows are the exact rows (up to the output's rounding)
+        err = row_rel_err(g["out"][hd][P], g["o_probe"][hd])
+        assert err.max() < ROW_TOL
