@@ -61,6 +61,11 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--regime", choices=["warm", "cold"], default="warm",
                     help="headline regime: later calls (App. C.1 warm start) or cold calls")
+    ap.add_argument("--probe-mode", choices=["stratified", "random", "uniform"], default="stratified",
+                    help="probe choice (Table 4); the operator's is stratified")
+    ap.add_argument("--fit-family", choices=["full", "mean", "scalar", "diag"], default="full",
+                    help="correction family (App. D.4); the operator's is the full ridge")
+    ap.add_argument("--out-rank", type=int, default=0, help="output truncation rank (App. D.3); 0: none")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for traffic counters)")
     return ap.parse_args()
@@ -122,7 +127,8 @@ def main():
     if args.max_iters is not None:
         cfg = cfg.with_(max_iters=args.max_iters)
     opc = spr.OperatorConfig(Ck=cfg.Ck, Cq=cfg.Cq, rK=cfg.rK, rQ=min(cfg.rQ, cfg.d), Ms=cfg.Ms,
-                             max_iters=cfg.max_iters, tol=cfg.tol, M=cfg.M, rho=cfg.rho, lam=cfg.lam, seed=0)
+                             max_iters=cfg.max_iters, tol=cfg.tol, M=cfg.M, rho=cfg.rho, lam=cfg.lam, seed=0,
+                             probe_mode=args.probe_mode, fit_family=args.fit_family, out_rank=args.out_rank)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     # two input sets of the same heads (consecutive calls: same positions, fresh noise); calls
     # alternate between them so that every later call sees inputs that differ from the last one
@@ -200,6 +206,7 @@ def main():
         "config": {"workload": (f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} grid={'x'.join(map(str, cfg.grid))} "
                                 f"d={cfg.d} {cfg.dtype} n_text={cfg.n_text}"),
                    "Ck": cfg.Ck, "Cq": cfg.Cq, "M": cfg.M, "rho_target": cfg.rho, "max_iters": cfg.max_iters,
+                   "probes": args.probe_mode, "fit_family": args.fit_family, "out_rank": args.out_rank,
                    "parallelism": "single GPU, heads batched"},
         "ms_per_call": round(ms_call, 4),
         "regime": ("later calls of App. C.1 (warm start: k-means from the previous centroids, 2 "
