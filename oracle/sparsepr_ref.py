@@ -50,6 +50,11 @@ against the pages; the tests pin them against mathematics instead):
   the row-major (t, h, w) sequence; both carry weights Nv / M.  The output truncation
   takes the leading eigenvectors of Rbar^T W Rbar, eigenvalues at or below eig_clamp
   times the largest counted as absent.
+* Grouped-query attention (Sec. 4.3; App. C.2): the concatenation of the G heads'
+  video query rows is sampled like one head's rows with G * Ms in place of Ms, which
+  takes the same evenly spaced rows from each head.  The K/V k-means draws from the
+  stream of the K/V head's index b * Hkv + j; the query k-means and random probes from
+  that of the query head b * H + h, which uses K/V head h // G.
 """
 from __future__ import annotations
 
@@ -67,6 +72,7 @@ __all__ = [
     "select_probes_random", "select_probes_uniform", "output_projector",
     "executed_density", "allocate_probes", "select_probes", "ridge_fit", "correct", "relative_error",
     "sparsepr_head", "cholesky_upper", "metric_factor_warm", "warm_centres",
+    "key_metric_shared", "kv_side", "query_side", "sparsepr_group",
 ]
 
 U64 = (1 << 64) - 1
@@ -125,6 +131,14 @@ def key_metric(Q: np.ndarray, Ms: int) -> np.ndarray:
     """Key-response metric M_K = Q_s^T Q_s / M_s (Sec. 4.1, App. B.1)."""
     Qs = np.asarray(Q, dtype=np.float64)[sample_rows(Q.shape[0], Ms)]
     return Qs.T @ Qs / Qs.shape[0]
+
+
+def key_metric_shared(Qs: Sequence[np.ndarray], Ms: int) -> np.ndarray:
+    """Key-response metric shared by the G query heads of one K/V head under grouped-query
+    attention (Sec. 4.3, routing and GQA; App. C.2): their query rows are concatenated and
+    up to G * Ms evenly spaced rows of the concatenation give one metric."""
+    Qc = np.concatenate([np.asarray(Q, dtype=np.float64) for Q in Qs], axis=0)
+    return key_metric(Qc, Ms * len(Qs))
 
 
 def metric_factor(Mmat: np.ndarray, r: int, clamp: float) -> Tuple[np.ndarray, np.ndarray]:
@@ -602,21 +616,17 @@ def relative_error(O: np.ndarray, O_dense: np.ndarray) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ whole head
-def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int]] = None,
-                  full: bool = True, warm: Optional[Dict] = None) -> Dict:
-    """One head of the operator, every stage in the order of Sec. 4 and App. C.3.
-    ``rows`` limits the attention outputs to a subset (default: all rows).  ``warm``
-    (the ``state`` of the previous call of this head: FK, FQ, kbar, qbar) selects the
-    later-call path of App. C.1: factors by subspace iteration from the previous ones
-    and k-means started from the previous centroids."""
-    q = np.asarray(q, dtype=np.float64)
+def kv_side(qs: Sequence, k, v, p: Params, kv_head: int = 0, warm: Optional[Dict] = None) -> Dict:
+    """The K/V side of one K/V head (Sec. 4.1, 4.2): key metric from the query rows of the heads
+    in ``qs`` (one head, or the G heads that share this K/V head), key factor, K/V k-means, group
+    statistics, query metric and query factor.  The k-means stream is that of ``kv_head``."""
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    N, d = q.shape
+    N, d = k.shape
     Nv = N - p.n_text
-    qv, kv, vv = q[:Nv], k[:Nv], v[:Nv]
-    out: Dict = {}
-    MK = key_metric(qv, p.Ms)
+    kv, vv = k[:Nv], v[:Nv]
+    qvs = [np.asarray(q, dtype=np.float64)[:Nv] for q in qs]
+    MK = key_metric(qvs[0], p.Ms) if len(qvs) == 1 else key_metric_shared(qvs, p.Ms)
     warm_ok = []
     if warm is None:
         FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
@@ -626,8 +636,8 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
         warm_ok.append(ok)
     phiK = project(kv, FK)
     initK = None if warm is None else warm_centres(warm["kbar"], lambda x: project(x, FK), phiK, p.Ck,
-                                                   p.seed, head, 0)
-    km = kmeans(phiK, p.Ck, p.seed, head, 0, p.max_iters, p.tol, init=initK)
+                                                   p.seed, kv_head, 0)
+    km = kmeans(phiK, p.Ck, p.seed, kv_head, 0, p.max_iters, p.tol, init=initK)
     kv_lab, nkv = compact_labels(km["labels"], p.Ck)
     kv_size, kbar, vbar = key_group_stats(kv, vv, kv_lab, nkv)
     MQ = query_metric(kbar)
@@ -637,6 +647,24 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
         FQ, ok = metric_factor_warm(MQ, warm["FQ"], p.rQ, p.eig_clamp)
         wQ = None
         warm_ok.append(ok)
+    return dict(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
+                kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, warm_ok=warm_ok)
+
+
+def query_side(q, k, v, kvs: Dict, p: Params, head: int = 0, rows: Optional[Sequence[int]] = None,
+               full: bool = True, warm: Optional[Dict] = None) -> Dict:
+    """The query side of one query head given its K/V head's ``kv_side`` result: query
+    partition (Sec. 4.2), routing (Sec. 4.3), probes (App. A.2), and with ``full`` the sparse
+    and probe attention, the ridge fit and the correction (Sec. 4.4).  Streams are those of
+    ``head``; ``warm`` supplies the previous query centroids ``qbar``."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, d = q.shape
+    Nv = N - p.n_text
+    qv, kv, vv = q[:Nv], k[:Nv], v[:Nv]
+    FQ, kv_lab, kv_size = kvs["FQ"], kvs["kv_label"], kvs["kv_size"]
+    out: Dict = dict(kvs)
     phiQ = query_coords(qv, FQ, p.rms_eps)
     initQ = None if warm is None else warm_centres(warm["qbar"], lambda x: query_coords(x, FQ, p.rms_eps),
                                                    phiQ, p.Cq, p.seed, head, 1)
@@ -644,7 +672,7 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
     q_lab, nq = compact_labels(qm["labels"], p.Cq)
     q_size, qbar, cbar, dist = query_group_stats(qv, phiQ, q_lab, nq)
     T = key_budget(p.rho, N, Nv, p.M, p.n_text)
-    sel, scores, rinfo = route(qbar, kv, vv, kv_lab, kbar, vbar, kv_size, T)
+    sel, scores, rinfo = route(qbar, kv, vv, kv_lab, kvs["kbar"], kvs["vbar"], kv_size, T)
     pairs = int(sum(int(q_size[a]) * (int(kv_size[sel[a]].sum()) + p.n_text) for a in range(nq)))
     rho_exec = executed_density(pairs, N, p.M, p.n_text)
     if p.probe_mode == "stratified":
@@ -655,11 +683,10 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
         (probes, w), m_a = select_probes_uniform(Nv, p.M), None
     else:
         raise ValueError(p.probe_mode)
-    out.update(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
-               kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, phiQ=phiQ, kmQ=qm, q_label=q_lab, n_q=nq,
+    out.update(phiQ=phiQ, kmQ=qm, q_label=q_lab, n_q=nq,
                q_size=q_size, qbar=qbar, cbar=cbar, qdist=dist, T=T, sel=sel, scores=scores,
                route_info=rinfo, pairs=pairs, rho_exec=rho_exec, probes=probes, probe_w=w, m_a=m_a,
-               warm_ok=warm_ok, state=dict(FK=FK, FQ=FQ, kbar=kbar, qbar=qbar))
+               state=dict(FK=kvs["FK"], FQ=FQ, kbar=kvs["kbar"], qbar=qbar))
     if not full:
         return out
     q_lab_full = np.concatenate([q_lab, np.full(p.n_text, -1)])
@@ -677,3 +704,26 @@ def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int
             Ohat[ir] = Od[pos[int(r)]]
     out.update(rows=rows, O_sp=Osp, O_hat=Ohat, probe_dense=Od, probe_sparse=X, fit=fit)
     return out
+
+
+def sparsepr_head(q, k, v, p: Params, head: int = 0, rows: Optional[Sequence[int]] = None,
+                  full: bool = True, warm: Optional[Dict] = None) -> Dict:
+    """One head of the operator, every stage in the order of Sec. 4 and App. C.3.
+    ``rows`` limits the attention outputs to a subset (default: all rows).  ``warm``
+    (the ``state`` of the previous call of this head: FK, FQ, kbar, qbar) selects the
+    later-call path of App. C.1: factors by subspace iteration from the previous ones
+    and k-means started from the previous centroids."""
+    kvs = kv_side([q], k, v, p, head, warm)
+    return query_side(q, k, v, kvs, p, head, rows, full, warm)
+
+
+def sparsepr_group(qs: Sequence, k, v, p: Params, kv_head: int, heads: Sequence[int],
+                   rows: Optional[Sequence[int]] = None, full: bool = True,
+                   warm: Optional[Sequence[Dict]] = None) -> List[Dict]:
+    """Grouped-query attention (Sec. 4.3, routing and GQA; App. C.2): the G query heads ``qs``
+    (stream indices ``heads``) share K/V head ``kv_head`` (k, v): one shared key metric and K/V
+    partition, then a query partition, routing, probes and fit per query head.  ``warm`` is the
+    list of the heads' previous ``state``s (their K/V-side entries are the shared ones)."""
+    kvs = kv_side(qs, k, v, p, kv_head, None if warm is None else warm[0])
+    return [query_side(q, k, v, kvs, p, h, rows, full, None if warm is None else warm[g])
+            for g, (q, h) in enumerate(zip(qs, heads))]

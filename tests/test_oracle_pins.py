@@ -697,3 +697,76 @@ def test_variant_pipeline_runs_and_reduces_to_reference_choices():
     mean = O.sparsepr_head(q, k, v, O.Params(**base, fit_family="mean"), rows=np.arange(0, N, 7))
     un = ~np.isin(mean["rows"], mean["probes"])
     np.testing.assert_allclose(mean["O_hat"][un], mean["O_sp"][un] + mean["fit"]["muR"], rtol=1e-12)
+
+
+# ------------------------------------------------------------------ grouped-query attention
+def test_shared_key_metric_takes_the_evenly_spaced_rows_of_every_head():
+    # Sec. 4.3 (routing and GQA), App. C.2: G = 2 heads of 8 rows, Ms = 4 -> 8 of the 16
+    # concatenated rows, which are rows 0, 2, 4, 6 of each head
+    d = 3
+    Q0 = np.full((8, d), 1e6)
+    Q1 = np.full((8, d), -1e6)
+    Q0[[0, 2, 4, 6]] = [[1, 0, 0], [0, 2, 0], [0, 0, 3], [1, 1, 0]]
+    Q1[[0, 2, 4, 6]] = [[2, 0, 0], [0, 0, 1], [0, 1, 0], [0, 0, 0]]
+    expect = np.array([[6, 1, 0], [1, 6, 0], [0, 0, 10]], dtype=float) / 8.0
+    np.testing.assert_allclose(O.key_metric_shared([Q0, Q1], 4), expect, rtol=0, atol=1e-12)
+    # fewer rows than G * Ms: every row of every head
+    Qs = [_rng(90, g).standard_normal((5, d)) for g in range(3)]
+    allrows = np.concatenate(Qs)
+    np.testing.assert_allclose(O.key_metric_shared(Qs, 2048), allrows.T @ allrows / 15, rtol=1e-13)
+
+
+def test_shared_key_metric_is_the_mean_of_the_heads_metrics():
+    # evenly spaced rows of the concatenation fall at the same offsets in every head, so the
+    # shared metric is the mean of the per-head metrics, ragged row counts included
+    for Nv, Ms, G in [(1000, 96, 3), (777, 2048, 2), (4096, 2048, 4)]:
+        Qs = [_rng(91, Nv, g).standard_normal((Nv, 8)) for g in range(G)]
+        want = sum(O.key_metric(Q, Ms) for Q in Qs) / G
+        np.testing.assert_allclose(O.key_metric_shared(Qs, Ms), want, rtol=1e-12, atol=1e-14)
+
+
+def _gqa_problem(seed, N=320, d=16):
+    q, k, v = _rng(seed).standard_normal((3, N, d))
+    p = O.Params(Ck=12, Cq=10, rK=8, rQ=12, Ms=128, M=10, rho=0.4, lam=1.0, seed=6, max_iters=30, tol=0.0)
+    return q, k, v, p
+
+
+def test_gqa_group_of_identical_heads_is_the_single_head_operator():
+    q, k, v, p = _gqa_problem(92)
+    single = O.sparsepr_head(q, k, v, p, head=3)
+    for out in O.sparsepr_group([q, q, q], k, v, p, kv_head=3, heads=[3, 3, 3]):
+        assert np.array_equal(out["kv_label"], single["kv_label"])
+        assert np.array_equal(out["q_label"], single["q_label"])
+        assert all(np.array_equal(a, b) for a, b in zip(out["sel"], single["sel"]))
+        assert np.array_equal(out["probes"], single["probes"])
+        np.testing.assert_allclose(out["O_hat"], single["O_hat"], rtol=0, atol=1e-10)
+
+
+def test_gqa_scaled_head_changes_the_metric_but_not_the_partition():
+    # with q2 = 2 q1 the shared metric is (1 + 4) / 2 = 2.5 times head 1's: F_K scales by
+    # sqrt(2.5), k-means on uniformly scaled coordinates takes the same decisions, so the K/V
+    # partition is head 1's alone; RMSNorm removes the scale from the query coordinates
+    q, k, v, p = _gqa_problem(93)
+    single = O.sparsepr_head(q, k, v, p, head=0, full=False)
+    outs = O.sparsepr_group([q, 2 * q], k, v, p, kv_head=0, heads=[0, 0], full=False)
+    np.testing.assert_allclose(outs[0]["MK"], 2.5 * single["MK"], rtol=1e-12)
+    for out in outs:
+        assert np.array_equal(out["kv_label"], single["kv_label"])
+        np.testing.assert_allclose(out["kbar"], single["kbar"], rtol=0, atol=1e-12)
+        assert np.array_equal(out["q_label"], single["q_label"])
+    # the query side is per head: the scaled head routes from its own (doubled) centroids
+    np.testing.assert_allclose(outs[1]["qbar"], 2 * outs[0]["qbar"], rtol=1e-12)
+
+
+def test_gqa_kv_side_does_not_depend_on_the_order_of_the_query_heads():
+    q, k, v, p = _gqa_problem(94)
+    q2 = _rng(95).standard_normal(q.shape)
+    a = O.sparsepr_group([q, q2], k, v, p, kv_head=1, heads=[2, 3], full=False)
+    b = O.sparsepr_group([q2, q], k, v, p, kv_head=1, heads=[3, 2], full=False)
+    assert np.array_equal(a[0]["kv_label"], b[0]["kv_label"])
+    np.testing.assert_allclose(a[0]["MK"], b[0]["MK"], rtol=1e-13)
+    # each query head keeps its own partition whatever its position in the group
+    assert np.array_equal(a[0]["q_label"], b[1]["q_label"]) and np.array_equal(a[1]["q_label"], b[0]["q_label"])
+    # and the shared partition is not that of either head alone
+    alone = O.sparsepr_head(q, k, v, p, head=1, full=False)
+    assert not np.allclose(a[0]["MK"], alone["MK"])
