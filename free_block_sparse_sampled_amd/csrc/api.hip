@@ -32,7 +32,7 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.km_region = take(kmeans_ws_bytes(int(BH), int(Nv), L.Cmax, L.rmax));
   L.cbar = take(BH * p.Cq * p.rQ * 8);
   L.vstat = take(BH * Nv * 2 * 8);
-  L.gstat = take(BH * 8 * 4);
+  L.gstat = take(2 * BH * 8 * 4);  // per query head, then per K/V head
   L.pstat = take(BH * p.Cq * 2 * 4);
   L.shift = take(BH * p.Cq * 8);
   L.lbar = take(BH * p.Cq * p.Ck * 8);
@@ -68,13 +68,20 @@ static spr_status check_desc(const spr_desc* d) {
   const int64_t es = d->dtype == SPR_BF16 ? 2 : 4;
   if (d->sn < d->d || d->sh < 1 || d->sb < 1) return SPR_EINVAL;
   if ((d->sn * es) % 16 || (d->sh * es) % 16 || (d->sb * es) % 16) return SPR_EINVAL;
+  if (d->Hkv < 0 || d->Hkv > d->H || d->reserved != 0) return SPR_EINVAL;
+  if (is_gqa(*d)) {
+    if (d->H % d->Hkv) return SPR_EINVAL;
+    if (d->ksn < d->d || d->ksh < 1 || d->ksb < 1) return SPR_EINVAL;
+    if ((d->ksn * es) % 16 || (d->ksh * es) % 16 || (d->ksb * es) % 16) return SPR_EINVAL;
+  }
   return SPR_OK;
 }
 
 // The attention kernels address one head's rows with 32-bit byte offsets.
 static bool head_fits_32bit(const spr_desc* d) {
   const int64_t es = d->dtype == SPR_BF16 ? 2 : 4;
-  return (int64_t(d->N) - 1) * d->sn * es + int64_t(d->d) * es < (int64_t(1) << 31);
+  const int64_t sn = is_gqa(*d) && d->ksn > d->sn ? d->ksn : d->sn;
+  return (int64_t(d->N) - 1) * sn * es + int64_t(d->d) * es < (int64_t(1) << 31);
 }
 
 static spr_status check_params(const spr_desc* d, const spr_part_params* p) {

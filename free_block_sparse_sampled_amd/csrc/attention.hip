@@ -42,13 +42,15 @@ struct AttnParams {
   const void* k;
   const void* v;
   HeadGeom g;
+  HeadGeom gk;             // DENSE, PROBE: geometry of k and v (K/V head hd / G of query head hd)
+  int G;                   // query heads per K/V head; SPARSE: Kp, Vp, n_kv, kv_off are per K/V head
   // sparse routing
   const int* tiles;        // [BH][tmax][8]: a0, row0, n0, a1, row1, n1 (row0 / row1 index Qp rows)
   const int* ntiles;       // [BH]
   const int* tile_prefix;  // [BH + 1]: tiles of the heads before each head; [BH] = all tiles
   int tmax, BH;
-  const int* n_kv;
-  const int* kv_off;     // [BH][Ck+1]
+  const int* n_kv;       // [BH / G]
+  const int* kv_off;     // [BH / G][Ck+1]
   const int* sel_cnt;    // [BH][Cq+1]
   const int* sel_kv;     // [BH][Cq+1][Ck+1]
   int Cq, Ck;
@@ -124,7 +126,7 @@ __device__ inline TileInfo decode_tile(const AttnParams& P) {
   return t;
 }
 
-// Length of K/V group b of head hd (the text group when b == n_kv) and its first row in Kp.
+// Length of K/V group b of a K/V head (the text group when b == n_kv) and its first row in Kp.
 __device__ __forceinline__ void kv_group(const AttnParams& P, const int* off, int nkv, int b, int* s, int* l) {
   if (b < nkv) {
     *s = off[b];
@@ -158,8 +160,8 @@ __device__ inline int build_segments(const AttnParams& P, int hd, int a, int* se
                                      int* nseg) {
   const int cnt = P.sel_cnt[size_t(hd) * (P.Cq + 1) + a];
   const int* sel = P.sel_kv + (size_t(hd) * (P.Cq + 1) + a) * (P.Ck + 1);
-  const int* off = P.kv_off + size_t(hd) * (P.Ck + 1);
-  const int nkv = P.n_kv[hd];
+  const int* off = P.kv_off + size_t(hd / P.G) * (P.Ck + 1);
+  const int nkv = P.n_kv[hd / P.G];
   for (int i = threadIdx.x; i < cnt; i += blockDim.x) kv_group(P, off, nkv, sel[i], seg_start + i, seg_cum + i);
   __syncthreads();
   *nseg = cnt;
@@ -172,8 +174,8 @@ __device__ inline int build_segments(const AttnParams& P, int hd, int a, int* se
 // ascending group id.  Returns the total number of keys.
 __device__ inline int build_union_segments(const AttnParams& P, const TileInfo& t, int* seg_start, int* seg_cum,
                                            int* seg_cat, unsigned* bm /* [2][33] */, int* scan, int* nseg_out) {
-  const int hd = t.hd;
-  const int nkv = P.n_kv[hd];
+  const int hd = t.hd, hk = hd / P.G;  // query head, its K/V head
+  const int nkv = P.n_kv[hk];
   const int ng = nkv + (P.g.n_text > 0 ? 1 : 0);
   for (int i = threadIdx.x; i < 66; i += blockDim.x) bm[i] = 0u;
   __syncthreads();
@@ -208,7 +210,7 @@ __device__ inline int build_union_segments(const AttnParams& P, const TileInfo& 
   const int ex = block_exscan_i(c3 | (c1 << 11) | (c2 << 22), scan, &tot);
   const int n3 = tot & 0x7ff, n1 = (tot >> 11) & 0x7ff, n2 = (tot >> 22) & 0x7ff;
   int o3 = ex & 0x7ff, o1 = n3 + ((ex >> 11) & 0x7ff), o2 = n3 + n1 + ((ex >> 22) & 0x7ff);
-  const int* off = P.kv_off + size_t(hd) * (P.Ck + 1);
+  const int* off = P.kv_off + size_t(hk) * (P.Ck + 1);
   for (int b = i0; b < min(i0 + per, ng); ++b) {
     const int c = cat_of(b);
     if (c == 0) continue;
@@ -295,13 +297,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const uint16_t* Vb;
   int row_bytes;
   if constexpr (SPARSE) {
-    Kb = static_cast<const uint16_t*>(P.k) + size_t(hd) * P.g.N * D;
-    Vb = static_cast<const uint16_t*>(P.v) + size_t(hd) * P.g.N * D;
+    Kb = static_cast<const uint16_t*>(P.k) + size_t(hd / P.G) * P.g.N * D;
+    Vb = static_cast<const uint16_t*>(P.v) + size_t(hd / P.G) * P.g.N * D;
     row_bytes = D * 2;
   } else {
-    Kb = static_cast<const uint16_t*>(P.k) + P.g.base(hd);
-    Vb = static_cast<const uint16_t*>(P.v) + P.g.base(hd);
-    row_bytes = int(P.g.sn) * 2;
+    Kb = static_cast<const uint16_t*>(P.k) + P.gk.base(hd / P.G);
+    Vb = static_cast<const uint16_t*>(P.v) + P.gk.base(hd / P.G);
+    row_bytes = int(P.gk.sn) * 2;
   }
   const int head_bytes = (P.g.N - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, head_bytes, 0x00020000);
@@ -694,13 +696,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
   const float* Vb;
   int64_t krs;
   if constexpr (MODE == MODE_SPARSE) {
-    Kb = static_cast<const float*>(P.k) + size_t(hd) * P.g.N * D;
-    Vb = static_cast<const float*>(P.v) + size_t(hd) * P.g.N * D;
+    Kb = static_cast<const float*>(P.k) + size_t(hd / P.G) * P.g.N * D;
+    Vb = static_cast<const float*>(P.v) + size_t(hd / P.G) * P.g.N * D;
     krs = D;
   } else {
-    Kb = static_cast<const float*>(P.k) + P.g.base(hd);
-    Vb = static_cast<const float*>(P.v) + P.g.base(hd);
-    krs = P.g.sn;
+    Kb = static_cast<const float*>(P.k) + P.gk.base(hd / P.G);
+    Vb = static_cast<const float*>(P.v) + P.gk.base(hd / P.G);
+    krs = P.gk.sn;
   }
   int nseg = 0, total;
   if constexpr (MODE == MODE_SPARSE) {
@@ -905,6 +907,8 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
   P.q = part.Qp; P.k = part.Kp; P.v = part.Vp;
   if (desc.dtype == SPR_BF16) P.v = ws_ptr<void>(ws, L.vh);
   P.g = make_geom(desc);
+  P.gk = make_kv_geom(desc);
+  P.G = kv_group_size(desc);
   P.tiles = tiles; P.ntiles = ntiles; P.tile_prefix = tprefix; P.tmax = L.tmax; P.BH = BH;
   P.n_kv = part.n_kv; P.kv_off = part.kv_off; P.sel_cnt = route.sel_cnt; P.sel_kv = route.sel_kv;
   P.Cq = p.Cq; P.Ck = p.Ck;
@@ -921,6 +925,8 @@ spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, c
   AttnParams P = {};
   P.q = q; P.k = k; P.v = v;
   P.g = make_geom(desc);
+  P.gk = make_kv_geom(desc);
+  P.G = kv_group_size(desc);
   P.probe_idx = probe_idx; P.M = M; P.splits = L.splits;
   P.part = ws_ptr<float>(ws, L.pr_part);
   const int BH = desc.B * desc.H;
@@ -937,6 +943,8 @@ spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, co
   AttnParams P = {};
   P.q = q; P.k = k; P.v = v;
   P.g = make_geom(desc);
+  P.gk = make_kv_geom(desc);
+  P.G = kv_group_size(desc);
   P.out = out; P.out_dtype = out_dtype;
   const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_DENSE>() : kTileRows;
   return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, rows), desc.B * desc.H), desc.d, desc.dtype, st);

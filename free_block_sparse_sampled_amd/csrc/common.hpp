@@ -74,6 +74,22 @@ inline HeadGeom make_geom(const spr_desc& d) {
   return g;
 }
 
+// Grouped-query attention: Hkv K/V heads, each shared by G = H / Hkv query heads (query head hd
+// of the flattened index uses K/V head hd / G).
+inline bool is_gqa(const spr_desc& d) { return d.Hkv > 0 && d.Hkv < d.H; }
+inline int kv_heads(const spr_desc& d) { return is_gqa(d) ? d.Hkv : d.H; }
+inline int kv_group_size(const spr_desc& d) { return d.H / kv_heads(d); }
+
+// Geometry of k and v: Hkv heads with their own strides, or the geometry of q.
+inline HeadGeom make_kv_geom(const spr_desc& d) {
+  HeadGeom g = make_geom(d);
+  if (is_gqa(d)) {
+    g.H = d.Hkv;
+    g.sb = d.ksb; g.sh = d.ksh; g.sn = d.ksn;
+  }
+  return g;
+}
+
 // ----------------------------------------------------------------- reductions
 __device__ __forceinline__ double wave_sum_d(double x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -168,7 +184,7 @@ struct Workspace {
   size_t km_region;  // k-means scratch (see kmeans_carve)
   size_t cbar;       // double [BH][Cq][rQ]      mean query coordinates c_a
   size_t vstat;      // double [BH][Nv][2]       v_j . vbar_b(j), |v_j|^2 in Kp order
-  size_t gstat;      // int    [BH][8]           flags / counters per head
+  size_t gstat;      // int    [2 BH][8]         flags per query head, then per K/V head
   size_t pstat;      // int    [BH][Cq][2]       probes per query group, prefix
   size_t shift;      // double [BH][Cq]          per-query-group exponent shift of the scores
   size_t lbar;       // double [BH][Cq][Ck]      centroid logits qbar_a . kbar_b / sqrt d

@@ -12,36 +12,40 @@ namespace spr {
 
 // ------------------------------------------------------------------ key metric
 // M_K = Q_s^T Q_s / M_s over rows s_i = floor(i * Nv / M_s) (Sec. 4.1 / App. B.1 for the
-// metric, App. C.2 for the evenly spaced sampling).  16x16 output tile per block, fp64 sums.
+// metric, App. C.2 for the evenly spaced sampling); with grouped-query attention Q_s stacks the
+// sampled rows of the G query heads of K/V head j (heads j G .. j G + G - 1), M_K = Q_s^T Q_s /
+// (G M_s).  16x16 output tile per block, fp64 sums.
 template <int DT>
-__global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict__ q, HeadGeom g, int Ms,
+__global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict__ q, HeadGeom g, int Ms, int G,
                                                          double* __restrict__ out) {
-  const int hd = blockIdx.y;
+  const int hj = blockIdx.y;
   const int tiles = g.d / 16;
   const int i0 = (blockIdx.x / tiles) * 16, j0 = (blockIdx.x % tiles) * 16;
   const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
   __shared__ float As[32][17], Bs[32][17];
   const int m = min(Ms, g.Nv);
-  const int64_t base = g.base(hd);
   double acc = 0.0;
-  for (int s0 = 0; s0 < m; s0 += 32) {
-    for (int e = threadIdx.x; e < 32 * 16; e += 256) {
-      const int rr = e >> 4, cc = e & 15, s = s0 + rr;
-      float a = 0.f, b = 0.f;
-      if (s < m) {
-        const int64_t row = (int64_t(s) * g.Nv) / m;
-        a = load_elem<DT>(q, base + row * g.sn + i0 + cc);
-        b = load_elem<DT>(q, base + row * g.sn + j0 + cc);
+  for (int gi = 0; gi < G; ++gi) {
+    const int64_t base = g.base(hj * G + gi);
+    for (int s0 = 0; s0 < m; s0 += 32) {
+      for (int e = threadIdx.x; e < 32 * 16; e += 256) {
+        const int rr = e >> 4, cc = e & 15, s = s0 + rr;
+        float a = 0.f, b = 0.f;
+        if (s < m) {
+          const int64_t row = (int64_t(s) * g.Nv) / m;
+          a = load_elem<DT>(q, base + row * g.sn + i0 + cc);
+          b = load_elem<DT>(q, base + row * g.sn + j0 + cc);
+        }
+        As[rr][cc] = a;
+        Bs[rr][cc] = b;
       }
-      As[rr][cc] = a;
-      Bs[rr][cc] = b;
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll 8
-    for (int rr = 0; rr < 32; ++rr) acc = fma(double(As[rr][ti]), double(Bs[rr][tj]), acc);
-    __syncthreads();
+      for (int rr = 0; rr < 32; ++rr) acc = fma(double(As[rr][ti]), double(Bs[rr][tj]), acc);
+      __syncthreads();
+    }
   }
-  out[size_t(hd) * g.d * g.d + size_t(i0 + ti) * g.d + j0 + tj] = acc / double(m);
+  out[size_t(hj) * g.d * g.d + size_t(i0 + ti) * g.d + j0 + tj] = acc / (double(m) * G);
 }
 
 // Centred key centroids K~ = kbar_b - mu_K over the n_kv nonempty groups (App. B.2).  One block
@@ -492,11 +496,11 @@ __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restr
                                                            const int* __restrict__ n_prev, int C, int d,
                                                            const double* __restrict__ Fall, int r, double eps,
                                                            const double* __restrict__ feat, int n, uint64_t seed,
-                                                           int stage, double* __restrict__ cent) {
+                                                           int stage, int fdiv, double* __restrict__ cent) {
   __shared__ double ys[64][65];
   const int hd = blockIdx.y, m0 = blockIdx.x * 64;
   const int np = min(n_prev[hd], C);
-  const double* F = Fall + size_t(hd) * d * r;
+  const double* F = Fall + size_t(hd / fdiv) * d * r;  // factor of the head's K/V head
   for (int e = threadIdx.x; e < 64 * r; e += blockDim.x) {
     const int ml = e / r, j = e % r, m = m0 + ml;
     if (m >= C) continue;
@@ -541,7 +545,8 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 template <int DT, bool RMS>
 __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
                                                       const double* __restrict__ Fall, int r, double eps,
-                                                      double* __restrict__ out, int* __restrict__ gstat, int chunks) {
+                                                      double* __restrict__ out, int* __restrict__ gstat, int chunks,
+                                                      int fdiv) {
   extern __shared__ double smem[];
   const int d = g.d;
   const int NT = (r + 15) >> 4;
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
   double* Fs = smem;                                      // [d][FS]
   float* Xs = reinterpret_cast<float*>(smem + d * FS);  // [128][XS]
   const int hd = blockIdx.y;
-  const double* F = Fall + size_t(hd) * d * r;
+  const double* F = Fall + size_t(hd / fdiv) * d * r;  // factor of the head's K/V head
   for (int e = threadIdx.x; e < d * FS; e += 512) {
     const int kk = e / FS, c = e % FS;
     Fs[e] = c < r ? F[size_t(kk) * r + c] : 0.0;
@@ -868,6 +873,12 @@ __global__ __launch_bounds__(256) void qdist_kernel(const double* __restrict__ f
   if (i < n && sub == 0) out[size_t(hd) * n + i] = sqrt(s);
 }
 
+// Status bits of the K/V side (kvstat, per K/V head) into every query head of the group.
+__global__ void merge_kv_status_kernel(int* __restrict__ gstat, const int* __restrict__ kvstat, int BH, int G) {
+  const int hd = blockIdx.x * 256 + threadIdx.x;
+  if (hd < BH) gstat[hd * 8 + 0] |= kvstat[(hd / G) * 8 + 0];
+}
+
 // ------------------------------------------------------------------ host drivers
 size_t compact_smem(int C) { return size_t(3 * C + 1024 + 16 * C) * sizeof(int); }
 
@@ -908,16 +919,23 @@ template <int DT>
 static spr_status partition_impl(const spr_desc& desc, const void* q, const void* k, const void* v,
                                  const spr_part_params& p, const spr_warm* warm, spr_partition& out, void* ws,
                                  const Workspace& L, hipStream_t st) {
-  const HeadGeom g = make_geom(desc);
+  // The K/V side (M_K, F_K, the K/V partition, the centroids, M_Q and F_Q) runs once per K/V
+  // head (BHkv heads, geometry gk); the query side per query head, which takes the factor F_Q
+  // of its K/V head hd / G.  Status bits of the K/V side go to kvstat and are merged at the end.
+  const HeadGeom g = make_geom(desc), gk = make_kv_geom(desc);
   const int BH = desc.B * desc.H, d = desc.d, Nv = g.Nv;
+  const int G = kv_group_size(desc), BHkv = BH / G;
   double* metric = wsp<double>(ws, L.metric);
   double* phiK = out.phiK ? out.phiK : wsp<double>(ws, L.phiK);
   double* phiQ = out.phiQ ? out.phiQ : wsp<double>(ws, L.phiQ);
   int* gstat = wsp<int>(ws, L.gstat);
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(ceil_div(BH * 8, 256)), dim3(256), 0, st, gstat, size_t(BH) * 8);
+  int* kvstat = gstat + size_t(BH) * 8;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(ceil_div((BH + BHkv) * 8, 256)), dim3(256), 0, st, gstat,
+                     size_t(BH + BHkv) * 8);
 
   // M_K and F_K
-  hipLaunchKernelGGL(key_metric_kernel<DT>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, q, g, p.Ms, metric);
+  hipLaunchKernelGGL(key_metric_kernel<DT>, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, q, g, p.Ms, G,
+                     metric);
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
   allow_lds(eigen_factor_kernel, jac_smem);
@@ -925,80 +943,81 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   const size_t sub_smem = (2 * size_t(d) * rmx + size_t(rmx) * rmx) * sizeof(double);
   allow_lds(subspace_factor_kernel, sub_smem);
   if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
-    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BH), dim3(256), sub_smem, st, metric, warm->FK, d, p.rK,
-                       p.eig_clamp, out.FK, gstat, 2);
-  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
-                     gstat, warm ? 2 : -1);
+    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BHkv), dim3(256), sub_smem, st, metric, warm->FK, d, p.rK,
+                       p.eig_clamp, out.FK, kvstat, 2);
+  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
+                     kvstat, warm ? 2 : -1);
   SPR_CHECK_LAUNCH();
   // phi_K = K F_K
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
-  const int pchunks = project_chunks(Nv, BH);
+  const int pchunks = project_chunks(Nv, BH), kchunks = project_chunks(Nv, BHkv);
   allow_lds(project_kernel<DT, false>, prj_smem);
   allow_lds(project_kernel<DT, true>, prj_smem);
-  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
-                     prj_smem, st, k, g, Nv, out.FK, p.rK, p.rms_eps, phiK, gstat, pchunks);
+  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), dim3(512),
+                     prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1);
   SPR_CHECK_LAUNCH();
   // K/V k-means
   KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
-  ka.BH = BH; ka.n = Nv; ka.r = p.rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
+  ka.BH = BHkv; ka.n = Nv; ka.r = p.rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
   ka.max_iters = p.max_iters; ka.tol = p.tol;
   ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
   if (warm) {
-    hipLaunchKernelGGL(warm_centres_kernel<false>, dim3(ceil_div(p.Ck, 64), BH), dim3(256), 0, st, warm->kbar,
-                       warm->n_kv, p.Ck, d, out.FK, p.rK, p.rms_eps, phiK, Nv, p.seed, 0, ka.cent);
+    hipLaunchKernelGGL(warm_centres_kernel<false>, dim3(ceil_div(p.Ck, 64), BHkv), dim3(256), 0, st, warm->kbar,
+                       warm->n_kv, p.Ck, d, out.FK, p.rK, p.rms_eps, phiK, Nv, p.seed, 0, 1, ka.cent);
     SPR_CHECK_LAUNCH();
     ka.cent_given = true;
   }
   spr_status s = run_kmeans(ka, st);
   if (s != SPR_OK) return s;
-  if (out.passes) launch_copy_passes(ka.ctrl, BH, out.passes, 2, 0, st);
+  if (out.passes) launch_copy_passes(ka.ctrl, BHkv, out.passes, 2, 0, st);
   if (out.cK_last) {
     // centres are stored with stride rK, exactly the caller's layout
-    const size_t nel = size_t(BH) * p.Ck * p.rK;
+    const size_t nel = size_t(BHkv) * p.Ck * p.rK;
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, ka.cent,
                        out.cK_last, nel);
   }
-  s = launch_compact(ka.labels, BH, Nv, p.Ck, out.kv_label, out.kv_perm, nullptr, out.kv_off, out.n_kv, gstat,
+  s = launch_compact(ka.labels, BHkv, Nv, p.Ck, out.kv_label, out.kv_perm, nullptr, out.kv_off, out.n_kv, kvstat,
                      SPR_HS_KV_GROUPS_EMPTY, st);
   if (s != SPR_OK) return s;
   // group-major K and V, key / value centroids
   const int pieces = d * ElemSize<DT>::value / 16;
   const dim3 ggrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BH);
-  hipLaunchKernelGGL(gather_rows_kernel<DT>, ggrid, dim3(256), 0, st, k, g, out.kv_perm, out.Kp);
-  hipLaunchKernelGGL(gather_rows_kernel<DT>, ggrid, dim3(256), 0, st, v, g, out.kv_perm, out.Vp);
+  const dim3 kgrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BHkv);
+  hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, k, gk, out.kv_perm, out.Kp);
+  hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp);
   SPR_CHECK_LAUNCH();
   if constexpr (DT == SPR_BF16) {
-    const size_t nel = size_t(BH) * desc.N * d;
+    const size_t nel = size_t(BHkv) * desc.N * d;
     hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(unsigned(ceil_div64(int64_t(nel / 8), 256))), dim3(256), 0, st,
                        static_cast<const uint16_t*>(out.Vp), wsp<_Float16>(ws, L.vh), nel);
     SPR_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BH), dim3(256), 0, st, out.Kp, desc.N, d,
+  hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Kp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.kbar);
-  hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BH), dim3(256), 0, st, out.Vp, desc.N, d,
+  hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Vp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.vbar);
   SPR_CHECK_LAUNCH();
   // M_Q and F_Q
   double* kt = wsp<double>(ws, L.ktilde);
-  hipLaunchKernelGGL(ktilde_kernel, dim3(BH), dim3(1024), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
-  hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
+  hipLaunchKernelGGL(ktilde_kernel, dim3(BHkv), dim3(1024), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
+  hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
                      metric);
   if (warm)
-    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BH), dim3(256), sub_smem, st, metric, warm->FQ, d, p.rQ,
-                       p.eig_clamp, out.FQ, gstat, 3);
-  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BH), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
-                     gstat, warm ? 3 : -1);
+    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BHkv), dim3(256), sub_smem, st, metric, warm->FQ, d, p.rQ,
+                       p.eig_clamp, out.FQ, kvstat, 3);
+  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
+                     kvstat, warm ? 3 : -1);
   SPR_CHECK_LAUNCH();
   // phi_Q = RMSNorm(Q F_Q)
   hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
-                     prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks);
+                     prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G);
   SPR_CHECK_LAUNCH();
   // query k-means
   KmArgs qa = ka;
-  qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1;
+  qa.BH = BH; qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1; qa.cent_given = warm != nullptr;
   if (warm) {
     hipLaunchKernelGGL(warm_centres_kernel<true>, dim3(ceil_div(p.Cq, 64), BH), dim3(256), 0, st, warm->qbar,
-                       warm->n_q, p.Cq, d, out.FQ, p.rQ, p.rms_eps, phiQ, Nv, p.seed, 1, qa.cent);
+                       warm->n_q, p.Cq, d, out.FQ, p.rQ, p.rms_eps, phiQ, Nv, p.seed, 1, G, qa.cent);
     SPR_CHECK_LAUNCH();
   }
   s = run_kmeans(qa, st);
@@ -1020,6 +1039,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
                      out.q_perm, out.q_off, out.n_q, p.Cq, cbar);
   hipLaunchKernelGGL(qdist_kernel, dim3(ceil_div(Nv, 16), BH), dim3(256), 0, st, phiQ, Nv, p.rQ, out.q_label, cbar,
                      p.Cq, out.qdist);
+  hipLaunchKernelGGL(merge_kv_status_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, gstat, kvstat, BH, G);
   SPR_CHECK_LAUNCH();
   return SPR_OK;
 }

@@ -57,10 +57,10 @@ template <int D>
 __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __restrict__ qbar,
                                                               const double* __restrict__ kbar,
                                                               const int* __restrict__ n_q,
-                                                              const int* __restrict__ n_kv, int Cq, int Ck,
+                                                              const int* __restrict__ n_kv, int Cq, int Ck, int G,
                                                               double* __restrict__ lbar, double* __restrict__ shift) {
-  const int hd = blockIdx.y, a0 = blockIdx.x * 64;
-  const int nq = n_q[hd], nkv = n_kv[hd];
+  const int hd = blockIdx.y, hk = hd / G, a0 = blockIdx.x * 64;  // query head, its K/V head
+  const int nq = n_q[hd], nkv = n_kv[hk];
   if (a0 >= nq) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   double qa[D / 4];
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __re
   double mx[4] = {-1.0e308, -1.0e308, -1.0e308, -1.0e308};
   for (int b0 = 0; b0 < nkv; b0 += 16) {
     const int b = b0 + r16;
-    const double* kb = kbar + (size_t(hd) * Ck + min(b, nkv - 1)) * D + gq;
+    const double* kb = kbar + (size_t(hk) * Ck + min(b, nkv - 1)) * D + gq;
     f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks * 4], lg, 0, 0, 0);
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
                                                           const double* __restrict__ vbar,
                                                           const int* __restrict__ kv_off,
                                                           const int* __restrict__ n_q,
-                                                          const int* __restrict__ n_kv, int Cq, int Ck,
+                                                          const int* __restrict__ n_kv, int Cq, int Ck, int G,
                                                           const double* __restrict__ shift,
                                                           const double* __restrict__ vstat,
                                                           double* __restrict__ scores) {
@@ -153,12 +153,12 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
   double* wsv = us + PIECE;           // [PIECE]
   double* T = wsv + PIECE;            // [64] 2^(j/64)
   double* vns = T + 64;               // [16]
-  const int hd = blockIdx.z;
+  const int hd = blockIdx.z, hk = hd / G;  // query head, its K/V head
   const int a0 = blockIdx.x * 64, b0 = blockIdx.y * 16;
-  const int nq = n_q[hd], nkv = n_kv[hd];
+  const int nq = n_q[hd], nkv = n_kv[hk];
   if (a0 >= nq || b0 >= nkv) return;
   const int b1 = min(b0 + 16, nkv);
-  const int* off = kv_off + size_t(hd) * (Ck + 1);
+  const int* off = kv_off + size_t(hk) * (Ck + 1);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   if (threadIdx.x < 64) T[threadIdx.x] = exp2(double(threadIdx.x) / 64.0);
   double qa[D / 4];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
     double x = 0.0;
     if (b < b1)
       for (int c = lane; c < D; c += 64) {
-        const double y = vbar[(size_t(hd) * Ck + b) * D + c];
+        const double y = vbar[(size_t(hk) * Ck + b) * D + c];
         x = fma(y, y, x);
       }
     x = wave_sum_d(x);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
         const int jl = e / (D / 8), c8 = (e % (D / 8)) * 8;
         float x[8];
         if (jl < n) {
-          load8<DT>(Kp, (int64_t(hd) * N + p0 + jl) * D + c8, x);
+          load8<DT>(Kp, (int64_t(hk) * N + p0 + jl) * D + c8, x);
         } else {
 #pragma unroll
           for (int t = 0; t < 8; ++t) x[t] = 0.f;
@@ -209,8 +209,8 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
       }
       if (threadIdx.x < PIECE) {
         const int jl = threadIdx.x;
-        us[jl] = jl < n ? vstat[(size_t(hd) * Nv + p0 + jl) * 2 + 0] : 0.0;
-        wsv[jl] = jl < n ? vstat[(size_t(hd) * Nv + p0 + jl) * 2 + 1] : 0.0;
+        us[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 2 + 0] : 0.0;
+        wsv[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 2 + 1] : 0.0;
       }
       __syncthreads();
       for (int t = 0; t * 16 < n; ++t) {
@@ -262,16 +262,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
                                                            const int* __restrict__ kv_off,
                                                            const int* __restrict__ q_off,
                                                            const int* __restrict__ n_q, const int* __restrict__ n_kv,
-                                                           int Cq, int Ck, int n_text, int64_t Tk,
+                                                           int Cq, int Ck, int G, int n_text, int64_t Tk,
                                                            int* __restrict__ sel_cnt, int* __restrict__ sel_kv,
                                                            int64_t* __restrict__ pairs, int* __restrict__ gstat) {
   __shared__ double ks[1024];
   __shared__ int ids[1024];
   __shared__ int buf[1024];
   __shared__ int Ls;
-  const int hd = blockIdx.y, a = blockIdx.x;
-  const int nq = n_q[hd], nkv = n_kv[hd];
-  const int* off = kv_off + size_t(hd) * (Ck + 1);
+  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x;  // query head, its K/V head
+  const int nq = n_q[hd], nkv = n_kv[hk];
+  const int* off = kv_off + size_t(hk) * (Ck + 1);
   int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
   if (a > nq || (a == nq && n_text == 0)) return;
   if (a == nq) {  // text query rows: every group
@@ -510,34 +510,35 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
                              int64_t Tk, const spr_probe_options& probes, spr_route& out, void* ws,
                              const Workspace& L, hipStream_t st) {
   const int BH = desc.B * desc.H, d = desc.d, N = desc.N, Nv = N - desc.n_text;
+  const int G = kv_group_size(desc), BHkv = BH / G;
   double* vstat = ws_ptr<double>(ws, L.vstat);
   double* shift = ws_ptr<double>(ws, L.shift);
   double* scores = out.scores ? out.scores : ws_ptr<double>(ws, L.scores);
   int* gstat = ws_ptr<int>(ws, L.gstat);
   int* pstat = ws_ptr<int>(ws, L.pstat);
-  hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256 / (d / 8)), BH), dim3(256), 0, st, part.Vp, N, Nv, d,
+  hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256 / (d / 8)), BHkv), dim3(256), 0, st, part.Vp, N, Nv, d,
                      part.kv_perm, part.kv_label, part.vbar, p.Ck, vstat);
   double* lbar = ws_ptr<double>(ws, L.lbar);
   const dim3 lgrid(ceil_div(p.Cq, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
   if (d == 128) {
     hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, lbar, shift);
+                       part.n_kv, p.Cq, p.Ck, G, lbar, shift);
     allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
     hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), route_score_smem<128>(), st, part.Kp, N, Nv,
                        part.qbar, lbar,
-                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
+                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat, scores);
   } else {
     hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, lbar, shift);
+                       part.n_kv, p.Cq, p.Ck, G, lbar, shift);
     allow_lds(route_score_kernel<DT, 64>, route_score_smem<64>());
     hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), route_score_smem<64>(), st, part.Kp, N, Nv,
                        part.qbar, lbar,
-                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, shift, vstat, scores);
+                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat, scores);
   }
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(zero_i64_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, out.pairs, BH);
   hipLaunchKernelGGL(route_select_kernel, dim3(p.Cq + 1, BH), dim3(256), 0, st, scores, part.kv_off, part.q_off,
-                     part.n_q, part.n_kv, p.Cq, p.Ck, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
+                     part.n_q, part.n_kv, p.Cq, p.Ck, G, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_finalize_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, N, Nv,
                      desc.n_text, M, out.pairs, out.rho_exec, pstat);

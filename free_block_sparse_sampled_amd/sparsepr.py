@@ -28,7 +28,9 @@ P = ctypes.c_void_p
 class spr_desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("n_text", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64)]
+                ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("sn", ctypes.c_int64),
+                ("Hkv", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ksb", ctypes.c_int64), ("ksh", ctypes.c_int64), ("ksn", ctypes.c_int64)]
 
 
 class spr_part_params(ctypes.Structure):
@@ -175,15 +177,29 @@ class OperatorConfig:
                                self.eig_clamp, self.seed)
 
 
-def make_desc(q: torch.Tensor, n_text: int = 0) -> spr_desc:
-    """Descriptor of a [B, H, N, d] tensor (any strides with a contiguous last dim)."""
+def make_desc(q: torch.Tensor, n_text: int = 0, k: Optional[torch.Tensor] = None) -> spr_desc:
+    """Descriptor of a [B, H, N, d] tensor (any strides with a contiguous last dim).
+
+    With ``k`` of shape [B, Hkv, N, d], Hkv < H dividing H, the descriptor is that of grouped-query
+    attention: k and v (same strides as k) hold Hkv heads, each shared by H / Hkv query heads."""
     if q.dim() != 4 or q.stride(3) != 1:
         raise SparsePRError("q, k, v must be [B, H, N, d] with a contiguous last dimension")
     dt = {torch.bfloat16: SPR_BF16, torch.float32: SPR_F32}.get(q.dtype)
     if dt is None:
         raise SparsePRError(f"unsupported dtype {q.dtype}")
     B, H, N, d = q.shape
-    return spr_desc(B, H, N, d, n_text, dt, q.stride(0), q.stride(1), q.stride(2))
+    desc = spr_desc(B, H, N, d, n_text, dt, q.stride(0), q.stride(1), q.stride(2))
+    if k is not None and k.shape[1] != H:
+        if k.dim() != 4 or k.stride(3) != 1 or (k.shape[0], k.shape[2], k.shape[3]) != (B, N, d):
+            raise SparsePRError("k, v must be [B, Hkv, N, d] with a contiguous last dimension")
+        desc.Hkv = k.shape[1]
+        desc.ksb, desc.ksh, desc.ksn = k.stride(0), k.stride(1), k.stride(2)
+    return desc
+
+
+def kv_heads(desc: spr_desc) -> int:
+    """K/V heads per batch entry of a descriptor."""
+    return desc.Hkv if 0 < desc.Hkv < desc.H else desc.H
 
 
 class Partition:
@@ -191,33 +207,34 @@ class Partition:
 
     def __init__(self, desc: spr_desc, cfg: OperatorConfig, device, diagnostics: bool = False):
         BH, N, d = desc.B * desc.H, desc.N, desc.d
+        BHkv = desc.B * kv_heads(desc)  # K/V-side arrays are per K/V head
         Nv = N - desc.n_text
         i32, f64 = torch.int32, torch.float64
         dt = torch.bfloat16 if desc.dtype == SPR_BF16 else torch.float32
         z = lambda shape, t: torch.empty(shape, dtype=t, device=device)  # noqa: E731
-        self.kv_label = z((BH, Nv), i32)
+        self.kv_label = z((BHkv, Nv), i32)
         self.q_label = z((BH, Nv), i32)
-        self.kv_perm = z((BH, Nv), i32)
+        self.kv_perm = z((BHkv, Nv), i32)
         self.q_perm = z((BH, Nv), i32)
         self.q_pos = z((BH, Nv), i32)
-        self.kv_off = z((BH, cfg.Ck + 1), i32)
+        self.kv_off = z((BHkv, cfg.Ck + 1), i32)
         self.q_off = z((BH, cfg.Cq + 1), i32)
-        self.n_kv = z((BH,), i32)
+        self.n_kv = z((BHkv,), i32)
         self.n_q = z((BH,), i32)
-        self.kbar = z((BH, cfg.Ck, d), f64)
-        self.vbar = z((BH, cfg.Ck, d), f64)
+        self.kbar = z((BHkv, cfg.Ck, d), f64)
+        self.vbar = z((BHkv, cfg.Ck, d), f64)
         self.qbar = z((BH, cfg.Cq, d), f64)
         self.qdist = z((BH, Nv), f64)
-        self.FK = z((BH, d, cfg.rK), f64)
-        self.FQ = z((BH, d, cfg.rQ), f64)
+        self.FK = z((BHkv, d, cfg.rK), f64)
+        self.FQ = z((BHkv, d, cfg.rQ), f64)
         self.Qp = z((BH, N, d), dt)
-        self.Kp = z((BH, N, d), dt)
-        self.Vp = z((BH, N, d), dt)
+        self.Kp = z((BHkv, N, d), dt)
+        self.Vp = z((BHkv, N, d), dt)
         self.phiK = self.phiQ = self.cK_last = self.cQ_last = self.passes = None
         if diagnostics:
-            self.phiK = z((BH, Nv, cfg.rK), f64)
+            self.phiK = z((BHkv, Nv, cfg.rK), f64)
             self.phiQ = z((BH, Nv, cfg.rQ), f64)
-            self.cK_last = z((BH, cfg.Ck, cfg.rK), f64)
+            self.cK_last = z((BHkv, cfg.Ck, cfg.rK), f64)
             self.cQ_last = z((BH, cfg.Cq, cfg.rQ), f64)
             self.passes = z((BH, 2), i32)
         self.struct = spr_partition(*[_ptr(getattr(self, n)) for n in _PART_FIELDS])
@@ -324,12 +341,14 @@ def sparsepr_kmeans(feat: torch.Tensor, C: int, seed: int, stage: int, max_iters
 class SparsePR:
     """The five calls of one operator invocation with buffers allocated once.
 
-    ``run(q, k, v)`` returns the corrected output [B, H, N, d] (fp32 by default)."""
+    ``run(q, k, v)`` returns the corrected output [B, H, N, d] (fp32 by default).  Passing ``k``
+    (or any tensor of its shape and strides) with fewer heads than q selects grouped-query
+    attention; later calls must then pass k and v of that shape."""
 
     def __init__(self, q: torch.Tensor, cfg: OperatorConfig, n_text: int = 0, out_dtype=torch.float32,
-                 diagnostics: bool = False, keep_scores: bool = False):
+                 diagnostics: bool = False, keep_scores: bool = False, k: Optional[torch.Tensor] = None):
         self.cfg = cfg
-        self.desc = make_desc(q, n_text)
+        self.desc = make_desc(q, n_text, k)
         dev = q.device
         B, H, N, d = q.shape
         self.ws = torch.empty(sparsepr_workspace_size(self.desc, cfg), dtype=torch.uint8, device=dev)

@@ -77,12 +77,21 @@ enum {
   SPR_HS_EIGEN_NOCONV = 32      /* a metric eigendecomposition did not converge in 60 QL iterations */
 };
 
-/* Shape of q, k, v: element (b, h, n, c) lives at b*sb + h*sh + n*sn + c. */
+/* Shape of q, k, v: element (b, h, n, c) of q lives at b*sb + h*sh + n*sn + c.
+   Grouped-query attention: with 0 < Hkv < H (H % Hkv == 0, G = H / Hkv) k and v hold Hkv heads,
+   element (b, j, n, c) at b*ksb + j*ksh + n*ksn + c, and query head h attends with K/V head
+   h / G; the key metric and the K/V partition are shared by the G query heads of a K/V head,
+   the query partition and the routing are per query head (Sec. 4.3, routing and GQA; App. C.2,
+   which samples up to G * Ms rows of the G heads for the shared metric).  Hkv = 0 or
+   Hkv = H: one K/V head per query head, k and v with the strides of q (ksb .. ksn unused). */
 typedef struct {
   int32_t B, H, N, d; /* d in {64, 128}; N includes the n_text trailing text tokens */
   int32_t n_text;     /* 0 <= n_text < N */
   int32_t dtype;      /* spr_dtype of q, k, v */
   int64_t sb, sh, sn; /* element strides; the innermost stride is 1 */
+  int32_t Hkv;        /* K/V heads (see above) */
+  int32_t reserved;   /* 0 */
+  int64_t ksb, ksh, ksn; /* element strides of k and v when 0 < Hkv < H */
 } spr_desc;
 
 /* Partition hyperparameters (defaults of Table C.1, App. C.2, in brackets). */
@@ -97,44 +106,47 @@ typedef struct {
   uint64_t seed;     /* k-means initialisation seed (SplitMix64) */
 } spr_part_params;
 
-/* Outputs of sparsepr_partition (caller-owned device buffers). */
+/* Outputs of sparsepr_partition (caller-owned device buffers).  Arrays of the K/V side are per
+   K/V head, BHkv = B * Hkv (BHkv = BH without grouped-query attention); K/V head j serves the
+   query heads j G .. j G + G - 1 of the flattened index. */
 typedef struct {
-  int32_t* kv_label; /* [BH][Nv]  K/V group of each video key, original order, groups renumbered
+  int32_t* kv_label; /* [BHkv][Nv] K/V group of each video key, original order, groups renumbered
                                   0..n_kv-1 in ascending cluster id (empty clusters dropped) */
   int32_t* q_label;  /* [BH][Nv]  query group of each video query row, likewise */
-  int32_t* kv_perm;  /* [BH][Nv]  group-major position -> original key row (stable) */
+  int32_t* kv_perm;  /* [BHkv][Nv] group-major position -> original key row (stable) */
   int32_t* q_perm;   /* [BH][Nv]  group-major position -> original query row (stable) */
   int32_t* q_pos;    /* [BH][Nv]  original query row -> group-major position */
-  int32_t* kv_off;   /* [BH][Ck+1] start of each K/V group in kv_perm order; kv_off[n_kv] = Nv */
+  int32_t* kv_off;   /* [BHkv][Ck+1] start of each K/V group in kv_perm order; kv_off[n_kv] = Nv */
   int32_t* q_off;    /* [BH][Cq+1] start of each query group; q_off[n_q] = Nv */
-  int32_t* n_kv;     /* [BH] nonempty K/V groups */
+  int32_t* n_kv;     /* [BHkv] nonempty K/V groups */
   int32_t* n_q;      /* [BH] nonempty query groups */
-  double* kbar;      /* [BH][Ck][d] key centroids of the K/V groups (original space) */
-  double* vbar;      /* [BH][Ck][d] value centroids */
+  double* kbar;      /* [BHkv][Ck][d] key centroids of the K/V groups (original space) */
+  double* vbar;      /* [BHkv][Ck][d] value centroids */
   double* qbar;      /* [BH][Cq][d] mean query of each query group */
   double* qdist;     /* [BH][Nv]  |phi_Q(q_i) - c_a| (App. A.2), original order */
-  double* FK;        /* [BH][d][rK] key response factor, F F^T = rank-rK truncation of M_K */
-  double* FQ;        /* [BH][d][rQ] query response factor */
+  double* FK;        /* [BHkv][d][rK] key response factor, F F^T = rank-rK truncation of M_K */
+  double* FQ;        /* [BHkv][d][rQ] query response factor (M_Q depends on the K/V side only) */
   void* Qp;          /* [BH][N][d] q rows in group-major order, then the text rows; input dtype */
-  void* Kp;          /* [BH][N][d] k rows likewise (kv_perm order) */
-  void* Vp;          /* [BH][N][d] v rows likewise (kv_perm order) */
+  void* Kp;          /* [BHkv][N][d] k rows likewise (kv_perm order) */
+  void* Vp;          /* [BHkv][N][d] v rows likewise (kv_perm order) */
   /* optional diagnostics, each may be NULL */
-  double* phiK;      /* [BH][Nv][rK] key coordinates k F_K */
+  double* phiK;      /* [BHkv][Nv][rK] key coordinates k F_K */
   double* phiQ;      /* [BH][Nv][rQ] query coordinates RMSNorm(q F_Q) */
-  double* cK_last;   /* [BH][Ck][rK] k-means centres used by the final K/V assignment pass */
+  double* cK_last;   /* [BHkv][Ck][rK] k-means centres used by the final K/V assignment pass */
   double* cQ_last;   /* [BH][Cq][rQ] k-means centres used by the final query assignment pass */
-  int32_t* passes;   /* [BH][2] assignment passes run by the K/V and the query k-means */
+  int32_t* passes;   /* [BH][2] assignment passes: [j][0] of the K/V k-means of K/V head j < BHkv,
+                                  [hd][1] of the query k-means of query head hd */
 } spr_partition;
 
 /* State of the previous call of the same heads, for the later-call path of App. C.1
    (device buffers laid out as the corresponding spr_partition outputs; they may be the
    very buffers this call writes: every one is read before it is overwritten). */
 typedef struct {
-  const double* FK;    /* [BH][d][rK] previous key response factor */
-  const double* FQ;    /* [BH][d][rQ] previous query response factor */
-  const double* kbar;  /* [BH][Ck][d] previous key centroids (original space) */
+  const double* FK;    /* [BHkv][d][rK] previous key response factor */
+  const double* FQ;    /* [BHkv][d][rQ] previous query response factor */
+  const double* kbar;  /* [BHkv][Ck][d] previous key centroids (original space) */
   const double* qbar;  /* [BH][Cq][d] previous mean queries (original space) */
-  const int32_t* n_kv; /* [BH] previous nonempty K/V groups */
+  const int32_t* n_kv; /* [BHkv] previous nonempty K/V groups */
   const int32_t* n_q;  /* [BH] previous nonempty query groups */
 } spr_warm;
 

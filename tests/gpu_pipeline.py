@@ -25,7 +25,7 @@ def device_inputs(cfg: WorkloadConfig, heads=None, step: int = 0):
 
 
 def run_operator(cfg: WorkloadConfig, opc: spr.OperatorConfig, tq, tk, tv):
-    op = spr.SparsePR(tq, opc, n_text=cfg.n_text, diagnostics=True, keep_scores=True)
+    op = spr.SparsePR(tq, opc, n_text=cfg.n_text, diagnostics=True, keep_scores=True, k=tk)
     op.run(tq, tk, tv)
     torch.cuda.synchronize()
     return op

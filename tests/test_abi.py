@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import free_block_sparse_sampled_amd as spr
 from free_block_sparse_sampled_amd import sparsepr as B
@@ -119,3 +120,28 @@ def test_entry_points_reject_invalid_arguments_on_the_host(lib):
     ws_need = lib.sparsepr_workspace_size(ctypes.byref(d), ctypes.byref(p), 1)
     assert lib.sparsepr_attn_sparse(ctypes.byref(d), ctypes.byref(p), ctypes.byref(part), ctypes.byref(route), dummy,
                                     dummy, ws_need - 1, None) == 3
+
+
+def test_grouped_query_descriptors_are_validated(lib):
+    p = _params()
+    N, d = 4096, 128
+
+    def gqa(H=4, Hkv=2, ksn=d, reserved=0):
+        dd = _desc(N=N, d=d, H=H)
+        dd.Hkv, dd.reserved = Hkv, reserved
+        dd.ksb, dd.ksh, dd.ksn = Hkv * N * d, N * d, ksn
+        return dd
+
+    ok = lib.sparsepr_workspace_size(ctypes.byref(gqa()), ctypes.byref(p), 64)
+    assert ok > 0
+    # Hkv = H is plain multi-head attention (k strides unused); Hkv = 0 likewise
+    assert lib.sparsepr_workspace_size(ctypes.byref(gqa(Hkv=4, ksn=0)), ctypes.byref(p), 64) > 0
+    assert lib.sparsepr_workspace_size(ctypes.byref(gqa(Hkv=0, ksn=0)), ctypes.byref(p), 64) > 0
+    for bad in [gqa(Hkv=3), gqa(Hkv=5), gqa(Hkv=-1), gqa(reserved=1), gqa(ksn=d - 1), gqa(ksn=d + 1)]:
+        assert lib.sparsepr_workspace_size(ctypes.byref(bad), ctypes.byref(p), 64) == 0
+    # the binding builds the descriptor from tensors of H and Hkv heads
+    q = torch.empty((1, 4, N, d), dtype=torch.bfloat16)
+    k = torch.empty((1, 2, N, d), dtype=torch.bfloat16)
+    dd = B.make_desc(q, 0, k)
+    assert (dd.Hkv, dd.ksb, dd.ksh, dd.ksn) == (2, 2 * N * d, N * d, d) and B.kv_heads(dd) == 2
+    assert B.make_desc(q, 0, q).Hkv == 0

@@ -70,24 +70,25 @@ def test_kmeans_matches_oracle(r, C, n):
 
 
 # ------------------------------------------------------------------ whole operator
-def _compare_head(g, ref, hd, Nv, N, n_text, discrete_exact=True):
-    """Compare GPU outputs of head hd against an oracle run of that head."""
+def _compare_head(g, ref, hd, Nv, N, n_text, discrete_exact=True, kh=None):
+    """Compare GPU outputs of query head hd (K/V head kh, default hd) against an oracle run."""
+    kh = hd if kh is None else kh
     d = g["FK"].shape[1]
     # factors: F F^T is unique (eigenvector signs / rotations are not)
-    for F, Fo in ((g["FK"][hd], ref["FK"]), (g["FQ"][hd], ref["FQ"])):
+    for F, Fo in ((g["FK"][kh], ref["FK"]), (g["FQ"][kh], ref["FQ"])):
         A, Ao = F @ F.T, Fo @ Fo.T
         assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
-    nkv, nq = int(g["n_kv"][hd]), int(g["n_q"][hd])
+    nkv, nq = int(g["n_kv"][kh]), int(g["n_q"][hd])
     if discrete_exact:
         assert nkv == ref["n_kv"] and nq == ref["n_q"]
-        assert np.array_equal(g["kv_label"][hd], ref["kv_label"])
+        assert np.array_equal(g["kv_label"][kh], ref["kv_label"])
         assert np.array_equal(g["q_label"][hd], ref["q_label"])
         perm_k, off_k = O.group_perm(ref["kv_label"], nkv)
         perm_q, off_q = O.group_perm(ref["q_label"], nq)
-        assert np.array_equal(g["kv_perm"][hd], perm_k) and np.array_equal(g["kv_off"][hd][: nkv + 1], off_k)
+        assert np.array_equal(g["kv_perm"][kh], perm_k) and np.array_equal(g["kv_off"][kh][: nkv + 1], off_k)
         assert np.array_equal(g["q_perm"][hd], perm_q) and np.array_equal(g["q_off"][hd][: nq + 1], off_q)
-        np.testing.assert_allclose(g["kbar"][hd][:nkv], ref["kbar"], rtol=0, atol=1e-12)
-        np.testing.assert_allclose(g["vbar"][hd][:nkv], ref["vbar"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(g["kbar"][kh][:nkv], ref["kbar"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(g["vbar"][kh][:nkv], ref["vbar"], rtol=0, atol=1e-12)
         np.testing.assert_allclose(g["qbar"][hd][:nq], ref["qbar"], rtol=0, atol=1e-12)
         np.testing.assert_allclose(g["qdist"][hd], ref["qdist"], rtol=1e-8, atol=1e-10)
         for a in range(nq):
@@ -117,9 +118,28 @@ def _compare_head(g, ref, hd, Nv, N, n_text, discrete_exact=True):
     assert np.linalg.norm(Bg - fit["B"]) <= 1e-6 * max(np.linalg.norm(fit["B"]), 1e-12)
     np.testing.assert_allclose(fs[:d], fit["muX"], rtol=0, atol=1e-9)
     np.testing.assert_allclose(fs[2 * d:3 * d], fit["muR"], rtol=0, atol=1e-9)
-    # final output against the oracle's end-to-end output
-    err = row_rel_err(g["out"][hd][rows], ref["O_hat"])
-    assert err.max() < ROW_TOL, ("out", err.max())
+    # final output: the oracle's correction of the GPU's sparse rows with that fit (probe rows
+    # exact, text rows uncorrected) checks the fit and apply arithmetic on identical inputs
+    want = osp[rows].copy()
+    video = rows < Nv
+    want[video] = O.correct(osp[rows][video], fit)
+    pidx = {int(r): i for i, r in enumerate(g["probe_idx"][hd])}
+    for ir, r in enumerate(rows):
+        if int(r) in pidx:
+            want[ir] = g["o_probe"][hd][pidx[int(r)]]
+    err = row_rel_err(g["out"][hd][rows], want)
+    assert err.max() < ROW_TOL, ("out (lockstep fit)", err.max())
+    # end to end against the oracle's own output.  The difference splits into the lockstep
+    # error above and the oracle's own response to the GPU's sub-2e-3 sparse and probe rows,
+    # `own`, which an ill-conditioned ridge (probe count near d on diffuse attention) can
+    # amplify; where the fit does not amplify (own < ROW_TOL / 2 everywhere) the bar is ROW_TOL
+    e2e = row_rel_err(g["out"][hd][rows], ref["O_hat"])
+    own = row_rel_err(want, ref["O_hat"])
+    if own.max() < ROW_TOL / 2:
+        assert e2e.max() < ROW_TOL, ("out", e2e.max())
+    else:
+        assert np.all(e2e <= own + ROW_TOL), ("out", e2e.max(), own.max())
+        assert np.median(e2e) < ROW_TOL, ("out median", np.median(e2e))
 
 
 def _oracle_is_tie_free(ref):
@@ -240,27 +260,29 @@ def _lockstep_head(g, q, k, v, cfg, opc, b, h, rng, nrows=96, ngroups=6):
     applied to the GPU's own inputs of that stage."""
     N, Nv, d = cfg.N, cfg.Nv, cfg.d
     T = O.key_budget(opc.rho, N, Nv, opc.M, cfg.n_text)
-    hd = b * cfg.H + h
-    qh, kh, vh = (x[b, h].astype(np.float64) for x in (q, k, v))
-    nkv, nq = int(g["n_kv"][hd]), int(g["n_q"][hd])
+    G = cfg.H // cfg.Hkv if cfg.Hkv else 1             # query heads per K/V head
+    hd, hk = b * cfg.H + h, b * (cfg.H // G) + h // G  # query head, its K/V head (flattened)
+    qh = q[b, h].astype(np.float64)
+    kh, vh = k[b, h // G].astype(np.float64), v[b, h // G].astype(np.float64)
+    nkv, nq = int(g["n_kv"][hk]), int(g["n_q"][hd])
     # K/V and query partitions: final assignment pass and compaction
-    for feat, cent, lab_g, C in ((g["phiK"][hd], g["cK_last"][hd], g["kv_label"][hd], opc.Ck),
+    for feat, cent, lab_g, C in ((g["phiK"][hk], g["cK_last"][hk], g["kv_label"][hk], opc.Ck),
                                  (g["phiQ"][hd], g["cQ_last"][hd], g["q_label"][hd], opc.Cq)):
         lab, _, margin = O.kmeans_assign(feat, cent)
         lab_c, n = O.compact_labels(lab, C)
         ok = margin > TIE
         assert ok.mean() > 0.99
         assert np.array_equal(lab_g[ok], lab_c[ok])
-    perm, off = O.group_perm(g["kv_label"][hd], nkv)
-    assert np.array_equal(g["kv_perm"][hd], perm) and np.array_equal(g["kv_off"][hd][: nkv + 1], off)
+    perm, off = O.group_perm(g["kv_label"][hk], nkv)
+    assert np.array_equal(g["kv_perm"][hk], perm) and np.array_equal(g["kv_off"][hk][: nkv + 1], off)
     perm, off = O.group_perm(g["q_label"][hd], nq)
     assert np.array_equal(g["q_perm"][hd], perm) and np.array_equal(g["q_off"][hd][: nq + 1], off)
-    size, kbar, vbar = O.key_group_stats(kh[:Nv], vh[:Nv], g["kv_label"][hd], nkv)
-    np.testing.assert_allclose(g["kbar"][hd][:nkv], kbar, rtol=0, atol=1e-12)
+    size, kbar, vbar = O.key_group_stats(kh[:Nv], vh[:Nv], g["kv_label"][hk], nkv)
+    np.testing.assert_allclose(g["kbar"][hk][:nkv], kbar, rtol=0, atol=1e-12)
     # routing of sampled query groups from the GPU's centroids
     groups = rng.choice(nq, size=min(ngroups, nq), replace=False)
-    sc, _ = O.route_scores(g["qbar"][hd][:nq], kh[:Nv], vh[:Nv], g["kv_label"][hd], g["kbar"][hd][:nkv],
-                           g["vbar"][hd][:nkv], groups=groups)
+    sc, _ = O.route_scores(g["qbar"][hd][:nq], kh[:Nv], vh[:Nv], g["kv_label"][hk], g["kbar"][hk][:nkv],
+                           g["vbar"][hk][:nkv], groups=groups)
     for ia, a in enumerate(groups):
         sel, info = O.route_select(sc[ia], size, T)
         cnt = int(g["sel_cnt"][hd][a])
@@ -279,7 +301,7 @@ def _lockstep_head(g, q, k, v, cfg, opc, b, h, rng, nrows=96, ngroups=6):
     qlab = np.concatenate([g["q_label"][hd], np.full(cfg.n_text, -1)])
     rows = np.unique(np.concatenate([rng.choice(N, nrows, replace=False), [0, Nv - 1, N - 1]]))
     qpos = g["q_pos"][hd]
-    osp = O.sparse_attention_rows(qh, kh, vh, rows, qlab, g["kv_label"][hd], sel_all, cfg.n_text)
+    osp = O.sparse_attention_rows(qh, kh, vh, rows, qlab, g["kv_label"][hk], sel_all, cfg.n_text)
     pos = np.where(rows < Nv, qpos[np.minimum(rows, Nv - 1)], rows)
     err = row_rel_err(g["o_sp"][hd][pos], osp)
     assert err.max() < ROW_TOL, ("o_sp", err.max())
@@ -317,6 +339,40 @@ def test_full_size_mid_sampled():
 
 def test_full_size_joint_text_sampled():
     _full_size_lockstep("joint", [(0, 0), (1, 23)])
+
+
+# ------------------------------------------------------------------ grouped-query attention
+@pytest.mark.parametrize("name", ["tiny_gqa", "small_gqa"])
+def test_gqa_end_to_end(name):
+    """Grouped-query attention (Sec. 4.3, routing and GQA; App. C.2): one key metric and K/V
+    partition per K/V head from the rows of its G query heads, the query side per query head.
+    Every query head is compared with the oracle's group run of its K/V head."""
+    cfg = config(name)
+    G = cfg.H // cfg.Hkv
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    assert tk.shape[1] == cfg.Hkv
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    assert g["kv_label"].shape[0] == cfg.B * cfg.Hkv and g["q_label"].shape[0] == cfg.B * cfg.H
+    p = _oracle_params(opc, cfg.n_text)
+    for b in range(cfg.B):
+        for j in range(cfg.Hkv):
+            kh = b * cfg.Hkv + j
+            heads = [b * cfg.H + j * G + i for i in range(G)]
+            refs = O.sparsepr_group([q[b, j * G + i] for i in range(G)], k[b, j], v[b, j], p, kh, heads)
+            # the shared key factor (no discrete decision before it): F F^T is unique
+            A, Ao = g["FK"][kh] @ g["FK"][kh].T, refs[0]["FK"] @ refs[0]["FK"].T
+            assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
+            for hd, ref in zip(heads, refs):
+                ref["lam"] = p.lam
+                if _oracle_is_tie_free(ref):
+                    _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text, kh=kh)
+                    assert g["passes"][kh][0] == ref["kmK"]["passes"] and g["passes"][hd][1] == ref["kmQ"]["passes"]
+                else:
+                    # a decision within the 1e-6 tie margin: every stage in lockstep instead
+                    _lockstep_head(g, q, k, v, cfg, opc, b, hd - b * cfg.H, np.random.default_rng(hd))
+    assert np.all(g["head_status"] & 1 == 0)
 
 
 # ------------------------------------------------------------------ probe and estimator variants

@@ -24,6 +24,10 @@ Seeds: per-head draws use ``numpy.random.default_rng([cfg_seed, b, h])``,
 sink positions ``[cfg_seed, b, h, 7]``, text tokens ``[cfg_seed, b, h, 11]``
 and draws shared by a whole config ``[cfg_seed, 999]``.
 
+Grouped-query attention (``Hkv`` > 0, dividing ``H``): q holds the H query heads
+drawn as above and k, v hold Hkv heads, K/V head j of batch entry b being the
+k, v drawn for head (b, j * H / Hkv).
+
 ``step`` > 0 gives the inputs of a later call of the same heads (consecutive
 denoising steps): same frequencies, positions, sinks and mixture centres, fresh
 token noise and values from ``[cfg_seed, b, h, 1000 + step]`` (text tokens from
@@ -58,6 +62,7 @@ class WorkloadConfig:
     max_iters: int = 25
     tol: float = 1e-4
     generator: str = "rff"
+    Hkv: int = 0          # K/V heads under grouped-query attention (0: one per query head)
 
     @property
     def Nv(self) -> int:
@@ -90,6 +95,10 @@ CONFIGS: Dict[str, WorkloadConfig] = {
 }
 # parity-test shape with text tokens: the small video latent plus 128 text tokens, two heads
 CONFIGS["small_text"] = CONFIGS["small"].with_(name="small_text", H=2, n_text=128)
+# grouped-query attention parity shapes: two query heads on one K/V head (fp32, d = 64), and
+# six query heads on two K/V heads with 64 text tokens (bf16, d = 128)
+CONFIGS["tiny_gqa"] = CONFIGS["tiny"].with_(name="tiny_gqa", H=2, Hkv=1)
+CONFIGS["small_gqa"] = CONFIGS["small"].with_(name="small_gqa", H=6, Hkv=2, n_text=64)
 
 
 def config(name: str) -> WorkloadConfig:
@@ -161,7 +170,8 @@ def head_inputs(cfg: WorkloadConfig, b: int, h: int, step: int = 0):
 
 
 def batch_inputs(cfg: WorkloadConfig, heads=None, step: int = 0):
-    """Q, K, V as float32 arrays [B, H, N, d]; ``heads`` optionally restricts to a list of (b, h)."""
+    """Q, K, V as float32 arrays [B, H, N, d]; ``heads`` optionally restricts to a list of (b, h).
+    Under grouped-query attention K and V are [B, Hkv, N, d] (no ``heads`` restriction)."""
     B, H = cfg.B, cfg.H
     out = np.empty((3, B, H, cfg.N, cfg.d), dtype=np.float32)
     for b in range(B):
@@ -170,4 +180,8 @@ def batch_inputs(cfg: WorkloadConfig, heads=None, step: int = 0):
                 out[:, b, h] = 0.0
                 continue
             out[0, b, h], out[1, b, h], out[2, b, h] = head_inputs(cfg, b, h, step)
+    if 0 < cfg.Hkv < H:
+        assert heads is None and H % cfg.Hkv == 0
+        G = H // cfg.Hkv
+        return out[0], np.ascontiguousarray(out[1][:, ::G]), np.ascontiguousarray(out[2][:, ::G])
     return out[0], out[1], out[2]
