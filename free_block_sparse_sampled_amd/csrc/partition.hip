@@ -341,151 +341,231 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
 }
 
 // ------------------------------------------------------------------ later-call factor
-// C (m x n, row stride ldc) = op(A) op(B) with 4 x 4 register tiles per thread (16 independent
-// accumulators hide the load latency).  op(A)(i, k) = A[i * lda + k], or A[k * lda + i] when AT;
-// op(B)(k, j) = B[k * ldb + j], or B[j * ldb + k] when BT; K terms; m, n multiples of 4 (d is 64
-// or 128, ranks are 8 to 64 in steps of 8 or 16).
-template <bool AT, bool BT>
-__device__ inline void gemm_4x4(const double* A, int lda, const double* B, int ldb, double* C, int ldc, int m, int n,
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// C (m x n, row stride ldc) = op(A) op(B) on the fp64 matrix cores (16x16x4 tiles).  Each wave
+// takes 16-row blocks of C with all TN = ceil(n / 16) column tiles at once, so one A fragment
+// feeds TN independent accumulation chains.  op(A)(i, k) = A[i * lda + k], or A[k * lda + i]
+// when AT; op(B)(k, j) = B[k * ldb + j], or B[j * ldb + k] when BT.  K % 4 == 0; rows at or
+// past m and columns at or past n read as zero and are not stored.  Fragments: lane l supplies A(i0 + l % 16,
+// k + l / 16) and B(k + l / 16, 16 t + l % 16); it receives C(i0 + l / 16 + 4 v, 16 t + l % 16).
+template <int TN, bool AT, bool BT>
+__device__ inline void gemm_f64(const double* A, int lda, const double* B, int ldb, double* C, int ldc, int m, int n,
                                 int K) {
-  const int tr = m / 4, tc = n / 4;
-  for (int t = threadIdx.x; t < tr * tc; t += blockDim.x) {
-    const int i0 = (t / tc) * 4, j0 = (t % tc) * 4;
-    double acc[4][4] = {};
-    for (int k = 0; k < K; ++k) {
-      double a[4], b[4];
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6, lane = threadIdx.x & 63;
+  const int i = lane & 15, kq = lane >> 4;
+  for (int i0 = w * 16; i0 < m; i0 += nw * 16) {
+    f64x4_t acc[TN];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) a[x] = AT ? A[size_t(k) * lda + i0 + x] : A[size_t(i0 + x) * lda + k];
+    for (int t = 0; t < TN; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+    for (int k = 0; k < K; k += 4) {
+      const double a = i0 + i >= m ? 0.0 : AT ? A[size_t(k + kq) * lda + i0 + i] : A[size_t(i0 + i) * lda + k + kq];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) b[y] = BT ? B[size_t(j0 + y) * ldb + k] : B[size_t(k) * ldb + j0 + y];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+      for (int t = 0; t < TN; ++t) {
+        const int col = t * 16 + i;
+        const double b = col < n ? (BT ? B[size_t(col) * ldb + k + kq] : B[size_t(k + kq) * ldb + col]) : 0.0;
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[t], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int t = 0; t < TN; ++t) {
+      const int col = t * 16 + i;
+      if (col < n)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) C[size_t(i0 + x) * ldc + j0 + y] = acc[x][y];
-  }
-}
-
-// Largest diagonal entry of the n x n matrix G (n <= 64), computed by every wave on its own so
-// that no shared scratch is needed; all threads return the same value.
-__device__ inline double diag_max(const double* G, int n) {
-  const int lane = threadIdx.x & 63;
-  double x = lane < n ? G[lane * n + lane] : 0.0;
-  for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
-  return x;
-}
-
-// In-place upper Cholesky of the symmetric n x n matrix G (row stride n): the upper triangle
-// becomes R with G = R^T R and the strict lower triangle is cleared.  Returns false (for every
-// thread) when a pivot is not above floor.
-__device__ inline bool chol_upper(double* G, int n, double floor) {
-  for (int j = 0; j < n; ++j) {
-    __syncthreads();
-    const double piv = G[j * n + j];
-    if (!(piv > floor)) return false;
-    const double rjj = sqrt(piv);
-    __syncthreads();
-    for (int k = j + threadIdx.x; k < n; k += blockDim.x) G[j * n + k] = k == j ? rjj : G[j * n + k] / rjj;
-    __syncthreads();
-    const int m = n - j - 1;
-    for (int e = threadIdx.x; e < m * m; e += blockDim.x) {
-      const int a = j + 1 + e / m, b = j + 1 + e % m;
-      if (b >= a) G[a * n + b] -= G[j * n + a] * G[j * n + b];
+        for (int v = 0; v < 4; ++v)
+          if (i0 + kq + 4 * v < m) C[size_t(i0 + kq + 4 * v) * ldc + col] = acc[t][v];
     }
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < n * n; e += blockDim.x)
-    if (e % n < e / n) G[e] = 0.0;
-  __syncthreads();
-  return true;
 }
 
-// In-place inverse of the upper triangular R (strict lower triangle zero), column by column:
-// column j of R^{-1} is -(1 / R_jj) times the leading inverse block applied to column j of R.
-// The new column is formed in registers and written after a barrier, since its rows are read
-// as the old column while it is formed.
-__device__ inline void tri_inv_upper_inplace(double* R, int n) {
-  for (int j = 0; j < n; ++j) {
-    const double rjj = R[j * n + j];
-    double x = 0.0;
-    const int i = threadIdx.x;
-    if (i < j)
-      for (int k = i; k < j; ++k) x = fma(R[i * n + k], R[k * n + j], x);
-    __syncthreads();
-    if (i < j) R[i * n + j] = -x / rjj;
-    if (i == j) R[j * n + j] = 1.0 / rjj;
-    __syncthreads();
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_readlane(unsigned(u), l);
+  const unsigned hi = __builtin_amdgcn_readlane(unsigned(u >> 32), l);
+  return __longlong_as_double((long long)((unsigned long long)hi << 32 | lo));
+}
+
+// Upper Cholesky G = R^T R of the R x R matrix in LDS (row stride R) by one wave, with the
+// trailing matrix in registers: lane c holds column c, g[a] being row j + a at step j, so that
+// every register index is a constant and the rows shift down by one per step as they are
+// updated.  Step j: pivot from lane j, row j of R (R[j][c] = G[j][c] / R[j][j]) written to G and
+// to `rowbuf` (2R doubles of LDS scratch; entries past R stay zero), then g[a - 1] = g[a] -
+// R[j][j + a] R[j][c] with the multipliers read back from rowbuf as broadcasts.  LDS accesses of
+// one wave complete in program order, so wave barriers (which stop the compiler from moving
+// memory operations across them) are the only synchronisation.  A pivot not above scale times
+// the largest diagonal entry fails; the remaining steps then run on a unit pivot.  On success G
+// holds R (upper triangular, row-major); on failure G[0] is -1, a value R[0][0] = sqrt(pivot) > 0
+// never takes, so that every wave can read the outcome after a block barrier.
+template <int R>
+__device__ inline void chol_wave(double* G, double* rowbuf, double scale) {
+  const int c = threadIdx.x & 63;
+  const int cc = c < R ? c : R - 1;  // lanes past R shadow the last column and store nothing
+  double g[R];
+#pragma unroll
+  for (int a = 0; a < R; ++a) g[a] = G[a * R + cc];
+  double dmax = G[cc * R + cc];
+  for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o));
+  const double floor = scale * dmax;
+  if (c < R) rowbuf[R + c] = 0.0;
+  bool ok = true;
+#pragma unroll 1
+  for (int j = 0; j < R; ++j) {
+    const double piv = readlane_d(g[0], j);
+    ok = ok && piv > floor;
+    const double rjj = ok ? sqrt(piv) : 1.0;
+    const double rjc = c == j ? rjj : (c > j ? g[0] / rjj : 0.0);
+    __builtin_amdgcn_wave_barrier();
+    if (c < R) {
+      rowbuf[c] = rjc;
+      G[j * R + c] = rjc;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // in chunks of 16, so that the loaded values fit in registers beside g
+#pragma unroll
+    for (int a = 1; a < R; ++a) {
+      g[a - 1] = fma(-rowbuf[j + a], rjc, g[a]);
+      if (a % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+    g[R - 1] = 0.0;
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (!ok && c == 0) G[0] = -1.0;
+}
+
+// Ut = (Z R^{-1})^T from Zt = Z^T (R x D) and the upper R (row-major, R x R): row i of U solves
+// u R = z_i, one thread per row.  Column by column, u_c = z_c / R_cc and then z_k -= u_c R_ck
+// for k > c, with the remaining z in registers shifted down by one per column (every register
+// index a constant) and row c of R read as broadcasts.  Reads past row c of R run into the rows
+// after it (or the buffer that follows R in LDS); they only touch the shifted-out tail, which
+// never feeds a column below R.  Thread i touches column i of Zt and Ut, so a wave's accesses
+// are contiguous.
+template <int R, int D>
+__device__ inline void right_solve_upper(const double* Zt, const double* Rm, double* Ut) {
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    double z[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) z[a] = Zt[a * D + i];
+#pragma unroll 1
+    for (int c = 0; c < R; ++c) {
+      const double* row = Rm + c * (R + 1);  // R[c][c + a] = row[a]
+      const double uc = z[0] / row[0];
+      Ut[c * D + i] = uc;
+      // in chunks of 16, so that the loaded values fit in registers beside z
+#pragma unroll
+      for (int a = 1; a < R; ++a) {
+        z[a - 1] = fma(-uc, row[a], z[a]);
+        if (a % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+      }
+      z[R - 1] = 0.0;
+    }
   }
 }
 
 // Factor update of later calls (App. C.1): two subspace iterations from the span of the previous
 // factor (columns scaled to unit length), U <- orth(M U) by Cholesky QR (Z = M U, Z^T Z = R^T R,
 // U = Z R^{-1}), then F = U L with L L^T = U^T M U, so F F^T = U U^T M U U^T.  One workgroup per
-// head; M is read from global memory, U and Z (d x r each) and one r x r matrix live in LDS.  A pivot of Z^T Z at or below clamp^2,
-// or of U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero
-// previous column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes
-// over; otherwise ok = 1 and F is written.
+// head: the products on the fp64 matrix cores, each Cholesky factorisation by one wave, the
+// triangular solve one row per thread.  U and Z are kept transposed in LDS (Ut, Zt: R x D) so
+// that the solve reads them contiguously; M is symmetric, so Zt = Ut M.  M is read from global
+// memory; one R x R matrix, Ut and Zt live in LDS, in that order.  A pivot of Z^T Z at or below clamp^2, or of
+// U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero previous
+// column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes over;
+// otherwise ok = 1 and F is written.
+template <int D, int R>
 __global__ __launch_bounds__(256) void subspace_factor_kernel(const double* __restrict__ Mall,
-                                                              const double* __restrict__ Fprev, int d, int r,
-                                                              double clamp, double* __restrict__ Fall,
-                                                              int* __restrict__ gstat, int ok_slot) {
+                                                              const double* __restrict__ Fprev, double clamp,
+                                                              double* __restrict__ Fall, int* __restrict__ gstat,
+                                                              int ok_slot) {
+  constexpr int TD = D / 16, TR = (R + 15) / 16;
   extern __shared__ double sub_sm[];
   const int hd = blockIdx.x, tid = threadIdx.x, nth = blockDim.x;
-  const double* M = Mall + size_t(hd) * d * d;
-  double* U = sub_sm;              // [d][r]
-  double* Z = sub_sm + d * r;      // [d][r]
-  double* G = sub_sm + 2 * d * r;  // [r][r]
-  for (int e = tid; e < d * r; e += nth) U[e] = Fprev[size_t(hd) * d * r + e];
+  const double* M = Mall + size_t(hd) * D * D;
+  double* G = sub_sm;                   // [R][R]
+  double* Ut = sub_sm + R * R;          // [R][D]
+  double* Zt = sub_sm + R * R + D * R;  // [R][D]
+  // U^T: consecutive threads take consecutive rows of U, so the LDS writes are contiguous
+  for (int e = tid; e < D * R; e += nth) {
+    const int j = e / D, i = e % D;
+    Ut[e] = Fprev[size_t(hd) * D * R + size_t(i) * R + j];
+  }
   __syncthreads();
   // the previous factor's span, columns scaled to unit length; a zero column means a rank
-  // below r, which the update cannot recover.  Every wave forms all r column norms (lane j holds
-  // column j), so the scale and the zero test need no shared scratch.
-  const int lane = tid & 63;
-  double cs = 0.0;
-  if (lane < r)
-    for (int i = 0; i < d; ++i) cs = fma(U[i * r + lane], U[i * r + lane], cs);
-  bool ok = !__any(lane < r && !(cs > 0.0));
-  const double cinv = cs > 0.0 ? 1.0 / sqrt(cs) : 0.0;
-  __syncthreads();
-  if (ok) {
-    for (int e = tid; e < d * r; e += nth) U[e] *= __shfl(cinv, e % r);
-    __syncthreads();
+  // below R, which the update cannot recover.  Wave w forms the norms of columns w, w + 4, ..
+  // (rows of U^T) and leaves 1 / norm, or 0 for a zero column, in G, unused until the first
+  // product.
+  const int lane = tid & 63, w = tid >> 6, nw = nth >> 6;
+  for (int j = w; j < R; j += nw) {
+    double cs = 0.0;
+    for (int i = lane; i < D; i += 64) cs = fma(Ut[j * D + i], Ut[j * D + i], cs);
+    for (int o = 32; o > 0; o >>= 1) cs += __shfl_xor(cs, o);
+    if (lane == 0) G[j] = cs > 0.0 ? 1.0 / sqrt(cs) : 0.0;
   }
+  __syncthreads();
+  bool ok = true;
+  for (int j = 0; j < R; ++j) ok = ok && G[j] > 0.0;
+  if (ok) {
+    for (int e = tid; e < D * R; e += nth) Ut[e] *= G[e / D];
+  }
+  __syncthreads();
   for (int it = 0; it < 2 && ok; ++it) {
-    gemm_4x4<false, false>(M, d, U, r, Z, r, d, r, d);  // Z = M U
+    gemm_f64<TD, false, false>(Ut, D, M, D, Zt, D, R, D, D);  // Zt = Ut M = (M U)^T
     __syncthreads();
-    gemm_4x4<true, false>(Z, r, Z, r, G, r, r, r, d);   // G = Z^T Z
+    gemm_f64<TR, false, true>(Zt, D, Zt, D, G, R, R, R, D);   // G = Z^T Z
     __syncthreads();
     // Z^T Z scales with the squared singular values of Z: tested against clamp^2
-    ok = chol_upper(G, r, clamp * clamp * diag_max(G, r));
+    if (tid < 64) chol_wave<R>(G, Ut, clamp * clamp);  // U is dead until the solve rewrites it
+    __syncthreads();
+    ok = G[0] > 0.0;
     if (!ok) break;
-    tri_inv_upper_inplace(G, r);
-    gemm_4x4<false, false>(Z, r, G, r, U, r, d, r, r);  // U = Z R^{-1}
+    right_solve_upper<R, D>(Zt, G, Ut);  // U = Z R^{-1}
     __syncthreads();
   }
   if (ok) {
-    gemm_4x4<false, false>(M, d, U, r, Z, r, d, r, d);  // W = M U
+    gemm_f64<TD, false, false>(Ut, D, M, D, Zt, D, R, D, D);  // Wt = (M U)^T
     __syncthreads();
-    gemm_4x4<true, false>(U, r, Z, r, G, r, r, r, d);   // U^T W
+    gemm_f64<TR, false, true>(Ut, D, Zt, D, G, R, R, R, D);   // U^T W
     __syncthreads();
-    for (int e = tid; e < r * r; e += nth) {
-      const int a = e / r, b = e % r;
+    for (int e = tid; e < R * R; e += nth) {
+      const int a = e / R, b = e % R;
       if (b > a) {
-        const double h = 0.5 * (G[a * r + b] + G[b * r + a]);
-        G[a * r + b] = h;
-        G[b * r + a] = h;
+        const double h = 0.5 * (G[a * R + b] + G[b * R + a]);
+        G[a * R + b] = h;
+        G[b * R + a] = h;
       }
     }
     __syncthreads();
-    ok = chol_upper(G, r, clamp * diag_max(G, r));
+    if (tid < 64) chol_wave<R>(G, Zt, clamp);  // W is dead after U^T W
+    __syncthreads();
+    ok = G[0] > 0.0;
     // F = U R^T
-    if (ok) gemm_4x4<false, true>(U, r, G, r, Fall + size_t(hd) * d * r, r, d, r, r);
+    if (ok) gemm_f64<TR, true, true>(Ut, D, G, R, Fall + size_t(hd) * D * R, R, D, R, R);
   }
   if (tid == 0) gstat[hd * 8 + ok_slot] = ok ? 1 : 0;
+}
+
+// The instantiation for (d, r); d in {64, 128}, r in {8, 16, 32, 48, 64}.
+template <int D>
+static void launch_subspace_d(int BH, int r, size_t smem, hipStream_t st, const double* M, const double* Fprev,
+                              double clamp, double* F, int* gstat, int slot) {
+  auto go = [&](auto kern) {
+    allow_lds(kern, smem);
+    hipLaunchKernelGGL(kern, dim3(BH), dim3(256), smem, st, M, Fprev, clamp, F, gstat, slot);
+  };
+  switch (r) {
+    case 8: go(subspace_factor_kernel<D, 8>); break;
+    case 16: go(subspace_factor_kernel<D, 16>); break;
+    case 32: go(subspace_factor_kernel<D, 32>); break;
+    case 48: go(subspace_factor_kernel<D, 48>); break;
+    default: go(subspace_factor_kernel<D, 64>); break;
+  }
+}
+
+static void launch_subspace(int BH, int d, int r, hipStream_t st, const double* M, const double* Fprev, double clamp,
+                            double* F, int* gstat, int slot) {
+  const size_t smem = (2 * size_t(d) * r + size_t(r) * r) * sizeof(double);
+  if (d == 128) launch_subspace_d<128>(BH, r, smem, st, M, Fprev, clamp, F, gstat, slot);
+  else launch_subspace_d<64>(BH, r, smem, st, M, Fprev, clamp, F, gstat, slot);
 }
 
 // Initial centres of a later call (App. C.1): previous centroid m (original space) mapped to the
@@ -534,7 +614,6 @@ __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restr
 }
 
 // ------------------------------------------------------------------ projection
-typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 // phi = X F (Sec. 4.1) on v_mfma_f64_16x16x4f64; with RMS the rows are RMS-normalised as in
 // App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  The fp64 MFMA takes A[i][k] from lane i + 16k
@@ -939,12 +1018,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
   allow_lds(eigen_factor_kernel, jac_smem);
-  const int rmx = p.rK > p.rQ ? p.rK : p.rQ;
-  const size_t sub_smem = (2 * size_t(d) * rmx + size_t(rmx) * rmx) * sizeof(double);
-  allow_lds(subspace_factor_kernel, sub_smem);
   if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
-    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BHkv), dim3(256), sub_smem, st, metric, warm->FK, d, p.rK,
-                       p.eig_clamp, out.FK, kvstat, 2);
+    launch_subspace(BHkv, d, p.rK, st, metric, warm->FK, p.eig_clamp, out.FK, kvstat, 2);
   hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
                      kvstat, warm ? 2 : -1);
   SPR_CHECK_LAUNCH();
@@ -1003,8 +1078,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
                      metric);
   if (warm)
-    hipLaunchKernelGGL(subspace_factor_kernel, dim3(BHkv), dim3(256), sub_smem, st, metric, warm->FQ, d, p.rQ,
-                       p.eig_clamp, out.FQ, kvstat, 3);
+    launch_subspace(BHkv, d, p.rQ, st, metric, warm->FQ, p.eig_clamp, out.FQ, kvstat, 3);
   hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
                      kvstat, warm ? 3 : -1);
   SPR_CHECK_LAUNCH();

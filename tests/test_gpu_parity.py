@@ -206,6 +206,34 @@ def test_warm_start_end_to_end(name, heads):
         _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text)
 
 
+@pytest.mark.parametrize("name,rK,rQ", [("small", 8, 16), ("small", 32, 32), ("tiny", 16, 8)])
+def test_warm_start_factor_ranks(name, rK, rQ):
+    """Later calls at the other factor ranks (8 to 32) and at d = 64: the subspace update of both
+    factors against the oracle's later-call path, then the whole head as in the test above."""
+    cfg = config(name)
+    opc = op_config(cfg, rK=rK, rQ=rQ)
+    (q0, k0, v0), (tq0, tk0, tv0) = device_inputs(cfg, step=0)
+    (q1, k1, v1), (tq1, tk1, tv1) = device_inputs(cfg, step=1)
+    op = spr.SparsePR(tq0, opc, n_text=cfg.n_text, diagnostics=True, keep_scores=True)
+    op.run(tq0, tk0, tv0)
+    op.run(tq1, tk1, tv1, warm=True)
+    torch.cuda.synchronize()
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    p2 = O.Params(**{**p.__dict__, "max_iters": op.warm_iters})
+    first = O.sparsepr_head(q0[0, 0], k0[0, 0], v0[0, 0], p, head=0, full=False)
+    rows = None if cfg.N <= 2048 else np.arange(0, cfg.N, 7)
+    ref = O.sparsepr_head(q1[0, 0], k1[0, 0], v1[0, 0], p2, head=0, rows=rows, warm=first["state"])
+    ref["lam"] = p.lam
+    assert ref["warm_ok"] == [True, True]
+    if _oracle_is_tie_free(first) and _oracle_is_tie_free(ref):
+        _compare_head(g, ref, 0, cfg.Nv, cfg.N, cfg.n_text)
+    else:
+        for F, Fo in ((g["FK"][0], ref["FK"]), (g["FQ"][0], ref["FQ"])):
+            A, Ao = F @ F.T, Fo @ Fo.T
+            assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
+
+
 def test_lockstep_stages_small():
     """Each stage's oracle function applied to the GPU's own inputs of that stage."""
     cfg = config("small")
