@@ -11,41 +11,70 @@
 namespace spr {
 
 // ------------------------------------------------------------------ key metric
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 // M_K = Q_s^T Q_s / M_s over rows s_i = floor(i * Nv / M_s) (Sec. 4.1 / App. B.1 for the
 // metric, App. C.2 for the evenly spaced sampling); with grouped-query attention Q_s stacks the
 // sampled rows of the G query heads of K/V head j (heads j G .. j G + G - 1), M_K = Q_s^T Q_s /
-// (G M_s).  16x16 output tile per block, fp64 sums.
-template <int DT>
+// (G M_s).  On the fp64 matrix cores: one block per 16 rows of M_K (i0 .. i0 + 15) and head; the
+// sampled rows stream through LDS in chunks of 64 (widened to fp64, the next chunk loaded into
+// registers meanwhile), and wave w accumulates columns 16 TW w .. 16 TW (w + 1) - 1.
+template <int DT, int D>
 __global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict__ q, HeadGeom g, int Ms, int G,
                                                          double* __restrict__ out) {
-  const int hj = blockIdx.y;
-  const int tiles = g.d / 16;
-  const int i0 = (blockIdx.x / tiles) * 16, j0 = (blockIdx.x % tiles) * 16;
-  const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-  __shared__ float As[32][17], Bs[32][17];
-  const int m = min(Ms, g.Nv);
-  double acc = 0.0;
-  for (int gi = 0; gi < G; ++gi) {
-    const int64_t base = g.base(hj * G + gi);
-    for (int s0 = 0; s0 < m; s0 += 32) {
-      for (int e = threadIdx.x; e < 32 * 16; e += 256) {
-        const int rr = e >> 4, cc = e & 15, s = s0 + rr;
-        float a = 0.f, b = 0.f;
-        if (s < m) {
-          const int64_t row = (int64_t(s) * g.Nv) / m;
-          a = load_elem<DT>(q, base + row * g.sn + i0 + cc);
-          b = load_elem<DT>(q, base + row * g.sn + j0 + cc);
-        }
-        As[rr][cc] = a;
-        Bs[rr][cc] = b;
+  constexpr int KC = 64, XS = D + 2, TW = D / 64, PER = KC * D / 8 / 256;
+  extern __shared__ double km_xs[];  // [KC][XS]
+  const int hj = blockIdx.y, i0 = blockIdx.x * 16;
+  const int m = min(Ms, g.Nv), total = m * G;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kq = lane >> 4;
+  float xv[PER][8];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u, kk = e / (D / 8), c8 = (e % (D / 8)) * 8, k = k0 + kk;
+      if (k < total) {
+        const int gi = k / m, sidx = k % m;
+        const int64_t row = (int64_t(sidx) * g.Nv) / m;
+        load8<DT>(q, g.base(hj * G + gi) + row * g.sn + c8, xv[u]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xv[u][t] = 0.f;
       }
-      __syncthreads();
-#pragma unroll 8
-      for (int rr = 0; rr < 32; ++rr) acc = fma(double(As[rr][ti]), double(Bs[rr][tj]), acc);
-      __syncthreads();
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u, kk = e / (D / 8), c8 = (e % (D / 8)) * 8;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2)
+        *reinterpret_cast<double2*>(km_xs + kk * XS + c8 + t) = make_double2(xv[u][t], xv[u][t + 1]);
+    }
+  };
+  f64x4_t acc[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) acc[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  fetch(0);
+  for (int k0 = 0; k0 < total; k0 += KC) {
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (k0 + KC < total) fetch(k0 + KC);
+#pragma unroll 4
+    for (int kk = 0; kk < KC; kk += 4) {
+      const double* xr = km_xs + (kk + kq) * XS;
+      const double a = xr[i0 + r16];
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, xr[(w * TW + t) * 16 + r16], acc[t], 0, 0, 0);
     }
   }
-  out[size_t(hj) * g.d * g.d + size_t(i0 + ti) * g.d + j0 + tj] = acc / (double(m) * G);
+  const double den = double(m) * G;
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      out[size_t(hj) * D * D + size_t(i0 + kq + 4 * v) * D + (w * TW + t) * 16 + r16] = acc[t][v] / den;
 }
 
 // Centred key centroids K~ = kbar_b - mu_K over the n_kv nonempty groups (App. B.2).  One block
@@ -341,7 +370,6 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
 }
 
 // ------------------------------------------------------------------ later-call factor
-typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 // C (m x n, row stride ldc) = op(A) op(B) on the fp64 matrix cores (16x16x4 tiles).  Each wave
 // takes 16-row blocks of C with all TN = ceil(n / 16) column tiles at once, so one A fragment
@@ -569,9 +597,9 @@ static void launch_subspace(int BH, int d, int r, hipStream_t st, const double* 
 }
 
 // Initial centres of a later call (App. C.1): previous centroid m (original space) mapped to the
-// current coordinates, x F (RMS-normalised as in App. B.2 for queries); slots m >= n_prev take
-// the cold draw of index m.  One block per 64 centres of a head.
-template <bool RMS>
+// current coordinates, x F on the fp64 matrix cores (RMS-normalised as in App. B.2 for queries);
+// slots m >= n_prev take the cold draw of index m.  One block per 64 centres of a head.
+template <bool RMS, int TN>
 __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restrict__ prev,
                                                            const int* __restrict__ n_prev, int C, int d,
                                                            const double* __restrict__ Fall, int r, double eps,
@@ -581,20 +609,15 @@ __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restr
   const int hd = blockIdx.y, m0 = blockIdx.x * 64;
   const int np = min(n_prev[hd], C);
   const double* F = Fall + size_t(hd / fdiv) * d * r;  // factor of the head's K/V head
+  // rows of slots at or past n_prev are stale previous centroids; they are replaced below
+  gemm_f64<TN, false, false>(prev + (size_t(hd) * C + m0) * d, d, F, r, &ys[0][0], 65, min(64, C - m0), r, d);
+  __syncthreads();
   for (int e = threadIdx.x; e < 64 * r; e += blockDim.x) {
     const int ml = e / r, j = e % r, m = m0 + ml;
-    if (m >= C) continue;
-    double y;
-    if (m < np) {
-      const double* x = prev + (size_t(hd) * C + m) * d;
-      y = 0.0;
-      for (int c = 0; c < d; ++c) y = fma(x[c], F[size_t(c) * r + j], y);
-    } else {
-      const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
-      const int row = int(splitmix64(seed, ctr) % uint64_t(n));
-      y = feat[(size_t(hd) * n + row) * r + j];
-    }
-    ys[ml][j] = y;
+    if (m >= C || m < np) continue;
+    const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
+    const int row = int(splitmix64(seed, ctr) % uint64_t(n));
+    ys[ml][j] = feat[(size_t(hd) * n + row) * r + j];
   }
   __syncthreads();
   if (RMS && threadIdx.x < 64) {
@@ -610,6 +633,30 @@ __global__ __launch_bounds__(256) void warm_centres_kernel(const double* __restr
   for (int e = threadIdx.x; e < 64 * r; e += blockDim.x) {
     const int ml = e / r, j = e % r, m = m0 + ml;
     if (m < C) cent[(size_t(hd) * C + m) * r + j] = ys[ml][j];
+  }
+}
+
+template <bool RMS>
+static void launch_warm_centres(dim3 grid, hipStream_t st, const double* prev, const int* n_prev, int C, int d,
+                                const double* F, int r, double eps, const double* feat, int n, uint64_t seed,
+                                int stage, int fdiv, double* cent) {
+  switch ((r + 15) / 16) {
+    case 1:
+      hipLaunchKernelGGL((warm_centres_kernel<RMS, 1>), grid, dim3(256), 0, st, prev, n_prev, C, d, F, r, eps, feat,
+                         n, seed, stage, fdiv, cent);
+      break;
+    case 2:
+      hipLaunchKernelGGL((warm_centres_kernel<RMS, 2>), grid, dim3(256), 0, st, prev, n_prev, C, d, F, r, eps, feat,
+                         n, seed, stage, fdiv, cent);
+      break;
+    case 3:
+      hipLaunchKernelGGL((warm_centres_kernel<RMS, 3>), grid, dim3(256), 0, st, prev, n_prev, C, d, F, r, eps, feat,
+                         n, seed, stage, fdiv, cent);
+      break;
+    default:
+      hipLaunchKernelGGL((warm_centres_kernel<RMS, 4>), grid, dim3(256), 0, st, prev, n_prev, C, d, F, r, eps, feat,
+                         n, seed, stage, fdiv, cent);
+      break;
   }
 }
 
@@ -1013,8 +1060,16 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
                      size_t(BH + BHkv) * 8);
 
   // M_K and F_K
-  hipLaunchKernelGGL(key_metric_kernel<DT>, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, q, g, p.Ms, G,
-                     metric);
+  {
+    const size_t kms = size_t(64) * (d + 2) * sizeof(double);
+    if (d == 128) {
+      allow_lds(key_metric_kernel<DT, 128>, kms);
+      hipLaunchKernelGGL((key_metric_kernel<DT, 128>), dim3(d / 16, BHkv), dim3(256), kms, st, q, g, p.Ms, G, metric);
+    } else {
+      allow_lds(key_metric_kernel<DT, 64>, kms);
+      hipLaunchKernelGGL((key_metric_kernel<DT, 64>), dim3(d / 16, BHkv), dim3(256), kms, st, q, g, p.Ms, G, metric);
+    }
+  }
   SPR_CHECK_LAUNCH();
   const size_t jac_smem = jacobi_smem(d);
   allow_lds(eigen_factor_kernel, jac_smem);
@@ -1037,8 +1092,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   ka.max_iters = p.max_iters; ka.tol = p.tol;
   ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
   if (warm) {
-    hipLaunchKernelGGL(warm_centres_kernel<false>, dim3(ceil_div(p.Ck, 64), BHkv), dim3(256), 0, st, warm->kbar,
-                       warm->n_kv, p.Ck, d, out.FK, p.rK, p.rms_eps, phiK, Nv, p.seed, 0, 1, ka.cent);
+    launch_warm_centres<false>(dim3(ceil_div(p.Ck, 64), BHkv), st, warm->kbar, warm->n_kv, p.Ck, d, out.FK, p.rK,
+                               p.rms_eps, phiK, Nv, p.seed, 0, 1, ka.cent);
     SPR_CHECK_LAUNCH();
     ka.cent_given = true;
   }
@@ -1090,8 +1145,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   KmArgs qa = ka;
   qa.BH = BH; qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1; qa.cent_given = warm != nullptr;
   if (warm) {
-    hipLaunchKernelGGL(warm_centres_kernel<true>, dim3(ceil_div(p.Cq, 64), BH), dim3(256), 0, st, warm->qbar,
-                       warm->n_q, p.Cq, d, out.FQ, p.rQ, p.rms_eps, phiQ, Nv, p.seed, 1, G, qa.cent);
+    launch_warm_centres<true>(dim3(ceil_div(p.Cq, 64), BH), st, warm->qbar, warm->n_q, p.Cq, d, out.FQ, p.rQ,
+                              p.rms_eps, phiQ, Nv, p.seed, 1, G, qa.cent);
     SPR_CHECK_LAUNCH();
   }
   s = run_kmeans(qa, st);

@@ -47,55 +47,64 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-// Centroid logits lbar_ab = qbar_a . kbar_b / sqrt d on the fp64 matrix cores, and the shift
-// m_a = max_b lbar_ab.  One block per 64 query groups of a head: wave w owns query groups
-// a0 + 16 w .. + 15 (A fragments of qbar in registers: lane l holds qbar[a0 + 16 w + l % 16]
-// at columns 4 ks + l / 16) and walks the K/V groups in tiles of 16 (B fragments read from
-// kbar); lane l, slot v of the result holds the logit of query group 16 w + l / 16 + 4 v and
-// K/V group l % 16 of the tile.
+// Centroid logits lbar_ab = qbar_a . kbar_b / sqrt d on the fp64 matrix cores.  One block per
+// 64 query groups x 64 K/V groups of a head: wave w owns query groups a0 + 16 w .. + 15 (A
+// fragments of qbar in registers: lane l holds qbar[a0 + 16 w + l % 16] at columns 4 ks + l / 16)
+// and the block's four tiles of 16 K/V groups, each its own accumulation chain; lane l, slot v
+// of tile t holds the logit of query group 16 w + l / 16 + 4 v and K/V group b0 + 16 t + l % 16.
 template <int D>
 __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __restrict__ qbar,
                                                               const double* __restrict__ kbar,
                                                               const int* __restrict__ n_q,
                                                               const int* __restrict__ n_kv, int Cq, int Ck, int G,
-                                                              double* __restrict__ lbar, double* __restrict__ shift) {
-  const int hd = blockIdx.y, hk = hd / G, a0 = blockIdx.x * 64;  // query head, its K/V head
+                                                              double* __restrict__ lbar) {
+  const int hd = blockIdx.z, hk = hd / G, a0 = blockIdx.x * 64, b0 = blockIdx.y * 64;  // query head, K/V head
   const int nq = n_q[hd], nkv = n_kv[hk];
-  if (a0 >= nq) return;
+  if (a0 >= nq || b0 >= nkv) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
+  const int aw = a0 + w * 16;
+  if (aw >= nq) return;
   double qa[D / 4];
   {
-    const int a = a0 + w * 16 + r16;
+    const int a = aw + r16;
 #pragma unroll
     for (int ks = 0; ks < D / 4; ++ks) qa[ks] = a < nq ? qbar[(size_t(hd) * Cq + a) * D + ks * 4 + gq] : 0.0;
   }
   const double inv = 1.0 / sqrt(double(D));
-  double mx[4] = {-1.0e308, -1.0e308, -1.0e308, -1.0e308};
-  for (int b0 = 0; b0 < nkv; b0 += 16) {
-    const int b = b0 + r16;
-    const double* kb = kbar + (size_t(hk) * Ck + min(b, nkv - 1)) * D + gq;
-    f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+  const double* kb[4];
 #pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks * 4], lg, 0, 0, 0);
+  for (int t = 0; t < 4; ++t) kb[t] = kbar + (size_t(hk) * Ck + min(b0 + 16 * t + r16, nkv - 1)) * D + gq;
+  f64x4_t lg[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) lg[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < D / 4; ++ks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lg[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[t][ks * 4], lg[t], 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int b = b0 + 16 * t + r16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int a = a0 + w * 16 + gq + 4 * v;
-      const double x = lg[v] * inv;
-      if (b < nkv && a < nq) {
-        lbar[(size_t(hd) * Cq + a) * Ck + b] = x;
-        mx[v] = fmax(mx[v], x);
-      }
+      const int a = aw + gq + 4 * v;
+      if (b < nkv && a < nq) lbar[(size_t(hd) * Cq + a) * Ck + b] = lg[t][v] * inv;
     }
   }
-#pragma unroll
-  for (int v = 0; v < 4; ++v)
-    for (int o = 1; o < 16; o <<= 1) mx[v] = fmax(mx[v], __shfl_xor(mx[v], o));
-  if (r16 == 0)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int a = a0 + w * 16 + gq + 4 * v;
-      if (a < nq) shift[size_t(hd) * Cq + a] = mx[v];
-    }
+}
+
+// The shift m_a = max_b lbar_ab of every query group, one wave per group.
+__global__ __launch_bounds__(256) void logit_shift_kernel(const double* __restrict__ lbar,
+                                                          const int* __restrict__ n_q,
+                                                          const int* __restrict__ n_kv, int Cq, int Ck, int G,
+                                                          double* __restrict__ shift) {
+  const int hd = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= n_q[hd]) return;
+  const int nkv = n_kv[hd / G];
+  const double* row = lbar + (size_t(hd) * Cq + a) * Ck;
+  double mx = -1.0e308;
+  for (int b = lane; b < nkv; b += 64) mx = fmax(mx, row[b]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+  if (lane == 0) shift[size_t(hd) * Cq + a] = mx;
 }
 
 // e^x in fp64 by Tang's table method: x = (64 n + j) ln2 / 64 + r with |r| <= ln2 / 128,
@@ -223,9 +232,14 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
           kb[2 * i] = u.x;
           kb[2 * i + 1] = u.y;
         }
-        f64x4_t lg = {0.0, 0.0, 0.0, 0.0};
+        // four independent accumulation chains keep the matrix pipe busy; summed pairwise
+        f64x4_t l4[4];
 #pragma unroll
-        for (int ks = 0; ks < D / 4; ++ks) lg = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks], lg, 0, 0, 0);
+        for (int h = 0; h < 4; ++h) l4[h] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < D / 4; ++ks)
+          l4[ks & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[ks], l4[ks & 3], 0, 0, 0);
+        const f64x4_t lg = (l4[0] + l4[1]) + (l4[2] + l4[3]);
         const double uu = us[jl], ww = wsv[jl];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -519,17 +533,21 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   hipLaunchKernelGGL(vstat_kernel<DT>, dim3(ceil_div(Nv, 256 / (d / 8)), BHkv), dim3(256), 0, st, part.Vp, N, Nv, d,
                      part.kv_perm, part.kv_label, part.vbar, p.Ck, vstat);
   double* lbar = ws_ptr<double>(ws, L.lbar);
-  const dim3 lgrid(ceil_div(p.Cq, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
+  const dim3 lgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
   if (d == 128) {
     hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, G, lbar, shift);
+                       part.n_kv, p.Cq, p.Ck, G, lbar);
+    hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
+                       p.Cq, p.Ck, G, shift);
     allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
     hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), route_score_smem<128>(), st, part.Kp, N, Nv,
                        part.qbar, lbar,
                        part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat, scores);
   } else {
     hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, G, lbar, shift);
+                       part.n_kv, p.Cq, p.Ck, G, lbar);
+    hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
+                       p.Cq, p.Ck, G, shift);
     allow_lds(route_score_kernel<DT, 64>, route_score_smem<64>());
     hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), route_score_smem<64>(), st, part.Kp, N, Nv,
                        part.qbar, lbar,
