@@ -50,6 +50,14 @@ against the pages; the tests pin them against mathematics instead):
   the row-major (t, h, w) sequence; both carry weights Nv / M.  The output truncation
   takes the leading eigenvectors of Rbar^T W Rbar, eigenvalues at or below eig_clamp
   times the largest counted as absent.
+* Semantic partition (Sec. 3.1; Table 2): k-means on the raw video keys and queries (d
+  coordinates, no RMSNorm), the same initialisation and stopping rules; values inherit their
+  key's group.  The key-response variant keeps the response-coupled K/V groups and takes
+  semantic query groups.  Probe distances d_i are taken in the coordinates the query groups
+  were formed in; warm starts map the previous centroids through the mode's feature map.
+* Affine representability (App. D.5): least squares on [1, O_sp] via an SVD of the centred,
+  column-scaled sparse outputs (relative tolerance 1e-10); explained fraction relative to the
+  uncentred residual energy.
 * Grouped-query attention (Sec. 4.3; App. C.2): the concatenation of the G heads'
   video query rows is sampled like one head's rows with G * Ms in place of Ms, which
   takes the same evenly spaced rows from each head.  The K/V k-means draws from the
@@ -72,7 +80,7 @@ __all__ = [
     "select_probes_random", "select_probes_uniform", "output_projector",
     "executed_density", "allocate_probes", "select_probes", "ridge_fit", "correct", "relative_error",
     "sparsepr_head", "cholesky_upper", "metric_factor_warm", "warm_centres",
-    "key_metric_shared", "kv_side", "query_side", "sparsepr_group",
+    "key_metric_shared", "kv_side", "query_side", "sparsepr_group", "affine_representability",
 ]
 
 U64 = (1 << 64) - 1
@@ -100,6 +108,7 @@ class Params:
     probe_mode: str = "stratified"   # "stratified" | "random" | "uniform" (Table 4)
     fit_family: str = "full"         # "full" | "mean" | "scalar" | "diag" (App. D.4)
     out_rank: int = 0                # rank of the output truncation (App. D.3); 0: none
+    partition_mode: str = "response"  # "response" | "semantic" | "key_response" (Sec. 3.1, Table 2)
 
 
 # --------------------------------------------------------------------------- RNG
@@ -608,6 +617,26 @@ def correct(O_sp: np.ndarray, fit: Dict) -> np.ndarray:
     return O_sp + fit["muR"] + ((O_sp - fit["muX"]) / fit["sd"]) @ fit["B"]
 
 
+def affine_representability(O_sp: np.ndarray, O_dense: np.ndarray, tol: float = 1e-10) -> Dict:
+    """Oracle affine fit of App. D.5: the residual R = O_dense - O_sp of the given rows regressed
+    on the features [1, O_sp] with all rows fitted.  Least squares through an SVD of the centred
+    sparse outputs with columns scaled to unit norm, singular values at or below tol times the
+    largest dropped; the residual mean is the intercept.  Returns the residual energy |R|^2, the
+    remaining energy |R - R_hat|^2 and the explained fraction 1 - remaining / energy."""
+    X = np.asarray(O_sp, dtype=np.float64)
+    R = np.asarray(O_dense, dtype=np.float64) - X
+    Xc = X - X.mean(axis=0)
+    Rc = R - R.mean(axis=0)
+    scale = np.linalg.norm(Xc, axis=0)
+    scale[scale == 0.0] = 1.0
+    U, S, _ = np.linalg.svd(Xc / scale, full_matrices=False)
+    keep = S > tol * S[0] if S.size and S[0] > 0 else np.zeros(S.shape, dtype=bool)
+    Uk = U[:, keep]
+    remaining = float(((Rc - Uk @ (Uk.T @ Rc)) ** 2).sum())
+    energy = float((R ** 2).sum())
+    return dict(energy=energy, remaining=remaining, explained=1.0 - remaining / energy if energy > 0 else 1.0)
+
+
 def relative_error(O: np.ndarray, O_dense: np.ndarray) -> np.ndarray:
     """Per-row |O_i - O_i^dense|_2 / (|O_i^dense|_2 + 1e-8) (caption of Table D.1)."""
     O = np.asarray(O, dtype=np.float64)
@@ -619,34 +648,42 @@ def relative_error(O: np.ndarray, O_dense: np.ndarray) -> np.ndarray:
 def kv_side(qs: Sequence, k, v, p: Params, kv_head: int = 0, warm: Optional[Dict] = None) -> Dict:
     """The K/V side of one K/V head (Sec. 4.1, 4.2): key metric from the query rows of the heads
     in ``qs`` (one head, or the G heads that share this K/V head), key factor, K/V k-means, group
-    statistics, query metric and query factor.  The k-means stream is that of ``kv_head``."""
+    statistics, query metric and query factor.  The k-means stream is that of ``kv_head``.
+    ``p.partition_mode`` "semantic" clusters the raw keys instead (no metric or factor, Sec. 3.1);
+    the query metric and factor are formed in "response" mode only, the one whose query
+    coordinates use them."""
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     N, d = k.shape
     Nv = N - p.n_text
     kv, vv = k[:Nv], v[:Nv]
     qvs = [np.asarray(q, dtype=np.float64)[:Nv] for q in qs]
-    MK = key_metric(qvs[0], p.Ms) if len(qvs) == 1 else key_metric_shared(qvs, p.Ms)
     warm_ok = []
-    if warm is None:
-        FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
+    MK = FK = wK = None
+    if p.partition_mode == "semantic":
+        phiK = kv.copy()
+        feature_map = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
     else:
-        FK, ok = metric_factor_warm(MK, warm["FK"], p.rK, p.eig_clamp)
-        wK = None
-        warm_ok.append(ok)
-    phiK = project(kv, FK)
-    initK = None if warm is None else warm_centres(warm["kbar"], lambda x: project(x, FK), phiK, p.Ck,
-                                                   p.seed, kv_head, 0)
+        MK = key_metric(qvs[0], p.Ms) if len(qvs) == 1 else key_metric_shared(qvs, p.Ms)
+        if warm is None:
+            FK, wK = metric_factor(MK, p.rK, p.eig_clamp)
+        else:
+            FK, ok = metric_factor_warm(MK, warm["FK"], p.rK, p.eig_clamp)
+            warm_ok.append(ok)
+        phiK = project(kv, FK)
+        feature_map = lambda x: project(x, FK)  # noqa: E731
+    initK = None if warm is None else warm_centres(warm["kbar"], feature_map, phiK, p.Ck, p.seed, kv_head, 0)
     km = kmeans(phiK, p.Ck, p.seed, kv_head, 0, p.max_iters, p.tol, init=initK)
     kv_lab, nkv = compact_labels(km["labels"], p.Ck)
     kv_size, kbar, vbar = key_group_stats(kv, vv, kv_lab, nkv)
-    MQ = query_metric(kbar)
-    if warm is None:
-        FQ, wQ = metric_factor(MQ, p.rQ, p.eig_clamp)
-    else:
-        FQ, ok = metric_factor_warm(MQ, warm["FQ"], p.rQ, p.eig_clamp)
-        wQ = None
-        warm_ok.append(ok)
+    MQ = FQ = wQ = None
+    if p.partition_mode == "response":
+        MQ = query_metric(kbar)
+        if warm is None:
+            FQ, wQ = metric_factor(MQ, p.rQ, p.eig_clamp)
+        else:
+            FQ, ok = metric_factor_warm(MQ, warm["FQ"], p.rQ, p.eig_clamp)
+            warm_ok.append(ok)
     return dict(MK=MK, FK=FK, wK=wK, phiK=phiK, kmK=km, kv_label=kv_lab, n_kv=nkv, kv_size=kv_size,
                 kbar=kbar, vbar=vbar, MQ=MQ, FQ=FQ, wQ=wQ, warm_ok=warm_ok)
 
@@ -665,9 +702,13 @@ def query_side(q, k, v, kvs: Dict, p: Params, head: int = 0, rows: Optional[Sequ
     qv, kv, vv = q[:Nv], k[:Nv], v[:Nv]
     FQ, kv_lab, kv_size = kvs["FQ"], kvs["kv_label"], kvs["kv_size"]
     out: Dict = dict(kvs)
-    phiQ = query_coords(qv, FQ, p.rms_eps)
-    initQ = None if warm is None else warm_centres(warm["qbar"], lambda x: query_coords(x, FQ, p.rms_eps),
-                                                   phiQ, p.Cq, p.seed, head, 1)
+    if p.partition_mode == "response":
+        phiQ = query_coords(qv, FQ, p.rms_eps)
+        feature_map = lambda x: query_coords(x, FQ, p.rms_eps)  # noqa: E731
+    else:  # semantic query groups: k-means on the raw queries (Sec. 3.1)
+        phiQ = qv.copy()
+        feature_map = lambda x: np.asarray(x, dtype=np.float64)  # noqa: E731
+    initQ = None if warm is None else warm_centres(warm["qbar"], feature_map, phiQ, p.Cq, p.seed, head, 1)
     qm = kmeans(phiQ, p.Cq, p.seed, head, 1, p.max_iters, p.tol, init=initQ)
     q_lab, nq = compact_labels(qm["labels"], p.Cq)
     q_size, qbar, cbar, dist = query_group_stats(qv, phiQ, q_lab, nq)

@@ -770,3 +770,75 @@ def test_gqa_kv_side_does_not_depend_on_the_order_of_the_query_heads():
     # and the shared partition is not that of either head alone
     alone = O.sparsepr_head(q, k, v, p, head=1, full=False)
     assert not np.allclose(a[0]["MK"], alone["MK"])
+
+
+# ------------------------------------------------------------------ semantic partition, D.5
+def _two_block_problem(seed, N=256, d=16):
+    """Queries live in the first d/2 coordinates; the keys carry two far-apart clusters in the
+    last d/2 coordinates, which no query sees."""
+    rng = _rng(seed)
+    h = d // 2
+    q = np.zeros((N, d))
+    q[:, :h] = rng.standard_normal((N, h))
+    k = np.zeros((N, d))
+    k[:, :h] = rng.standard_normal((N, h))
+    cl = rng.integers(0, 2, N)
+    k[:, h:] = np.where(cl[:, None] == 1, 50.0, -50.0) + 0.1 * rng.standard_normal((N, h))
+    v = rng.standard_normal((N, d))
+    return q, k, v, cl
+
+
+def test_semantic_partition_clusters_the_raw_keys():
+    # Sec. 3.1: raw k-means follows the key clusters the queries cannot see; the response
+    # coordinates k F_K (F_K spans the query subspace) do not see them
+    q, k, v, cl = _two_block_problem(96)
+    base = dict(Ck=2, Cq=4, rK=4, rQ=4, Ms=256, M=8, rho=0.5, lam=1.0, seed=1, max_iters=30, tol=0.0)
+    sem = O.sparsepr_head(q, k, v, O.Params(**base, partition_mode="semantic"), full=False)
+    lab = sem["kv_label"]
+    assert sem["n_kv"] == 2 and (np.array_equal(lab, cl) or np.array_equal(lab, 1 - cl))
+    assert sem["FK"] is None and sem["FQ"] is None
+    resp = O.sparsepr_head(q, k, v, O.Params(**base), full=False)
+    assert np.abs(resp["FK"][8:]).max() < 1e-12             # the factor ignores the hidden block
+    assert not (np.array_equal(resp["kv_label"], cl) or np.array_equal(resp["kv_label"], 1 - cl))
+
+
+def test_key_response_variant_combines_the_two_partitions():
+    # Table 2: the key-response variant changes only the K/V grouping of the semantic partition
+    q, k, v = _rng(97).standard_normal((3, 256, 16))
+    base = dict(Ck=10, Cq=8, rK=6, rQ=8, Ms=256, M=8, rho=0.4, lam=1.0, seed=3, max_iters=30, tol=0.0)
+    sem = O.sparsepr_head(q, k, v, O.Params(**base, partition_mode="semantic"), full=False)
+    resp = O.sparsepr_head(q, k, v, O.Params(**base), full=False)
+    mix = O.sparsepr_head(q, k, v, O.Params(**base, partition_mode="key_response"), full=False)
+    assert np.array_equal(mix["kv_label"], resp["kv_label"])
+    assert np.array_equal(mix["q_label"], sem["q_label"])
+    assert mix["FQ"] is None
+    # raw query coordinates: the probe distances are plain distances to the group means of q
+    qb = mix["qbar"][mix["q_label"]]
+    np.testing.assert_allclose(mix["qdist"], np.linalg.norm(q - qb, axis=1), rtol=1e-12)
+
+
+def test_affine_representability_limits():
+    rng = _rng(98)
+    X = rng.standard_normal((300, 6))
+    A, b = rng.standard_normal((6, 6)), rng.standard_normal(6)
+    # a residual that is exactly affine in O_sp is fully explained
+    out = O.affine_representability(X, X + X @ A + b)
+    assert out["explained"] > 1 - 1e-12 and out["remaining"] < 1e-20 * out["energy"]
+    # against least squares on [1, X] (full rank)
+    R = rng.standard_normal((300, 6))
+    out = O.affine_representability(X, X + R)
+    F = np.hstack([np.ones((300, 1)), X])
+    coef = np.linalg.lstsq(F, R, rcond=None)[0]
+    np.testing.assert_allclose(out["remaining"], ((R - F @ coef) ** 2).sum(), rtol=1e-10)
+    np.testing.assert_allclose(out["energy"], (R ** 2).sum(), rtol=1e-14)
+    # a duplicated feature column adds nothing (the tolerance drops the null direction), and
+    # column scaling does not change the fit
+    Xd = np.hstack([X, X[:, :1]])
+    Rd = rng.standard_normal((300, 7))
+    a = O.affine_representability(Xd, Xd + Rd)
+    Fd = np.hstack([np.ones((300, 1)), X])
+    cd = np.linalg.lstsq(Fd, Rd, rcond=None)[0]
+    np.testing.assert_allclose(a["remaining"], ((Rd - Fd @ cd) ** 2).sum(), rtol=1e-9)
+    Xs = X * np.array([1e3, 1e-3, 1, 2, 5, 7])
+    b2 = O.affine_representability(Xs, Xs + R)
+    np.testing.assert_allclose(b2["remaining"], out["remaining"], rtol=1e-9)
