@@ -13,8 +13,9 @@ static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   Workspace L = {};
   const size_t BH = size_t(desc.B) * desc.H, d = desc.d, Nv = size_t(desc.N - desc.n_text);
+  const int rK = kv_coord_rank(p, int(d)), rQ = q_coord_rank(p, int(d));
   L.Cmax = p.Ck > p.Cq ? p.Ck : p.Cq;
-  L.rmax = p.rK > p.rQ ? p.rK : p.rQ;
+  L.rmax = rK > rQ ? rK : rQ;
   L.nblk = int((Nv + kAssignThreads - 1) / kAssignThreads);
   L.splits = kProbeSplits;
   size_t o = 0;
@@ -25,12 +26,12 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   };
   L.metric = take(BH * d * d * 8);
   L.ktilde = take(BH * p.Ck * d * 8);
-  L.phiK = take(BH * Nv * p.rK * 8);
-  L.phiQ = take(BH * Nv * p.rQ * 8);
+  L.phiK = take(BH * Nv * rK * 8);
+  L.phiQ = take(BH * Nv * rQ * 8);
   L.km_cent = take(BH * L.Cmax * L.rmax * 8);
   L.km_lab = take(BH * Nv * 4);
   L.km_region = take(kmeans_ws_bytes(int(BH), int(Nv), L.Cmax, L.rmax));
-  L.cbar = take(BH * p.Cq * p.rQ * 8);
+  L.cbar = take(BH * p.Cq * rQ * 8);
   L.vstat = take(BH * Nv * 2 * 8);
   L.gstat = take(2 * BH * 8 * 4);  // per query head, then per K/V head
   L.pstat = take(BH * p.Cq * 2 * 4);
@@ -89,9 +90,12 @@ static spr_status check_params(const spr_desc* d, const spr_part_params* p) {
   const int Nv = d->N - d->n_text;
   if (p->Ck < 1 || p->Cq < 1 || p->Ck > 1024 || p->Cq > 1024 || p->Ck > Nv || p->Cq > Nv) return SPR_EINVAL;
   if (p->rK < 1 || p->rQ < 1 || p->rK > d->d || p->rQ > d->d) return SPR_EINVAL;
-  if (!kmeans_rank_supported(p->rK) || !kmeans_rank_supported(p->rQ)) return SPR_EUNSUPPORTED;
+  // response ranks up to 64 (the projection's tiles); rank 128 only for raw coordinates
+  if (p->rK > 64 || p->rQ > 64 || !kmeans_rank_supported(p->rK) || !kmeans_rank_supported(p->rQ))
+    return SPR_EUNSUPPORTED;
   if (p->Ms < 1 || p->max_iters < 1) return SPR_EINVAL;
   if (!(p->tol >= 0.0) || !(p->rms_eps > 0.0) || !(p->eig_clamp >= 0.0)) return SPR_EINVAL;
+  if (p->mode < SPR_PART_RESPONSE || p->mode > SPR_PART_KEY_RESPONSE || p->reserved != 0) return SPR_EINVAL;
   return SPR_OK;
 }
 
@@ -241,7 +245,7 @@ spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* 
 }
 
 size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C) {
-  if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || r < 1 || r > 64) return 0;
+  if (BH < 1 || n < 1 || C < 1 || C > n || C > 1024 || !kmeans_rank_supported(r)) return 0;
   return kmeans_ws_bytes(BH, n, C, r);
 }
 

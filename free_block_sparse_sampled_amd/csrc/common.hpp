@@ -74,6 +74,10 @@ inline HeadGeom make_geom(const spr_desc& d) {
   return g;
 }
 
+// Ranks of the k-means coordinates of a partition mode: raw activations have rank d.
+inline int kv_coord_rank(const spr_part_params& p, int d) { return p.mode == SPR_PART_SEMANTIC ? d : p.rK; }
+inline int q_coord_rank(const spr_part_params& p, int d) { return p.mode == SPR_PART_RESPONSE ? p.rQ : d; }
+
 // Grouped-query attention: Hkv K/V heads, each shared by G = H / Hkv query heads (query head hd
 // of the flattened index uses K/V head hd / G).
 inline bool is_gqa(const spr_desc& d) { return d.Hkv > 0 && d.Hkv < d.H; }

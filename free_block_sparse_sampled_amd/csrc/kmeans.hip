@@ -26,10 +26,14 @@ namespace spr {
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int RP = 64;        // coordinates padded for the MFMA screening
+// Coordinates are padded to RP = 64 (ranks up to 64) or 128 (rank 128, the raw 128-dimensional
+// activations of the semantic partition) for the MFMA screening; the mean point is stored with
+// stride RPMAX whatever the padding.
+constexpr int RPMAX = 128;
 constexpr int KC = 256;       // centres per LDS chunk
-constexpr int CROW = RP + 8;  // LDS row stride in fp16 elements (keeps 16-row reads conflict free)
 constexpr int CTRL = 8;       // doubles of control word per head
+__host__ __device__ constexpr int crow(int rp) { return rp + 8; }  // LDS row stride (fp16), conflict free
+__host__ __device__ constexpr int rpad(int r) { return r > 64 ? 128 : 64; }
 
 enum { C_DONE = 0, C_PASSES = 1, C_JPREV = 2, C_CMAX = 3, C_SCALE = 4, C_AMAX = 5, C_STOPNOW = 6 };
 
@@ -40,18 +44,20 @@ __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast
 // bit pattern, monotone for non-negative doubles); km_stats_final_kernel divides and scales.
 __global__ void km_stats_zero_kernel(double* __restrict__ mu, double* __restrict__ ctrl, int BH) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < BH * RP) mu[i] = 0.0;
+  if (i < BH * RPMAX) mu[i] = 0.0;
   if (i < BH) ctrl[i * CTRL + C_AMAX] = 0.0;
 }
 
 __global__ __launch_bounds__(256) void km_point_stats_kernel(const double* __restrict__ feat, int n, int r,
                                                              double* __restrict__ mu, double* __restrict__ ctrl) {
   __shared__ double ssum[256], smax[256];
-  const int hd = blockIdx.y, t = threadIdx.x, e = t & 63, r0 = t >> 6;
+  // EW threads per row (one coordinate each), 256 / EW rows at a time
+  const int EW = r > 64 ? 128 : 64, NR = 256 / EW;
+  const int hd = blockIdx.y, t = threadIdx.x, e = t % EW, r0 = t / EW;
   const int j0 = int(int64_t(n) * blockIdx.x / gridDim.x), j1 = int(int64_t(n) * (blockIdx.x + 1) / gridDim.x);
   double s = 0.0, m = 0.0;
   if (e < r)
-    for (int j = j0 + r0; j < j1; j += 4) {
+    for (int j = j0 + r0; j < j1; j += NR) {
       const double x = feat[(size_t(hd) * n + j) * r + e];
       s += x;
       m = fmax(m, fabs(x));
@@ -59,10 +65,13 @@ __global__ __launch_bounds__(256) void km_point_stats_kernel(const double* __res
   ssum[t] = s;
   smax[t] = m;
   __syncthreads();
+  if (t < EW) {
+    double tot = 0.0;
+    for (int q = 0; q < NR; ++q) tot += ssum[t + q * EW];
+    if (t < r) atomicAdd(mu + size_t(hd) * RPMAX + t, tot);
+  }
   if (t < 64) {
-    const double tot = ssum[t] + ssum[t + 64] + ssum[t + 128] + ssum[t + 192];
     double mx = fmax(fmax(smax[t], smax[t + 64]), fmax(smax[t + 128], smax[t + 192]));
-    if (t < r) atomicAdd(mu + size_t(hd) * RP + t, tot);
     for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
     if (t == 0)
       atomicMax(reinterpret_cast<unsigned long long*>(ctrl + hd * CTRL + C_AMAX),
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void km_point_stats_kernel(const double* __res
 
 __global__ void km_stats_final_kernel(double* __restrict__ mu, double* __restrict__ ctrl, int n) {
   const int hd = blockIdx.x, e = threadIdx.x;
-  mu[size_t(hd) * RP + e] /= double(n);
+  mu[size_t(hd) * RPMAX + e] /= double(n);
   if (e == 0) {
     const double amax = ctrl[hd * CTRL + C_AMAX];
     double sc = 1.0;
@@ -81,15 +90,17 @@ __global__ void km_stats_final_kernel(double* __restrict__ mu, double* __restric
   }
 }
 
-// Scaled, centred fp16 hi/lo parts of every point and their norms.  8 lanes per point.
+// Scaled, centred fp16 hi/lo parts of every point and their norms.  RP / 8 lanes per point.
+template <int RP>
 __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __restrict__ feat, int n, int r,
                                                             const double* __restrict__ mu,
                                                             const double* __restrict__ ctrl,
                                                             _Float16* __restrict__ xh, _Float16* __restrict__ xl,
                                                             float* __restrict__ xnrm) {
+  constexpr int LP = RP / 8;
   const int hd = blockIdx.y;
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int j = idx >> 3, cb = idx & 7;
+  const int j = idx / LP, cb = idx % LP;
   const bool valid = j < n;
   const double sc = ctrl[hd * CTRL + C_SCALE];
   double nrm = 0.0;
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __rest
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = cb * 8 + u;
-      const double x = e < r ? (feat[(size_t(hd) * n + j) * r + e] - mu[size_t(hd) * RP + e]) * sc : 0.0;
+      const double x = e < r ? (feat[(size_t(hd) * n + j) * r + e] - mu[size_t(hd) * RPMAX + e]) * sc : 0.0;
       const _Float16 h = _Float16(float(x));
       hv[u] = h;
       lv[u] = _Float16(float(x - double(h)));
@@ -109,14 +120,14 @@ __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __rest
     *reinterpret_cast<f16x8_t*>(xl + (size_t(hd) * n + j) * RP + cb * 8) =
         f16x8_t{lv[0], lv[1], lv[2], lv[3], lv[4], lv[5], lv[6], lv[7]};
   }
-  nrm += __shfl_xor(nrm, 1);
-  nrm += __shfl_xor(nrm, 2);
-  nrm += __shfl_xor(nrm, 4);
+#pragma unroll
+  for (int o = 1; o < LP; o <<= 1) nrm += __shfl_xor(nrm, o);
   if (valid && cb == 0) xnrm[size_t(hd) * n + j] = float(sqrt(nrm));
 }
 
 // fp16 split of the centres (same centring and scale as the points), their squared norms and
 // the largest norm.  Element-parallel over the whole block of one head; n2s is LDS [C].
+template <int RP>
 __device__ void prep_centres(int hd, int C, int r, const double* __restrict__ cent, const double* __restrict__ mu,
                              double sc, _Float16* __restrict__ ch, _Float16* __restrict__ cl,
                              float* __restrict__ cn2, double* __restrict__ ctrl, double* n2s, double* red) {
@@ -124,7 +135,7 @@ __device__ void prep_centres(int hd, int C, int r, const double* __restrict__ ce
   __syncthreads();
   for (int idx = threadIdx.x; idx < C * RP; idx += blockDim.x) {
     const int m = idx / RP, e = idx % RP;
-    const double x = e < r ? (cent[(size_t(hd) * C + m) * r + e] - mu[size_t(hd) * RP + e]) * sc : 0.0;
+    const double x = e < r ? (cent[(size_t(hd) * C + m) * r + e] - mu[size_t(hd) * RPMAX + e]) * sc : 0.0;
     const _Float16 h = _Float16(float(x));
     ch[(size_t(hd) * C + m) * RP + e] = h;
     cl[(size_t(hd) * C + m) * RP + e] = _Float16(float(x - double(h)));
@@ -149,6 +160,7 @@ __device__ void prep_centres(int hd, int C, int r, const double* __restrict__ ce
 
 // Initial centres: C feature rows drawn uniformly with replacement by SplitMix64,
 // counter ((head * 2 + stage) << 20) + m (App. C.1).
+template <int RP>
 __global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict__ feat, int n, int r, int C,
                                                       uint64_t seed, int stage, const double* __restrict__ mu,
                                                       double* __restrict__ cent, double* __restrict__ sums,
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict_
   }
   for (int m = threadIdx.x; m < C; m += blockDim.x) cnt[size_t(hd) * C + m] = 0;
   __syncthreads();
-  prep_centres(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, n2s, red);
+  prep_centres<RP>(hd, C, r, cent, mu, ctrl[hd * CTRL + C_SCALE], ch, cl, cn2, ctrl, n2s, red);
   if (threadIdx.x == 0) {
     ctrl[hd * CTRL + C_DONE] = 0.0;
     ctrl[hd * CTRL + C_PASSES] = 0.0;
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict_
 // Screening pass.  A wave owns 64 points (4 tiles of 16); centres stream through LDS in
 // chunks of 256.  The MFMA computes D^T tiles (16 centres x 16 points), so a lane holds four
 // centres of one point and keeps that point's best value, its index and the second best.
-template <int KS>
+template <int KS, int RP>
 __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Float16* __restrict__ xh,
                                                         const _Float16* __restrict__ xl,
                                                         const float* __restrict__ xnrm,
@@ -191,6 +203,7 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
                                                         const float* __restrict__ cn2,
                                                         const double* __restrict__ ctrl, int* __restrict__ lab_new,
                                                         int* __restrict__ rq_count, int* __restrict__ rq_list) {
+  constexpr int CROW = crow(RP);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   _Float16* Ch = reinterpret_cast<_Float16*>(smem);
   _Float16* Cl = Ch + KC * CROW;
@@ -307,12 +320,16 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
 }
 
 // fp64 nearest centre of every queued point, one wave per point (ties to the lowest index).
+// The point sits in registers for ranks up to 64 and in the wave's LDS row (broadcast reads)
+// for rank 128.
 template <int R>
 __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const double* __restrict__ feat,
                                                         const double* __restrict__ cent,
                                                         const double* __restrict__ ctrl,
                                                         const int* __restrict__ rq_count,
                                                         const int* __restrict__ rq_list, int* __restrict__ lab_new) {
+  constexpr bool INLDS = R > 64;
+  __shared__ double xs[INLDS ? 4 * R : 1];
   const int hd = blockIdx.y;
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int cnt = rq_count[hd];
@@ -321,9 +338,17 @@ __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const doub
   for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < cnt; i += nw) {
     const int j = rq_list[size_t(hd) * n + i];
     const double* f = feat + (size_t(hd) * n + j) * R;
-    double x[R];
+    double xr[INLDS ? 1 : R];
+    double* xw = xs + (INLDS ? (threadIdx.x >> 6) * R : 0);
+    if constexpr (INLDS) {
+      __builtin_amdgcn_wave_barrier();
+      for (int e = lane; e < R; e += 64) xw[e] = f[e];
+      __builtin_amdgcn_wave_barrier();
+    } else {
 #pragma unroll
-    for (int e = 0; e < R; ++e) x[e] = f[e];
+      for (int e = 0; e < R; ++e) xr[e] = f[e];
+    }
+    const double* x = INLDS ? xw : xr;
     double best = INFINITY;
     int bi = 0;
     for (int m = lane; m < C; m += 64) {
@@ -374,34 +399,57 @@ __global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict_
     changed = (*lp != lab);
     *lp = lab;
   }
+  // EPL coordinates per lane: lane + 64 q, q < EPL
+  constexpr int EPL = (R + 63) / 64;
   const int lane = threadIdx.x & 63;
   const int wbase = blockIdx.x * 256 + (threadIdx.x & ~63);
   const int L = valid ? lab : -1;
   int cur = __shfl(L, 0);
-  double acc = 0.0, jsq = 0.0;
-  double cc = (lane < R && cur >= 0) ? cent[(size_t(hd) * C + cur) * R + lane] : 0.0;
+  double acc[EPL], cc[EPL], jsq = 0.0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    const int e = lane + 64 * q;
+    acc[q] = 0.0;
+    cc[q] = (e < R && cur >= 0) ? cent[(size_t(hd) * C + cur) * R + e] : 0.0;
+  }
   int run = 0;
   for (int p = 0; p < 64; ++p) {
     const int Lp = __shfl(L, p);
     if (Lp < 0) break;
     if (Lp != cur) {
-      if (lane < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + lane, acc);
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const int e = lane + 64 * q;
+        if (e < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + e, acc[q]);
+        acc[q] = 0.0;
+      }
       if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
-      acc = 0.0;
       run = 0;
       cur = Lp;
-      if (lane < R) cc = cent[(size_t(hd) * C + cur) * R + lane];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const int e = lane + 64 * q;
+        if (e < R) cc[q] = cent[(size_t(hd) * C + cur) * R + e];
+      }
     }
-    if (lane < R) {
-      const double x = feat[(size_t(hd) * n + wbase + p) * R + lane];
-      acc += x;
-      const double t = x - cc;
-      jsq = fma(t, t, jsq);
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int e = lane + 64 * q;
+      if (e < R) {
+        const double x = feat[(size_t(hd) * n + wbase + p) * R + e];
+        acc[q] += x;
+        const double t = x - cc[q];
+        jsq = fma(t, t, jsq);
+      }
     }
     ++run;
   }
   if (run > 0) {
-    if (lane < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + lane, acc);
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int e = lane + 64 * q;
+      if (e < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + e, acc[q]);
+    }
     if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
   }
   const double jsum = block_sum_d(jsq, red);
@@ -444,6 +492,7 @@ __global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double to
 // Centre update (members' mean; empty centres stay), reset of the sums, and the fp16 split of
 // the new centres for the next screening pass.  64 centres per block, one wave per centre row
 // at a time; the largest centre norm is combined with atomicMax on its (non-negative) bits.
+template <int RP>
 __global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __restrict__ cent,
                                                         double* __restrict__ sums, int* __restrict__ cnt,
                                                         double* __restrict__ ctrl, const double* __restrict__ mu,
@@ -458,21 +507,29 @@ __global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __
   for (int m = blockIdx.x * 64 + w; m < min(C, blockIdx.x * 64 + 64); m += 4) {
     const size_t base = (size_t(hd) * C + m);
     const int k = cnt[base];
-    double x = 0.0;
-    if (lane < r) {
-      double c = cent[base * r + lane];
-      if (!stop && k > 0) {
-        c = sums[base * r + lane] / double(k);
-        cent[base * r + lane] = c;
+    double n2l = 0.0;
+#pragma unroll
+    for (int q = 0; q < RP / 64; ++q) {
+      const int e = lane + 64 * q;
+      double x = 0.0;
+      if (e < r) {
+        double c = cent[base * r + e];
+        if (!stop && k > 0) {
+          c = sums[base * r + e] / double(k);
+          cent[base * r + e] = c;
+        }
+        sums[base * r + e] = 0.0;
+        x = (c - mu[size_t(hd) * RPMAX + e]) * sc;
       }
-      sums[base * r + lane] = 0.0;
-      x = (c - mu[size_t(hd) * RP + lane]) * sc;
+      if (!stop) {
+        const _Float16 h = _Float16(float(x));
+        ch[base * RP + e] = h;
+        cl[base * RP + e] = _Float16(float(x - double(h)));
+        n2l = fma(x, x, n2l);
+      }
     }
     if (!stop) {
-      const _Float16 h = _Float16(float(x));
-      ch[base * RP + lane] = h;
-      cl[base * RP + lane] = _Float16(float(x - double(h)));
-      const double n2 = wave_sum_d(x * x);
+      const double n2 = wave_sum_d(n2l);
       if (lane == 0) cn2[base] = float(n2);
       cmax = fmax(cmax, sqrt(n2));
     }
@@ -496,7 +553,7 @@ void launch_copy_passes(const double* ctrl, int BH, int* passes, int stride, int
   hipLaunchKernelGGL(copy_passes1_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, ctrl, BH, passes, stride, slot);
 }
 
-bool kmeans_rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 48 || r == 64; }
+bool kmeans_rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 48 || r == 64 || r == 128; }
 
 size_t kmeans_ws_bytes(int BH, int n, int C, int rmax) {
   size_t o = 0;
@@ -508,7 +565,8 @@ size_t kmeans_ws_bytes(int BH, int n, int C, int rmax) {
   take(size_t(BH) * nblk * 8);      // cost partials
   take(size_t(BH) * nblk * 4);      // change partials
   take(size_t(BH) * CTRL * 8);      // control words
-  take(size_t(BH) * RP * 8);        // mean point
+  const int RP = rpad(rmax);
+  take(size_t(BH) * RPMAX * 8);     // mean point
   take(size_t(BH) * n * RP * 2);    // point hi
   take(size_t(BH) * n * RP * 2);    // point lo
   take(size_t(BH) * n * 4);         // point norms
@@ -536,7 +594,8 @@ KmArgs kmeans_carve(void* ws, int BH, int n, int C, int rmax) {
   a.jpart = reinterpret_cast<double*>(take(size_t(BH) * nblk * 8));
   a.cpart = reinterpret_cast<int*>(take(size_t(BH) * nblk * 4));
   a.ctrl = reinterpret_cast<double*>(take(size_t(BH) * CTRL * 8));
-  a.mu = reinterpret_cast<double*>(take(size_t(BH) * RP * 8));
+  const int RP = rpad(rmax);
+  a.mu = reinterpret_cast<double*>(take(size_t(BH) * RPMAX * 8));
   a.xh = take(size_t(BH) * n * RP * 2);
   a.xl = take(size_t(BH) * n * RP * 2);
   a.xnrm = reinterpret_cast<float*>(take(size_t(BH) * n * 4));
@@ -555,33 +614,42 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
   _Float16* xl = reinterpret_cast<_Float16*>(a.xl);
   _Float16* ch = reinterpret_cast<_Float16*>(a.ch);
   _Float16* cl = reinterpret_cast<_Float16*>(a.cl);
-  constexpr int KS = (R + 31) / 32;
-  const size_t sm = size_t(2) * KC * CROW * sizeof(_Float16) + KC * sizeof(float);
-  allow_lds(km_screen_kernel<KS>, sm);
-  hipLaunchKernelGGL(km_screen_kernel<KS>, dim3(ceil_div(a.n, 256), a.BH), dim3(256), sm, st, a.n, a.C, xh, xl, a.xnrm,
-                     ch, cl, a.cn2, a.ctrl, a.lab_new, a.rq_count, a.rq_list);
+  constexpr int KS = (R + 31) / 32, RP = rpad(R);
+  const size_t sm = size_t(2) * KC * crow(RP) * sizeof(_Float16) + KC * sizeof(float);
+  allow_lds(km_screen_kernel<KS, RP>, sm);
+  hipLaunchKernelGGL((km_screen_kernel<KS, RP>), dim3(ceil_div(a.n, 256), a.BH), dim3(256), sm, st, a.n, a.C, xh, xl,
+                     a.xnrm, ch, cl, a.cn2, a.ctrl, a.lab_new, a.rq_count, a.rq_list);
   hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(16, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
                      a.rq_count, a.rq_list, a.lab_new);
   hipLaunchKernelGGL(km_accum_kernel<R>, dim3(a.nblk, a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent, a.lab_new,
                      a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
   hipLaunchKernelGGL(km_decide_kernel, dim3(a.BH), dim3(256), 0, st, a.max_iters, a.tol, a.nblk, a.jpart, a.cpart,
                      a.ctrl);
-  hipLaunchKernelGGL(km_update_kernel, dim3(ceil_div(a.C, 64), a.BH), dim3(256), 0, st, a.C, a.r, a.cent, a.sums,
-                     a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
+  hipLaunchKernelGGL(km_update_kernel<RP>, dim3(ceil_div(a.C, 64), a.BH), dim3(256), 0, st, a.C, a.r, a.cent,
+                     a.sums, a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
+}
+
+template <int RP>
+static void launch_prep(const KmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(km_point_prep_kernel<RP>, dim3(ceil_div(a.n * (RP / 8), 256), a.BH), dim3(256), 0, st, a.feat,
+                     a.n, a.r, a.mu, a.ctrl, reinterpret_cast<_Float16*>(a.xh), reinterpret_cast<_Float16*>(a.xl),
+                     a.xnrm);
+  hipLaunchKernelGGL(km_init_kernel<RP>, dim3(a.BH), dim3(1024), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
+                     a.cent, a.sums, a.cnt, a.ctrl, reinterpret_cast<_Float16*>(a.ch),
+                     reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count, a.cent_given ? 1 : 0);
 }
 
 spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(km_stats_zero_kernel, dim3(ceil_div(a.BH * RP, 256)), dim3(256), 0, st, a.mu, a.ctrl, a.BH);
+  if (!kmeans_rank_supported(a.r)) return SPR_EUNSUPPORTED;
+  hipLaunchKernelGGL(km_stats_zero_kernel, dim3(ceil_div(a.BH * RPMAX, 256)), dim3(256), 0, st, a.mu, a.ctrl, a.BH);
   hipLaunchKernelGGL(km_point_stats_kernel, dim3(64, a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.mu, a.ctrl);
-  hipLaunchKernelGGL(km_stats_final_kernel, dim3(a.BH), dim3(RP), 0, st, a.mu, a.ctrl, a.n);
-  hipLaunchKernelGGL(km_point_prep_kernel, dim3(ceil_div(a.n * 8, 256), a.BH), dim3(256), 0, st, a.feat, a.n, a.r,
-                     a.mu, a.ctrl, reinterpret_cast<_Float16*>(a.xh), reinterpret_cast<_Float16*>(a.xl), a.xnrm);
-  hipLaunchKernelGGL(km_init_kernel, dim3(a.BH), dim3(1024), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
-                     a.cent, a.sums, a.cnt, a.ctrl, reinterpret_cast<_Float16*>(a.ch),
-                     reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count, a.cent_given ? 1 : 0);
+  hipLaunchKernelGGL(km_stats_final_kernel, dim3(a.BH), dim3(RPMAX), 0, st, a.mu, a.ctrl, a.n);
+  if (a.r > 64) launch_prep<128>(a, st);
+  else launch_prep<64>(a, st);
   SPR_CHECK_LAUNCH();
   for (int it = 0; it < a.max_iters; ++it) {
     switch (a.r) {
+      case 128: launch_pass<128>(a, st); break;
       case 64: launch_pass<64>(a, st); break;
       case 48: launch_pass<48>(a, st); break;
       case 32: launch_pass<32>(a, st); break;

@@ -937,8 +937,9 @@ __global__ __launch_bounds__(256) void group_mean_kernel(const void* __restrict_
   }
 }
 
-// c_a = mean of phi_Q over group a (App. A.2), members listed by perm.  One wave per group: each
-// half-wave reads a member row as 16-byte pairs, two rows per step, four steps in flight.
+// c_a = mean of phi_Q over group a (App. A.2), members listed by perm.  One wave per group and
+// block of 64 columns: each half-wave reads a member row as 16-byte pairs, two rows per step,
+// four steps in flight.
 __global__ __launch_bounds__(256) void group_mean_perm_kernel(const double* __restrict__ feat, int n, int r,
                                                               const int* __restrict__ perm,
                                                               const int* __restrict__ off,
@@ -947,7 +948,7 @@ __global__ __launch_bounds__(256) void group_mean_perm_kernel(const double* __re
   const int hd = blockIdx.y;
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= C || b >= ngroups[hd]) return;
-  const int half = lane >> 5, col = (lane & 31) * 2;
+  const int half = lane >> 5, col = blockIdx.z * 64 + (lane & 31) * 2;
   const bool act = col < r;
   const int r0 = off[size_t(hd) * (C + 1) + b], r1 = off[size_t(hd) * (C + 1) + b + 1];
   const int* pm = perm + size_t(hd) * n;
@@ -997,6 +998,40 @@ __global__ __launch_bounds__(256) void qdist_kernel(const double* __restrict__ f
   }
   for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (i < n && sub == 0) out[size_t(hd) * n + i] = sqrt(s);
+}
+
+// Raw activations as k-means coordinates (the semantic partition of Sec. 3.1): the video rows of
+// x widened to fp64, [BH][rows][d].  Eight consecutive elements per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void raw_rows_kernel(const void* __restrict__ x, HeadGeom g, int rows,
+                                                       double* __restrict__ out) {
+  const int hd = blockIdx.y;
+  const int64_t e8 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e8 >= int64_t(rows) * g.d) return;
+  const int row = int(e8 / g.d), c = int(e8 % g.d);
+  float v[8];
+  load8<DT>(x, g.base(hd) + int64_t(row) * g.sn + c, v);
+  double* o = out + (size_t(hd) * rows + row) * g.d + c;
+#pragma unroll
+  for (int t = 0; t < 8; t += 2) *reinterpret_cast<double2*>(o + t) = make_double2(v[t], v[t + 1]);
+}
+
+// Initial centres of a later call on raw coordinates: previous centroid m as it stands; slots
+// m >= n_prev take the cold draw of index m.
+__global__ __launch_bounds__(256) void warm_centres_raw_kernel(const double* __restrict__ prev,
+                                                               const int* __restrict__ n_prev, int C, int d,
+                                                               const double* __restrict__ feat, int n, uint64_t seed,
+                                                               int stage, double* __restrict__ cent) {
+  const int hd = blockIdx.y, m = blockIdx.x;
+  const int np = min(n_prev[hd], C);
+  const double* src;
+  if (m < np) {
+    src = prev + (size_t(hd) * C + m) * d;
+  } else {
+    const uint64_t ctr = ((uint64_t(hd) * 2ull + uint64_t(stage)) << 20) + uint64_t(m);
+    src = feat + (size_t(hd) * n + int(splitmix64(seed, ctr) % uint64_t(n))) * d;
+  }
+  for (int e = threadIdx.x; e < d; e += blockDim.x) cent[(size_t(hd) * C + m) * d + e] = src[e];
 }
 
 // Status bits of the K/V side (kvstat, per K/V head) into every query head of the group.
@@ -1059,8 +1094,14 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(zero_ints_kernel, dim3(ceil_div((BH + BHkv) * 8, 256)), dim3(256), 0, st, gstat,
                      size_t(BH + BHkv) * 8);
 
+  // Coordinates of the two k-means: response-coupled (factor products) or raw activations
+  // (semantic partition), per mode; raw coordinates have rank d.
+  const bool kv_raw = p.mode == SPR_PART_SEMANTIC, q_raw = p.mode != SPR_PART_RESPONSE;
+  const int rK = kv_coord_rank(p, d), rQ = q_coord_rank(p, d);
+  const size_t jac_smem = jacobi_smem(d);
+  allow_lds(eigen_factor_kernel, jac_smem);
   // M_K and F_K
-  {
+  if (!kv_raw) {
     const size_t kms = size_t(64) * (d + 2) * sizeof(double);
     if (d == 128) {
       allow_lds(key_metric_kernel<DT, 128>, kms);
@@ -1071,29 +1112,37 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     }
   }
   SPR_CHECK_LAUNCH();
-  const size_t jac_smem = jacobi_smem(d);
-  allow_lds(eigen_factor_kernel, jac_smem);
-  if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
-    launch_subspace(BHkv, d, p.rK, st, metric, warm->FK, p.eig_clamp, out.FK, kvstat, 2);
-  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp, out.FK,
-                     kvstat, warm ? 2 : -1);
-  SPR_CHECK_LAUNCH();
-  // phi_K = K F_K
+  if (!kv_raw) {
+    if (warm)  // later call: subspace update, the eigendecomposition only for heads it rejects
+      launch_subspace(BHkv, d, p.rK, st, metric, warm->FK, p.eig_clamp, out.FK, kvstat, 2);
+    hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rK, p.eig_clamp,
+                       out.FK, kvstat, warm ? 2 : -1);
+    SPR_CHECK_LAUNCH();
+  }
+  // phi_K = K F_K, or the raw keys
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
   const int pchunks = project_chunks(Nv, BH), kchunks = project_chunks(Nv, BHkv);
   allow_lds(project_kernel<DT, false>, prj_smem);
   allow_lds(project_kernel<DT, true>, prj_smem);
-  hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), dim3(512),
-                     prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1);
+  const dim3 rgrid(unsigned(ceil_div64(int64_t(Nv) * d / 8, 256)), BHkv), rqgrid(rgrid.x, BH);
+  if (kv_raw)
+    hipLaunchKernelGGL(raw_rows_kernel<DT>, rgrid, dim3(256), 0, st, k, gk, Nv, phiK);
+  else
+    hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), dim3(512),
+                       prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1);
   SPR_CHECK_LAUNCH();
   // K/V k-means
   KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
-  ka.BH = BHkv; ka.n = Nv; ka.r = p.rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
+  ka.BH = BHkv; ka.n = Nv; ka.r = rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
   ka.max_iters = p.max_iters; ka.tol = p.tol;
   ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
   if (warm) {
-    launch_warm_centres<false>(dim3(ceil_div(p.Ck, 64), BHkv), st, warm->kbar, warm->n_kv, p.Ck, d, out.FK, p.rK,
-                               p.rms_eps, phiK, Nv, p.seed, 0, 1, ka.cent);
+    if (kv_raw)
+      hipLaunchKernelGGL(warm_centres_raw_kernel, dim3(p.Ck, BHkv), dim3(128), 0, st, warm->kbar, warm->n_kv, p.Ck, d,
+                         phiK, Nv, p.seed, 0, ka.cent);
+    else
+      launch_warm_centres<false>(dim3(ceil_div(p.Ck, 64), BHkv), st, warm->kbar, warm->n_kv, p.Ck, d, out.FK, p.rK,
+                                 p.rms_eps, phiK, Nv, p.seed, 0, 1, ka.cent);
     SPR_CHECK_LAUNCH();
     ka.cent_given = true;
   }
@@ -1102,7 +1151,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   if (out.passes) launch_copy_passes(ka.ctrl, BHkv, out.passes, 2, 0, st);
   if (out.cK_last) {
     // centres are stored with stride rK, exactly the caller's layout
-    const size_t nel = size_t(BHkv) * p.Ck * p.rK;
+    const size_t nel = size_t(BHkv) * p.Ck * rK;
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, ka.cent,
                        out.cK_last, nel);
   }
@@ -1127,33 +1176,41 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Vp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.vbar);
   SPR_CHECK_LAUNCH();
-  // M_Q and F_Q
-  double* kt = wsp<double>(ws, L.ktilde);
-  hipLaunchKernelGGL(ktilde_kernel, dim3(BHkv), dim3(1024), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
-  hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, kt, out.n_kv, p.Ck, d,
-                     metric);
-  if (warm)
-    launch_subspace(BHkv, d, p.rQ, st, metric, warm->FQ, p.eig_clamp, out.FQ, kvstat, 3);
-  hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp, out.FQ,
-                     kvstat, warm ? 3 : -1);
-  SPR_CHECK_LAUNCH();
-  // phi_Q = RMSNorm(Q F_Q)
-  hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
-                     prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G);
+  if (!q_raw) {
+    // M_Q and F_Q
+    double* kt = wsp<double>(ws, L.ktilde);
+    hipLaunchKernelGGL(ktilde_kernel, dim3(BHkv), dim3(1024), 0, st, out.kbar, out.n_kv, p.Ck, d, kt);
+    hipLaunchKernelGGL(query_metric_kernel, dim3((d / 16) * (d / 16), BHkv), dim3(256), 0, st, kt, out.n_kv, p.Ck,
+                       d, metric);
+    if (warm)
+      launch_subspace(BHkv, d, p.rQ, st, metric, warm->FQ, p.eig_clamp, out.FQ, kvstat, 3);
+    hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp,
+                       out.FQ, kvstat, warm ? 3 : -1);
+    SPR_CHECK_LAUNCH();
+    // phi_Q = RMSNorm(Q F_Q)
+    hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
+                       prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G);
+  } else {
+    hipLaunchKernelGGL(raw_rows_kernel<DT>, rqgrid, dim3(256), 0, st, q, g, Nv, phiQ);
+  }
   SPR_CHECK_LAUNCH();
   // query k-means
   KmArgs qa = ka;
-  qa.BH = BH; qa.r = p.rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1; qa.cent_given = warm != nullptr;
+  qa.BH = BH; qa.r = rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1; qa.cent_given = warm != nullptr;
   if (warm) {
-    launch_warm_centres<true>(dim3(ceil_div(p.Cq, 64), BH), st, warm->qbar, warm->n_q, p.Cq, d, out.FQ, p.rQ,
-                              p.rms_eps, phiQ, Nv, p.seed, 1, G, qa.cent);
+    if (q_raw)
+      hipLaunchKernelGGL(warm_centres_raw_kernel, dim3(p.Cq, BH), dim3(128), 0, st, warm->qbar, warm->n_q, p.Cq, d,
+                         phiQ, Nv, p.seed, 1, qa.cent);
+    else
+      launch_warm_centres<true>(dim3(ceil_div(p.Cq, 64), BH), st, warm->qbar, warm->n_q, p.Cq, d, out.FQ, p.rQ,
+                                p.rms_eps, phiQ, Nv, p.seed, 1, G, qa.cent);
     SPR_CHECK_LAUNCH();
   }
   s = run_kmeans(qa, st);
   if (s != SPR_OK) return s;
   if (out.passes) launch_copy_passes(qa.ctrl, BH, out.passes, 2, 1, st);
   if (out.cQ_last) {
-    const size_t nel = size_t(BH) * p.Cq * p.rQ;
+    const size_t nel = size_t(BH) * p.Cq * rQ;
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, qa.cent,
                        out.cQ_last, nel);
   }
@@ -1164,9 +1221,9 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, out.Qp, desc.N, d,
                      out.q_off, out.n_q, p.Cq, out.qbar);
   double* cbar = wsp<double>(ws, L.cbar);
-  hipLaunchKernelGGL(group_mean_perm_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, phiQ, Nv, p.rQ,
-                     out.q_perm, out.q_off, out.n_q, p.Cq, cbar);
-  hipLaunchKernelGGL(qdist_kernel, dim3(ceil_div(Nv, 16), BH), dim3(256), 0, st, phiQ, Nv, p.rQ, out.q_label, cbar,
+  hipLaunchKernelGGL(group_mean_perm_kernel, dim3(ceil_div(p.Cq, 4), BH, ceil_div(rQ, 64)), dim3(256), 0, st, phiQ,
+                     Nv, rQ, out.q_perm, out.q_off, out.n_q, p.Cq, cbar);
+  hipLaunchKernelGGL(qdist_kernel, dim3(ceil_div(Nv, 16), BH), dim3(256), 0, st, phiQ, Nv, rQ, out.q_label, cbar,
                      p.Cq, out.qdist);
   hipLaunchKernelGGL(merge_kv_status_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, gstat, kvstat, BH, G);
   SPR_CHECK_LAUNCH();

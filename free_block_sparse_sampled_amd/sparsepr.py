@@ -36,7 +36,8 @@ class spr_desc(ctypes.Structure):
 class spr_part_params(ctypes.Structure):
     _fields_ = [("Ck", ctypes.c_int32), ("Cq", ctypes.c_int32), ("rK", ctypes.c_int32), ("rQ", ctypes.c_int32),
                 ("Ms", ctypes.c_int32), ("max_iters", ctypes.c_int32), ("tol", ctypes.c_double),
-                ("rms_eps", ctypes.c_double), ("eig_clamp", ctypes.c_double), ("seed", ctypes.c_uint64)]
+                ("rms_eps", ctypes.c_double), ("eig_clamp", ctypes.c_double), ("seed", ctypes.c_uint64),
+                ("mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _PART_FIELDS = ["kv_label", "q_label", "kv_perm", "q_perm", "q_pos", "kv_off", "q_off", "n_kv", "n_q", "kbar",
@@ -70,6 +71,7 @@ class spr_fit_options(ctypes.Structure):
 # spr_probe_mode and spr_fit_family of include/sparsepr.h
 PROBE_MODES = {"stratified": 0, "random": 1, "uniform": 2}
 FIT_FAMILIES = {"full": 0, "mean": 1, "scalar": 2, "diag": 3}
+PART_MODES = {"response": 0, "semantic": 1, "key_response": 2}
 
 
 class SparsePRError(RuntimeError):
@@ -165,6 +167,13 @@ class OperatorConfig:
     probe_mode: str = "stratified"  # Table 4: "stratified" | "random" | "uniform"
     fit_family: str = "full"        # App. D.4: "full" | "mean" | "scalar" | "diag"
     out_rank: int = 0               # App. D.3 output truncation rank; 0: none
+    partition_mode: str = "response"  # Sec. 3.1, Table 2: "response" | "semantic" | "key_response"
+
+    def coord_ranks(self, d: int):
+        """Ranks of the K/V and query k-means coordinates (raw activations have rank d)."""
+        rK = d if self.partition_mode == "semantic" else self.rK
+        rQ = self.rQ if self.partition_mode == "response" else d
+        return rK, rQ
 
     def probe_options(self) -> spr_probe_options:
         return spr_probe_options(PROBE_MODES[self.probe_mode], self.seed)
@@ -174,7 +183,7 @@ class OperatorConfig:
 
     def part_params(self) -> spr_part_params:
         return spr_part_params(self.Ck, self.Cq, self.rK, self.rQ, self.Ms, self.max_iters, self.tol, self.rms_eps,
-                               self.eig_clamp, self.seed)
+                               self.eig_clamp, self.seed, PART_MODES[self.partition_mode], 0)
 
 
 def make_desc(q: torch.Tensor, n_text: int = 0, k: Optional[torch.Tensor] = None) -> spr_desc:
@@ -232,10 +241,11 @@ class Partition:
         self.Vp = z((BHkv, N, d), dt)
         self.phiK = self.phiQ = self.cK_last = self.cQ_last = self.passes = None
         if diagnostics:
-            self.phiK = z((BHkv, Nv, cfg.rK), f64)
-            self.phiQ = z((BH, Nv, cfg.rQ), f64)
-            self.cK_last = z((BHkv, cfg.Ck, cfg.rK), f64)
-            self.cQ_last = z((BH, cfg.Cq, cfg.rQ), f64)
+            rK, rQ = cfg.coord_ranks(d)
+            self.phiK = z((BHkv, Nv, rK), f64)
+            self.phiQ = z((BH, Nv, rQ), f64)
+            self.cK_last = z((BHkv, cfg.Ck, rK), f64)
+            self.cQ_last = z((BH, cfg.Cq, rQ), f64)
             self.passes = z((BH, 2), i32)
         self.struct = spr_partition(*[_ptr(getattr(self, n)) for n in _PART_FIELDS])
 

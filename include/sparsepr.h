@@ -94,16 +94,28 @@ typedef struct {
   int64_t ksb, ksh, ksn; /* element strides of k and v when 0 < Hkv < H */
 } spr_desc;
 
+/* Partition construction (spr_part_params.mode).  RESPONSE is the operator's response-coupled
+   partition (Sec. 4.1).  SEMANTIC is the reference partition of Sec. 3.1 and Table 2: k-means
+   on the raw key and query activations (d coordinates, no factor, no normalisation), each value
+   inheriting its key's group.  KEY_RESPONSE is the Table 2 variant that changes only the K/V
+   grouping: response-coupled K/V groups, semantic (raw) query groups.  Routing, probes and the
+   fit are the same in every mode, and the query distances d_i of App. A.2 are taken in the
+   coordinates the query groups were formed in. */
+typedef enum { SPR_PART_RESPONSE = 0, SPR_PART_SEMANTIC = 1, SPR_PART_KEY_RESPONSE = 2 } spr_part_mode;
+
 /* Partition hyperparameters (defaults of Table C.1, App. C.2, in brackets). */
 typedef struct {
   int32_t Ck, Cq;    /* requested K/V and query groups [1000, 300]; 1 <= C <= min(Nv, 1024) */
-  int32_t rK, rQ;    /* response ranks [48, 64]; 1 <= r <= min(d, 64) */
+  int32_t rK, rQ;    /* response ranks [48, 64]; in {8, 16, 32, 48, 64}, <= d */
   int32_t Ms;        /* metric query-sampling budget [2048]; min(Ms, Nv) evenly spaced rows */
   int32_t max_iters; /* k-means assignment passes [25]; >= 1 */
   double tol;        /* k-means relative cost-decrease tolerance [1e-4]; >= 0 */
   double rms_eps;    /* RMSNorm floor of the query coordinates [1e-6]; > 0 */
   double eig_clamp;  /* eigenvalues below eig_clamp * lambda_max count as zero [1e-6] */
   uint64_t seed;     /* k-means initialisation seed (SplitMix64) */
+  int32_t mode;      /* spr_part_mode [SPR_PART_RESPONSE]; raw coordinates have rank d (k-means
+                        coordinates, phiK / phiQ and the k-means centres are then d wide) */
+  int32_t reserved;  /* 0 */
 } spr_part_params;
 
 /* Outputs of sparsepr_partition (caller-owned device buffers).  Arrays of the K/V side are per
@@ -124,16 +136,20 @@ typedef struct {
   double* vbar;      /* [BHkv][Ck][d] value centroids */
   double* qbar;      /* [BH][Cq][d] mean query of each query group */
   double* qdist;     /* [BH][Nv]  |phi_Q(q_i) - c_a| (App. A.2), original order */
-  double* FK;        /* [BHkv][d][rK] key response factor, F F^T = rank-rK truncation of M_K */
-  double* FQ;        /* [BHkv][d][rQ] query response factor (M_Q depends on the K/V side only) */
+  double* FK;        /* [BHkv][d][rK] key response factor, F F^T = rank-rK truncation of M_K
+                        (not written in SEMANTIC mode) */
+  double* FQ;        /* [BHkv][d][rQ] query response factor (M_Q depends on the K/V side only;
+                        written in RESPONSE mode only) */
   void* Qp;          /* [BH][N][d] q rows in group-major order, then the text rows; input dtype */
   void* Kp;          /* [BHkv][N][d] k rows likewise (kv_perm order) */
   void* Vp;          /* [BHkv][N][d] v rows likewise (kv_perm order) */
   /* optional diagnostics, each may be NULL */
-  double* phiK;      /* [BHkv][Nv][rK] key coordinates k F_K */
-  double* phiQ;      /* [BH][Nv][rQ] query coordinates RMSNorm(q F_Q) */
+  double* phiK;      /* [BHkv][Nv][rK] key coordinates k F_K (raw k, rank d, in SEMANTIC mode) */
+  double* phiQ;      /* [BH][Nv][rQ] query coordinates RMSNorm(q F_Q) (raw q, rank d, unless
+                        RESPONSE mode) */
   double* cK_last;   /* [BHkv][Ck][rK] k-means centres used by the final K/V assignment pass */
-  double* cQ_last;   /* [BH][Cq][rQ] k-means centres used by the final query assignment pass */
+  double* cQ_last;   /* [BH][Cq][rQ] k-means centres used by the final query assignment pass
+                        (rK, rQ: the coordinate ranks of the mode) */
   int32_t* passes;   /* [BH][2] assignment passes: [j][0] of the K/V k-means of K/V head j < BHkv,
                                   [hd][1] of the query k-means of query head hd */
 } spr_partition;
@@ -263,8 +279,9 @@ spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* par
 spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v,
                                void* out, int32_t out_dtype, void* stream);
 
-/* Test helper: k-means of `feat` [BH][n][r] fp64 (r <= 64, C <= min(n, 1024)) with the operator's
-   initialisation (stage 0 or 1), assignment, update and stopping rules.  labels [BH][n] receive
+/* Test helper: k-means of `feat` [BH][n][r] fp64 (r in {8, 16, 32, 48, 64, 128},
+   C <= min(n, 1024)) with the operator's initialisation (stage 0 or 1), assignment, update and
+   stopping rules.  labels [BH][n] receive
    the uncompacted cluster ids; centres [BH][C][r] the centres used by the final assignment pass;
    passes [BH] the number of assignment passes. */
 spr_status sparsepr_kmeans(int32_t BH, int32_t n, int32_t r, int32_t C, const double* feat, uint64_t seed,

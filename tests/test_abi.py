@@ -67,7 +67,9 @@ def test_kmeans_workspace_size_limits(lib):
     assert lib.sparsepr_kmeans_workspace_size(2, 1000, 48, 64) > 0
     assert lib.sparsepr_kmeans_workspace_size(2, 1000, 48, 1025) == 0  # C above the supported 1024
     assert lib.sparsepr_kmeans_workspace_size(2, 10, 48, 11) == 0      # more centres than points
-    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 65, 64) == 0    # rank above 64
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 65, 64) == 0    # rank not built
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 128, 64) > 0    # raw 128-dimensional coordinates
+    assert lib.sparsepr_kmeans_workspace_size(2, 1000, 256, 64) == 0
 
 
 def test_entry_points_reject_invalid_arguments_on_the_host(lib):

@@ -54,7 +54,8 @@ def _clustered(n, r, C, seed):
     return centres[rng.integers(0, C, n)] + rng.standard_normal((n, r))
 
 
-@pytest.mark.parametrize("r,C,n", [(48, 20, 1000), (64, 37, 777), (16, 5, 300), (48, 700, 3001), (64, 1024, 2500)])
+@pytest.mark.parametrize("r,C,n", [(48, 20, 1000), (64, 37, 777), (16, 5, 300), (48, 700, 3001), (64, 1024, 2500),
+                                   (128, 40, 1500), (128, 300, 3001)])
 def test_kmeans_matches_oracle(r, C, n):
     BH = 2
     feats = np.stack([_clustered(n, r, C, [r, C, h]) for h in range(BH)])
@@ -76,6 +77,8 @@ def _compare_head(g, ref, hd, Nv, N, n_text, discrete_exact=True, kh=None):
     d = g["FK"].shape[1]
     # factors: F F^T is unique (eigenvector signs / rotations are not)
     for F, Fo in ((g["FK"][kh], ref["FK"]), (g["FQ"][kh], ref["FQ"])):
+        if Fo is None:  # not formed by this partition mode
+            continue
         A, Ao = F @ F.T, Fo @ Fo.T
         assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
     nkv, nq = int(g["n_kv"][kh]), int(g["n_q"][hd])
@@ -367,6 +370,35 @@ def test_full_size_mid_sampled():
 
 def test_full_size_joint_text_sampled():
     _full_size_lockstep("joint", [(0, 0), (1, 23)])
+
+
+# ------------------------------------------------------------------ partition modes
+@pytest.mark.parametrize("name,mode,heads", [("tiny", "semantic", [0]), ("tiny", "key_response", [0]),
+                                             ("small", "semantic", [0, 3]), ("small", "key_response", [0, 3])])
+def test_partition_modes_end_to_end(name, mode, heads):
+    """The semantic reference partition of Sec. 3.1 (k-means on the raw keys and queries) and the
+    key-response variant of Table 2 (response-coupled K/V groups, raw query groups), end to end
+    against the oracle's run of the same mode; heads with an oracle decision inside the 1e-6
+    tie margin are checked stage by stage instead."""
+    cfg = config(name)
+    opc = op_config(cfg, partition_mode=mode)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = O.Params(**{**_oracle_params(opc, cfg.n_text).__dict__, "partition_mode": mode})
+    Nv = cfg.Nv
+    for h in heads:
+        # raw coordinates are the activations themselves, exactly
+        if mode == "semantic":
+            assert np.array_equal(g["phiK"][h], k[0, h][:Nv].astype(np.float64))
+        assert np.array_equal(g["phiQ"][h], q[0, h][:Nv].astype(np.float64))
+        ref = O.sparsepr_head(q[0, h], k[0, h], v[0, h], p, head=h)
+        ref["lam"] = p.lam
+        if _oracle_is_tie_free(ref):
+            _compare_head(g, ref, h, Nv, cfg.N, cfg.n_text)
+        else:
+            _lockstep_head(g, q, k, v, cfg, opc, 0, h, np.random.default_rng(h))
+    assert np.all(g["head_status"] & 1 == 0)
 
 
 # ------------------------------------------------------------------ grouped-query attention
