@@ -66,9 +66,26 @@ def parse():
     ap.add_argument("--fit-family", choices=["full", "mean", "scalar", "diag"], default="full",
                     help="correction family (App. D.4); the operator's is the full ridge")
     ap.add_argument("--out-rank", type=int, default=0, help="output truncation rank (App. D.3); 0: none")
+    ap.add_argument("--partition-mode", choices=["response", "semantic", "key_response"], default="response",
+                    help="partition construction (Sec. 3.1, Table 2); the operator's is response")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for traffic counters)")
     return ap.parse_args()
+
+
+def affine_fit_energy(X: np.ndarray, D: np.ndarray, tol: float = 1e-10):
+    """Residual energy |R|^2 and the energy left by the best affine fit of R = D - X on [1, X]
+    over the given rows (the oracle fit of App. D.5): an SVD of the centred, column-scaled X with
+    relative singular value tolerance tol, the residual mean as intercept."""
+    X = X.astype(np.float64)
+    R = D.astype(np.float64) - X
+    Xc = X - X.mean(axis=0)
+    Rc = R - R.mean(axis=0)
+    sc = np.linalg.norm(Xc, axis=0)
+    sc[sc == 0] = 1.0
+    U, S, _ = np.linalg.svd(Xc / sc, full_matrices=False)
+    Uk = U[:, S > tol * S[0]] if S.size and S[0] > 0 else U[:, :0]
+    return float((R ** 2).sum()), float(((Rc - Uk @ (Uk.T @ Rc)) ** 2).sum())
 
 
 def cpu_baseline(cfg, opc):
@@ -128,7 +145,8 @@ def main():
         cfg = cfg.with_(max_iters=args.max_iters)
     opc = spr.OperatorConfig(Ck=cfg.Ck, Cq=cfg.Cq, rK=cfg.rK, rQ=min(cfg.rQ, cfg.d), Ms=cfg.Ms,
                              max_iters=cfg.max_iters, tol=cfg.tol, M=cfg.M, rho=cfg.rho, lam=cfg.lam, seed=0,
-                             probe_mode=args.probe_mode, fit_family=args.fit_family, out_rank=args.out_rank)
+                             probe_mode=args.probe_mode, fit_family=args.fit_family, out_rank=args.out_rank,
+                             partition_mode=args.partition_mode)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     # two input sets of the same heads (consecutive calls: same positions, fresh noise); calls
     # alternate between them so that every later call sees inputs that differ from the last one
@@ -207,6 +225,7 @@ def main():
                                 f"d={cfg.d} {cfg.dtype} n_text={cfg.n_text}"),
                    "Ck": cfg.Ck, "Cq": cfg.Cq, "M": cfg.M, "rho_target": cfg.rho, "max_iters": cfg.max_iters,
                    "probes": args.probe_mode, "fit_family": args.fit_family, "out_rank": args.out_rank,
+                   "partition": args.partition_mode,
                    "parallelism": "single GPU, heads batched"},
         "ms_per_call": round(ms_call, 4),
         "regime": ("later calls of App. C.1 (warm start: k-means from the previous centroids, 2 "
@@ -268,6 +287,17 @@ def main():
                                   "sparse_only_mean": round(esp.mean().item(), 5),
                                   "sparse_only_p99": round(torch.quantile(esp.float()[:1 << 24], 0.99).item(), 5),
                                   "rows": "all unprobed video rows, dense reference = sparsepr_attn_dense"}
+        # affine representability of the residual (App. D.5) on 2048 evenly spaced video rows of
+        # every head, energies summed over heads before the fraction is formed
+        m = min(2048, cfg.Nv)
+        rows = (torch.arange(m, device=o.device) * cfg.Nv) // m
+        Xs = osp[:, rows].double().cpu().numpy()
+        Ds = dref[:, rows].double().cpu().numpy()
+        tot = [affine_fit_energy(Xs[h], Ds[h]) for h in range(BH)]
+        energy = sum(t[0] for t in tot)
+        left = sum(t[1] for t in tot)
+        result["affine_representability"] = {"rows_per_head": m, "residual_energy": energy, "remaining_energy": left,
+                                             "explained_fraction": round(1.0 - left / energy, 5)}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, opc)
     print(json.dumps(result))
