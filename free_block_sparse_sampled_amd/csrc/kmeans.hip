@@ -639,10 +639,18 @@ static void launch_prep(const KmArgs& a, hipStream_t st) {
                      reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count, a.cent_given ? 1 : 0);
 }
 
+KmStatsTarget km_stats_target(const KmArgs& a) { return KmStatsTarget{a.mu, a.ctrl, RPMAX, CTRL, C_AMAX}; }
+
+void kmeans_stats_zero(const KmArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(km_stats_zero_kernel, dim3(ceil_div(a.BH * RPMAX, 256)), dim3(256), 0, st, a.mu, a.ctrl, a.BH);
+}
+
 spr_status run_kmeans(const KmArgs& a, hipStream_t st) {
   if (!kmeans_rank_supported(a.r)) return SPR_EUNSUPPORTED;
-  hipLaunchKernelGGL(km_stats_zero_kernel, dim3(ceil_div(a.BH * RPMAX, 256)), dim3(256), 0, st, a.mu, a.ctrl, a.BH);
-  hipLaunchKernelGGL(km_point_stats_kernel, dim3(64, a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.mu, a.ctrl);
+  if (!a.stats_given) {
+    kmeans_stats_zero(a, st);
+    hipLaunchKernelGGL(km_point_stats_kernel, dim3(64, a.BH), dim3(256), 0, st, a.feat, a.n, a.r, a.mu, a.ctrl);
+  }
   hipLaunchKernelGGL(km_stats_final_kernel, dim3(a.BH), dim3(RPMAX), 0, st, a.mu, a.ctrl, a.n);
   if (a.r > 64) launch_prep<128>(a, st);
   else launch_prep<64>(a, st);

@@ -663,7 +663,9 @@ static void launch_warm_centres(dim3 grid, hipStream_t st, const double* prev, c
 // ------------------------------------------------------------------ projection
 
 // phi = X F (Sec. 4.1) on v_mfma_f64_16x16x4f64; with RMS the rows are RMS-normalised as in
-// App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  The fp64 MFMA takes A[i][k] from lane i + 16k
+// App. B.2: phi / max(sqrt(|phi|^2 / r), eps).  With a statistics target the kernel also
+// accumulates the k-means point statistics of phi (column sums and the largest |phi|): per wave
+// over its chunks in registers, then one atomic per column and block.  The fp64 MFMA takes A[i][k] from lane i + 16k
 // and B[k][j] from lane j + 16k, and returns D[(lane / 16) + 4 v][lane % 16] in slot v.  F is
 // staged in LDS once per block; the block then walks `chunks` chunks of 128 rows (8 waves x 16
 // rows), the next chunk's rows loaded into registers (16-byte loads) while the current one is
@@ -672,7 +674,7 @@ template <int DT, bool RMS>
 __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
                                                       const double* __restrict__ Fall, int r, double eps,
                                                       double* __restrict__ out, int* __restrict__ gstat, int chunks,
-                                                      int fdiv) {
+                                                      int fdiv, KmStatsTarget kst) {
   extern __shared__ double smem[];
   const int d = g.d;
   const int NT = (r + 15) >> 4;
@@ -713,6 +715,7 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
   };
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   const int first = blockIdx.x * chunks * 128;
+  double csum[4] = {0.0, 0.0, 0.0, 0.0}, cmax = 0.0;  // this lane's rows of columns nt * 16 + r16
   fetch(first);
   for (int ch = 0; ch < chunks; ++ch) {
     const int row0 = first + ch * 128;
@@ -754,9 +757,41 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int c = nt * 16 + r16;
-          if (nt < NT && c < r) o[c] = acc[nt][v] * scale;
+          if (nt < NT && c < r) {
+            const double y = acc[nt][v] * scale;
+            o[c] = y;
+            csum[nt] += y;
+            cmax = fmax(cmax, fabs(y));
+          }
         }
       }
+    }
+  }
+  if (kst.mu) {
+    // the four row groups of a column, then the waves of the block through LDS (Xs is free)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      csum[nt] += __shfl_xor(csum[nt], 16);
+      csum[nt] += __shfl_xor(csum[nt], 32);
+    }
+    for (int o = 32; o > 0; o >>= 1) cmax = fmax(cmax, __shfl_xor(cmax, o));
+    __syncthreads();
+    double* red = reinterpret_cast<double*>(Xs);  // [8 waves][64 columns + 1]
+    if (gq == 0)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) red[w * 65 + nt * 16 + r16] = csum[nt];
+    if (lane == 0) red[w * 65 + 64] = cmax;
+    __syncthreads();
+    if (threadIdx.x < r) {
+      double t = 0.0;
+      for (int q = 0; q < 8; ++q) t += red[q * 65 + threadIdx.x];
+      atomicAdd(kst.mu + size_t(hd) * kst.mu_stride + threadIdx.x, t);
+    }
+    if (threadIdx.x == 64) {
+      double m = 0.0;
+      for (int q = 0; q < 8; ++q) m = fmax(m, red[q * 65 + 64]);
+      atomicMax(reinterpret_cast<unsigned long long*>(kst.ctrl + size_t(hd) * kst.ctrl_stride + kst.amax_slot),
+                (unsigned long long)__double_as_longlong(m));
     }
   }
 }
@@ -1125,15 +1160,20 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   allow_lds(project_kernel<DT, false>, prj_smem);
   allow_lds(project_kernel<DT, true>, prj_smem);
   const dim3 rgrid(unsigned(ceil_div64(int64_t(Nv) * d / 8, 256)), BHkv), rqgrid(rgrid.x, BH);
-  if (kv_raw)
+  KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
+  ka.BH = BHkv;
+  const KmStatsTarget kst = km_stats_target(ka);
+  if (kv_raw) {
     hipLaunchKernelGGL(raw_rows_kernel<DT>, rgrid, dim3(256), 0, st, k, gk, Nv, phiK);
-  else
+  } else {
+    kmeans_stats_zero(ka, st);  // the projection accumulates the k-means point statistics
     hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), dim3(512),
-                       prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1);
+                       prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1, kst);
+    ka.stats_given = true;
+  }
   SPR_CHECK_LAUNCH();
   // K/V k-means
-  KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
-  ka.BH = BHkv; ka.n = Nv; ka.r = rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
+  ka.n = Nv; ka.r = rK; ka.C = p.Ck; ka.feat = phiK; ka.seed = p.seed; ka.stage = 0;
   ka.max_iters = p.max_iters; ka.tol = p.tol;
   ka.cent = wsp<double>(ws, L.km_cent); ka.labels = wsp<int>(ws, L.km_lab);
   if (warm) {
@@ -1187,9 +1227,13 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     hipLaunchKernelGGL(eigen_factor_kernel, dim3(BHkv), dim3(256), jac_smem, st, metric, d, p.rQ, p.eig_clamp,
                        out.FQ, kvstat, warm ? 3 : -1);
     SPR_CHECK_LAUNCH();
-    // phi_Q = RMSNorm(Q F_Q)
+    // phi_Q = RMSNorm(Q F_Q), with the query k-means statistics (after the K/V k-means is done
+    // with the shared buffers)
+    KmArgs qz = ka;
+    qz.BH = BH;
+    kmeans_stats_zero(qz, st);
     hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
-                       prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G);
+                       prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G, kst);
   } else {
     hipLaunchKernelGGL(raw_rows_kernel<DT>, rqgrid, dim3(256), 0, st, q, g, Nv, phiQ);
   }
@@ -1197,6 +1241,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   // query k-means
   KmArgs qa = ka;
   qa.BH = BH; qa.r = rQ; qa.C = p.Cq; qa.feat = phiQ; qa.stage = 1; qa.cent_given = warm != nullptr;
+  qa.stats_given = !q_raw;
   if (warm) {
     if (q_raw)
       hipLaunchKernelGGL(warm_centres_raw_kernel, dim3(p.Cq, BH), dim3(128), 0, st, warm->qbar, warm->n_q, p.Cq, d,

@@ -11,6 +11,7 @@ struct KmArgs {
   const double* feat;  // [BH][n][r] coordinates
   double* cent;        // [BH][C][r] centres
   bool cent_given;     // cent already holds the initial centres (later calls)
+  bool stats_given;    // the producer of feat accumulated the point statistics (see km_stats_target)
   int* labels;         // [BH][n] labels after the last pass
   // scratch carved by kmeans_carve()
   double* sums;
@@ -35,6 +36,17 @@ KmArgs kmeans_carve(void* ws, int BH, int n, int C, int rmax);
 void launch_copy_passes(const double* ctrl, int BH, int* passes, int stride, int slot, hipStream_t st);
 
 spr_status run_kmeans(const KmArgs& a, hipStream_t st);
+// Where a producer of the k-means coordinates accumulates the point statistics itself: fp64
+// column sums into mu[head * mu_stride + column] (atomics) and the largest |x| into
+// ctrl[head * ctrl_stride + amax_slot] (atomicMax on the non-negative bit pattern), after
+// kmeans_stats_zero has cleared them; run_kmeans then skips its own statistics pass.
+struct KmStatsTarget {
+  double* mu;
+  double* ctrl;
+  int mu_stride, ctrl_stride, amax_slot;
+};
+KmStatsTarget km_stats_target(const KmArgs& a);
+void kmeans_stats_zero(const KmArgs& a, hipStream_t st);
 bool kmeans_rank_supported(int r);
 size_t compact_smem(int C);
 size_t jacobi_smem(int d);
