@@ -268,10 +268,13 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
   }
 }
 
-// Budgeted prefix of Sec. 4.3 for one query group: sort the n_kv scores descending (ties to
-// the lower group) with a bitonic sort in LDS, then take the shortest prefix whose key count
-// reaches Tk (at least one group, all groups when out of reach).  Block n_q handles the text
-// query group, which selects every group.
+// Budgeted prefix of Sec. 4.3 for one query group, one wave per group: the n_kv scores sorted
+// descending (ties to the lower group) by a bitonic network over P = 64 E entries held E per
+// lane in rank order (lane l holds ranks l E .. l E + E - 1; strides below E are exchanges
+// inside a lane, larger strides between lanes l and l ^ (stride / E)), then the shortest prefix
+// whose key count reaches Tk (at least one group, all groups when out of reach).  The group past
+// the last query group (index n_q) is the text query group, which selects every group.
+template <int E>
 __global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ scores,
                                                            const int* __restrict__ kv_off,
                                                            const int* __restrict__ q_off,
@@ -279,83 +282,93 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
                                                            int Cq, int Ck, int G, int n_text, int64_t Tk,
                                                            int* __restrict__ sel_cnt, int* __restrict__ sel_kv,
                                                            int64_t* __restrict__ pairs, int* __restrict__ gstat) {
-  __shared__ double ks[1024];
-  __shared__ int ids[1024];
-  __shared__ int buf[1024];
-  __shared__ int Ls;
-  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x;  // query head, its K/V head
+  constexpr int P = 64 * E;
+  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nq = n_q[hd], nkv = n_kv[hk];
   const int* off = kv_off + size_t(hk) * (Ck + 1);
-  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
   if (a > nq || (a == nq && n_text == 0)) return;
+  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
   if (a == nq) {  // text query rows: every group
-    for (int b = threadIdx.x; b <= nkv; b += 256) out[b] = b;
-    if (threadIdx.x == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
+    for (int b = lane; b <= nkv; b += 64) out[b] = b;
+    if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
     return;
   }
-  int P = 1;
-  while (P < nkv) P <<= 1;
-  for (int i = threadIdx.x; i < P; i += 256) {
-    ks[i] = i < nkv ? scores[(size_t(hd) * Cq + a) * Ck + i] : -1.0e308;
-    ids[i] = i < nkv ? i : 0x7fffffff;
+  double sc[E];
+  int id[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int i = lane * E + t;
+    sc[t] = i < nkv ? scores[(size_t(hd) * Cq + a) * Ck + i] : -1.0e308;
+    id[t] = i < nkv ? i : 0x7fffffff;
   }
-  __syncthreads();
-  // bitonic sort, "before" = larger score, then lower id
+  // "before" = larger score, then lower id
+  auto before = [](double s1, int i1, double s2, int i2) { return s1 > s2 || (s1 == s2 && i1 < i2); };
   for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < P; i += 256) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const double si = ks[i], sj = ks[j];
-          const int ii = ids[i], ij = ids[j];
-          const bool j_before_i = (sj > si) || (sj == si && ij < ii);
-          if (j_before_i == up) {
-            ks[i] = sj; ks[j] = si;
-            ids[i] = ij; ids[j] = ii;
+    for (int stride = size >> 1; stride >= E; stride >>= 1) {  // between lanes
+      const int pl = lane ^ (stride / E);
+      const bool low = lane < pl, up = ((lane * E) & size) == 0;
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        const double os = __shfl(sc[t], pl);
+        const int oi = __shfl(id[t], pl);
+        const bool mine_first = before(sc[t], id[t], os, oi);
+        // the lower position keeps the entry that comes first in this block's direction
+        const bool keep_mine = (low == up) ? mine_first : !mine_first;
+        if (!keep_mine) {
+          sc[t] = os;
+          id[t] = oi;
+        }
+      }
+    }
+#pragma unroll
+    for (int stride = E / 2; stride >= 1; stride >>= 1) {  // inside a lane
+      if (stride >= size) continue;
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        const int u = t ^ stride;
+        if (u > t) {
+          const bool up = ((lane * E + t) & size) == 0;
+          if (before(sc[u], id[u], sc[t], id[t]) == up) {
+            const double ts = sc[t];
+            const int ti = id[t];
+            sc[t] = sc[u]; id[t] = id[u];
+            sc[u] = ts; id[u] = ti;
           }
         }
       }
-      __syncthreads();
     }
   }
-  // prefix sums of group sizes in ranked order (4 consecutive ranks per thread)
-  int loc[4];
-  int s = 0;
+  // group sizes in ranked order and their running sum across the wave
+  int loc[E], s = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = threadIdx.x * 4 + u;
-    loc[u] = i < nkv ? off[ids[i] + 1] - off[ids[i]] : 0;
-    s += loc[u];
+  for (int t = 0; t < E; ++t) {
+    loc[t] = lane * E + t < nkv ? off[id[t] + 1] - off[id[t]] : 0;
+    s += loc[t];
   }
-  buf[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int y = threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
-    __syncthreads();
-    buf[threadIdx.x] += y;
-    __syncthreads();
+  int incl = s;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  if (threadIdx.x == 0) Ls = nkv;
-  __syncthreads();
-  int cum = buf[threadIdx.x] - s;
+  int cum = incl - s, L = nkv;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = threadIdx.x * 4 + u;
-    cum += loc[u];
-    if (i < nkv && cum >= Tk && cum - loc[u] < Tk) Ls = i + 1;  // unique crossing
+  for (int t = 0; t < E; ++t) {
+    const int i = lane * E + t;
+    cum += loc[t];
+    if (i < nkv && cum >= Tk && cum - loc[t] < Tk) L = i + 1;  // unique crossing
   }
-  __syncthreads();
-  const int L = Ls;
+  for (int o = 32; o > 0; o >>= 1) L = min(L, __shfl_xor(L, o));
   int64_t keys = 0;
-  for (int i = threadIdx.x; i < L; i += 256) {
-    out[i] = ids[i];
-    keys += off[ids[i] + 1] - off[ids[i]];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int i = lane * E + t;
+    if (i < L) {
+      out[i] = id[t];
+      keys += loc[t];
+    }
   }
-  __syncthreads();
-  __shared__ int64_t red[32];
-  keys = block_sum_i64(keys, red);
-  if (threadIdx.x == 0) {
+  for (int o = 32; o > 0; o >>= 1) keys += __shfl_xor(keys, o);
+  if (lane == 0) {
     int cnt = L;
     if (n_text > 0) out[cnt++] = nkv;
     sel_cnt[size_t(hd) * (Cq + 1) + a] = cnt;
@@ -555,8 +568,18 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   }
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(zero_i64_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, out.pairs, BH);
-  hipLaunchKernelGGL(route_select_kernel, dim3(p.Cq + 1, BH), dim3(256), 0, st, scores, part.kv_off, part.q_off,
-                     part.n_q, part.n_kv, p.Cq, p.Ck, G, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
+  {
+    const dim3 grid(ceil_div(p.Cq + 1, 4), BH);
+    auto sel = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, scores, part.kv_off, part.q_off, part.n_q, part.n_kv, p.Cq,
+                         p.Ck, G, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
+    };
+    if (p.Ck <= 64) sel(route_select_kernel<1>);
+    else if (p.Ck <= 128) sel(route_select_kernel<2>);
+    else if (p.Ck <= 256) sel(route_select_kernel<4>);
+    else if (p.Ck <= 512) sel(route_select_kernel<8>);
+    else sel(route_select_kernel<16>);
+  }
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(route_finalize_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, N, Nv,
                      desc.n_text, M, out.pairs, out.rho_exec, pstat);
