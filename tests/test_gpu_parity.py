@@ -435,6 +435,37 @@ def test_gqa_end_to_end(name):
     assert np.all(g["head_status"] & 1 == 0)
 
 
+def test_gqa_warm_start():
+    """A later call under grouped-query attention: the K/V-side state (factors, key centroids) is
+    per K/V head, the query centroids per query head (App. C.1 with the sharing of Sec. 4.3)."""
+    cfg = config("small_gqa")
+    G = cfg.H // cfg.Hkv
+    opc = op_config(cfg)
+    (q0, k0, v0), (tq0, tk0, tv0) = device_inputs(cfg, step=0)
+    (q1, k1, v1), (tq1, tk1, tv1) = device_inputs(cfg, step=1)
+    op = spr.SparsePR(tq0, opc, n_text=cfg.n_text, diagnostics=True, keep_scores=True, k=tk0)
+    op.run(tq0, tk0, tv0)
+    op.run(tq1, tk1, tv1, warm=True)
+    torch.cuda.synchronize()
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    p2 = O.Params(**{**p.__dict__, "max_iters": op.warm_iters})
+    for j in range(cfg.Hkv):
+        heads = [j * G + i for i in range(G)]
+        first = O.sparsepr_group([q0[0, h] for h in heads], k0[0, j], v0[0, j], p, j, heads, full=False)
+        refs = O.sparsepr_group([q1[0, h] for h in heads], k1[0, j], v1[0, j], p2, j, heads,
+                                warm=[r["state"] for r in first])
+        A, Ao = g["FK"][j] @ g["FK"][j].T, refs[0]["FK"] @ refs[0]["FK"].T
+        assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
+        for hd, ref in zip(heads, refs):
+            ref["lam"] = p.lam
+            if all(_oracle_is_tie_free(r) for r in first) and _oracle_is_tie_free(ref):
+                _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text, kh=j)
+            else:
+                _lockstep_head(g, q1, k1, v1, cfg, opc, 0, hd, np.random.default_rng(hd))
+    assert np.all(g["passes"] <= op.warm_iters)
+
+
 # ------------------------------------------------------------------ probe and estimator variants
 @pytest.mark.parametrize("name,heads,probe_mode,family,out_rank", [
     ("tiny", [0], "random", "full", 0),
