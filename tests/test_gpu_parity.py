@@ -175,6 +175,28 @@ def test_operator_end_to_end(name, heads):
     assert np.all(g["head_status"] & 1 == 0)
 
 
+@pytest.mark.parametrize("grid,Ck,Cq,M,rho,n_text", [
+    ((4, 8, 8), 1, 1, 8, 0.5, 0),         # one group each: the route is every key
+    ((4, 8, 8), 256, 256, 16, 0.3, 0),    # one group per key requested (duplicate draws leave empties)
+    ((2, 8, 8), 7, 5, 4, 0.9, 16),        # an empty query group, text tokens, a budget near N
+    ((1, 3, 43), 16, 16, 8, 0.22, 0),     # 129 video rows: ragged against every tile size
+])
+def test_degenerate_group_counts(grid, Ck, Cq, M, rho, n_text):
+    """Edge cases of the partition and route on the tiny mixture workload (fp32, d = 64)."""
+    cfg = config("tiny").with_(grid=grid, Ck=Ck, Cq=Cq, M=M, rho=rho, n_text=n_text, Ms=4096)
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    ref = O.sparsepr_head(q[0, 0], k[0, 0], v[0, 0], p, head=0)
+    ref["lam"] = p.lam
+    assert _oracle_is_tie_free(ref)
+    _compare_head(g, ref, 0, cfg.Nv, cfg.N, cfg.n_text)
+    empty_q = ref["n_q"] < Cq
+    assert bool(g["head_status"][0] & 8) == empty_q  # SPR_HS_Q_GROUPS_EMPTY
+
+
 @pytest.mark.parametrize("name,heads", [("tiny", [(0, 0)]), ("small", [(0, 0), (0, 4)]),
                                         ("small_text", [(0, 0)])])
 def test_warm_start_end_to_end(name, heads):
