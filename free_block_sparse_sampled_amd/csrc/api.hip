@@ -32,12 +32,14 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.km_lab = take(BH * Nv * 4);
   L.km_region = take(kmeans_ws_bytes(int(BH), int(Nv), L.Cmax, L.rmax));
   L.cbar = take(BH * p.Cq * rQ * 8);
-  L.vstat = take(BH * Nv * 2 * 8);
+  L.vstat = take(BH * Nv * 4 * 8);
   L.gstat = take(2 * BH * 8 * 4);  // per query head, then per K/V head
   L.pstat = take(BH * p.Cq * 2 * 4);
   L.shift = take(BH * p.Cq * 8);
   L.lbar = take(BH * p.Cq * p.Ck * 8);
   L.scores = take(BH * p.Cq * p.Ck * 8);
+  const size_t nsc = desc.dtype == SPR_BF16 ? BH * p.Cq * p.Ck : 0;
+  L.serr = take(nsc * 8);
   L.vh = take(desc.dtype == SPR_BF16 ? BH * size_t(desc.N) * d * 2 : 0);
   const size_t Mm = M > 0 ? size_t(M) : 1;
   L.pr_part = take(BH * Mm * L.splits * (d + 2) * 4);

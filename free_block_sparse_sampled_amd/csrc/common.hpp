@@ -187,12 +187,13 @@ struct Workspace {
   size_t km_lab;     // int    [BH][Nv]          uncompacted labels
   size_t km_region;  // k-means scratch (see kmeans_carve)
   size_t cbar;       // double [BH][Cq][rQ]      mean query coordinates c_a
-  size_t vstat;      // double [BH][Nv][2]       v_j . vbar_b(j), |v_j|^2 in Kp order
+  size_t vstat;      // double [BH][Nv][4]       v.vbar, |v|^2, (vbar - v).v, |vbar - v|^2 per key, Kp order
   size_t gstat;      // int    [2 BH][8]         flags per query head, then per K/V head
   size_t pstat;      // int    [BH][Cq][2]       probes per query group, prefix
   size_t shift;      // double [BH][Cq]          per-query-group exponent shift of the scores
   size_t lbar;       // double [BH][Cq][Ck]      centroid logits qbar_a . kbar_b / sqrt d
   size_t scores;     // double [BH][Cq][Ck]      (unless the caller keeps them)
+  size_t serr;       // double [BH][Cq][Ck]      bounds of the bf16 scores (unless the caller keeps them)
   size_t vh;         // fp16   [BH][N][d]        group-major values converted to fp16 (bf16 inputs)
   size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows
   size_t fitX;       // double [BH][M][d]        standardised probe features

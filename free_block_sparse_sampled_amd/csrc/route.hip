@@ -12,8 +12,9 @@
 
 namespace spr {
 
-// Per key (group-major order): u_j = v_j . vbar_b(j) and w_j = |v_j|^2, fp64.  d / 8 lanes per
-// key, eight consecutive elements each (one 16-byte load for bf16), reduced across those lanes.
+// Per key (group-major order), fp64: u_j = v_j . vbar_b(j), w_j = |v_j|^2, c_j = (vbar_b - v_j) . v_j
+// and r_j = |vbar_b - v_j|^2.  d / 8 lanes per key, eight consecutive elements each (one 16-byte
+// load for bf16), reduced across those lanes.
 template <int DT>
 __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp, int N, int Nv, int d,
                                                     const int* __restrict__ kv_perm,
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
   const int hd = blockIdx.y;
   const int L = d >> 3;
   const int pos = blockIdx.x * (256 / L) + threadIdx.x / L, sub = threadIdx.x % L;
-  double u = 0.0, w = 0.0;
+  double u = 0.0, w = 0.0, cr = 0.0, r = 0.0;
   if (pos < Nv) {
     const int b = kv_label[size_t(hd) * Nv + kv_perm[size_t(hd) * Nv + pos]];
     const double* vb = vbar + (size_t(hd) * Ck + b) * d + sub * 8;
@@ -31,17 +32,23 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
     load8<DT>(Vp, (int64_t(hd) * N + pos) * d + sub * 8, x);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      u = fma(double(x[c]), vb[c], u);
-      w = fma(double(x[c]), double(x[c]), w);
+      const double xv = double(x[c]), dv = vb[c] - xv;
+      u = fma(xv, vb[c], u);
+      w = fma(xv, xv, w);
+      cr = fma(dv, xv, cr);
+      r = fma(dv, dv, r);
     }
   }
   for (int o = L >> 1; o > 0; o >>= 1) {
     u += __shfl_xor(u, o);
     w += __shfl_xor(w, o);
+    cr += __shfl_xor(cr, o);
+    r += __shfl_xor(r, o);
   }
   if (pos < Nv && sub == 0) {
-    vstat[(size_t(hd) * Nv + pos) * 2 + 0] = u;
-    vstat[(size_t(hd) * Nv + pos) * 2 + 1] = w;
+    double* o = vstat + (size_t(hd) * Nv + pos) * 4;
+    *reinterpret_cast<double2*>(o) = make_double2(u, w);
+    *reinterpret_cast<double2*>(o + 2) = make_double2(cr, r);
   }
 }
 
@@ -218,8 +225,8 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
       }
       if (threadIdx.x < PIECE) {
         const int jl = threadIdx.x;
-        us[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 2 + 0] : 0.0;
-        wsv[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 2 + 1] : 0.0;
+        us[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 4 + 0] : 0.0;
+        wsv[jl] = jl < n ? vstat[(size_t(hk) * Nv + p0 + jl) * 4 + 1] : 0.0;
       }
       __syncthreads();
       for (int t = 0; t * 16 < n; ++t) {
@@ -268,55 +275,355 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
   }
 }
 
-// Budgeted prefix of Sec. 4.3 for one query group, one wave per group: the n_kv scores sorted
-// descending (ties to the lower group) by a bitonic network over P = 64 E entries held E per
-// lane in rank order (lane l holds ranks l E .. l E + E - 1; strides below E are exchanges
-// inside a lane, larger strides between lanes l and l ^ (stride / E)), then the shortest prefix
-// whose key count reaches Tk (at least one group, all groups when out of reach).  The group past
-// the last query group (index n_q) is the text query group, which selects every group.
-template <int E>
-__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ scores,
-                                                           const int* __restrict__ kv_off,
-                                                           const int* __restrict__ q_off,
-                                                           const int* __restrict__ n_q, const int* __restrict__ n_kv,
-                                                           int Cq, int Ck, int G, int n_text, int64_t Tk,
-                                                           int* __restrict__ sel_cnt, int* __restrict__ sel_kv,
-                                                           int64_t* __restrict__ pairs, int* __restrict__ gstat) {
-  constexpr int P = 64 * E;
-  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+// ------------------------------------------------------------ bf16 scores with error bounds
+// For bf16 keys the logits run on the bf16 matrix cores: qbar_a is split into three bf16
+// slices (hi + mid + lo, each the rounding of what the previous slices leave), the keys are
+// exact in bf16, and the three products accumulate in fp32.  Each pair is shifted by its own
+// centroid logit, E'_j = e^{l_j - lbar_ab} = E_j / A, and the score is taken in centred form:
+// with delta_j = 1 - E'_j, c_j = (vbar_b - v_j) . v_j and r_j = |vbar_b - v_j|^2,
+//   g s_ab / A^2 = sum_j |vbar_b - E'_j v_j|^2 = sum_j r_j + 2 sum_j delta_j c_j + sum_j delta_j^2 |v_j|^2,
+// the first sum fp64, the others fp32.  Nothing cancels.  A group of one key scores exactly 0
+// (its centroid is its key) and is written so with a zero bound.  Each score comes with a bound on its
+// distance to the exact score (same row factor), from:
+//   - the logit: the hi slice takes one product per 32 columns, each from zero, so at most
+//     2 (32 + 8) 2^-24 |qbar_a| max_j |k_j| for its products and the fp32 sums that join them
+//     (every fp32 operation rounded, with a factor 2 for any rounding mode of the matrix
+//     cores), 2 d 2^-32 of the same for the mid and lo chains, plus 2^-22 for the slices;
+//   - the exponent argument: the fp32 scale (three roundings), the pair's shift and the fma;
+//   - v_exp_f32 within 2^-21 relative;
+//   - delta_j: within (relE + 2^-24)(E'_j + |delta_j|) of 1 - e^{x_j}, relE the relative error
+//     of E'_j; the sums of |c_j| (E' + |delta|), |v_j|^2 |delta| (E' + |delta|) and
+//     |v_j|^2 (E' + |delta|)^2 carry it to the two fp32 sums;
+//   - the fp32 sums: at most g + 8 roundings on any path (g keys, four reduction levels),
+//     each within 2^-24 of the sum of the magnitudes.
+// A score whose sums overflow gets an infinite bound.
+//
+// A block takes 16 query groups per wave and 16 consecutive K/V groups, whose keys are
+// contiguous; they pass through LDS in pieces of at most 64 keys of one group, double-buffered
+// (the loads of the next piece are in flight while this one is computed), with the key norms
+// formed while staging.  The sums of a group are reduced across the 16 lanes of each query
+// group by DPP, and the scores and bounds of four groups are formed at once, one per lane.
+// Blocks are ordered so that the query tiles sharing a K/V range run on one XCD (one L2).
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+template <int CTRL>
+__device__ __forceinline__ float dppf(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum and maximum over 8 / 16 consecutive lanes (aligned): quad_perm [1,0,3,2] and [2,3,0,1],
+// then row_half_mirror and row_mirror; every lane gets the result
+__device__ __forceinline__ float lanes_sum8(float x) {
+  x += dppf<0xB1>(x);
+  x += dppf<0x4E>(x);
+  return x + dppf<0x141>(x);
+}
+__device__ __forceinline__ float lanes_sum16(float x) {
+  x = lanes_sum8(x);
+  return x + dppf<0x140>(x);
+}
+__device__ __forceinline__ float lanes_max16(float x) {
+  x = fmaxf(x, dppf<0xB1>(x));
+  x = fmaxf(x, dppf<0x4E>(x));
+  x = fmaxf(x, dppf<0x141>(x));
+  return fmaxf(x, dppf<0x140>(x));
+}
+__device__ __forceinline__ float sel4f(const float (&x)[4], int v) {
+  return v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
+}
+constexpr int kFastPiece = 64;
+constexpr int kFastWaves = 8;
+template <int D>
+constexpr size_t route_fast_buf() {
+  return size_t(kFastPiece) * D * 2 + 3 * kFastPiece * 4;
+}
+template <int D>
+constexpr size_t route_fast_smem() {
+  return 2 * route_fast_buf<D>() + 16 * 8 + size_t(16) * 16 * kFastWaves * 8;
+}
+// blocks of the fast score kernel: one run of query tiles per (head, K/V range), eight runs
+// side by side (one per XCD)
+inline int64_t route_fast_blocks(int Cq, int Ck, int BH) {
+  const int64_t TX = (Cq + 16 * kFastWaves - 1) / (16 * kFastWaves), TY = (Ck + 15) / 16;
+  return 8 * TX * ((int64_t(BH) * TY + 7) / 8);
+}
+template <int D>
+__global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const uint16_t* __restrict__ Kp, int N, int Nv,
+                                                               const double* __restrict__ qbar,
+                                                               const double* __restrict__ lbar,
+                                                               const double* __restrict__ vbar,
+                                                               const int* __restrict__ kv_off,
+                                                               const int* __restrict__ n_q,
+                                                               const int* __restrict__ n_kv, int Cq, int Ck, int G,
+                                                               int BH, const double* __restrict__ shift,
+                                                               const double* __restrict__ vstat,
+                                                               double* __restrict__ scores,
+                                                               double* __restrict__ serr) {
+  constexpr int PIECE = kFastPiece;
+  constexpr int KS = D / 32;                   // 32-column steps
+  constexpr int KPR = D / 8;                   // 16-byte pieces per key row
+  constexpr int NTH = kFastWaves * 64, QT = 16 * kFastWaves;  // threads, query groups per block
+  constexpr int KPT = PIECE * KPR / NTH;       // 16-byte pieces staged per thread
+  constexpr size_t BUF = route_fast_buf<D>();
+  extern __shared__ __attribute__((aligned(16))) char rf_sm[];
+  double* p0s = reinterpret_cast<double*>(rf_sm + 2 * BUF);  // [16] sum_j r_j per group
+  double* lbs = p0s + 16;                                    // [16][QT] lbar of the block's pairs
+  const int TX = (Cq + QT - 1) / QT, TY = (Ck + 15) / 16;
+  const int L = blockIdx.x, kq = L >> 3;
+  const int tx = kq % TX, grp = (kq / TX) * 8 + (L & 7);
+  if (grp >= BH * TY) return;
+  const int hd = grp / TY, hk = hd / G, a0 = tx * QT, b0 = (grp % TY) * 16;
   const int nq = n_q[hd], nkv = n_kv[hk];
+  if (a0 >= nq || b0 >= nkv) return;
+  const int b1 = min(b0 + 16, nkv);
   const int* off = kv_off + size_t(hk) * (Ck + 1);
-  if (a > nq || (a == nq && n_text == 0)) return;
-  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
-  if (a == nq) {  // text query rows: every group
-    for (int b = lane; b <= nkv; b += 64) out[b] = b;
-    if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
-    return;
-  }
-  double sc[E];
-  int id[E];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, r16 = lane & 15;
+  const uint16_t* Kh = Kp + size_t(hk) * N * D;
+
+  // A fragments: lane l holds query group a0 + 16 w + l % 16, columns 32 ks + 8 (l / 16) .. + 7
+  rbf16x8_t qh[KS], qm[KS], ql[KS];
+  double qn2 = 0.0;
+  {
+    const int a = min(a0 + w * 16 + r16, nq - 1);
+    const bool ok = a0 + w * 16 + r16 < nq;
 #pragma unroll
-  for (int t = 0; t < E; ++t) {
-    const int i = lane * E + t;
-    sc[t] = i < nkv ? scores[(size_t(hd) * Cq + a) * Ck + i] : -1.0e308;
-    id[t] = i < nkv ? i : 0x7fffffff;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double x = qbar[(size_t(hd) * Cq + a) * D + ks * 32 + gq * 8 + e];
+        x = ok ? x : 0.0;
+        const __bf16 h = __bf16(float(x));
+        const double r1 = x - double(float(h));
+        const __bf16 m = __bf16(float(r1));
+        const double r2 = r1 - double(float(m));
+        qh[ks][e] = h;
+        qm[ks][e] = m;
+        ql[ks][e] = __bf16(float(r2));
+        qn2 = fma(x, x, qn2);
+      }
   }
-  // "before" = larger score, then lower id
+  qn2 += __shfl_xor(qn2, 16);
+  qn2 += __shfl_xor(qn2, 32);
+  // output slot v of lane l: query group a0 + 16 w + 4 (l / 16) + v, key l % 16 of the tile;
+  // in the epilogue lane l forms the pair (query group slot v = l % 4, K/V group slot l % 16 / 4)
+  const int my_v = r16 & 3, my_slot = r16 >> 2, my_a = a0 + w * 16 + gq * 4 + my_v;
+  const double my_m = my_a < nq ? shift[size_t(hd) * Cq + my_a] : 0.0;
+  const double my_qn = sqrt(__shfl(qn2, gq * 4 + my_v));
+  // the block's centroid logits lbar_ab in LDS; the pair shifts (times log2 e, fp32) of the
+  // lane's four query groups and group b
+  for (int e = tid; e < 16 * QT; e += NTH) {
+    const int bl = e % 16, al = e / 16;
+    const int a = min(a0 + al, nq - 1), bg = min(b0 + bl, b1 - 1);
+    lbs[bl * QT + al] = lbar[(size_t(hd) * Cq + a) * Ck + bg];
+  }
+  float m2[4];
+  auto load_shift = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) m2[v] = float(lbs[(b - b0) * QT + w * 16 + gq * 4 + v] * 1.4426950408889634);
+  };
+  if (tid < 16) p0s[tid] = 0.0;
+
+  uint4 pk[KPT];
+  double pu = 0.0, pw = 0.0, pr = 0.0;
+  auto fetch = [&](int b, int p0) __attribute__((always_inline)) {
+    const int n = min(PIECE, off[b + 1] - p0);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + NTH * i, row = e / KPR, pc = e % KPR;
+      pk[i] = make_uint4(0, 0, 0, 0);
+      if (row < n) pk[i] = *reinterpret_cast<const uint4*>(Kh + size_t(p0 + row) * D + pc * 8);
+    }
+    if (tid < PIECE) {
+      const double* st4 = vstat + (size_t(hk) * Nv + p0 + tid) * 4;
+      pw = tid < n ? st4[1] : 0.0;
+      pu = tid < n ? st4[2] : 0.0;
+      pr = tid < n ? st4[3] : 0.0;
+    }
+  };
+  // registers -> LDS buffer: key rows (16-byte piece p of row r at p ^ (r % KPR)), c, |v|^2,
+  // |k|; the piece's sum of r_j is added to its group's (wave 0)
+  auto put = [&](int bi, int bgrp) __attribute__((always_inline)) {
+    uint16_t* K = reinterpret_cast<uint16_t*>(rf_sm + bi * BUF);
+    float* F = reinterpret_cast<float*>(rf_sm + bi * BUF + size_t(PIECE) * D * 2);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + NTH * i, row = e / KPR, pc = e % KPR;
+      *reinterpret_cast<uint4*>(K + row * D + ((pc ^ (row % KPR)) * 8)) = pk[i];
+      const uint32_t wd[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+      float sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
+        sq = fmaf(lo, lo, fmaf(hi, hi, sq));
+      }
+      sq = KPR == 16 ? lanes_sum16(sq) : lanes_sum8(sq);
+      if (pc == 0) F[2 * PIECE + row] = sqrtf(sq);
+    }
+    if (tid < PIECE) {
+      F[tid] = float(pu);
+      F[PIECE + tid] = float(pw);
+      const double rs = wave_sum_d(pr);
+      if (tid == 0) p0s[bgrp - b0] += rs;
+    }
+  };
+
+  const float c2 = 1.4426950408889634f / sqrtf(float(D));
+  int b = b0, p0 = off[b0];
+  fetch(b, p0);
+  __syncthreads();  // p0s cleared, lbs filled
+  put(0, b);
+  load_shift(b);
+  __syncthreads();
+  int nb = b, np0 = p0 + PIECE;
+  if (np0 >= off[nb + 1]) {
+    ++nb;
+    np0 = nb < b1 ? off[nb] : 0;
+  }
+  // per output slot: P1 = sum delta c, P2 = sum delta^2 |v|^2 and the three bound sums
+  float P1[4], P2[4], B1[4], B2[4], B3[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) P1[v] = P2[v] = B1[v] = B2[v] = B3[v] = 0.f;
+  float kmax = 0.f;
+  float kP1 = 0.f, kP2 = 0.f, kB1 = 0.f, kB2 = 0.f, kB3 = 0.f, kK = 0.f;  // this lane's pair of the batch
+  int slot = 0, gstart = b0, buf = 0;
+  for (;;) {
+    const bool has_next = nb < b1;
+    if (has_next) fetch(nb, np0);
+    const int n = min(PIECE, off[b + 1] - p0);
+    {
+      const uint16_t* K = reinterpret_cast<const uint16_t*>(rf_sm + buf * BUF);
+      const float* F = reinterpret_cast<const float*>(rf_sm + buf * BUF + size_t(PIECE) * D * 2);
+      for (int t = 0; t * 16 < n; ++t) {
+        const int jl = t * 16 + r16;
+        rbf16x8_t kb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kb[ks] = __builtin_bit_cast(rbf16x8_t,
+                                      *reinterpret_cast<const uint4*>(K + jl * D + (((ks * 4 + gq) ^ (jl % KPR)) * 8)));
+        const rf32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+        rf32x4_t ch[KS], cm = zero, cl = zero;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          ch[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kb[ks], zero, 0, 0, 0);
+          cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm[ks], kb[ks], cm, 0, 0, 0);
+          cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb[ks], cl, 0, 0, 0);
+        }
+        rf32x4_t lg = cm + cl;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) lg += ch[ks];
+        const bool live = jl < n;
+        const float cc = F[jl], ww = F[PIECE + jl], ac = fabsf(cc);
+        if (live) kmax = fmaxf(kmax, F[2 * PIECE + jl]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float l = lg[v];
+          const float E = live ? __builtin_amdgcn_exp2f(fmaf(l, c2, -m2[v])) : 1.f;
+          const float dl = 1.f - E, ad = fabsf(dl), tt = E + ad;
+          P1[v] = fmaf(dl, cc, P1[v]);
+          P2[v] = fmaf(dl * dl, ww, P2[v]);
+          B1[v] = fmaf(ac, tt, B1[v]);
+          B2[v] = fmaf(ww * ad, tt, B2[v]);
+          B3[v] = fmaf(ww * tt, tt, B3[v]);
+        }
+      }
+    }
+    if (p0 + PIECE >= off[b + 1]) {  // group b complete
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        P1[v] = lanes_sum16(P1[v]);
+        P2[v] = lanes_sum16(P2[v]);
+        B1[v] = lanes_sum16(B1[v]);
+        B2[v] = lanes_sum16(B2[v]);
+        B3[v] = lanes_sum16(B3[v]);
+      }
+      kmax = lanes_max16(kmax);
+      if (my_slot == slot) {
+        kP1 = sel4f(P1, my_v);
+        kP2 = sel4f(P2, my_v);
+        kB1 = sel4f(B1, my_v);
+        kB2 = sel4f(B2, my_v);
+        kB3 = sel4f(B3, my_v);
+        kK = kmax;
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P1[v] = P2[v] = B1[v] = B2[v] = B3[v] = 0.f;
+      kmax = 0.f;
+      ++slot;
+      if (slot == 4 || b + 1 == b1) {
+        const int bb = gstart + my_slot;
+        if (my_slot < slot && my_a < nq) {
+          constexpr double u = 0x1p-24;
+          const int g_keys = off[bb + 1] - off[bb];
+          const double g = double(g_keys), ig = 1.0 / g, R0 = p0s[bb - b0];
+          const double Q1 = kP1, Q2 = kP2, C1 = kB1, C2 = kB2, C3 = kB3;
+          const size_t at = (size_t(hd) * Cq + my_a) * Ck + bb;
+          const double lb = lbs[(bb - b0) * QT + w * 16 + gq * 4 + my_v], A = exp(lb - my_m), A2 = A * A;
+          double score = A2 * ((R0 + 2.0 * Q1 + Q2) * ig);
+          // |qbar_a| |k_j| bounds |l_j| and the sum of the product magnitudes (norms from fp32 sums)
+          const double C = my_qn * double(kK) * (1.0 + 1e-5);
+          const double eps_l = 2.0 * (32 + 8) * u * C + 2.0 * D * 0x1p-32 * C + 0x1p-22 * C +
+                               D * 0x1p-100 * double(kK);
+          const double c2d = 1.4426950408889634 / sqrt(double(D)), m2d = fabs(lb * 1.4426950408889634);
+          const double dx = eps_l * c2d * 1.001 + 6.0 * u * (C * c2d + m2d) * 1.001;
+          const double y = dx * 0.69314718055994531;
+          const double relE = (y < 0.5 ? y * (1.0 + y) : expm1(y)) * (1.0 + 0x1p-21) + 0x1p-21;
+          const double nr = (g + 8.0) * u, re = relE + u;
+          const double ep = (2.0 * (re + nr) * C1 + re * (2.0 * C2 + re * C3) + nr * fabs(Q2)) * 1.01;
+          double err = A2 * (ep * ig * 1.001 + 1e-15 * (R0 + 2.0 * C1 + fabs(Q2)) * ig);
+          if (!(fabs(score) <= 1.0e300) || !(err <= 1.0e300)) {
+            score = 0.0;
+            err = INFINITY;
+          }
+          if (g_keys == 1) score = err = 0.0;
+          scores[at] = score;
+          serr[at] = err;
+        }
+        slot = 0;
+        gstart = b + 1;
+      }
+    }
+    if (!has_next) break;
+    put(buf ^ 1, nb);
+    __syncthreads();
+    buf ^= 1;
+    if (nb != b) load_shift(nb);
+    b = nb;
+    p0 = np0;
+    np0 += PIECE;
+    if (np0 >= off[nb + 1]) {
+      ++nb;
+      np0 = nb < b1 ? off[nb] : 0;
+    }
+  }
+}
+
+// Bitonic network of one wave over P = 64 E entries held E per lane in rank order (lane l holds
+// ranks l E .. l E + E - 1; strides below E are exchanges inside a lane, larger strides between
+// lanes l and l ^ (stride / E)): key descending, ties to the lower id.  NP payload doubles per
+// entry travel with it.
+template <int E, int NP>
+__device__ __forceinline__ void wave_sort_desc(double (&key)[E], int (&id)[E], double (&pl)[NP > 0 ? NP : 1][E],
+                                               int lane) {
+  constexpr int P = 64 * E;
   auto before = [](double s1, int i1, double s2, int i2) { return s1 > s2 || (s1 == s2 && i1 < i2); };
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride >= E; stride >>= 1) {  // between lanes
-      const int pl = lane ^ (stride / E);
-      const bool low = lane < pl, up = ((lane * E) & size) == 0;
+      const int pl_lane = lane ^ (stride / E);
+      const bool low = lane < pl_lane, up = ((lane * E) & size) == 0;
 #pragma unroll
       for (int t = 0; t < E; ++t) {
-        const double os = __shfl(sc[t], pl);
-        const int oi = __shfl(id[t], pl);
-        const bool mine_first = before(sc[t], id[t], os, oi);
+        const double os = __shfl(key[t], pl_lane);
+        const int oi = __shfl(id[t], pl_lane);
+        double op[NP > 0 ? NP : 1];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) op[k] = __shfl(pl[k][t], pl_lane);
+        const bool mine_first = before(key[t], id[t], os, oi);
         // the lower position keeps the entry that comes first in this block's direction
         const bool keep_mine = (low == up) ? mine_first : !mine_first;
         if (!keep_mine) {
-          sc[t] = os;
+          key[t] = os;
           id[t] = oi;
+#pragma unroll
+          for (int k = 0; k < NP; ++k) pl[k][t] = op[k];
         }
       }
     }
@@ -328,17 +635,32 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
         const int u = t ^ stride;
         if (u > t) {
           const bool up = ((lane * E + t) & size) == 0;
-          if (before(sc[u], id[u], sc[t], id[t]) == up) {
-            const double ts = sc[t];
+          if (before(key[u], id[u], key[t], id[t]) == up) {
+            const double ts = key[t];
             const int ti = id[t];
-            sc[t] = sc[u]; id[t] = id[u];
-            sc[u] = ts; id[u] = ti;
+            key[t] = key[u]; id[t] = id[u];
+            key[u] = ts; id[u] = ti;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) {
+              const double tp = pl[k][t];
+              pl[k][t] = pl[k][u];
+              pl[k][u] = tp;
+            }
           }
         }
       }
     }
   }
-  // group sizes in ranked order and their running sum across the wave
+}
+
+// Budgeted prefix of Sec. 4.3 from the ranked groups id (E per lane, rank order): the shortest
+// prefix whose key count reaches Tk (at least one group, all groups when out of reach), written
+// to out followed by the text group when n_text > 0, with the count, the routed pairs and the
+// budget flag.
+template <int E>
+__device__ __forceinline__ void emit_prefix(const int (&id)[E], int nkv, const int* off, int64_t Tk, int lane,
+                                            int n_text, int* out, int* cnt_out, int64_t ga, int64_t* pairs,
+                                            int* gflag) {
   int loc[E], s = 0;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
@@ -371,11 +693,354 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   if (lane == 0) {
     int cnt = L;
     if (n_text > 0) out[cnt++] = nkv;
-    sel_cnt[size_t(hd) * (Cq + 1) + a] = cnt;
-    if (keys < Tk) atomicOr(gstat + hd * 8 + 0, SPR_HS_BUDGET_UNREACHED);
-    const int64_t ga = q_off[size_t(hd) * (Cq + 1) + a + 1] - q_off[size_t(hd) * (Cq + 1) + a];
-    atomicAdd(reinterpret_cast<unsigned long long*>(pairs + hd), (unsigned long long)(ga * (keys + n_text)));
+    *cnt_out = cnt;
+    if (keys < Tk) atomicOr(gflag, SPR_HS_BUDGET_UNREACHED);
+    atomicAdd(reinterpret_cast<unsigned long long*>(pairs), (unsigned long long)(ga * (keys + n_text)));
   }
+}
+
+// Budgeted prefix for one query group from fp64 scores, one wave per group.  The group past the
+// last query group (index n_q) is the text query group, which selects every group.
+template <int E>
+__global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ scores,
+                                                           const int* __restrict__ kv_off,
+                                                           const int* __restrict__ q_off,
+                                                           const int* __restrict__ n_q, const int* __restrict__ n_kv,
+                                                           int Cq, int Ck, int G, int n_text, int64_t Tk,
+                                                           int* __restrict__ sel_cnt, int* __restrict__ sel_kv,
+                                                           int64_t* __restrict__ pairs, int* __restrict__ gstat) {
+  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nq = n_q[hd], nkv = n_kv[hk];
+  const int* off = kv_off + size_t(hk) * (Ck + 1);
+  if (a > nq || (a == nq && n_text == 0)) return;
+  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
+  if (a == nq) {  // text query rows: every group
+    for (int b = lane; b <= nkv; b += 64) out[b] = b;
+    if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
+    return;
+  }
+  double sc[E], none[1][E];
+  int id[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int i = lane * E + t;
+    sc[t] = i < nkv ? scores[(size_t(hd) * Cq + a) * Ck + i] : -1.0e308;
+    id[t] = i < nkv ? i : 0x7fffffff;
+  }
+  wave_sort_desc<E, 0>(sc, id, none, lane);
+  const int64_t ga = q_off[size_t(hd) * (Cq + 1) + a + 1] - q_off[size_t(hd) * (Cq + 1) + a];
+  emit_prefix<E>(id, nkv, off, Tk, lane, n_text, out, sel_cnt + size_t(hd) * (Cq + 1) + a, ga, pairs + hd,
+                 gstat + hd * 8 + 0);
+}
+
+// fp64 score of K/V group b for one query group (qbar in LDS), by the whole wave: lanes take the
+// keys of the group (all loads of a lane's key row and statistics issued before any use), each
+// logit an fp64 dot product, then the sums of the score expansion.
+// (The pointers carry their address spaces: the function is not inlined, and generic pointers
+// would turn the LDS reads into flat loads.)
+typedef __attribute__((address_space(3))) const double lds_cdouble;
+typedef unsigned int ru32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const ru32x4_t glb_cuint4;
+typedef __attribute__((address_space(1))) const double glb_cdouble;
+template <int DT, int D>
+__device__ __attribute__((noinline)) double route_exact_score(glb_cuint4* Kp, int N, int Nv, lds_cdouble* qs,
+                                                              glb_cdouble* vbar, glb_cdouble* vstat, double lb,
+                                                              double m, int k0, int k1, int hk, int Ck, int b,
+                                                              int lane) {
+  constexpr int PER = DT == SPR_BF16 ? 8 : 4;  // elements per 16-byte load
+  const double inv = 1.0 / sqrt(double(D));
+  double vn = 0.0;
+  for (int c = lane; c < D; c += 64) {
+    const double y = vbar[(size_t(hk) * Ck + b) * D + c];
+    vn = fma(y, y, vn);
+  }
+  double s1 = 0.0, s2 = 0.0;
+  for (int j0 = k0; j0 < k1; j0 += 64) {
+    const int j = min(j0 + lane, k1 - 1);
+    glb_cuint4* kr = Kp + (int64_t(hk) * N + j) * (D / PER);
+    ru32x4_t raw[D / PER];
+#pragma unroll
+    for (int i = 0; i < D / PER; ++i) raw[i] = kr[i];
+    const double uw_x = vstat[(size_t(hk) * Nv + j) * 4], uw_y = vstat[(size_t(hk) * Nv + j) * 4 + 1];
+    double l = 0.0;
+#pragma unroll
+    for (int i = 0; i < D / PER; ++i) {
+      const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (DT == SPR_BF16) {
+          l = fma(qs[i * 8 + 2 * h], double(__uint_as_float(wd[h] << 16)), l);
+          l = fma(qs[i * 8 + 2 * h + 1], double(__uint_as_float(wd[h] & 0xFFFF0000u)), l);
+        } else {
+          l = fma(qs[i * 4 + h], double(__uint_as_float(wd[h])), l);
+        }
+      }
+    }
+    if (j0 + lane < k1) {
+      const double Ej = exp(fma(l, inv, -m));
+      s1 = fma(Ej, uw_x, s1);
+      s2 = fma(Ej * Ej, uw_y, s2);
+    }
+  }
+  vn = wave_sum_d(vn);
+  s1 = wave_sum_d(s1);
+  s2 = wave_sum_d(s2);
+  const double g = double(k1 - k0);
+  const double A = exp(lb - m);
+  return A * A * vn - 2.0 * A * s1 / g + s2 / g;
+}
+
+// Routing of one query group from the bf16 scores and their bounds, one wave per group.  With
+// I_b = [s_b - e_b, s_b + e_b] holding the exact score:
+//   1. scores whose bound is not finite or above 1e-3 of the row's largest score are recomputed
+//      in fp64;
+//   2. the groups are ranked by score, and lambda' is the smallest lower end among the shortest
+//      ranked prefix holding Tk keys.  A group whose upper end is below lambda' is preceded (in
+//      exact order) by groups holding at least Tk keys, so it is outside the prefix; it ranks
+//      last (a stable partition through LDS);
+//   3. among the others, in rank order, a group meets an earlier interval iff the smallest
+//      earlier lower end reaches its upper end, and a later one iff the largest later upper end
+//      reaches its lower end; such groups get an fp64 score;
+//   4. a group left with its bf16 score is disjoint from every other interval, so it sits
+//      correctly against every score of the row; the recomputed groups form runs of consecutive
+//      ranks (a group between two overlapping intervals meets one of them), which odd-even
+//      transposition passes put in order.  The ranking is then that of the fp64 scores.
+template <int E, int DT, int D>
+__global__ __launch_bounds__(256) void route_resolve_kernel(
+    const double* __restrict__ scores, const double* __restrict__ serr, double* __restrict__ scores_out,
+    double* __restrict__ serr_out, const void* __restrict__ Kp, int N, int Nv, const double* __restrict__ qbar,
+    const double* __restrict__ lbar, const double* __restrict__ vbar, const double* __restrict__ shift,
+    const double* __restrict__ vstat, const int* __restrict__ kv_off, const int* __restrict__ q_off,
+    const int* __restrict__ n_q, const int* __restrict__ n_kv, int Cq, int Ck, int G, int n_text, int64_t Tk,
+    int* __restrict__ sel_cnt, int* __restrict__ sel_kv, int64_t* __restrict__ pairs, int* __restrict__ gstat) {
+  __shared__ __attribute__((aligned(16))) double qs[4][D];
+  __shared__ double part_val[4][64 * E];
+  __shared__ int part_id[4][64 * E];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + w;
+  const int nq = n_q[hd], nkv = n_kv[hk];
+  const int* off = kv_off + size_t(hk) * (Ck + 1);
+  if (a > nq || (a == nq && n_text == 0)) return;
+  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
+  if (a == nq) {  // text query rows: every group
+    for (int b = lane; b <= nkv; b += 64) out[b] = b;
+    if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
+    return;
+  }
+  const size_t row = (size_t(hd) * Cq + a) * Ck;
+  for (int c = lane; c < D; c += 64) qs[w][c] = qbar[(size_t(hd) * Cq + a) * D + c];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const double m = shift[size_t(hd) * Cq + a];
+  const bool keep = scores_out != nullptr;
+  double sc[E], pl[1][E];  // score and its bound
+  int id[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    const int i = lane * E + t;
+    sc[t] = i < nkv ? scores[row + i] : 0.0;
+    pl[0][t] = i < nkv ? serr[row + i] : 0.0;
+    id[t] = i < nkv ? i : 0x7fffffff;
+  }
+  // recompute, one group at a time, every entry whose flag is set
+  bool any_fixed = false;
+  auto resolve = [&](bool (&flag)[E]) {
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      unsigned long long mk = __ballot(flag[t]);
+      any_fixed |= mk != 0ull;
+      while (mk) {
+        const int src = __ffsll(mk) - 1;
+        mk &= mk - 1;
+        const int b = __shfl(id[t], src);
+        const double v = route_exact_score<DT, D>(
+            (glb_cuint4*)Kp, N, Nv, (lds_cdouble*)qs[w], (glb_cdouble*)vbar, (glb_cdouble*)vstat, lbar[row + b], m,
+            off[b], off[b + 1], hk, Ck, b, lane);
+        if (lane == src) {
+          sc[t] = v;
+          pl[0][t] = 0.0;
+        }
+      }
+    }
+  };
+  // 1. bounds that would overlap most of the row
+  double rmax = 0.0;
+#pragma unroll
+  for (int t = 0; t < E; ++t)
+    if (id[t] < nkv) rmax = fmax(rmax, fabs(sc[t]));
+  for (int o = 32; o > 0; o >>= 1) rmax = fmax(rmax, __shfl_xor(rmax, o));
+  bool flag[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) flag[t] = id[t] < nkv && !(pl[0][t] <= 1e-3 * rmax);
+  resolve(flag);
+  // 2. rank by score; lambda' = the smallest lower end among the shortest ranked prefix holding
+  //    Tk keys.  Those groups hold at least Tk keys with lower ends >= lambda', so a group whose
+  //    upper end is below lambda' is outside the prefix (-inf when Tk is out of reach)
+#pragma unroll
+  for (int t = 0; t < E; ++t)
+    if (id[t] >= nkv) sc[t] = -1.0e308;
+  wave_sort_desc<E, 1>(sc, id, pl, lane);
+  int sz[E], s_loc = 0;
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    sz[t] = id[t] < nkv ? off[id[t] + 1] - off[id[t]] : 0;
+    s_loc += sz[t];
+  }
+  int incl = s_loc;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  double lam = INFINITY;
+  {
+    int cum = incl - s_loc;
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      if (id[t] < nkv && cum < Tk) lam = fmin(lam, sc[t] - pl[0][t]);  // ranks up to the crossing
+      cum += sz[t];
+    }
+    for (int o = 32; o > 0; o >>= 1) lam = fmin(lam, __shfl_xor(lam, o));
+    if (__shfl(incl, 63) < Tk) lam = -INFINITY;
+  }
+  // 3. stable partition through LDS: the groups that can be in the prefix first, in rank order
+  //    (their scores and bounds are written out now for the others)
+  bool in[E];
+  int n_in_l = 0;
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    in[t] = id[t] < nkv && sc[t] + pl[0][t] >= lam;
+    n_in_l += in[t] ? 1 : 0;
+    if (keep && id[t] < nkv && !in[t]) {
+      scores_out[row + id[t]] = sc[t];
+      serr_out[row + id[t]] = -(pl[0][t] + 1.0e-300);
+    }
+  }
+  int in_incl = n_in_l;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(in_incl, o);
+    if (lane >= o) in_incl += y;
+  }
+  const int n_in = __shfl(in_incl, 63);
+  {
+    const int r_in0 = in_incl - n_in_l, r_out0 = n_in + (lane * E - (in_incl - n_in_l));
+    double* vs = &part_val[w][0];
+    int* is = &part_id[w][0];
+    auto wave_sync = [] {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    int r_in = r_in0, r_out = r_out0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) {  // keys and ids
+      const int dst = in[t] ? r_in++ : r_out++;
+      vs[dst] = in[t] ? sc[t] : (id[t] < nkv ? -1.0e300 : -1.0e308);
+      is[dst] = id[t];
+    }
+    wave_sync();
+    double nk[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      nk[t] = vs[lane * E + t];
+      id[t] = is[lane * E + t];
+    }
+    wave_sync();
+    r_in = r_in0;
+    r_out = r_out0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) vs[in[t] ? r_in++ : r_out++] = pl[0][t];  // bounds
+    wave_sync();
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      sc[t] = nk[t];
+      pl[0][t] = vs[lane * E + t];
+      in[t] = lane * E + t < n_in;
+    }
+  }
+  // overlaps among the groups that can be in the prefix: in rank order a group meets an earlier
+  // interval iff the smallest earlier lower end reaches its upper end, a later one iff the
+  // largest later upper end reaches its lower end
+  double lmin = INFINITY, hmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < E; ++t)
+    if (in[t]) {
+      lmin = fmin(lmin, sc[t] - pl[0][t]);
+      hmax = fmax(hmax, sc[t] + pl[0][t]);
+    }
+  double pmin = lmin, smax = hmax;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(pmin, o), z = __shfl_down(smax, o);
+    if (lane >= o) pmin = fmin(pmin, y);
+    if (lane + o < 64) smax = fmax(smax, z);
+  }
+  double run_lo = __shfl_up(pmin, 1), run_hi = __shfl_down(smax, 1);
+  if (lane == 0) run_lo = INFINITY;
+  if (lane == 63) run_hi = -INFINITY;
+  double before_lo[E];
+#pragma unroll
+  for (int t = 0; t < E; ++t) {
+    before_lo[t] = run_lo;
+    if (in[t]) run_lo = fmin(run_lo, sc[t] - pl[0][t]);
+  }
+#pragma unroll
+  for (int t = E - 1; t >= 0; --t) {
+    const double lo = sc[t] - pl[0][t], hi = sc[t] + pl[0][t];
+    flag[t] = in[t] && pl[0][t] > 0.0 && (before_lo[t] <= hi || run_hi >= lo);
+    if (in[t]) run_hi = fmax(run_hi, hi);
+  }
+  any_fixed = false;
+  resolve(flag);
+  // 4. odd-even transposition passes over the first n_in ranks until their ranking is that of
+  //    the scores
+  if (__any(any_fixed)) {
+    auto before = [](double s1, int i1, double s2, int i2) { return s1 > s2 || (s1 == s2 && i1 < i2); };
+    auto pass = [&](int parity) -> bool {
+      bool sw_any = false;
+#pragma unroll
+      for (int t = 0; t + 1 < E; ++t)
+        if (((lane * E + t) & 1) == parity && lane * E + t + 1 < n_in &&
+            before(sc[t + 1], id[t + 1], sc[t], id[t])) {
+          const double ts = sc[t], te = pl[0][t];
+          const int ti = id[t];
+          sc[t] = sc[t + 1]; pl[0][t] = pl[0][t + 1]; id[t] = id[t + 1];
+          sc[t + 1] = ts; pl[0][t + 1] = te; id[t + 1] = ti;
+          sw_any = true;
+        }
+      // the pair (last of this lane, first of the next lane)
+      const double ns = __shfl_down(sc[0], 1), ne = __shfl_down(pl[0][0], 1);
+      const int ni = __shfl_down(id[0], 1);
+      const double ps = __shfl_up(sc[E - 1], 1), pe = __shfl_up(pl[0][E - 1], 1);
+      const int pi = __shfl_up(id[E - 1], 1);
+      const bool mine = lane < 63 && ((lane * E + E - 1) & 1) == parity && (lane + 1) * E < n_in &&
+                        before(ns, ni, sc[E - 1], id[E - 1]);
+      const bool take = __shfl_up(mine ? 1 : 0, 1) != 0 && lane > 0;
+      if (mine) {
+        sc[E - 1] = ns; pl[0][E - 1] = ne; id[E - 1] = ni;
+        sw_any = true;
+      }
+      if (take) {
+        sc[0] = ps; pl[0][0] = pe; id[0] = pi;
+      }
+      return __any(sw_any);
+    };
+    for (;;) {
+      const bool s0 = pass(0);
+      const bool s1 = pass(1);
+      if (!s0 && !s1) break;
+    }
+  }
+  if (keep) {
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+      if (sc[t] > -1.0e299) {
+        scores_out[row + id[t]] = sc[t];
+        serr_out[row + id[t]] = pl[0][t];
+      }
+  }
+  const int64_t ga = q_off[size_t(hd) * (Cq + 1) + a + 1] - q_off[size_t(hd) * (Cq + 1) + a];
+  emit_prefix<E>(id, nkv, off, Tk, lane, n_text, out, sel_cnt + size_t(hd) * (Cq + 1) + a, ga, pairs + hd,
+                 gstat + hd * 8 + 0);
 }
 
 __global__ void zero_i64_kernel(int64_t* p, int n) {
@@ -550,26 +1215,66 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   if (d == 128) {
     hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
                        part.n_kv, p.Cq, p.Ck, G, lbar);
-    hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
-                       p.Cq, p.Ck, G, shift);
-    allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
-    hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), route_score_smem<128>(), st, part.Kp, N, Nv,
-                       part.qbar, lbar,
-                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat, scores);
   } else {
     hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
                        part.n_kv, p.Cq, p.Ck, G, lbar);
-    hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
-                       p.Cq, p.Ck, G, shift);
-    allow_lds(route_score_kernel<DT, 64>, route_score_smem<64>());
-    hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), route_score_smem<64>(), st, part.Kp, N, Nv,
-                       part.qbar, lbar,
-                       part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat, scores);
   }
-  SPR_CHECK_LAUNCH();
+  hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
+                     p.Cq, p.Ck, G, shift);
   hipLaunchKernelGGL(zero_i64_kernel, dim3(ceil_div(BH, 256)), dim3(256), 0, st, out.pairs, BH);
-  {
-    const dim3 grid(ceil_div(p.Cq + 1, 4), BH);
+  const dim3 grid(ceil_div(p.Cq + 1, 4), BH);
+  if constexpr (DT == SPR_BF16) {
+    // bf16 keys: scores on the bf16 matrix cores with bounds, fp64 where the selection needs it
+    double* serr = out.score_err ? out.score_err : ws_ptr<double>(ws, L.serr);
+    const unsigned nblk = unsigned(route_fast_blocks(p.Cq, p.Ck, BH));
+    auto fast = [&](auto kern, size_t smem) {
+      allow_lds(kern, smem);
+      hipLaunchKernelGGL(kern, dim3(nblk), dim3(kFastWaves * 64), smem, st, static_cast<const uint16_t*>(part.Kp), N, Nv,
+                         part.qbar, lbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, BH, shift,
+                         vstat, scores, serr);
+    };
+    if (d == 128) fast(route_score_fast_kernel<128>, route_fast_smem<128>());
+    else fast(route_score_fast_kernel<64>, route_fast_smem<64>());
+    SPR_CHECK_LAUNCH();
+    const bool keep = out.scores || out.score_err;
+    double* keep_s = keep ? scores : nullptr;
+    double* keep_e = keep ? serr : nullptr;
+    auto res = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, scores, serr, keep_s, keep_e, part.Kp, N, Nv, part.qbar,
+                         lbar, part.vbar, shift, vstat, part.kv_off, part.q_off, part.n_q, part.n_kv, p.Cq, p.Ck, G,
+                         desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
+    };
+    if (d == 128) {
+      if (p.Ck <= 64) res(route_resolve_kernel<1, DT, 128>);
+      else if (p.Ck <= 128) res(route_resolve_kernel<2, DT, 128>);
+      else if (p.Ck <= 256) res(route_resolve_kernel<4, DT, 128>);
+      else if (p.Ck <= 512) res(route_resolve_kernel<8, DT, 128>);
+      else res(route_resolve_kernel<16, DT, 128>);
+    } else {
+      if (p.Ck <= 64) res(route_resolve_kernel<1, DT, 64>);
+      else if (p.Ck <= 128) res(route_resolve_kernel<2, DT, 64>);
+      else if (p.Ck <= 256) res(route_resolve_kernel<4, DT, 64>);
+      else if (p.Ck <= 512) res(route_resolve_kernel<8, DT, 64>);
+      else res(route_resolve_kernel<16, DT, 64>);
+    }
+  } else {
+    if (d == 128) {
+      allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
+      hipLaunchKernelGGL((route_score_kernel<DT, 128>), sgrid, dim3(256), route_score_smem<128>(), st, part.Kp, N,
+                         Nv, part.qbar, lbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat,
+                         scores);
+    } else {
+      allow_lds(route_score_kernel<DT, 64>, route_score_smem<64>());
+      hipLaunchKernelGGL((route_score_kernel<DT, 64>), sgrid, dim3(256), route_score_smem<64>(), st, part.Kp, N,
+                         Nv, part.qbar, lbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, shift, vstat,
+                         scores);
+    }
+    if (out.score_err) {
+      const int64_t n = int64_t(BH) * p.Cq * p.Ck;
+      hipLaunchKernelGGL(zero_i64_kernel, dim3(unsigned(ceil_div64(n, 256))), dim3(256), 0, st,
+                         reinterpret_cast<int64_t*>(out.score_err), int(n));
+    }
+    SPR_CHECK_LAUNCH();
     auto sel = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, scores, part.kv_off, part.q_off, part.n_q, part.n_kv, p.Cq,
                          p.Ck, G, desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);

@@ -42,7 +42,7 @@ class spr_part_params(ctypes.Structure):
 
 _PART_FIELDS = ["kv_label", "q_label", "kv_perm", "q_perm", "q_pos", "kv_off", "q_off", "n_kv", "n_q", "kbar",
                 "vbar", "qbar", "qdist", "FK", "FQ", "Qp", "Kp", "Vp", "phiK", "phiQ", "cK_last", "cQ_last", "passes"]
-_ROUTE_FIELDS = ["sel_cnt", "sel_kv", "probe_idx", "probe_w", "pairs", "rho_exec", "scores"]
+_ROUTE_FIELDS = ["sel_cnt", "sel_kv", "probe_idx", "probe_w", "pairs", "rho_exec", "scores", "score_err"]
 
 
 class spr_partition(ctypes.Structure):
@@ -264,6 +264,7 @@ class Route:
         self.pairs = z((BH,), torch.int64)
         self.rho_exec = z((BH,), torch.float64)
         self.scores = z((BH, cfg.Cq, cfg.Ck), torch.float64) if keep_scores else None
+        self.score_err = z((BH, cfg.Cq, cfg.Ck), torch.float64) if keep_scores else None
         self.struct = spr_route(*[_ptr(getattr(self, n)) for n in _ROUTE_FIELDS])
 
 

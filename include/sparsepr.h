@@ -178,6 +178,9 @@ typedef struct {
   int64_t* pairs;     /* [BH] routed query-key pairs, text keys of video rows included */
   double* rho_exec;   /* [BH] executed-pair density incl. probes and text rows */
   double* scores;     /* optional [BH][Cq][Ck] routing scores times a positive per-row factor */
+  double* score_err;  /* optional [BH][Cq][Ck] bound on |scores - exact score| (same factor): 0 where
+                                 the score was computed in fp64 (every score of fp32 inputs),
+                                 negated where the group cannot enter the budgeted prefix */
 } spr_route;
 
 /* Probe choice of sparsepr_route (Table 4; App. D.3).  Weights w_p: |G_a| / m_a for stratified

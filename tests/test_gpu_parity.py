@@ -259,6 +259,21 @@ def test_warm_start_factor_ranks(name, rK, rQ):
             assert np.abs(A - Ao).max() <= 1e-9 * np.abs(Ao).max()
 
 
+def _check_scores(gs, ge, sc):
+    """GPU scores of one row against the oracle's: equal up to one positive row factor, within the
+    bound the GPU reports for each score (0 where it was computed in fp64) plus fp64 rounding."""
+    ge = np.abs(ge)
+    assert np.all(np.isfinite(ge))
+    exact = ge == 0
+    r = int(np.argmax(np.where(exact, sc, -np.inf))) if exact.any() else int(np.argmax(sc))
+    f = gs[r] / sc[r]                                            # one positive factor per row
+    assert f > 0
+    rel_f = ge[r] / gs[r]                                        # uncertainty of that factor
+    assert rel_f < 1e-2
+    tol = ge + rel_f / (1 - rel_f) * f * np.abs(sc) + 1e-9 * f * sc.max()
+    assert np.all(np.abs(gs - f * sc) <= tol)
+
+
 def test_lockstep_stages_small():
     """Each stage's oracle function applied to the GPU's own inputs of that stage."""
     cfg = config("small")
@@ -289,16 +304,13 @@ def test_lockstep_stages_small():
         sc, _ = O.route_scores(g["qbar"][hd][:nq], kh, vh, kvl, g["kbar"][hd][:nkv], g["vbar"][hd][:nkv],
                                groups=range(0, nq, 9))
         for ia, a in enumerate(range(0, nq, 9)):
-            gs = g["scores"][hd][a][:nkv]
-            top = int(np.argmax(sc[ia]))
-            f = gs[top] / sc[ia][top]                                # one positive factor per row
-            assert f > 0
-            np.testing.assert_allclose(gs, f * sc[ia], rtol=0, atol=1e-9 * f * sc[ia][top])
-        # selections from the GPU's scores
+            _check_scores(g["scores"][hd][a][:nkv], g["score_err"][hd][a][:nkv], sc[ia])
+        # selections from the GPU's scores (groups flagged as outside the prefix rank last)
         size = np.diff(g["kv_off"][hd][: nkv + 1])
         T = O.key_budget(opc.rho, cfg.N, cfg.Nv, opc.M, 0)
         for a in range(nq):
-            sel, info = O.route_select(g["scores"][hd][a][:nkv], size, T)
+            gs = np.where(g["score_err"][hd][a][:nkv] < 0, -1e300, g["scores"][hd][a][:nkv])
+            sel, info = O.route_select(gs, size, T)
             cnt = int(g["sel_cnt"][hd][a])
             assert list(g["sel_kv"][hd][a][:cnt]) == list(sel)
         # probes from the GPU's groups and distances
@@ -542,3 +554,35 @@ def test_probe_and_estimator_variants(name, heads, probe_mode, family, out_rank)
         # probe rows are the exact rows (up to the output's rounding)
         err = row_rel_err(g["out"][hd][P], g["o_probe"][hd])
         assert err.max() < ROW_TOL
+
+
+@pytest.mark.gpu
+def test_bf16_score_bounds_small():
+    """bf16 keys: every routing score of two heads lies within its reported bound of the oracle's
+    fp64 score (one positive factor per row), the bounds are tight enough to leave most scores
+    unrecomputed, and each selection equals the oracle's selection on the oracle's scores unless
+    the oracle's boundary gap is a tie."""
+    cfg = config("small")
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    T = O.key_budget(opc.rho, cfg.N, cfg.Nv, opc.M, 0)
+    n_exact = n_all = n_out = 0
+    for hd in (3, 8):
+        kh, vh = (x[0, hd].astype(np.float64) for x in (k, v))
+        nkv, nq = int(g["n_kv"][hd]), int(g["n_q"][hd])
+        sc, _ = O.route_scores(g["qbar"][hd][:nq], kh, vh, g["kv_label"][hd], g["kbar"][hd][:nkv],
+                               g["vbar"][hd][:nkv])
+        size = np.diff(g["kv_off"][hd][: nkv + 1])
+        for a in range(nq):
+            ge = g["score_err"][hd][a][:nkv]
+            _check_scores(g["scores"][hd][a][:nkv], ge, sc[a])
+            n_exact += int((ge == 0).sum())
+            n_out += int((ge < 0).sum())
+            n_all += nkv
+            sel, info = O.route_select(sc[a], size, T)
+            if info["min_gap"] > TIE:
+                cnt = int(g["sel_cnt"][hd][a])
+                assert list(g["sel_kv"][hd][a][:cnt]) == list(sel), (hd, a)
+    assert n_exact < 0.2 * n_all and n_out > 0.3 * n_all, (n_exact, n_out, n_all)
