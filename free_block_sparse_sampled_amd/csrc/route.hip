@@ -330,6 +330,26 @@ __device__ __forceinline__ float lanes_max16(float x) {
 __device__ __forceinline__ float sel4f(const float (&x)[4], int v) {
   return v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
 }
+template <int CTRL>
+__device__ __forceinline__ double dppd(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_update_dpp(0, unsigned(u), CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0, unsigned(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+__device__ __forceinline__ double readlane_dbl(double x, int l) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_readlane(unsigned(u), l), hi = __builtin_amdgcn_readlane(unsigned(u >> 32), l);
+  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+// sum over the 64 lanes (all active): DPP sums over each 16-lane row, then the four rows
+__device__ __forceinline__ double wave_allsum_d(double x) {
+  x += dppd<0xB1>(x);
+  x += dppd<0x4E>(x);
+  x += dppd<0x141>(x);
+  x += dppd<0x140>(x);
+  return (readlane_dbl(x, 0) + readlane_dbl(x, 16)) + (readlane_dbl(x, 32) + readlane_dbl(x, 48));
+}
 constexpr int kFastPiece = 64;
 constexpr int kFastWaves = 8;
 template <int D>
@@ -422,33 +442,42 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
   };
   if (tid < 16) p0s[tid] = 0.0;
 
-  uint4 pk[KPT];
-  double pu = 0.0, pw = 0.0, pr = 0.0;
-  auto fetch = [&](int b, int p0) __attribute__((always_inline)) {
+  // two register sets: the loads of a piece are issued two pieces before it is staged
+  constexpr int KW = PIECE / 64;  // keys of a piece per lane of wave 0 (statistics)
+  uint4 pk[2][KPT];
+  double pu[2][KW], pw[2][KW], pr[2] = {0.0, 0.0};
+  auto fetch = [&](auto set, int b, int p0) __attribute__((always_inline)) {
+    constexpr int S = decltype(set)::value;
     const int n = min(PIECE, off[b + 1] - p0);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = tid + NTH * i, row = e / KPR, pc = e % KPR;
-      pk[i] = make_uint4(0, 0, 0, 0);
-      if (row < n) pk[i] = *reinterpret_cast<const uint4*>(Kh + size_t(p0 + row) * D + pc * 8);
+      pk[S][i] = make_uint4(0, 0, 0, 0);
+      if (row < n) pk[S][i] = *reinterpret_cast<const uint4*>(Kh + size_t(p0 + row) * D + pc * 8);
     }
-    if (tid < PIECE) {
-      const double* st4 = vstat + (size_t(hk) * Nv + p0 + tid) * 4;
-      pw = tid < n ? st4[1] : 0.0;
-      pu = tid < n ? st4[2] : 0.0;
-      pr = tid < n ? st4[3] : 0.0;
+    if (tid < 64) {
+      pr[S] = 0.0;
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const int jl = tid + 64 * k;
+        const double* st4 = vstat + (size_t(hk) * Nv + p0 + jl) * 4;
+        pw[S][k] = jl < n ? st4[1] : 0.0;
+        pu[S][k] = jl < n ? st4[2] : 0.0;
+        pr[S] += jl < n ? st4[3] : 0.0;
+      }
     }
   };
   // registers -> LDS buffer: key rows (16-byte piece p of row r at p ^ (r % KPR)), c, |v|^2,
   // |k|; the piece's sum of r_j is added to its group's (wave 0)
-  auto put = [&](int bi, int bgrp) __attribute__((always_inline)) {
+  auto put = [&](auto set, int bi, int bgrp) __attribute__((always_inline)) {
+    constexpr int S = decltype(set)::value;
     uint16_t* K = reinterpret_cast<uint16_t*>(rf_sm + bi * BUF);
     float* F = reinterpret_cast<float*>(rf_sm + bi * BUF + size_t(PIECE) * D * 2);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = tid + NTH * i, row = e / KPR, pc = e % KPR;
-      *reinterpret_cast<uint4*>(K + row * D + ((pc ^ (row % KPR)) * 8)) = pk[i];
-      const uint32_t wd[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+      *reinterpret_cast<uint4*>(K + row * D + ((pc ^ (row % KPR)) * 8)) = pk[S][i];
+      const uint32_t wd[4] = {pk[S][i].x, pk[S][i].y, pk[S][i].z, pk[S][i].w};
       float sq = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -458,26 +487,40 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
       sq = KPR == 16 ? lanes_sum16(sq) : lanes_sum8(sq);
       if (pc == 0) F[2 * PIECE + row] = sqrtf(sq);
     }
-    if (tid < PIECE) {
-      F[tid] = float(pu);
-      F[PIECE + tid] = float(pw);
-      const double rs = wave_sum_d(pr);
+    if (tid < 64) {
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        F[tid + 64 * k] = float(pu[S][k]);
+        F[PIECE + tid + 64 * k] = float(pw[S][k]);
+      }
+      const double rs = wave_allsum_d(pr[S]);
       if (tid == 0) p0s[bgrp - b0] += rs;
     }
   };
 
   const float c2 = 1.4426950408889634f / sqrtf(float(D));
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // pieces: cur (in LDS buffer buf), nxt (register set of the other parity, loads in flight),
+  // nn (loaded next); a piece position is (group, first key), group b1 once past the end
+  auto advance = [&](int& pb, int& pp) {
+    pp += PIECE;
+    if (pp >= off[pb + 1]) {
+      ++pb;
+      pp = pb < b1 ? off[pb] : 0;
+    }
+  };
   int b = b0, p0 = off[b0];
-  fetch(b, p0);
+  int nb = b, np0 = p0;
+  advance(nb, np0);
+  int nnb = nb, nnp0 = np0;
+  if (nnb < b1) advance(nnb, nnp0);
+  fetch(S0{}, b, p0);
+  if (nb < b1) fetch(S1{}, nb, np0);
   __syncthreads();  // p0s cleared, lbs filled
-  put(0, b);
+  put(S0{}, 0, b);
   load_shift(b);
   __syncthreads();
-  int nb = b, np0 = p0 + PIECE;
-  if (np0 >= off[nb + 1]) {
-    ++nb;
-    np0 = nb < b1 ? off[nb] : 0;
-  }
   // per output slot: P1 = sum delta c, P2 = sum delta^2 |v|^2 and the three bound sums
   float P1[4], P2[4], B1[4], B2[4], B3[4];
 #pragma unroll
@@ -485,9 +528,11 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
   float kmax = 0.f;
   float kP1 = 0.f, kP2 = 0.f, kB1 = 0.f, kB2 = 0.f, kB3 = 0.f, kK = 0.f;  // this lane's pair of the batch
   int slot = 0, gstart = b0, buf = 0;
-  for (;;) {
-    const bool has_next = nb < b1;
-    if (has_next) fetch(nb, np0);
+  // one piece: set S held cur (staged), set S ^ 1 holds nxt; returns false after the last piece
+  auto step = [&](auto set) __attribute__((always_inline)) -> bool {
+    constexpr int S = decltype(set)::value;
+    using SO = std::integral_constant<int, S ^ 1>;
+    if (nnb < b1) fetch(set, nnb, nnp0);
     const int n = min(PIECE, off[b + 1] - p0);
     {
       const uint16_t* K = reinterpret_cast<const uint16_t*>(rf_sm + buf * BUF);
@@ -581,18 +626,19 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
         gstart = b + 1;
       }
     }
-    if (!has_next) break;
-    put(buf ^ 1, nb);
+    if (nb >= b1) return false;
+    put(SO{}, buf ^ 1, nb);
     __syncthreads();
     buf ^= 1;
     if (nb != b) load_shift(nb);
     b = nb;
     p0 = np0;
-    np0 += PIECE;
-    if (np0 >= off[nb + 1]) {
-      ++nb;
-      np0 = nb < b1 ? off[nb] : 0;
-    }
+    nb = nnb;
+    np0 = nnp0;
+    if (nnb < b1) advance(nnb, nnp0);
+    return true;
+  };
+  while (step(S0{}) && step(S1{})) {
   }
 }
 
@@ -782,9 +828,9 @@ __device__ __attribute__((noinline)) double route_exact_score(glb_cuint4* Kp, in
       s2 = fma(Ej * Ej, uw_y, s2);
     }
   }
-  vn = wave_sum_d(vn);
-  s1 = wave_sum_d(s1);
-  s2 = wave_sum_d(s2);
+  vn = wave_allsum_d(vn);
+  s1 = wave_allsum_d(s1);
+  s2 = wave_allsum_d(s2);
   const double g = double(k1 - k0);
   const double A = exp(lb - m);
   return A * A * vn - 2.0 * A * s1 / g + s2 / g;
@@ -816,6 +862,7 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
   __shared__ __attribute__((aligned(16))) double qs[4][D];
   __shared__ double part_val[4][64 * E];
   __shared__ int part_id[4][64 * E];
+  __shared__ int q_cnt[4];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + w;
   const int nq = n_q[hd], nkv = n_kv[hk];
@@ -989,8 +1036,59 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
     flag[t] = in[t] && pl[0][t] > 0.0 && (before_lo[t] <= hi || run_hi >= lo);
     if (in[t]) run_hi = fmax(run_hi, hi);
   }
+  // the four query groups of the block share their fp64 scores: each publishes its list in LDS,
+  // the waves take the block's items in turn, and each reads its own results back
+  {
+    int nmk = 0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) nmk += flag[t] ? 1 : 0;
+    int mincl = nmk;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(mincl, o);
+      if (lane >= o) mincl += y;
+    }
+    if (lane == 63) q_cnt[w] = mincl;
+    int k = mincl - nmk;
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+      if (flag[t]) part_id[w][k++] = id[t];
+  }
   any_fixed = false;
-  resolve(flag);
+  __syncthreads();
+  {
+    // waves whose query group does not exist (or is the text group) left early: no items
+    auto cnt_of = [&](int ow) { return blockIdx.x * 4 + ow < nq ? q_cnt[ow] : 0; };
+    const int c0 = cnt_of(0), c1 = c0 + cnt_of(1), c2 = c1 + cnt_of(2), tot = c2 + cnt_of(3);
+    for (int i = w; i < tot; i += 4) {
+      const int ow = i < c0 ? 0 : i < c1 ? 1 : i < c2 ? 2 : 3;
+      const int k = i - (ow == 0 ? 0 : ow == 1 ? c0 : ow == 2 ? c1 : c2);
+      const int oa = blockIdx.x * 4 + ow, b = part_id[ow][k];
+      const size_t orow = (size_t(hd) * Cq + oa) * Ck;
+      const double v = route_exact_score<DT, D>((glb_cuint4*)Kp, N, Nv, (lds_cdouble*)qs[ow], (glb_cdouble*)vbar,
+                                                (glb_cdouble*)vstat, lbar[orow + b], shift[size_t(hd) * Cq + oa],
+                                                off[b], off[b + 1], hk, Ck, b, lane);
+      if (lane == 0) part_val[ow][k] = v;
+    }
+  }
+  __syncthreads();
+  {
+    int nmk = 0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) nmk += flag[t] ? 1 : 0;
+    int mincl = nmk;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(mincl, o);
+      if (lane >= o) mincl += y;
+    }
+    int k = mincl - nmk;
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+      if (flag[t]) {
+        sc[t] = part_val[w][k++];
+        pl[0][t] = 0.0;
+      }
+    any_fixed = __any(nmk > 0);
+  }
   // 4. odd-even transposition passes over the first n_in ranks until their ranking is that of
   //    the scores
   if (__any(any_fixed)) {
