@@ -91,7 +91,7 @@ def affine_fit_energy(X: np.ndarray, D: np.ndarray, tol: float = 1e-10):
 def cpu_baseline(cfg, opc):
     """The oracle, untuned, on head 0 of the workload: partition, routing and probes in full,
     the sparse attention of 64 evenly spaced rows, the exact probe rows and the fit; scaled to
-    a whole call (every head, every attention row)."""
+    a whole call (every head, every attention row) and reported in the metric's unit."""
     import oracle as O
     from workloads import head_inputs
     try:
@@ -118,7 +118,10 @@ def cpu_baseline(cfg, opc):
     t_fit = time.perf_counter() - t0
     sample = t_part + t_rows + t_fit
     per_head = t_part + t_rows * (cfg.N / len(rows)) + t_fit
-    return {"value": per_head * cfg.heads * 1e3, "unit": "ms/call", "cores": int(cores), "kind": "oracle",
+    ms_call = per_head * cfg.heads * 1e3
+    dense_flops = 4.0 * cfg.heads * cfg.N * cfg.N * cfg.d
+    return {"value": dense_flops / (ms_call * 1e-3) / 1e12, "unit": "TFLOP/s (dense-equivalent attention, whole call)",
+            "ms_per_call": ms_call, "cores": int(cores), "kind": "oracle",
             "sample": (f"head 0 of {cfg.heads}: partition, routing and probes in full, sparse attention of "
                        f"{len(rows)} of {cfg.N} rows, probe rows and fit ({sample:.1f} s of CPU); scaled by "
                        f"rows and heads to one call (extrapolated)"),
