@@ -794,14 +794,75 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
 // ------------------------------------------------------------------ sparse tiles
 // Per head, the tile list of the block-sparse kernel: text rows first (they attend to every key,
 // so their tiles are the longest), then each query group of more than kHalfRows rows in tiles of
-// 2 kHalfRows rows, then the remaining groups paired in ascending id order.  A tile is
+// 2 kHalfRows rows, then the remaining (small) groups two to a tile.  A tile is
 // {a0, row0, n0, a1, row1, n1}: the query group, first Qp row and row count of each half.
+//
+// A paired tile runs over the union of its two selections, so the small groups are paired by
+// overlap (`ov`, the number of K/V groups two query groups both selected; null for ascending id
+// order): a few rounds of mutual best matches (each unmatched group finds the unmatched group
+// sharing the most K/V groups, ties to the lower rank; two groups that choose each other are
+// paired), then the rest in ascending id order.  The pairing changes no row's result.
+constexpr int kPairRounds = 4;
+constexpr size_t kTilesLds = 128 * 1024;  // LDS for the small groups' overlaps
+// Selections of the video query groups as bitmaps over K/V groups, one wave per query group.
+constexpr int kOvTile = 32, kOvWords = 16;  // up to 1024 K/V groups
+__global__ __launch_bounds__(256) void sel_bits_kernel(const int* __restrict__ n_q, const int* __restrict__ n_kv,
+                                                       const int* __restrict__ sel_cnt, const int* __restrict__ sel_kv,
+                                                       int Cq, int Ck, int G, int n_text,
+                                                       unsigned long long* __restrict__ bits) {
+  __shared__ unsigned long long wb[4][kOvWords];
+  const int hd = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63, a = blockIdx.x * 4 + w;
+  const int nq = n_q[hd], nkv = n_kv[hd / G];
+  if (a >= nq) return;
+  if (lane < kOvWords) wb[w][lane] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int* sl = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
+  const int cnt = sel_cnt[size_t(hd) * (Cq + 1) + a] - (n_text > 0 ? 1 : 0);
+  for (int k = lane; k < cnt; k += 64) {
+    const int b = sl[k];
+    if (b < nkv) atomicOr(&wb[w][b >> 6], 1ull << (b & 63));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < kOvWords) bits[(size_t(hd) * Cq + a) * kOvWords + lane] = wb[w][lane];
+}
+// Number of K/V groups two query groups both selected (saturated at 255), for every pair of video
+// query groups of a head: blocks of 32 x 32 pairs.
+__global__ __launch_bounds__(256) void pair_overlap_kernel(const int* __restrict__ n_q, const int* __restrict__ n_kv,
+                                                           const unsigned long long* __restrict__ bits, int Cq,
+                                                           int G, uint8_t* __restrict__ ov) {
+  __shared__ unsigned long long bt[2 * kOvTile][kOvWords];
+  const int hd = blockIdx.z, nq = n_q[hd], W = (n_kv[hd / G] + 63) / 64;
+  const int a0 = blockIdx.x * kOvTile, c0 = blockIdx.y * kOvTile;
+  if (a0 >= nq || c0 >= nq) return;
+  for (int e = threadIdx.x; e < 2 * kOvTile * kOvWords; e += 256) {
+    const int g = e / kOvWords, x = e % kOvWords;
+    const int a = g < kOvTile ? a0 + g : c0 + g - kOvTile;
+    bt[g][x] = a < nq ? bits[(size_t(hd) * Cq + a) * kOvWords + x] : 0ull;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kOvTile * kOvTile; e += 256) {
+    const int i = e / kOvTile, j = e % kOvTile, a = a0 + i, c = c0 + j;
+    if (a >= nq || c >= nq) continue;
+    int v = 0;
+    for (int x = 0; x < W; ++x) v += __popcll(bt[i][x] & bt[kOvTile + j][x]);
+    ov[(size_t(hd) * Cq + a) * Cq + c] = uint8_t(min(v, 255));
+  }
+}
 __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restrict__ q_off, const int* __restrict__ n_q,
-                                                            int Cq, int Nv, int n_text, int tmax,
+                                                            const int* __restrict__ n_kv,
+                                                            const int* __restrict__ sel_cnt,
+                                                            const int* __restrict__ sel_kv, int Cq, int Ck, int G,
+                                                            int Nv, int n_text, int tmax,
+                                                            const uint8_t* __restrict__ ov,
                                                             int* __restrict__ tiles, int* __restrict__ ntiles) {
-  __shared__ int buf[1024];
+  __shared__ int buf[1024], small_id[1024], partner[1024], best_of[1024];
+  extern __shared__ uint8_t ovs[];  // [n_small][n_small] overlaps of the small groups, when they fit
   const int hd = blockIdx.x, t = threadIdx.x;
-  const int nq = n_q[hd];
+  const int nq = n_q[hd], nkv = n_kv[hd / G];
   const int* qo = q_off + size_t(hd) * (Cq + 1);
   int* out = tiles + size_t(hd) * tmax * 8;
   constexpr int H2 = 2 * kHalfRows;
@@ -832,12 +893,78 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
       put(n_text_tiles + big_off + k, 1, t, r + kHalfRows, max(0, n - kHalfRows));
     }
   }
-  if (small) {
-    const int tile = n_text_tiles + n_big_tiles + small_rank / 2;
-    put(tile, small_rank & 1, t, qo[t], s);
-    if ((small_rank & 1) == 0 && small_rank == n_small - 1) put(tile, 1, t, qo[t], 0);  // no partner
+  // small groups by rank; partner[i] = rank of the paired group, -1 while unpaired
+  if (small) small_id[small_rank] = t;
+  if (t < n_small) partner[t] = -1;
+  if (ov) {
+    const uint8_t* ovh = ov + size_t(hd) * Cq * Cq;
+    // the small groups' overlaps gathered into LDS when they fit
+    const bool in_lds = size_t(n_small) * n_small <= kTilesLds;
+    __syncthreads();  // small_id complete
+    if (in_lds)
+      for (int e = t; e < n_small * n_small; e += blockDim.x)
+        ovs[e] = ovh[size_t(small_id[e / n_small]) * Cq + small_id[e % n_small]];
+    // four threads per group (adjacent lanes) split the candidates
+    for (int round = 0; round < kPairRounds; ++round) {
+      __syncthreads();
+      for (int i0 = 0; i0 < n_small; i0 += 256) {
+        const int i = i0 + (t >> 2), q = t & 3;
+        int best = -1, bestv = -1;
+        if (i < n_small && partner[i] < 0) {
+          const uint8_t* row = ovh + size_t(small_id[i]) * Cq;
+          // candidates j = q, q + 4, ... in batches of 8 (all loads of a batch issued first)
+          for (int j0 = q; j0 < n_small; j0 += 32) {
+            int vv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int j = j0 + 4 * u;
+              vv[u] = j >= n_small ? -1 : in_lds ? int(ovs[i * n_small + j]) : int(row[small_id[j]]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int j = j0 + 4 * u;
+              if (j < n_small && j != i && partner[j] < 0 && vv[u] > bestv) {
+                bestv = vv[u];
+                best = j;
+              }
+            }
+          }
+        }
+        // best of the four (ties to the lower rank)
+#pragma unroll
+        for (int o = 1; o < 4; o <<= 1) {
+          const int obv = __shfl_xor(bestv, o), ob = __shfl_xor(best, o);
+          if (obv > bestv || (obv == bestv && ob >= 0 && (best < 0 || ob < best))) {
+            bestv = obv;
+            best = ob;
+          }
+        }
+        if (i < n_small && q == 0) best_of[i] = best;
+      }
+      __syncthreads();
+      if (t < n_small && partner[t] < 0 && best_of[t] >= 0 && best_of[best_of[t]] == t) partner[t] = best_of[t];
+    }
   }
-  if (t == 0) ntiles[hd] = min(tmax, n_text_tiles + n_big_tiles + (n_small + 1) / 2);
+  __syncthreads();
+  // matched pairs (listed by their lower rank), then the unmatched in rank order, two per tile
+  const bool lead = t < n_small && partner[t] > t;
+  const bool loose = t < n_small && partner[t] < 0;
+  int n_pairs, n_loose;
+  const int pair_rank = block_exscan_i(lead ? 1 : 0, buf, &n_pairs);
+  const int loose_rank = block_exscan_i(loose ? 1 : 0, buf, &n_loose);
+  const int base = n_text_tiles + n_big_tiles;
+  if (lead) {
+    const int a = small_id[t], c = small_id[partner[t]];
+    put(base + pair_rank, 0, a, qo[a], qo[a + 1] - qo[a]);
+    put(base + pair_rank, 1, c, qo[c], qo[c + 1] - qo[c]);
+  }
+  if (loose) {
+    const int a = small_id[t];
+    const int tile = base + n_pairs + loose_rank / 2;
+    put(tile, loose_rank & 1, a, qo[a], qo[a + 1] - qo[a]);
+    if ((loose_rank & 1) == 0 && loose_rank == n_loose - 1) put(tile, 1, a, qo[a], 0);  // no partner
+  }
+  if (t == 0) ntiles[hd] = min(tmax, base + n_pairs + (n_loose + 1) / 2);
 }
 
 // ------------------------------------------------------------------ host drivers
@@ -898,8 +1025,21 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
   const int BH = desc.B * desc.H, Nv = desc.N - desc.n_text;
   int* tiles = ws_ptr<int>(ws, L.tiles);
   int* ntiles = ws_ptr<int>(ws, L.ntiles);
-  hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), 0, st, part.q_off, part.n_q, p.Cq, Nv, desc.n_text,
-                     L.tmax, tiles, ntiles);
+  // selection overlaps of every pair of query groups (for up to 1024 K/V groups), then the tiles
+  uint8_t* ov = nullptr;
+  if (p.Ck <= 64 * kOvWords) {
+    ov = ws_ptr<uint8_t>(ws, L.pair_ov);
+    unsigned long long* sbits = ws_ptr<unsigned long long>(ws, L.sel_bits);
+    hipLaunchKernelGGL(sel_bits_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.n_q, part.n_kv,
+                       route.sel_cnt, route.sel_kv, p.Cq, p.Ck, kv_group_size(desc), desc.n_text, sbits);
+    const dim3 og(ceil_div(p.Cq, kOvTile), ceil_div(p.Cq, kOvTile), BH);
+    hipLaunchKernelGGL(pair_overlap_kernel, og, dim3(256), 0, st, part.n_q, part.n_kv, sbits, p.Cq,
+                       kv_group_size(desc), ov);
+  }
+  allow_lds(sparse_tiles_kernel, ov ? kTilesLds : 0);
+  hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), ov ? kTilesLds : 0, st, part.q_off, part.n_q, part.n_kv,
+                     route.sel_cnt, route.sel_kv, p.Cq, p.Ck, kv_group_size(desc), Nv, desc.n_text, L.tmax, ov, tiles,
+                     ntiles);
   int* tprefix = ws_ptr<int>(ws, L.tile_prefix);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, ntiles, BH, tprefix);
   SPR_CHECK_LAUNCH();

@@ -208,6 +208,8 @@ struct Workspace {
   size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
   size_t ntiles;     // int    [BH]              tiles used per head
   size_t tile_prefix;  // int  [BH + 1]          exclusive prefix of ntiles
+  size_t pair_ov;    // uint8  [BH][Cq][Cq]     shared K/V groups of two query groups' selections
+  size_t sel_bits;   // uint64 [BH][Cq][16]     selections as bitmaps over K/V groups
   size_t total;
   int tmax;          // tile capacity per head
   int nblk;          // k-means assign blocks per head
