@@ -586,3 +586,49 @@ def test_bf16_score_bounds_small():
                 cnt = int(g["sel_cnt"][hd][a])
                 assert list(g["sel_kv"][hd][a][:cnt]) == list(sel), (hd, a)
     assert n_exact < 0.2 * n_all and n_out > 0.3 * n_all, (n_exact, n_out, n_all)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Ck", [48, 200, 640])
+def test_bf16_route_widths(Ck):
+    """The bounded bf16 routing path at other K/V group counts (one, four and sixteen entries per
+    lane of its ranking network): two heads of small end to end against the oracle."""
+    cfg = config("small").with_(H=2, Ck=Ck)
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    rows = np.unique(np.concatenate([np.arange(0, cfg.N, 7), np.arange(cfg.N - 100, cfg.N)]))
+    for h in (0, 1):
+        ref = O.sparsepr_head(q[0, h], k[0, h], v[0, h], p, head=h, rows=rows)
+        ref["lam"] = p.lam
+        if _oracle_is_tie_free(ref):
+            _compare_head(g, ref, h, cfg.Nv, cfg.N, cfg.n_text)
+        else:
+            _lockstep_head(g, q, k, v, cfg, opc, 0, h, np.random.default_rng(1))
+        nkv = int(g["n_kv"][h])
+        e = g["score_err"][h][: int(g["n_q"][h]), :nkv]
+        assert np.all(np.isfinite(e)) and (e < 0).any()
+    assert np.all(g["head_status"] & 1 == 0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("grid,Ck,Cq,M,rho", [
+    ((2, 8, 8), 96, 8, 8, 0.6),      # mostly one-key groups (exact zero scores in the bf16 path)
+    ((1, 5, 29), 40, 9, 8, 0.3),     # 145 rows, ragged against every tile
+])
+def test_bf16_degenerate_groups(grid, Ck, Cq, M, rho):
+    """Edge cases of the bounded bf16 routing on the positional workload (bf16, d = 128)."""
+    cfg = config("small").with_(grid=grid, H=1, Ck=Ck, Cq=Cq, M=M, rho=rho, Ms=64)
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    ref = O.sparsepr_head(q[0, 0], k[0, 0], v[0, 0], p, head=0)
+    ref["lam"] = p.lam
+    if _oracle_is_tie_free(ref):
+        _compare_head(g, ref, 0, cfg.Nv, cfg.N, cfg.n_text)
+    else:
+        _lockstep_head(g, q, k, v, cfg, opc, 0, 0, np.random.default_rng(1), nrows=64, ngroups=min(6, Cq))
