@@ -40,6 +40,8 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.scores = take(BH * p.Cq * p.Ck * 8);
   const size_t nsc = desc.dtype == SPR_BF16 ? BH * p.Cq * p.Ck : 0;
   L.serr = take(nsc * 8);
+  L.qsplit = take(desc.dtype == SPR_BF16 ? BH * p.Cq * 3 * d * 2 : 0);
+  L.qnorm = take(BH * p.Cq * 8);
   L.vh = take(desc.dtype == SPR_BF16 ? BH * size_t(desc.N) * d * 2 : 0);
   const size_t Mm = M > 0 ? size_t(M) : 1;
   L.pr_part = take(BH * Mm * L.splits * (d + 2) * 4);

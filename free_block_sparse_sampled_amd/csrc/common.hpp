@@ -194,6 +194,8 @@ struct Workspace {
   size_t lbar;       // double [BH][Cq][Ck]      centroid logits qbar_a . kbar_b / sqrt d
   size_t scores;     // double [BH][Cq][Ck]      (unless the caller keeps them)
   size_t serr;       // double [BH][Cq][Ck]      bounds of the bf16 scores (unless the caller keeps them)
+  size_t qsplit;     // bf16   [BH][Cq][3][d]    qbar as hi, mid, lo bf16 slices (bf16 inputs)
+  size_t qnorm;      // double [BH][Cq]          |qbar_a|
   size_t vh;         // fp16   [BH][N][d]        group-major values converted to fp16 (bf16 inputs)
   size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows
   size_t fitX;       // double [BH][M][d]        standardised probe features

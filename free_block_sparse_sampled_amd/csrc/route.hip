@@ -366,9 +366,34 @@ inline int64_t route_fast_blocks(int Cq, int Ck, int BH) {
   const int64_t TX = (Cq + 16 * kFastWaves - 1) / (16 * kFastWaves), TY = (Ck + 15) / 16;
   return 8 * TX * ((int64_t(BH) * TY + 7) / 8);
 }
+// qbar_a as three bf16 slices (hi, then mid = the rounding of what hi leaves, then lo) and its
+// norm, one wave per query group.
+template <int D>
+__global__ __launch_bounds__(256) void qbar_split_kernel(const double* __restrict__ qbar, const int* __restrict__ n_q,
+                                                         int Cq, __bf16* __restrict__ qsplit,
+                                                         double* __restrict__ qnorm) {
+  const int hd = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= n_q[hd]) return;
+  double n2 = 0.0;
+  __bf16* o = qsplit + (size_t(hd) * Cq + a) * 3 * D;
+  for (int c = lane; c < D; c += 64) {
+    const double x = qbar[(size_t(hd) * Cq + a) * D + c];
+    const __bf16 h = __bf16(float(x));
+    const double r1 = x - double(float(h));
+    const __bf16 m = __bf16(float(r1));
+    const double r2 = r1 - double(float(m));
+    o[c] = h;
+    o[D + c] = m;
+    o[2 * D + c] = __bf16(float(r2));
+    n2 = fma(x, x, n2);
+  }
+  n2 = wave_allsum_d(n2);
+  if (lane == 0) qnorm[size_t(hd) * Cq + a] = sqrt(n2);
+}
 template <int D>
 __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const uint16_t* __restrict__ Kp, int N, int Nv,
-                                                               const double* __restrict__ qbar,
+                                                               const __bf16* __restrict__ qsplit,
+                                                               const double* __restrict__ qnorm,
                                                                const double* __restrict__ lbar,
                                                                const double* __restrict__ vbar,
                                                                const int* __restrict__ kv_off,
@@ -399,35 +424,27 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, r16 = lane & 15;
   const uint16_t* Kh = Kp + size_t(hk) * N * D;
 
-  // A fragments: lane l holds query group a0 + 16 w + l % 16, columns 32 ks + 8 (l / 16) .. + 7
+  // A fragments (from qsplit): lane l holds query group a0 + 16 w + l % 16, columns
+  // 32 ks + 8 (l / 16) .. + 7 of the three slices (zero past the last group)
   rbf16x8_t qh[KS], qm[KS], ql[KS];
-  double qn2 = 0.0;
   {
-    const int a = min(a0 + w * 16 + r16, nq - 1);
-    const bool ok = a0 + w * 16 + r16 < nq;
+    const int a = a0 + w * 16 + r16;
+    const uint4* qs4 = reinterpret_cast<const uint4*>(qsplit + (size_t(hd) * Cq + min(a, nq - 1)) * 3 * D);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        double x = qbar[(size_t(hd) * Cq + a) * D + ks * 32 + gq * 8 + e];
-        x = ok ? x : 0.0;
-        const __bf16 h = __bf16(float(x));
-        const double r1 = x - double(float(h));
-        const __bf16 m = __bf16(float(r1));
-        const double r2 = r1 - double(float(m));
-        qh[ks][e] = h;
-        qm[ks][e] = m;
-        ql[ks][e] = __bf16(float(r2));
-        qn2 = fma(x, x, qn2);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 h = qs4[(0 * D + ks * 32 + gq * 8) / 8], m = qs4[(1 * D + ks * 32 + gq * 8) / 8],
+            l = qs4[(2 * D + ks * 32 + gq * 8) / 8];
+      if (a >= nq) h = m = l = make_uint4(0, 0, 0, 0);
+      qh[ks] = __builtin_bit_cast(rbf16x8_t, h);
+      qm[ks] = __builtin_bit_cast(rbf16x8_t, m);
+      ql[ks] = __builtin_bit_cast(rbf16x8_t, l);
+    }
   }
-  qn2 += __shfl_xor(qn2, 16);
-  qn2 += __shfl_xor(qn2, 32);
   // output slot v of lane l: query group a0 + 16 w + 4 (l / 16) + v, key l % 16 of the tile;
   // in the epilogue lane l forms the pair (query group slot v = l % 4, K/V group slot l % 16 / 4)
   const int my_v = r16 & 3, my_slot = r16 >> 2, my_a = a0 + w * 16 + gq * 4 + my_v;
   const double my_m = my_a < nq ? shift[size_t(hd) * Cq + my_a] : 0.0;
-  const double my_qn = sqrt(__shfl(qn2, gq * 4 + my_v));
+  const double my_qn = my_a < nq ? qnorm[size_t(hd) * Cq + my_a] : 0.0;
   // the block's centroid logits lbar_ab in LDS; the pair shifts (times log2 e, fp32) of the
   // lane's four query groups and group b
   for (int e = tid; e < 16 * QT; e += NTH) {
@@ -1325,10 +1342,18 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
     // bf16 keys: scores on the bf16 matrix cores with bounds, fp64 where the selection needs it
     double* serr = out.score_err ? out.score_err : ws_ptr<double>(ws, L.serr);
     const unsigned nblk = unsigned(route_fast_blocks(p.Cq, p.Ck, BH));
+    __bf16* qsplit = ws_ptr<__bf16>(ws, L.qsplit);
+    double* qnorm = ws_ptr<double>(ws, L.qnorm);
+    if (d == 128)
+      hipLaunchKernelGGL(qbar_split_kernel<128>, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.qbar, part.n_q,
+                         p.Cq, qsplit, qnorm);
+    else
+      hipLaunchKernelGGL(qbar_split_kernel<64>, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.qbar, part.n_q,
+                         p.Cq, qsplit, qnorm);
     auto fast = [&](auto kern, size_t smem) {
       allow_lds(kern, smem);
       hipLaunchKernelGGL(kern, dim3(nblk), dim3(kFastWaves * 64), smem, st, static_cast<const uint16_t*>(part.Kp), N, Nv,
-                         part.qbar, lbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, BH, shift,
+                         qsplit, qnorm, lbar, part.vbar, part.kv_off, part.n_q, part.n_kv, p.Cq, p.Ck, G, BH, shift,
                          vstat, scores, serr);
     };
     if (d == 128) fast(route_score_fast_kernel<128>, route_fast_smem<128>());
