@@ -853,16 +853,13 @@ __global__ __launch_bounds__(256) void pair_overlap_kernel(const int* __restrict
   }
 }
 __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restrict__ q_off, const int* __restrict__ n_q,
-                                                            const int* __restrict__ n_kv,
-                                                            const int* __restrict__ sel_cnt,
-                                                            const int* __restrict__ sel_kv, int Cq, int Ck, int G,
-                                                            int Nv, int n_text, int tmax,
+                                                            int Cq, int Nv, int n_text, int tmax,
                                                             const uint8_t* __restrict__ ov,
                                                             int* __restrict__ tiles, int* __restrict__ ntiles) {
   __shared__ int buf[1024], small_id[1024], partner[1024], best_of[1024];
   extern __shared__ uint8_t ovs[];  // [n_small][n_small] overlaps of the small groups, when they fit
   const int hd = blockIdx.x, t = threadIdx.x;
-  const int nq = n_q[hd], nkv = n_kv[hd / G];
+  const int nq = n_q[hd];
   const int* qo = q_off + size_t(hd) * (Cq + 1);
   int* out = tiles + size_t(hd) * tmax * 8;
   constexpr int H2 = 2 * kHalfRows;
@@ -1037,9 +1034,8 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
                        kv_group_size(desc), ov);
   }
   allow_lds(sparse_tiles_kernel, ov ? kTilesLds : 0);
-  hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), ov ? kTilesLds : 0, st, part.q_off, part.n_q, part.n_kv,
-                     route.sel_cnt, route.sel_kv, p.Cq, p.Ck, kv_group_size(desc), Nv, desc.n_text, L.tmax, ov, tiles,
-                     ntiles);
+  hipLaunchKernelGGL(sparse_tiles_kernel, dim3(BH), dim3(1024), ov ? kTilesLds : 0, st, part.q_off, part.n_q, p.Cq,
+                     Nv, desc.n_text, L.tmax, ov, tiles, ntiles);
   int* tprefix = ws_ptr<int>(ws, L.tile_prefix);
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, st, ntiles, BH, tprefix);
   SPR_CHECK_LAUNCH();

@@ -4,9 +4,14 @@
 // The value-error score of App. B.3 expands, per (query group a, K/V group b), to
 //   |G_b| s_ab = A^2 |G_b| |vbar_b|^2 - 2 A sum_j E_j (v_j . vbar_b) + sum_j E_j^2 |v_j|^2
 // with A = e^{qbar_a kbar_b / sqrt d - m_a} and E_j = e^{qbar_a k_j / sqrt d - m_a}, so one
-// fp64 pass over all (a, key) logits with two segmented sums per (a, b) gives every score.
-// The shift m_a (the largest centroid logit of row a) multiplies a whole row by one positive
-// factor and leaves the ranking unchanged.
+// pass over all (a, key) logits with segmented sums per (a, b) gives every score.  The shift m_a
+// (the largest centroid logit of row a) multiplies a whole row by one positive factor and leaves
+// the ranking unchanged.
+//
+// fp32 keys: that pass in fp64 (route_score_kernel), then the ranked prefix (route_select_kernel).
+// bf16 keys: the pass on the bf16 matrix cores with a rigorous bound per score
+// (route_score_fast_kernel), then route_resolve_kernel, which recomputes in fp64 exactly the
+// scores the prefix and its order depend on; the outcome is that of the fp64 scores.
 #include "common.hpp"
 #include "stages.hpp"
 
