@@ -900,7 +900,8 @@ __global__ __launch_bounds__(1024) void km_compact_kernel(const int* __restrict_
 // positions and dst[hd][pos] = src[hd][pos] for the trailing text rows.  16-byte pieces.
 template <int DT>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict__ src, HeadGeom g,
-                                                          const int* __restrict__ perm, void* __restrict__ dst) {
+                                                          const int* __restrict__ perm, void* __restrict__ dst,
+                                                          _Float16* __restrict__ dst16 = nullptr) {
   constexpr int ES = ElemSize<DT>::value;
   const int hd = blockIdx.y;
   const int pieces = g.d * ES / 16;
@@ -910,24 +911,19 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict
   const int row = pos < g.Nv ? perm[size_t(hd) * g.Nv + pos] : pos;
   const char* s = static_cast<const char*>(src) + (g.base(hd) + int64_t(row) * g.sn) * ES + pc * 16;
   char* dd = static_cast<char*>(dst) + ((size_t(hd) * g.N + pos) * g.d) * ES + pc * 16;
-  *reinterpret_cast<uint4*>(dd) = *reinterpret_cast<const uint4*>(s);
-}
-
-// fp16 copy of the group-major bf16 values (the operand type of the P V products).
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ src, _Float16* __restrict__ dst,
-                                                          size_t n) {
-  const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * 8;
-  if (i >= n) return;
-  const uint4 u = *reinterpret_cast<const uint4*>(src + i);
-  const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  h8 o;
+  const uint4 u = *reinterpret_cast<const uint4*>(s);
+  *reinterpret_cast<uint4*>(dd) = u;
+  if (dst16) {  // bf16 rows: also the fp16 copy (the operand type of the P V products)
+    const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8 o;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    o[2 * c] = _Float16(__uint_as_float(wv[c] << 16));
-    o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+    for (int c = 0; c < 4; ++c) {
+      o[2 * c] = _Float16(__uint_as_float(wv[c] << 16));
+      o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+    }
+    *reinterpret_cast<h8*>(dst16 + (size_t(hd) * g.N + pos) * g.d + pc * 8) = o;
   }
-  *reinterpret_cast<h8*>(dst + i) = o;
 }
 
 // Means of rows [off[b], off[b+1]) of a group-major [BH][N][d] tensor, one wave per group: d / 8
@@ -1203,14 +1199,9 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   const dim3 ggrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BH);
   const dim3 kgrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BHkv);
   hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, k, gk, out.kv_perm, out.Kp);
-  hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp);
+  hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp,
+                     DT == SPR_BF16 ? wsp<_Float16>(ws, L.vh) : nullptr);
   SPR_CHECK_LAUNCH();
-  if constexpr (DT == SPR_BF16) {
-    const size_t nel = size_t(BHkv) * desc.N * d;
-    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(unsigned(ceil_div64(int64_t(nel / 8), 256))), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(out.Vp), wsp<_Float16>(ws, L.vh), nel);
-    SPR_CHECK_LAUNCH();
-  }
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Kp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.kbar);
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Vp, desc.N, d,
