@@ -106,10 +106,20 @@ __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __rest
   double nrm = 0.0;
   if (valid) {
     _Float16 hv[8], lv[8];
+    // r is a multiple of 8: a lane's eight coordinates are four aligned 16-byte loads
+    double xr[8];
+    const bool live = cb * 8 < r;
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const double2 t2 = live ? *reinterpret_cast<const double2*>(feat + (size_t(hd) * n + j) * r + cb * 8 + u)
+                              : make_double2(0.0, 0.0);
+      xr[u] = t2.x;
+      xr[u + 1] = t2.y;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int e = cb * 8 + u;
-      const double x = e < r ? (feat[(size_t(hd) * n + j) * r + e] - mu[size_t(hd) * RPMAX + e]) * sc : 0.0;
+      const double x = live ? (xr[u] - mu[size_t(hd) * RPMAX + e]) * sc : 0.0;
       const _Float16 h = _Float16(float(x));
       hv[u] = h;
       lv[u] = _Float16(float(x - double(h)));
