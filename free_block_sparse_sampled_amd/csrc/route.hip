@@ -326,14 +326,24 @@ __device__ __forceinline__ float lanes_sum16(float x) {
   x = lanes_sum8(x);
   return x + dppf<0x140>(x);
 }
+// Sum over the 16 lanes of a row of x[my_v], my_v = (lane % 16) % 4, delivered to the lanes with
+// that my_v: halves exchanged across lane bit 0 (quad_perm [1,0,3,2]) and bit 1 ([2,3,0,1]), then
+// the four lanes of equal my_v summed by rotating the row by 4 and 8.
+__device__ __forceinline__ float lanes_scatter_sum4(const float (&x)[4], int r16) {
+  const bool b0 = r16 & 1, b1 = (r16 >> 1) & 1;
+  float k0 = b0 ? x[1] : x[0], k1 = b0 ? x[3] : x[2];  // keep v = b0 and v = b0 + 2
+  k0 += dppf<0xB1>(b0 ? x[0] : x[1]);
+  k1 += dppf<0xB1>(b0 ? x[2] : x[3]);
+  float z = b1 ? k1 : k0;  // keep v = b0 + 2 b1
+  z += dppf<0x4E>(b1 ? k0 : k1);
+  z += dppf<0x124>(z);  // row_ror:4
+  return z + dppf<0x128>(z);  // row_ror:8
+}
 __device__ __forceinline__ float lanes_max16(float x) {
   x = fmaxf(x, dppf<0xB1>(x));
   x = fmaxf(x, dppf<0x4E>(x));
   x = fmaxf(x, dppf<0x141>(x));
   return fmaxf(x, dppf<0x140>(x));
-}
-__device__ __forceinline__ float sel4f(const float (&x)[4], int v) {
-  return v == 0 ? x[0] : v == 1 ? x[1] : v == 2 ? x[2] : x[3];
 }
 template <int CTRL>
 __device__ __forceinline__ double dppd(double x) {
@@ -594,21 +604,16 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
       }
     }
     if (p0 + PIECE >= off[b + 1]) {  // group b complete
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        P1[v] = lanes_sum16(P1[v]);
-        P2[v] = lanes_sum16(P2[v]);
-        B1[v] = lanes_sum16(B1[v]);
-        B2[v] = lanes_sum16(B2[v]);
-        B3[v] = lanes_sum16(B3[v]);
-      }
+      const float s1 = lanes_scatter_sum4(P1, r16), s2 = lanes_scatter_sum4(P2, r16),
+                  s3 = lanes_scatter_sum4(B1, r16), s4 = lanes_scatter_sum4(B2, r16),
+                  s5 = lanes_scatter_sum4(B3, r16);
       kmax = lanes_max16(kmax);
       if (my_slot == slot) {
-        kP1 = sel4f(P1, my_v);
-        kP2 = sel4f(P2, my_v);
-        kB1 = sel4f(B1, my_v);
-        kB2 = sel4f(B2, my_v);
-        kB3 = sel4f(B3, my_v);
+        kP1 = s1;
+        kP2 = s2;
+        kB1 = s3;
+        kB2 = s4;
+        kB3 = s5;
         kK = kmax;
       }
 #pragma unroll
