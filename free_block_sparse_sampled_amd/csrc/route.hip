@@ -290,10 +290,11 @@ __global__ __launch_bounds__(256) void route_score_kernel(const void* __restrict
 // the first sum fp64, the others fp32.  Nothing cancels.  A group of one key scores exactly 0
 // (its centroid is its key) and is written so with a zero bound.  Each score comes with a bound on its
 // distance to the exact score (same row factor), from:
-//   - the logit: the hi slice takes one product per 32 columns, each from zero, so at most
-//     2 (32 + 8) 2^-24 |qbar_a| max_j |k_j| for its products and the fp32 sums that join them
-//     (every fp32 operation rounded, with a factor 2 for any rounding mode of the matrix
-//     cores), 2 d 2^-32 of the same for the mid and lo chains, plus 2^-22 for the slices;
+//   - the logit: the hi slice takes one product per 32 columns (the first one seeded with the
+//     mid and lo chain), so at most 2 (32 + 8) 2^-24 |qbar_a| max_j |k_j| for its products and
+//     the fp32 sums that join them (every fp32 operation rounded, with a factor 2 for any
+//     rounding mode of the matrix cores), 2 (2 d + 8) 2^-32 of the same for the mid and lo
+//     chain, plus 2^-22 for the slices;
 //   - the exponent argument: the fp32 scale (three roundings), the pair's shift and the fma;
 //   - v_exp_f32 within 2^-21 relative;
 //   - delta_j: within (relE + 2^-24)(E'_j + |delta_j|) of 1 - e^{x_j}, relE the relative error
@@ -576,17 +577,21 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
         for (int ks = 0; ks < KS; ++ks)
           kb[ks] = __builtin_bit_cast(rbf16x8_t,
                                       *reinterpret_cast<const uint4*>(K + jl * D + (((ks * 4 + gq) ^ (jl % KPR)) * 8)));
+        // mid and lo slices in one chain, which then seeds the first hi product; the other hi
+        // products start from zero
         const rf32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-        rf32x4_t ch[KS], cm = zero, cl = zero;
+        rf32x4_t cml = zero, ch[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          ch[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kb[ks], zero, 0, 0, 0);
-          cm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm[ks], kb[ks], cm, 0, 0, 0);
-          cl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb[ks], cl, 0, 0, 0);
+          cml = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm[ks], kb[ks], cml, 0, 0, 0);
+          cml = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kb[ks], cml, 0, 0, 0);
         }
-        rf32x4_t lg = cm + cl;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) lg += ch[ks];
+        for (int ks = 1; ks < KS; ++ks) ch[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kb[ks], zero, 0, 0, 0);
+        ch[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[0], kb[0], cml, 0, 0, 0);
+        rf32x4_t lg = ch[0];
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) lg += ch[ks];
         const bool live = jl < n;
         const float cc = F[jl], ww = F[PIECE + jl], ac = fabsf(cc);
         if (live) kmax = fmaxf(kmax, F[2 * PIECE + jl]);
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
           double score = A2 * ((R0 + 2.0 * Q1 + Q2) * ig);
           // |qbar_a| |k_j| bounds |l_j| and the sum of the product magnitudes (norms from fp32 sums)
           const double C = my_qn * double(kK) * (1.0 + 1e-5);
-          const double eps_l = 2.0 * (32 + 8) * u * C + 2.0 * D * 0x1p-32 * C + 0x1p-22 * C +
+          const double eps_l = 2.0 * (32 + 8) * u * C + 2.0 * (2 * D + 8) * 0x1p-32 * C + 0x1p-22 * C +
                                D * 0x1p-100 * double(kK);
           const double c2d = 1.4426950408889634 / sqrt(double(D)), m2d = fabs(lb * 1.4426950408889634);
           const double dx = eps_l * c2d * 1.001 + 6.0 * u * (C * c2d + m2d) * 1.001;
