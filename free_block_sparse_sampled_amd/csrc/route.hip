@@ -956,10 +956,24 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
   // 2. rank by score; lambda' = the smallest lower end among the shortest ranked prefix holding
   //    Tk keys.  Those groups hold at least Tk keys with lower ends >= lambda', so a group whose
   //    upper end is below lambda' is outside the prefix (-inf when Tk is out of reach)
+  // the bounds wait in LDS by group (the ranking network carries only scores and groups)
 #pragma unroll
-  for (int t = 0; t < E; ++t)
+  for (int t = 0; t < E; ++t) {
+    part_val[w][lane * E + t] = pl[0][t];
     if (id[t] >= nkv) sc[t] = -1.0e308;
-  wave_sort_desc<E, 1>(sc, id, pl, lane);
+  }
+  {
+    double none[1][E];
+    wave_sort_desc<E, 0>(sc, id, none, lane);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int t = 0; t < E; ++t) pl[0][t] = id[t] < nkv ? part_val[w][id[t]] : 0.0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int sz[E], s_loc = 0;
 #pragma unroll
   for (int t = 0; t < E; ++t) {
