@@ -898,9 +898,11 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
     // the small groups' overlaps gathered into LDS when they fit
     const bool in_lds = size_t(n_small) * n_small <= kTilesLds;
     __syncthreads();  // small_id complete
-    if (in_lds)
-      for (int e = t; e < n_small * n_small; e += blockDim.x)
-        ovs[e] = ovh[size_t(small_id[e / n_small]) * Cq + small_id[e % n_small]];
+    if (in_lds)  // row i by wave, columns by lane
+      for (int i = t >> 6; i < n_small; i += blockDim.x >> 6) {
+        const uint8_t* src = ovh + size_t(small_id[i]) * Cq;
+        for (int j = t & 63; j < n_small; j += 64) ovs[i * n_small + j] = src[small_id[j]];
+      }
     // four threads per group (adjacent lanes) split the candidates
     for (int round = 0; round < kPairRounds; ++round) {
       __syncthreads();
