@@ -1070,16 +1070,16 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
   double run_lo = __shfl_up(pmin, 1), run_hi = __shfl_down(smax, 1);
   if (lane == 0) run_lo = INFINITY;
   if (lane == 63) run_hi = -INFINITY;
-  double before_lo[E];
+  // earlier intervals forward, later ones backward (flags only, no per-entry minima kept)
 #pragma unroll
   for (int t = 0; t < E; ++t) {
-    before_lo[t] = run_lo;
+    flag[t] = in[t] && pl[0][t] > 0.0 && run_lo <= sc[t] + pl[0][t];
     if (in[t]) run_lo = fmin(run_lo, sc[t] - pl[0][t]);
   }
 #pragma unroll
   for (int t = E - 1; t >= 0; --t) {
     const double lo = sc[t] - pl[0][t], hi = sc[t] + pl[0][t];
-    flag[t] = in[t] && pl[0][t] > 0.0 && (before_lo[t] <= hi || run_hi >= lo);
+    flag[t] = flag[t] || (in[t] && pl[0][t] > 0.0 && run_hi >= lo);
     if (in[t]) run_hi = fmax(run_hi, hi);
   }
   // the four query groups of the block share their fp64 scores: each publishes its list in LDS,
