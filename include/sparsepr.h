@@ -243,6 +243,9 @@ spr_status sparsepr_partition(const spr_desc* desc, const void* q, const void* k
    ceil((rho*N^2 - n_text*N - M*N - Nv*n_text) / Nv); M probe rows stratified by query
    group (or the choice in `probes`, host, nullable: NULL is SPR_PROBES_STRATIFIED).
    `rho_exec_target` is the total executed-pair target including probes.
+   The prefixes and their order are those of the fp64 scores: for bf16 keys the scores run on
+   the bf16 matrix cores with a rigorous bound each, and the scores the prefix depends on are
+   recomputed in fp64 (ties of exactly equal scores go to the lower group).
    EINVAL: 1 <= M < Nv violated, the budget is below one key, an unknown probe mode. */
 spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
                           double rho_exec_target, int32_t M, const spr_probe_options* probes, spr_route* out,
