@@ -17,6 +17,28 @@
 
 namespace spr {
 
+// DPP lane moves and sums of doubles (all lanes of the rows involved active)
+template <int CTRL>
+__device__ __forceinline__ double dppd(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_update_dpp(0, unsigned(u), CTRL, 0xF, 0xF, false);
+  const unsigned hi = __builtin_amdgcn_update_dpp(0, unsigned(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+__device__ __forceinline__ double readlane_dbl(double x, int l) {
+  const unsigned long long u = __double_as_longlong(x);
+  const unsigned lo = __builtin_amdgcn_readlane(unsigned(u), l), hi = __builtin_amdgcn_readlane(unsigned(u >> 32), l);
+  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+// sum over the 64 lanes (all active): DPP sums over each 16-lane row, then the four rows
+__device__ __forceinline__ double wave_allsum_d(double x) {
+  x += dppd<0xB1>(x);
+  x += dppd<0x4E>(x);
+  x += dppd<0x141>(x);
+  x += dppd<0x140>(x);
+  return (readlane_dbl(x, 0) + readlane_dbl(x, 16)) + (readlane_dbl(x, 32) + readlane_dbl(x, 48));
+}
+
 // Per key (group-major order), fp64: u_j = v_j . vbar_b(j), w_j = |v_j|^2, c_j = (vbar_b - v_j) . v_j
 // and r_j = |vbar_b - v_j|^2.  d / 8 lanes per key, eight consecutive elements each (one 16-byte
 // load for bf16), reduced across those lanes.
@@ -44,12 +66,19 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
       r = fma(dv, dv, r);
     }
   }
-  for (int o = L >> 1; o > 0; o >>= 1) {
-    u += __shfl_xor(u, o);
-    w += __shfl_xor(w, o);
-    cr += __shfl_xor(cr, o);
-    r += __shfl_xor(r, o);
-  }
+  // sums over the L = d / 8 lanes of a key (8 or 16 adjacent lanes: quad_perm [1,0,3,2],
+  // [2,3,0,1], row_half_mirror, and row_mirror for 16)
+  auto lsum = [L](double x) {
+    x += dppd<0xB1>(x);
+    x += dppd<0x4E>(x);
+    x += dppd<0x141>(x);
+    if (L == 16) x += dppd<0x140>(x);
+    return x;
+  };
+  u = lsum(u);
+  w = lsum(w);
+  cr = lsum(cr);
+  r = lsum(r);
   if (pos < Nv && sub == 0) {
     double* o = vstat + (size_t(hd) * Nv + pos) * 4;
     *reinterpret_cast<double2*>(o) = make_double2(u, w);
@@ -345,26 +374,6 @@ __device__ __forceinline__ float lanes_max16(float x) {
   x = fmaxf(x, dppf<0x4E>(x));
   x = fmaxf(x, dppf<0x141>(x));
   return fmaxf(x, dppf<0x140>(x));
-}
-template <int CTRL>
-__device__ __forceinline__ double dppd(double x) {
-  const unsigned long long u = __double_as_longlong(x);
-  const unsigned lo = __builtin_amdgcn_update_dpp(0, unsigned(u), CTRL, 0xF, 0xF, false);
-  const unsigned hi = __builtin_amdgcn_update_dpp(0, unsigned(u >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
-}
-__device__ __forceinline__ double readlane_dbl(double x, int l) {
-  const unsigned long long u = __double_as_longlong(x);
-  const unsigned lo = __builtin_amdgcn_readlane(unsigned(u), l), hi = __builtin_amdgcn_readlane(unsigned(u >> 32), l);
-  return __longlong_as_double((unsigned long long)lo | ((unsigned long long)hi << 32));
-}
-// sum over the 64 lanes (all active): DPP sums over each 16-lane row, then the four rows
-__device__ __forceinline__ double wave_allsum_d(double x) {
-  x += dppd<0xB1>(x);
-  x += dppd<0x4E>(x);
-  x += dppd<0x141>(x);
-  x += dppd<0x140>(x);
-  return (readlane_dbl(x, 0) + readlane_dbl(x, 16)) + (readlane_dbl(x, 32) + readlane_dbl(x, 48));
 }
 constexpr int kFastPiece = 64;
 constexpr int kFastWaves = 8;
