@@ -144,22 +144,27 @@ __device__ inline int64_t block_sum_i64(int64_t x, int64_t* red /* [32] */) {
 }
 
 // Exclusive scan of one int per thread over the block (blockDim.x <= 1024); returns the
-// exclusive prefix and writes the total to *total.
-__device__ inline int block_exscan_i(int x, int* buf /* [1024] */, int* total) {
-  const int t = threadIdx.x;
-  buf[t] = x;
-  __syncthreads();
-  for (int o = 1; o < (int)blockDim.x; o <<= 1) {
-    int y = (t >= o) ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += y;
-    __syncthreads();
+// exclusive prefix and writes the total to *total.  A scan inside each wave (lane shuffles),
+// then the wave totals through buf (at least 16 entries): three barriers.
+__device__ inline int block_exscan_i(int x, int* buf /* [>= 16] */, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (int(blockDim.x) + 63) >> 6;
+  int incl = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  int incl = buf[t];
-  int tot = buf[blockDim.x - 1];
+  __syncthreads();  // buf may still be read by a previous call
+  if (lane == min(63, int(blockDim.x) - 1 - w * 64)) buf[w] = incl;
   __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int v = buf[i];
+    before += i < w ? v : 0;
+    tot += v;
+  }
+  __syncthreads();  // buf is free again
   *total = tot;
-  return incl - x;
+  return before + incl - x;
 }
 
 // ----------------------------------------------------------------- SplitMix64
