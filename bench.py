@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--max-iters", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--no-other", action="store_true", help="skip the measurement of the other regime")
     ap.add_argument("--regime", choices=["warm", "cold"], default="warm",
                     help="headline regime: later calls (App. C.1 warm start) or cold calls")
     ap.add_argument("--probe-mode", choices=["stratified", "random", "uniform"], default="stratified",
@@ -198,11 +199,13 @@ def main():
     names = ["partition", "route", "attn_sparse", "probe_exact", "fit_correct"]
     warm_regime = args.regime == "warm"
     # the other regime first (a short measurement reported beside the headline one)
-    per_o, total_o, _ = timed(not warm_regime, max(2, args.steps // 3), 1)
+    other = None
+    if not args.no_other:
+        per_o, total_o, _ = timed(not warm_regime, max(2, args.steps // 3), 1)
+        other = {"ms_per_call": round(float(np.median(total_o)), 4),
+                 "stages_ms": {n: round(float(np.median(per_o[:, i])), 4) for i, n in enumerate(names)}}
     per, total, wall = timed(warm_regime, args.steps, max(args.warmup, 1))
     ms_call = float(np.median(total))
-    other = {"ms_per_call": round(float(np.median(total_o)), 4),
-             "stages_ms": {n: round(float(np.median(per_o[:, i])), 4) for i, n in enumerate(names)}}
     tq, tk, tv = inputs[(call[0] - 1) % 2]  # inputs of the last timed call (op holds its results)
 
     pairs = op.route.pairs.double().sum().item()
@@ -251,14 +254,15 @@ def main():
     if not args.no_dense:
         dense_out = torch.empty((cfg.B, cfg.H, N, d), dtype=torch.float32, device="cuda")
         desc = spr.make_desc(tq)
+        dws = spr.dense_workspace(desc, tq.device)
         for _ in range(2):
-            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out)
+            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out, dws)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = max(2, args.steps // 2)
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(reps):
-            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out)
+            spr.sparsepr_attn_dense(desc, tq, tk, tv, dense_out, dws)
         e1.record(stream)
         torch.cuda.synchronize()
         t_dense = e0.elapsed_time(e1) / reps

@@ -42,9 +42,11 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.serr = take(nsc * 8);
   L.qsplit = take(desc.dtype == SPR_BF16 ? BH * p.Cq * 3 * d * 2 : 0);
   L.qnorm = take(BH * p.Cq * 8);
-  L.vh = take(desc.dtype == SPR_BF16 ? BH * size_t(desc.N) * d * 2 : 0);
+  const size_t BHkv = size_t(desc.B) * kv_heads(desc);
+  L.vh = take(desc.dtype == SPR_BF16 ? BHkv * size_t(desc.N) * d * 2 : 0);
+  L.vamax = take(BHkv * 4);
+  L.vscale = take(2 * BHkv * 4);
   const size_t Mm = M > 0 ? size_t(M) : 1;
-  L.pr_part = take(BH * Mm * L.splits * (d + 2) * 4);
   L.fitX = take(BH * Mm * d * 8);
   L.fitR = take(BH * Mm * d * 8);
   L.fitG = take(BH * d * d * 8);
@@ -199,6 +201,16 @@ spr_status sparsepr_attn_sparse(const spr_desc* desc, const spr_part_params* par
   return run_attn_sparse(*desc, *params, *part, *route, o_sp, ws, L, static_cast<hipStream_t>(stream));
 }
 
+// Workspace of the probe call: split-K partials, then (bf16) the scaled fp16 copy of v.
+static Workspace probe_layout(const spr_desc& desc, int M) {
+  Workspace L = {};
+  L.splits = kProbeSplits;
+  L.pr_part = 0;
+  L.pr_vcopy = align_up(size_t(desc.B) * desc.H * M * kProbeSplits * (desc.d + 2) * 4);
+  L.total = L.pr_vcopy + v_copy_bytes(desc);
+  return L;
+}
+
 spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void* k, const void* v,
                                 const int32_t* probe_idx, int32_t M, float* o_probe, void* ws, size_t ws_bytes,
                                 void* stream) {
@@ -208,14 +220,15 @@ spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void*
   if (!head_fits_32bit(desc)) return SPR_EUNSUPPORTED;
   const int Nv = desc->N - desc->n_text;
   if (M < 1 || M >= Nv) return SPR_EINVAL;
-  // the probe stage only needs the split-K partial buffer, sized by (BH, M, d)
-  const size_t need = size_t(desc->B) * desc->H * M * kProbeSplits * (desc->d + 2) * 4;
+  const Workspace L = probe_layout(*desc, M);
   if (!ws || !aligned16(ws)) return SPR_EINVAL;
-  if (ws_bytes < need) return SPR_EWORKSPACE;
-  Workspace L = {};
-  L.pr_part = 0;
-  L.splits = kProbeSplits;
+  if (ws_bytes < L.total) return SPR_EWORKSPACE;
   return run_probe_exact(*desc, q, k, v, probe_idx, M, o_probe, ws, L, static_cast<hipStream_t>(stream));
+}
+
+size_t sparsepr_probe_workspace_size(const spr_desc* desc, int32_t M) {
+  if (check_desc(desc) != SPR_OK || M < 1) return 0;
+  return probe_layout(*desc, M).total;
 }
 
 spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* params, const spr_partition* part,
@@ -240,14 +253,22 @@ spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* par
                          out_dtype, fit_state, head_status, ws, L, static_cast<hipStream_t>(stream));
 }
 
+size_t sparsepr_dense_workspace_size(const spr_desc* desc) {
+  if (check_desc(desc) != SPR_OK) return 0;
+  const size_t n = v_copy_bytes(*desc);
+  return n ? n : 256;
+}
+
 spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v, void* out,
-                               int32_t out_dtype, void* stream) {
+                               int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
   spr_status s = check_desc(desc);
   if (s != SPR_OK) return s;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
   if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
   if (!head_fits_32bit(desc)) return SPR_EUNSUPPORTED;
-  return run_attn_dense(*desc, q, k, v, out, out_dtype, static_cast<hipStream_t>(stream));
+  if (!ws || !aligned16(ws)) return SPR_EINVAL;
+  if (ws_bytes < v_copy_bytes(*desc)) return SPR_EWORKSPACE;
+  return run_attn_dense(*desc, q, k, v, out, out_dtype, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C) {

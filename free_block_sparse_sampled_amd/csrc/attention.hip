@@ -5,18 +5,16 @@
 //    group with more than 64 rows fills both halves of its blocks; smaller groups are paired,
 //    and the block streams the union of the two groups' selected K/V groups (groups selected
 //    by both halves first, then those of one half only), each half skipping or masking keys it
-//    did not select.  Either way every K/V chunk staged in LDS serves up to 128 query rows,
-//    which is what bounds the kernel: with 64 rows per fetch it is limited by the traffic of
-//    re-fetching K/V, not by the MFMA pipe.
-//  - dense (Eq. (1)): the same kernel over one segment holding every key;
+//    did not select.  Either way every K/V chunk staged in LDS serves up to 128 query rows.
+//  - dense (Eq. (1)): the same kernel over one run of every key;
 //  - probe rows (Sec. 4.2): gathered query rows against a contiguous key range (split-K),
 //    partial (max, sum, unnormalised output) merged by a second kernel.
 //
-// bf16 inputs use MFMA: S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (exact products, fp32
-// sums), P rounded to fp16 and O^T += V^T P^T with v_mfma_f32_16x16x32_f16 (V staged,
-// transposed, into LDS as fp16).  Computing the transposes puts a query row's scores and its
-// output columns in the same lane, so the softmax rescaling needs no cross-lane traffic.
-// fp32 inputs use a plain VALU kernel.
+// bf16 inputs use MFMA: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (exact products, fp32
+// sums), P rounded to fp16 and O^T += V^T P^T with v_mfma_f32_32x32x16_f16 from an fp16 copy of
+// V scaled by a power of two per K/V head (the scale is undone on the output).  Computing the
+// transposes puts a query row's scores and its output columns in one lane.  fp32 inputs use a
+// plain VALU kernel.
 #include <type_traits>
 
 #include "common.hpp"
@@ -62,9 +60,22 @@ struct AttnParams {
   float* o_sp;           // SPARSE: [BH][N][d]
   void* out;             // DENSE: [BH][N][d] contiguous
   int out_dtype;
+  // bf16: power-of-two factor per K/V head that undoes the scaling of the fp16 copy of V (null: 1)
+  const float* vinv;
+  __device__ float vscale_inv(int hk) const { return vinv ? vinv[hk] : 1.f; }
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// two floats rounded to bf16 (nearest even; inf and nan pass through), packed low then high
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u) return u >> 16;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
+  return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+}
 
 // ------------------------------------------------------------------ tile geometry
 struct TileInfo {
@@ -173,7 +184,8 @@ __device__ inline int build_segments(const AttnParams& P, int hd, int a, int* se
 // Groups selected by both halves come first, then half 0 alone, then half 1 alone, each run in
 // ascending group id.  Returns the total number of keys.
 __device__ inline int build_union_segments(const AttnParams& P, const TileInfo& t, int* seg_start, int* seg_cum,
-                                           int* seg_cat, unsigned* bm /* [2][33] */, int* scan, int* nseg_out) {
+                                           uint8_t* seg_cat, unsigned* bm /* [2][33] */, int* scan,
+                                           int* nseg_out, int* n3_out, int* n1_out) {
   const int hd = t.hd, hk = hd / P.G;  // query head, its K/V head
   const int nkv = P.n_kv[hk];
   const int ng = nkv + (P.g.n_text > 0 ? 1 : 0);
@@ -205,21 +217,25 @@ __device__ inline int build_union_segments(const AttnParams& P, const TileInfo& 
     c1 += c == 1;
     c2 += c == 2;
   }
-  // three counts (each <= 1025) packed in 11-bit fields share one scan
-  int tot;
-  const int ex = block_exscan_i(c3 | (c1 << 11) | (c2 << 22), scan, &tot);
-  const int n3 = tot & 0x7ff, n1 = (tot >> 11) & 0x7ff, n2 = (tot >> 22) & 0x7ff;
-  int o3 = ex & 0x7ff, o1 = n3 + ((ex >> 11) & 0x7ff), o2 = n3 + n1 + ((ex >> 22) & 0x7ff);
+  // the counts of categories 3 and 1 (each <= 1025) share one scan in 16-bit fields, category 2
+  // takes a second scan
+  int tot, tot2;
+  const int ex = block_exscan_i(c3 | (c1 << 16), scan, &tot);
+  const int ex2 = block_exscan_i(c2, scan, &tot2);
+  const int n3 = tot & 0xffff, n1 = tot >> 16, n2 = tot2;
+  int o3 = ex & 0xffff, o1 = n3 + (ex >> 16), o2 = n3 + n1 + ex2;
   const int* off = P.kv_off + size_t(hk) * (P.Ck + 1);
   for (int b = i0; b < min(i0 + per, ng); ++b) {
     const int c = cat_of(b);
     if (c == 0) continue;
     const int pos = c == 3 ? o3++ : c == 1 ? o1++ : o2++;
     kv_group(P, off, nkv, b, seg_start + pos, seg_cum + pos);
-    seg_cat[pos] = c;
+    seg_cat[pos] = uint8_t(c);
   }
   __syncthreads();
   *nseg_out = n3 + n1 + n2;
+  *n3_out = n3;
+  *n1_out = n1;
   return prefix_lengths(seg_cum, n3 + n1 + n2, scan);
 }
 
@@ -233,124 +249,149 @@ __device__ __forceinline__ int seg_find(const int* seg_cum, int cnt, int pos) {
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-// WAVES waves of 16 query rows share each 64-key chunk staged in LDS (K as bf16 rows, V
-// transposed to fp16).  The global loads of chunk c+1 are issued into registers before the
-// MFMAs of chunk c, and the rows of chunk c+1 (with, for sparse tiles, a 64-bit mask per half
-// of the keys that half selected) are resolved meanwhile, so memory latency overlaps compute.
-// Full chunks run unmasked, empty ones are skipped.  The running maximum used for the
-// exponentials is raised lazily: O and l are rescaled only when a row's maximum grows by more
-// than 2^8, which keeps p <= 256 (exact range in fp16) and skips most rescales.
-template <int D, int MODE, int WAVES, bool VF16>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnParams P) {
-  constexpr bool SPARSE = MODE == MODE_SPARSE;
-  constexpr int NTH = WAVES * 64;
-  constexpr int HW = SPARSE ? WAVES / 2 : WAVES;  // waves per row half
-  constexpr int ROWS = WAVES * 16;
-  // LDS tiles are unpadded; 16-byte pieces are XOR-swizzled so that the fragment reads of a
-  // 16-lane group (and the staging writes) touch every bank once:
-  //   K  [key][D]:   piece p of row r at p ^ (r % (D / 8))
-  //   V^T[col][64]:  piece p of row r at p ^ ((r / 2) % 8)   (two 128-byte rows per bank line)
-  constexpr int KS = D;           // Ks row stride (bf16 elements)
-  constexpr int VS = kChunk;      // Vt row stride (fp16 elements)
-  constexpr int KPR = D / 8;      // 16-byte pieces per K row
-  constexpr int NT = D / 16;
-  constexpr int KSTEPS = D / 32;
-  constexpr int KPIECES = kChunk * (D / 8);              // 16-byte pieces of a K chunk
-  constexpr int VITEMS = (kChunk / 4) * (D / 8);         // 4 keys x 8 columns items of a V chunk
-  // threads [0, VTH) stage V (VPT items each), threads [VTH, NTH) stage K (up to KPT pieces each)
-  constexpr int VPT = (VITEMS + NTH / 2 - 1) / (NTH / 2);
-  constexpr int VTH = VITEMS / VPT;
-  constexpr int KPT = (KPIECES + (NTH - VTH) - 1) / (NTH - VTH);
-  constexpr int KTH = KPIECES / KPT;  // threads [VTH, VTH + KTH) stage K
-  constexpr int NPRE = 4 * VPT > KPT ? 4 * VPT : KPT;  // 16-byte registers per stage
-  static_assert(VTH * VPT == VITEMS && VTH % 64 == 0, "staging split (V)");
-  static_assert(KTH * KPT == KPIECES && KTH % 64 == 0 && VTH + KTH <= NTH, "staging split (K)");
-  constexpr float kRescale = 8.0f;                       // lazy rescale threshold (log2 units)
-  static_assert(!SPARSE || HW * 16 == kHalfRows, "a sparse tile half is kHalfRows rows");
-  constexpr int KBUF = kChunk * KS;  // bf16 elements of one K buffer
-  constexpr int VBUF = D * VS;       // fp16 elements of one V buffer
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem_raw);                    // [2][KBUF]
-  _Float16* Vt = reinterpret_cast<_Float16*>(smem_raw + 2 * KBUF * 2);     // [3][VBUF]
-  int* rowidx = reinterpret_cast<int*>(smem_raw + 2 * KBUF * 2 + 3 * VBUF * 2);  // [8][kChunk]
-  unsigned long long* cmask = reinterpret_cast<unsigned long long*>(rowidx + 8 * kChunk);  // [8][2]
-  int* seg_start = reinterpret_cast<int*>(cmask + 16);
-  int* seg_cum = seg_start + (SPARSE ? kSegCap : 0);
-  int* seg_cat = seg_cum + (SPARSE ? kSegCap : 0);
-  unsigned* bm = reinterpret_cast<unsigned*>(seg_cat + (SPARSE ? kSegCap : 0));
-  int* scan = reinterpret_cast<int*>(bm + (SPARSE ? 66 : 0));
+// A block holds 128 query rows in four waves of 32 rows (for sparse tiles: two halves of two
+// waves).  Every 64-key chunk is staged once in LDS for all four waves:
+//  - K rows (bf16) by direct global-to-LDS loads, rows padded to D + 8 elements so that the
+//    fragment reads of consecutive rows fall on different banks;
+//  - V rows (fp16) by direct loads into unpadded rows whose 16-byte pieces are XOR-swizzled by
+//    the row's residue mod 4; the P V operand is read with transposing LDS reads.
+// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16 (bf16, then fp16): a lane holds one
+// query row's scores and output columns, so the softmax needs one cross-lane exchange (the two
+// 32-lane halves hold the two halves of the keys) only when the running maximum is raised.
+// Each step computes the scores of chunk c+1 interleaved with the exponentials of chunk c,
+// then the P V products of chunk c, while the loads of K(c+2) and V(c+1) are in flight; one
+// barrier per step.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __fp16 h4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+#define SPR_LDS __attribute__((address_space(3)))
 
-  const TileInfo t = decode_tile<MODE, ROWS>(P);
+// 16 bytes per lane from a buffer resource straight into LDS: lane l writes lds + 16 l
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, char* lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SPR_LDS void*)lds, 16, voffset, 0, 0, 0);
+#endif
+}
+
+template <int D>
+struct Attn32Shape {
+  static constexpr int KC = 64;              // keys per chunk
+  static constexpr int PCS = D / 8;          // 16-byte pieces per row
+  static constexpr int KSTR = PCS + 1;       // K row stride in pieces (padded)
+  static constexpr int KLOADS = KC * KSTR / 64;  // wave-wide 1 KB loads per K chunk
+  static constexpr int VLOADS = KC * PCS / 64;   // per V chunk
+  static constexpr int KBUF = KC * KSTR * 16;    // bytes of one K buffer
+  static constexpr int VBUF = KC * PCS * 16;     // bytes of one V buffer
+  static constexpr int NT = D / 32;          // 32-column output tiles
+  static constexpr int KS = D / 16;          // 16-column steps of the score product
+  // XOR applied to the piece index of a V row with residue k mod 4: the four rows of one
+  // transposing read (two pieces each) land on eight distinct 16-byte bank groups, and the
+  // 32 lanes of a 32-column tile on sixteen
+  static __device__ __forceinline__ int vswz(int k) { return D == 128 ? (0xAC60 >> (4 * k)) & 15 : 2 * k; }
+};
+
+constexpr int kRing = 4;  // chunk slots of the key-bias ring and of the row ring (sparse)
+
+template <int D, int MODE>
+static constexpr size_t attn32_smem() {
+  using S = Attn32Shape<D>;
+  size_t s = 2 * size_t(S::KBUF) + 2 * size_t(S::VBUF) + kRing * 2 * 64 * sizeof(float);
+  if (MODE == MODE_SPARSE)
+    s += kRing * 64 * sizeof(int) + 2 * kSegCap * sizeof(int) + kSegCap + 66 * sizeof(unsigned) + 32 * sizeof(int);
+  return s;
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn32_kernel(AttnParams P) {
+  using S = Attn32Shape<D>;
+  constexpr bool SPARSE = MODE == MODE_SPARSE;
+  constexpr int KC = S::KC, NT = S::NT, KS = S::KS, VROW = D * 2;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  char* Kl = smem_raw;                                               // [2][KBUF]
+  char* Vl = smem_raw + 2 * S::KBUF;                                 // [2][VBUF]
+  float* kbias = reinterpret_cast<float*>(Vl + 2 * S::VBUF);         // [kRing][2][64]
+  int* rowidx = reinterpret_cast<int*>(kbias + kRing * 2 * 64);      // [kRing][64]
+  int* seg_start = rowidx + kRing * 64;                              // [kSegCap]
+  int* seg_cum = seg_start + kSegCap;                                // [kSegCap]
+  uint8_t* seg_cat = reinterpret_cast<uint8_t*>(seg_cum + kSegCap);  // [kSegCap]
+  unsigned* bm = reinterpret_cast<unsigned*>(seg_cat + kSegCap);     // [66]
+  int* scan = reinterpret_cast<int*>(bm + 66);                       // [32]
+
+  const TileInfo t = decode_tile<MODE, 128>(P);
   if (!t.valid || t.n0 <= 0) return;
   const int hd = t.hd;
-  // the wave index comes from a scalar register so that every per-wave decision is a scalar branch
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, r16 = lane & 15;
-  const int half = SPARSE ? w / HW : 0;
-  const int my_row0 = half ? t.row1 : t.row0;
-  const int my_n = half ? t.n1 : t.n0;
-  const int qslot = (w % HW) * 16 + r16;
+  const int q32 = lane & 31, kg = lane >> 5;
+  // this wave's 32 rows: sparse tiles give waves 0-1 to half 0 and waves 2-3 to half 1
+  const int half = SPARSE ? (w >> 1) : 0;
+  const int my_row0 = SPARSE ? (half ? t.row1 : t.row0) + 32 * (w & 1) : t.row0 + 32 * w;
+  const int my_n = SPARSE ? (half ? t.n1 : t.n0) - 32 * (w & 1) : t.n0 - 32 * w;
+  const bool wave_active = my_n > 0;
+  const bool qvalid = q32 < my_n;
 
-  // K and V rows of the head are read through buffer resources with 32-bit byte offsets (the
-  // host guarantees that a head's rows span less than 2 GiB)
+  // K rows through buffer resources with 32-bit byte offsets (a head's rows span < 2 GiB); V is
+  // the contiguous fp16 copy [heads][N][D]
+  const int hk = hd / P.G;
   const uint16_t* Kb;
-  const uint16_t* Vb;
-  int row_bytes;
+  int krow_bytes;
   if constexpr (SPARSE) {
-    Kb = static_cast<const uint16_t*>(P.k) + size_t(hd / P.G) * P.g.N * D;
-    Vb = static_cast<const uint16_t*>(P.v) + size_t(hd / P.G) * P.g.N * D;
-    row_bytes = D * 2;
+    Kb = static_cast<const uint16_t*>(P.k) + size_t(hk) * P.g.N * D;
+    krow_bytes = D * 2;
   } else {
-    Kb = static_cast<const uint16_t*>(P.k) + P.gk.base(hd / P.G);
-    Vb = static_cast<const uint16_t*>(P.v) + P.gk.base(hd / P.G);
-    row_bytes = int(P.gk.sn) * 2;
+    Kb = static_cast<const uint16_t*>(P.k) + P.gk.base(hk);
+    krow_bytes = int(P.gk.sn) * 2;
   }
-  const int head_bytes = (P.g.N - 1) * row_bytes + D * 2;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, head_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, head_bytes, 0x00020000);
-  int nseg = 0, total;
-  if constexpr (SPARSE) total = build_union_segments(P, t, seg_start, seg_cum, seg_cat, bm, scan, &nseg);
-  else total = t.key1 - t.key0;
-  const int nchunks = (total + kChunk - 1) / kChunk;
+  const _Float16* Vb = static_cast<const _Float16*>(P.v) + size_t(hk) * P.g.N * D;
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kb, (short)0, (P.g.N - 1) * krow_bytes + D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vb, (short)0, P.g.N * VROW, 0x00020000);
 
-  // query fragments: the lane holds row r16 of the wave's 16 rows, dims ks*32 + 8g .. +7
-  bf16x8_t qf[KSTEPS];
-  const bool qvalid = qslot < my_n;
+  // keys of the tile; a sparse tile's halves attend to keys [0, k31) (half 0: categories 3 and 1)
+  // and [0, k3) with [k31, total) (half 1: categories 3 and 2)
+  int nseg = 0, total, k3, k31;
+  if constexpr (SPARSE) {
+    int n3, n1;
+    total = build_union_segments(P, t, seg_start, seg_cum, seg_cat, bm, scan, &nseg, &n3, &n1);
+    k3 = seg_cum[n3];
+    k31 = seg_cum[n3 + n1];
+  } else {
+    total = k3 = k31 = t.key1 - t.key0;
+  }
+  const int nchunks = (total + KC - 1) / KC;
+
+  // query fragments (B operand of S^T = K Q^T): row q32, columns 16 s + 8 kg .. + 7
+  uint4 qf[KS];
   {
     const uint16_t* qrow = nullptr;
     if (qvalid) {
       if constexpr (SPARSE) {
-        qrow = static_cast<const uint16_t*>(P.q) + (size_t(hd) * P.g.N + my_row0 + qslot) * D;
+        qrow = static_cast<const uint16_t*>(P.q) + (size_t(hd) * P.g.N + my_row0 + q32) * D;
       } else if constexpr (MODE == MODE_DENSE) {
-        qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(my_row0 + qslot) * P.g.sn;
+        qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(my_row0 + q32) * P.g.sn;
       } else {
-        const int pr = P.probe_idx[size_t(hd) * P.M + my_row0 + qslot];
+        const int pr = P.probe_idx[size_t(hd) * P.M + my_row0 + q32];
         qrow = static_cast<const uint16_t*>(P.q) + P.g.base(hd) + int64_t(pr) * P.g.sn;
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qvalid) u = *reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g);
-      qf[ks] = as_bf16x8(u);
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = qvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * kg) : make_uint4(0, 0, 0, 0);
   }
-  const bool wave_active = (w % HW) * 16 < my_n;
 
-  // Wave 0: Kp rows of chunk ch and, per half, the mask of keys that half attends to (ring of 8
-  // slots).  Chunks are resolved in increasing order, so the segment holding the chunk's first
-  // key is carried over from the previous chunk and only the segment starts inside the chunk are
-  // visited.  Keys past the end get row 0 and no mask bit.
+  // Wave 0 prepares each chunk two steps ahead (ring of kRing slots): per half, the bias of every
+  // key (0 when the half attends to it, -inf otherwise, which also masks the keys past the end),
+  // and for sparse tiles the Kp row of every key.  A sparse chunk's segments are found from the
+  // segment holding its first key, carried over from the previous chunk.
   int seg_cursor = 0;
-  auto resolve = [&](int ch) __attribute__((always_inline)) {
-    const int stage = ch & 7;
-    const int p0 = ch * kChunk, pos = p0 + lane;
-    int row = 0, cat = 0;
+  auto prepare = [&](int ch) __attribute__((always_inline)) {
+    const int slot = ch & (kRing - 1);
+    const int pos = ch * KC + lane;
+    int cat = pos < total ? 3 : 0;
     if constexpr (SPARSE) {
-      int sg = seg_cursor;
+      int sg = seg_cursor, row = 0;
       for (int k = seg_cursor + 1; k < nseg; ++k) {
         const int start = __builtin_amdgcn_readfirstlane(seg_cum[k]);
-        if (start > p0 + kChunk) break;
+        if (start > ch * KC + KC) break;
         if (pos >= start) sg = k;
         seg_cursor = k;
       }
@@ -358,313 +399,272 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         row = seg_start[sg] + (pos - seg_cum[sg]);
         cat = seg_cat[sg];
       }
-    } else {
-      if (pos < total) {
-        row = t.key0 + pos;
-        cat = 3;
-      }
+      rowidx[slot * 64 + lane] = row;
     }
-    rowidx[stage * kChunk + lane] = row;
-    const unsigned long long m0 = __ballot(cat & 1), m1 = __ballot(cat & 2);
-    if (lane == 0) {
-      cmask[stage * 2] = m0;
-      cmask[stage * 2 + 1] = m1;
-    }
-  };
-  // Staging of one chunk in registers: threads [0, VTH) hold VPT V items (4 keys x 8 columns
-  // each), threads [VTH, VTH + KTH) hold KPT 16-byte pieces of K.  Two register sets and two LDS buffers
-  // pipeline the chunks: while chunk c is computed, chunk c+1 sits in LDS and chunks c+2, c+3
-  // are in flight.
-  const bool stages_v = w * 64 < VTH;
-  const int sidx = stages_v ? threadIdx.x : threadIdx.x - VTH;
-  const bool stages_k = !stages_v && w * 64 - VTH < KTH;
-  uint4 pre0[NPRE], pre1[NPRE];
-  // Every thread issues exactly NPRE loads per chunk from straight-line code (no branch between
-  // the loads of the two roles, which would make the loads of a set wait for each other): load
-  // i reads row slot lslot[i] of the chunk at byte column lcol[i] through the wave's descriptor.
-  // Roles with fewer pieces, and idle threads, load row slot 0 again.
-  int lslot[NPRE], lcol[NPRE];
-#pragma unroll
-  for (int i = 0; i < NPRE; ++i) {
-    if (stages_v) {
-      const int e = sidx + (i / 4 < VPT ? i / 4 : 0) * VTH;
-      lslot[i] = (e % (kChunk / 4)) * 4 + (i & 3);
-      lcol[i] = (e / (kChunk / 4)) * 16;
-    } else {
-      const int e = stages_k ? sidx + (i < KPT ? i : 0) * KTH : 0;
-      lslot[i] = e / KPR;
-      lcol[i] = (e % KPR) * 16;
-    }
-  }
-  const __amdgpu_buffer_rsrc_t lrsrc = stages_v ? vrsrc : krsrc;
-  auto load_into = [&](uint4 (&pre)[NPRE], int ch) __attribute__((always_inline)) {
-    const int* ridx = rowidx + (ch & 7) * kChunk;
-#pragma unroll
-    for (int i = 0; i < NPRE; ++i)
-      pre[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(lrsrc, ridx[lslot[i]] * row_bytes + lcol[i], 0, 0));
-  };
-  // V chunk stored transposed ([column][key], fp16).  Inside each 32-key half the key k sits at
-  // position 8*((k % 16) / 4) + 4*(k / 16) + k % 4, so the eight keys that lane group g feeds to
-  // one P V product ({4g..4g+3} and {16+4g..16+4g+3}) are one contiguous 16-byte read.
-  auto store_out_of = [&](const uint4 (&pre)[NPRE], int kbuf, int vbuf) __attribute__((always_inline)) {
-    if (stages_v) {
-      _Float16* V = Vt + vbuf * VBUF;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int e = sidx + i * VTH;
-        const int kq = e % (kChunk / 4), dq = e / (kChunk / 4);
-        uint32_t wv[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 u = pre[4 * i + j];
-          if constexpr (VF16) {
-            wv[j][0] = u.x; wv[j][1] = u.y; wv[j][2] = u.z; wv[j][3] = u.w;
-          } else {
-            const uint32_t src[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const _Float16 lo = _Float16(__uint_as_float(src[c] << 16));
-              const _Float16 hi = _Float16(__uint_as_float(src[c] & 0xFFFF0000u));
-              wv[j][c] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
-            }
-          }
-        }
-        const int pos = (kq / 8) * 32 + 8 * (kq % 4) + 4 * ((kq % 8) / 4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // columns 2c (low halves) and 2c + 1 (high halves) of the four keys
-          const uint2 lo = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x05040100u),
-                                      __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x05040100u));
-          const uint2 hi = make_uint2(__builtin_amdgcn_perm(wv[1][c], wv[0][c], 0x07060302u),
-                                      __builtin_amdgcn_perm(wv[3][c], wv[2][c], 0x07060302u));
-          // rows 2c and 2c + 1 (relative to dq * 8) share one swizzle
-          const int row = dq * 8 + 2 * c;
-          const int at = ((pos >> 3) ^ ((row >> 1) & 7)) * 8 + (pos & 7);
-          *reinterpret_cast<uint2*>(V + row * VS + at) = lo;
-          *reinterpret_cast<uint2*>(V + (row + 1) * VS + at) = hi;
-        }
-      }
-    } else if (stages_k) {
-      uint16_t* K = Ks + kbuf * KBUF;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int e = sidx + i * KTH;
-        const int row = e / KPR;
-        *reinterpret_cast<uint4*>(K + row * KS + ((e % KPR) ^ (row % KPR)) * 8) = pre[i];
-      }
-    }
+    kbias[(slot * 2) * 64 + lane] = (cat & 1) ? 0.f : -INFINITY;
+    kbias[(slot * 2 + 1) * 64 + lane] = (cat & 2) ? 0.f : -INFINITY;
   };
 
-  auto load_to = [&](auto set, int ch) __attribute__((always_inline)) {
-    if constexpr (decltype(set)::value) load_into(pre1, ch);
-    else load_into(pre0, ch);
+  // Direct loads: wave w issues K loads j = 4 i + w and V loads j = 4 i + w (i < KQ, VQ); K loads
+  // past 4 KQ (the padding makes KLOADS = 4 KQ + 1) go to wave 0.  Lane l of load j fills 16-byte
+  // slot 64 j + l of its buffer: K slot s is piece s % KSTR of row s / KSTR (the padding piece
+  // re-reads piece 0), V slot s holds piece (s % PCS) ^ vswz(row % 4) of row s / PCS.
+  constexpr int KQ = S::KLOADS / 4, VQ = S::VLOADS / 4;
+  static_assert(S::VLOADS == 4 * VQ && S::KLOADS == 4 * KQ + 1, "load split");
+  auto kslot = [&](int j) __attribute__((always_inline)) -> int {  // row | byte column << 8
+    const int s = 64 * j + lane, pc = s % S::KSTR;
+    return (s / S::KSTR) | ((pc < S::PCS ? pc : 0) * 16) << 8;
   };
-  auto store_from = [&](auto set, int kbuf, int vbuf) __attribute__((always_inline)) {
-    if constexpr (decltype(set)::value) store_out_of(pre1, kbuf, vbuf);
-    else store_out_of(pre0, kbuf, vbuf);
+  int kslots[KQ];
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) kslots[i] = kslot(4 * i + w);
+  const int kslot_x = kslot(4 * KQ);
+  constexpr int VRPL = 64 / S::PCS;  // V rows per load: 4 (D = 128) or 8 (D = 64)
+  const int vrow_l = lane / S::PCS, vcol = ((lane % S::PCS) ^ S::vswz(vrow_l & 3)) * 16;
+  const int klast = t.key1 - 1;
+  auto key_row = [&](int ch, int r) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) return rowidx[(ch & (kRing - 1)) * 64 + r];
+    else return min(t.key0 + ch * KC + r, klast);
   };
+  auto kload = [&](int ch, int buf, int j, int slot) __attribute__((always_inline)) {
+    lds_load16(krsrc, Kl + buf * S::KBUF + j * 1024, key_row(ch, slot & 255) * krow_bytes + (slot >> 8));
+  };
+  auto issue_k = [&](int ch, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) kload(ch, buf, 4 * i + w, kslots[i]);
+    if (w == 0) kload(ch, buf, 4 * KQ, kslot_x);
+  };
+  auto issue_v = [&](int ch, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < VQ; ++i) {
+      const int j = 4 * i + w;
+      lds_load16(vrsrc, Vl + buf * S::VBUF + j * 1024, key_row(ch, VRPL * j + vrow_l) * VROW + vcol);
+    }
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+  // LDS read addresses.  K fragment of key row 32 tt + q32, columns 16 s + 8 kg: byte
+  // (32 tt + q32) KSTR 16 + (2 s + kg) 16.  V transposing read of a 16-lane group: lane
+  // i = 4 k + c supplies row R0 + k (R0 = 16 sg + 8 j + 4 kg) and columns 32 dt + 16 gg + 4 c .. + 3.
+  const int kaddr = q32 * S::KSTR * 16 + kg * 16;
+  int vaddr[NT];
+  {
+    const int i16 = lane & 15, gg = (lane >> 4) & 1, kk = i16 >> 2, cc = i16 & 3;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+      vaddr[dt] = (4 * kg + kk) * VROW + (((4 * dt + 2 * gg + (cc >> 1)) ^ S::vswz(kk)) * 16) + (cc & 1) * 8;
+  }
 
   const float scale = kLog2e / sqrtf(float(D));
-  float m_run = -INFINITY;
-  f32x4_t oacc[NT], lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, lsum = 0.f;
+  f32x16_t oacc[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) oacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f16x8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  for (int dt = 0; dt < NT; ++dt) oacc[dt] = f32x16_t{};
+  const f16x2_t ones2 = {_Float16(1.0f), _Float16(1.0f)};
 
-  // S^T = K Q^T of one chunk
-  auto qk = [&](f32x4_t (&sacc)[4], int kbuf) __attribute__((always_inline)) {
-    const uint16_t* K = Ks + kbuf * KBUF;
+  // scores of chunk c: the accumulators start from this half's key bias (score register r of tile
+  // tt holds key 32 tt + 8 (r / 4) + 4 kg + r % 4); K fragment reads run two MFMAs ahead
+  auto qk = [&](f32x16_t (&sacc)[2], int c) __attribute__((always_inline)) {
+    const float* bias = kbias + ((c & (kRing - 1)) * 2 + half) * 64 + 4 * kg;
+    const char* K = Kl + (c & 1) * S::KBUF + kaddr;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int row = mt * 16 + r16;
-        const bf16x8_t kf = as_bf16x8(
-            *reinterpret_cast<const uint4*>(K + row * KS + (((ks * 4 + g) ^ (row % KPR)) * 8)));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const float4 b = *reinterpret_cast<const float4*>(bias + 32 * tt + 8 * j);
+        sacc[tt][4 * j] = b.x; sacc[tt][4 * j + 1] = b.y; sacc[tt][4 * j + 2] = b.z; sacc[tt][4 * j + 3] = b.w;
       }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(*reinterpret_cast<const uint4*>(K + (32 * tt * S::KSTR + 2 * s) * 16)), as_bf16x8(qf[s]),
+            sacc[tt], 0, 0, 0);
     }
   };
-  // Keys whose bit in m is clear get the score -inf (partial chunks only: tails and the seams
-  // between the runs of a paired tile).
-  auto apply_mask = [&](f32x4_t (&sacc)[4], unsigned long long m) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (!((m >> (mt * 16 + 4 * g + v)) & 1ull)) sacc[mt][v] = -INFINITY;
-  };
-  // Online softmax of one chunk's scores and O^T += V^T P^T; the row sums come from the same
-  // fp16 P through an MFMA against a tile of ones.  P is formed with the running shift first; if
-  // any p of the wave exceeds 2^8 (tested on the bit patterns, which order non-negative floats
-  // and put inf and NaN above every finite value) the rare path forms the row maxima over the
-  // four lanes of each row, raises the shift where it grew by more than 2^8, rescales O and l,
-  // and forms P again.
-  auto exps = [&](const f32x4_t (&sacc)[4], float (&pv)[16]) __attribute__((always_inline)) {
+  // The running maximum is raised lazily: while every p of the wave stays <= 2^8 (exact range in
+  // fp16; tested on the bit patterns, which order non-negative floats and put inf and NaN above
+  // every finite value) the shift is kept; otherwise the rows whose maximum grew by more than
+  // 2^8 take it as their new shift and O and l, which by then hold every earlier chunk, are
+  // rescaled before the exponentials are formed again.
+  auto exps = [&](const f32x16_t (&sacc)[2], f16x2_t (&pk)[16]) __attribute__((always_inline)) -> unsigned {
     const float mneg = -m_run;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) pv[mt * 4 + v] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][v], scale, mneg));
-  };
-  auto finish_pv = [&](const f32x4_t (&sacc)[4], float (&pv)[16], int vbuf, auto&& mid) __attribute__((always_inline)) {
-    const _Float16* V = Vt + vbuf * VBUF;
     unsigned big = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) big = max(big, __float_as_uint(pv[i]));
-    if (__builtin_expect(__any(big > 0x43800000u), 0)) {
-      __asm__ volatile("; rare rescale of the running output" ::);
-      float mx = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
-#pragma unroll
-      for (int mt = 1; mt < 4; ++mt)
-        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][0], sacc[mt][1])), fmaxf(sacc[mt][2], sacc[mt][3]));
-      mx *= scale;
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m_run + kRescale;
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      lacc *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) oacc[nt] *= alpha;
-      exps(sacc, pv);
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 3][(2 * i) & 15], scale, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 3][(2 * i + 1) & 15], scale, mneg));
+      big = max(big, max(__float_as_uint(p0), __float_as_uint(p1)));
+      pk[i] = f16x2_t{_Float16(p0), _Float16(p1)};
     }
-    f16x8_t pf[2];
+    return big;
+  };
+  auto rescale = [&](const f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pf[i >> 3][i & 7] = _Float16(pv[i]);
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[h], lacc, 0, 0, 0);
-    mid();
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[tt][r]);
+    mx *= scale;
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool grow = mx > m_run + 8.0f;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    lsum *= alpha;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int dt = 0; dt < NT; ++dt) oacc[dt] *= alpha;
+  };
+  auto exps_settled = [&](const f32x16_t (&sacc)[2], f16x2_t (&pk)[16], unsigned big) __attribute__((always_inline)) {
+    if (__builtin_expect(__any(big > 0x43800000u), 0)) {
+      rescale(sacc);
+      exps(sacc, pk);
+    }
+  };
+  auto pv = [&](const f16x2_t (&pk)[16], int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f16x8_t av = __builtin_bit_cast(
-            f16x8_t, *reinterpret_cast<const uint4*>(V + (nt * 16 + r16) * VS +
-                                                      (((4 * h + g) ^ (((nt * 16 + r16) >> 1) & 7)) * 8)));
-        oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pf[h], oacc[nt], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) lsum = __builtin_amdgcn_fdot2(pk[i], ones2, lsum, false);
+    const char* V = Vl + (c & 1) * S::VBUF;
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+      // B operand: p of keys 16 sg + 8 (j / 4) + 4 kg + j % 4, i.e. registers 8 (sg % 2) .. + 7 of tile sg / 2
+      typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+      f16x8 b;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b[2 * j] = pk[4 * sg + j][0];
+        b[2 * j + 1] = pk[4 * sg + j][1];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        const h4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPR_LDS h4_t*)(V + vaddr[dt] + (16 * sg) * VROW));
+        const h4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((SPR_LDS h4_t*)(V + vaddr[dt] + (16 * sg + 8) * VROW));
+        const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+        const f16x8 a = __builtin_bit_cast(f16x8, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, oacc[dt], 0, 0, 0);
       }
     }
-  };
-  auto softmax_pv = [&](f32x4_t (&sacc)[4], int vbuf, auto&& mid) __attribute__((always_inline)) {
-    float pv[16];
-    exps(sacc, pv);
-    finish_pv(sacc, pv, vbuf, mid);
-  };
-  // The scores of the next chunk on the matrix cores interleaved with the exponentials of this
-  // chunk on the vector ALU (one K fragment read, one MFMA and two VALU operations per slot).
-  auto qk_exps = [&](f32x4_t (&s_nxt)[4], int kbuf, const f32x4_t (&s_cur)[4], float (&pv)[16])
-                     __attribute__((always_inline)) {
-    qk(s_nxt, kbuf);
-    exps(s_cur, pv);
-    constexpr int AHEAD = 4;  // K fragment reads issued ahead of their MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-      if (i + AHEAD < 4 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-  };
-  auto half_mask = [&](int c) __attribute__((always_inline)) -> unsigned long long {
-    const unsigned long long mk = cmask[(c & 7) * 2 + half];
-    const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(mk));
-    const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(mk >> 32));
-    return (static_cast<unsigned long long>(hi) << 32) | lo;
   };
 
-  // Pipeline over 64-key chunks.  Chunk x is staged in register set x & 1, then in K buffer
-  // x & 1 and V buffer x % 3.  Step c computes the scores of chunk c+1 and the softmax and PV
-  // product of chunk c (whose scores step c-1 computed), stores chunk c+2 into LDS, issues the
-  // loads of chunk c+4 and resolves the rows of chunk c+5.  Loads, stores and row resolution
-  // run for chunks past the end too (rows clamp to 0, masks are empty), so no branch skips a
-  // load and every step keeps the same number of loads in flight.
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  if (w == 0)
-    for (int c = 0; c < 5; ++c) resolve(c);
-  __syncthreads();
-  load_to(S0{}, 0);
-  load_to(S1{}, 1);
-  store_from(S0{}, 0, 0);
-  load_to(S0{}, 2);
-  store_from(S1{}, 1, 1);
-  load_to(S1{}, 3);
-  __syncthreads();
-  f32x4_t sa[4], sb[4];
-  if (wave_active && half_mask(0) != 0ull) qk(sa, 0);
-  __syncthreads();  // step 0 overwrites K buffer 0
-  // The LDS staging of chunk c+2 runs inside the P V products of chunk c (its VALU and LDS
-  // writes issue while the matrix cores work); the loads of chunk c+4 reuse its registers after.
-  auto step = [&](auto set, int c, f32x4_t (&s_cur)[4], f32x4_t (&s_nxt)[4]) __attribute__((always_inline)) {
-    auto stage = [&]() __attribute__((always_inline)) { store_from(set, c & 1, (c + 2) % 3); };
-    // the dense and probe kernels convert V while staging, which needs the registers the
-    // overlap would take: they stage first
-    constexpr bool kLate = SPARSE;
-    if constexpr (!kLate) {
-      stage();
-      load_to(set, c + 4);
-    }
-    auto mid = [&]() __attribute__((always_inline)) {
-      if constexpr (kLate) stage();
-    };
-    if (w == 0) resolve(c + 5);
-    bool staged = !kLate;
-    if (wave_active) {
-      const unsigned long long mn = half_mask(c + 1), m = half_mask(c);
-      if (__builtin_expect(m != ~0ull, 0) && m != 0ull) apply_mask(s_cur, m);
-      if (__builtin_expect(mn != 0ull && m != 0ull, 1)) {
-        float pv[16];
-        qk_exps(s_nxt, (c + 1) & 1, s_cur, pv);
-        finish_pv(s_cur, pv, c % 3, mid);
-        staged = true;
-      } else if (mn != 0ull) {
-        qk(s_nxt, (c + 1) & 1);
-      } else if (m != 0ull) {
-        softmax_pv(s_cur, c % 3, mid);
-        staged = true;
-      }
-    }
-    if constexpr (kLate) {
-      if (!staged) stage();
-      load_to(set, c + 4);
-    }
-    __syncthreads();
+  // Steps: step c (one barrier) computes the scores of chunk c, then its exponentials interleaved
+  // with the P V products of chunk c - 1, while K(c + 1) and V(c) load and wave 0 prepares chunk
+  // c + 2.  Every wave takes part in all nchunks + 1 steps; it computes over the chunk runs its
+  // half attends to (one run, or for half 1 of a paired tile the shared run and its own run)
+  // and only loads in the other steps.  An empty key range (a probe split of fewer keys than
+  // splits) leaves l = 0 and the shift at -inf.
+  auto begin_step = [&](int c) __attribute__((always_inline)) {
+    __syncthreads();  // K(c) and V(c - 1) are staged; every wave is done with K(c - 1) and V(c - 2)
+    if (w == 0) prepare(c + 2);
+    issue_k(c + 1, (c + 1) & 1);
+    issue_v(c, c & 1);
   };
-  for (int c = 0; c < nchunks; c += 2) {
-    step(S0{}, c, sa, sb);
-    step(S1{}, c + 1, sb, sa);
+  f32x16_t sacc[2];
+  f16x2_t p_old[16];
+  // chunks [lo, hi) in steps lo .. hi: a first step without P V products, straight steps with
+  // them (the hot loop), and a last step with the P V products of chunk hi - 1 alone
+  auto run = [&](int lo, int hi) __attribute__((always_inline)) {
+    if (lo >= hi) return;
+    begin_step(lo);
+    qk(sacc, lo);
+    exps_settled(sacc, p_old, exps(sacc, p_old));
+    wait_loads();
+    for (int c = lo + 1; c < hi; ++c) {
+      begin_step(c);
+      qk(sacc, c);
+      f16x2_t p_new[16];
+      const unsigned big = exps(sacc, p_new);
+      pv(p_old, c - 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * NT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 64 / (4 * NT), 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 32 / (4 * NT), 0);
+        if (i + 2 < 4 * NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      exps_settled(sacc, p_new, big);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p_old[i] = p_new[i];
+      wait_loads();
+    }
+    begin_step(hi);
+    pv(p_old, hi - 1);
+    wait_loads();
+  };
+  auto idle = [&](int lo, int hi) __attribute__((always_inline)) {
+    for (int c = lo; c < hi; ++c) {
+      begin_step(c);
+      wait_loads();
+    }
+  };
+  if (nchunks > 0) {
+    if (w == 0)
+      for (int c = 0; c < 2; ++c) prepare(c);
+    __syncthreads();
+    issue_k(0, 0);
+    wait_loads();
+    // this wave's chunk runs
+    int lo0 = 0, hi0 = nchunks, lo1 = nchunks, hi1 = nchunks;
+    if (SPARSE && half == 1 && t.pair) {
+      // the shared run, then from the chunk holding key k31 (when half 1 has keys of its own)
+      const int b = (k3 + KC - 1) / KC, c1 = k31 < total ? k31 / KC : nchunks;
+      if (c1 > b) {
+        hi0 = b;
+        lo1 = c1;
+      }
+    } else if (SPARSE && t.pair) {
+      hi0 = (k31 + KC - 1) / KC;
+    }
+    if (!wave_active) {
+      hi0 = lo1 = hi1 = 0;
+    }
+    run(lo0, hi0);
+    int st = hi0 > lo0 ? hi0 + 1 : 0;
+    idle(st, lo1);
+    run(lo1, hi1);
+    st = hi1 > lo1 ? hi1 + 1 : max(st, lo1);
+    idle(st, nchunks + 1);
   }
   if (!qvalid) return;
-  const float lt = lacc[0];
+  // the two 32-lane halves hold the sums of the two halves of every chunk's keys
+  const float lt = lsum + __shfl_xor(lsum, 32);
+  // output column of register r of tile dt: 32 dt + 8 (r / 4) + 4 kg + r % 4
   if constexpr (MODE == MODE_PROBE) {
-    float* dst = P.part + ((size_t(hd) * P.M + my_row0 + qslot) * P.splits + t.split) * (D + 2);
+    float* dst = P.part + ((size_t(hd) * P.M + my_row0 + q32) * P.splits + t.split) * (D + 2);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) = make_float4(oacc[nt][0], oacc[nt][1], oacc[nt][2], oacc[nt][3]);
-    if (g == 0) {
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * j + 4 * kg) =
+            make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
+    if (kg == 0) {
       dst[D] = m_run;
       dst[D + 1] = lt;
     }
   } else {
-    const float inv = 1.f / lt;
+    const float inv = P.vscale_inv(hk) / lt;
     if constexpr (SPARSE) {
-      float* dst = P.o_sp + (size_t(hd) * P.g.N + my_row0 + qslot) * D;
+      float* dst = P.o_sp + (size_t(hd) * P.g.N + my_row0 + q32) * D;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<float4*>(dst + nt * 16 + 4 * g) =
-            make_float4(oacc[nt][0] * inv, oacc[nt][1] * inv, oacc[nt][2] * inv, oacc[nt][3] * inv);
+      for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(dst + 32 * dt + 8 * j + 4 * kg) =
+              make_float4(oacc[dt][4 * j] * inv, oacc[dt][4 * j + 1] * inv, oacc[dt][4 * j + 2] * inv,
+                          oacc[dt][4 * j + 3] * inv);
     } else {
-      const size_t rowbase = (size_t(hd) * P.g.N + my_row0 + qslot) * D;
+      const size_t rowbase = (size_t(hd) * P.g.N + my_row0 + q32) * D;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const size_t idx = rowbase + nt * 16 + 4 * g + v;
-          if (P.out_dtype == SPR_BF16) store_out<SPR_BF16>(P.out, idx, oacc[nt][v] * inv);
-          else store_out<SPR_F32>(P.out, idx, oacc[nt][v] * inv);
+        for (int j = 0; j < 4; ++j) {
+          const size_t idx = rowbase + 32 * dt + 8 * j + 4 * kg;
+          const float x0 = oacc[dt][4 * j] * inv, x1 = oacc[dt][4 * j + 1] * inv;
+          const float x2 = oacc[dt][4 * j + 2] * inv, x3 = oacc[dt][4 * j + 3] * inv;
+          if (P.out_dtype == SPR_BF16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(P.out) + idx) =
+                make_uint2(bf16_pair_rne(x0, x1), bf16_pair_rne(x2, x3));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(P.out) + idx) = make_float4(x0, x1, x2, x3);
         }
     }
   }
@@ -774,9 +774,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams P) {
   }
 }
 
-// Merge split-K partials: O = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
+// Merge split-K partials: O = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m), times the factor that
+// undoes the scaling of the fp16 copy of V (bf16 inputs).
 __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restrict__ part, int M, int splits, int D,
-                                                          int BH, float* __restrict__ o_probe) {
+                                                          int BH, int G, const float* __restrict__ vinv,
+                                                          float* __restrict__ o_probe) {
   const int row = blockIdx.x;  // over BH * M
   if (row >= BH * M) return;
   const float* pr = part + size_t(row) * splits * (D + 2);
@@ -784,11 +786,109 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
   for (int s = 0; s < splits; ++s) mx = fmaxf(mx, pr[s * (D + 2) + D]);
   float l = 0.f;
   for (int s = 0; s < splits; ++s) l += pr[s * (D + 2) + D + 1] * exp2f(pr[s * (D + 2) + D] - mx);
+  const float f = vinv ? vinv[(row / M) / G] : 1.f;
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float acc = 0.f;
     for (int s = 0; s < splits; ++s) acc += pr[s * (D + 2) + c] * exp2f(pr[s * (D + 2) + D] - mx);
-    o_probe[size_t(row) * D + c] = acc / l;
+    o_probe[size_t(row) * D + c] = acc / l * f;
   }
+}
+
+// ------------------------------------------------------------------ fp16 copy of V
+// The P V products run in fp16, whose range is narrower than bf16's.  Every K/V head's V is
+// scaled by 2^e, e chosen from its largest magnitude so that it lies in [2^14, 2^15) (e within
+// [-100, 100]; a head of zeros, infinities or NaN keeps e = 0), and the output is multiplied by
+// 2^-e.  Scaling by a power of two is exact; only magnitudes below 2^-24 of the head's largest
+// lose bits to fp16 rounding.
+
+// largest |v| per K/V head as a float bit pattern (non-negative patterns order like the values);
+// grid (ceil(N d / 8 / 256), heads), amax cleared by v_amax_clear_kernel
+__global__ __launch_bounds__(256) void v_absmax_kernel(const uint16_t* __restrict__ v, HeadGeom gk,
+                                                       unsigned* __restrict__ amax) {
+  __shared__ unsigned red[4];
+  const int hk = blockIdx.y, per = gk.d / 8;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  unsigned m = 0;
+  if (idx < int64_t(gk.N) * per) {
+    const int row = int(idx / per), pc = int(idx % per);
+    const uint4 u = *reinterpret_cast<const uint4*>(v + gk.base(hk) + int64_t(row) * gk.sn + pc * 8);
+    const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const unsigned lo = (wv[c] << 16) & 0x7FFF0000u, hi = wv[c] & 0x7FFF0000u;
+      m = max(m, max(lo, hi));
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) m = max(m, unsigned(__shfl_xor(int(m), o)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax + hk, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+__global__ void v_amax_clear_kernel(unsigned* __restrict__ amax, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) amax[i] = 0u;
+}
+// scale[hk] = 2^e, scale[n + hk] = 2^-e
+__global__ void v_scale_kernel(const unsigned* __restrict__ amax, int n, float* __restrict__ scale) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const unsigned a = amax[i];
+  int e = 0;
+  if (a != 0u && (a & 0x7F800000u) != 0x7F800000u) {
+    const int E = int(a >> 23) - 127;  // floor(log2 a) for normal a; subnormals clamp below
+    e = min(100, max(-100, 14 - E));
+  }
+  scale[i] = __uint_as_float(uint32_t(127 + e) << 23);
+  scale[n + i] = __uint_as_float(uint32_t(127 - e) << 23);
+}
+// contiguous [heads][N][d] fp16 copy of v scaled by scale[hk]; grid (ceil(N d / 8 / 256), heads)
+__global__ __launch_bounds__(256) void v_to_f16_kernel(const uint16_t* __restrict__ v, HeadGeom gk,
+                                                       const float* __restrict__ scale, _Float16* __restrict__ vh) {
+  const int hk = blockIdx.y, per = gk.d / 8;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= int64_t(gk.N) * per) return;
+  const int row = int(idx / per), pc = int(idx % per);
+  const uint4 u = *reinterpret_cast<const uint4*>(v + gk.base(hk) + int64_t(row) * gk.sn + pc * 8);
+  const float f = scale[hk];
+  const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  h8 o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    o[2 * c] = _Float16(__uint_as_float(wv[c] << 16) * f);
+    o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u) * f);
+  }
+  *reinterpret_cast<h8*>(vh + (size_t(hk) * gk.N + row) * gk.d + pc * 8) = o;
+}
+
+void launch_v_scale(const void* v, const HeadGeom& gk, int heads, unsigned* amax, float* scale, hipStream_t st) {
+  hipLaunchKernelGGL(v_amax_clear_kernel, dim3(ceil_div(heads, 256)), dim3(256), 0, st, amax, heads);
+  const dim3 grid(unsigned(ceil_div64(int64_t(gk.N) * gk.d / 8, 256)), heads);
+  hipLaunchKernelGGL(v_absmax_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(v), gk, amax);
+  hipLaunchKernelGGL(v_scale_kernel, dim3(ceil_div(heads, 256)), dim3(256), 0, st, amax, heads, scale);
+}
+
+size_t v_copy_bytes(const spr_desc& desc) {
+  if (desc.dtype != SPR_BF16) return 0;
+  const size_t heads = size_t(desc.B) * kv_heads(desc);
+  return ((heads * desc.N * desc.d * 2 + 255) & ~size_t(255)) + ((heads * 4 + 255) & ~size_t(255)) +
+         ((2 * heads * 4 + 255) & ~size_t(255));
+}
+
+// scaled fp16 copy of v in ws (layout of v_copy_bytes); returns the inverse factors
+static const float* make_v_copy(const spr_desc& desc, const void* v, void* ws, _Float16** vh, hipStream_t st) {
+  const int heads = desc.B * kv_heads(desc);
+  const HeadGeom gk = make_kv_geom(desc);
+  char* base = static_cast<char*>(ws);
+  *vh = reinterpret_cast<_Float16*>(base);
+  base += (size_t(heads) * desc.N * desc.d * 2 + 255) & ~size_t(255);
+  unsigned* amax = reinterpret_cast<unsigned*>(base);
+  base += (size_t(heads) * 4 + 255) & ~size_t(255);
+  float* scale = reinterpret_cast<float*>(base);
+  launch_v_scale(v, gk, heads, amax, scale, st);
+  const dim3 grid(unsigned(ceil_div64(int64_t(gk.N) * gk.d / 8, 256)), heads);
+  hipLaunchKernelGGL(v_to_f16_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(v), gk, scale, *vh);
+  return scale + heads;
 }
 
 // ------------------------------------------------------------------ sparse tiles
@@ -984,27 +1084,14 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict
   if (threadIdx.x == 0) prefix[BH] = carry;
 }
 
-template <int MODE>
-constexpr int mfma_waves() { return 8; }
-template <int MODE>
-constexpr int mfma_rows() { return 16 * mfma_waves<MODE>(); }
-
-template <int D, int MODE>
-static size_t mfma_smem() {
-  size_t s = 2 * size_t(kChunk) * D * 2 + 3 * size_t(D) * kChunk * 2 + 8 * kChunk * sizeof(int) +
-             16 * sizeof(unsigned long long);
-  if (MODE == MODE_SPARSE) s += (3 * kSegCap + 66 + mfma_waves<MODE>() * 64) * sizeof(int);
-  return s;
-}
+constexpr int kAttnRows = 128;  // query rows per block of the bf16 kernel
 
 template <int D, int MODE>
 static void launch_attn(const AttnParams& P, dim3 grid, int dtype, hipStream_t st) {
   if (dtype == SPR_BF16) {
-    constexpr int W = mfma_waves<MODE>();
-    constexpr bool VF16 = MODE == MODE_SPARSE;  // the sparse kernel reads the fp16 copy of V
-    const size_t sm = mfma_smem<D, MODE>();
-    allow_lds(attn_mfma_kernel<D, MODE, W, VF16>, sm);
-    hipLaunchKernelGGL((attn_mfma_kernel<D, MODE, W, VF16>), grid, dim3(W * 64), sm, st, P);
+    constexpr size_t sm = attn32_smem<D, MODE>();
+    allow_lds(attn32_kernel<D, MODE>, sm);
+    hipLaunchKernelGGL((attn32_kernel<D, MODE>), grid, dim3(256), sm, st, P);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, MODE>), grid, dim3(64), 0, st, P);
   }
@@ -1043,7 +1130,10 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
   SPR_CHECK_LAUNCH();
   AttnParams P = {};
   P.q = part.Qp; P.k = part.Kp; P.v = part.Vp;
-  if (desc.dtype == SPR_BF16) P.v = ws_ptr<void>(ws, L.vh);
+  if (desc.dtype == SPR_BF16) {
+    P.v = ws_ptr<void>(ws, L.vh);
+    P.vinv = ws_ptr<float>(ws, L.vscale) + desc.B * kv_heads(desc);
+  }
   P.g = make_geom(desc);
   P.gk = make_kv_geom(desc);
   P.G = kv_group_size(desc);
@@ -1067,24 +1157,35 @@ spr_status run_probe_exact(const spr_desc& desc, const void* q, const void* k, c
   P.G = kv_group_size(desc);
   P.probe_idx = probe_idx; P.M = M; P.splits = L.splits;
   P.part = ws_ptr<float>(ws, L.pr_part);
+  if (desc.dtype == SPR_BF16) {
+    _Float16* vh;
+    P.vinv = make_v_copy(desc, v, ws_ptr<char>(ws, L.pr_vcopy), &vh, st);
+    P.v = vh;
+  }
   const int BH = desc.B * desc.H;
-  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_PROBE>() : kTileRows;
+  const int rows = desc.dtype == SPR_BF16 ? kAttnRows : kTileRows;
   spr_status s = dispatch_d<MODE_PROBE>(P, dim3(ceil_div(M, rows), BH, L.splits), desc.d, desc.dtype, st);
   if (s != SPR_OK) return s;
-  hipLaunchKernelGGL(probe_merge_kernel, dim3(BH * M), dim3(128), 0, st, P.part, M, L.splits, desc.d, BH, o_probe);
+  hipLaunchKernelGGL(probe_merge_kernel, dim3(BH * M), dim3(128), 0, st, P.part, M, L.splits, desc.d, BH, P.G, P.vinv,
+                     o_probe);
   SPR_CHECK_LAUNCH();
   return SPR_OK;
 }
 
 spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
-                          int out_dtype, hipStream_t st) {
+                          int out_dtype, void* ws, hipStream_t st) {
   AttnParams P = {};
   P.q = q; P.k = k; P.v = v;
   P.g = make_geom(desc);
   P.gk = make_kv_geom(desc);
   P.G = kv_group_size(desc);
   P.out = out; P.out_dtype = out_dtype;
-  const int rows = desc.dtype == SPR_BF16 ? mfma_rows<MODE_DENSE>() : kTileRows;
+  if (desc.dtype == SPR_BF16) {
+    _Float16* vh;
+    P.vinv = make_v_copy(desc, v, ws, &vh, st);
+    P.v = vh;
+  }
+  const int rows = desc.dtype == SPR_BF16 ? kAttnRows : kTileRows;
   return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, rows), desc.B * desc.H), desc.d, desc.dtype, st);
 }
 

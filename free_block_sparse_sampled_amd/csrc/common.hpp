@@ -201,8 +201,11 @@ struct Workspace {
   size_t serr;       // double [BH][Cq][Ck]      bounds of the bf16 scores (unless the caller keeps them)
   size_t qsplit;     // bf16   [BH][Cq][3][d]    qbar as hi, mid, lo bf16 slices (bf16 inputs)
   size_t qnorm;      // double [BH][Cq]          |qbar_a|
-  size_t vh;         // fp16   [BH][N][d]        group-major values converted to fp16 (bf16 inputs)
-  size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows
+  size_t vh;         // fp16   [BHkv][N][d]      group-major values, scaled, in fp16 (bf16 inputs)
+  size_t vamax;      // uint   [BHkv]            largest |v| per K/V head (bit pattern)
+  size_t vscale;     // float  [2][BHkv]         2^e and 2^-e, the scaling of the fp16 values
+  size_t pr_part;    // float  [BH][M][S][d+2]   split-K partials of the probe rows (probe call)
+  size_t pr_vcopy;   // fp16 copy of v and its scales (probe call; see v_copy_bytes)
   size_t fitX;       // double [BH][M][d]        standardised probe features
   size_t fitR;       // double [BH][M][d]        centred probe residuals
   size_t fitG;       // double [BH][d][d]        normal matrix

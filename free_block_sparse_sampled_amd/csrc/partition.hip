@@ -500,10 +500,13 @@ __device__ inline void right_solve_upper(const double* Zt, const double* Rm, dou
 // U^T M U at or below clamp, times the largest diagonal entry of its matrix (or a zero previous
 // column) stops the head: ok = 0 in gstat[hd][slot] and the eigendecomposition takes over;
 // otherwise ok = 1 and F is written.
+// The previous factor may be the very buffer the new one is written to (a later call that passes
+// the operator's own outputs as its state): each block reads its head's previous factor before a
+// barrier and writes the new one last, and neither pointer is restrict-qualified.
 template <int D, int R>
 __global__ __launch_bounds__(256) void subspace_factor_kernel(const double* __restrict__ Mall,
-                                                              const double* __restrict__ Fprev, double clamp,
-                                                              double* __restrict__ Fall, int* __restrict__ gstat,
+                                                              const double* Fprev, double clamp,
+                                                              double* Fall, int* __restrict__ gstat,
                                                               int ok_slot) {
   constexpr int TD = D / 16, TR = (R + 15) / 16;
   extern __shared__ double sub_sm[];
@@ -901,7 +904,8 @@ __global__ __launch_bounds__(1024) void km_compact_kernel(const int* __restrict_
 template <int DT>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict__ src, HeadGeom g,
                                                           const int* __restrict__ perm, void* __restrict__ dst,
-                                                          _Float16* __restrict__ dst16 = nullptr) {
+                                                          _Float16* __restrict__ dst16 = nullptr,
+                                                          const float* __restrict__ scale16 = nullptr) {
   constexpr int ES = ElemSize<DT>::value;
   const int hd = blockIdx.y;
   const int pieces = g.d * ES / 16;
@@ -913,14 +917,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const void* __restrict
   char* dd = static_cast<char*>(dst) + ((size_t(hd) * g.N + pos) * g.d) * ES + pc * 16;
   const uint4 u = *reinterpret_cast<const uint4*>(s);
   *reinterpret_cast<uint4*>(dd) = u;
-  if (dst16) {  // bf16 rows: also the fp16 copy (the operand type of the P V products)
+  if (dst16) {  // bf16 rows: also the fp16 copy scaled by 2^e (the operand of the P V products)
     const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+    const float f = scale16[hd];
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     h8 o;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      o[2 * c] = _Float16(__uint_as_float(wv[c] << 16));
-      o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u));
+      o[2 * c] = _Float16(__uint_as_float(wv[c] << 16) * f);
+      o[2 * c + 1] = _Float16(__uint_as_float(wv[c] & 0xFFFF0000u) * f);
     }
     *reinterpret_cast<h8*>(dst16 + (size_t(hd) * g.N + pos) * g.d + pc * 8) = o;
   }
@@ -1199,8 +1204,15 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   const dim3 ggrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BH);
   const dim3 kgrid(unsigned(ceil_div64(int64_t(desc.N) * pieces, 256)), BHkv);
   hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, k, gk, out.kv_perm, out.Kp);
-  hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp,
-                     DT == SPR_BF16 ? wsp<_Float16>(ws, L.vh) : nullptr);
+  if (DT == SPR_BF16) {
+    // power-of-two scale of each K/V head's values for their fp16 copy
+    launch_v_scale(v, gk, BHkv, wsp<unsigned>(ws, L.vamax), wsp<float>(ws, L.vscale), st);
+    hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp,
+                       wsp<_Float16>(ws, L.vh), static_cast<const float*>(wsp<float>(ws, L.vscale)));
+  } else {
+    hipLaunchKernelGGL(gather_rows_kernel<DT>, kgrid, dim3(256), 0, st, v, gk, out.kv_perm, out.Vp, nullptr,
+                       nullptr);
+  }
   SPR_CHECK_LAUNCH();
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Ck, 4), BHkv), dim3(256), 0, st, out.Kp, desc.N, d,
                      out.kv_off, out.n_kv, p.Ck, out.kbar);

@@ -71,7 +71,12 @@ spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const
 spr_status launch_eigen_factor(const double* Mall, int BH, int d, int r, double clamp, double* Fall, int* gstat,
                                hipStream_t st);
 spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
-                          int out_dtype, hipStream_t st);
+                          int out_dtype, void* ws, hipStream_t st);
+// Power-of-two scaling of bf16 values into fp16 (attention.hip): the largest |v| of every K/V head
+// of v (geometry gk) into amax, then scale[hk] = 2^e and scale[heads + hk] = 2^-e.
+void launch_v_scale(const void* v, const HeadGeom& gk, int heads, unsigned* amax, float* scale, hipStream_t st);
+// Bytes of a scaled fp16 copy of v with its scales (0 for fp32 inputs).
+size_t v_copy_bytes(const spr_desc& desc);
 
 // Raise the dynamic-LDS limit of a kernel above the 64 KB default once per process.
 template <typename K>

@@ -113,8 +113,13 @@ def library():
                                              ctypes.POINTER(spr_fit_options), P, ctypes.c_int32, P, P, P,
                                              ctypes.c_size_t, P]
         lib.sparsepr_fit_correct.restype = st
-        lib.sparsepr_attn_dense.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P]
+        lib.sparsepr_attn_dense.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
+                                            P]
         lib.sparsepr_attn_dense.restype = st
+        lib.sparsepr_dense_workspace_size.argtypes = [ctypes.POINTER(spr_desc)]
+        lib.sparsepr_dense_workspace_size.restype = ctypes.c_size_t
+        lib.sparsepr_probe_workspace_size.argtypes = [ctypes.POINTER(spr_desc), ctypes.c_int32]
+        lib.sparsepr_probe_workspace_size.restype = ctypes.c_size_t
         lib.sparsepr_kmeans.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P,
                                         ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, P, P, P, P,
                                         ctypes.c_size_t, P]
@@ -128,8 +133,9 @@ def library():
 
 
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attn_sparse",
-            "sparsepr_probe_exact", "sparsepr_fit_correct", "sparsepr_attn_dense", "sparsepr_kmeans",
-            "sparsepr_kmeans_workspace_size", "sparsepr_status_string"]
+            "sparsepr_probe_exact", "sparsepr_probe_workspace_size", "sparsepr_fit_correct", "sparsepr_attn_dense",
+            "sparsepr_dense_workspace_size", "sparsepr_kmeans", "sparsepr_kmeans_workspace_size",
+            "sparsepr_status_string"]
 
 
 def _check(status: int, what: str):
@@ -326,10 +332,27 @@ def sparsepr_fit_correct(desc, cfg: OperatorConfig, part: Partition, route: Rout
            "sparsepr_fit_correct")
 
 
-def sparsepr_attn_dense(desc, q, k, v, out, stream=None):
+def dense_workspace(desc, device) -> torch.Tensor:
+    n = library().sparsepr_dense_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise SparsePRError("sparsepr_dense_workspace_size: invalid descriptor")
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def probe_workspace(desc, M: int, device) -> torch.Tensor:
+    n = library().sparsepr_probe_workspace_size(ctypes.byref(desc), M)
+    if n == 0:
+        raise SparsePRError("sparsepr_probe_workspace_size: invalid arguments")
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def sparsepr_attn_dense(desc, q, k, v, out, ws: Optional[torch.Tensor] = None, stream=None):
+    """Dense flash attention of every row; ``ws`` (from ``dense_workspace``) is allocated when omitted."""
     out_dt = SPR_BF16 if out.dtype == torch.bfloat16 else SPR_F32
+    if ws is None:
+        ws = dense_workspace(desc, q.device)
     _check(library().sparsepr_attn_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dt,
-                                         _stream(stream)), "sparsepr_attn_dense")
+                                         _ptr(ws), ws.numel(), _stream(stream)), "sparsepr_attn_dense")
 
 
 def sparsepr_kmeans(feat: torch.Tensor, C: int, seed: int, stage: int, max_iters: int, tol: float, stream=None):
@@ -363,6 +386,7 @@ class SparsePR:
         dev = q.device
         B, H, N, d = q.shape
         self.ws = torch.empty(sparsepr_workspace_size(self.desc, cfg), dtype=torch.uint8, device=dev)
+        self.ws_probe = probe_workspace(self.desc, cfg.M, dev)
         self.part = Partition(self.desc, cfg, dev, diagnostics)
         self.route = Route(self.desc, cfg, dev, keep_scores)
         self.o_sp = torch.empty((B * H, N, d), dtype=torch.float32, device=dev)
@@ -388,7 +412,7 @@ class SparsePR:
         sparsepr_attn_sparse(self.desc, self.cfg, self.part, self.route, self.o_sp, self.ws)
 
     def probe_exact(self, q, k, v):
-        sparsepr_probe_exact(self.desc, q, k, v, self.route.probe_idx, self.cfg.M, self.o_probe, self.ws)
+        sparsepr_probe_exact(self.desc, q, k, v, self.route.probe_idx, self.cfg.M, self.o_probe, self.ws_probe)
 
     def fit_correct(self):
         sparsepr_fit_correct(self.desc, self.cfg, self.part, self.route, self.o_sp, self.o_probe, self.out,

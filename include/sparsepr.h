@@ -253,16 +253,27 @@ spr_status sparsepr_route(const spr_desc* desc, const spr_part_params* params, c
 
 /* Renormalised block-sparse attention (Eq. (2)): each row of query group a attends to the
    keys of its selected K/V groups (and the text keys); text rows attend to all keys.
-   o_sp: [BH][N][d] fp32, rows in Qp order. */
+   o_sp: [BH][N][d] fp32, rows in Qp order.
+   Numeric domain of bf16 inputs: scores are exact products summed in fp32; P and V enter the
+   P V products in fp16, V scaled per K/V head by the power of two 2^e that puts its largest
+   magnitude in [2^14, 2^15) (|e| <= 100, undone on the output), so the whole bf16 range is
+   accepted; entries below 2^-24 of their head's largest magnitude are rounded to fp16 steps
+   of that size.  Non-finite values propagate. */
 spr_status sparsepr_attn_sparse(const spr_desc* desc, const spr_part_params* params,
                                 const spr_partition* part, const spr_route* route, float* o_sp,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Exact dense attention (Eq. (1)) of the probe rows probe_idx [BH][M] against all N keys of the
-   original q, k, v.  o_probe: [BH][M][d] fp32. */
+   original q, k, v.  o_probe: [BH][M][d] fp32.  The workspace of this call is its own (split-K
+   partials and, for bf16, a scaled fp16 copy of v; numeric domain as sparsepr_attn_sparse), of
+   sparsepr_probe_workspace_size() bytes; it may be any buffer not in use by the other calls.
+   EWORKSPACE: ws_bytes below that size. */
 spr_status sparsepr_probe_exact(const spr_desc* desc, const void* q, const void* k, const void* v,
                                 const int32_t* probe_idx, int32_t M, float* o_probe, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sparsepr_probe_exact (host; 0 for invalid arguments). */
+size_t sparsepr_probe_workspace_size(const spr_desc* desc, int32_t M);
 
 /* Weighted ridge fit of the probe residuals against the sparse outputs and correction of the
    unprobed rows (Sec. 4.2, App. A.3, App. D.3): alpha = w / sum w; W = diag(M w / sum w);
@@ -280,10 +291,15 @@ spr_status sparsepr_fit_correct(const spr_desc* desc, const spr_part_params* par
                                 const spr_fit_options* opts, void* out, int32_t out_dtype, double* fit_state,
                                 int32_t* head_status, void* ws, size_t ws_bytes, void* stream);
 
-/* Baseline: dense flash attention softmax(q k^T / sqrt d) v for every row, same kernel family as
-   sparsepr_attn_sparse.  out: [B][H][N][d] contiguous, fp32 or bf16 (out_dtype). */
+/* Baseline: dense flash attention softmax(q k^T / sqrt d) v for every row, same kernel as
+   sparsepr_attn_sparse.  out: [B][H][N][d] contiguous, fp32 or bf16 (out_dtype).  ws: scratch of
+   sparsepr_dense_workspace_size() bytes (the scaled fp16 copy of v for bf16 inputs).
+   EWORKSPACE: ws_bytes below that size. */
 spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* k, const void* v,
-                               void* out, int32_t out_dtype, void* stream);
+                               void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sparsepr_attn_dense (host; 0 for an invalid descriptor). */
+size_t sparsepr_dense_workspace_size(const spr_desc* desc);
 
 /* Test helper: k-means of `feat` [BH][n][r] fp64 (r in {8, 16, 32, 48, 64, 128},
    C <= min(n, 1024)) with the operator's initialisation (stage 0 or 1), assignment, update and

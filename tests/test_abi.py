@@ -87,8 +87,15 @@ def test_entry_points_reject_invalid_arguments_on_the_host(lib):
     assert lib.sparsepr_partition(ctypes.byref(d), dummy, dummy, dummy, ctypes.byref(p), ctypes.byref(warm),
                                   ctypes.byref(full), dummy, 1 << 40, None) == 1
     # unsupported head dimension
-    assert lib.sparsepr_attn_dense(ctypes.byref(_desc(d=80)), dummy, dummy, dummy, dummy, 0, None) == 2
-    assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 5, None) == 2
+    assert lib.sparsepr_attn_dense(ctypes.byref(_desc(d=80)), dummy, dummy, dummy, dummy, 0, dummy, 1 << 40,
+                                   None) == 2
+    assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 5, dummy, 1 << 40, None) == 2
+    # dense workspace: null, then too small for the fp16 copy of v
+    assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, None, 1 << 40, None) == 1
+    need = lib.sparsepr_dense_workspace_size(ctypes.byref(d))
+    assert need >= d.B * d.H * d.N * d.d * 2
+    assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, dummy, need - 1, None) == 3
+    assert lib.sparsepr_probe_workspace_size(ctypes.byref(d), 64) >= need
     # probes: M must lie in [1, Nv)
     assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, dummy, dummy, 1 << 40, None) == 1
     assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 4096, dummy, dummy, 1 << 40,

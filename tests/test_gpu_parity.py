@@ -497,7 +497,10 @@ def test_gqa_warm_start():
                 _compare_head(g, ref, hd, cfg.Nv, cfg.N, cfg.n_text, kh=j)
             else:
                 _lockstep_head(g, q1, k1, v1, cfg, opc, 0, hd, np.random.default_rng(hd))
-    assert np.all(g["passes"] <= op.warm_iters)
+    # passes[j][0] holds the K/V passes of K/V head j (rows past B * Hkv are not written),
+    # passes[hd][1] the query passes of query head hd
+    BHkv = cfg.B * cfg.Hkv
+    assert np.all(g["passes"][:BHkv, 0] <= op.warm_iters) and np.all(g["passes"][:, 1] <= op.warm_iters)
 
 
 # ------------------------------------------------------------------ probe and estimator variants

@@ -223,6 +223,56 @@ def test_key_budget_reserves_probes():
     assert T == math.ceil((rho * N * N - nt * N - M * N - Nv * nt) / Nv)
 
 
+@pytest.mark.parametrize("n_text,rho,M", [(0, 0.22, 8), (8, 0.22, 8), (24, 0.5, 16), (16, 0.35, 4)])
+def test_executed_pairs_from_an_explicit_mask(n_text, rho, M):
+    """rho_exec of Sec. 4.3 (App. B.3: rho_exec = rho_route + M / N_q) counted cell by cell.  The
+    executed cells of one head are drawn as N x N boolean masks from the routing alone: every video
+    row against the keys of the groups its query group selected and against every text key, every
+    text row against every key; the probe rows' exact rows are a second mask, counted on top
+    (their routed cells run as well, since their sparse rows feed the fit).  The count must equal
+    the oracle's pair total and density, and the common per-row budget must land the density in
+    [rho*, rho* + (max|G_b| + 1) Nv / N^2): every row reaches ceil(T) keys, and the shortest
+    prefix overshoots by less than its last group."""
+    grid = (2, 8, 8)
+    Nv = int(np.prod(grid))
+    N = Nv + n_text
+    rng = _rng(31, n_text, M)
+    d = 16
+    q = rng.standard_normal((N, d)) * 0.6
+    k = q + 0.5 * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    p = O.Params(Ck=12, Cq=9, rK=8, rQ=8, Ms=N, max_iters=25, tol=1e-4, seed=3, M=M, rho=rho, lam=1.0,
+                 n_text=n_text)
+    st = O.sparsepr_head(q, k, v, p, head=0, full=False)
+    kv_lab, q_lab = st["kv_label"], st["q_label"]
+    routed = np.zeros((N, N), dtype=bool)
+    for i in range(Nv):
+        chosen = np.isin(kv_lab, st["sel"][q_lab[i]])
+        routed[i, :Nv] = chosen
+        routed[i, Nv:] = True                      # text keys: always selected
+    routed[Nv:, :] = True                          # text query rows: dense
+    probe = np.zeros((N, N), dtype=bool)
+    probe[st["probes"], :] = True
+    assert len(np.unique(st["probes"])) == M and st["probes"].max() < Nv
+    # the oracle's pair total counts the video rows of the routed mask
+    assert int(routed[:Nv].sum()) == st["pairs"]
+    cells = int(routed.sum()) + int(probe.sum())
+    assert st["rho_exec"] == pytest.approx(cells / N ** 2, rel=0, abs=1e-15)
+    # the per-row budget: every video row reaches ceil(T) keys (video plus text) unless every group
+    # is taken, and the prefix stops at the first group that reaches it
+    T = st["T"]
+    assert T >= 1  # a reachable target (below the fixed text and probe cost the call is rejected)
+    size = np.bincount(kv_lab, minlength=st["n_kv"])
+    for a in range(st["n_q"]):
+        got = int(size[st["sel"][a]].sum())
+        if len(st["sel"][a]) < st["n_kv"]:
+            assert got >= T
+        assert got - int(size[st["sel"][a][-1]]) < T or len(st["sel"][a]) == 1
+    assert T >= (rho * N * N - n_text * N - M * N - Nv * n_text) / Nv
+    if all(len(s) < st["n_kv"] for s in st["sel"]):
+        assert rho <= st["rho_exec"] < rho + (size.max() + 1) * Nv / N ** 2
+
+
 # ---------------------------------------------------------------- routing score
 def test_route_score_special_cases():
     d = 4
