@@ -267,9 +267,12 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 #define SPR_LDS __attribute__((address_space(3)))
 
 // 16 bytes per lane from a buffer resource straight into LDS: lane l writes lds + 16 l
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, char* lds, int voffset) {
+// (the LDS destination is given as a byte offset into the kernel's dynamic LDS)
+extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rsrc, int lds_off, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SPR_LDS void*)lds, 16, voffset, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (SPR_LDS void*)((SPR_LDS char*)smem_raw + lds_off), 16, voffset, 0,
+                                           0, 0);
 #endif
 }
 
@@ -306,7 +309,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using S = Attn32Shape<D>;
   constexpr bool SPARSE = MODE == MODE_SPARSE;
   constexpr int KC = S::KC, NT = S::NT, KS = S::KS, VROW = D * 2;
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   char* Kl = smem_raw;                                               // [2][KBUF]
   char* Vl = smem_raw + 2 * S::KBUF;                                 // [2][VBUF]
   float* kbias = reinterpret_cast<float*>(Vl + 2 * S::VBUF);         // [kRing][2][64]
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     else return min(t.key0 + ch * KC + r, klast);
   };
   auto kload = [&](int ch, int buf, int j, int slot) __attribute__((always_inline)) {
-    lds_load16(krsrc, Kl + buf * S::KBUF + j * 1024, key_row(ch, slot & 255) * krow_bytes + (slot >> 8));
+    lds_load16(krsrc, buf * S::KBUF + j * 1024, key_row(ch, slot & 255) * krow_bytes + (slot >> 8));
   };
   auto issue_k = [&](int ch, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < VQ; ++i) {
       const int j = 4 * i + w;
-      lds_load16(vrsrc, Vl + buf * S::VBUF + j * 1024, key_row(ch, VRPL * j + vrow_l) * VROW + vcol);
+      lds_load16(vrsrc, 2 * S::KBUF + buf * S::VBUF + j * 1024, key_row(ch, VRPL * j + vrow_l) * VROW + vcol);
     }
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
