@@ -968,8 +968,12 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
   const int n_text_tiles = (n_text + H2 - 1) / H2;
   int s = 0;
   if (t < nq) s = qo[t + 1] - qo[t];
-  const bool big = t < nq && s > kHalfRows, small = t < nq && !big;
-  const int my_big_tiles = big ? (s + H2 - 1) / H2 : 0;
+  // A group of more than one tile whose last tile would hold at most a half's rows keeps only its
+  // full tiles and offers the rest, like a group of at most a half's rows, for pairing.
+  const bool big = t < nq && s > kHalfRows;
+  const bool rest = big && s > H2 && (s % H2) != 0 && (s % H2) <= kHalfRows;
+  const bool small = t < nq && (!big || rest);
+  const int my_big_tiles = big ? (rest ? s / H2 : (s + H2 - 1) / H2) : 0;
   int n_big_tiles, n_small;
   const int big_off = block_exscan_i(my_big_tiles, buf, &n_big_tiles);
   const int small_rank = block_exscan_i(small ? 1 : 0, buf, &n_small);
@@ -992,6 +996,15 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
       put(n_text_tiles + big_off + k, 1, t, r + kHalfRows, max(0, n - kHalfRows));
     }
   }
+  // rows offered for pairing by group a: the whole group, or the rows past its full tiles
+  auto item_row = [&](int a) {
+    const int n = qo[a + 1] - qo[a];
+    return n > kHalfRows ? qo[a] + (n / H2) * H2 : qo[a];
+  };
+  auto item_n = [&](int a) {
+    const int n = qo[a + 1] - qo[a];
+    return n > kHalfRows ? n % H2 : n;
+  };
   // small groups by rank; partner[i] = rank of the paired group, -1 while unpaired
   if (small) small_id[small_rank] = t;
   if (t < n_small) partner[t] = -1;
@@ -1056,14 +1069,14 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
   const int base = n_text_tiles + n_big_tiles;
   if (lead) {
     const int a = small_id[t], c = small_id[partner[t]];
-    put(base + pair_rank, 0, a, qo[a], qo[a + 1] - qo[a]);
-    put(base + pair_rank, 1, c, qo[c], qo[c + 1] - qo[c]);
+    put(base + pair_rank, 0, a, item_row(a), item_n(a));
+    put(base + pair_rank, 1, c, item_row(c), item_n(c));
   }
   if (loose) {
     const int a = small_id[t];
     const int tile = base + n_pairs + loose_rank / 2;
-    put(tile, loose_rank & 1, a, qo[a], qo[a + 1] - qo[a]);
-    if ((loose_rank & 1) == 0 && loose_rank == n_loose - 1) put(tile, 1, a, qo[a], 0);  // no partner
+    put(tile, loose_rank & 1, a, item_row(a), item_n(a));
+    if ((loose_rank & 1) == 0 && loose_rank == n_loose - 1) put(tile, 1, a, item_row(a), 0);  // no partner
   }
   if (t == 0) ntiles[hd] = min(tmax, base + n_pairs + (n_loose + 1) / 2);
 }
