@@ -2,9 +2,10 @@
 
 A step is one whole call (partition -> route -> block-sparse attention -> exact probes ->
 fit + correct + restore) over one batch of seeded synthetic Q/K/V already resident in
-HBM.  Prints one JSON line.  Default workload: the mid-size video DiT call (B=1, H=40,
-N=32760 tokens on a 21x39x40 grid, d=128, bf16, 512 K/V and 512 query groups, 256
-probes, 22% executed-pair density).
+HBM.  Prints one JSON line.  Default workload: the long video DiT call (B=1, H=24,
+N=118800 tokens on a 33x60x60 grid, d=128, bf16, 1024 K/V and 1024 query groups, 512
+probes, 22% executed-pair density), the largest of the 22% workloads; the mid-size call
+(H=40, N=32760) is measured after it and reported under "secondary".
 
 The headline regime (--regime warm, the default) is the steady state of App. C.1: each
 timed call is a later call that starts from the previous call's centroids and factors, on
@@ -28,17 +29,18 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "attn_sparse_mid_counters.txt")
 ATTN_SOURCE = os.path.join(ROOT, "free_block_sparse_sampled_amd", "csrc", "attention.hip")
 
 
 def measured_traffic(cfg_name):
-    """HBM-side bytes per sparse-attention launch from the committed FETCH_SIZE / WRITE_SIZE summary,
-    or None when that summary is for another workload or another version of the kernel source."""
+    """HBM-side bytes per sparse-attention launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    of this workload, or None when there is none or it was taken on another version of the kernel
+    source."""
     import hashlib
-    if cfg_name != "mid" or not os.path.exists(COUNTERS):
+    counters = os.path.join(ROOT, "profiles", f"attn_sparse_{cfg_name}_counters.txt")
+    if not os.path.exists(counters):
         return None
-    text = open(COUNTERS).read()
+    text = open(counters).read()
     sha = re.search(r"attention\.hip sha1 ([0-9a-f]{40})", text)
     val = re.search(r"sparse attention traffic per launch: ([0-9.e+]+) bytes", text)
     if not sha or not val:
@@ -53,7 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="mid")
+    ap.add_argument("--config", default="long")
+    ap.add_argument("--secondary", default="mid", help="second workload measured after the headline one ('none': skip)")
     ap.add_argument("--rho", type=float, default=None)
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--max-iters", type=int, default=None)
@@ -89,10 +92,33 @@ def affine_fit_energy(X: np.ndarray, D: np.ndarray, tol: float = 1e-10):
     return float((R ** 2).sum()), float(((Rc - Uk @ (Uk.T @ Rc)) ** 2).sum())
 
 
-def cpu_baseline(cfg, opc):
-    """The oracle, untuned, on head 0 of the workload: partition, routing and probes in full,
-    the sparse attention of 64 evenly spaced rows, the exact probe rows and the fit; scaled to
-    a whole call (every head, every attention row) and reported in the metric's unit."""
+def cpu_info():
+    """(CPU model name, number of CPUs this process may run on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        nproc = os.cpu_count()
+    return model, nproc
+
+
+def cpu_baseline(cfg, opc, warm, warm_iters, step):
+    """The oracle, untuned, on head 0 of the workload in the headline's regime: partition, routing
+    and probes in full, the sparse attention of 64 evenly spaced video rows, the exact probe rows
+    and the fit, on the inputs of ``step``; scaled to a whole call (every head, every attention
+    row) and reported in the metric's unit.  A later call (``warm``) starts from the oracle's own
+    previous call on the other step's inputs, made with the same iteration limit and not timed.
+
+    Beside the timing, the oracle's error against dense attention on the sampled rows that are
+    not probes (corrected and sparse-only), which the GPU's error on the same rows is set against."""
     import oracle as O
     from workloads import head_inputs
     try:
@@ -100,16 +126,26 @@ def cpu_baseline(cfg, opc):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
-    q, k, v = head_inputs(cfg, 0, 0)
-    p = O.Params(Ck=opc.Ck, Cq=opc.Cq, rK=opc.rK, rQ=opc.rQ, Ms=opc.Ms, max_iters=opc.max_iters, tol=opc.tol,
-                 seed=opc.seed, M=opc.M, rho=opc.rho, lam=opc.lam, n_text=cfg.n_text)
+    model, nproc = cpu_info()
+    p = O.Params(Ck=opc.Ck, Cq=opc.Cq, rK=opc.rK, rQ=opc.rQ, Ms=opc.Ms,
+                 max_iters=warm_iters if warm else opc.max_iters, tol=opc.tol, seed=opc.seed, M=opc.M,
+                 rho=opc.rho, lam=opc.lam, n_text=cfg.n_text)
+    prev = None
+    t_setup = 0.0
+    if warm:
+        t0 = time.perf_counter()
+        qp, kp, vp = head_inputs(cfg, 0, 0, 1 - step)
+        prev = O.sparsepr_head(qp, kp, vp, p, head=0, full=False)["state"]
+        t_setup = time.perf_counter() - t0
+        del qp, kp, vp
+    q, k, v = head_inputs(cfg, 0, 0, step)
     t0 = time.perf_counter()
-    st = O.sparsepr_head(q, k, v, p, head=0, full=False)
+    st = O.sparsepr_head(q, k, v, p, head=0, full=False, warm=prev)
     t_part = time.perf_counter() - t0
     rows = np.linspace(0, cfg.Nv - 1, 64).astype(np.int64)
     qlab = np.concatenate([st["q_label"], np.full(cfg.n_text, -1)])
     t0 = time.perf_counter()
-    O.sparse_attention_rows(q, k, v, rows, qlab, st["kv_label"], st["sel"], cfg.n_text)
+    osp_rows = O.sparse_attention_rows(q, k, v, rows, qlab, st["kv_label"], st["sel"], cfg.n_text)
     t_rows = time.perf_counter() - t0
     t0 = time.perf_counter()
     X = O.sparse_attention_rows(q, k, v, st["probes"], qlab, st["kv_label"], st["sel"], cfg.n_text)
@@ -121,26 +157,36 @@ def cpu_baseline(cfg, opc):
     per_head = t_part + t_rows * (cfg.N / len(rows)) + t_fit
     ms_call = per_head * cfg.heads * 1e3
     dense_flops = 4.0 * cfg.heads * cfg.N * cfg.N * cfg.d
+    # method error of the oracle on the sampled rows that are not probes
+    keep = ~np.isin(rows, st["probes"])
+    od_rows = O.dense_attention_rows(q, k, v, rows[keep])
+    e_corr = O.relative_error(O.correct(osp_rows[keep], fit), od_rows)
+    e_sp = O.relative_error(osp_rows[keep], od_rows)
+    regime = (f"later call (warm start from the oracle's previous call, {warm_iters} k-means iterations)"
+              if warm else f"cold call (up to {opc.max_iters} k-means iterations)")
     return {"value": dense_flops / (ms_call * 1e-3) / 1e12, "unit": "TFLOP/s (dense-equivalent attention, whole call)",
-            "ms_per_call": ms_call, "cores": int(cores), "kind": "oracle",
-            "sample": (f"head 0 of {cfg.heads}: partition, routing and probes in full, sparse attention of "
-                       f"{len(rows)} of {cfg.N} rows, probe rows and fit ({sample:.1f} s of CPU); scaled by "
-                       f"rows and heads to one call (extrapolated)"),
-            "sample_seconds": round(sample, 2)}
+            "ms_per_call": ms_call, "cores": int(cores), "nproc": nproc, "cpu_model": model, "kind": "oracle",
+            "regime": regime,
+            "sample": (f"head 0 of {cfg.heads}, {regime}: partition, routing and probes in full, sparse attention "
+                       f"of {len(rows)} of {cfg.N} rows, probe rows and fit ({sample:.1f} s of CPU, plus "
+                       f"{t_setup:.1f} s untimed for the previous call); scaled by rows and heads to one call "
+                       f"(extrapolated)"),
+            "sample_seconds": round(sample, 2),
+            "_rows": rows[keep],
+            "oracle_err_vs_dense": {"head": 0, "rows": int(keep.sum()),
+                                    "corrected_mean": round(float(e_corr.mean()), 5),
+                                    "sparse_only_mean": round(float(e_sp.mean()), 5)}}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (the operator shards by head with no communication); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
+def measure(args, name, headline):
+    """Time the operator on workload ``name``; the full record for the headline workload, a
+    compact one for the secondary workload."""
     import torch
 
     import free_block_sparse_sampled_amd as spr
     from workloads import batch_inputs, config
 
-    cfg = config(args.config)
+    cfg = config(name)
     if args.rho is not None:
         cfg = cfg.with_(rho=args.rho)
     if args.M is not None:
@@ -161,7 +207,7 @@ def main():
         del q, k, v
     op = spr.SparsePR(inputs[0][0], opc, n_text=cfg.n_text)
     stream = torch.cuda.current_stream()
-    if args.calib_copy_mb:
+    if headline and args.calib_copy_mb:
         src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -200,57 +246,66 @@ def main():
     warm_regime = args.regime == "warm"
     # the other regime first (a short measurement reported beside the headline one)
     other = None
-    if not args.no_other:
+    if headline and not args.no_other:
         per_o, total_o, _ = timed(not warm_regime, max(2, args.steps // 3), 1)
         other = {"ms_per_call": round(float(np.median(total_o)), 4),
                  "stages_ms": {n: round(float(np.median(per_o[:, i])), 4) for i, n in enumerate(names)}}
-    per, total, wall = timed(warm_regime, args.steps, max(args.warmup, 1))
+    steps = args.steps if headline else max(3, args.steps // 2)
+    per, total, wall = timed(warm_regime, steps, max(args.warmup, 1))
     ms_call = float(np.median(total))
-    tq, tk, tv = inputs[(call[0] - 1) % 2]  # inputs of the last timed call (op holds its results)
+    last_step = (call[0] - 1) % 2
+    tq, tk, tv = inputs[last_step]  # inputs of the last timed call (op holds its results)
 
     pairs = op.route.pairs.double().sum().item()
     rho_exec = op.route.rho_exec.mean().item()
-    passes = None
     BH, N, d = cfg.heads, cfg.N, cfg.d
     dense_flops = 4.0 * BH * N * N * d
     exec_flops = 4.0 * d * (pairs + BH * cfg.M * N + BH * cfg.n_text * N)
     t_attn = float(np.median(per[:, 2]))
     t_probe = float(np.median(per[:, 3]))
     sparse_tflops = 4.0 * d * pairs / (t_attn * 1e-3) / 1e12
+    workload = (f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} grid={'x'.join(map(str, cfg.grid))} "
+                f"d={cfg.d} {cfg.dtype} n_text={cfg.n_text}")
+    stages = {n: round(float(np.median(per[:, i])), 4) for i, n in enumerate(names)}
+    if headline:
+        result = {
+            "metric": "ms/call & dense-equiv TFLOP/s at 22% density; rel-L2 err vs dense",
+            "value": round(dense_flops / (ms_call * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s (dense-equivalent attention, whole call)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_call, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+            "data": "synthetic (seeded positional-Fourier Q/K + noise + sinks, Gaussian V)",
+            "config": {"workload": workload,
+                       "Ck": cfg.Ck, "Cq": cfg.Cq, "M": cfg.M, "rho_target": cfg.rho, "max_iters": cfg.max_iters,
+                       "probes": args.probe_mode, "fit_family": args.fit_family, "out_rank": args.out_rank,
+                       "partition": args.partition_mode,
+                       "parallelism": "single GPU, heads batched"},
+            "ms_per_call": round(ms_call, 4),
+            "regime": ("later calls of App. C.1 (warm start: k-means from the previous centroids, 2 "
+                       "iterations; factors by 2 subspace iterations), inputs alternating between two "
+                       "fresh-noise steps" if warm_regime else
+                       "cold calls (k-means from sampled centres, up to 25 iterations; eigendecomposition)"),
+            "stages_ms": stages,
+            ("cold" if warm_regime else "warm"): other,
+            "rho_exec": round(rho_exec, 5),
+            "executed_pair_mfma_frac": round(exec_flops / ((t_attn + t_probe) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "wall_ms_per_step": round(wall / steps * 1e3, 3),
+            "roofline": {"kernel": "attn32_kernel<128, sparse> (sparsepr_attn_sparse)", "bound": "mfma",
+                         "achieved": round(sparse_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
+                         "work": "4*d flops per routed query-key pair, pairs summed over heads"},
+        }
+        status = op.head_status.cpu().numpy()
+        result["head_status_bits"] = int(np.bitwise_or.reduce(status))
+    else:
+        result = {"workload": workload, "ms_per_call": round(ms_call, 4),
+                  "value": round(dense_flops / (ms_call * 1e-3) / 1e12, 3), "stages_ms": stages,
+                  "rho_exec": round(rho_exec, 5), "attn_sparse_tflops": round(sparse_tflops, 2),
+                  "attn_sparse_frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4)}
 
-    result = {
-        "metric": "ms/call & dense-equiv TFLOP/s at 22% density; rel-L2 err vs dense",
-        "value": round(dense_flops / (ms_call * 1e-3) / 1e12, 3),
-        "unit": "TFLOP/s (dense-equivalent attention, whole call)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_call, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded positional-Fourier Q/K + noise + sinks, Gaussian V)",
-        "config": {"workload": (f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} grid={'x'.join(map(str, cfg.grid))} "
-                                f"d={cfg.d} {cfg.dtype} n_text={cfg.n_text}"),
-                   "Ck": cfg.Ck, "Cq": cfg.Cq, "M": cfg.M, "rho_target": cfg.rho, "max_iters": cfg.max_iters,
-                   "probes": args.probe_mode, "fit_family": args.fit_family, "out_rank": args.out_rank,
-                   "partition": args.partition_mode,
-                   "parallelism": "single GPU, heads batched"},
-        "ms_per_call": round(ms_call, 4),
-        "regime": ("later calls of App. C.1 (warm start: k-means from the previous centroids, 2 "
-                   "iterations; factors by 2 subspace iterations), inputs alternating between two "
-                   "fresh-noise steps" if warm_regime else
-                   "cold calls (k-means from sampled centres, up to 25 iterations; eigendecomposition)"),
-        "stages_ms": {n: round(float(np.median(per[:, i])), 4) for i, n in enumerate(names)},
-        ("cold" if warm_regime else "warm"): other,
-        "rho_exec": round(rho_exec, 5),
-        "executed_pair_mfma_frac": round(exec_flops / ((t_attn + t_probe) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "wall_ms_per_step": round(wall / args.steps * 1e3, 3),
-        "roofline": {"kernel": "attn_mfma_kernel<128, sparse> (sparsepr_attn_sparse)", "bound": "mfma",
-                     "achieved": round(sparse_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(sparse_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(cfg.name),
-                     "work": "4*d flops per routed query-key pair, pairs summed over heads"},
-    }
-    status = op.head_status.cpu().numpy()
-    result["head_status_bits"] = int(np.bitwise_or.reduce(status))
-
+    err_rows0 = None
     if not args.no_dense:
         dense_out = torch.empty((cfg.B, cfg.H, N, d), dtype=torch.float32, device="cuda")
         desc = spr.make_desc(tq)
@@ -280,33 +335,60 @@ def main():
         e = err[mask]
         osp = torch.empty_like(o)
         osp.scatter_(1, op.part.q_perm.long()[..., None].expand(-1, -1, d), op.o_sp[:, : cfg.Nv])
-        esp = ((osp - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8))[mask]
-        ph = (err * mask).sum(1) / mask.sum(1)
-        phs = (((osp - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8)) * mask).sum(1) / mask.sum(1)
-        result["err_vs_dense_per_head"] = {
-            "corrected_mean_min_med_max": [round(x, 4) for x in torch.quantile(ph, torch.tensor(
-                [0.0, 0.5, 1.0], device=ph.device, dtype=ph.dtype)).tolist()],
-            "sparse_only_mean_min_med_max": [round(x, 4) for x in torch.quantile(phs, torch.tensor(
-                [0.0, 0.5, 1.0], device=phs.device, dtype=phs.dtype)).tolist()],
-            "heads_worsened_by_correction": int((ph > phs).sum().item())}
-        result["err_vs_dense"] = {"corrected_mean": round(e.mean().item(), 5),
-                                  "corrected_p99": round(torch.quantile(e.float()[:1 << 24], 0.99).item(), 5),
-                                  "sparse_only_mean": round(esp.mean().item(), 5),
-                                  "sparse_only_p99": round(torch.quantile(esp.float()[:1 << 24], 0.99).item(), 5),
-                                  "rows": "all unprobed video rows, dense reference = sparsepr_attn_dense"}
-        # affine representability of the residual (App. D.5) on 2048 evenly spaced video rows of
-        # every head, energies summed over heads before the fraction is formed
-        m = min(2048, cfg.Nv)
-        rows = (torch.arange(m, device=o.device) * cfg.Nv) // m
-        Xs = osp[:, rows].double().cpu().numpy()
-        Ds = dref[:, rows].double().cpu().numpy()
-        tot = [affine_fit_energy(Xs[h], Ds[h]) for h in range(BH)]
-        energy = sum(t[0] for t in tot)
-        left = sum(t[1] for t in tot)
-        result["affine_representability"] = {"rows_per_head": m, "residual_energy": energy, "remaining_energy": left,
-                                             "explained_fraction": round(1.0 - left / energy, 5)}
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, opc)
+        err_sp = (osp - dref).norm(dim=-1) / (dref.norm(dim=-1) + 1e-8)
+        esp = err_sp[mask]
+        err_rows0 = (err[0].cpu().numpy(), err_sp[0].cpu().numpy())
+        if not headline:
+            result["err_vs_dense"] = {"corrected_mean": round(e.mean().item(), 5),
+                                      "sparse_only_mean": round(esp.mean().item(), 5)}
+        else:
+            ph = (err * mask).sum(1) / mask.sum(1)
+            phs = (err_sp * mask).sum(1) / mask.sum(1)
+            qs = torch.tensor([0.0, 0.5, 1.0], device=ph.device, dtype=ph.dtype)
+            result["err_vs_dense_per_head"] = {
+                "corrected_mean_min_med_max": [round(x, 4) for x in torch.quantile(ph, qs).tolist()],
+                "sparse_only_mean_min_med_max": [round(x, 4) for x in torch.quantile(phs, qs).tolist()],
+                "heads_worsened_by_correction": int((ph > phs).sum().item())}
+            result["err_vs_dense"] = {"corrected_mean": round(e.mean().item(), 5),
+                                      "corrected_p99": round(torch.quantile(e.float()[:1 << 24], 0.99).item(), 5),
+                                      "sparse_only_mean": round(esp.mean().item(), 5),
+                                      "sparse_only_p99": round(torch.quantile(esp.float()[:1 << 24], 0.99).item(), 5),
+                                      "rows": "all unprobed video rows, dense reference = sparsepr_attn_dense"}
+            # affine representability of the residual (App. D.5) on 2048 evenly spaced video rows of
+            # every head, energies summed over heads before the fraction is formed
+            m = min(2048, cfg.Nv)
+            rows = (torch.arange(m, device=o.device) * cfg.Nv) // m
+            Xs = osp[:, rows].double().cpu().numpy()
+            Ds = dref[:, rows].double().cpu().numpy()
+            tot = [affine_fit_energy(Xs[h], Ds[h]) for h in range(BH)]
+            energy = sum(t_[0] for t_ in tot)
+            left = sum(t_[1] for t_ in tot)
+            result["affine_representability"] = {"rows_per_head": m, "residual_energy": energy,
+                                                 "remaining_energy": left,
+                                                 "explained_fraction": round(1.0 - left / energy, 5)}
+        del dense_out, o, dref, osp, err, err_sp
+    if headline and not args.no_cpu:
+        cb = cpu_baseline(cfg, opc, warm_regime, op.warm_iters, last_step)
+        rows = cb.pop("_rows")
+        if err_rows0 is not None:
+            # the GPU's error on the oracle's sample rows of head 0, beside the oracle's own
+            cb["oracle_err_vs_dense"]["gpu_corrected_mean"] = round(float(err_rows0[0][rows].mean()), 5)
+            cb["oracle_err_vs_dense"]["gpu_sparse_only_mean"] = round(float(err_rows0[1][rows].mean()), 5)
+        result["cpu_baseline"] = cb
+    del op, inputs
+    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the operator shards by head with no communication); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    result = measure(args, args.config, True)
+    if args.secondary not in ("none", "", args.config):
+        result["secondary"] = measure(args, args.secondary, False)
     print(json.dumps(result))
 
 
