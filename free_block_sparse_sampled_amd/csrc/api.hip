@@ -136,6 +136,7 @@ const char* sparsepr_status_string(spr_status s) {
     case SPR_EUNSUPPORTED: return "unsupported head dimension, rank or dtype";
     case SPR_EWORKSPACE: return "workspace too small";
     case SPR_EHIP: return "HIP launch failed";
+    case SPR_ETOOLARGE: return "problem exceeds the fixed scratch of the allocation-free call";
   }
   return "unknown status";
 }
@@ -269,6 +270,19 @@ spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* 
   if (!ws || !aligned16(ws)) return SPR_EINVAL;
   if (ws_bytes < v_copy_bytes(*desc)) return SPR_EWORKSPACE;
   return run_attn_dense(*desc, q, k, v, out, out_dtype, ws, static_cast<hipStream_t>(stream));
+}
+
+spr_status sparsepr_attn_dense_noalloc(const spr_desc* desc, const void* q, const void* k, const void* v, void* out,
+                                       int32_t out_dtype, void* stream) {
+  spr_status s = check_desc(desc);
+  if (s != SPR_OK) return s;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v)) return SPR_EINVAL;
+  if (out_dtype != SPR_BF16 && out_dtype != SPR_F32) return SPR_EUNSUPPORTED;
+  if (!head_fits_32bit(desc)) return SPR_EUNSUPPORTED;
+  if (v_copy_bytes(*desc) > kNoallocScratchBytes) return SPR_ETOOLARGE;
+  void* scratch = nullptr;
+  if ((s = noalloc_scratch(&scratch)) != SPR_OK) return s;
+  return run_attn_dense(*desc, q, k, v, out, out_dtype, scratch, static_cast<hipStream_t>(stream));
 }
 
 size_t sparsepr_kmeans_workspace_size(int32_t BH, int32_t n, int32_t r, int32_t C) {

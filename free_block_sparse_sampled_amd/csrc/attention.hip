@@ -15,6 +15,7 @@
 // V scaled by a power of two per K/V head (the scale is undone on the output).  Computing the
 // transposes puts a query row's scores and its output columns in one lane.  fp32 inputs use a
 // plain VALU kernel.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1202,6 +1203,30 @@ spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, co
   }
   const int rows = desc.dtype == SPR_BF16 ? kAttnRows : kTileRows;
   return dispatch_d<MODE_DENSE>(P, dim3(ceil_div(desc.N, rows), desc.B * desc.H), desc.d, desc.dtype, st);
+}
+
+// ------------------------------------------------------------------ allocation-free dense call
+// Scratch of sparsepr_attn_dense_noalloc: a fixed array in device memory that every call on a
+// device shares (the scaled fp16 copy of V and its per-head statistics).  Host code never uses the
+// array's name as an address: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+spr_status noalloc_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPR_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPR_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SPR_OK;
 }
 
 }  // namespace spr

@@ -72,6 +72,10 @@ spr_status launch_eigen_factor(const double* Mall, int BH, int d, int r, double 
                                hipStream_t st);
 spr_status run_attn_dense(const spr_desc& desc, const void* q, const void* k, const void* v, void* out,
                           int out_dtype, void* ws, hipStream_t st);
+// device address of the fixed scratch of the allocation-free dense call on the current device
+constexpr size_t kNoallocScratchBytes = SPR_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+spr_status noalloc_scratch(void** ptr);
 // Power-of-two scaling of bf16 values into fp16 (attention.hip): the largest |v| of every K/V head
 // of v (geometry gk) into amax, then scale[hk] = 2^e and scale[heads + hk] = 2^-e.
 void launch_v_scale(const void* v, const HeadGeom& gk, int heads, unsigned* amax, float* scale, hipStream_t st);

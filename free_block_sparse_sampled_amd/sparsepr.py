@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparsepr.so")
 
 SPR_BF16, SPR_F32 = 0, 1
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP launch failed"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP launch failed",
+          5: "problem exceeds the fixed scratch of the allocation-free call"}
 HS_BITS = {1: "cholesky_fallback", 2: "budget_unreached", 4: "kv_groups_empty", 8: "q_groups_empty", 16: "rms_floor",
            32: "eigen_noconv"}
 
@@ -116,6 +117,8 @@ def library():
         lib.sparsepr_attn_dense.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
                                             P]
         lib.sparsepr_attn_dense.restype = st
+        lib.sparsepr_attn_dense_noalloc.argtypes = [ctypes.POINTER(spr_desc), P, P, P, P, ctypes.c_int32, P]
+        lib.sparsepr_attn_dense_noalloc.restype = st
         lib.sparsepr_dense_workspace_size.argtypes = [ctypes.POINTER(spr_desc)]
         lib.sparsepr_dense_workspace_size.restype = ctypes.c_size_t
         lib.sparsepr_probe_workspace_size.argtypes = [ctypes.POINTER(spr_desc), ctypes.c_int32]
@@ -134,8 +137,9 @@ def library():
 
 EXPORTED = ["sparsepr_workspace_size", "sparsepr_partition", "sparsepr_route", "sparsepr_attn_sparse",
             "sparsepr_probe_exact", "sparsepr_probe_workspace_size", "sparsepr_fit_correct", "sparsepr_attn_dense",
-            "sparsepr_dense_workspace_size", "sparsepr_kmeans", "sparsepr_kmeans_workspace_size",
-            "sparsepr_status_string"]
+            "sparsepr_dense_workspace_size", "sparsepr_attn_dense_noalloc", "sparsepr_kmeans",
+            "sparsepr_kmeans_workspace_size", "sparsepr_status_string"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SPR_NOALLOC_SCRATCH_BYTES
 
 
 def _check(status: int, what: str):
@@ -353,6 +357,13 @@ def sparsepr_attn_dense(desc, q, k, v, out, ws: Optional[torch.Tensor] = None, s
         ws = dense_workspace(desc, q.device)
     _check(library().sparsepr_attn_dense(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dt,
                                          _ptr(ws), ws.numel(), _stream(stream)), "sparsepr_attn_dense")
+
+
+def sparsepr_attn_dense_noalloc(desc, q, k, v, out, stream=None):
+    """sparsepr_attn_dense on the library's fixed device scratch: no allocation anywhere in the call."""
+    out_dt = SPR_BF16 if out.dtype == torch.bfloat16 else SPR_F32
+    _check(library().sparsepr_attn_dense_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), out_dt,
+                                                 _stream(stream)), "sparsepr_attn_dense_noalloc")
 
 
 def sparsepr_kmeans(feat: torch.Tensor, C: int, seed: int, stage: int, max_iters: int, tol: float, stream=None):

@@ -40,6 +40,8 @@
  *                        within a head)
  *      SPR_EWORKSPACE    workspace smaller than sparsepr_workspace_size()
  *      SPR_EHIP          a HIP launch failed (the stream state is undefined)
+ *      SPR_ETOOLARGE     the problem needs more scratch than the fixed array of
+ *                        the allocation-free call holds
  *    Anomalies that depend on the data are reported per head in the device
  *    array `head_status` of sparsepr_fit_correct (SPR_HS_* bits).
  *  - The workspace `ws` is scratch owned by the caller; the same workspace
@@ -62,7 +64,8 @@ typedef enum {
   SPR_EINVAL = 1,
   SPR_EUNSUPPORTED = 2,
   SPR_EWORKSPACE = 3,
-  SPR_EHIP = 4
+  SPR_EHIP = 4,
+  SPR_ETOOLARGE = 5
 } spr_status;
 
 typedef enum { SPR_BF16 = 0, SPR_F32 = 1 } spr_dtype;
@@ -300,6 +303,20 @@ spr_status sparsepr_attn_dense(const spr_desc* desc, const void* q, const void* 
 
 /* Workspace bytes of sparsepr_attn_dense (host; 0 for an invalid descriptor). */
 size_t sparsepr_dense_workspace_size(const spr_desc* desc);
+
+/* sparsepr_attn_dense for callers that cannot allocate device memory (work under HIP graph
+   capture, tight serving loops, harnesses that forbid allocation): same arguments, kernels and
+   result, without a workspace argument.  The scratch (the scaled fp16 copy of v for bf16 inputs)
+   is a fixed array of SPR_NOALLOC_SCRATCH_BYTES in device memory that the library holds on every
+   device it runs on until the process ends; its address is looked up once per device on the first
+   call there.  The call allocates nothing.  Every call on one device shares that array, which keeps
+   the last call's contents: calls that overlap on one device (two streams, two host threads) race
+   and must be serialised by the caller.  ETOOLARGE: sparsepr_dense_workspace_size(desc) exceeds
+   SPR_NOALLOC_SCRATCH_BYTES (for bf16, B * kv heads * N * d above about 32 Mi elements).
+   EHIP: the scratch's device address could not be obtained. */
+#define SPR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+spr_status sparsepr_attn_dense_noalloc(const spr_desc* desc, const void* q, const void* k, const void* v,
+                                       void* out, int32_t out_dtype, void* stream);
 
 /* Test helper: k-means of `feat` [BH][n][r] fp64 (r in {8, 16, 32, 48, 64, 128},
    C <= min(n, 1024)) with the operator's initialisation (stage 0 or 1), assignment, update and

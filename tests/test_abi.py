@@ -36,7 +36,8 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small")]:
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"),
+                       (5, b"problem exceeds the fixed scratch of the allocation-free call")]:
         assert lib.sparsepr_status_string(code) == text
     assert lib.sparsepr_status_string(99) == b"unknown status"
 
@@ -96,6 +97,12 @@ def test_entry_points_reject_invalid_arguments_on_the_host(lib):
     assert need >= d.B * d.H * d.N * d.d * 2
     assert lib.sparsepr_attn_dense(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, dummy, need - 1, None) == 3
     assert lib.sparsepr_probe_workspace_size(ctypes.byref(d), 64) >= need
+    # allocation-free dense call: null pointer, unknown output dtype, a v copy beyond its fixed scratch
+    assert lib.sparsepr_attn_dense_noalloc(ctypes.byref(d), None, dummy, dummy, dummy, 0, None) == 1
+    assert lib.sparsepr_attn_dense_noalloc(ctypes.byref(d), dummy, dummy, dummy, dummy, 5, None) == 2
+    huge = _desc(N=1 << 17, H=4)  # 4 heads x 131072 x 128 bf16 = 128 MiB of fp16 v
+    assert lib.sparsepr_dense_workspace_size(ctypes.byref(huge)) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.sparsepr_attn_dense_noalloc(ctypes.byref(huge), dummy, dummy, dummy, dummy, 0, None) == 5
     # probes: M must lie in [1, Nv)
     assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 0, dummy, dummy, 1 << 40, None) == 1
     assert lib.sparsepr_probe_exact(ctypes.byref(d), dummy, dummy, dummy, dummy, 4096, dummy, dummy, 1 << 40,
