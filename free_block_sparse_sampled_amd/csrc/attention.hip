@@ -425,23 +425,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int VRPL = 64 / S::PCS;  // V rows per load: 4 (D = 128) or 8 (D = 64)
   const int vrow_l = lane / S::PCS, vcol = ((lane % S::PCS) ^ S::vswz(vrow_l & 3)) * 16;
   const int klast = t.key1 - 1;
-  auto key_row = [&](int ch, int r) __attribute__((always_inline)) -> int {
-    if constexpr (SPARSE) return rowidx[(ch & (kRing - 1)) * 64 + r];
-    else return min(t.key0 + ch * KC + r, klast);
-  };
-  auto kload = [&](int ch, int buf, int j, int slot) __attribute__((always_inline)) {
-    lds_load16(krsrc, buf * S::KBUF + j * 1024, key_row(ch, slot & 255) * krow_bytes + (slot >> 8));
-  };
-  auto issue_k = [&](int ch, int buf) __attribute__((always_inline)) {
+  // Dense and probe tiles address chunk ch through resources based at its first row, key0 + 64 ch,
+  // whose range ends after row klast: every lane's offset is then the same in every chunk, and
+  // the rows past klast of the last chunk read as zero (their bias masks them).  Sparse tiles read
+  // each lane's row from the chunk's row list in LDS, all of a step's rows before its first load.
+  int kvoff[KQ + 1], vvoff[VQ];
 #pragma unroll
-    for (int i = 0; i < KQ; ++i) kload(ch, buf, 4 * i + w, kslots[i]);
-    if (w == 0) kload(ch, buf, 4 * KQ, kslot_x);
-  };
-  auto issue_v = [&](int ch, int buf) __attribute__((always_inline)) {
+  for (int i = 0; i <= KQ; ++i) {
+    const int sl = i < KQ ? kslots[i] : kslot_x;
+    kvoff[i] = SPARSE ? (sl >> 8) : (sl & 255) * krow_bytes + (sl >> 8);
+  }
 #pragma unroll
-    for (int i = 0; i < VQ; ++i) {
-      const int j = 4 * i + w;
-      lds_load16(vrsrc, 2 * S::KBUF + buf * S::VBUF + j * 1024, key_row(ch, VRPL * j + vrow_l) * VROW + vcol);
+  for (int i = 0; i < VQ; ++i) vvoff[i] = SPARSE ? vcol : (VRPL * (4 * i + w) + vrow_l) * VROW + vcol;
+  auto chunk_k = [&](int ch) __attribute__((always_inline)) {
+    const int rb = t.key0 + ch * KC;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(Kb + int64_t(rb) * (krow_bytes >> 1)), (short)0,
+                                             max(0, (klast - rb) * krow_bytes + D * 2), 0x00020000);
+  };
+  auto chunk_v = [&](int ch) __attribute__((always_inline)) {
+    const int rb = t.key0 + ch * KC;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(Vb + int64_t(rb) * D), (short)0, max(0, (klast + 1 - rb) * VROW),
+                                             0x00020000);
+  };
+  // K of chunk kc into buffer kb, and with with_v V of chunk vc into buffer vb
+  auto issue = [&](int kc, int kb, int vc, int vb, bool with_v) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      const int* kr = rowidx + (kc & (kRing - 1)) * 64;
+      const int* vr = rowidx + (vc & (kRing - 1)) * 64;
+      int krow[KQ + 1], vrow[VQ];
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) krow[i] = kr[kslots[i] & 255];
+      krow[KQ] = kr[kslot_x & 255];
+#pragma unroll
+      for (int i = 0; i < VQ; ++i) vrow[i] = with_v ? vr[VRPL * (4 * i + w) + vrow_l] : 0;
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) lds_load16(krsrc, kb * S::KBUF + (4 * i + w) * 1024, krow[i] * krow_bytes + kvoff[i]);
+      if (w == 0) lds_load16(krsrc, kb * S::KBUF + 4 * KQ * 1024, krow[KQ] * krow_bytes + kvoff[KQ]);
+      if (with_v)
+#pragma unroll
+        for (int i = 0; i < VQ; ++i)
+          lds_load16(vrsrc, 2 * S::KBUF + vb * S::VBUF + (4 * i + w) * 1024, vrow[i] * VROW + vvoff[i]);
+    } else {
+      const __amdgpu_buffer_rsrc_t rk = chunk_k(kc), rv = chunk_v(vc);
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) lds_load16(rk, kb * S::KBUF + (4 * i + w) * 1024, kvoff[i]);
+      if (w == 0) lds_load16(rk, kb * S::KBUF + 4 * KQ * 1024, kvoff[KQ]);
+      if (with_v)
+#pragma unroll
+        for (int i = 0; i < VQ; ++i) lds_load16(rv, 2 * S::KBUF + vb * S::VBUF + (4 * i + w) * 1024, vvoff[i]);
     }
   };
   auto wait_loads = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
@@ -557,8 +588,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto begin_step = [&](int c) __attribute__((always_inline)) {
     __syncthreads();  // K(c) and V(c - 1) are staged; every wave is done with K(c - 1) and V(c - 2)
     if (w == 0) prepare(c + 2);
-    issue_k(c + 1, (c + 1) & 1);
-    issue_v(c, c & 1);
+    issue(c + 1, (c + 1) & 1, c, c & 1, true);
   };
   f32x16_t sacc[2];
   f16x2_t p_old[16];
@@ -603,7 +633,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (w == 0)
       for (int c = 0; c < 2; ++c) prepare(c);
     __syncthreads();
-    issue_k(0, 0);
+    issue(0, 0, 0, 0, false);
     wait_loads();
     // this wave's chunk runs
     int lo0 = 0, hi0 = nchunks, lo1 = nchunks, hi1 = nchunks;
