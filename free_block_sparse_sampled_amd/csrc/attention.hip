@@ -835,14 +835,16 @@ __global__ __launch_bounds__(256) void probe_merge_kernel(const float* __restric
 // lose bits to fp16 rounding.
 
 // largest |v| per K/V head as a float bit pattern (non-negative patterns order like the values);
-// grid (ceil(N d / 8 / 256), heads), amax cleared by v_amax_clear_kernel
+// grid (kAbsmaxBlocks, heads), amax cleared by v_amax_clear_kernel: each block strides over its
+// head's 16-byte pieces and adds one atomic maximum, so a head sees kAbsmaxBlocks atomics
+constexpr int kAbsmaxBlocks = 128;
 __global__ __launch_bounds__(256) void v_absmax_kernel(const uint16_t* __restrict__ v, HeadGeom gk,
                                                        unsigned* __restrict__ amax) {
   __shared__ unsigned red[4];
   const int hk = blockIdx.y, per = gk.d / 8;
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n = int64_t(gk.N) * per;
   unsigned m = 0;
-  if (idx < int64_t(gk.N) * per) {
+  for (int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x; idx < n; idx += int64_t(gridDim.x) * 256) {
     const int row = int(idx / per), pc = int(idx % per);
     const uint4 u = *reinterpret_cast<const uint4*>(v + gk.base(hk) + int64_t(row) * gk.sn + pc * 8);
     const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
@@ -896,8 +898,8 @@ __global__ __launch_bounds__(256) void v_to_f16_kernel(const uint16_t* __restric
 
 void launch_v_scale(const void* v, const HeadGeom& gk, int heads, unsigned* amax, float* scale, hipStream_t st) {
   hipLaunchKernelGGL(v_amax_clear_kernel, dim3(ceil_div(heads, 256)), dim3(256), 0, st, amax, heads);
-  const dim3 grid(unsigned(ceil_div64(int64_t(gk.N) * gk.d / 8, 256)), heads);
-  hipLaunchKernelGGL(v_absmax_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(v), gk, amax);
+  hipLaunchKernelGGL(v_absmax_kernel, dim3(kAbsmaxBlocks, heads), dim3(256), 0, st, static_cast<const uint16_t*>(v),
+                     gk, amax);
   hipLaunchKernelGGL(v_scale_kernel, dim3(ceil_div(heads, 256)), dim3(256), 0, st, amax, heads, scale);
 }
 
