@@ -60,7 +60,7 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   L.tiles = take(BH * size_t(L.tmax) * 8 * 4);
   L.ntiles = take(BH * 4);
   L.tile_prefix = take((BH + 1) * 4);
-  L.pair_ov = take(BH * p.Cq * p.Cq);
+  L.pair_ov = take(BH * p.Cq * p.Cq * 2);
   L.sel_bits = take(BH * p.Cq * 16 * 8);
   L.total = o;
   return L;

@@ -962,11 +962,11 @@ __global__ __launch_bounds__(256) void sel_bits_kernel(const int* __restrict__ n
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < kOvWords) bits[(size_t(hd) * Cq + a) * kOvWords + lane] = wb[w][lane];
 }
-// Number of K/V groups two query groups both selected (saturated at 255), for every pair of video
+// Number of K/V groups two query groups both selected, for every pair of video
 // query groups of a head: blocks of 32 x 32 pairs.
 __global__ __launch_bounds__(256) void pair_overlap_kernel(const int* __restrict__ n_q, const int* __restrict__ n_kv,
                                                            const unsigned long long* __restrict__ bits, int Cq,
-                                                           int G, uint8_t* __restrict__ ov) {
+                                                           int G, uint16_t* __restrict__ ov) {
   __shared__ unsigned long long bt[2 * kOvTile][kOvWords];
   const int hd = blockIdx.z, nq = n_q[hd], W = (n_kv[hd / G] + 63) / 64;
   const int a0 = blockIdx.x * kOvTile, c0 = blockIdx.y * kOvTile;
@@ -982,15 +982,15 @@ __global__ __launch_bounds__(256) void pair_overlap_kernel(const int* __restrict
     if (a >= nq || c >= nq) continue;
     int v = 0;
     for (int x = 0; x < W; ++x) v += __popcll(bt[i][x] & bt[kOvTile + j][x]);
-    ov[(size_t(hd) * Cq + a) * Cq + c] = uint8_t(min(v, 255));
+    ov[(size_t(hd) * Cq + a) * Cq + c] = uint16_t(v);
   }
 }
 __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restrict__ q_off, const int* __restrict__ n_q,
                                                             int Cq, int Nv, int n_text, int tmax,
-                                                            const uint8_t* __restrict__ ov,
+                                                            const uint16_t* __restrict__ ov,
                                                             int* __restrict__ tiles, int* __restrict__ ntiles) {
   __shared__ int buf[1024], small_id[1024], partner[1024], best_of[1024];
-  extern __shared__ uint8_t ovs[];  // [n_small][n_small] overlaps of the small groups, when they fit
+  extern __shared__ uint16_t ovs[];  // [n_small][n_small] overlaps of the small groups, when they fit
   const int hd = blockIdx.x, t = threadIdx.x;
   const int nq = n_q[hd];
   const int* qo = q_off + size_t(hd) * (Cq + 1);
@@ -1040,13 +1040,13 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
   if (small) small_id[small_rank] = t;
   if (t < n_small) partner[t] = -1;
   if (ov) {
-    const uint8_t* ovh = ov + size_t(hd) * Cq * Cq;
+    const uint16_t* ovh = ov + size_t(hd) * Cq * Cq;
     // the small groups' overlaps gathered into LDS when they fit
-    const bool in_lds = size_t(n_small) * n_small <= kTilesLds;
+    const bool in_lds = size_t(n_small) * n_small * sizeof(uint16_t) <= kTilesLds;
     __syncthreads();  // small_id complete
     if (in_lds)  // row i by wave, columns by lane
       for (int i = t >> 6; i < n_small; i += blockDim.x >> 6) {
-        const uint8_t* src = ovh + size_t(small_id[i]) * Cq;
+        const uint16_t* src = ovh + size_t(small_id[i]) * Cq;
         for (int j = t & 63; j < n_small; j += 64) ovs[i * n_small + j] = src[small_id[j]];
       }
     // four threads per group (adjacent lanes) split the candidates
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(1024) void sparse_tiles_kernel(const int* __restric
         const int i = i0 + (t >> 2), q = t & 3;
         int best = -1, bestv = -1;
         if (i < n_small && partner[i] < 0) {
-          const uint8_t* row = ovh + size_t(small_id[i]) * Cq;
+          const uint16_t* row = ovh + size_t(small_id[i]) * Cq;
           // candidates j = q, q + 4, ... in batches of 8 (all loads of a batch issued first)
           for (int j0 = q; j0 < n_small; j0 += 32) {
             int vv[8];
@@ -1158,9 +1158,9 @@ spr_status run_attn_sparse(const spr_desc& desc, const spr_part_params& p, const
   int* tiles = ws_ptr<int>(ws, L.tiles);
   int* ntiles = ws_ptr<int>(ws, L.ntiles);
   // selection overlaps of every pair of query groups (for up to 1024 K/V groups), then the tiles
-  uint8_t* ov = nullptr;
+  uint16_t* ov = nullptr;
   if (p.Ck <= 64 * kOvWords) {
-    ov = ws_ptr<uint8_t>(ws, L.pair_ov);
+    ov = ws_ptr<uint16_t>(ws, L.pair_ov);
     unsigned long long* sbits = ws_ptr<unsigned long long>(ws, L.sel_bits);
     hipLaunchKernelGGL(sel_bits_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, part.n_q, part.n_kv,
                        route.sel_cnt, route.sel_kv, p.Cq, p.Ck, kv_group_size(desc), desc.n_text, sbits);

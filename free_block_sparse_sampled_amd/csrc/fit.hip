@@ -76,43 +76,60 @@ __global__ __launch_bounds__(256) void fit_prep_kernel(const float* __restrict__
   }
 }
 
-// G = Xb^T W Xb + lam I and H = Xb^T W Rb, 16 x 16 tiles, probes staged in LDS; with Cr
-// WITH_C also Cr = Rb^T W Rb (the residual second moment of the output truncation, App. D.3).
-template <bool WITH_C>
+// G = Xb^T W Xb + lam I and H = Xb^T W Rb on v_mfma_f64_16x16x4f64; with WITH_C also
+// Cr = Rb^T W Rb (the residual second moment of the output truncation, App. D.3).  Block
+// (i0 / 16, head) forms rows i0 .. i0 + 15 of each product, wave w its column tiles w, w + 4, ..;
+// the probes stream through LDS in chunks of 16.  Products with A = rows of w Xb (or w Rb) and
+// B = rows of Xb or Rb: lane l feeds probe k0 + l / 16 of column i0 + l % 16 (A) and of column
+// j0 + l % 16 (B); accumulator v of lane l is entry (i0 + l / 16 + 4 v, j0 + l % 16).
+typedef double fit_f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kNePc = 16;
+template <bool WITH_C, int D>
 __global__ __launch_bounds__(256) void normal_eq_kernel(const double* __restrict__ Xb, const double* __restrict__ Rb,
-                                                        const double* __restrict__ Wt, int d, int M, double lam,
+                                                        const double* __restrict__ Wt, int M, double lam,
                                                         double* __restrict__ G, double* __restrict__ Hm,
                                                         double* __restrict__ Cr) {
-  __shared__ double Xi[32][17], Xj[32][17], Rj[32][17], Ri[WITH_C ? 32 : 1][17], Ws[32];
-  const int hd = blockIdx.y;
-  const int tiles = d / 16;
-  const int i0 = (blockIdx.x / tiles) * 16, j0 = (blockIdx.x % tiles) * 16;
-  const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-  double g = 0.0, h = 0.0, cr = 0.0;
-  for (int p0 = 0; p0 < M; p0 += 32) {
-    for (int e = threadIdx.x; e < 32 * 16; e += 256) {
-      const int pp = e >> 4, cc = e & 15, p = p0 + pp;
+  constexpr int XS = D + 1, TW = D / 64;  // LDS row stride; column tiles per wave
+  __shared__ double Xs[kNePc][XS], Rs[kNePc][XS], Ws[kNePc];
+  const int hd = blockIdx.y, i0 = blockIdx.x * 16;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, kq = lane >> 4;
+  fit_f64x4 ag[TW], ah[TW], ac[TW];
+#pragma unroll
+  for (int u = 0; u < TW; ++u) ag[u] = ah[u] = ac[u] = fit_f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int p0 = 0; p0 < M; p0 += kNePc) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kNePc * D; e += 256) {
+      const int pp = e / D, c = e % D, p = p0 + pp;
       const bool ok = p < M;
-      Xi[pp][cc] = ok ? Xb[(size_t(hd) * M + p) * d + i0 + cc] : 0.0;
-      Xj[pp][cc] = ok ? Xb[(size_t(hd) * M + p) * d + j0 + cc] : 0.0;
-      Rj[pp][cc] = ok ? Rb[(size_t(hd) * M + p) * d + j0 + cc] : 0.0;
-      if constexpr (WITH_C) Ri[pp][cc] = ok ? Rb[(size_t(hd) * M + p) * d + i0 + cc] : 0.0;
+      Xs[pp][c] = ok ? Xb[(size_t(hd) * M + p) * D + c] : 0.0;
+      Rs[pp][c] = ok ? Rb[(size_t(hd) * M + p) * D + c] : 0.0;
     }
-    if (threadIdx.x < 32) Ws[threadIdx.x] = p0 + threadIdx.x < M ? Wt[size_t(hd) * M + p0 + threadIdx.x] : 0.0;
+    if (threadIdx.x < kNePc) Ws[threadIdx.x] = p0 + threadIdx.x < M ? Wt[size_t(hd) * M + p0 + threadIdx.x] : 0.0;
     __syncthreads();
-    for (int pp = 0; pp < 32; ++pp) {
-      const double wx = Ws[pp] * Xi[pp][ti];
-      g = fma(wx, Xj[pp][tj], g);
-      h = fma(wx, Rj[pp][tj], h);
+#pragma unroll
+    for (int kk = 0; kk < kNePc; kk += 4) {
+      const int p = kk + kq;
+      const double a = Ws[p] * Xs[p][i0 + r16];
+      const double ar = WITH_C ? Ws[p] * Rs[p][i0 + r16] : 0.0;
+#pragma unroll
+      for (int u = 0; u < TW; ++u) {
+        const int j = (w + 4 * u) * 16 + r16;
+        ag[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Xs[p][j], ag[u], 0, 0, 0);
+        ah[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Rs[p][j], ah[u], 0, 0, 0);
+        if constexpr (WITH_C) ac[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(ar, Rs[p][j], ac[u], 0, 0, 0);
+      }
     }
-    if constexpr (WITH_C)
-      for (int pp = 0; pp < 32; ++pp) cr = fma(Ws[pp] * Ri[pp][ti], Rj[pp][tj], cr);
-    __syncthreads();
   }
-  if (i0 + ti == j0 + tj) g += lam;
-  G[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = g;
-  Hm[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = h;
-  if constexpr (WITH_C) Cr[size_t(hd) * d * d + size_t(i0 + ti) * d + j0 + tj] = cr;
+#pragma unroll
+  for (int u = 0; u < TW; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = i0 + kq + 4 * v, j = (w + 4 * u) * 16 + r16;
+      const size_t at = size_t(hd) * D * D + size_t(i) * D + j;
+      G[at] = ag[u][v] + (i == j ? lam : 0.0);
+      Hm[at] = ah[u][v];
+      if constexpr (WITH_C) Cr[at] = ac[u][v];
+    }
 }
 
 // C (m x n, row stride ldc) = op(A) op(B) with 4 x 4 register tiles per thread; op(A)(i, k) is
@@ -529,12 +546,18 @@ spr_status run_fit_correct(const spr_desc& desc, const spr_part_params& p, const
   double* Fr = ws_ptr<double>(ws, L.fitF);
   hipLaunchKernelGGL(fit_prep_kernel, dim3(d / 32, BH), dim3(256), 0, st, o_sp, o_probe, route.probe_idx, route.probe_w,
                      part.q_pos, N, Nv, d, M, std_eps, Xb, Rb, S, Wt);
-  if (trunc)
-    hipLaunchKernelGGL(normal_eq_kernel<true>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M, lam,
-                       G, Hm, Cr);
-  else
-    hipLaunchKernelGGL(normal_eq_kernel<false>, dim3((d / 16) * (d / 16), BH), dim3(256), 0, st, Xb, Rb, Wt, d, M,
-                       lam, G, Hm, Cr);
+  const dim3 neg(d / 16, BH);
+  if (d == 128) {
+    if (trunc)
+      hipLaunchKernelGGL((normal_eq_kernel<true, 128>), neg, dim3(256), 0, st, Xb, Rb, Wt, M, lam, G, Hm, Cr);
+    else
+      hipLaunchKernelGGL((normal_eq_kernel<false, 128>), neg, dim3(256), 0, st, Xb, Rb, Wt, M, lam, G, Hm, Cr);
+  } else {
+    if (trunc)
+      hipLaunchKernelGGL((normal_eq_kernel<true, 64>), neg, dim3(256), 0, st, Xb, Rb, Wt, M, lam, G, Hm, Cr);
+    else
+      hipLaunchKernelGGL((normal_eq_kernel<false, 64>), neg, dim3(256), 0, st, Xb, Rb, Wt, M, lam, G, Hm, Cr);
+  }
   SPR_CHECK_LAUNCH();
   if (trunc) {
     const spr_status s = launch_eigen_factor(Cr, BH, d, out_rank, p.eig_clamp, Fr, gstat, st);

@@ -12,7 +12,7 @@ import torch
 import free_block_sparse_sampled_amd as spr
 import oracle as O
 from tests.gpu_pipeline import device_inputs, op_config, pull, row_rel_err, run_operator
-from workloads import config, head_inputs
+from workloads import batch_inputs, config, head_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -672,6 +672,10 @@ def test_bf16_route_widths(Ck):
 @pytest.mark.parametrize("grid,Ck,Cq,M,rho", [
     ((2, 8, 8), 96, 8, 8, 0.6),      # mostly one-key groups (exact zero scores in the bf16 path)
     ((1, 5, 29), 40, 9, 8, 0.3),     # 145 rows, ragged against every tile
+    # many K/V groups at high density: paired small query groups whose union runs to hundreds of
+    # segments per category (the segment tables of the sparse tiles near their capacity)
+    ((8, 16, 16), 800, 256, 64, 0.8),
+    ((8, 16, 16), 1000, 256, 64, 0.5),
 ])
 def test_bf16_degenerate_groups(grid, Ck, Cq, M, rho):
     """Edge cases of the bounded bf16 routing on the positional workload (bf16, d = 128)."""
@@ -687,3 +691,25 @@ def test_bf16_degenerate_groups(grid, Ck, Cq, M, rho):
         _compare_head(g, ref, 0, cfg.Nv, cfg.N, cfg.n_text)
     else:
         _lockstep_head(g, q, k, v, cfg, opc, 0, 0, np.random.default_rng(1), nrows=64, ngroups=min(6, Cq))
+
+
+@pytest.mark.gpu
+def test_large_and_small_magnitude_values():
+    """V far outside the fp16 range (head 0 scaled by 2^20, |v| up to ~4e6) and far below it
+    (head 1 scaled by 2^-30): the fp16 copy of V is scaled by a power of two per K/V head and the
+    scale undone on the output, so every stage still matches the oracle in lockstep."""
+    cfg = config("small").with_(H=2)
+    opc = op_config(cfg)
+    q, k, v = batch_inputs(cfg)
+    v = v.astype(np.float64)
+    v[0, 0] *= 2.0 ** 20
+    v[0, 1] *= 2.0 ** -30
+    v = v.astype(np.float32)  # exact: bf16 values times a power of two
+    tq, tk, tv = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
+    assert torch.equal(tv.float().cpu(), torch.from_numpy(v))
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    assert np.all(np.isfinite(g["o_sp"])) and np.all(np.isfinite(g["out"]))
+    rng = np.random.default_rng(4)
+    for h in (0, 1):
+        _lockstep_head(g, q, k, v, cfg, opc, 0, h, rng)
