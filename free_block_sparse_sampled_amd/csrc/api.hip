@@ -41,6 +41,13 @@ Workspace layout(const spr_desc& desc, const spr_part_params& p, int M) {
   const size_t nsc = desc.dtype == SPR_BF16 ? BH * p.Cq * p.Ck : 0;
   L.serr = take(nsc * 8);
   L.qsplit = take(desc.dtype == SPR_BF16 ? BH * p.Cq * 3 * d * 2 : 0);
+  {  // the bf16 routing resolve: request bits, and each query group's ranking (64 E >= Ck entries)
+    const size_t bf = desc.dtype == SPR_BF16 ? 1 : 0;
+    const size_t e64 = p.Ck <= 64 ? 64 : p.Ck <= 128 ? 128 : p.Ck <= 256 ? 256 : p.Ck <= 512 ? 512 : 1024;
+    L.rr_bits = take(bf * BH * p.Ck * ((p.Cq + 63) / 64) * 8);
+    L.rr_order = take(bf * BH * p.Cq * e64 * 4);
+    L.rr_nin = take(bf * BH * p.Cq * 4);
+  }
   L.qnorm = take(BH * p.Cq * 8);
   const size_t BHkv = size_t(desc.B) * kv_heads(desc);
   L.vh = take(desc.dtype == SPR_BF16 ? BHkv * size_t(desc.N) * d * 2 : 0);

@@ -218,6 +218,9 @@ struct Workspace {
   size_t tiles;      // int    [BH][tmax][8]     block-sparse attention tiles (two row halves each)
   size_t ntiles;     // int    [BH]              tiles used per head
   size_t tile_prefix;  // int  [BH + 1]          exclusive prefix of ntiles
+  size_t rr_bits;    // u64    [BH][Ck][Cq / 64]  fp64 rescoring requests of the routing resolve
+  size_t rr_order;   // int    [BH][Cq][64 E]      ranking of each query group between resolve phases
+  size_t rr_nin;     // int    [BH][Cq]            prefix candidates of each query group
   size_t pair_ov;    // uint16 [BH][Cq][Cq]     shared K/V groups of two query groups' selections
   size_t sel_bits;   // uint64 [BH][Cq][16]     selections as bitmaps over K/V groups
   size_t total;

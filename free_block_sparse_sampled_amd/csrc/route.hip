@@ -877,276 +877,225 @@ __device__ __attribute__((noinline)) double route_exact_score(glb_cuint4* Kp, in
   return A * A * vn - 2.0 * A * s1 / g + s2 / g;
 }
 
-// Routing of one query group from the bf16 scores and their bounds, one wave per group.  With
-// I_b = [s_b - e_b, s_b + e_b] holding the exact score:
-//   1. scores whose bound is not finite or above 1e-3 of the row's largest score are recomputed
-//      in fp64;
-//   2. the groups are ranked by score, and lambda' is the smallest lower end among the shortest
-//      ranked prefix holding Tk keys.  A group whose upper end is below lambda' is preceded (in
-//      exact order) by groups holding at least Tk keys, so it is outside the prefix; it ranks
-//      last (a stable partition through LDS);
-//   3. among the others, in rank order, a group meets an earlier interval iff the smallest
-//      earlier lower end reaches its upper end, and a later one iff the largest later upper end
-//      reaches its lower end; such groups get an fp64 score;
-//   4. a group left with its bf16 score is disjoint from every other interval, so it sits
-//      correctly against every score of the row; the recomputed groups form runs of consecutive
-//      ranks (a group between two overlapping intervals meets one of them), which odd-even
-//      transposition passes put in order.  The ranking is then that of the fp64 scores.
-template <int E, int DT, int D>
+// Routing of one query group from the bf16 scores and their bounds, one wave per group, in three
+// phases with the fp64 rescoring between them (route_rescore_kernel, which reads the keys of a
+// K/V group once for every query group that asked for it).  With I_b = [s_b - e_b, s_b + e_b]
+// holding the exact score:
+//   phase 0: scores whose bound is not finite or above 1e-3 of the row's largest score are
+//            marked for rescoring;
+//   phase 1: the groups are ranked by score, and lambda' is the smallest lower end among the
+//            shortest ranked prefix holding Tk keys.  A group whose upper end is below lambda' is
+//            preceded (in exact order) by groups holding at least Tk keys, so it is outside the
+//            prefix; it ranks last (a stable partition through LDS).  Among the others, in rank
+//            order, a group meets an earlier interval iff the smallest earlier lower end reaches
+//            its upper end, and a later one iff the largest later upper end reaches its lower
+//            end; such groups are marked for rescoring.  The ranking and the number of groups
+//            that can be in the prefix are kept for phase 2;
+//   phase 2: a group left with its bf16 score is disjoint from every other interval, so it sits
+//            correctly against every score of the row; the rescored groups form runs of
+//            consecutive ranks (a group between two overlapping intervals meets one of them),
+//            which odd-even transposition passes put in order.  The ranking is then that of the
+//            fp64 scores, and its prefix is the selection.
+// Rescored entries are written back to `scores` with bound 0 between the phases.
+template <int PHASE, int E, int D>
 __global__ __launch_bounds__(256) void route_resolve_kernel(
-    const double* __restrict__ scores, const double* __restrict__ serr, double* __restrict__ scores_out,
-    double* __restrict__ serr_out, const void* __restrict__ Kp, int N, int Nv, const double* __restrict__ qbar,
-    const double* __restrict__ lbar, const double* __restrict__ vbar, const double* __restrict__ shift,
-    const double* __restrict__ vstat, const int* __restrict__ kv_off, const int* __restrict__ q_off,
-    const int* __restrict__ n_q, const int* __restrict__ n_kv, int Cq, int Ck, int G, int n_text, int64_t Tk,
+    double* __restrict__ scores, double* __restrict__ serr, bool keep, const int* __restrict__ kv_off,
+    const int* __restrict__ q_off, const int* __restrict__ n_q, const int* __restrict__ n_kv, int Cq, int Ck, int G,
+    int n_text, int64_t Tk, unsigned long long* __restrict__ rbits, int* __restrict__ rorder, int* __restrict__ rnin,
     int* __restrict__ sel_cnt, int* __restrict__ sel_kv, int64_t* __restrict__ pairs, int* __restrict__ gstat) {
-  __shared__ __attribute__((aligned(16))) double qs[4][D];
   __shared__ double part_val[4][64 * E];
   __shared__ int part_id[4][64 * E];
-  __shared__ int q_cnt[4];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hd = blockIdx.y, hk = hd / G, a = blockIdx.x * 4 + w;
   const int nq = n_q[hd], nkv = n_kv[hk];
   const int* off = kv_off + size_t(hk) * (Ck + 1);
   if (a > nq || (a == nq && n_text == 0)) return;
-  int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
   if (a == nq) {  // text query rows: every group
-    for (int b = lane; b <= nkv; b += 64) out[b] = b;
-    if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
+    if constexpr (PHASE == 2) {
+      int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
+      for (int b = lane; b <= nkv; b += 64) out[b] = b;
+      if (lane == 0) sel_cnt[size_t(hd) * (Cq + 1) + a] = nkv + 1;
+    }
     return;
   }
   const size_t row = (size_t(hd) * Cq + a) * Ck;
-  for (int c = lane; c < D; c += 64) qs[w][c] = qbar[(size_t(hd) * Cq + a) * D + c];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const double m = shift[size_t(hd) * Cq + a];
-  const bool keep = scores_out != nullptr;
+  const int W = (Cq + 63) / 64;  // request words per K/V group
+  auto request = [&](int b) {
+    atomicOr(rbits + (size_t(hd) * Ck + b) * W + (a >> 6), 1ull << (a & 63));
+  };
+  int* ord = rorder + (size_t(hd) * Cq + a) * (64 * E);
   double sc[E], pl[1][E];  // score and its bound
   int id[E];
-#pragma unroll
-  for (int t = 0; t < E; ++t) {
-    const int i = lane * E + t;
-    sc[t] = i < nkv ? scores[row + i] : 0.0;
-    pl[0][t] = i < nkv ? serr[row + i] : 0.0;
-    id[t] = i < nkv ? i : 0x7fffffff;
-  }
-  // recompute, one group at a time, every entry whose flag is set
-  bool any_fixed = false;
-  auto resolve = [&](bool (&flag)[E]) {
+  if constexpr (PHASE < 2) {
+    // coalesced loads: entry t of lane l is group t 64 + l (the ranking below does not depend on
+    // where an entry starts, its order being a total one)
 #pragma unroll
     for (int t = 0; t < E; ++t) {
-      unsigned long long mk = __ballot(flag[t]);
-      any_fixed |= mk != 0ull;
-      while (mk) {
-        const int src = __ffsll(mk) - 1;
-        mk &= mk - 1;
-        const int b = __shfl(id[t], src);
-        const double v = route_exact_score<DT, D>(
-            (glb_cuint4*)Kp, N, Nv, (lds_cdouble*)qs[w], (glb_cdouble*)vbar, (glb_cdouble*)vstat, lbar[row + b], m,
-            off[b], off[b + 1], hk, Ck, b, lane);
-        if (lane == src) {
-          sc[t] = v;
-          pl[0][t] = 0.0;
-        }
-      }
-    }
-  };
-  // 1. bounds that would overlap most of the row
-  double rmax = 0.0;
-#pragma unroll
-  for (int t = 0; t < E; ++t)
-    if (id[t] < nkv) rmax = fmax(rmax, fabs(sc[t]));
-  for (int o = 32; o > 0; o >>= 1) rmax = fmax(rmax, __shfl_xor(rmax, o));
-  bool flag[E];
-#pragma unroll
-  for (int t = 0; t < E; ++t) flag[t] = id[t] < nkv && !(pl[0][t] <= 1e-3 * rmax);
-  resolve(flag);
-  // 2. rank by score; lambda' = the smallest lower end among the shortest ranked prefix holding
-  //    Tk keys.  Those groups hold at least Tk keys with lower ends >= lambda', so a group whose
-  //    upper end is below lambda' is outside the prefix (-inf when Tk is out of reach)
-  // the bounds wait in LDS by group (the ranking network carries only scores and groups)
-#pragma unroll
-  for (int t = 0; t < E; ++t) {
-    part_val[w][lane * E + t] = pl[0][t];
-    if (id[t] >= nkv) sc[t] = -1.0e308;
-  }
-  {
-    double none[1][E];
-    wave_sort_desc<E, 0>(sc, id, none, lane);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-  for (int t = 0; t < E; ++t) pl[0][t] = id[t] < nkv ? part_val[w][id[t]] : 0.0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int sz[E], s_loc = 0;
-#pragma unroll
-  for (int t = 0; t < E; ++t) {
-    sz[t] = id[t] < nkv ? off[id[t] + 1] - off[id[t]] : 0;
-    s_loc += sz[t];
-  }
-  int incl = s_loc;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  double lam = INFINITY;
-  {
-    int cum = incl - s_loc;
-#pragma unroll
-    for (int t = 0; t < E; ++t) {
-      if (id[t] < nkv && cum < Tk) lam = fmin(lam, sc[t] - pl[0][t]);  // ranks up to the crossing
-      cum += sz[t];
-    }
-    for (int o = 32; o > 0; o >>= 1) lam = fmin(lam, __shfl_xor(lam, o));
-    if (__shfl(incl, 63) < Tk) lam = -INFINITY;
-  }
-  // 3. stable partition through LDS: the groups that can be in the prefix first, in rank order
-  //    (their scores and bounds are written out now for the others)
-  bool in[E];
-  int n_in_l = 0;
-#pragma unroll
-  for (int t = 0; t < E; ++t) {
-    in[t] = id[t] < nkv && sc[t] + pl[0][t] >= lam;
-    n_in_l += in[t] ? 1 : 0;
-    if (keep && id[t] < nkv && !in[t]) {
-      scores_out[row + id[t]] = sc[t];
-      serr_out[row + id[t]] = -(pl[0][t] + 1.0e-300);
+      const int i = t * 64 + lane;
+      sc[t] = i < nkv ? scores[row + i] : 0.0;
+      pl[0][t] = i < nkv ? serr[row + i] : 0.0;
+      id[t] = i < nkv ? i : 0x7fffffff;
     }
   }
-  int in_incl = n_in_l;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(in_incl, o);
-    if (lane >= o) in_incl += y;
-  }
-  const int n_in = __shfl(in_incl, 63);
-  {
-    const int r_in0 = in_incl - n_in_l, r_out0 = n_in + (lane * E - (in_incl - n_in_l));
-    double* vs = &part_val[w][0];
-    int* is = &part_id[w][0];
-    auto wave_sync = [] {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    int r_in = r_in0, r_out = r_out0;
-#pragma unroll
-    for (int t = 0; t < E; ++t) {  // keys and ids
-      const int dst = in[t] ? r_in++ : r_out++;
-      vs[dst] = in[t] ? sc[t] : (id[t] < nkv ? -1.0e300 : -1.0e308);
-      is[dst] = id[t];
-    }
-    wave_sync();
-    double nk[E];
-#pragma unroll
-    for (int t = 0; t < E; ++t) {
-      nk[t] = vs[lane * E + t];
-      id[t] = is[lane * E + t];
-    }
-    wave_sync();
-    r_in = r_in0;
-    r_out = r_out0;
-#pragma unroll
-    for (int t = 0; t < E; ++t) vs[in[t] ? r_in++ : r_out++] = pl[0][t];  // bounds
-    wave_sync();
-#pragma unroll
-    for (int t = 0; t < E; ++t) {
-      sc[t] = nk[t];
-      pl[0][t] = vs[lane * E + t];
-      in[t] = lane * E + t < n_in;
-    }
-  }
-  // overlaps among the groups that can be in the prefix: in rank order a group meets an earlier
-  // interval iff the smallest earlier lower end reaches its upper end, a later one iff the
-  // largest later upper end reaches its lower end
-  double lmin = INFINITY, hmax = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < E; ++t)
-    if (in[t]) {
-      lmin = fmin(lmin, sc[t] - pl[0][t]);
-      hmax = fmax(hmax, sc[t] + pl[0][t]);
-    }
-  double pmin = lmin, smax = hmax;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(pmin, o), z = __shfl_down(smax, o);
-    if (lane >= o) pmin = fmin(pmin, y);
-    if (lane + o < 64) smax = fmax(smax, z);
-  }
-  double run_lo = __shfl_up(pmin, 1), run_hi = __shfl_down(smax, 1);
-  if (lane == 0) run_lo = INFINITY;
-  if (lane == 63) run_hi = -INFINITY;
-  // earlier intervals forward, later ones backward (flags only, no per-entry minima kept)
-#pragma unroll
-  for (int t = 0; t < E; ++t) {
-    flag[t] = in[t] && pl[0][t] > 0.0 && run_lo <= sc[t] + pl[0][t];
-    if (in[t]) run_lo = fmin(run_lo, sc[t] - pl[0][t]);
-  }
-#pragma unroll
-  for (int t = E - 1; t >= 0; --t) {
-    const double lo = sc[t] - pl[0][t], hi = sc[t] + pl[0][t];
-    flag[t] = flag[t] || (in[t] && pl[0][t] > 0.0 && run_hi >= lo);
-    if (in[t]) run_hi = fmax(run_hi, hi);
-  }
-  // the four query groups of the block share their fp64 scores: each publishes its list in LDS,
-  // the waves take the block's items in turn, and each reads its own results back
-  {
-    int nmk = 0;
-#pragma unroll
-    for (int t = 0; t < E; ++t) nmk += flag[t] ? 1 : 0;
-    int mincl = nmk;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(mincl, o);
-      if (lane >= o) mincl += y;
-    }
-    if (lane == 63) q_cnt[w] = mincl;
-    int k = mincl - nmk;
+  if constexpr (PHASE == 0) {
+    // bounds that would overlap most of the row
+    double rmax = 0.0;
 #pragma unroll
     for (int t = 0; t < E; ++t)
-      if (flag[t]) part_id[w][k++] = id[t];
-  }
-  any_fixed = false;
-  __syncthreads();
-  {
-    // waves whose query group does not exist (or is the text group) left early: no items
-    auto cnt_of = [&](int ow) { return blockIdx.x * 4 + ow < nq ? q_cnt[ow] : 0; };
-    const int c0 = cnt_of(0), c1 = c0 + cnt_of(1), c2 = c1 + cnt_of(2), tot = c2 + cnt_of(3);
-    for (int i = w; i < tot; i += 4) {
-      const int ow = i < c0 ? 0 : i < c1 ? 1 : i < c2 ? 2 : 3;
-      const int k = i - (ow == 0 ? 0 : ow == 1 ? c0 : ow == 2 ? c1 : c2);
-      const int oa = blockIdx.x * 4 + ow, b = part_id[ow][k];
-      const size_t orow = (size_t(hd) * Cq + oa) * Ck;
-      const double v = route_exact_score<DT, D>((glb_cuint4*)Kp, N, Nv, (lds_cdouble*)qs[ow], (glb_cdouble*)vbar,
-                                                (glb_cdouble*)vstat, lbar[orow + b], shift[size_t(hd) * Cq + oa],
-                                                off[b], off[b + 1], hk, Ck, b, lane);
-      if (lane == 0) part_val[ow][k] = v;
-    }
-  }
-  __syncthreads();
-  {
-    int nmk = 0;
-#pragma unroll
-    for (int t = 0; t < E; ++t) nmk += flag[t] ? 1 : 0;
-    int mincl = nmk;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(mincl, o);
-      if (lane >= o) mincl += y;
-    }
-    int k = mincl - nmk;
+      if (id[t] < nkv) rmax = fmax(rmax, fabs(sc[t]));
+    for (int o = 32; o > 0; o >>= 1) rmax = fmax(rmax, __shfl_xor(rmax, o));
 #pragma unroll
     for (int t = 0; t < E; ++t)
-      if (flag[t]) {
-        sc[t] = part_val[w][k++];
-        pl[0][t] = 0.0;
-      }
-    any_fixed = __any(nmk > 0);
+      if (id[t] < nkv && !(pl[0][t] <= 1e-3 * rmax)) request(id[t]);
+    return;
   }
-  // 4. odd-even transposition passes over the first n_in ranks until their ranking is that of
-  //    the scores
-  if (__any(any_fixed)) {
+  if constexpr (PHASE == 1) {
+    // rank by score; lambda' = the smallest lower end among the shortest ranked prefix holding Tk
+    // keys.  Those groups hold at least Tk keys with lower ends >= lambda', so a group whose upper
+    // end is below lambda' is outside the prefix (-inf when Tk is out of reach).  The bounds wait
+    // in LDS by group (the ranking network carries only scores and groups).
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      part_val[w][t * 64 + lane] = pl[0][t];  // by group
+      if (id[t] >= nkv) sc[t] = -1.0e308;
+    }
+    {
+      double none[1][E];
+      wave_sort_desc<E, 0>(sc, id, none, lane);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int t = 0; t < E; ++t) pl[0][t] = id[t] < nkv ? part_val[w][id[t]] : 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int sz[E], s_loc = 0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      sz[t] = id[t] < nkv ? off[id[t] + 1] - off[id[t]] : 0;
+      s_loc += sz[t];
+    }
+    int incl = s_loc;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    double lam = INFINITY;
+    {
+      int cum = incl - s_loc;
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        if (id[t] < nkv && cum < Tk) lam = fmin(lam, sc[t] - pl[0][t]);  // ranks up to the crossing
+        cum += sz[t];
+      }
+      for (int o = 32; o > 0; o >>= 1) lam = fmin(lam, __shfl_xor(lam, o));
+      if (__shfl(incl, 63) < Tk) lam = -INFINITY;
+    }
+    // stable partition through LDS: the groups that can be in the prefix first, in rank order
+    // (their scores and bounds are written out now for the others)
+    bool in[E];
+    int n_in_l = 0;
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      in[t] = id[t] < nkv && sc[t] + pl[0][t] >= lam;
+      n_in_l += in[t] ? 1 : 0;
+      if (keep && id[t] < nkv && !in[t]) serr[row + id[t]] = -(pl[0][t] + 1.0e-300);
+    }
+    int in_incl = n_in_l;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(in_incl, o);
+      if (lane >= o) in_incl += y;
+    }
+    const int n_in = __shfl(in_incl, 63);
+    {
+      const int r_in0 = in_incl - n_in_l, r_out0 = n_in + (lane * E - (in_incl - n_in_l));
+      double* vs = &part_val[w][0];
+      int* is = &part_id[w][0];
+      auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+      int r_in = r_in0, r_out = r_out0;
+#pragma unroll
+      for (int t = 0; t < E; ++t) {  // keys and ids
+        const int dst = in[t] ? r_in++ : r_out++;
+        vs[dst] = in[t] ? sc[t] : (id[t] < nkv ? -1.0e300 : -1.0e308);
+        is[dst] = id[t];
+      }
+      wave_sync();
+      double nk[E];
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        nk[t] = vs[lane * E + t];
+        id[t] = is[lane * E + t];
+      }
+      wave_sync();
+      r_in = r_in0;
+      r_out = r_out0;
+#pragma unroll
+      for (int t = 0; t < E; ++t) vs[in[t] ? r_in++ : r_out++] = pl[0][t];  // bounds
+      wave_sync();
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        sc[t] = nk[t];
+        pl[0][t] = vs[lane * E + t];
+        in[t] = lane * E + t < n_in;
+      }
+    }
+    // overlaps among the groups that can be in the prefix: in rank order a group meets an
+    // earlier interval iff the smallest earlier lower end reaches its upper end, a later one iff
+    // the largest later upper end reaches its lower end
+    double lmin = INFINITY, hmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < E; ++t)
+      if (in[t]) {
+        lmin = fmin(lmin, sc[t] - pl[0][t]);
+        hmax = fmax(hmax, sc[t] + pl[0][t]);
+      }
+    double pmin = lmin, smax = hmax;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(pmin, o), z = __shfl_down(smax, o);
+      if (lane >= o) pmin = fmin(pmin, y);
+      if (lane + o < 64) smax = fmax(smax, z);
+    }
+    double run_lo = __shfl_up(pmin, 1), run_hi = __shfl_down(smax, 1);
+    if (lane == 0) run_lo = INFINITY;
+    if (lane == 63) run_hi = -INFINITY;
+    bool flag[E];
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      flag[t] = in[t] && pl[0][t] > 0.0 && run_lo <= sc[t] + pl[0][t];
+      if (in[t]) run_lo = fmin(run_lo, sc[t] - pl[0][t]);
+    }
+#pragma unroll
+    for (int t = E - 1; t >= 0; --t) {
+      const double lo = sc[t] - pl[0][t], hi = sc[t] + pl[0][t];
+      flag[t] = flag[t] || (in[t] && pl[0][t] > 0.0 && run_hi >= lo);
+      if (in[t]) run_hi = fmax(run_hi, hi);
+    }
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      if (flag[t]) request(id[t]);
+      ord[lane * E + t] = id[t];
+    }
+    if (lane == 0) rnin[size_t(hd) * Cq + a] = n_in;
+    return;
+  }
+  if constexpr (PHASE == 2) {
+    const int n_in = rnin[size_t(hd) * Cq + a];
+#pragma unroll
+    for (int t = 0; t < E; ++t) {
+      const int i = lane * E + t;
+      id[t] = ord[i];
+      const bool inn = i < n_in;
+      sc[t] = inn ? scores[row + id[t]] : -1.0e300;
+      pl[0][t] = inn ? serr[row + id[t]] : 0.0;
+    }
+    // odd-even transposition passes over the first n_in ranks until their ranking is that of
+    // the scores (none swap when no score in the prefix candidates was rescored)
     auto before = [](double s1, int i1, double s2, int i2) { return s1 > s2 || (s1 == s2 && i1 < i2); };
     auto pass = [&](int parity) -> bool {
       bool sw_any = false;
@@ -1182,18 +1131,127 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
       const bool s1 = pass(1);
       if (!s0 && !s1) break;
     }
+    int* out = sel_kv + (size_t(hd) * (Cq + 1) + a) * (Ck + 1);
+    const int64_t ga = q_off[size_t(hd) * (Cq + 1) + a + 1] - q_off[size_t(hd) * (Cq + 1) + a];
+    emit_prefix<E>(id, nkv, off, Tk, lane, n_text, out, sel_cnt + size_t(hd) * (Cq + 1) + a, ga, pairs + hd,
+                   gstat + hd * 8 + 0);
   }
-  if (keep) {
-#pragma unroll
-    for (int t = 0; t < E; ++t)
-      if (sc[t] > -1.0e299) {
-        scores_out[row + id[t]] = sc[t];
-        serr_out[row + id[t]] = pl[0][t];
+}
+
+// fp64 rescoring of the (query group, K/V group) pairs the resolve phases asked for, grouped by
+// K/V group: block (b, head) reads the requests of its column of request bits (clearing them),
+// stages the group's keys and their statistics in LDS once, and each wave computes the scores of
+// one query group after another as route_exact_score does (a lane per key, the sums of the score
+// expansion over the wave), the logit in four partial sums.  A group of more keys than fit the
+// 48 KB of LDS reads them from memory.
+template <int D>
+constexpr int rescore_keys() { return 49152 / (D * 2 + 16); }  // keys staged in LDS (48 KB)
+template <int D>
+__global__ __launch_bounds__(256) void route_rescore_kernel(
+    unsigned long long* __restrict__ rbits, const void* __restrict__ Kp, int N, int Nv,
+    const double* __restrict__ qbar, const double* __restrict__ lbar, const double* __restrict__ vbar,
+    const double* __restrict__ shift, const double* __restrict__ vstat, const int* __restrict__ kv_off,
+    const int* __restrict__ n_kv, int Cq, int Ck, int G, double* __restrict__ scores, double* __restrict__ serr) {
+  constexpr int PC = D / 8;  // 16-byte pieces per key row
+  constexpr int KR = rescore_keys<D>(), KSTR = PC + 1;  // key rows padded by 16 bytes in LDS
+  __shared__ __attribute__((aligned(16))) ru32x4_t ks[KR * KSTR];
+  __shared__ double kst[KR][2];
+  __shared__ __attribute__((aligned(16))) double qs[4][D];
+  __shared__ int list[1024];
+  __shared__ int nreq;
+  const int b = blockIdx.x, hd = blockIdx.y, hk = hd / G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (b >= n_kv[hk]) return;
+  const int W = (Cq + 63) / 64;
+  unsigned long long* bits = rbits + (size_t(hd) * Ck + b) * W;
+  if (threadIdx.x < 64) {  // wave 0: lane i takes request word i (W <= 16)
+    unsigned long long m = lane < W ? bits[lane] : 0ull;
+    if (m) bits[lane] = 0ull;
+    const int c = __popcll(m);
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int k = incl - c;
+    while (m) {
+      list[k++] = lane * 64 + __ffsll((long long)m) - 1;
+      m &= m - 1;
+    }
+    if (lane == 63) nreq = incl;
+  }
+  __syncthreads();
+  const int n = nreq;
+  if (n == 0) return;
+  const int k0 = kv_off[size_t(hk) * (Ck + 1) + b], k1 = kv_off[size_t(hk) * (Ck + 1) + b + 1];
+  const int nk = k1 - k0;
+  const bool staged = nk <= KR;
+  const ru32x4_t* Kg = static_cast<const ru32x4_t*>(Kp) + (int64_t(hk) * N + k0) * PC;
+  if (staged) {
+    for (int e = threadIdx.x; e < nk * PC; e += 256) ks[(e / PC) * KSTR + e % PC] = Kg[e];
+    for (int j = threadIdx.x; j < nk; j += 256) {
+      kst[j][0] = vstat[(size_t(hk) * Nv + k0 + j) * 4];
+      kst[j][1] = vstat[(size_t(hk) * Nv + k0 + j) * 4 + 1];
+    }
+  }
+  const double inv = 1.0 / sqrt(double(D));
+  double vn = 0.0;  // |vbar_b|^2, the same for every request
+  for (int c = lane; c < D; c += 64) {
+    const double y = vbar[(size_t(hk) * Ck + b) * D + c];
+    vn = fma(y, y, vn);
+  }
+  vn = wave_allsum_d(vn);
+  __syncthreads();
+  for (int r = w; r < n; r += 4) {
+    const int a = list[r];
+    for (int c = lane; c < D; c += 64) qs[w][c] = qbar[(size_t(hd) * Cq + a) * D + c];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const double m = shift[size_t(hd) * Cq + a];
+    double s1 = 0.0, s2 = 0.0;
+    for (int j0 = 0; j0 < nk; j0 += 64) {
+      const int j = min(j0 + lane, nk - 1);
+      double uw_x, uw_y;
+      if (staged) {
+        uw_x = kst[j][0];
+        uw_y = kst[j][1];
+      } else {
+        uw_x = vstat[(size_t(hk) * Nv + k0 + j) * 4];
+        uw_y = vstat[(size_t(hk) * Nv + k0 + j) * 4 + 1];
       }
+      // the logit in four interleaved partial sums (a short dependency chain per lane)
+      double lp[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < PC; ++i) {
+        const ru32x4_t raw = staged ? ks[j * KSTR + i] : Kg[int64_t(j) * PC + i];
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          lp[i & 3] = fma(qs[w][i * 8 + 2 * h], double(__uint_as_float(wd[h] << 16)), lp[i & 3]);
+          lp[i & 3] = fma(qs[w][i * 8 + 2 * h + 1], double(__uint_as_float(wd[h] & 0xFFFF0000u)), lp[i & 3]);
+        }
+      }
+      const double l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+      if (j0 + lane < nk) {
+        const double Ej = exp(fma(l, inv, -m));
+        s1 = fma(Ej, uw_x, s1);
+        s2 = fma(Ej * Ej, uw_y, s2);
+      }
+    }
+    s1 = wave_allsum_d(s1);
+    s2 = wave_allsum_d(s2);
+    const double g = double(nk);
+    const size_t at = (size_t(hd) * Cq + a) * Ck + b;
+    const double A = exp(lbar[at] - m);
+    if (lane == 0) {
+      scores[at] = A * A * vn - 2.0 * A * s1 / g + s2 / g;
+      serr[at] = 0.0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const int64_t ga = q_off[size_t(hd) * (Cq + 1) + a + 1] - q_off[size_t(hd) * (Cq + 1) + a];
-  emit_prefix<E>(id, nkv, off, Tk, lane, n_text, out, sel_cnt + size_t(hd) * (Cq + 1) + a, ga, pairs + hd,
-                 gstat + hd * 8 + 0);
 }
 
 __global__ void zero_i64_kernel(int64_t* p, int n) {
@@ -1398,26 +1456,47 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
     else fast(route_score_fast_kernel<64>, route_fast_smem<64>());
     SPR_CHECK_LAUNCH();
     const bool keep = out.scores || out.score_err;
-    double* keep_s = keep ? scores : nullptr;
-    double* keep_e = keep ? serr : nullptr;
-    auto res = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, scores, serr, keep_s, keep_e, part.Kp, N, Nv, part.qbar,
-                         lbar, part.vbar, shift, vstat, part.kv_off, part.q_off, part.n_q, part.n_kv, p.Cq, p.Ck, G,
-                         desc.n_text, Tk, out.sel_cnt, out.sel_kv, out.pairs, gstat);
+    // resolve in three phases with the fp64 rescoring of the requested pairs between them
+    unsigned long long* rbits = ws_ptr<unsigned long long>(ws, L.rr_bits);
+    int* rorder = ws_ptr<int>(ws, L.rr_order);
+    int* rnin = ws_ptr<int>(ws, L.rr_nin);
+    const int W = ceil_div(p.Cq, 64);
+    const int64_t nbits = int64_t(BH) * p.Ck * W;
+    hipLaunchKernelGGL(zero_i64_kernel, dim3(unsigned(ceil_div64(nbits, 256))), dim3(256), 0, st,
+                       reinterpret_cast<int64_t*>(rbits), int(nbits));
+    auto rescore = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(p.Ck, BH), dim3(256), 0, st, rbits, part.Kp, N, Nv, part.qbar, lbar, part.vbar,
+                         shift, vstat, part.kv_off, part.n_kv, p.Cq, p.Ck, G, scores, serr);
     };
+    auto phases = [&](auto k0, auto k1, auto k2, auto rk) {
+      auto ph = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, scores, serr, keep, part.kv_off, part.q_off, part.n_q,
+                           part.n_kv, p.Cq, p.Ck, G, desc.n_text, Tk, rbits, rorder, rnin, out.sel_cnt, out.sel_kv,
+                           out.pairs, gstat);
+      };
+      ph(k0);
+      rescore(rk);
+      ph(k1);
+      rescore(rk);
+      ph(k2);
+    };
+#define SPR_RESOLVE(E, D)                                                                                 \
+  phases(route_resolve_kernel<0, E, D>, route_resolve_kernel<1, E, D>, route_resolve_kernel<2, E, D>, \
+         route_rescore_kernel<D>)
     if (d == 128) {
-      if (p.Ck <= 64) res(route_resolve_kernel<1, DT, 128>);
-      else if (p.Ck <= 128) res(route_resolve_kernel<2, DT, 128>);
-      else if (p.Ck <= 256) res(route_resolve_kernel<4, DT, 128>);
-      else if (p.Ck <= 512) res(route_resolve_kernel<8, DT, 128>);
-      else res(route_resolve_kernel<16, DT, 128>);
+      if (p.Ck <= 64) SPR_RESOLVE(1, 128);
+      else if (p.Ck <= 128) SPR_RESOLVE(2, 128);
+      else if (p.Ck <= 256) SPR_RESOLVE(4, 128);
+      else if (p.Ck <= 512) SPR_RESOLVE(8, 128);
+      else SPR_RESOLVE(16, 128);
     } else {
-      if (p.Ck <= 64) res(route_resolve_kernel<1, DT, 64>);
-      else if (p.Ck <= 128) res(route_resolve_kernel<2, DT, 64>);
-      else if (p.Ck <= 256) res(route_resolve_kernel<4, DT, 64>);
-      else if (p.Ck <= 512) res(route_resolve_kernel<8, DT, 64>);
-      else res(route_resolve_kernel<16, DT, 64>);
+      if (p.Ck <= 64) SPR_RESOLVE(1, 64);
+      else if (p.Ck <= 128) SPR_RESOLVE(2, 64);
+      else if (p.Ck <= 256) SPR_RESOLVE(4, 64);
+      else if (p.Ck <= 512) SPR_RESOLVE(8, 64);
+      else SPR_RESOLVE(16, 64);
     }
+#undef SPR_RESOLVE
   } else {
     if (d == 128) {
       allow_lds(route_score_kernel<DT, 128>, route_score_smem<128>());
