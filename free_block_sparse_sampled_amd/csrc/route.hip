@@ -1202,13 +1202,26 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
   }
   vn = wave_allsum_d(vn);
   __syncthreads();
+  // the next request's centroid, shift and centroid logit are loaded while this one is scored
+  constexpr int QPL = D / 64;  // centroid coordinates per lane
+  double qn[QPL], mn = 0.0, lbn = 0.0;
+  auto fetch = [&](int r) {
+    const int a = list[r];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) qn[u] = qbar[(size_t(hd) * Cq + a) * D + lane + 64 * u];
+    mn = shift[size_t(hd) * Cq + a];
+    lbn = lbar[(size_t(hd) * Cq + a) * Ck + b];
+  };
+  if (w < n) fetch(w);
   for (int r = w; r < n; r += 4) {
     const int a = list[r];
-    for (int c = lane; c < D; c += 64) qs[w][c] = qbar[(size_t(hd) * Cq + a) * D + c];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) qs[w][lane + 64 * u] = qn[u];
+    const double m = mn, lb = lbn;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const double m = shift[size_t(hd) * Cq + a];
+    if (r + 4 < n) fetch(r + 4);
     double s1 = 0.0, s2 = 0.0;
     for (int j0 = 0; j0 < nk; j0 += 64) {
       const int j = min(j0 + lane, nk - 1);
@@ -1243,7 +1256,7 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
     s2 = wave_allsum_d(s2);
     const double g = double(nk);
     const size_t at = (size_t(hd) * Cq + a) * Ck + b;
-    const double A = exp(lbar[at] - m);
+    const double A = exp(lb - m);
     if (lane == 0) {
       scores[at] = A * A * vn - 2.0 * A * s1 / g + s2 / g;
       serr[at] = 0.0;
