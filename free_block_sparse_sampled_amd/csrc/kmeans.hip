@@ -25,6 +25,7 @@ namespace spr {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Coordinates are padded to RP = 64 (ranks up to 64) or 128 (rank 128, the raw 128-dimensional
 // activations of the semantic partition) for the MFMA screening; the mean point is stored with
@@ -201,9 +202,11 @@ __global__ __launch_bounds__(1024) void km_init_kernel(const double* __restrict_
   }
 }
 
-// Screening pass.  A wave owns 64 points (4 tiles of 16); centres stream through LDS in
-// chunks of 256.  The MFMA computes D^T tiles (16 centres x 16 points), so a lane holds four
-// centres of one point and keeps that point's best value, its index and the second best.
+// Screening pass.  A wave owns 64 points (2 tiles of 32); centres stream through LDS in chunks
+// of 256.  v_mfma_f32_32x32x16_f16 computes D^T tiles (32 centres x 32 points) as three split
+// products (hi hi, hi lo, lo hi): lane l holds 16 centres (rows 8 q + 4 (l / 32) + i, q, i < 4) of
+// point l % 32 and keeps that point's best value, its index and the second best; lanes l and
+// l ^ 32 hold the other 16 centres of the same point and are merged at the end.
 template <int KS, int RP>
 __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Float16* __restrict__ xh,
                                                         const _Float16* __restrict__ xl,
@@ -213,34 +216,35 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
                                                         const float* __restrict__ cn2,
                                                         const double* __restrict__ ctrl, int* __restrict__ lab_new,
                                                         int* __restrict__ rq_count, int* __restrict__ rq_list) {
-  constexpr int CROW = crow(RP);
+  constexpr int CROW = crow(RP), K16 = RP / 16;  // LDS row stride, 16-column steps
   extern __shared__ __attribute__((aligned(16))) char smem[];
   _Float16* Ch = reinterpret_cast<_Float16*>(smem);
   _Float16* Cl = Ch + KC * CROW;
   float* cns = reinterpret_cast<float*>(Cl + KC * CROW);
   const int hd = blockIdx.y;
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, r16 = lane & 15;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int p0 = blockIdx.x * 256 + w * 64;
-  f16x8_t bh[4][KS], bl[4][KS];
+  // B fragments: point p0 + 32 pt + l32, columns 16 ks + 8 h .. + 7 of the hi and lo slices
+  f16x8_t bh[2][K16], bl[2][K16];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    const int j = p0 + pt * 16 + r16;
+  for (int pt = 0; pt < 2; ++pt) {
+    const int j = p0 + pt * 32 + l32;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < K16; ++ks) {
       uint4 uh = make_uint4(0, 0, 0, 0), ul = make_uint4(0, 0, 0, 0);
       if (j < n) {
-        uh = *reinterpret_cast<const uint4*>(xh + (size_t(hd) * n + j) * RP + ks * 32 + 8 * g);
-        ul = *reinterpret_cast<const uint4*>(xl + (size_t(hd) * n + j) * RP + ks * 32 + 8 * g);
+        uh = *reinterpret_cast<const uint4*>(xh + (size_t(hd) * n + j) * RP + ks * 16 + 8 * h);
+        ul = *reinterpret_cast<const uint4*>(xl + (size_t(hd) * n + j) * RP + ks * 16 + 8 * h);
       }
       bh[pt][ks] = as_f16x8(uh);
       bl[pt][ks] = as_f16x8(ul);
     }
   }
-  float b1[4], b2[4];
-  int i1[4];
+  float b1[2], b2[2];
+  int i1[2];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
+  for (int pt = 0; pt < 2; ++pt) {
     b1[pt] = INFINITY;
     b2[pt] = INFINITY;
     i1[pt] = 0;
@@ -262,31 +266,35 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
     }
     for (int e = t; e < KC; e += 256) cns[e] = e < cc ? cn2[size_t(hd) * C + c0 + e] : INFINITY;
     __syncthreads();
-    const int nblk = (cc + 15) >> 4;
+    const int nblk = (cc + 31) >> 5;
     for (int cb = 0; cb < nblk; ++cb) {
-      f16x8_t ah[KS], al[KS];
+      // A fragments: centre c0 + 32 cb + l32, columns 16 ks + 8 h .. + 7
+      f16x8_t ah[K16], al[K16];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        ah[ks] = as_f16x8(*reinterpret_cast<const uint4*>(Ch + (cb * 16 + r16) * CROW + ks * 32 + 8 * g));
-        al[ks] = as_f16x8(*reinterpret_cast<const uint4*>(Cl + (cb * 16 + r16) * CROW + ks * 32 + 8 * g));
+      for (int ks = 0; ks < K16; ++ks) {
+        ah[ks] = as_f16x8(*reinterpret_cast<const uint4*>(Ch + (cb * 32 + l32) * CROW + ks * 16 + 8 * h));
+        al[ks] = as_f16x8(*reinterpret_cast<const uint4*>(Cl + (cb * 32 + l32) * CROW + ks * 16 + 8 * h));
       }
-      float cv[4];
+      float cv[16];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) cv[v] = cns[cb * 16 + 4 * g + v];
+      for (int q = 0; q < 4; ++q) {
+        const float4 c4 = *reinterpret_cast<const float4*>(cns + cb * 32 + 8 * q + 4 * h);
+        cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
+      }
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < 2; ++pt) {
+        f32x16_t acc = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh[pt][ks], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl[pt][ks], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh[pt][ks], acc, 0, 0, 0);
+        for (int ks = 0; ks < K16; ++ks) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[ks], bh[pt][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[ks], bl[pt][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[ks], bh[pt][ks], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          // branch-free running best / index / second best
+        for (int v = 0; v < 16; ++v) {
+          // branch-free running best / index / second best (centres in ascending index)
           const float val = fmaf(-2.f, acc[v], cv[v]);
-          const int m = c0 + cb * 16 + 4 * g + v;
+          const int m = c0 + cb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
           b2[pt] = fminf(b2[pt], fmaxf(b1[pt], val));
           i1[pt] = val < b1[pt] ? m : i1[pt];
           b1[pt] = fminf(b1[pt], val);
@@ -296,12 +304,11 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
   }
   const double cmax = ctrl[hd * CTRL + C_CMAX];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    // merge the four lanes of a point (their centre subsets are disjoint)
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float ob1 = __shfl_xor(b1[pt], o), ob2 = __shfl_xor(b2[pt], o);
-      const int oi = __shfl_xor(i1[pt], o);
+  for (int pt = 0; pt < 2; ++pt) {
+    // merge the two lanes of a point (their centre subsets are disjoint)
+    {
+      const float ob1 = __shfl_xor(b1[pt], 32), ob2 = __shfl_xor(b2[pt], 32);
+      const int oi = __shfl_xor(i1[pt], 32);
       if (ob1 < b1[pt] || (ob1 == b1[pt] && oi < i1[pt])) {
         b2[pt] = fminf(ob2, b1[pt]);
         b1[pt] = ob1;
@@ -310,8 +317,9 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
         b2[pt] = fminf(b2[pt], ob1);
       }
     }
-    const int j = p0 + pt * 16 + r16;
-    if (g == 0 && j < n) {
+    const int j = p0 + pt * 32 + l32;
+    bool queue = false;
+    if (h == 0 && j < n) {
       // bound on |screened - exact| squared distance (scaled units): cross-term error of
       // the split product with fp32 sums, plus fp32 rounding of norms and combination;
       // doubled for safety.  Decided when the runner-up is more than twice that away.
@@ -321,10 +329,15 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
                        1e-12 * (xn + cmax) * (xn + cmax);
       const bool decided = double(b2[pt]) - double(b1[pt]) > 2.0 * E;
       lab_new[size_t(hd) * n + j] = decided ? i1[pt] : -1;
-      if (!decided) {
-        const int k = atomicAdd(rq_count + hd, 1);
-        rq_list[size_t(hd) * n + k] = j;
-      }
+      queue = !decided;
+    }
+    // the undecided points of the wave join the rescan queue with one atomic
+    const unsigned long long qm = __ballot(queue);
+    if (qm) {
+      int base = 0;
+      if (lane == __ffsll((long long)qm) - 1) base = atomicAdd(rq_count + hd, __popcll(qm));
+      base = __shfl(base, __ffsll((long long)qm) - 1);
+      if (queue) rq_list[size_t(hd) * n + base + __popcll(qm & ((1ull << lane) - 1))] = j;
     }
   }
 }
@@ -629,7 +642,7 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
   allow_lds(km_screen_kernel<KS, RP>, sm);
   hipLaunchKernelGGL((km_screen_kernel<KS, RP>), dim3(ceil_div(a.n, 256), a.BH), dim3(256), sm, st, a.n, a.C, xh, xl,
                      a.xnrm, ch, cl, a.cn2, a.ctrl, a.lab_new, a.rq_count, a.rq_list);
-  hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(16, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
+  hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(64, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
                      a.rq_count, a.rq_list, a.lab_new);
   hipLaunchKernelGGL(km_accum_kernel<R>, dim3(a.nblk, a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent, a.lab_new,
                      a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
