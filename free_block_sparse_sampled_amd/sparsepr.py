@@ -406,6 +406,7 @@ class SparsePR:
         self.head_status = torch.empty((B * H,), dtype=torch.int32, device=dev)
         self.fit_state = torch.empty((B * H, 3 * d + d * d), dtype=torch.float64, device=dev) if diagnostics else None
         self.warm_iters = 2  # k-means iteration limit of later calls (Table C.1)
+        self.side = None     # stream of the exact probes, beside the sparse attention
 
     def partition(self, q, k, v, warm: bool = False):
         """warm: later call of App. C.1 from this object's previous partition (in place), with
@@ -429,10 +430,25 @@ class SparsePR:
         sparsepr_fit_correct(self.desc, self.cfg, self.part, self.route, self.o_sp, self.o_probe, self.out,
                              self.head_status, self.ws, self.fit_state)
 
+    def probes_beside(self, q, k, v):
+        """Start the exact probes on a second stream (default priority) once the routing on the
+        current stream is done; they need only the inputs and the probe rows, and run beside the
+        sparse attention.  ``join`` makes the current stream wait for them."""
+        main = torch.cuda.current_stream()
+        if self.side is None:
+            self.side = torch.cuda.Stream(device=q.device)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self.probe_exact(q, k, v)
+
+    def join(self):
+        torch.cuda.current_stream().wait_stream(self.side)
+
     def run(self, q, k, v, warm: bool = False) -> torch.Tensor:
         self.partition(q, k, v, warm)
         self.route_()
+        self.probes_beside(q, k, v)
         self.attn_sparse()
-        self.probe_exact(q, k, v)
+        self.join()
         self.fit_correct()
         return self.out
