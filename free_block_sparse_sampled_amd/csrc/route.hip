@@ -1330,18 +1330,33 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int* __restrict
   const int r0 = q_off[size_t(hd) * (Cq + 1) + a], r1 = q_off[size_t(hd) * (Cq + 1) + a + 1];
   const int* pm = q_perm + size_t(hd) * Nv;
   const double* dd = qdist + size_t(hd) * Nv;
-  for (int p = r0 + threadIdx.x; p < r1; p += 256) {
-    const int i = pm[p];
-    const double di = dd[i];
+  // the members' rows and distances in LDS (groups of up to kSelStage rows; larger ones rank
+  // from memory)
+  constexpr int kSelStage = 1024;
+  __shared__ double sd[kSelStage];
+  __shared__ int si[kSelStage];
+  const int n = r1 - r0;
+  const bool staged = n <= kSelStage;
+  if (staged) {
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int i = pm[r0 + e];
+      si[e] = i;
+      sd[e] = dd[i];
+    }
+    __syncthreads();
+  }
+  for (int p = threadIdx.x; p < n; p += 256) {
+    const int i = staged ? si[p] : pm[r0 + p];
+    const double di = staged ? sd[p] : dd[i];
     int rank = 0;
-    for (int o = r0; o < r1; ++o) {
-      const int io = pm[o];
-      const double dx = dd[io];
+    for (int o = 0; o < n; ++o) {
+      const int io = staged ? si[o] : pm[r0 + o];
+      const double dx = staged ? sd[o] : dd[io];
       rank += (dx < di) || (dx == di && io < i);
     }
     if (rank < m) {
       probe_idx[size_t(hd) * M + po + rank] = i;
-      probe_w[size_t(hd) * M + po + rank] = double(r1 - r0) / double(m);
+      probe_w[size_t(hd) * M + po + rank] = double(n) / double(m);
     }
   }
 }
