@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--out-rank", type=int, default=0, help="output truncation rank (App. D.3); 0: none")
     ap.add_argument("--partition-mode", choices=["response", "semantic", "key_response"], default="response",
                     help="partition construction (Sec. 3.1, Table 2); the operator's is response")
+    ap.add_argument("--sweep", choices=["none", "joint"], default="none",
+                    help="instead of the headline: the joint text+video trade-off sweep, error and throughput "
+                         "at densities 0.10/0.22/0.35/0.50 x probe budgets 64/256/1024 (one JSON line)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for traffic counters)")
     return ap.parse_args()
@@ -178,6 +181,9 @@ def cpu_baseline(cfg, opc, warm, warm_iters, step):
                                     "sparse_only_mean": round(float(e_sp.mean()), 5)}}
 
 
+_INPUTS = {}  # device inputs of the last workload measured
+
+
 def measure(args, name, headline):
     """Time the operator on workload ``name``; the full record for the headline workload, a
     compact one for the secondary workload."""
@@ -199,12 +205,19 @@ def measure(args, name, headline):
                              partition_mode=args.partition_mode)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     # two input sets of the same heads (consecutive calls: same positions, fresh noise); calls
-    # alternate between them so that every later call sees inputs that differ from the last one
-    inputs = []
-    for st in (0, 1):
-        q, k, v = batch_inputs(cfg, step=st)
-        inputs.append(tuple(torch.from_numpy(x).to(dt).cuda() for x in (q, k, v)))
-        del q, k, v
+    # alternate between them so that every later call sees inputs that differ from the last one.
+    # The points of a sweep differ only in density and probe budget and share the inputs.
+    key = (cfg.name, cfg.B, cfg.H, cfg.Hkv, cfg.grid, cfg.n_text, cfg.d, cfg.dtype)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        torch.cuda.empty_cache()
+        inputs = []
+        for st in (0, 1):
+            q, k, v = batch_inputs(cfg, step=st)
+            inputs.append(tuple(torch.from_numpy(x).to(dt).cuda() for x in (q, k, v)))
+            del q, k, v
+        _INPUTS[key] = inputs
+    inputs = _INPUTS[key]
     op = spr.SparsePR(inputs[0][0], opc, n_text=cfg.n_text)
     stream = torch.cuda.current_stream()
     if headline and args.calib_copy_mb:
@@ -380,8 +393,42 @@ def measure(args, name, headline):
             cb["oracle_err_vs_dense"]["gpu_sparse_only_mean"] = round(float(err_rows0[1][rows].mean()), 5)
         result["cpu_baseline"] = cb
     del op, inputs
+    if headline:
+        _INPUTS.clear()
     torch.cuda.empty_cache()
     return result
+
+
+SWEEP_RHO = (0.10, 0.22, 0.35, 0.50)
+SWEEP_M = (64, 256, 1024)
+
+
+def sweep_joint(args):
+    """Error and throughput of the joint text+video workload (B=2, H=24, 32760 video tokens on a
+    21x39x40 grid plus 256 text tokens, d=128, bf16) over target density x probe budget: for each
+    of the 12 points, the warm-call time, the dense-equivalent TFLOP/s, the speed-up over the dense
+    kernel, the executed density and the mean relative-L2 error per unprobed video row against
+    dense attention, corrected and sparse-only."""
+    import copy
+    points = []
+    for rho in SWEEP_RHO:
+        for M in SWEEP_M:
+            a = copy.copy(args)
+            a.rho, a.M = rho, M
+            t0 = time.perf_counter()
+            r = measure(a, "joint", False)
+            r = {"rho_target": rho, "M": M, **r}
+            points.append(r)
+            print(f"joint rho={rho} M={M}: {r['ms_per_call']} ms/call, speed-up {r.get('speedup_vs_dense_fa')}, "
+                  f"err {r.get('err_vs_dense')} ({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    _INPUTS.clear()
+    return {"metric": "ms/call & dense-equiv TFLOP/s vs density and probe budget; rel-L2 err vs dense",
+            "unit": "TFLOP/s (dense-equivalent attention, whole call)", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (seeded positional-Fourier Q/K + noise + sinks, Gaussian V; text tokens)",
+            "regime": "later calls (warm start), inputs alternating between two fresh-noise steps",
+            "config": {"workload": points[0]["workload"] if points else "joint"},
+            "sweep": points}
 
 
 def main():
@@ -390,6 +437,9 @@ def main():
         print(f"bench.py runs on one GPU only (the operator shards by head with no communication); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.sweep == "joint":
+        print(json.dumps(sweep_joint(args)))
+        return
     result = measure(args, args.config, True)
     if args.secondary not in ("none", "", args.config):
         result["secondary"] = measure(args, args.secondary, False)

@@ -292,10 +292,13 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          // branch-free running best / index / second best (centres in ascending index)
+          // branch-free running best / index / second best (centres in ascending index); with
+          // b1 <= b2 the new second best is the median of b1, b2 and the value.  The index is
+          // kept without the lane's 4 h, which is the same for all its centres (wave-uniform
+          // operand).
           const float val = fmaf(-2.f, acc[v], cv[v]);
-          const int m = c0 + cb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          b2[pt] = fminf(b2[pt], fmaxf(b1[pt], val));
+          const int m = c0 + cb * 32 + 8 * (v >> 2) + (v & 3);
+          b2[pt] = __builtin_amdgcn_fmed3f(b1[pt], b2[pt], val);
           i1[pt] = val < b1[pt] ? m : i1[pt];
           b1[pt] = fminf(b1[pt], val);
         }
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
   const double cmax = ctrl[hd * CTRL + C_CMAX];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
+    i1[pt] += 4 * h;
     // merge the two lanes of a point (their centre subsets are disjoint)
     {
       const float ob1 = __shfl_xor(b1[pt], 32), ob2 = __shfl_xor(b2[pt], 32);
@@ -399,95 +403,184 @@ __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const doub
   }
 }
 
-// Cost, label changes and Lloyd sums of the pass.  Each wave walks its 64 points in order with
-// one lane per coordinate: it adds x to a running sum that is flushed (fp64 atomics) when the
-// label changes, and (x - c_label)^2 to the lane's share of the cost.
-template <int R>
-__global__ __launch_bounds__(256) void km_accum_kernel(const double* __restrict__ feat, int n, int C,
-                                                       const double* __restrict__ cent,
-                                                       const int* __restrict__ lab_new, int* __restrict__ labels,
-                                                       double* __restrict__ jpart, int* __restrict__ cpart,
-                                                       const double* __restrict__ ctrl, double* __restrict__ sums,
-                                                       int* __restrict__ cnt, int nblk) {
-  __shared__ double red[32];
+// Cost, label changes and Lloyd sums of the pass, without atomics on the sums: the points are
+// counting-sorted by their new label (a histogram per slice of kSlicePts points, a scan per
+// head, a stable scatter), then one wave per centre adds its members' coordinates, one lane per
+// coordinate, in ascending point index, and their (x - c)^2 to the pass cost.  Every sum is
+// thus formed in the same order on every run.
+constexpr int kSlicePts = 4096;  // points per histogram / scatter block (1024 threads)
+
+// Label histogram of one slice, its count of changed labels, and the labels of the pass.
+__global__ __launch_bounds__(1024) void km_hist_kernel(int n, int C, const int* __restrict__ lab_new,
+                                                       int* __restrict__ labels, const double* __restrict__ ctrl,
+                                                       int* __restrict__ hist, int* __restrict__ cpart, int nsl) {
+  __shared__ int h[1024];  // C <= 1024
   __shared__ int64_t redi[32];
   const int hd = blockIdx.y;
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  const bool valid = j < n;
-  int lab = 0, changed = 0;
-  if (valid) {
-    lab = lab_new[size_t(hd) * n + j];
-    int* lp = labels + size_t(hd) * n + j;
-    changed = (*lp != lab);
-    *lp = lab;
+  const int t = threadIdx.x;
+  if (t < C) h[t] = 0;
+  __syncthreads();
+  int changed = 0;
+  const int j0 = blockIdx.x * kSlicePts;
+  for (int i = t; i < kSlicePts; i += 1024) {
+    const int j = j0 + i;
+    if (j < n) {
+      const int lab = lab_new[size_t(hd) * n + j];
+      int* lp = labels + size_t(hd) * n + j;
+      changed += *lp != lab;
+      *lp = lab;
+      atomicAdd(&h[lab], 1);
+    }
   }
-  // EPL coordinates per lane: lane + 64 q, q < EPL
-  constexpr int EPL = (R + 63) / 64;
-  const int lane = threadIdx.x & 63;
-  const int wbase = blockIdx.x * 256 + (threadIdx.x & ~63);
-  const int L = valid ? lab : -1;
-  int cur = __shfl(L, 0);
-  double acc[EPL], cc[EPL], jsq = 0.0;
+  const int64_t cs = block_sum_i64(changed, redi);  // (its barriers also complete the histogram)
+  if (t < C) hist[(size_t(hd) * nsl + blockIdx.x) * C + t] = h[t];
+  if (t == 0) cpart[size_t(hd) * nsl + blockIdx.x] = int(cs);
+}
+
+// Per head and centre: the member count, the first position of its members in the sorted order
+// (centres ascending), and in place of each slice's count the position of that slice's first
+// member.  One thread per centre.
+__global__ __launch_bounds__(1024) void km_scan_kernel(int C, int nsl, const double* __restrict__ ctrl,
+                                                       int* __restrict__ hist, int* __restrict__ cnt,
+                                                       int* __restrict__ cstart) {
+  __shared__ int scan[32];
+  const int hd = blockIdx.x;
+  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  const int c = threadIdx.x;
+  int* hc = hist + size_t(hd) * nsl * C + c;
+  int tot = 0;
+  if (c < C)
+    for (int b = 0; b < nsl; ++b) tot += hc[size_t(b) * C];
+  int all;
+  const int s0 = block_exscan_i(c < C ? tot : 0, scan, &all);
+  if (c < C) {
+    int run = s0;
+    for (int b = 0; b < nsl; ++b) {
+      const int v = hc[size_t(b) * C];
+      hc[size_t(b) * C] = run;
+      run += v;
+    }
+    cnt[size_t(hd) * C + c] = tot;
+    cstart[size_t(hd) * C + c] = s0;
+  }
+}
+
+// Stable scatter of one slice: order[position] = point, members of a centre in ascending point
+// index.  Ranks inside a wave come from ballots, ranks across the 16 waves of a 1024-point chunk
+// from per-wave counts in LDS.
+__global__ __launch_bounds__(1024) void km_scatter_kernel(int n, int C, const int* __restrict__ lab_new,
+                                                          const double* __restrict__ ctrl,
+                                                          const int* __restrict__ hist, int nsl,
+                                                          int* __restrict__ order) {
+  extern __shared__ int sc_sm[];
+  int* cursor = sc_sm;      // [C]
+  int* wcnt = sc_sm + C;    // [16][C]
+  const int hd = blockIdx.y;
+  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (t < C) cursor[t] = hist[(size_t(hd) * nsl + blockIdx.x) * C + t];
+  for (int e = t; e < 16 * C; e += 1024) wcnt[e] = 0;
+  __syncthreads();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int j0 = blockIdx.x * kSlicePts;
+  for (int c0 = 0; c0 < kSlicePts && j0 + c0 < n; c0 += 1024) {
+    const int j = j0 + c0 + t;
+    const bool valid = j < n;
+    const int L = valid ? lab_new[size_t(hd) * n + j] : -1;
+    unsigned long long todo = __ballot(valid);
+    int myrank = 0, mycnt = 0;
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int Ll = __shfl(L, leader);
+      const unsigned long long msk = __ballot(L == Ll);
+      if (L == Ll) {
+        myrank = __popcll(msk & lt);
+        mycnt = __popcll(msk);
+      }
+      todo &= ~msk;
+    }
+    if (valid && myrank == 0) wcnt[w * C + L] = mycnt;
+    __syncthreads();
+    int before = 0, after = 0, pos = 0;
+    if (valid) {
+      for (int w2 = 0; w2 < w; ++w2) before += wcnt[w2 * C + L];
+      for (int w2 = w + 1; w2 < 16; ++w2) after += wcnt[w2 * C + L];
+      pos = cursor[L] + before + myrank;
+    }
+    __syncthreads();
+    if (valid) {
+      if (myrank == mycnt - 1 && after == 0) cursor[L] = pos + 1;
+      if (myrank == 0) wcnt[w * C + L] = 0;
+      order[size_t(hd) * n + pos] = j;
+    }
+    __syncthreads();
+  }
+}
+
+// Sums and cost per centre, one wave per centre: members in sorted order, their loads issued
+// PB at a time ahead of the additions.
+template <int R>
+__global__ __launch_bounds__(256) void km_reduce_kernel(const double* __restrict__ feat, int n, int C,
+                                                        const double* __restrict__ cent,
+                                                        const int* __restrict__ order, const int* __restrict__ cnt,
+                                                        const int* __restrict__ cstart,
+                                                        const double* __restrict__ ctrl, double* __restrict__ sums,
+                                                        double* __restrict__ jpart) {
+  constexpr int EPL = (R + 63) / 64, PB = 8;
+  const int hd = blockIdx.y;
+  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  const int c = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  if (c >= C) return;
+  const int k = cnt[size_t(hd) * C + c];
+  const int* od = order + size_t(hd) * n + cstart[size_t(hd) * C + c];
+  const double* fh = feat + size_t(hd) * n * R;
+  double acc[EPL], cc[EPL], jl = 0.0;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     const int e = lane + 64 * q;
     acc[q] = 0.0;
-    cc[q] = (e < R && cur >= 0) ? cent[(size_t(hd) * C + cur) * R + e] : 0.0;
+    cc[q] = e < R ? cent[(size_t(hd) * C + c) * R + e] : 0.0;
   }
-  int run = 0;
-  for (int p = 0; p < 64; ++p) {
-    const int Lp = __shfl(L, p);
-    if (Lp < 0) break;
-    if (Lp != cur) {
+  for (int i0 = 0; i0 < k; i0 += PB) {
+    double xb[PB][EPL];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int jj = i0 + i < k ? od[i0 + i] : 0;
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
         const int e = lane + 64 * q;
-        if (e < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + e, acc[q]);
-        acc[q] = 0.0;
+        xb[i][q] = (e < R && i0 + i < k) ? fh[size_t(jj) * R + e] : 0.0;
       }
-      if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
-      run = 0;
-      cur = Lp;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      if (i0 + i >= k) break;
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
         const int e = lane + 64 * q;
-        if (e < R) cc[q] = cent[(size_t(hd) * C + cur) * R + e];
+        if (e < R) {
+          acc[q] += xb[i][q];
+          const double d = xb[i][q] - cc[q];
+          jl = fma(d, d, jl);
+        }
       }
     }
+  }
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      const int e = lane + 64 * q;
-      if (e < R) {
-        const double x = feat[(size_t(hd) * n + wbase + p) * R + e];
-        acc[q] += x;
-        const double t = x - cc[q];
-        jsq = fma(t, t, jsq);
-      }
-    }
-    ++run;
+  for (int q = 0; q < EPL; ++q) {
+    const int e = lane + 64 * q;
+    if (e < R) sums[(size_t(hd) * C + c) * R + e] = acc[q];
   }
-  if (run > 0) {
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      const int e = lane + 64 * q;
-      if (e < R) atomicAdd(sums + (size_t(hd) * C + cur) * R + e, acc[q]);
-    }
-    if (lane == 0) atomicAdd(cnt + size_t(hd) * C + cur, run);
-  }
-  const double jsum = block_sum_d(jsq, red);
-  const int64_t csum = block_sum_i64(changed, redi);
-  if (threadIdx.x == 0) {
-    jpart[size_t(hd) * nblk + blockIdx.x] = jsum;
-    cpart[size_t(hd) * nblk + blockIdx.x] = int(csum);
-  }
+  jl = wave_sum_d(jl);
+  if (lane == 0) jpart[size_t(hd) * C + c] = jl;
 }
 
 // Stopping rule after a pass (one block per head): stop when the labels did not change, when
 // the cost fell by at most tol relative to the previous pass, or at max_iters.  The decision is
 // written to ctrl[C_STOPNOW]; km_update_kernel then moves the centres of heads that go on.
-__global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double tol, int nblk,
-                                                        const double* __restrict__ jpart,
+__global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double tol, int C,
+                                                        const double* __restrict__ jpart, int nsl,
                                                         const int* __restrict__ cpart, double* __restrict__ ctrl) {
   __shared__ double red[32];
   __shared__ int64_t redi[32];
@@ -495,10 +588,8 @@ __global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double to
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
   double js = 0.0;
   int64_t cs = 0;
-  for (int i = threadIdx.x; i < nblk; i += blockDim.x) {
-    js += jpart[size_t(hd) * nblk + i];
-    cs += cpart[size_t(hd) * nblk + i];
-  }
+  for (int i = threadIdx.x; i < C; i += blockDim.x) js += jpart[size_t(hd) * C + i];
+  for (int i = threadIdx.x; i < nsl; i += blockDim.x) cs += cpart[size_t(hd) * nsl + i];
   const double J = block_sum_d(js, red);
   const int64_t chg = block_sum_i64(cs, redi);
   if (threadIdx.x == 0) {
@@ -512,12 +603,12 @@ __global__ __launch_bounds__(256) void km_decide_kernel(int max_iters, double to
   }
 }
 
-// Centre update (members' mean; empty centres stay), reset of the sums, and the fp16 split of
-// the new centres for the next screening pass.  64 centres per block, one wave per centre row
+// Centre update (members' mean; empty centres stay) and the fp16 split of the new centres for
+// the next screening pass.  64 centres per block, one wave per centre row
 // at a time; the largest centre norm is combined with atomicMax on its (non-negative) bits.
 template <int RP>
 __global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __restrict__ cent,
-                                                        double* __restrict__ sums, int* __restrict__ cnt,
+                                                        const double* __restrict__ sums, const int* __restrict__ cnt,
                                                         double* __restrict__ ctrl, const double* __restrict__ mu,
                                                         _Float16* __restrict__ ch, _Float16* __restrict__ cl,
                                                         float* __restrict__ cn2, int* __restrict__ rq_count) {
@@ -541,7 +632,6 @@ __global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __
           c = sums[base * r + e] / double(k);
           cent[base * r + e] = c;
         }
-        sums[base * r + e] = 0.0;
         x = (c - mu[size_t(hd) * RPMAX + e]) * sc;
       }
       if (!stop) {
@@ -556,7 +646,6 @@ __global__ __launch_bounds__(256) void km_update_kernel(int C, int r, double* __
       if (lane == 0) cn2[base] = float(n2);
       cmax = fmax(cmax, sqrt(n2));
     }
-    if (lane == 0) cnt[base] = 0;
   }
   if (!stop && lane == 0 && cmax > 0.0)
     atomicMax(reinterpret_cast<unsigned long long*>(ctrl + hd * CTRL + C_CMAX),
@@ -581,12 +670,15 @@ bool kmeans_rank_supported(int r) { return r == 8 || r == 16 || r == 32 || r == 
 size_t kmeans_ws_bytes(int BH, int n, int C, int rmax) {
   size_t o = 0;
   auto take = [&](size_t b) { o += (b + 255) & ~size_t(255); };
-  const int nblk = ceil_div(n, 256);
+  const int nsl = ceil_div(n, kSlicePts);
   take(size_t(BH) * C * rmax * 8);  // sums
   take(size_t(BH) * C * 4);         // counts
   take(size_t(BH) * n * 4);         // new labels
-  take(size_t(BH) * nblk * 8);      // cost partials
-  take(size_t(BH) * nblk * 4);      // change partials
+  take(size_t(BH) * C * 8);         // cost partials (per centre)
+  take(size_t(BH) * nsl * 4);       // change partials (per slice)
+  take(size_t(BH) * nsl * C * 4);   // slice histograms, then slice positions
+  take(size_t(BH) * C * 4);         // first sorted position per centre
+  take(size_t(BH) * n * 4);         // points sorted by label
   take(size_t(BH) * CTRL * 8);      // control words
   const int RP = rpad(rmax);
   take(size_t(BH) * RPMAX * 8);     // mean point
@@ -610,12 +702,15 @@ KmArgs kmeans_carve(void* ws, int BH, int n, int C, int rmax) {
     o += (b + 255) & ~size_t(255);
     return p;
   };
-  const int nblk = ceil_div(n, 256);
+  const int nsl = ceil_div(n, kSlicePts);
   a.sums = reinterpret_cast<double*>(take(size_t(BH) * C * rmax * 8));
   a.cnt = reinterpret_cast<int*>(take(size_t(BH) * C * 4));
   a.lab_new = reinterpret_cast<int*>(take(size_t(BH) * n * 4));
-  a.jpart = reinterpret_cast<double*>(take(size_t(BH) * nblk * 8));
-  a.cpart = reinterpret_cast<int*>(take(size_t(BH) * nblk * 4));
+  a.jpart = reinterpret_cast<double*>(take(size_t(BH) * C * 8));
+  a.cpart = reinterpret_cast<int*>(take(size_t(BH) * nsl * 4));
+  a.hist = reinterpret_cast<int*>(take(size_t(BH) * nsl * C * 4));
+  a.cstart = reinterpret_cast<int*>(take(size_t(BH) * C * 4));
+  a.order = reinterpret_cast<int*>(take(size_t(BH) * n * 4));
   a.ctrl = reinterpret_cast<double*>(take(size_t(BH) * CTRL * 8));
   const int RP = rpad(rmax);
   a.mu = reinterpret_cast<double*>(take(size_t(BH) * RPMAX * 8));
@@ -627,7 +722,7 @@ KmArgs kmeans_carve(void* ws, int BH, int n, int C, int rmax) {
   a.cn2 = reinterpret_cast<float*>(take(size_t(BH) * C * 4));
   a.rq_count = reinterpret_cast<int*>(take(size_t(BH) * 4));
   a.rq_list = reinterpret_cast<int*>(take(size_t(BH) * n * 4));
-  a.nblk = nblk;
+  a.nsl = nsl;
   return a;
 }
 
@@ -644,10 +739,17 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
                      a.xnrm, ch, cl, a.cn2, a.ctrl, a.lab_new, a.rq_count, a.rq_list);
   hipLaunchKernelGGL(km_rescan_kernel<R>, dim3(64, a.BH), dim3(256), 0, st, a.n, a.C, a.feat, a.cent, a.ctrl,
                      a.rq_count, a.rq_list, a.lab_new);
-  hipLaunchKernelGGL(km_accum_kernel<R>, dim3(a.nblk, a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent, a.lab_new,
-                     a.labels, a.jpart, a.cpart, a.ctrl, a.sums, a.cnt, a.nblk);
-  hipLaunchKernelGGL(km_decide_kernel, dim3(a.BH), dim3(256), 0, st, a.max_iters, a.tol, a.nblk, a.jpart, a.cpart,
-                     a.ctrl);
+  hipLaunchKernelGGL(km_hist_kernel, dim3(a.nsl, a.BH), dim3(1024), 0, st, a.n, a.C, a.lab_new, a.labels, a.ctrl,
+                     a.hist, a.cpart, a.nsl);
+  hipLaunchKernelGGL(km_scan_kernel, dim3(a.BH), dim3(1024), 0, st, a.C, a.nsl, a.ctrl, a.hist, a.cnt, a.cstart);
+  const size_t ssm = size_t(17) * a.C * sizeof(int);
+  allow_lds(km_scatter_kernel, ssm);
+  hipLaunchKernelGGL(km_scatter_kernel, dim3(a.nsl, a.BH), dim3(1024), ssm, st, a.n, a.C, a.lab_new, a.ctrl, a.hist,
+                     a.nsl, a.order);
+  hipLaunchKernelGGL(km_reduce_kernel<R>, dim3(ceil_div(a.C, 4), a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent,
+                     a.order, a.cnt, a.cstart, a.ctrl, a.sums, a.jpart);
+  hipLaunchKernelGGL(km_decide_kernel, dim3(a.BH), dim3(256), 0, st, a.max_iters, a.tol, a.C, a.jpart, a.nsl,
+                     a.cpart, a.ctrl);
   hipLaunchKernelGGL(km_update_kernel<RP>, dim3(ceil_div(a.C, 64), a.BH), dim3(256), 0, st, a.C, a.r, a.cent,
                      a.sums, a.cnt, a.ctrl, a.mu, ch, cl, a.cn2, a.rq_count);
 }

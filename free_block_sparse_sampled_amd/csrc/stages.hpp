@@ -5,7 +5,7 @@
 namespace spr {
 
 struct KmArgs {
-  int BH, n, r, C, stage, max_iters, nblk;
+  int BH, n, r, C, stage, max_iters, nsl;  // nsl: slices of the label sort
   double tol;
   uint64_t seed;
   const double* feat;  // [BH][n][r] coordinates
@@ -19,6 +19,9 @@ struct KmArgs {
   int* lab_new;
   double* jpart;
   int* cpart;
+  int* hist;
+  int* cstart;
+  int* order;
   double* ctrl;
   double* mu;
   void* xh;

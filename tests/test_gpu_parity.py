@@ -713,3 +713,26 @@ def test_large_and_small_magnitude_values():
     rng = np.random.default_rng(4)
     for h in (0, 1):
         _lockstep_head(g, q, k, v, cfg, opc, 0, h, rng)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Cq", [48, 24])
+def test_sparse_tiles_of_large_query_groups(Cq):
+    """Query groups of 170 and 340 rows on average: most groups span several sparse tiles, and the
+    rows past a group's full tiles are offered for pairing with other groups.  Two heads of small
+    end to end against the oracle."""
+    cfg = config("small").with_(H=2, Cq=Cq)
+    assert cfg.Nv >= 96 * Cq
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    rows = np.unique(np.concatenate([np.arange(0, cfg.N, 5), np.arange(cfg.N - 100, cfg.N)]))
+    for h in (0, 1):
+        ref = O.sparsepr_head(q[0, h], k[0, h], v[0, h], p, head=h, rows=rows)
+        ref["lam"] = p.lam
+        if _oracle_is_tie_free(ref):
+            _compare_head(g, ref, h, cfg.Nv, cfg.N, cfg.n_text)
+        else:
+            _lockstep_head(g, q, k, v, cfg, opc, 0, h, np.random.default_rng(5), nrows=256)
