@@ -410,14 +410,15 @@ __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const doub
 // thus formed in the same order on every run.
 constexpr int kSlicePts = 4096;  // points per histogram / scatter block (1024 threads)
 
-// Label histogram of one slice, its count of changed labels, and the labels of the pass.
+// Label histogram of one slice, its count of changed labels, and the labels of the pass (the
+// compaction of the final labels passes no labels, ctrl or cpart).
 __global__ __launch_bounds__(1024) void km_hist_kernel(int n, int C, const int* __restrict__ lab_new,
                                                        int* __restrict__ labels, const double* __restrict__ ctrl,
                                                        int* __restrict__ hist, int* __restrict__ cpart, int nsl) {
   __shared__ int h[1024];  // C <= 1024
   __shared__ int64_t redi[32];
   const int hd = blockIdx.y;
-  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  if (ctrl && ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int t = threadIdx.x;
   if (t < C) h[t] = 0;
   __syncthreads();
@@ -427,15 +428,17 @@ __global__ __launch_bounds__(1024) void km_hist_kernel(int n, int C, const int* 
     const int j = j0 + i;
     if (j < n) {
       const int lab = lab_new[size_t(hd) * n + j];
-      int* lp = labels + size_t(hd) * n + j;
-      changed += *lp != lab;
-      *lp = lab;
+      if (labels) {
+        int* lp = labels + size_t(hd) * n + j;
+        changed += *lp != lab;
+        *lp = lab;
+      }
       atomicAdd(&h[lab], 1);
     }
   }
   const int64_t cs = block_sum_i64(changed, redi);  // (its barriers also complete the histogram)
   if (t < C) hist[(size_t(hd) * nsl + blockIdx.x) * C + t] = h[t];
-  if (t == 0) cpart[size_t(hd) * nsl + blockIdx.x] = int(cs);
+  if (t == 0 && cpart) cpart[size_t(hd) * nsl + blockIdx.x] = int(cs);
 }
 
 // Per head and centre: the member count, the first position of its members in the sorted order
@@ -466,18 +469,53 @@ __global__ __launch_bounds__(1024) void km_scan_kernel(int C, int nsl, const dou
   }
 }
 
+// Compaction of the final labels: empty centres dropped and the others renumbered in ascending
+// id (remap), group offsets, the group count and the empty-group status bit; in place of each
+// slice's counts the position of the slice's first member of every group.
+__global__ __launch_bounds__(1024) void km_compact_scan_kernel(int n, int C, int nsl, int* __restrict__ hist,
+                                                               int* __restrict__ remap, int* __restrict__ off,
+                                                               int* __restrict__ ngroups, int* __restrict__ gstat,
+                                                               int empty_bit) {
+  __shared__ int scan[32];
+  const int hd = blockIdx.x, c = threadIdx.x;
+  int* hc = hist + size_t(hd) * nsl * C + c;
+  int tot = 0;
+  if (c < C)
+    for (int b = 0; b < nsl; ++b) tot += hc[size_t(b) * C];
+  int ng, all;
+  const int newid = block_exscan_i(c < C && tot > 0 ? 1 : 0, scan, &ng);
+  const int s0 = block_exscan_i(c < C ? tot : 0, scan, &all);
+  if (c < C) {
+    int run = s0;
+    for (int b = 0; b < nsl; ++b) {
+      const int v = hc[size_t(b) * C];
+      hc[size_t(b) * C] = run;
+      run += v;
+    }
+    remap[size_t(hd) * C + c] = newid;
+    if (tot > 0) off[size_t(hd) * (C + 1) + newid] = s0;
+  }
+  if (c == 0) {
+    off[size_t(hd) * (C + 1) + ng] = n;
+    ngroups[hd] = ng;
+    if (ng < C) atomicOr(gstat + hd * 8 + 0, empty_bit);
+  }
+}
+
 // Stable scatter of one slice: order[position] = point, members of a centre in ascending point
-// index.  Ranks inside a wave come from ballots, ranks across the 16 waves of a 1024-point chunk
-// from per-wave counts in LDS.
+// index (for the compaction also the position of every point and its renumbered label).  Ranks
+// inside a wave come from ballots, ranks across the 16 waves of a 1024-point chunk from
+// per-wave counts in LDS.
 __global__ __launch_bounds__(1024) void km_scatter_kernel(int n, int C, const int* __restrict__ lab_new,
                                                           const double* __restrict__ ctrl,
                                                           const int* __restrict__ hist, int nsl,
-                                                          int* __restrict__ order) {
+                                                          int* __restrict__ order, int* __restrict__ pos_of,
+                                                          int* __restrict__ lab_c, const int* __restrict__ remap) {
   extern __shared__ int sc_sm[];
   int* cursor = sc_sm;      // [C]
   int* wcnt = sc_sm + C;    // [16][C]
   const int hd = blockIdx.y;
-  if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
+  if (ctrl && ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   if (t < C) cursor[t] = hist[(size_t(hd) * nsl + blockIdx.x) * C + t];
   for (int e = t; e < 16 * C; e += 1024) wcnt[e] = 0;
@@ -513,6 +551,8 @@ __global__ __launch_bounds__(1024) void km_scatter_kernel(int n, int C, const in
       if (myrank == mycnt - 1 && after == 0) cursor[L] = pos + 1;
       if (myrank == 0) wcnt[w * C + L] = 0;
       order[size_t(hd) * n + pos] = j;
+      if (pos_of) pos_of[size_t(hd) * n + j] = pos;
+      if (lab_c) lab_c[size_t(hd) * n + j] = remap[size_t(hd) * C + L];
     }
     __syncthreads();
   }
@@ -745,7 +785,7 @@ static void launch_pass(const KmArgs& a, hipStream_t st) {
   const size_t ssm = size_t(17) * a.C * sizeof(int);
   allow_lds(km_scatter_kernel, ssm);
   hipLaunchKernelGGL(km_scatter_kernel, dim3(a.nsl, a.BH), dim3(1024), ssm, st, a.n, a.C, a.lab_new, a.ctrl, a.hist,
-                     a.nsl, a.order);
+                     a.nsl, a.order, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(km_reduce_kernel<R>, dim3(ceil_div(a.C, 4), a.BH), dim3(256), 0, st, a.feat, a.n, a.C, a.cent,
                      a.order, a.cnt, a.cstart, a.ctrl, a.sums, a.jpart);
   hipLaunchKernelGGL(km_decide_kernel, dim3(a.BH), dim3(256), 0, st, a.max_iters, a.tol, a.C, a.jpart, a.nsl,
@@ -762,6 +802,21 @@ static void launch_prep(const KmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(km_init_kernel<RP>, dim3(a.BH), dim3(1024), 0, st, a.feat, a.n, a.r, a.C, a.seed, a.stage, a.mu,
                      a.cent, a.sums, a.cnt, a.ctrl, reinterpret_cast<_Float16*>(a.ch),
                      reinterpret_cast<_Float16*>(a.cl), a.cn2, a.rq_count, a.cent_given ? 1 : 0);
+}
+
+spr_status launch_compact(const KmArgs& a, int* lab_c, int* perm, int* pos_of, int* off, int* ngroups, int* gstat,
+                          int empty_bit, hipStream_t st) {
+  // the pass scratch is free once the passes are done: slice histograms in hist, remap in cstart
+  hipLaunchKernelGGL(km_hist_kernel, dim3(a.nsl, a.BH), dim3(1024), 0, st, a.n, a.C, a.labels, nullptr, nullptr,
+                     a.hist, nullptr, a.nsl);
+  hipLaunchKernelGGL(km_compact_scan_kernel, dim3(a.BH), dim3(1024), 0, st, a.n, a.C, a.nsl, a.hist, a.cstart, off,
+                     ngroups, gstat, empty_bit);
+  const size_t ssm = size_t(17) * a.C * sizeof(int);
+  allow_lds(km_scatter_kernel, ssm);
+  hipLaunchKernelGGL(km_scatter_kernel, dim3(a.nsl, a.BH), dim3(1024), ssm, st, a.n, a.C, a.labels, nullptr, a.hist,
+                     a.nsl, perm, pos_of, lab_c, a.cstart);
+  SPR_CHECK_LAUNCH();
+  return SPR_OK;
 }
 
 KmStatsTarget km_stats_target(const KmArgs& a) { return KmStatsTarget{a.mu, a.ctrl, RPMAX, CTRL, C_AMAX}; }

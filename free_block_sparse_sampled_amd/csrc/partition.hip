@@ -820,84 +820,6 @@ static int project_chunks(int rows, int BH) {
   return best;
 }
 
-// ------------------------------------------------------------------ compaction
-// One block of 1024 threads per head: drop empty clusters (renumber the rest in ascending
-// id), group offsets, and a stable counting-sort scatter that lists each group's members in
-// ascending original index.  Ranks inside a wave come from ballots, ranks across the 16
-// waves of a 1024-point chunk from per-wave counts in LDS.
-__global__ __launch_bounds__(1024) void km_compact_kernel(const int* __restrict__ lab_raw, int n, int C,
-                                                          int* __restrict__ lab_c, int* __restrict__ perm,
-                                                          int* __restrict__ pos_of, int* __restrict__ off,
-                                                          int* __restrict__ ngroups, int* __restrict__ gstat,
-                                                          int empty_bit) {
-  extern __shared__ int sm[];
-  int* cntr = sm;              // [C]
-  int* cursor = sm + C;        // [C]
-  int* remap = sm + 2 * C;     // [C]
-  int* scan = sm + 3 * C;      // [1024]
-  int* wcnt = sm + 3 * C + 1024;  // [16][C]
-  const int hd = blockIdx.x, t = threadIdx.x;
-  const int* lr = lab_raw + size_t(hd) * n;
-  for (int m = t; m < C; m += 1024) cntr[m] = 0;
-  for (int e = t; e < 16 * C; e += 1024) wcnt[e] = 0;
-  __syncthreads();
-  for (int j = t; j < n; j += 1024) atomicAdd(&cntr[lr[j]], 1);
-  __syncthreads();
-  // C <= 1024: one cluster per thread
-  const int cm = t < C ? cntr[t] : 0;
-  int ng;
-  const int newid = block_exscan_i(cm > 0 ? 1 : 0, scan, &ng);
-  int tot;
-  const int start = block_exscan_i(cm, scan, &tot);
-  if (t < C) {
-    remap[t] = newid;
-    cursor[t] = start;
-    if (cm > 0) off[size_t(hd) * (C + 1) + newid] = start;
-  }
-  if (t == 0) {
-    off[size_t(hd) * (C + 1) + ng] = n;
-    ngroups[hd] = ng;
-    if (ng < C) atomicOr(gstat + hd * 8 + 0, empty_bit);
-  }
-  __syncthreads();
-  const int lane = t & 63, w = t >> 6;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int j = c0 + t;
-    const bool valid = j < n;
-    const int L = valid ? lr[j] : -1;
-    unsigned long long todo = __ballot(valid);
-    int myrank = 0, mycnt = 0;
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int Ll = __shfl(L, leader);
-      const unsigned long long msk = __ballot(L == Ll);
-      if (L == Ll) {
-        myrank = __popcll(msk & lt);
-        mycnt = __popcll(msk);
-      }
-      todo &= ~msk;
-    }
-    if (valid && myrank == 0) wcnt[w * C + L] = mycnt;
-    __syncthreads();
-    int before = 0, after = 0, pos = 0;
-    if (valid) {
-      for (int w2 = 0; w2 < w; ++w2) before += wcnt[w2 * C + L];
-      for (int w2 = w + 1; w2 < 16; ++w2) after += wcnt[w2 * C + L];
-      pos = cursor[L] + before + myrank;
-    }
-    __syncthreads();
-    if (valid) {
-      if (myrank == mycnt - 1 && after == 0) cursor[L] = pos + 1;
-      if (myrank == 0) wcnt[w * C + L] = 0;
-      perm[size_t(hd) * n + pos] = j;
-      if (pos_of) pos_of[size_t(hd) * n + j] = pos;
-      lab_c[size_t(hd) * n + j] = remap[L];
-    }
-    __syncthreads();
-  }
-}
-
 // ------------------------------------------------------------------ gathers and means
 // Group-major copy of the rows of one tensor: dst[hd][pos] = src[hd][perm[pos]] for video
 // positions and dst[hd][pos] = src[hd][pos] for the trailing text rows.  16-byte pieces.
@@ -1077,17 +999,6 @@ __global__ void merge_kv_status_kernel(int* __restrict__ gstat, const int* __res
 }
 
 // ------------------------------------------------------------------ host drivers
-size_t compact_smem(int C) { return size_t(3 * C + 1024 + 16 * C) * sizeof(int); }
-
-spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, int* perm, int* pos_of, int* off,
-                          int* ngroups, int* gstat, int empty_bit, hipStream_t st) {
-  allow_lds(km_compact_kernel, compact_smem(C));
-  hipLaunchKernelGGL(km_compact_kernel, dim3(BH), dim3(1024), compact_smem(C), st, lab_raw, n, C, lab_c, perm,
-                     pos_of, off, ngroups, gstat, empty_bit);
-  SPR_CHECK_LAUNCH();
-  return SPR_OK;
-}
-
 __global__ void copy_doubles_kernel(const double* src, double* dst, size_t n) {
   const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (i < n) dst[i] = src[i];
@@ -1196,8 +1107,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, ka.cent,
                        out.cK_last, nel);
   }
-  s = launch_compact(ka.labels, BHkv, Nv, p.Ck, out.kv_label, out.kv_perm, nullptr, out.kv_off, out.n_kv, kvstat,
-                     SPR_HS_KV_GROUPS_EMPTY, st);
+  s = launch_compact(ka, out.kv_label, out.kv_perm, nullptr, out.kv_off, out.n_kv, kvstat, SPR_HS_KV_GROUPS_EMPTY, st);
   if (s != SPR_OK) return s;
   // group-major K and V, key / value centroids
   const int pieces = d * ElemSize<DT>::value / 16;
@@ -1262,8 +1172,7 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     hipLaunchKernelGGL(copy_doubles_kernel, dim3(unsigned(ceil_div64(nel, 256))), dim3(256), 0, st, qa.cent,
                        out.cQ_last, nel);
   }
-  s = launch_compact(qa.labels, BH, Nv, p.Cq, out.q_label, out.q_perm, out.q_pos, out.q_off, out.n_q, gstat,
-                     SPR_HS_Q_GROUPS_EMPTY, st);
+  s = launch_compact(qa, out.q_label, out.q_perm, out.q_pos, out.q_off, out.n_q, gstat, SPR_HS_Q_GROUPS_EMPTY, st);
   if (s != SPR_OK) return s;
   hipLaunchKernelGGL(gather_rows_kernel<DT>, ggrid, dim3(256), 0, st, q, g, out.q_perm, out.Qp);
   hipLaunchKernelGGL(group_mean_kernel<DT>, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, out.Qp, desc.N, d,

@@ -51,10 +51,12 @@ struct KmStatsTarget {
 KmStatsTarget km_stats_target(const KmArgs& a);
 void kmeans_stats_zero(const KmArgs& a, hipStream_t st);
 bool kmeans_rank_supported(int r);
-size_t compact_smem(int C);
 size_t jacobi_smem(int d);
-spr_status launch_compact(const int* lab_raw, int BH, int n, int C, int* lab_c, int* perm, int* pos_of, int* off,
-                          int* ngroups, int* gstat, int empty_bit, hipStream_t st);
+// Groups from the final labels of a run_kmeans call (its scratch reused): empty clusters dropped,
+// the others renumbered in ascending id (lab_c), offsets, group count, status bit, and a stable
+// counting sort (perm: members of each group in ascending point index; pos_of: its inverse).
+spr_status launch_compact(const KmArgs& a, int* lab_c, int* perm, int* pos_of, int* off, int* ngroups, int* gstat,
+                          int empty_bit, hipStream_t st);
 
 spr_status run_partition(const spr_desc& desc, const void* q, const void* k, const void* v, const spr_part_params& p,
                          const spr_warm* warm, spr_partition& out, void* ws, const Workspace& L, hipStream_t st);
