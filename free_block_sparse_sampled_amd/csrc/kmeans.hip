@@ -567,7 +567,7 @@ __global__ __launch_bounds__(256) void km_reduce_kernel(const double* __restrict
                                                         const int* __restrict__ cstart,
                                                         const double* __restrict__ ctrl, double* __restrict__ sums,
                                                         double* __restrict__ jpart) {
-  constexpr int EPL = (R + 63) / 64, PB = 8;
+  constexpr int EPL = (R + 63) / 64, PB = 16;
   const int hd = blockIdx.y;
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int c = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6)), lane = threadIdx.x & 63;
