@@ -2,19 +2,21 @@
 // Sec. 4.1 for the K/V and query partitions, App. C.1 for the initialisation, Table C.1 for
 // the limits) on gfx950.
 //
-// One Lloyd pass = four kernels:
+// One Lloyd pass:
 //  screen   squared distances of every point to every centre from an MFMA cross term.
 //           Coordinates are centred by the head's mean point and scaled by a power of two,
 //           then split into fp16 hi + lo parts; x.c ~ hi.hi + hi.lo + lo.hi on
-//           v_mfma_f32_16x16x32_f16.  A bound on the error of the screened distances decides,
+//           v_mfma_f32_32x32x16_f16.  A bound on the error of the screened distances decides,
 //           per point, whether the nearest centre is certain; the rest go to a queue.
 //  rescan   queued points: fp64 direct-difference distances to every centre (exact nearest,
-//           ties to the lowest index), one wave per point.
-//  accum    fp64 distance to the chosen centre (cost), label change count, and the Lloyd sums:
-//           a wave walks its 64 points in order, one lane per coordinate, flushing a running sum
-//           with fp64 atomics when the label changes.
-//  finalize stopping rule (labels unchanged, relative cost decrease <= tol, or max_iters),
-//           centre update (empty centres stay), and the fp16 split of the new centres.
+//           ties to the lowest index).
+//  sort     label histograms of 4096-point slices, a scan per head, a stable scatter: the
+//           points of every new label in ascending index, and the count of changed labels.
+//  reduce   one wave per centre: the Lloyd sums of its members (no atomics, a fixed order) and
+//           their fp64 distances to the old centre (cost).
+//  decide / update   stopping rule (labels unchanged, relative cost decrease <= tol, or
+//           max_iters), centre update (empty centres stay), the fp16 split of the new centres.
+// The final labels are compacted on the same sort (empty groups dropped, offsets, permutation).
 // The control word per head (done flag, pass count, previous cost, largest centre norm, scale)
 // lives on the device, so the host launches max_iters passes without synchronising and
 // finished heads return immediately.
