@@ -32,6 +32,11 @@ PEAK_HBM_GBS = 8000.0
 ATTN_SOURCE = os.path.join(ROOT, "free_block_sparse_sampled_amd", "csrc", "attention.hip")
 
 
+def progress(msg):
+    """One progress line on stderr (stdout carries only the JSON result)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def measured_traffic(cfg_name):
     """HBM-side bytes per sparse-attention launch from the committed FETCH_SIZE / WRITE_SIZE summary
     of this workload, or None when there is none or it was taken on another version of the kernel
@@ -141,6 +146,7 @@ def cpu_baseline(cfg, opc, warm, warm_iters, step):
         prev = O.sparsepr_head(qp, kp, vp, p, head=0, full=False)["state"]
         t_setup = time.perf_counter() - t0
         del qp, kp, vp
+        progress(f"oracle: previous call done ({t_setup:.0f} s)")
     q, k, v = head_inputs(cfg, 0, 0, step)
     t0 = time.perf_counter()
     st = O.sparsepr_head(q, k, v, p, head=0, full=False, warm=prev)
@@ -211,6 +217,7 @@ def measure(args, name, headline):
     if key not in _INPUTS:
         _INPUTS.clear()
         torch.cuda.empty_cache()
+        progress(f"{cfg.name}: generating inputs")
         inputs = []
         for st in (0, 1):
             q, k, v = batch_inputs(cfg, step=st)
@@ -262,10 +269,12 @@ def measure(args, name, headline):
     # the other regime first (a short measurement reported beside the headline one)
     other = None
     if headline and not args.no_other:
+        progress(f"{cfg.name}: {'cold' if warm_regime else 'later'} calls")
         per_o, total_o, _ = timed(not warm_regime, max(2, args.steps // 3), 1)
         other = {"ms_per_call": round(float(np.median(total_o)), 4),
                  "stages_ms": {n: round(float(np.median(per_o[:, i])), 4) for i, n in enumerate(names)}}
     steps = args.steps if headline else max(3, args.steps // 2)
+    progress(f"{cfg.name}: timed {'later' if warm_regime else 'cold'} calls")
     per, total, wall = timed(warm_regime, steps, max(args.warmup, 1))
     ms_call = float(np.median(total))
     last_step = (call[0] - 1) % 2
@@ -324,6 +333,7 @@ def measure(args, name, headline):
 
     err_rows0 = None
     if not args.no_dense:
+        progress(f"{cfg.name}: dense attention and errors")
         dense_out = torch.empty((cfg.B, cfg.H, N, d), dtype=torch.float32, device="cuda")
         desc = spr.make_desc(tq)
         dws = spr.dense_workspace(desc, tq.device)
@@ -385,6 +395,7 @@ def measure(args, name, headline):
                                                  "explained_fraction": round(1.0 - left / energy, 5)}
         del dense_out, o, dref, osp, err, err_sp
     if headline and not args.no_cpu:
+        progress(f"{cfg.name}: oracle on the host cores")
         cb = cpu_baseline(cfg, opc, warm_regime, op.warm_iters, last_step)
         rows = cb.pop("_rows")
         if err_rows0 is not None:
