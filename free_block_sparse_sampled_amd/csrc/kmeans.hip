@@ -348,60 +348,92 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
   }
 }
 
-// fp64 nearest centre of every queued point, one wave per point (ties to the lowest index).
-// The point sits in registers for ranks up to 64 and in the wave's LDS row (broadcast reads)
-// for rank 128.
+// fp64 nearest centre of every queued point (ties to the lowest index).  A block takes eight
+// queued points at a time, staged in LDS; thread t walks centres t, t + 256, ..., reads each
+// centre row once for the eight points and keeps eight direct-difference distances, summed
+// over the coordinates in ascending order; the four waves' nearest centres are then merged.
 template <int R>
 __global__ __launch_bounds__(256) void km_rescan_kernel(int n, int C, const double* __restrict__ feat,
                                                         const double* __restrict__ cent,
                                                         const double* __restrict__ ctrl,
                                                         const int* __restrict__ rq_count,
                                                         const int* __restrict__ rq_list, int* __restrict__ lab_new) {
-  constexpr bool INLDS = R > 64;
-  __shared__ double xs[INLDS ? 4 * R : 1];
+  constexpr int PP = 8;
+  static_assert(R % 2 == 0, "pairs of coordinates");
+  __shared__ __attribute__((aligned(16))) double xs[PP][R];
+  __shared__ double rb[4][PP];
+  __shared__ int ri[4][PP], jl[PP];
   const int hd = blockIdx.y;
   if (ctrl[hd * CTRL + C_DONE] != 0.0) return;
   const int cnt = rq_count[hd];
-  const int lane = threadIdx.x & 63;
-  const int nw = gridDim.x * 4;
-  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < cnt; i += nw) {
-    const int j = rq_list[size_t(hd) * n + i];
-    const double* f = feat + (size_t(hd) * n + j) * R;
-    double xr[INLDS ? 1 : R];
-    double* xw = xs + (INLDS ? (threadIdx.x >> 6) * R : 0);
-    if constexpr (INLDS) {
-      __builtin_amdgcn_wave_barrier();
-      for (int e = lane; e < R; e += 64) xw[e] = f[e];
-      __builtin_amdgcn_wave_barrier();
-    } else {
-#pragma unroll
-      for (int e = 0; e < R; ++e) xr[e] = f[e];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i0 = blockIdx.x * PP; i0 < cnt; i0 += gridDim.x * PP) {
+    const int np = min(PP, cnt - i0);
+    __syncthreads();  // the previous points' rows and results are no longer read
+    if (t < PP) jl[t] = t < np ? rq_list[size_t(hd) * n + i0 + t] : 0;
+    __syncthreads();
+    for (int e = t; e < PP * R; e += 256) {
+      const int p = e / R;
+      xs[p][e % R] = p < np ? feat[(size_t(hd) * n + jl[p]) * R + e % R] : 0.0;
     }
-    const double* x = INLDS ? xw : xr;
-    double best = INFINITY;
-    int bi = 0;
-    for (int m = lane; m < C; m += 64) {
+    __syncthreads();
+    double best[PP];
+    int bi[PP];
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      best[p] = INFINITY;
+      bi[p] = 0;
+    }
+    for (int m = t; m < C; m += 256) {
       const double* c = cent + (size_t(hd) * C + m) * R;
-      double dd = 0.0;
+      double dd[PP];
 #pragma unroll
-      for (int e = 0; e < R; ++e) {
-        const double tdiff = x[e] - c[e];
-        dd = fma(tdiff, tdiff, dd);
+      for (int p = 0; p < PP; ++p) dd[p] = 0.0;
+      for (int e = 0; e < R; e += 2) {
+        const double2 ce = *reinterpret_cast<const double2*>(c + e);
+#pragma unroll
+        for (int p = 0; p < PP; ++p) {
+          const double2 xv = *reinterpret_cast<const double2*>(&xs[p][e]);
+          const double t0 = xv.x - ce.x;
+          dd[p] = fma(t0, t0, dd[p]);
+          const double t1 = xv.y - ce.y;
+          dd[p] = fma(t1, t1, dd[p]);
+        }
       }
-      if (dd < best) {
-        best = dd;
-        bi = m;
+#pragma unroll
+      for (int p = 0; p < PP; ++p)
+        if (dd[p] < best[p]) {
+          best[p] = dd[p];
+          bi[p] = m;
+        }
+    }
+    auto better = [](double ob, int oi, double b, int i) { return ob < b || (ob == b && oi < i); };
+#pragma unroll
+    for (int p = 0; p < PP; ++p) {
+      for (int o = 32; o > 0; o >>= 1) {
+        const double ob = __shfl_xor(best[p], o);
+        const int oi = __shfl_xor(bi[p], o);
+        if (better(ob, oi, best[p], bi[p])) {
+          best[p] = ob;
+          bi[p] = oi;
+        }
+      }
+      if (lane == 0) {
+        rb[w][p] = best[p];
+        ri[w][p] = bi[p];
       }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ob < best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-      }
+    __syncthreads();
+    if (t < np) {
+      double b = rb[0][t];
+      int i = ri[0][t];
+      for (int q = 1; q < 4; ++q)
+        if (better(rb[q][t], ri[q][t], b, i)) {
+          b = rb[q][t];
+          i = ri[q][t];
+        }
+      lab_new[size_t(hd) * n + jl[t]] = i;
     }
-    if (lane == 0) lab_new[size_t(hd) * n + j] = bi;
   }
 }
 
