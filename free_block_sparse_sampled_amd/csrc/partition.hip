@@ -672,53 +672,51 @@ static void launch_warm_centres(dim3 grid, hipStream_t st, const double* prev, c
 // and B[k][j] from lane j + 16k, and returns D[(lane / 16) + 4 v][lane % 16] in slot v.  F is
 // staged in LDS once per block; the block then walks `chunks` chunks of 128 rows (8 waves x 16
 // rows), the next chunk's rows loaded into registers (16-byte loads) while the current one is
-// multiplied, then widened to fp32 in LDS.
-template <int DT, bool RMS>
+// multiplied, then widened to fp32 in LDS.  The row width D and the NT = ceil(r / 16) column
+// tiles are compile-time, so the product loop is straight-line code whose LDS reads run ahead of
+// the matrix-core chain.
+template <int DT, bool RMS, int D, int NT>
 __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x, HeadGeom g, int rows,
                                                       const double* __restrict__ Fall, int r, double eps,
                                                       double* __restrict__ out, int* __restrict__ gstat, int chunks,
                                                       int fdiv, KmStatsTarget kst) {
   extern __shared__ double smem[];
-  const int d = g.d;
-  const int NT = (r + 15) >> 4;
-  const int FS = NT * 16 + 8;  // F row stride (doubles)
-  const int XS = d + 4;        // X tile row stride (floats)
-  double* Fs = smem;                                      // [d][FS]
-  float* Xs = reinterpret_cast<float*>(smem + d * FS);  // [128][XS]
+  constexpr int FS = NT * 16 + 8;  // F row stride (doubles)
+  constexpr int XS = D + 4;        // X tile row stride (floats)
+  double* Fs = smem;                                      // [D][FS]
+  float* Xs = reinterpret_cast<float*>(smem + D * FS);  // [128][XS]
   const int hd = blockIdx.y;
-  const double* F = Fall + size_t(hd / fdiv) * d * r;  // factor of the head's K/V head
-  for (int e = threadIdx.x; e < d * FS; e += 512) {
+  const double* F = Fall + size_t(hd / fdiv) * D * r;  // factor of the head's K/V head
+  for (int e = threadIdx.x; e < D * FS; e += 512) {
     const int kk = e / FS, c = e % FS;
     Fs[e] = c < r ? F[size_t(kk) * r + c] : 0.0;
   }
   const int64_t base = g.base(hd);
-  // this thread's share of a chunk: groups of 8 elements e8 = threadIdx.x + 512 u, u < d / 32
-  const int per = d >> 5;  // 4 for d = 128, 2 for d = 64
-  float xv[4][8];
+  // this thread's share of a chunk: groups of 8 elements e8 = threadIdx.x + 512 u, u < D / 32
+  constexpr int PER = D >> 5;  // 4 for d = 128, 2 for d = 64
+  float xv[PER][8];
   auto fetch = [&](int row0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u < per) {
-        const int e = (threadIdx.x + 512 * u) * 8, rr = e / d, cc = e % d;
-        const int row = row0 + rr < rows ? row0 + rr : rows - 1;
-        load8<DT>(x, base + int64_t(row) * g.sn + cc, xv[u]);
-      }
+    for (int u = 0; u < PER; ++u) {
+      const int e = (threadIdx.x + 512 * u) * 8, rr = e / D, cc = e % D;
+      const int row = row0 + rr < rows ? row0 + rr : rows - 1;
+      load8<DT>(x, base + int64_t(row) * g.sn + cc, xv[u]);
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (u < per) {
-        const int e = (threadIdx.x + 512 * u) * 8, rr = e / d, cc = e % d;
-        float* dst = Xs + rr * XS + cc;
-        *reinterpret_cast<float4*>(dst) = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[u][4], xv[u][5], xv[u][6], xv[u][7]);
-      }
+    for (int u = 0; u < PER; ++u) {
+      const int e = (threadIdx.x + 512 * u) * 8, rr = e / D, cc = e % D;
+      float* dst = Xs + rr * XS + cc;
+      *reinterpret_cast<float4*>(dst) = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[u][4], xv[u][5], xv[u][6], xv[u][7]);
     }
   };
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   const int first = blockIdx.x * chunks * 128;
-  double csum[4] = {0.0, 0.0, 0.0, 0.0}, cmax = 0.0;  // this lane's rows of columns nt * 16 + r16
+  double csum[NT], cmax = 0.0;  // this lane's rows of columns nt * 16 + r16
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) csum[nt] = 0.0;
   fetch(first);
   for (int ch = 0; ch < chunks; ++ch) {
     const int row0 = first + ch * 128;
@@ -727,16 +725,17 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
     stage();
     __syncthreads();
     if (ch + 1 < chunks && row0 + 128 < rows) fetch(row0 + 128);
-    f64x4_t acc[4];
+    f64x4_t acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int ks = 0; ks < d / 4; ++ks) {
-      const double av = Xs[(w * 16 + r16) * XS + ks * 4 + gq];
-      const double* fr = Fs + (ks * 4 + gq) * FS + r16;
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    const float* xr = Xs + (w * 16 + r16) * XS + gq;
+    const double* fr = Fs + gq * FS + r16;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        if (nt < NT) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, fr[nt * 16], acc[nt], 0, 0, 0);
+    for (int ks = 0; ks < D / 4; ++ks) {
+      const double av = xr[ks * 4];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, fr[ks * 4 * FS + nt * 16], acc[nt], 0, 0, 0);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -745,8 +744,7 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
       if constexpr (RMS) {
         double s2 = 0.0;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (nt < NT) s2 = fma(acc[nt][v], acc[nt][v], s2);
+        for (int nt = 0; nt < NT; ++nt) s2 = fma(acc[nt][v], acc[nt][v], s2);
         s2 += __shfl_xor(s2, 1);
         s2 += __shfl_xor(s2, 2);
         s2 += __shfl_xor(s2, 4);
@@ -758,9 +756,9 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
       if (row < rows) {
         double* o = out + (size_t(hd) * rows + row) * r;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const int c = nt * 16 + r16;
-          if (nt < NT && c < r) {
+          if (c < r) {
             const double y = acc[nt][v] * scale;
             o[c] = y;
             csum[nt] += y;
@@ -773,7 +771,7 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
   if (kst.mu) {
     // the four row groups of a column, then the waves of the block through LDS (Xs is free)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       csum[nt] += __shfl_xor(csum[nt], 16);
       csum[nt] += __shfl_xor(csum[nt], 32);
     }
@@ -782,7 +780,7 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
     double* red = reinterpret_cast<double*>(Xs);  // [8 waves][64 columns + 1]
     if (gq == 0)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) red[w * 65 + nt * 16 + r16] = csum[nt];
+      for (int nt = 0; nt < 4; ++nt) red[w * 65 + nt * 16 + r16] = nt < NT ? csum[nt] : 0.0;
     if (lane == 0) red[w * 65 + 64] = cmax;
     __syncthreads();
     if (threadIdx.x < r) {
@@ -818,6 +816,29 @@ static int project_chunks(int rows, int BH) {
     }
   }
   return best;
+}
+
+// Projection launch for row width d (64 or 128) and rank r <= 64 (NT = ceil(r / 16) tiles).
+template <int DT, bool RMS>
+static void launch_project(int d, int r, dim3 grid, size_t smem, hipStream_t st, const void* x, const HeadGeom& g,
+                           int rows, const double* F, double eps, double* out, int* gstat, int chunks, int fdiv,
+                           const KmStatsTarget& kst) {
+  auto go = [&](auto kernel) {
+    allow_lds(kernel, smem);
+    hipLaunchKernelGGL(kernel, grid, dim3(512), smem, st, x, g, rows, F, r, eps, out, gstat, chunks, fdiv, kst);
+  };
+  const int nt = (r + 15) >> 4;
+  if (d == 128) {
+    if (nt == 1) go(project_kernel<DT, RMS, 128, 1>);
+    else if (nt == 2) go(project_kernel<DT, RMS, 128, 2>);
+    else if (nt == 3) go(project_kernel<DT, RMS, 128, 3>);
+    else go(project_kernel<DT, RMS, 128, 4>);
+  } else {
+    if (nt == 1) go(project_kernel<DT, RMS, 64, 1>);
+    else if (nt == 2) go(project_kernel<DT, RMS, 64, 2>);
+    else if (nt == 3) go(project_kernel<DT, RMS, 64, 3>);
+    else go(project_kernel<DT, RMS, 64, 4>);
+  }
 }
 
 // ------------------------------------------------------------------ gathers and means
@@ -1069,8 +1090,6 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
   // phi_K = K F_K, or the raw keys
   const size_t prj_smem = project_smem(d, p.rK > p.rQ ? p.rK : p.rQ);
   const int pchunks = project_chunks(Nv, BH), kchunks = project_chunks(Nv, BHkv);
-  allow_lds(project_kernel<DT, false>, prj_smem);
-  allow_lds(project_kernel<DT, true>, prj_smem);
   const dim3 rgrid(unsigned(ceil_div64(int64_t(Nv) * d / 8, 256)), BHkv), rqgrid(rgrid.x, BH);
   KmArgs ka = kmeans_carve(wsp<char>(ws, L.km_region), BH, Nv, L.Cmax, L.rmax);
   ka.BH = BHkv;
@@ -1079,8 +1098,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     hipLaunchKernelGGL(raw_rows_kernel<DT>, rgrid, dim3(256), 0, st, k, gk, Nv, phiK);
   } else {
     kmeans_stats_zero(ka, st);  // the projection accumulates the k-means point statistics
-    hipLaunchKernelGGL((project_kernel<DT, false>), dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), dim3(512),
-                       prj_smem, st, k, gk, Nv, out.FK, p.rK, p.rms_eps, phiK, kvstat, kchunks, 1, kst);
+    launch_project<DT, false>(d, p.rK, dim3(ceil_div(ceil_div(Nv, 128), kchunks), BHkv), prj_smem, st, k, gk, Nv,
+                              out.FK, p.rms_eps, phiK, kvstat, kchunks, 1, kst);
     ka.stats_given = true;
   }
   SPR_CHECK_LAUNCH();
@@ -1145,8 +1164,8 @@ static spr_status partition_impl(const spr_desc& desc, const void* q, const void
     KmArgs qz = ka;
     qz.BH = BH;
     kmeans_stats_zero(qz, st);
-    hipLaunchKernelGGL((project_kernel<DT, true>), dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), dim3(512),
-                       prj_smem, st, q, g, Nv, out.FQ, p.rQ, p.rms_eps, phiQ, gstat, pchunks, G, kst);
+    launch_project<DT, true>(d, p.rQ, dim3(ceil_div(ceil_div(Nv, 128), pchunks), BH), prj_smem, st, q, g, Nv,
+                             out.FQ, p.rms_eps, phiQ, gstat, pchunks, G, kst);
   } else {
     hipLaunchKernelGGL(raw_rows_kernel<DT>, rqgrid, dim3(256), 0, st, q, g, Nv, phiQ);
   }

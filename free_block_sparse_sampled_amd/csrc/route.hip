@@ -89,19 +89,34 @@ __global__ __launch_bounds__(256) void vstat_kernel(const void* __restrict__ Vp,
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 // Centroid logits lbar_ab = qbar_a . kbar_b / sqrt d on the fp64 matrix cores.  One block per
-// 64 query groups x 64 K/V groups of a head: wave w owns query groups a0 + 16 w .. + 15 (A
-// fragments of qbar in registers: lane l holds qbar[a0 + 16 w + l % 16] at columns 4 ks + l / 16)
+// 64 query groups x 64 K/V groups of a head: the block's 64 key centroids are staged in LDS once
+// (rows padded to D + 4 doubles) for its four waves; wave w owns query groups a0 + 16 w .. + 15
+// (A fragments of qbar in registers: lane l holds qbar[a0 + 16 w + l % 16] at columns 4 ks + l / 16)
 // and the block's four tiles of 16 K/V groups, each its own accumulation chain; lane l, slot v
 // of tile t holds the logit of query group 16 w + l / 16 + 4 v and K/V group b0 + 16 t + l % 16.
+template <int D>
+constexpr size_t centroid_logits_smem() {
+  return size_t(64) * (D + 4) * sizeof(double);
+}
 template <int D>
 __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __restrict__ qbar,
                                                               const double* __restrict__ kbar,
                                                               const int* __restrict__ n_q,
                                                               const int* __restrict__ n_kv, int Cq, int Ck, int G,
                                                               double* __restrict__ lbar) {
+  constexpr int KST = D + 4;  // LDS row stride (doubles)
+  extern __shared__ __attribute__((aligned(16))) double kbs[];  // [64][KST]
   const int hd = blockIdx.z, hk = hd / G, a0 = blockIdx.x * 64, b0 = blockIdx.y * 64;  // query head, K/V head
   const int nq = n_q[hd], nkv = n_kv[hk];
   if (a0 >= nq || b0 >= nkv) return;
+  // rows past the last K/V group repeat it (their logits are not stored)
+  for (int e = threadIdx.x; e < 64 * D / 2; e += 256) {
+    const int row = e / (D / 2), c2 = e % (D / 2);
+    const double2 v2 =
+        *reinterpret_cast<const double2*>(kbar + (size_t(hk) * Ck + min(b0 + row, nkv - 1)) * D + 2 * c2);
+    *reinterpret_cast<double2*>(kbs + row * KST + 2 * c2) = v2;
+  }
+  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
   const int aw = a0 + w * 16;
   if (aw >= nq) return;
@@ -112,16 +127,15 @@ __global__ __launch_bounds__(256) void centroid_logits_kernel(const double* __re
     for (int ks = 0; ks < D / 4; ++ks) qa[ks] = a < nq ? qbar[(size_t(hd) * Cq + a) * D + ks * 4 + gq] : 0.0;
   }
   const double inv = 1.0 / sqrt(double(D));
-  const double* kb[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) kb[t] = kbar + (size_t(hk) * Ck + min(b0 + 16 * t + r16, nkv - 1)) * D + gq;
+  const double* kb = kbs + r16 * KST + gq;
   f64x4_t lg[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) lg[t] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int ks = 0; ks < D / 4; ++ks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lg[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[t][ks * 4], lg[t], 0, 0, 0);
+    for (int t = 0; t < 4; ++t)
+      lg[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], kb[16 * t * KST + ks * 4], lg[t], 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int b = b0 + 16 * t + r16;
@@ -1452,11 +1466,12 @@ static spr_status route_impl(const spr_desc& desc, const spr_part_params& p, con
   double* lbar = ws_ptr<double>(ws, L.lbar);
   const dim3 lgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 64), BH), sgrid(ceil_div(p.Cq, 64), ceil_div(p.Ck, 16), BH);
   if (d == 128) {
-    hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, G, lbar);
+    allow_lds(centroid_logits_kernel<128>, centroid_logits_smem<128>());
+    hipLaunchKernelGGL(centroid_logits_kernel<128>, lgrid, dim3(256), centroid_logits_smem<128>(), st, part.qbar,
+                       part.kbar, part.n_q, part.n_kv, p.Cq, p.Ck, G, lbar);
   } else {
-    hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), 0, st, part.qbar, part.kbar, part.n_q,
-                       part.n_kv, p.Cq, p.Ck, G, lbar);
+    hipLaunchKernelGGL(centroid_logits_kernel<64>, lgrid, dim3(256), centroid_logits_smem<64>(), st, part.qbar,
+                       part.kbar, part.n_q, part.n_kv, p.Cq, p.Ck, G, lbar);
   }
   hipLaunchKernelGGL(logit_shift_kernel, dim3(ceil_div(p.Cq, 4), BH), dim3(256), 0, st, lbar, part.n_q, part.n_kv,
                      p.Cq, p.Ck, G, shift);
