@@ -243,13 +243,15 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
       bl[pt][ks] = as_f16x8(ul);
     }
   }
+  // running best, its index and the second best per point tile; the index is kept as the
+  // 32-centre block that last lowered the best (ib) and the register slot within it (iv)
   float b1[2], b2[2];
-  int i1[2];
+  int ib[2], iv[2];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
     b1[pt] = INFINITY;
     b2[pt] = INFINITY;
-    i1[pt] = 0;
+    ib[pt] = iv[pt] = 0;
   }
   const _Float16* chh = ch + size_t(hd) * C * RP;
   const _Float16* cll = cl + size_t(hd) * C * RP;
@@ -292,33 +294,34 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[ks], bl[pt][ks], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[ks], bh[pt][ks], acc, 0, 0, 0);
         }
+        // branch-free running best / slot / second best (centres in ascending index); with
+        // b1 <= b2 the new second best is the median of b1, b2 and the value.  The slot v is an
+        // inline constant of the select; the block is recorded once, when it lowered the best.
+        const float b1_in = b1[pt];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          // branch-free running best / index / second best (centres in ascending index); with
-          // b1 <= b2 the new second best is the median of b1, b2 and the value.  The index is
-          // kept without the lane's 4 h, which is the same for all its centres (wave-uniform
-          // operand).
           const float val = fmaf(-2.f, acc[v], cv[v]);
-          const int m = c0 + cb * 32 + 8 * (v >> 2) + (v & 3);
           b2[pt] = __builtin_amdgcn_fmed3f(b1[pt], b2[pt], val);
-          i1[pt] = val < b1[pt] ? m : i1[pt];
+          iv[pt] = val < b1[pt] ? v : iv[pt];
           b1[pt] = fminf(b1[pt], val);
         }
+        ib[pt] = b1[pt] < b1_in ? (c0 >> 5) + cb : ib[pt];
       }
     }
   }
   const double cmax = ctrl[hd * CTRL + C_CMAX];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
-    i1[pt] += 4 * h;
+    // centre of slot v of block ib: 32 ib + 8 (v / 4) + 4 h + v % 4
+    int i1 = 32 * ib[pt] + 8 * (iv[pt] >> 2) + (iv[pt] & 3) + 4 * h;
     // merge the two lanes of a point (their centre subsets are disjoint)
     {
       const float ob1 = __shfl_xor(b1[pt], 32), ob2 = __shfl_xor(b2[pt], 32);
-      const int oi = __shfl_xor(i1[pt], 32);
-      if (ob1 < b1[pt] || (ob1 == b1[pt] && oi < i1[pt])) {
+      const int oi = __shfl_xor(i1, 32);
+      if (ob1 < b1[pt] || (ob1 == b1[pt] && oi < i1)) {
         b2[pt] = fminf(ob2, b1[pt]);
         b1[pt] = ob1;
-        i1[pt] = oi;
+        i1 = oi;
       } else {
         b2[pt] = fminf(b2[pt], ob1);
       }
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(256) void km_screen_kernel(int n, int C, const _Flo
       const double E = 2.0 * (2.0 * tcross + 4.0 * 5.960464477539063e-8 * (xn + cmax) * (xn + cmax)) +
                        1e-12 * (xn + cmax) * (xn + cmax);
       const bool decided = double(b2[pt]) - double(b1[pt]) > 2.0 * E;
-      lab_new[size_t(hd) * n + j] = decided ? i1[pt] : -1;
+      lab_new[size_t(hd) * n + j] = decided ? i1 : -1;
       queue = !decided;
     }
     // the undecided points of the wave join the rescan queue with one atomic

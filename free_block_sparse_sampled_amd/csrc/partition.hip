@@ -209,6 +209,7 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
     for (int j = tid; j <= l; j += nth) {
       const double* Aj = A + size_t(j) * ld;
       double s = 0.0;
+#pragma unroll 8
       for (int k = 0; k <= l; ++k) s = fma(Aj[k], Ai[k], s);
       pv[j] = s / h;
       part += pv[j] * Ai[j];
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
     const double K = block_sum(part) / (h + h);
     for (int j = tid; j <= l; j += nth) pv[j] -= K * Ai[j];
     __syncthreads();
+#pragma unroll 4
     for (int e = tid; e < (l + 1) * (l + 1); e += nth) {
       const int j = e / (l + 1), k = e % (l + 1);
       A[size_t(j) * ld + k] -= Ai[j] * pv[k] + pv[j] * Ai[k];
@@ -233,10 +235,12 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
     if (dg[i] != 0.0) {  // a reflector was applied at step i
       for (int j = tid; j <= l; j += nth) {
         double s = 0.0;
+#pragma unroll 8
         for (int k = 0; k <= l; ++k) s = fma(A[size_t(i) * ld + k], A[size_t(k) * ld + j], s);
         pv[j] = s;
       }
       __syncthreads();
+#pragma unroll 4
       for (int e = tid; e < (l + 1) * (l + 1); e += nth) {
         const int k = e / (l + 1), j = e % (l + 1);
         A[size_t(k) * ld + j] -= pv[j] * A[size_t(k) * ld + i];
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(256) void eigen_factor_kernel(const double* __restr
       if (tid < d) {
         double* Zk = A + size_t(tid) * ld;
         double zhi = Zk[m];
+#pragma unroll 4
         for (int t = 0; t < nrot; ++t) {
           const int i = m - 1 - t;
           const double zi = Zk[i];
