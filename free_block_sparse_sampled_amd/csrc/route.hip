@@ -1153,11 +1153,13 @@ __global__ __launch_bounds__(256) void route_resolve_kernel(
 }
 
 // fp64 rescoring of the (query group, K/V group) pairs the resolve phases asked for, grouped by
-// K/V group: block (b, head) reads the requests of its column of request bits (clearing them),
-// stages the group's keys and their statistics in LDS once, and each wave computes the scores of
-// one query group after another as route_exact_score does (a lane per key, the sums of the score
-// expansion over the wave), the logit in four partial sums.  A group of more keys than fit the
-// 48 KB of LDS reads them from memory.
+// K/V group: block (b, head) reads the requests of its column of request bits (clearing them) and
+// stages the group's keys and their statistics in LDS once.  The logits of 16 requests x 16 keys
+// at a time are products on v_mfma_f64_16x16x4f64 (exact products of the bf16 keys with the fp64
+// centroids, fp64 sums): lane l supplies centroid and key elements D/4 (l / 16) .. + D/4 - 1 and
+// receives the logits of requests l / 16 + 4 v and key l % 16.  The four waves take the group's
+// 16-key tiles in turn; the score expansion's two sums are reduced over the key lanes by DPP and
+// over the waves in LDS.  A group of more keys than fit the 48 KB of LDS reads them from memory.
 template <int D>
 constexpr int rescore_keys() { return 49152 / (D * 2 + 16); }  // keys staged in LDS (48 KB)
 template <int D>
@@ -1168,9 +1170,11 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
     const int* __restrict__ n_kv, int Cq, int Ck, int G, double* __restrict__ scores, double* __restrict__ serr) {
   constexpr int PC = D / 8;  // 16-byte pieces per key row
   constexpr int KR = rescore_keys<D>(), KSTR = PC + 1;  // key rows padded by 16 bytes in LDS
+  constexpr int S = D / 4;   // elements per lane group (and matrix-core steps per tile)
+  constexpr int SP = S / 8;  // their 16-byte pieces
   __shared__ __attribute__((aligned(16))) ru32x4_t ks[KR * KSTR];
   __shared__ double kst[KR][2];
-  __shared__ __attribute__((aligned(16))) double qs[4][D];
+  __shared__ double red[4][2][16];
   __shared__ int list[1024];
   __shared__ int nreq;
   const int b = blockIdx.x, hd = blockIdx.y, hk = hd / G;
@@ -1208,7 +1212,6 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
       kst[j][1] = vstat[(size_t(hk) * Nv + k0 + j) * 4 + 1];
     }
   }
-  const double inv = 1.0 / sqrt(double(D));
   double vn = 0.0;  // |vbar_b|^2, the same for every request
   for (int c = lane; c < D; c += 64) {
     const double y = vbar[(size_t(hk) * Ck + b) * D + c];
@@ -1216,68 +1219,89 @@ __global__ __launch_bounds__(256) void route_rescore_kernel(
   }
   vn = wave_allsum_d(vn);
   __syncthreads();
-  // the next request's centroid, shift and centroid logit are loaded while this one is scored
-  constexpr int QPL = D / 64;  // centroid coordinates per lane
-  double qn[QPL], mn = 0.0, lbn = 0.0;
-  auto fetch = [&](int r) {
-    const int a = list[r];
-#pragma unroll
-    for (int u = 0; u < QPL; ++u) qn[u] = qbar[(size_t(hd) * Cq + a) * D + lane + 64 * u];
-    mn = shift[size_t(hd) * Cq + a];
-    lbn = lbar[(size_t(hd) * Cq + a) * Ck + b];
+  const double inv = 1.0 / sqrt(double(D));
+  const int i16 = lane & 15, kq = lane >> 4;
+  const int KT = (nk + 15) >> 4;  // 16-key tiles
+  // row sums over the 16 lanes of a DPP row (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+  // row_mirror)
+  auto rowsum = [](double x) {
+    x += dppd<0xB1>(x);
+    x += dppd<0x4E>(x);
+    x += dppd<0x141>(x);
+    return x + dppd<0x140>(x);
   };
-  if (w < n) fetch(w);
-  for (int r = w; r < n; r += 4) {
-    const int a = list[r];
+  for (int rt = 0; rt < n; rt += 16) {
+    // A fragments: centroid of request rt + l % 16 (zero past the last request)
+    const int ra = rt + i16 < n ? list[rt + i16] : -1;
+    double qa[S];
+    {
+      const double* qp = qbar + (size_t(hd) * Cq + (ra >= 0 ? ra : 0)) * D + S * kq;
 #pragma unroll
-    for (int u = 0; u < QPL; ++u) qs[w][lane + 64 * u] = qn[u];
-    const double m = mn, lb = lbn;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (r + 4 < n) fetch(r + 4);
-    double s1 = 0.0, s2 = 0.0;
-    for (int j0 = 0; j0 < nk; j0 += 64) {
-      const int j = min(j0 + lane, nk - 1);
-      double uw_x, uw_y;
-      if (staged) {
-        uw_x = kst[j][0];
-        uw_y = kst[j][1];
-      } else {
-        uw_x = vstat[(size_t(hk) * Nv + k0 + j) * 4];
-        uw_y = vstat[(size_t(hk) * Nv + k0 + j) * 4 + 1];
+      for (int e = 0; e < S; e += 2) {
+        const double2 t2 = ra >= 0 ? *reinterpret_cast<const double2*>(qp + e) : make_double2(0.0, 0.0);
+        qa[e] = t2.x;
+        qa[e + 1] = t2.y;
       }
-      // the logit in four interleaved partial sums (a short dependency chain per lane)
-      double lp[4] = {0.0, 0.0, 0.0, 0.0};
+    }
+    double mv[4], s1[4], s2[4];
 #pragma unroll
-      for (int i = 0; i < PC; ++i) {
-        const ru32x4_t raw = staged ? ks[j * KSTR + i] : Kg[int64_t(j) * PC + i];
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int v = 0; v < 4; ++v) {
+      const int r = rt + kq + 4 * v;
+      mv[v] = r < n ? shift[size_t(hd) * Cq + list[r]] : 0.0;
+      s1[v] = s2[v] = 0.0;
+    }
+    for (int kt = w; kt < KT; kt += 4) {
+      const int jl = kt * 16 + i16;
+      const bool live = jl < nk;
+      const int jc = live ? jl : nk - 1;
+      ru32x4_t raw[SP];
+#pragma unroll
+      for (int t = 0; t < SP; ++t) raw[t] = staged ? ks[jc * KSTR + SP * kq + t] : Kg[int64_t(jc) * PC + SP * kq + t];
+      f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int t = 0; t < SP; ++t) {
+        const uint32_t wd[4] = {raw[t].x, raw[t].y, raw[t].z, raw[t].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          lp[i & 3] = fma(qs[w][i * 8 + 2 * h], double(__uint_as_float(wd[h] << 16)), lp[i & 3]);
-          lp[i & 3] = fma(qs[w][i * 8 + 2 * h + 1], double(__uint_as_float(wd[h] & 0xFFFF0000u)), lp[i & 3]);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[8 * t + 2 * h], double(__uint_as_float(wd[h] << 16)), acc,
+                                                     0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[8 * t + 2 * h + 1],
+                                                     double(__uint_as_float(wd[h] & 0xFFFF0000u)), acc, 0, 0, 0);
         }
       }
-      const double l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-      if (j0 + lane < nk) {
-        const double Ej = exp(fma(l, inv, -m));
-        s1 = fma(Ej, uw_x, s1);
-        s2 = fma(Ej * Ej, uw_y, s2);
+      double ux = 0.0, uy = 0.0;
+      if (live) {
+        ux = staged ? kst[jl][0] : vstat[(size_t(hk) * Nv + k0 + jl) * 4];
+        uy = staged ? kst[jl][1] : vstat[(size_t(hk) * Nv + k0 + jl) * 4 + 1];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const double Ej = live ? exp(fma(acc[v], inv, -mv[v])) : 0.0;
+        s1[v] = fma(Ej, ux, s1[v]);
+        s2[v] = fma(Ej * Ej, uy, s2[v]);
       }
     }
-    s1 = wave_allsum_d(s1);
-    s2 = wave_allsum_d(s2);
-    const double g = double(nk);
-    const size_t at = (size_t(hd) * Cq + a) * Ck + b;
-    const double A = exp(lb - m);
-    if (lane == 0) {
-      scores[at] = A * A * vn - 2.0 * A * s1 / g + s2 / g;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      s1[v] = rowsum(s1[v]);
+      s2[v] = rowsum(s2[v]);
+      if (i16 == 0) {
+        red[w][0][kq + 4 * v] = s1[v];
+        red[w][1][kq + 4 * v] = s2[v];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 16 && rt + int(threadIdx.x) < n) {
+      const int i = threadIdx.x, a = list[rt + i];
+      const double t1 = (red[0][0][i] + red[1][0][i]) + (red[2][0][i] + red[3][0][i]);
+      const double t2 = (red[0][1][i] + red[1][1][i]) + (red[2][1][i] + red[3][1][i]);
+      const double g = double(nk);
+      const size_t at = (size_t(hd) * Cq + a) * Ck + b;
+      const double A = exp(lbar[at] - shift[size_t(hd) * Cq + a]);
+      scores[at] = A * A * vn - 2.0 * A * t1 / g + t2 / g;
       serr[at] = 0.0;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __syncthreads();  // red is free again
   }
 }
 
