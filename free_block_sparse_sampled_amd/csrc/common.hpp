@@ -55,6 +55,40 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float (&x)[
   }
 }
 
+// The same eight elements in their stored form (one 16-byte piece for bf16, two for fp32), for
+// loads issued ahead of their use: widen8 turns them into fp32 once they are needed, so that the
+// wait for the load falls there and not at the load.
+template <int DT>
+struct Raw8 {
+  uint4 p[DT == SPR_BF16 ? 1 : 2];
+};
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load8_raw(const void* base, int64_t idx) {
+  Raw8<DT> r;
+  if constexpr (DT == SPR_BF16) {
+    r.p[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+  } else {
+    r.p[0] = *reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+    r.p[1] = *reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx + 4);
+  }
+  return r;
+}
+template <int DT>
+__device__ __forceinline__ void widen8(const Raw8<DT>& r, float (&x)[8]) {
+  if constexpr (DT == SPR_BF16) {
+    const uint32_t w[4] = {r.p[0].x, r.p[0].y, r.p[0].z, r.p[0].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x[2 * c] = __uint_as_float(w[c] << 16);
+      x[2 * c + 1] = __uint_as_float(w[c] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r.p[0].x, r.p[0].y, r.p[0].z, r.p[0].w, r.p[1].x, r.p[1].y, r.p[1].z, r.p[1].w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = __uint_as_float(w[c]);
+  }
+}
+
 template <int DT>
 struct ElemSize {
   static constexpr int value = DT == SPR_BF16 ? 2 : 4;

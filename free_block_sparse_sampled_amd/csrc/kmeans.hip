@@ -119,10 +119,17 @@ __global__ __launch_bounds__(256) void km_point_prep_kernel(const double* __rest
       xr[u] = t2.x;
       xr[u + 1] = t2.y;
     }
+    // the mean point's eight coordinates (cb * 8 + 7 < RP <= RPMAX), loaded together
+    double mv[8];
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const double2 m2 = *reinterpret_cast<const double2*>(mu + size_t(hd) * RPMAX + cb * 8 + u);
+      mv[u] = m2.x;
+      mv[u + 1] = m2.y;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = cb * 8 + u;
-      const double x = live ? (xr[u] - mu[size_t(hd) * RPMAX + e]) * sc : 0.0;
+      const double x = live ? (xr[u] - mv[u]) * sc : 0.0;
       const _Float16 h = _Float16(float(x));
       hv[u] = h;
       lv[u] = _Float16(float(x - double(h)));

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict_
   const int hj = blockIdx.y, i0 = blockIdx.x * 16;
   const int m = min(Ms, g.Nv), total = m * G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, kq = lane >> 4;
-  float xv[PER][8];
+  Raw8<DT> xr8[PER];  // the next chunk's rows as stored (zero past the last sampled row)
   auto fetch = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -35,10 +35,9 @@ __global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict_
       if (k < total) {
         const int gi = k / m, sidx = k % m;
         const int64_t row = (int64_t(sidx) * g.Nv) / m;
-        load8<DT>(q, g.base(hj * G + gi) + row * g.sn + c8, xv[u]);
+        xr8[u] = load8_raw<DT>(q, g.base(hj * G + gi) + row * g.sn + c8);
       } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) xv[u][t] = 0.f;
+        xr8[u] = Raw8<DT>{};
       }
     }
   };
@@ -46,9 +45,11 @@ __global__ __launch_bounds__(256) void key_metric_kernel(const void* __restrict_
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + 256 * u, kk = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      float xv[8];
+      widen8<DT>(xr8[u], xv);
 #pragma unroll
       for (int t = 0; t < 8; t += 2)
-        *reinterpret_cast<double2*>(km_xs + kk * XS + c8 + t) = make_double2(xv[u][t], xv[u][t + 1]);
+        *reinterpret_cast<double2*>(km_xs + kk * XS + c8 + t) = make_double2(xv[t], xv[t + 1]);
     }
   };
   f64x4_t acc[TW];
@@ -699,22 +700,24 @@ __global__ __launch_bounds__(512) void project_kernel(const void* __restrict__ x
   const int64_t base = g.base(hd);
   // this thread's share of a chunk: groups of 8 elements e8 = threadIdx.x + 512 u, u < D / 32
   constexpr int PER = D >> 5;  // 4 for d = 128, 2 for d = 64
-  float xv[PER][8];
+  Raw8<DT> xr8[PER];  // the next chunk's rows as stored
   auto fetch = [&](int row0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = (threadIdx.x + 512 * u) * 8, rr = e / D, cc = e % D;
       const int row = row0 + rr < rows ? row0 + rr : rows - 1;
-      load8<DT>(x, base + int64_t(row) * g.sn + cc, xv[u]);
+      xr8[u] = load8_raw<DT>(x, base + int64_t(row) * g.sn + cc);
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = (threadIdx.x + 512 * u) * 8, rr = e / D, cc = e % D;
+      float xv[8];
+      widen8<DT>(xr8[u], xv);
       float* dst = Xs + rr * XS + cc;
-      *reinterpret_cast<float4*>(dst) = make_float4(xv[u][0], xv[u][1], xv[u][2], xv[u][3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[u][4], xv[u][5], xv[u][6], xv[u][7]);
+      *reinterpret_cast<float4*>(dst) = make_float4(xv[0], xv[1], xv[2], xv[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(xv[4], xv[5], xv[6], xv[7]);
     }
   };
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4, r16 = lane & 15;
