@@ -593,9 +593,7 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
     {
       const uint16_t* K = reinterpret_cast<const uint16_t*>(rf_sm + buf * BUF);
       const float* F = reinterpret_cast<const float*>(rf_sm + buf * BUF + size_t(PIECE) * D * 2);
-      // 16-key sub-tiles; all but a group's last one are full (no key past the piece)
-      auto sub = [&](auto full, int t) __attribute__((always_inline)) {
-        constexpr bool FULL = decltype(full)::value;
+      for (int t = 0; t * 16 < n; ++t) {
         const int jl = t * 16 + r16;
         rbf16x8_t kb[KS];
 #pragma unroll
@@ -617,25 +615,20 @@ __global__ __launch_bounds__(kFastWaves * 64) void route_score_fast_kernel(const
         rf32x4_t lg = ch[0];
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) lg += ch[ks];
-        const bool live = FULL || jl < n;
+        const bool live = jl < n;
         const float cc = F[jl], ww = F[PIECE + jl], ac = fabsf(cc);
-        kmax = fmaxf(kmax, live ? F[2 * PIECE + jl] : 0.f);
+        if (live) kmax = fmaxf(kmax, F[2 * PIECE + jl]);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const float l = lg[v];
-          const float e = __builtin_amdgcn_exp2f(fmaf(l, c2, -m2[v]));
-          const float E = FULL ? e : (live ? e : 1.f);
-          const float dl = 1.f - E, ad = fabsf(dl), tt = E + ad, wt = ww * tt;
+          const float E = live ? __builtin_amdgcn_exp2f(fmaf(l, c2, -m2[v])) : 1.f;
+          const float dl = 1.f - E, ad = fabsf(dl), tt = E + ad;
           P1[v] = fmaf(dl, cc, P1[v]);
           P2[v] = fmaf(dl * dl, ww, P2[v]);
           B1[v] = fmaf(ac, tt, B1[v]);
-          B2[v] = fmaf(wt, ad, B2[v]);
-          B3[v] = fmaf(wt, tt, B3[v]);
+          B2[v] = fmaf(ww * ad, tt, B2[v]);
+          B3[v] = fmaf(ww * tt, tt, B3[v]);
         }
-      };
-      for (int t = 0; t * 16 < n; ++t) {
-        if (t * 16 + 16 <= n) sub(std::true_type{}, t);
-        else sub(std::false_type{}, t);
       }
     }
     if (p0 + PIECE >= off[b + 1]) {  // group b complete
