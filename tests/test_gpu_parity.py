@@ -175,6 +175,32 @@ def test_operator_end_to_end(name, heads):
     assert np.all(g["head_status"] & 1 == 0)
 
 
+@pytest.mark.parametrize("d,Ck,n_text", [
+    (64, 128, 32),   # bf16 at d = 64 (every d = 64 instance of the bf16 path), with text tokens
+    (64, 16, 0),     # K/V groups of about 500 keys: past what the fp64 rescoring stages in LDS at d = 64
+    (128, 24, 0),    # the same at d = 128 (groups of about 340 keys against 180 staged)
+])
+def test_bf16_head_dims_and_large_groups(d, Ck, n_text):
+    """The bf16 operator at d = 64, and with K/V groups larger than the fp64 rescoring keeps in LDS
+    (it then reads the group's keys from memory), end to end against the oracle on two heads of a
+    small video latent, with the usual lockstep fallback for decisions inside the tie margin."""
+    cfg = config("small").with_(name=f"small_d{d}_ck{Ck}", H=2, d=d, Ck=Ck, n_text=n_text)
+    opc = op_config(cfg)
+    (q, k, v), (tq, tk, tv) = device_inputs(cfg)
+    op = run_operator(cfg, opc, tq, tk, tv)
+    g = pull(op)
+    p = _oracle_params(opc, cfg.n_text)
+    rows = np.unique(np.concatenate([np.arange(0, cfg.N, 7), np.arange(cfg.N - 100, cfg.N)]))
+    for h in range(cfg.H):
+        ref = O.sparsepr_head(q[0, h], k[0, h], v[0, h], p, head=h, rows=rows)
+        ref["lam"] = p.lam
+        if _oracle_is_tie_free(ref):
+            _compare_head(g, ref, h, cfg.Nv, cfg.N, cfg.n_text)
+        else:
+            _lockstep_head(g, q, k, v, cfg, opc, 0, h, np.random.default_rng(h))
+    assert np.all(g["head_status"] & 1 == 0)
+
+
 @pytest.mark.parametrize("grid,Ck,Cq,M,rho,n_text", [
     ((4, 8, 8), 1, 1, 8, 0.5, 0),         # one group each: the route is every key
     ((4, 8, 8), 256, 256, 16, 0.3, 0),    # one group per key requested (duplicate draws leave empties)
