@@ -1387,10 +1387,19 @@ __global__ __launch_bounds__(256) void probe_select_kernel(const int* __restrict
     const int i = staged ? si[p] : pm[r0 + p];
     const double di = staged ? sd[p] : dd[i];
     int rank = 0;
-    for (int o = 0; o < n; ++o) {
-      const int io = staged ? si[o] : pm[r0 + o];
-      const double dx = staged ? sd[o] : dd[io];
-      rank += (dx < di) || (dx == di && io < i);
+    if (staged) {  // the members from LDS, eight at a time (broadcast reads)
+#pragma unroll 8
+      for (int o = 0; o < n; ++o) {
+        const double dx = sd[o];
+        const int io = si[o];
+        rank += int(dx < di) | (int(dx == di) & int(io < i));
+      }
+    } else {
+      for (int o = 0; o < n; ++o) {
+        const int io = pm[r0 + o];
+        const double dx = dd[io];
+        rank += (dx < di) || (dx == di && io < i);
+      }
     }
     if (rank < m) {
       probe_idx[size_t(hd) * M + po + rank] = i;
