@@ -834,62 +834,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
                  gstat + hd * 8 + 0);
 }
 
-// fp64 score of K/V group b for one query group (qbar in LDS), by the whole wave: lanes take the
-// keys of the group (all loads of a lane's key row and statistics issued before any use), each
-// logit an fp64 dot product, then the sums of the score expansion.
-// (The pointers carry their address spaces: the function is not inlined, and generic pointers
-// would turn the LDS reads into flat loads.)
-typedef __attribute__((address_space(3))) const double lds_cdouble;
 typedef unsigned int ru32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const ru32x4_t glb_cuint4;
-typedef __attribute__((address_space(1))) const double glb_cdouble;
-template <int DT, int D>
-__device__ __attribute__((noinline)) double route_exact_score(glb_cuint4* Kp, int N, int Nv, lds_cdouble* qs,
-                                                              glb_cdouble* vbar, glb_cdouble* vstat, double lb,
-                                                              double m, int k0, int k1, int hk, int Ck, int b,
-                                                              int lane) {
-  constexpr int PER = DT == SPR_BF16 ? 8 : 4;  // elements per 16-byte load
-  const double inv = 1.0 / sqrt(double(D));
-  double vn = 0.0;
-  for (int c = lane; c < D; c += 64) {
-    const double y = vbar[(size_t(hk) * Ck + b) * D + c];
-    vn = fma(y, y, vn);
-  }
-  double s1 = 0.0, s2 = 0.0;
-  for (int j0 = k0; j0 < k1; j0 += 64) {
-    const int j = min(j0 + lane, k1 - 1);
-    glb_cuint4* kr = Kp + (int64_t(hk) * N + j) * (D / PER);
-    ru32x4_t raw[D / PER];
-#pragma unroll
-    for (int i = 0; i < D / PER; ++i) raw[i] = kr[i];
-    const double uw_x = vstat[(size_t(hk) * Nv + j) * 4], uw_y = vstat[(size_t(hk) * Nv + j) * 4 + 1];
-    double l = 0.0;
-#pragma unroll
-    for (int i = 0; i < D / PER; ++i) {
-      const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if constexpr (DT == SPR_BF16) {
-          l = fma(qs[i * 8 + 2 * h], double(__uint_as_float(wd[h] << 16)), l);
-          l = fma(qs[i * 8 + 2 * h + 1], double(__uint_as_float(wd[h] & 0xFFFF0000u)), l);
-        } else {
-          l = fma(qs[i * 4 + h], double(__uint_as_float(wd[h])), l);
-        }
-      }
-    }
-    if (j0 + lane < k1) {
-      const double Ej = exp(fma(l, inv, -m));
-      s1 = fma(Ej, uw_x, s1);
-      s2 = fma(Ej * Ej, uw_y, s2);
-    }
-  }
-  vn = wave_allsum_d(vn);
-  s1 = wave_allsum_d(s1);
-  s2 = wave_allsum_d(s2);
-  const double g = double(k1 - k0);
-  const double A = exp(lb - m);
-  return A * A * vn - 2.0 * A * s1 / g + s2 / g;
-}
 
 // Routing of one query group from the bf16 scores and their bounds, one wave per group, in three
 // phases with the fp64 rescoring between them (route_rescore_kernel, which reads the keys of a
