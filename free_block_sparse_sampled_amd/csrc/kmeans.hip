@@ -628,53 +628,25 @@ __global__ __launch_bounds__(256) void km_reduce_kernel(const double* __restrict
   }
   for (int i0 = 0; i0 < k; i0 += PB) {
     double xb[PB][EPL];
-    if constexpr (R % 64 == 0) {
-      // every lane holds coordinates: the batch's member indices in one vector load (lane i,
-      // i < PB, reads member i0 + i, clamped to the last), broadcast, and the rows loaded with no
-      // branch between the loads; positions past the last member are zero and skipped below
-      static_assert(PB <= 64, "one index per lane");
-      const int idx = od[min(i0 + (lane % PB), k - 1)];
 #pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const int jj = __builtin_amdgcn_readlane(idx, i);
+    for (int i = 0; i < PB; ++i) {
+      const int jj = i0 + i < k ? od[i0 + i] : 0;
 #pragma unroll
-        for (int q = 0; q < EPL; ++q) {
-          const double x = fh[size_t(jj) * R + lane + 64 * q];
-          xb[i][q] = i0 + i < k ? x : 0.0;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const int jj = i0 + i < k ? od[i0 + i] : 0;
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) {
-          const int e = lane + 64 * q;
-          xb[i][q] = (e < R && i0 + i < k) ? fh[size_t(jj) * R + e] : 0.0;
-        }
+      for (int q = 0; q < EPL; ++q) {
+        const int e = lane + 64 * q;
+        xb[i][q] = (e < R && i0 + i < k) ? fh[size_t(jj) * R + e] : 0.0;
       }
     }
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      if constexpr (R % 64 == 0) {
-        if (i0 + i < k) {  // the batch's members in order (a wave-uniform test)
+      if (i0 + i >= k) break;
 #pragma unroll
-          for (int q = 0; q < EPL; ++q) {
-            acc[q] += xb[i][q];
-            const double d = xb[i][q] - cc[q];
-            jl = fma(d, d, jl);
-          }
-        }
-      } else {
-        if (i0 + i >= k) break;
-#pragma unroll
-        for (int q = 0; q < EPL; ++q) {
-          const int e = lane + 64 * q;
-          if (e < R) {
-            acc[q] += xb[i][q];
-            const double d = xb[i][q] - cc[q];
-            jl = fma(d, d, jl);
-          }
+      for (int q = 0; q < EPL; ++q) {
+        const int e = lane + 64 * q;
+        if (e < R) {
+          acc[q] += xb[i][q];
+          const double d = xb[i][q] - cc[q];
+          jl = fma(d, d, jl);
         }
       }
     }
